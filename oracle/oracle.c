@@ -1,0 +1,336 @@
+/*
+ * CPU reference oracle for the CSR conjugate-gradient solve and its adjoint.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code, header or constant with the HIP
+ * library: both sides see only the seeded inputs made by `workloads/`.
+ *
+ * Source of the method: "torch-sla: Differentiable Sparse Linear Algebra with
+ * Adjoint Solvers and Sparse Tensor Parallelism for PyTorch" (gist.science
+ * explainer of arXiv 2601.13994), technical summary:
+ *   - Methodology 1 (unified backend): the sparse tensor API (.solve, .matvec)
+ *     and the shared-pattern SparseTensor; the CPU/GPU CG backends.
+ *   - Methodology 2 (adjoint framework), linear systems: the backward pass
+ *     solves A^T lambda = dL/dx and the matrix gradient is -lambda_i x_j,
+ *     only on the sparsity pattern.
+ *   - Methodology 2, complexity: O(1) graph nodes, O(n + nnz) memory.
+ * The CG steps themselves are the textbook Hestenes-Stiefel method that the
+ * pages call "CG"; the pages fix no variant, so the plain one is used.
+ *
+ * Conventions (the pages are silent; these are the readings this oracle
+ * takes):
+ *   - x0 = 0 unless a start vector is supplied; stop when rr <= (tol*tol)*bb
+ *     with rr the recursively updated residual norm squared and bb = b.b;
+ *     the test is made before each iteration.
+ *   - iterations = number of completed alpha updates.
+ *   - breakdown: p.Ap not finite -> NONFINITE; p.Ap <= 0 -> NOT_SPD.
+ *   - dot products: sequential sums over fixed 4096-element blocks, then a
+ *     sequential sum of the block sums; the bits do not depend on the number
+ *     of OpenMP threads.
+ *   - SpMV: per row, ascending slot order, y = 0 then y = y + a*x per slot.
+ *   - duplicate COO entries: merged into one CSR slot, values summed in
+ *     input order, starting from the first value (not from 0.0).
+ *   - built with -O2 -ffp-contract=off: every * and + is rounded on its own.
+ *
+ * Floating point is IEEE binary64 throughout.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_CSR 2
+#define ORACLE_ERR_NOT_SPD 5
+#define ORACLE_ERR_NONFINITE 6
+#define ORACLE_ERR_NOT_SYMMETRIC 7
+
+#define DOT_BLOCK 4096
+
+/* ------------------------------------------------------------------------ */
+/* COO -> CSR                                                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t row, col, pos;
+} coo_key;
+
+static int cmp_coo_key(const void* pa, const void* pb) {
+  const coo_key* a = (const coo_key*)pa;
+  const coo_key* b = (const coo_key*)pb;
+  if (a->row != b->row) return a->row < b->row ? -1 : 1;
+  if (a->col != b->col) return a->col < b->col ? -1 : 1;
+  if (a->pos != b->pos) return a->pos < b->pos ? -1 : 1;
+  return 0;
+}
+
+/*
+ * Sparse matrix from coordinate triplets: sort the entries by (row, col),
+ * ties kept in input order; equal (row, col) pairs become one stored slot.
+ *
+ *   rowptr[n+1]   out: row i's slots are rowptr[i] .. rowptr[i+1]-1
+ *   col_out[<=m]  out: column of each slot, ascending inside a row
+ *   perm[m]       out: perm[k] = slot that COO entry k was merged into
+ * Returns the number of slots, or -1 if an index is out of range.
+ */
+int64_t oracle_csr_from_coo(int64_t n, int64_t m, const int64_t* row,
+                            const int64_t* col, int64_t* rowptr,
+                            int32_t* col_out, int64_t* perm) {
+  for (int64_t k = 0; k < m; ++k)
+    if (row[k] < 0 || row[k] >= n || col[k] < 0 || col[k] >= n) return -1;
+
+  coo_key* keys = (coo_key*)malloc(sizeof(coo_key) * (size_t)(m > 0 ? m : 1));
+  for (int64_t k = 0; k < m; ++k) {
+    keys[k].row = row[k];
+    keys[k].col = col[k];
+    keys[k].pos = k;
+  }
+  /* (row, col, pos) is a total order, so qsort gives the one sorted result */
+  qsort(keys, (size_t)m, sizeof(coo_key), cmp_coo_key);
+
+  for (int64_t i = 0; i <= n; ++i) rowptr[i] = 0;
+  int64_t slots = 0;
+  for (int64_t s = 0; s < m; ++s) {
+    int first = (s == 0) || keys[s].row != keys[s - 1].row ||
+                keys[s].col != keys[s - 1].col;
+    if (first) {
+      col_out[slots] = (int32_t)keys[s].col;
+      rowptr[keys[s].row + 1] += 1; /* count slots per row */
+      slots += 1;
+    }
+    perm[keys[s].pos] = slots - 1;
+  }
+  for (int64_t i = 0; i < n; ++i) rowptr[i + 1] += rowptr[i];
+  free(keys);
+  return slots;
+}
+
+/*
+ * Values of the merged matrix from COO values: every slot takes the values
+ * of the COO entries mapped onto it, added in input order, starting from the
+ * first one.
+ */
+void oracle_values_from_coo(int64_t m, int64_t nnz, const int64_t* perm,
+                            const double* coo_val, double* vals) {
+  char* seen = (char*)calloc((size_t)(nnz > 0 ? nnz : 1), 1);
+  for (int64_t k = 0; k < m; ++k) {
+    int64_t s = perm[k];
+    if (!seen[s]) {
+      vals[s] = coo_val[k];
+      seen[s] = 1;
+    } else {
+      vals[s] = vals[s] + coo_val[k];
+    }
+  }
+  free(seen);
+}
+
+/* Explicit transpose (A^T) of a CSR matrix; columns come out ascending. */
+void oracle_transpose(int64_t n, const int64_t* rowptr, const int32_t* col,
+                      const double* vals, int64_t* rowptr_t, int32_t* col_t,
+                      double* vals_t) {
+  int64_t nnz = rowptr[n];
+  for (int64_t i = 0; i <= n; ++i) rowptr_t[i] = 0;
+  for (int64_t k = 0; k < nnz; ++k) rowptr_t[col[k] + 1] += 1;
+  for (int64_t i = 0; i < n; ++i) rowptr_t[i + 1] += rowptr_t[i];
+  int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  for (int64_t i = 0; i < n; ++i) fill[i] = rowptr_t[i];
+  /* walking rows in order puts each transposed row's columns in order */
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) {
+      int64_t j = col[k];
+      int64_t dst = fill[j]++;
+      col_t[dst] = (int32_t)i;
+      vals_t[dst] = vals[k];
+    }
+  }
+  free(fill);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Vector kernels                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* y = A x  (the sparse tensor's .matvec) */
+void oracle_spmv(int64_t n, const int64_t* rowptr, const int32_t* col,
+                 const double* vals, const double* x, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double s = 0.0;
+    for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) s = s + vals[k] * x[col[k]];
+    y[i] = s;
+  }
+}
+
+/* u . v, blocked so that the result is the same for any thread count */
+double oracle_dot(int64_t n, const double* u, const double* v) {
+  int64_t nb = (n + DOT_BLOCK - 1) / DOT_BLOCK;
+  double* part = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t lo = b * DOT_BLOCK;
+    int64_t hi = lo + DOT_BLOCK < n ? lo + DOT_BLOCK : n;
+    double s = 0.0;
+    for (int64_t i = lo; i < hi; ++i) s = s + u[i] * v[i];
+    part[b] = s;
+  }
+  double total = 0.0;
+  for (int64_t b = 0; b < nb; ++b) total = total + part[b];
+  free(part);
+  return total;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Conjugate gradient                                                        */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t iterations;
+  double rr;        /* final recursive residual norm squared */
+  double bb;        /* b . b */
+  int32_t converged;
+} oracle_cg_info;
+
+/*
+ * Solve A x = b for SPD A by plain CG.
+ *   use_x0      : x holds the start vector on entry (else x0 = 0)
+ *   hist_*      : optional (may be NULL), length >= maxit; per iteration k
+ *                 alpha_k, beta_k and the residual norm squared after it.
+ * Returns ORACLE_OK (converged or not), ORACLE_ERR_NOT_SPD or
+ * ORACLE_ERR_NONFINITE; x then holds the last iterate.
+ */
+int oracle_cg(int64_t n, const int64_t* rowptr, const int32_t* col,
+              const double* vals, const double* b, double* x, double tol,
+              int64_t maxit, int use_x0, oracle_cg_info* info,
+              double* hist_alpha, double* hist_beta, double* hist_rr) {
+  size_t bytes = sizeof(double) * (size_t)(n > 0 ? n : 1);
+  double* r = (double*)malloc(bytes);
+  double* p = (double*)malloc(bytes);
+  double* q = (double*)malloc(bytes);
+  int status = ORACLE_OK;
+
+  /* r0 = b - A x0 ; p0 = r0 */
+  if (use_x0) {
+    oracle_spmv(n, rowptr, col, vals, x, q);
+    for (int64_t i = 0; i < n; ++i) r[i] = b[i] - q[i];
+  } else {
+    for (int64_t i = 0; i < n; ++i) {
+      x[i] = 0.0;
+      r[i] = b[i];
+    }
+  }
+  for (int64_t i = 0; i < n; ++i) p[i] = r[i];
+
+  double bb = oracle_dot(n, b, b);
+  double rr = oracle_dot(n, r, r);
+  double stop = (tol * tol) * bb;
+  int64_t k = 0;
+  if (!isfinite(bb) || !isfinite(rr)) {
+    status = ORACLE_ERR_NONFINITE;
+  } else {
+    while (k < maxit) {
+      if (rr <= stop) break;
+      oracle_spmv(n, rowptr, col, vals, p, q); /* q = A p */
+      double pq = oracle_dot(n, p, q);
+      if (!isfinite(pq)) {
+        status = ORACLE_ERR_NONFINITE;
+        break;
+      }
+      if (!(pq > 0.0)) {
+        status = ORACLE_ERR_NOT_SPD;
+        break;
+      }
+      double alpha = rr / pq;
+      for (int64_t i = 0; i < n; ++i) {
+        x[i] = x[i] + alpha * p[i];
+        r[i] = r[i] - alpha * q[i];
+      }
+      double rr_new = oracle_dot(n, r, r);
+      if (!isfinite(rr_new)) {
+        status = ORACLE_ERR_NONFINITE;
+        break;
+      }
+      double beta = rr_new / rr;
+      for (int64_t i = 0; i < n; ++i) p[i] = r[i] + beta * p[i];
+      if (hist_alpha) hist_alpha[k] = alpha;
+      if (hist_beta) hist_beta[k] = beta;
+      if (hist_rr) hist_rr[k] = rr_new;
+      rr = rr_new;
+      k = k + 1;
+    }
+  }
+  info->iterations = k;
+  info->rr = rr;
+  info->bb = bb;
+  info->converged = (status == ORACLE_OK && rr <= stop) ? 1 : 0;
+  free(r);
+  free(p);
+  free(q);
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Adjoint of the linear solve                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Backward pass of x = A^{-1} b for a loss L with g = dL/dx:
+ *   A^T lambda = g          (solved by the same CG, on an explicit A^T)
+ *   grad_b     = lambda
+ *   grad_A     = -lambda_i x_j for every stored slot (i, j), nothing else.
+ * Returns the CG status; ORACLE_ERR_NOT_SYMMETRIC if A^T differs from A
+ * (CG needs a symmetric matrix; the solve is still done on A^T).
+ */
+int oracle_adjoint(int64_t n, const int64_t* rowptr, const int32_t* col,
+                   const double* vals, const double* x, const double* g,
+                   double* grad_b, double* grad_vals, double tol,
+                   int64_t maxit, oracle_cg_info* info) {
+  int64_t nnz = rowptr[n];
+  int64_t* rowptr_t = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int32_t* col_t = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+  double* vals_t = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
+  oracle_transpose(n, rowptr, col, vals, rowptr_t, col_t, vals_t);
+  int symmetric = 1;
+  for (int64_t i = 0; i <= n && symmetric; ++i)
+    if (rowptr_t[i] != rowptr[i]) symmetric = 0;
+  for (int64_t k = 0; k < nnz && symmetric; ++k)
+    if (col_t[k] != col[k] || memcmp(&vals_t[k], &vals[k], sizeof(double)) != 0)
+      symmetric = 0;
+
+  int status = oracle_cg(n, rowptr_t, col_t, vals_t, g, grad_b, tol, maxit, 0,
+                         info, NULL, NULL, NULL);
+  const double* lambda = grad_b;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k)
+      grad_vals[k] = -(lambda[i] * x[col[k]]);
+
+  free(rowptr_t);
+  free(col_t);
+  free(vals_t);
+  if (status == ORACLE_OK && !symmetric) status = ORACLE_ERR_NOT_SYMMETRIC;
+  return status;
+}
+
+/* grad_vals[k] = -lambda_i x_j on every stored slot (the last step above) */
+void oracle_pattern_grad(int64_t n, const int64_t* rowptr, const int32_t* col,
+                         const double* lambda, const double* x,
+                         double* grad_vals) {
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k)
+      grad_vals[k] = -(lambda[i] * x[col[k]]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Threads                                                                   */
+/* ------------------------------------------------------------------------ */
+#ifdef _OPENMP
+#include <omp.h>
+void oracle_set_threads(int t) { omp_set_num_threads(t > 0 ? t : 1); }
+int oracle_get_threads(void) { return omp_get_max_threads(); }
+#else
+void oracle_set_threads(int t) { (void)t; }
+int oracle_get_threads(void) { return 1; }
+#endif

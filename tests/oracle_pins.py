@@ -1,0 +1,470 @@
+"""Pins of the CPU oracle against what the mathematics fixes.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle (or a
+deliberately broken build of it, passed as ``lib``) disagrees with a closed
+form, a textbook identity, brute force or a hand-derived value.  None of
+them re-types the oracle's own formulas: they check properties the correct
+result must have.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import workloads as W
+from closed_forms import eigval, eigvec, spectrum_bounds
+
+EPS = np.finfo(np.float64).eps
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _poisson(N):
+    rp, c, v = W.poisson_csr(N, np.int64)
+    return oracle.CSR(N * N, rp, c, v)
+
+
+def _random_spd_csr(n, density, seed):
+    """A random sparse SPD matrix (diagonally dominant), CSR built by numpy."""
+    rng = np.random.default_rng(seed)
+    M = np.where(rng.random((n, n)) < density, rng.uniform(-1, 1, (n, n)), 0.0)
+    M = np.triu(M, 1)
+    M = M + M.T
+    M += np.diag(np.abs(M).sum(axis=1) + rng.uniform(0.5, 1.5, n))
+    rows, cols = np.nonzero(M)
+    rowptr = np.zeros(n + 1, np.int64)
+    np.add.at(rowptr, rows + 1, 1)
+    rowptr = np.cumsum(rowptr)
+    return oracle.CSR(n, rowptr, cols.astype(np.int32), M[rows, cols].copy()), M
+
+
+# --------------------------------------------------------------------------
+# CSR construction
+# --------------------------------------------------------------------------
+
+def pin_csr_poisson_closed_form(lib=None):
+    """P0: the merged CSR of a shuffled Poisson COO is the closed-form CSR."""
+    for N in (1, 2, 7, 16):
+        row, col, val = W.poisson_coo(N)
+        r2, c2, v2 = W.shuffled_coo(row, col, val, seed=N)
+        rp, cc, perm = oracle.csr_from_coo(N * N, r2, c2, lib=lib)
+        vals = oracle.values_from_coo(perm, int(rp[-1]), v2, lib=lib)
+        rp_ref, c_ref, v_ref = W.poisson_csr(N, np.int64)
+        assert np.array_equal(rp, rp_ref), "rowptr"
+        assert np.array_equal(cc, c_ref), "col"
+        assert np.array_equal(vals.view(np.int64), v_ref.view(np.int64)), "vals"
+        # every COO entry points at a slot with its own row and column
+        rows_of_slot = np.repeat(np.arange(N * N), np.diff(rp))
+        assert np.array_equal(rows_of_slot[perm], r2) and np.array_equal(cc[perm], c2)
+
+
+def brute_force_csr(n, row, col, val):
+    """Python sorted() over (row, col, input position) and a left fold."""
+    order = sorted(range(len(row)), key=lambda k: (row[k], col[k], k))
+    rowptr = [0] * (n + 1)
+    cols, vals, perm = [], [], [0] * len(row)
+    prev = None
+    for k in order:
+        key = (row[k], col[k])
+        if key != prev:
+            cols.append(col[k])
+            vals.append(val[k])
+            rowptr[row[k] + 1] += 1
+            prev = key
+        else:
+            vals[-1] = vals[-1] + val[k]
+        perm[k] = len(cols) - 1
+    for i in range(n):
+        rowptr[i + 1] += rowptr[i]
+    return (np.array(rowptr, np.int64), np.array(cols, np.int32),
+            np.array(vals, np.float64), np.array(perm, np.int64))
+
+
+def tiny_coo_cases():
+    rng = np.random.default_rng(123)
+    cases = [
+        (1, [0], [0], [-0.0]),             # a lone negative zero keeps its sign
+        (3, [], [], []),                   # no entries at all: three empty rows
+        (4, [3, 3, 3], [1, 1, 1], [0.1, 0.2, 0.3]),  # triple duplicate
+        (5, [4, 0, 4, 0], [0, 4, 0, 4], [1.0, 2.0, -1.0, -2.0]),  # cancels to 0
+    ]
+    for t in range(24):
+        n = int(rng.integers(1, 65))
+        m = int(rng.integers(0, 4 * n))
+        row = rng.integers(0, n, m)
+        col = rng.integers(0, n, m)
+        # force duplicates
+        if m > 4:
+            k = rng.integers(0, m, m // 4)
+            row = np.concatenate([row, row[k]])
+            col = np.concatenate([col, col[k]])
+        val = rng.standard_normal(row.shape[0])
+        val[rng.random(val.shape[0]) < 0.1] = 0.0  # explicit zeros stay stored
+        cases.append((n, row.tolist(), col.tolist(), val.tolist()))
+    return cases
+
+
+def pin_csr_brute_force(lib=None):
+    """P0b: bit-exact agreement with brute force on tiny COO with duplicates."""
+    for n, row, col, val in tiny_coo_cases():
+        rp_b, c_b, v_b, p_b = brute_force_csr(n, row, col, val)
+        rp, cc, perm = oracle.csr_from_coo(n, np.array(row, np.int64),
+                                           np.array(col, np.int64), lib=lib)
+        vals = oracle.values_from_coo(perm, int(rp[-1]), np.array(val, np.float64), lib=lib)
+        assert np.array_equal(rp, rp_b), (n, "rowptr")
+        assert np.array_equal(cc, c_b), (n, "col")
+        assert np.array_equal(perm, p_b), (n, "perm")
+        assert np.array_equal(vals.view(np.int64), v_b.view(np.int64)), (n, "vals")
+
+
+def pin_csr_rgg_symmetric(lib=None):
+    """P0c: the random-geometric-graph Laplacian is bitwise symmetric and its
+    rows sum to the shift (up to rounding)."""
+    n = 3000
+    row, col, val, _ = W.rgg_coo(n, 4, 5)
+    rp, cc, perm = oracle.csr_from_coo(n, row, col, lib=lib)
+    vals = oracle.values_from_coo(perm, int(rp[-1]), val, lib=lib)
+    A = oracle.CSR(n, rp, cc, vals)
+    T = oracle.transpose(A, lib=lib)
+    assert np.array_equal(T.rowptr, A.rowptr) and np.array_equal(T.col, A.col)
+    assert np.array_equal(T.vals.view(np.int64), A.vals.view(np.int64))
+    rowsum = np.add.reduceat(vals, rp[:-1]) if n else vals
+    diag = np.abs(vals).max()
+    assert np.all(np.abs(rowsum - 1e-2) <= 64 * EPS * diag)
+    assert 7.0 < A.nnz / n < 10.0
+
+
+# --------------------------------------------------------------------------
+# SpMV and dot
+# --------------------------------------------------------------------------
+
+def pin_spmv_eigenpairs(lib=None):
+    """P1: A v = lambda v for the closed-form Laplacian eigenpairs."""
+    for N, modes in ((16, [(1, 1), (3, 7), (16, 16)]), (100, [(1, 1), (50, 2), (99, 100)])):
+        A = _poisson(N)
+        for p, q in modes:
+            v = eigvec(N, p, q)
+            lam = eigval(N, p, q)
+            Av = oracle.spmv(A, v, lib=lib)
+            rel = np.linalg.norm(Av - lam * v) / np.linalg.norm(lam * v)
+            assert rel <= 64 * EPS * 8.0 / lam, (N, p, q, rel)
+            rq = oracle.dot(v, Av, lib=lib) / oracle.dot(v, v, lib=lib)
+            assert abs(rq - lam) <= 64 * EPS * 8.0, (N, p, q, rq, lam)
+
+
+def pin_spmv_dense(lib=None):
+    """P1b: matches dense A @ x within the summation error bound."""
+    for seed, n in ((0, 1), (1, 17), (2, 64), (3, 200)):
+        A, M = _random_spd_csr(n, 0.1, seed)
+        x = np.random.default_rng(seed + 100).standard_normal(n)
+        y = oracle.spmv(A, x, lib=lib)
+        bound = 8 * EPS * (np.abs(M) @ np.abs(x)) + 1e-300
+        assert np.all(np.abs(y - M @ x) <= bound), seed
+
+
+def pin_dot(lib=None):
+    """dot agrees with the exactly rounded sum (math.fsum) within n*eps*sum|uv|."""
+    rng = np.random.default_rng(9)
+    for n in (0, 1, 4095, 4096, 4097, 20000):
+        u = rng.standard_normal(n)
+        v = rng.standard_normal(n)
+        d = oracle.dot(u, v, lib=lib)
+        exact = math.fsum((u * v).tolist()) if n else 0.0
+        # products are exact-ish: the bound covers their rounding too
+        assert abs(d - exact) <= (n + 2) * EPS * float(np.abs(u * v).sum()) + 1e-300, n
+
+
+# --------------------------------------------------------------------------
+# CG
+# --------------------------------------------------------------------------
+
+def pin_cg_one_step(lib=None):
+    """P2: an eigenvector right-hand side is solved in one iteration."""
+    for N, (p, q) in ((8, (2, 3)), (32, (5, 5)), (64, (64, 1))):
+        A = _poisson(N)
+        v = eigvec(N, p, q)
+        lam = eigval(N, p, q)
+        x, info = oracle.cg(A, v, 1e-10, 100, lib=lib)
+        assert info.status == oracle.OK and info.iterations == 1, (N, info)
+        assert np.linalg.norm(x - v / lam) <= 1e-12 * np.linalg.norm(v / lam)
+
+
+def pin_cg_m_step(lib=None):
+    """P3: m eigenvectors with distinct eigenvalues above 4 need exactly m
+    iterations (Krylov space of dimension m)."""
+    N = 32
+    A = _poisson(N)
+    for m in range(1, 7):
+        modes = [(N, N - k) for k in range(m)]
+        lams = [eigval(N, p, q) for p, q in modes]
+        assert min(lams) > 4.0 and len(set(np.round(lams, 12))) == m
+        b = sum(eigvec(N, p, q) * (1.0 + 0.5 * k) for k, (p, q) in enumerate(modes))
+        x, info = oracle.cg(A, b, 1e-12, 100, lib=lib)
+        assert info.status == oracle.OK and info.converged and info.iterations == m, (m, info)
+        xe = sum(eigvec(N, p, q) * (1.0 + 0.5 * k) / eigval(N, p, q)
+                 for k, (p, q) in enumerate(modes))
+        assert np.linalg.norm(x - xe) <= 1e-11 * np.linalg.norm(xe)
+
+
+def pin_cg_dense_lu(lib=None):
+    """P4: tiny grids and random SPD matrices agree with a dense LU solve."""
+    for N in (1, 2, 5, 16):
+        A = _poisson(N)
+        b = W.uniform_rhs(N * N, N)
+        x, info = oracle.cg(A, b, 1e-13, 1000, lib=lib)
+        xl = np.linalg.solve(A.to_dense(), b)
+        assert info.converged and np.linalg.norm(x - xl) <= 1e-10 * np.linalg.norm(xl), N
+    for seed in range(3):
+        A, M = _random_spd_csr(60, 0.15, seed)
+        b = np.random.default_rng(seed).standard_normal(60)
+        x, info = oracle.cg(A, b, 1e-13, 1000, lib=lib)
+        xl = np.linalg.solve(M, b)
+        assert info.converged and np.linalg.norm(x - xl) <= 1e-10 * np.linalg.norm(xl), seed
+
+
+def pin_cg_manufactured(lib=None):
+    """P5: b = A u* for u* = sin(pi x) sin(pi y) gives back u*.  n = 10^4 > 4096
+    so the blocked dot product uses several blocks."""
+    N = 100
+    A = _poisson(N)
+    u, b = W.manufactured(N)
+    x, info = oracle.cg(A, b, 0.0, 600, lib=lib)
+    assert info.status == oracle.OK and info.iterations == 600 and not info.converged
+    assert np.linalg.norm(x - u) <= 1e-12 * np.linalg.norm(u), np.linalg.norm(x - u)
+    # the recursive residual tracks the true one
+    r_true = b - A.to_dense() @ x if N <= 40 else b - oracle.spmv(A, x, lib=lib)
+    assert np.linalg.norm(r_true) <= 1e-11 * np.linalg.norm(b)
+
+
+def pin_cg_ritz(lib=None):
+    """P10: Ritz values of the Lanczos matrix built from (alpha, beta) lie in
+    the closed-form spectrum and reach both ends."""
+    N = 32
+    A = _poisson(N)
+    b = W.uniform_rhs(N * N, 0)
+    x, info, (al, be, rr) = oracle.cg(A, b, 1e-10, 10000, history=True, lib=lib)
+    k = info.iterations
+    lo, hi = spectrum_bounds(N)
+    for kk in (10, 50, k):
+        d = np.array([1.0 / al[j] + (be[j - 1] / al[j - 1] if j else 0.0) for j in range(kk)])
+        e = np.array([np.sqrt(be[j]) / al[j] for j in range(kk - 1)])
+        T = np.diag(d) + np.diag(e, 1) + np.diag(e, -1)
+        ritz = np.linalg.eigvalsh(T)
+        assert ritz.min() >= lo * (1 - 1e-9) and ritz.max() <= hi * (1 + 1e-12), kk
+    assert abs(ritz.max() - hi) <= 1e-8 * hi and abs(ritz.min() - lo) <= 1e-6 * lo
+
+
+def pin_cg_energy(lib=None):
+    """P13: with x0 = 0, b.x_k = sum_j alpha_j r_j.r_j (exact arithmetic), and
+    the recursive residual matches b - A x_k."""
+    for N, tol, maxit in ((32, 1e-10, 10000), (60, 0.0, 150)):
+        A = _poisson(N)
+        b = W.uniform_rhs(N * N, 0)
+        x, info, (al, be, rr) = oracle.cg(A, b, tol, maxit, history=True, lib=lib)
+        rrs = np.concatenate([[info.bb], rr[:-1]])
+        lhs = float(b @ x)
+        rhs = math.fsum((al * rrs).tolist())
+        assert abs(lhs - rhs) <= 1e-13 * abs(rhs), (N, lhs, rhs)
+        r_true = b - A.to_dense() @ x
+        assert abs(np.linalg.norm(r_true) ** 2 - info.rr) <= 1e-6 * info.rr + 1e-28 * info.bb
+
+
+def pin_cg_statuses(lib=None):
+    """Degenerate inputs: b = 0, NaN, an indefinite matrix, maxit, tol = 0, n = 1."""
+    A = _poisson(8)
+    n = 64
+    x, info = oracle.cg(A, np.zeros(n), 1e-10, 100, lib=lib)
+    assert info.status == oracle.OK and info.iterations == 0 and info.converged
+    assert np.all(x == 0)
+    bad = W.uniform_rhs(n, 1)
+    bad[5] = np.nan
+    _, info = oracle.cg(A, bad, 1e-10, 100, lib=lib)
+    assert info.status == oracle.ERR_NONFINITE
+    neg = oracle.CSR(A.n, A.rowptr, A.col, -A.vals)
+    _, info = oracle.cg(neg, W.uniform_rhs(n, 2), 1e-10, 100, lib=lib)
+    assert info.status == oracle.ERR_NOT_SPD and info.iterations == 0
+    _, info = oracle.cg(A, W.uniform_rhs(n, 3), 1e-10, 1, lib=lib)
+    assert info.status == oracle.OK and info.iterations == 1 and not info.converged
+    _, info = oracle.cg(A, W.uniform_rhs(n, 3), 0.0, 7, lib=lib)
+    assert info.iterations == 7 and not info.converged
+    A1 = oracle.CSR(1, np.array([0, 1], np.int64), np.array([0], np.int32), np.array([2.5]))
+    x, info = oracle.cg(A1, np.array([3.0]), 1e-12, 10, lib=lib)
+    assert info.iterations == 1 and abs(x[0] - 1.2) <= 2 * EPS * 1.2
+    # a warm start at the solution needs no iteration
+    b = W.uniform_rhs(n, 4)
+    xl = np.linalg.solve(A.to_dense(), b)
+    x, info = oracle.cg(A, b, 1e-8, 100, x0=xl, lib=lib)
+    assert info.iterations == 0 and np.array_equal(x, xl)
+
+
+def pin_cg_warm_start(lib=None):
+    """A start vector away from the solution still converges to the dense LU
+    solution, and from x0 the run equals plain CG on A e = b - A x0."""
+    N = 12
+    A = _poisson(N)
+    n = N * N
+    b = W.uniform_rhs(n, 5)
+    x0 = W.normal_rhs(n, 6)
+    x, info = oracle.cg(A, b, 1e-13, 1000, x0=x0, lib=lib)
+    xl = np.linalg.solve(A.to_dense(), b)
+    assert info.converged and np.linalg.norm(x - xl) <= 1e-10 * np.linalg.norm(xl)
+    e, info_e = oracle.cg(A, b - A.to_dense() @ x0, 1e-13 * np.linalg.norm(b) /
+                          np.linalg.norm(b - A.to_dense() @ x0), 1000, lib=lib)
+    assert abs(info_e.iterations - info.iterations) <= 1
+    assert np.linalg.norm(x0 + e - xl) <= 1e-10 * np.linalg.norm(xl)
+
+
+# --------------------------------------------------------------------------
+# Adjoint
+# --------------------------------------------------------------------------
+
+def pin_adjoint_identities(lib=None):
+    """P6: g.x = lambda.b;  P6b: sum_k vals_k grad_k = -lambda.(A x) = -lambda.b."""
+    N = 32
+    A = _poisson(N)
+    b = W.uniform_rhs(N * N, 0)
+    g = W.normal_rhs(N * N, 1)
+    x, _ = oracle.cg(A, b, 1e-12, 10000, lib=lib)
+    gb, gv, info = oracle.adjoint(A, x, g, 1e-12, 10000, lib=lib)
+    assert info.status == oracle.OK and info.converged
+    assert abs(g @ x - gb @ b) <= 1e-10 * abs(g @ x)
+    assert abs(A.vals @ gv + gb @ b) <= 1e-10 * abs(gb @ b)
+
+
+def _dense_loss(M, b, g):
+    return float(g @ np.linalg.solve(M, b))
+
+
+def pin_adjoint_fd(lib=None):
+    """P7: central finite differences of L = g.x over every stored slot (the
+    perturbed matrix is not symmetric, so it is solved by dense LU) and over b."""
+    for N in (3, 4):
+        A = _poisson(N)
+        n = N * N
+        rng = np.random.default_rng(N)
+        vals = A.vals + rng.uniform(-0.2, 0.2, A.nnz) * (A.vals == 4.0)  # vary the diagonal
+        A = oracle.CSR(n, A.rowptr, A.col, vals)
+        b = rng.uniform(-1, 1, n)
+        g = rng.standard_normal(n)
+        x, _ = oracle.cg(A, b, 1e-14, 1000, lib=lib)
+        gb, gv, _ = oracle.adjoint(A, x, g, 1e-14, 1000, lib=lib)
+        M = A.to_dense()
+        rows = np.repeat(np.arange(n), np.diff(A.rowptr))
+        fd = np.zeros(A.nnz)
+        for k in range(A.nnz):
+            d = 1e-5 * max(1.0, abs(vals[k]))
+            Mp = M.copy()
+            Mp[rows[k], A.col[k]] += d
+            Mm = M.copy()
+            Mm[rows[k], A.col[k]] -= d
+            fd[k] = (_dense_loss(Mp, b, g) - _dense_loss(Mm, b, g)) / (2 * d)
+        assert np.max(np.abs(fd - gv)) <= 1e-6 * np.max(np.abs(gv)), N
+        fdb = np.zeros(n)
+        for i in range(n):
+            e = np.zeros(n)
+            e[i] = 1e-5
+            fdb[i] = (_dense_loss(M, b + e, g) - _dense_loss(M, b - e, g)) / 2e-5
+        assert np.max(np.abs(fdb - gb)) <= 1e-6 * np.max(np.abs(gb)), N
+
+
+def pin_adjoint_support(lib=None):
+    """P8: one gradient per stored slot, in slot order; a stored explicit zero
+    still gets -lambda_i x_j; nothing is written for absent entries."""
+    n = 6
+    # tridiagonal SPD with explicit zeros stored at (0, 5) and (5, 0)
+    entries = {}
+    for i in range(n):
+        entries[(i, i)] = 3.0
+        if i + 1 < n:
+            entries[(i, i + 1)] = -1.0
+            entries[(i + 1, i)] = -1.0
+    entries[(0, 5)] = 0.0
+    entries[(5, 0)] = 0.0
+    keys = sorted(entries)
+    rows = [k[0] for k in keys]
+    cols = [k[1] for k in keys]
+    vals = [entries[k] for k in keys]
+    rp = np.zeros(n + 1, np.int64)
+    np.add.at(rp, np.array(rows) + 1, 1)
+    A = oracle.CSR(n, np.cumsum(rp), np.array(cols, np.int32), np.array(vals))
+    b = np.arange(1.0, n + 1)
+    g = np.ones(n)
+    x, _ = oracle.cg(A, b, 1e-14, 100, lib=lib)
+    gb, gv, _ = oracle.adjoint(A, x, g, 1e-14, 100, lib=lib)
+    assert gv.shape == (A.nnz,)
+    k05 = [k for k in range(A.nnz) if rows[k] == 0 and cols[k] == 5][0]
+    assert vals[k05] == 0.0 and gv[k05] != 0.0
+    M = A.to_dense()
+    xl = np.linalg.solve(M, b)
+    ll = np.linalg.solve(M.T, g)
+    full = -np.outer(ll, xl)
+    assert np.allclose(gv, full[rows, cols], rtol=1e-10, atol=0)
+
+
+def pin_adjoint_golden(lib=None):
+    """P11: hand-derived exact values (tests/golden/adjoint_small.json) and the
+    1 x 1 closed form x = b/a, lambda = g/a, grad = -g b / a^2."""
+    with open(os.path.join(GOLDEN, "adjoint_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        fr = lambda xs: np.array([float(Fraction(s)) for s in xs])
+        A = oracle.CSR(c["n"], np.array(c["rowptr"], np.int64),
+                       np.array(c["col"], np.int32), fr(c["vals"]))
+        b, g = fr(c["b"]), fr(c["g"])
+        x, info = oracle.cg(A, b, 1e-15, 100, lib=lib)
+        assert np.allclose(x, fr(c["x"]), rtol=0, atol=1e-14), c["name"]
+        gb, gv, _ = oracle.adjoint(A, x, g, 1e-15, 100, lib=lib)
+        assert np.allclose(gb, fr(c["lambda"]), rtol=0, atol=1e-14), c["name"]
+        assert np.allclose(gv, fr(c["grad_vals"]), rtol=0, atol=1e-14), c["name"]
+        assert abs(g @ x - float(Fraction(c["loss"]))) <= 1e-14
+    for a, bb, gg in ((2.5, 3.0, -1.5), (7.0, 0.5, 2.0)):
+        A1 = oracle.CSR(1, np.array([0, 1], np.int64), np.array([0], np.int32), np.array([a]))
+        x, _ = oracle.cg(A1, np.array([bb]), 1e-15, 10, lib=lib)
+        gb, gv, _ = oracle.adjoint(A1, x, np.array([gg]), 1e-15, 10, lib=lib)
+        assert abs(gb[0] - gg / a) <= 4 * EPS * abs(gg / a)
+        assert abs(gv[0] + gg * bb / a**2) <= 8 * EPS * abs(gg * bb / a**2)
+
+
+def pin_adjoint_nonsymmetric_flag(lib=None):
+    """The adjoint solves with the explicit transpose and reports a matrix that
+    is not symmetric."""
+    A = oracle.CSR(2, np.array([0, 2, 4], np.int64), np.array([0, 1, 0, 1], np.int32),
+                   np.array([4.0, 1.0, 0.5, 3.0]))
+    x = np.array([1.0, 2.0])
+    g = np.array([1.0, -1.0])
+    gb, gv, info = oracle.adjoint(A, x, g, 1e-15, 10, lib=lib)
+    assert info.status == oracle.ERR_NOT_SYMMETRIC
+    # the gradient is still -lambda_i x_j on the four stored slots
+    assert np.array_equal(gv, -(np.repeat(gb, 2) * x[[0, 1, 0, 1]]))
+
+
+# --------------------------------------------------------------------------
+# Batched
+# --------------------------------------------------------------------------
+
+def pin_batched_shift_spectrum(lib=None):
+    """P9: system s of the shifted batch has spectrum lambda_pq + c_s, so an
+    eigenvector right-hand side is solved in one iteration with x = v/(lambda+c_s)."""
+    N, B = 16, 5
+    rowptr, col, vals, _, shifts = W.batched_poisson(N, B, 2, 3)
+    v = eigvec(N, 3, 4)
+    lam = eigval(N, 3, 4)
+    xs, infos = oracle.cg_batched(rowptr.astype(np.int64), col, vals,
+                                  np.repeat(v[None], B, 0), 1e-10, 100, lib=lib)
+    for s in range(B):
+        assert infos[s].iterations == 1
+        assert np.linalg.norm(xs[s] - v / (lam + shifts[s])) <= 1e-12 * np.linalg.norm(v)
+
+
+ALL_PINS = [
+    pin_csr_poisson_closed_form, pin_csr_brute_force, pin_csr_rgg_symmetric,
+    pin_spmv_eigenpairs, pin_spmv_dense, pin_dot,
+    pin_cg_one_step, pin_cg_m_step, pin_cg_dense_lu, pin_cg_manufactured,
+    pin_cg_ritz, pin_cg_energy, pin_cg_statuses, pin_cg_warm_start,
+    pin_adjoint_identities, pin_adjoint_fd, pin_adjoint_support, pin_adjoint_golden,
+    pin_adjoint_nonsymmetric_flag, pin_batched_shift_spectrum,
+]

@@ -1,0 +1,73 @@
+"""Planted mistakes: each mutation below is a plausible slip in the oracle
+(a dropped term, a wrong sign, index or operand).  A mutated copy of
+``oracle.c`` is compiled into a temporary directory and every pin is run
+against it in a child process; at least one pin must fail.  The real oracle
+source is never modified.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTATIONS = {
+    "spmv_row_for_col": ("s = s + vals[k] * x[col[k]]", "s = s + vals[k] * x[i]"),
+    "grad_sign": ("grad_vals[k] = -(lambda[i] * x[col[k]])", "grad_vals[k] = (lambda[i] * x[col[k]])"),
+    "grad_transposed": ("grad_vals[k] = -(lambda[i] * x[col[k]])", "grad_vals[k] = -(lambda[col[k]] * x[i])"),
+    "beta_inverted": ("double beta = rr_new / rr;", "double beta = rr / rr_new;"),
+    "alpha_inverted": ("double alpha = rr / pq;", "double alpha = pq / rr;"),
+    "residual_sign": ("r[i] = r[i] - alpha * q[i];", "r[i] = r[i] + alpha * q[i];"),
+    "x_uses_q": ("x[i] = x[i] + alpha * p[i];", "x[i] = x[i] + alpha * q[i];"),
+    "p_drops_old_p": ("p[i] = r[i] + beta * p[i];", "p[i] = r[i] + beta * r[i];"),
+    "dot_drops_last_block": ("for (int64_t b = 0; b < nb; ++b) total = total + part[b];",
+                             "for (int64_t b = 0; b + 1 < nb; ++b) total = total + part[b];"),
+    "merge_last_wins": ("vals[s] = vals[s] + coo_val[k];", "vals[s] = coo_val[k];"),
+    "sort_ignores_col": ("  if (a->col != b->col) return a->col < b->col ? -1 : 1;\n", ""),
+    "stop_strict": ("if (rr <= stop) break;", "if (rr < stop) break;"),
+    "adjoint_rhs_is_x": ("oracle_cg(n, rowptr_t, col_t, vals_t, g, grad_b",
+                         "oracle_cg(n, rowptr_t, col_t, vals_t, x, grad_b"),
+    "rowptr_shifted": ("rowptr[keys[s].row + 1] += 1;", "rowptr[keys[s].row] += 1;"),
+    "warm_start_sign": ("r[i] = b[i] - q[i];", "r[i] = q[i] - b[i];"),
+    "transpose_keeps_rows": ("col_t[dst] = (int32_t)i;", "col_t[dst] = (int32_t)j;"),
+}
+
+CHILD = r"""
+import sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, oracle_pins
+lib = oracle._load({lib!r})
+failed = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(lib=lib)
+    except Exception as e:
+        failed.append(pin.__name__)
+        break
+print("FAILED:" + ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    import oracle
+
+    src = open(SRC).read()
+    old, new = MUTATIONS[name]
+    assert old in src, f"mutation anchor not found: {old!r}"
+    with tempfile.TemporaryDirectory() as d:
+        msrc = os.path.join(d, "oracle_mut.c")
+        with open(msrc, "w") as f:
+            f.write(src.replace(old, new))
+        lib = os.path.join(d, "liboracle_mut.so")
+        oracle.build(msrc, lib)
+        code = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                           timeout=300, env=env)
+        out = p.stdout.strip().splitlines()
+        caught = p.returncode != 0 or (out and out[-1] != "FAILED:")
+        assert caught, f"mutation {name} survived every pin"

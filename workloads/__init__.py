@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs shared by the HIP library's tests, the oracle's
+tests and the benchmark.
+
+This module only *defines inputs*: matrix patterns and values, right-hand
+sides and loss gradients, all from fixed seeds (numpy PCG64).  It contains
+none of the solver's arithmetic (no CSR build from COO, no SpMV, no dot, no
+CG) and imports neither the product library nor the oracle.
+
+Workloads (the torch-sla explainer's experiments use 2D Poisson systems on
+one GPU up to 169M unknowns; the unstructured and batched cases stand in for
+its SparseTensor batching and graph-Laplacian use):
+
+* Poisson 5-point Laplacian on an N x N interior grid, Dirichlet-zero
+  boundary eliminated, diagonal 4, neighbours -1 (no 1/h^2 scaling),
+  unknown (a, c) with 1 <= a, c <= N numbered i = (c-1) N + (a-1),
+  columns ascending i-N, i-1, i, i+1, i+N.
+* A shared-pattern batch: the same Laplacian plus a per-system diagonal
+  shift c_s ~ U(0, 1).
+* A random geometric graph Laplacian: points i.i.d. uniform in the unit
+  square in sampling order (hence a random node order), an edge when two
+  points are within r = sqrt(deg / (pi n)), one weight ~ U(0.5, 1.5) per
+  undirected edge drawn in lexicographic (i < j) order, A = D - W + shift I.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "poisson_n", "poisson_nnz", "poisson_csr", "poisson_coo", "manufactured",
+    "uniform_rhs", "normal_rhs", "batched_poisson", "rgg_coo", "shuffled_coo",
+    "CONFIGS",
+]
+
+
+def poisson_n(N: int) -> int:
+    return N * N
+
+
+def poisson_nnz(N: int) -> int:
+    return 5 * N * N - 4 * N
+
+
+def _poisson_slots(N: int):
+    """(n, 5) candidate columns and the mask of the ones inside the grid."""
+    n = N * N
+    idx_t = np.int64 if n >= 2**31 - N else np.int32
+    i = np.arange(n, dtype=idx_t)
+    a = i % N  # x position, 0-based
+    c = i // N  # y position, 0-based
+    cand = np.empty((n, 5), dtype=idx_t)
+    cand[:, 0] = i - N
+    cand[:, 1] = i - 1
+    cand[:, 2] = i
+    cand[:, 3] = i + 1
+    cand[:, 4] = i + N
+    mask = np.empty((n, 5), dtype=bool)
+    mask[:, 0] = c > 0
+    mask[:, 1] = a > 0
+    mask[:, 2] = True
+    mask[:, 3] = a < N - 1
+    mask[:, 4] = c < N - 1
+    return cand, mask
+
+
+def poisson_csr(N: int, rowptr_dtype=np.int32, diag: float = 4.0, off: float = -1.0):
+    """Closed-form CSR of the N x N 5-point Laplacian.
+
+    Returns (rowptr[rowptr_dtype, n+1], col[int32, nnz], vals[float64, nnz]).
+    """
+    cand, mask = _poisson_slots(N)
+    counts = mask.sum(axis=1, dtype=np.int64)
+    rowptr = np.zeros(N * N + 1, dtype=np.int64)
+    np.cumsum(counts, out=rowptr[1:])
+    col = cand[mask].astype(np.int32, copy=False)
+    del cand
+    kind = np.broadcast_to(np.array([0, 0, 1, 0, 0], dtype=bool), mask.shape)[mask]
+    vals = np.where(kind, diag, off).astype(np.float64)
+    return rowptr.astype(rowptr_dtype), col, vals
+
+
+def poisson_coo(N: int):
+    """The same matrix as coordinate triplets (row, col int64; val float64)."""
+    rowptr, col, vals = poisson_csr(N, np.int64)
+    row = np.repeat(np.arange(N * N, dtype=np.int64), np.diff(rowptr))
+    return row, col.astype(np.int64), vals
+
+
+def manufactured(N: int):
+    """u*(x, y) = sin(pi x) sin(pi y) at the interior nodes, h = 1/(N+1),
+    and b = A u* written out with the 5-point stencil on the grid."""
+    h = 1.0 / (N + 1)
+    s = np.sin(np.pi * h * np.arange(1, N + 1))
+    U = np.outer(s, s)  # U[c-1, a-1] = sin(pi a h) sin(pi c h)
+    P = np.zeros((N + 2, N + 2))
+    P[1:-1, 1:-1] = U
+    B = 4.0 * U - P[1:-1, :-2] - P[1:-1, 2:] - P[:-2, 1:-1] - P[2:, 1:-1]
+    return U.reshape(-1).copy(), B.reshape(-1).copy()
+
+
+def uniform_rhs(n: int, seed: int) -> np.ndarray:
+    return np.random.default_rng(seed).uniform(-1.0, 1.0, n)
+
+
+def normal_rhs(n: int, seed: int, shape=None) -> np.ndarray:
+    return np.random.default_rng(seed).standard_normal(shape if shape is not None else n)
+
+
+def batched_poisson(N: int, batch: int, seed_shift: int, seed_rhs: int):
+    """Shared 5-point pattern; system s has diagonal 4 + c_s, c_s ~ U(0, 1).
+
+    Returns (rowptr, col, vals[batch, nnz], b[batch, n], shifts[batch]).
+    """
+    rowptr, col, base = poisson_csr(N, np.int32)
+    shifts = np.random.default_rng(seed_shift).uniform(0.0, 1.0, batch)
+    diag_slot = base == 4.0
+    vals = np.repeat(base[None, :], batch, axis=0)
+    vals[:, diag_slot] = 4.0 + shifts[:, None]
+    b = np.random.default_rng(seed_rhs).standard_normal((batch, N * N))
+    return rowptr, col, vals, b, shifts
+
+
+def rgg_coo(n: int, seed_points: int, seed_weights: int, degree: float = 8.0,
+            shift: float = 1e-2):
+    """Random geometric graph Laplacian + shift*I as unsorted COO triplets.
+
+    Entry order: (i, j) for every edge i < j, then (j, i) for the same
+    edges, then the n diagonal entries; the matrix is symmetric bit for bit.
+    Returns (row int64, col int64, val float64, points).
+    """
+    from scipy.spatial import cKDTree
+
+    pts = np.random.default_rng(seed_points).random((n, 2))
+    r = float(np.sqrt(degree / (np.pi * n)))
+    pairs = cKDTree(pts).query_pairs(r, output_type="ndarray").astype(np.int64)
+    order = np.lexsort((pairs[:, 1], pairs[:, 0]))
+    i, j = pairs[order, 0], pairs[order, 1]
+    w = np.random.default_rng(seed_weights).uniform(0.5, 1.5, i.shape[0])
+    deg = np.bincount(i, weights=w, minlength=n) + np.bincount(j, weights=w, minlength=n)
+    d = np.arange(n, dtype=np.int64)
+    row = np.concatenate([i, j, d])
+    col = np.concatenate([j, i, d])
+    val = np.concatenate([-w, -w, deg + shift])
+    return row, col, val, pts
+
+
+def shuffled_coo(row, col, val, seed: int, dup_frac: float = 0.0):
+    """A permutation of COO triplets, optionally with some entries split into
+    duplicates whose values add up to the original only up to rounding (the
+    test compares merged results, not the original values)."""
+    rng = np.random.default_rng(seed)
+    m = row.shape[0]
+    if dup_frac > 0:
+        k = rng.choice(m, size=max(1, int(dup_frac * m)), replace=False)
+        extra = rng.uniform(-1.0, 1.0, k.shape[0])
+        row = np.concatenate([row, row[k]])
+        col = np.concatenate([col, col[k]])
+        val = np.concatenate([val, extra])
+    perm = rng.permutation(row.shape[0])
+    return row[perm], col[perm], val[perm]
+
+
+# The benchmark / parity workloads, named by what they are.
+CONFIGS = {
+    "poisson32": dict(kind="poisson", N=32, rhs="uniform", seed_b=0, seed_g=1,
+                      tol=1e-10, maxit=10000, rowptr="i32"),
+    "poisson1000_fixed1000": dict(kind="poisson", N=1000, rhs="manufactured",
+                                  seed_g=1, tol=0.0, maxit=1000, rowptr="i32"),
+    "batched64_poisson128": dict(kind="batched", N=128, batch=64, seed_shift=2,
+                                 seed_b=3, tol=1e-8, maxit=10000, rowptr="i32"),
+    "rgg4m": dict(kind="rgg", n=4_000_000, seed_points=4, seed_weights=5,
+                  seed_b=6, seed_g=7, tol=1e-8, maxit=20000, rowptr="i32"),
+    "poisson4000_fixed500": dict(kind="poisson", N=4000, rhs="uniform", seed_b=0,
+                                 tol=0.0, maxit=500, rowptr="i32"),
+    "poisson13000_fixed500": dict(kind="poisson", N=13000, rhs="uniform", seed_b=0,
+                                  tol=0.0, maxit=500, rowptr="i64"),
+}
