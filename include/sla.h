@@ -1,0 +1,204 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) sparse CG solver with an adjoint
+ * backward pass.
+ *
+ * The operations are those of the torch-sla explainer (gist.science, arXiv
+ * 2601.13994), technical summary:
+ *   - Methodology 1 (unified backend abstraction): a sparse tensor with a
+ *     .matvec and a .solve; a SparseTensor is one matrix or a batch of
+ *     matrices sharing one sparsity pattern.
+ *   - Methodology 2 (adjoint differentiation framework), linear systems: the
+ *     backward pass of x = A^{-1} b solves A^T lambda = dL/dx, returns
+ *     dL/db = lambda and dL/dA = -lambda_i x_j only on the sparsity pattern;
+ *     the graph is O(1) nodes and the memory O(n + nnz), whatever the number
+ *     of solver iterations.
+ *   - Experimental results: the CG backend on 2D Poisson systems.
+ * The solver is plain (unpreconditioned) conjugate gradients for symmetric
+ * positive definite A, so A^T = A and the adjoint reuses A.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - Floating point is IEEE binary64.  Column indices are int32 (n < 2^31);
+ *     row pointers are int32 or int64 (sla_index), chosen per matrix.
+ *   - Batched arrays are system-major: values [batch][nnz], vectors
+ *     [batch][n], contiguous.
+ *   - Work is enqueued on `stream` (0 = the null stream).  Calls that fill a
+ *     _host output synchronise `stream` before returning; the others are
+ *     asynchronous.
+ *   - No C++ exception crosses this boundary.  Every call returns an
+ *     sla_status; on failure sla_last_error() gives a message (per thread).
+ *     Arguments are checked before anything is launched.
+ *   - A handle is not thread-safe: calls on one handle must not overlap.
+ */
+#ifndef SLA_H_
+#define SLA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLA_OK = 0,
+  SLA_ERR_ARG = 1,        /* bad argument (null pointer, size, flag)          */
+  SLA_ERR_CSR = 2,        /* malformed pattern (range, order, duplicates)     */
+  SLA_ERR_OOM = 3,        /* device allocation failed                          */
+  SLA_ERR_DEVICE = 4,     /* a HIP call failed                                  */
+  SLA_ERR_NOT_SPD = 5,    /* CG breakdown: p.Ap <= 0                            */
+  SLA_ERR_NONFINITE = 6   /* b.b, p.Ap or r.r is not finite                     */
+} sla_status;
+
+typedef enum { SLA_I32 = 4, SLA_I64 = 8 } sla_index;
+
+/* Result of one solve (one system of a batch). */
+typedef struct {
+  int64_t iterations;   /* completed CG iterations (alpha updates)            */
+  double rel_residual;  /* sqrt(rr / bb), rr the recursive residual norm^2    */
+  int32_t converged;    /* rr <= (tol*tol) * bb                               */
+  int32_t status;       /* sla_status of this system                          */
+} sla_cg_info;
+
+enum {
+  SLA_FLAG_X0 = 1,      /* x holds the start vector (default: x0 = 0)        */
+  SLA_FLAG_HISTORY = 2  /* record alpha, beta, rr of every iteration         */
+};
+
+/* Opaque matrix handle: the sparsity pattern (owned by the library, copied
+ * or built at creation) plus a borrowed pointer to the values. */
+typedef struct sla_csr_s* sla_csr;
+
+/*
+ * Build a CSR pattern from COO coordinates (Methodology 1: SparseTensor).
+ *   n            matrix order (square), 1 <= n < 2^31
+ *   nnz_coo      number of triplets, 0 <= nnz_coo < 2^32
+ *   coo_idx      width of coo_row / coo_col entries (SLA_I32 or SLA_I64)
+ *   rowptr_idx   width of the CSR row pointer to build (SLA_I32 needs the
+ *                merged nnz < 2^31)
+ * The result is the unique sorted pattern: entries ordered by (row, col);
+ * equal (row, col) pairs merge into one slot; explicit zeros are kept.  It is
+ * bit-identical on every run.  sla_csr_values_from_coo maps values onto it.
+ * Errors: SLA_ERR_ARG (sizes, nulls), SLA_ERR_CSR (an index out of range),
+ * SLA_ERR_OOM.  *out is set only on SLA_OK.  Synchronises `stream`.
+ */
+sla_status sla_csr_create(int64_t n, int64_t nnz_coo, sla_index coo_idx,
+                          const void* coo_row, const void* coo_col,
+                          sla_index rowptr_idx, hipStream_t stream, sla_csr* out);
+
+/*
+ * Take a CSR pattern as given: rowptr [n+1] (rowptr_idx wide), col [nnz].
+ * Validated (rowptr[0] = 0, rowptr[n] = nnz, non-decreasing; columns in range
+ * and strictly increasing inside each row) and copied.  Errors: SLA_ERR_ARG,
+ * SLA_ERR_CSR, SLA_ERR_OOM.  Synchronises `stream`.
+ */
+sla_status sla_csr_create_from_csr(int64_t n, int64_t nnz, sla_index rowptr_idx,
+                                   const void* rowptr, const int32_t* col,
+                                   hipStream_t stream, sla_csr* out);
+
+/* Free the handle and everything the library allocated for it. */
+sla_status sla_csr_destroy(sla_csr A);
+
+/* Sizes: order, stored slots, COO triplets it was built from (0 if from CSR),
+ * row-pointer width.  Any output pointer may be NULL. */
+sla_status sla_csr_get_info(sla_csr A, int64_t* n_host, int64_t* nnz_host,
+                            int64_t* nnz_coo_host, sla_index* rowptr_idx_host);
+
+/* Borrowed views of the pattern (valid until destroy).  perm[k] is the CSR
+ * slot COO triplet k was merged into; NULL for a handle made from CSR. */
+sla_status sla_csr_pattern(sla_csr A, const void** rowptr_host,
+                           const int32_t** col_host, const int64_t** perm_host);
+
+/* Copy the pattern into caller buffers (any may be NULL): rowptr_out [n+1]
+ * of the handle's row-pointer width, col_out [nnz], perm_out [nnz_coo]
+ * (COO-built handles only).  Asynchronous on `stream`. */
+sla_status sla_csr_copy_pattern(sla_csr A, void* rowptr_out, int32_t* col_out,
+                                int64_t* perm_out, hipStream_t stream);
+
+/*
+ * CSR values from COO values: vals[s][slot] = the COO values mapped onto that
+ * slot, added in input order starting from the first one.  coo_val
+ * [batch][nnz_coo], vals [batch][nnz].  Needs a COO-built handle.
+ */
+sla_status sla_csr_values_from_coo(sla_csr A, const double* coo_val, double* vals,
+                                   int64_t batch, hipStream_t stream);
+
+/* Gradient of COO values from the gradient of CSR values:
+ * grad_coo[s][k] = grad_vals[s][perm[k]] (every duplicate gets its slot's). */
+sla_status sla_csr_grad_to_coo(sla_csr A, const double* grad_vals, double* grad_coo,
+                               int64_t batch, hipStream_t stream);
+
+/*
+ * Bind the values: vals [batch][nnz] in CSR slot order, owned by the caller,
+ * read by every later spmv / solve / adjoint until re-bound.  batch >= 1.
+ */
+sla_status sla_csr_set_values(sla_csr A, const double* vals, int64_t batch);
+
+/* y[s] = A_s x[s] for every system s of the bound batch (the .matvec). */
+sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream);
+
+/*
+ * Solve A x = b by CG (bound batch must be 1).  x0 = 0 unless SLA_FLAG_X0.
+ * Stops when rr <= (tol*tol)*bb with rr the recursive residual norm squared
+ * and bb = b.b (checked before each iteration), or after maxit iterations;
+ * tol = 0 runs exactly maxit iterations.  Not converging is SLA_OK with
+ * info.converged = 0.  SLA_ERR_NOT_SPD / SLA_ERR_NONFINITE leave the last
+ * iterate in x.  The loop runs on the device (alpha, beta and the stopping
+ * test never leave it); the host polls a small status word between blocks
+ * of iterations.  info_host may be NULL.  Synchronises `stream`.
+ */
+sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol,
+                        int64_t maxit, uint32_t flags, sla_cg_info* info_host,
+                        hipStream_t stream);
+
+/*
+ * Backward pass of x = A^{-1} b (Methodology 2, linear systems): given x and
+ * grad_x = dL/dx, solve A^T lambda = grad_x by the same CG (A^T = A for the
+ * SPD matrices CG accepts), write grad_b = lambda and
+ * grad_vals[k] = -lambda_i x_j for every stored slot k = (i, j).  grad_vals
+ * may be NULL (then only grad_b).  Memory: O(n + nnz), independent of the
+ * iteration count.  Same stopping rule and statuses as sla_cg_solve.
+ */
+sla_status sla_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
+                          double* grad_b, double* grad_vals, double tol,
+                          int64_t maxit, uint32_t flags, sla_cg_info* info_host,
+                          hipStream_t stream);
+
+/* Shared-pattern batch (Methodology 1, SparseTensor batching): every system
+ * of the bound batch solved independently, each with its own scalars and
+ * stopping test.  b, x [batch][n]; info_host [batch] (may be NULL).  Returns
+ * the first non-OK system status, else SLA_OK. */
+sla_status sla_cg_solve_batched(sla_csr A, const double* b, double* x, double tol,
+                                int64_t maxit, uint32_t flags, sla_cg_info* info_host,
+                                hipStream_t stream);
+
+sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad_x,
+                                  double* grad_b, double* grad_vals, double tol,
+                                  int64_t maxit, uint32_t flags,
+                                  sla_cg_info* info_host, hipStream_t stream);
+
+/* The pattern gradient alone: grad_vals[s][k] = -lambda[s][i] * x[s][j]. */
+sla_status sla_pattern_grad(sla_csr A, const double* lambda, const double* x,
+                            double* grad_vals, hipStream_t stream);
+
+/* After a solve with SLA_FLAG_HISTORY: copy system `system`'s per-iteration
+ * alpha_k, beta_k and r.r after iteration k (host arrays of length cap; any
+ * may be NULL).  *count_host = iterations recorded. */
+sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha_host,
+                          double* beta_host, double* rr_host, int64_t cap,
+                          int64_t* count_host);
+
+/* Iterations per captured HIP graph block (default 32; 0 = launch kernels
+ * one by one without graphs).  Affects speed only, never results. */
+sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sla_last_error(void);
+
+/* Name of a status code. */
+const char* sla_status_string(sla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLA_H_ */

@@ -1,0 +1,427 @@
+"""Python face of ``libsla.so``: a sparse CG solve with an O(1)-graph adjoint.
+
+Every function here only marshals arguments (torch CUDA tensors -> device
+pointers, the current HIP stream) and calls the C ABI declared in
+``include/sla.h`` under the same name; every step of the computation runs in
+the library's HIP kernels.  PyTorch provides device memory, streams and the
+autograd node.  The library must be built (``python
+krylov_solvers_adjoint_amd/_build.py``); importing this package without it
+raises ImportError: there is no fallback.
+
+Source of the method: the torch-sla explainer (gist.science, arXiv
+2601.13994), technical summary -- Methodology 1 (sparse tensors with
+.solve/.matvec, shared-pattern batches) and Methodology 2 (linear-system
+adjoint: A^T lambda = dL/dx, grad_b = lambda, grad_A = -lambda_i x_j on the
+pattern; one graph node, O(n + nnz) memory).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loads torch's HIP runtime first: the library then shares it
+
+__all__ = [
+    "SlaError", "CGInfo", "CSRPattern", "SparseTensor", "solve",
+    "sla_csr_create", "sla_csr_create_from_csr", "sla_csr_values_from_coo",
+    "sla_csr_grad_to_coo", "sla_spmv", "sla_cg_solve", "sla_cg_adjoint",
+    "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
+    "LIB_PATH", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
+
+OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE = range(7)
+I32, I64 = 4, 8
+FLAG_X0, FLAG_HISTORY = 1, 2
+
+EXPORTS = [
+    "sla_csr_create", "sla_csr_create_from_csr", "sla_csr_destroy", "sla_csr_get_info",
+    "sla_csr_pattern", "sla_csr_copy_pattern", "sla_csr_values_from_coo",
+    "sla_csr_grad_to_coo", "sla_csr_set_values", "sla_spmv", "sla_cg_solve",
+    "sla_cg_adjoint", "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
+    "sla_cg_history", "sla_csr_set_graph_block", "sla_last_error", "sla_status_string",
+]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python krylov_solvers_adjoint_amd/_build.py` "
+        "(there is no CPU fallback)")
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("iterations", ctypes.c_int64), ("rel_residual", ctypes.c_double),
+                ("converged", ctypes.c_int32), ("status", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+_U32 = ctypes.c_uint32
+_S = ctypes.c_int
+
+
+def _bind(lib):
+    sig = {
+        "sla_csr_create": [_I64, _I64, _S, _P, _P, _S, _P, ctypes.POINTER(_P)],
+        "sla_csr_create_from_csr": [_I64, _I64, _S, _P, _P, _P, ctypes.POINTER(_P)],
+        "sla_csr_destroy": [_P],
+        "sla_csr_get_info": [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                             ctypes.POINTER(_I64), ctypes.POINTER(_S)],
+        "sla_csr_pattern": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P)],
+        "sla_csr_copy_pattern": [_P, _P, _P, _P, _P],
+        "sla_csr_values_from_coo": [_P, _P, _P, _I64, _P],
+        "sla_csr_grad_to_coo": [_P, _P, _P, _I64, _P],
+        "sla_csr_set_values": [_P, _P, _I64],
+        "sla_spmv": [_P, _P, _P, _P],
+        "sla_cg_solve": [_P, _P, _P, _D, _I64, _U32, _P, _P],
+        "sla_cg_adjoint": [_P, _P, _P, _P, _P, _D, _I64, _U32, _P, _P],
+        "sla_cg_solve_batched": [_P, _P, _P, _D, _I64, _U32, _P, _P],
+        "sla_cg_adjoint_batched": [_P, _P, _P, _P, _P, _D, _I64, _U32, _P, _P],
+        "sla_pattern_grad": [_P, _P, _P, _P, _P],
+        "sla_cg_history": [_P, _I64, _P, _P, _P, _I64, ctypes.POINTER(_I64)],
+        "sla_csr_set_graph_block": [_P, _I64],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = _S
+    lib.sla_last_error.argtypes = []
+    lib.sla_last_error.restype = ctypes.c_char_p
+    lib.sla_status_string.argtypes = [_S]
+    lib.sla_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _bind(ctypes.CDLL(LIB_PATH))
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = _lib.sla_status_string(status).decode()
+        super().__init__(f"{name}: {message}")
+
+
+def _check(status: int):
+    if status != OK:
+        raise SlaError(status, _lib.sla_last_error().decode(errors="replace"))
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor (the library has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _shape(t: torch.Tensor, shape: tuple, name: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _vec_shape(A: "CSRPattern", batch: int, like: torch.Tensor) -> tuple:
+    return (A.n,) if like.dim() == 1 and batch == 1 else (batch, A.n)
+
+
+def _idx_code(dtype) -> int:
+    if dtype == torch.int32:
+        return I32
+    if dtype == torch.int64:
+        return I64
+    raise TypeError(f"index dtype must be int32 or int64, got {dtype}")
+
+
+@dataclass
+class CGInfo:
+    iterations: int
+    rel_residual: float
+    converged: bool
+    status: int
+
+
+def _infos(arr) -> list:
+    return [CGInfo(int(i.iterations), float(i.rel_residual), bool(i.converged), int(i.status))
+            for i in arr]
+
+
+# ---------------------------------------------------------------------------
+# The pattern handle
+# ---------------------------------------------------------------------------
+class CSRPattern:
+    """Owner of an ``sla_csr`` handle: the sparsity pattern in HBM (int32 or
+    int64 row pointers, int32 columns) and the solver workspace."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        n, nnz, m = _I64(), _I64(), _I64()
+        w = _S()
+        _check(_lib.sla_csr_get_info(self._h, ctypes.byref(n), ctypes.byref(nnz),
+                                     ctypes.byref(m), ctypes.byref(w)))
+        self.n, self.nnz, self.nnz_coo = n.value, nnz.value, m.value
+        self.rowptr_dtype = torch.int32 if w.value == I32 else torch.int64
+        self._bound = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            _lib.sla_csr_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pattern(self):
+        """(rowptr, col, perm) as new device tensors (perm None if built from CSR)."""
+        dev = torch.device("cuda", torch.cuda.current_device())
+        rowptr = torch.empty(self.n + 1, dtype=self.rowptr_dtype, device=dev)
+        col = torch.empty(max(self.nnz, 0), dtype=torch.int32, device=dev)
+        perm = (torch.empty(self.nnz_coo, dtype=torch.int64, device=dev)
+                if self.nnz_coo > 0 else None)
+        _check(_lib.sla_csr_copy_pattern(self._h, rowptr.data_ptr(), col.data_ptr(),
+                                         perm.data_ptr() if perm is not None else None,
+                                         _stream()))
+        return rowptr, col, perm
+
+    def bind(self, values: torch.Tensor) -> int:
+        """Bind values [nnz] or [batch, nnz] (float64, CSR slot order)."""
+        if values.dim() not in (1, 2):
+            raise ValueError("values must be [nnz] or [batch, nnz]")
+        batch = 1 if values.dim() == 1 else values.shape[0]
+        if values.shape[-1] != self.nnz or batch < 1:
+            raise ValueError(f"values has shape {tuple(values.shape)}, the pattern {self.nnz} slots")
+        _check(_lib.sla_csr_set_values(self._h, _dev(values, torch.float64, "values"), batch))
+        self._bound = values
+        return batch
+
+    def set_graph_block(self, iterations: int):
+        _check(_lib.sla_csr_set_graph_block(self._h, int(iterations)))
+
+    def history(self, system: int = 0, cap: int = 1 << 20):
+        import numpy as np
+        cnt = _I64()
+        _check(_lib.sla_cg_history(self._h, system, None, None, None, 0, ctypes.byref(cnt)))
+        k = min(cnt.value, cap)
+        a, b, r = (np.zeros(max(k, 1)) for _ in range(3))
+        _check(_lib.sla_cg_history(self._h, system, a.ctypes.data, b.ctypes.data,
+                                   r.ctypes.data, k, ctypes.byref(cnt)))
+        return a[:k], b[:k], r[:k]
+
+
+# ---------------------------------------------------------------------------
+# Same-named wrappers of the C ABI
+# ---------------------------------------------------------------------------
+def sla_csr_create(n: int, row: torch.Tensor, col: torch.Tensor,
+                   rowptr_dtype=torch.int32, stream=None) -> CSRPattern:
+    """COO coordinates (int32 or int64 device tensors) -> CSR pattern."""
+    if row.shape != col.shape or row.dtype != col.dtype:
+        raise ValueError("row and col must have the same shape and dtype")
+    code = _idx_code(row.dtype)
+    h = ctypes.c_void_p()
+    m = row.numel()
+    _check(_lib.sla_csr_create(int(n), m, code, _dev(row, row.dtype, "row") if m else None,
+                               _dev(col, col.dtype, "col") if m else None,
+                               _idx_code(rowptr_dtype), _stream(stream), ctypes.byref(h)))
+    return CSRPattern(h.value)
+
+
+def sla_csr_create_from_csr(rowptr: torch.Tensor, col: torch.Tensor, stream=None) -> CSRPattern:
+    n = rowptr.numel() - 1
+    h = ctypes.c_void_p()
+    _check(_lib.sla_csr_create_from_csr(
+        n, col.numel(), _idx_code(rowptr.dtype), _dev(rowptr, rowptr.dtype, "rowptr"),
+        _dev(col, torch.int32, "col") if col.numel() else None, _stream(stream),
+        ctypes.byref(h)))
+    return CSRPattern(h.value)
+
+
+def sla_csr_values_from_coo(A: CSRPattern, coo_val: torch.Tensor, stream=None) -> torch.Tensor:
+    batch = 1 if coo_val.dim() == 1 else coo_val.shape[0]
+    if A.nnz_coo == 0 and A.nnz > 0:
+        raise ValueError("pattern was not built from COO")
+    _shape(coo_val, (A.nnz_coo,) if coo_val.dim() == 1 else (batch, A.nnz_coo), "coo_val")
+    out = torch.empty((batch, A.nnz) if coo_val.dim() == 2 else (A.nnz,),
+                      dtype=torch.float64, device=coo_val.device)
+    _check(_lib.sla_csr_values_from_coo(A.handle, _dev(coo_val, torch.float64, "coo_val"),
+                                        out.data_ptr(), batch, _stream(stream)))
+    return out
+
+
+def sla_csr_grad_to_coo(A: CSRPattern, grad_vals: torch.Tensor, stream=None) -> torch.Tensor:
+    batch = 1 if grad_vals.dim() == 1 else grad_vals.shape[0]
+    _shape(grad_vals, (A.nnz,) if grad_vals.dim() == 1 else (batch, A.nnz), "grad_vals")
+    out = torch.empty((batch, A.nnz_coo) if grad_vals.dim() == 2 else (A.nnz_coo,),
+                      dtype=torch.float64, device=grad_vals.device)
+    _check(_lib.sla_csr_grad_to_coo(A.handle, _dev(grad_vals, torch.float64, "grad_vals"),
+                                    out.data_ptr(), batch, _stream(stream)))
+    return out
+
+
+def sla_spmv(A: CSRPattern, values: torch.Tensor, x: torch.Tensor, stream=None) -> torch.Tensor:
+    batch = A.bind(values)
+    _shape(x, _vec_shape(A, batch, x), "x")
+    y = torch.empty_like(x)
+    _check(_lib.sla_spmv(A.handle, _dev(x, torch.float64, "x"), y.data_ptr(), _stream(stream)))
+    return y
+
+
+def _solve_call(fn, A, b, x, tol, maxit, flags, batch, stream, check):
+    _shape(b, _vec_shape(A, batch, b), "b")
+    _shape(x, _vec_shape(A, batch, b), "x")
+    infos = (_Info * batch)()
+    st = fn(A.handle, _dev(b, torch.float64, "b"), _dev(x, torch.float64, "x"), float(tol),
+            int(maxit), int(flags), infos, _stream(stream))
+    if check:
+        _check(st)
+    return st, _infos(infos)
+
+
+def sla_cg_solve(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: float, maxit: int,
+                 x0: torch.Tensor | None = None, history: bool = False, stream=None,
+                 check: bool = True):
+    """x, CGInfo.  Raises SlaError on breakdown unless check=False."""
+    batch = A.bind(values)
+    if batch != 1:
+        raise ValueError("sla_cg_solve takes one system; use sla_cg_solve_batched")
+    x = x0.clone() if x0 is not None else torch.empty_like(b)
+    flags = (FLAG_X0 if x0 is not None else 0) | (FLAG_HISTORY if history else 0)
+    st, infos = _solve_call(_lib.sla_cg_solve, A, b, x, tol, maxit, flags, 1, stream, check)
+    return x, infos[0]
+
+
+def sla_cg_solve_batched(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: float,
+                         maxit: int, x0: torch.Tensor | None = None, history: bool = False,
+                         stream=None, check: bool = True):
+    batch = A.bind(values)
+    if b.shape[0] != batch:
+        raise ValueError("b must be [batch, n]")
+    x = x0.clone() if x0 is not None else torch.empty_like(b)
+    flags = (FLAG_X0 if x0 is not None else 0) | (FLAG_HISTORY if history else 0)
+    st, infos = _solve_call(_lib.sla_cg_solve_batched, A, b, x, tol, maxit, flags, batch,
+                            stream, check)
+    return x, infos
+
+
+def _adjoint_call(fn, A, x, grad_x, tol, maxit, want_vals, flags, batch, stream, check):
+    _shape(grad_x, _vec_shape(A, batch, grad_x), "grad_x")
+    _shape(x, _vec_shape(A, batch, grad_x), "x")
+    grad_b = torch.empty_like(grad_x)
+    grad_vals = (torch.empty((batch, A.nnz) if grad_x.dim() == 2 else (A.nnz,),
+                             dtype=torch.float64, device=grad_x.device) if want_vals else None)
+    infos = (_Info * batch)()
+    st = fn(A.handle, _dev(x, torch.float64, "x"), _dev(grad_x, torch.float64, "grad_x"),
+            grad_b.data_ptr(), grad_vals.data_ptr() if grad_vals is not None else None,
+            float(tol), int(maxit), int(flags), infos, _stream(stream))
+    if check:
+        _check(st)
+    return grad_b, grad_vals, _infos(infos)
+
+
+def sla_cg_adjoint(A: CSRPattern, values: torch.Tensor, x: torch.Tensor, grad_x: torch.Tensor,
+                   tol: float, maxit: int, want_vals: bool = True, history: bool = False,
+                   stream=None, check: bool = True):
+    """(grad_b = lambda, grad_vals or None, CGInfo)."""
+    if A.bind(values) != 1:
+        raise ValueError("sla_cg_adjoint takes one system; use sla_cg_adjoint_batched")
+    gb, gv, infos = _adjoint_call(_lib.sla_cg_adjoint, A, x, grad_x, tol, maxit, want_vals,
+                                  FLAG_HISTORY if history else 0, 1, stream, check)
+    return gb, gv, infos[0]
+
+
+def sla_cg_adjoint_batched(A: CSRPattern, values: torch.Tensor, x: torch.Tensor,
+                           grad_x: torch.Tensor, tol: float, maxit: int,
+                           want_vals: bool = True, stream=None, check: bool = True):
+    batch = A.bind(values)
+    return _adjoint_call(_lib.sla_cg_adjoint_batched, A, x, grad_x, tol, maxit, want_vals, 0,
+                         batch, stream, check)
+
+
+def sla_pattern_grad(A: CSRPattern, values_shape_ref: torch.Tensor, lam: torch.Tensor,
+                     x: torch.Tensor, stream=None) -> torch.Tensor:
+    """grad_vals = -lambda_i x_j on every stored slot (batch from the values)."""
+    batch = A.bind(values_shape_ref)
+    _shape(lam, _vec_shape(A, batch, lam), "lambda")
+    _shape(x, _vec_shape(A, batch, lam), "x")
+    out = torch.empty((batch, A.nnz) if lam.dim() == 2 else (A.nnz,), dtype=torch.float64,
+                      device=lam.device)
+    _check(_lib.sla_pattern_grad(A.handle, _dev(lam, torch.float64, "lambda"),
+                                 _dev(x, torch.float64, "x"), out.data_ptr(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Autograd: one graph node per solve, saved state (values, x) = O(n + nnz)
+# ---------------------------------------------------------------------------
+class _CGSolve(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, values, b, pattern, tol, maxit):
+        batched = b.dim() == 2
+        if batched:
+            x, infos = sla_cg_solve_batched(pattern, values, b.contiguous(), tol, maxit)
+        else:
+            x, info = sla_cg_solve(pattern, values, b.contiguous(), tol, maxit)
+            infos = [info]
+        ctx.pattern, ctx.tol, ctx.maxit, ctx.batched = pattern, tol, maxit, batched
+        ctx.infos = infos
+        ctx.save_for_backward(values, x)
+        return x
+
+    @staticmethod
+    def backward(ctx, grad_x):
+        values, x = ctx.saved_tensors
+        want_vals = ctx.needs_input_grad[0]
+        g = grad_x.contiguous()
+        if ctx.batched:
+            gb, gv, _ = sla_cg_adjoint_batched(ctx.pattern, values, x, g, ctx.tol, ctx.maxit,
+                                               want_vals)
+        else:
+            gb, gv, _ = sla_cg_adjoint(ctx.pattern, values, x, g, ctx.tol, ctx.maxit, want_vals)
+        return gv, gb, None, None, None
+
+
+class SparseTensor:
+    """A sparse matrix (or a batch sharing one pattern) with .solve / .matvec.
+
+    ``values`` is a float64 CUDA tensor [nnz] or [batch, nnz] in CSR slot
+    order; it may require grad.  ``pattern`` is a CSRPattern.
+    """
+
+    def __init__(self, pattern: CSRPattern, values: torch.Tensor):
+        if values.shape[-1] != pattern.nnz:
+            raise ValueError("values do not match the pattern")
+        self.pattern = pattern
+        self.values = values
+
+    @property
+    def shape(self):
+        return (self.pattern.n, self.pattern.n)
+
+    def solve(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000) -> torch.Tensor:
+        return _CGSolve.apply(self.values, b, self.pattern, float(tol), int(maxit))
+
+    def matvec(self, x: torch.Tensor) -> torch.Tensor:
+        """y = A x (forward only; its own backward is not built)."""
+        return sla_spmv(self.pattern, self.values.detach().contiguous(), x.contiguous())
+
+
+def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000):
+    """x = A^{-1} b with the adjoint backward pass."""
+    return A.solve(b, tol, maxit)

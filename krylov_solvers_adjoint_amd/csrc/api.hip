@@ -1,0 +1,383 @@
+// C ABI of the library (declared in include/sla.h).  Every entry point checks
+// its arguments before launching anything, converts every failure into an
+// sla_status, and never lets a C++ exception escape.
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+
+#include "handle.h"
+
+namespace sla {
+
+static thread_local char g_err[1024] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+void clear_error() { g_err[0] = '\0'; }
+
+sla_status dev_alloc(void** p, size_t bytes, const char* what) {
+  *p = nullptr;
+  hipError_t e = hipMalloc(p, bytes == 0 ? 1 : bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    set_error("out of device memory allocating %zu bytes for %s", bytes, what);
+    return SLA_ERR_OOM;
+  }
+  return SLA_OK;
+}
+
+void dev_free(void* p) {
+  if (p) (void)hipFree(p);
+}
+
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+}  // namespace sla
+
+using namespace sla;
+
+#define API_BEGIN try {
+#define API_END                                                                \
+  }                                                                            \
+  catch (const std::bad_alloc&) {                                              \
+    set_error("host out of memory");                                           \
+    return SLA_ERR_OOM;                                                        \
+  }                                                                            \
+  catch (...) {                                                                \
+    set_error("internal error");                                               \
+    return SLA_ERR_DEVICE;                                                     \
+  }
+
+#define REQUIRE(cond, ...)                                                     \
+  do {                                                                         \
+    if (!(cond)) {                                                             \
+      set_error(__VA_ARGS__);                                                  \
+      return SLA_ERR_ARG;                                                      \
+    }                                                                          \
+  } while (0)
+
+static bool valid_index(sla_index v) { return v == SLA_I32 || v == SLA_I64; }
+
+static void destroy_handle(sla_csr A) {
+  if (!A) return;
+  release_workspace(A);
+  dev_free(A->rowptr);
+  dev_free(A->col);
+  dev_free(A->perm);
+  dev_free(A->sorted_idx);
+  dev_free(A->grp);
+  delete A;
+}
+
+extern "C" {
+
+const char* sla_last_error(void) { return g_err; }
+
+const char* sla_status_string(sla_status s) {
+  switch (s) {
+    case SLA_OK: return "SLA_OK";
+    case SLA_ERR_ARG: return "SLA_ERR_ARG";
+    case SLA_ERR_CSR: return "SLA_ERR_CSR";
+    case SLA_ERR_OOM: return "SLA_ERR_OOM";
+    case SLA_ERR_DEVICE: return "SLA_ERR_DEVICE";
+    case SLA_ERR_NOT_SPD: return "SLA_ERR_NOT_SPD";
+    case SLA_ERR_NONFINITE: return "SLA_ERR_NONFINITE";
+  }
+  return "SLA_UNKNOWN";
+}
+
+sla_status sla_csr_create(int64_t n, int64_t nnz_coo, sla_index coo_idx, const void* coo_row,
+                          const void* coo_col, sla_index rowptr_idx, hipStream_t stream,
+                          sla_csr* out) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(out != nullptr, "sla_csr_create: out is NULL");
+  REQUIRE(n >= 1 && n < (int64_t(1) << 31) - 1, "sla_csr_create: n=%lld out of range",
+          (long long)n);
+  REQUIRE(nnz_coo >= 0 && nnz_coo < (int64_t(1) << 32),
+          "sla_csr_create: nnz_coo=%lld out of range", (long long)nnz_coo);
+  REQUIRE(valid_index(coo_idx) && valid_index(rowptr_idx), "sla_csr_create: bad index width");
+  REQUIRE(nnz_coo == 0 || (coo_row != nullptr && coo_col != nullptr),
+          "sla_csr_create: NULL coordinates");
+  sla_csr A = new sla_csr_s();
+  (void)hipGetDevice(&A->device);
+  A->n = n;
+  A->nnz_coo = nnz_coo;
+  A->rp_idx = rowptr_idx;
+  sla_status s = build_from_coo(A, coo_idx, coo_row, coo_col, stream);
+  if (s == SLA_OK) s = analyse_pattern(A, stream);
+  if (s != SLA_OK) {
+    destroy_handle(A);
+    return s;
+  }
+  *out = A;
+  return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_create_from_csr(int64_t n, int64_t nnz, sla_index rowptr_idx,
+                                   const void* rowptr, const int32_t* col, hipStream_t stream,
+                                   sla_csr* out) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(out != nullptr, "sla_csr_create_from_csr: out is NULL");
+  REQUIRE(n >= 1 && n < (int64_t(1) << 31) - 1, "sla_csr_create_from_csr: n out of range");
+  REQUIRE(valid_index(rowptr_idx), "sla_csr_create_from_csr: bad index width");
+  REQUIRE(nnz >= 0 && (rowptr_idx == SLA_I64 || nnz < (int64_t(1) << 31)),
+          "sla_csr_create_from_csr: nnz=%lld does not fit the row pointer", (long long)nnz);
+  REQUIRE(rowptr != nullptr && (nnz == 0 || col != nullptr),
+          "sla_csr_create_from_csr: NULL array");
+  sla_csr A = new sla_csr_s();
+  (void)hipGetDevice(&A->device);
+  A->n = n;
+  A->nnz = nnz;
+  A->rp_idx = rowptr_idx;
+  sla_status s = build_from_csr(A, rowptr, col, stream);
+  if (s == SLA_OK) s = analyse_pattern(A, stream);
+  if (s != SLA_OK) {
+    destroy_handle(A);
+    return s;
+  }
+  *out = A;
+  return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_destroy(sla_csr A) {
+  API_BEGIN
+  if (A) {
+    (void)hipDeviceSynchronize();
+    destroy_handle(A);
+  }
+  return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_get_info(sla_csr A, int64_t* n, int64_t* nnz, int64_t* nnz_coo,
+                            sla_index* rowptr_idx) {
+  REQUIRE(A != nullptr, "sla_csr_get_info: NULL handle");
+  if (n) *n = A->n;
+  if (nnz) *nnz = A->nnz;
+  if (nnz_coo) *nnz_coo = A->nnz_coo;
+  if (rowptr_idx) *rowptr_idx = A->rp_idx;
+  return SLA_OK;
+}
+
+sla_status sla_csr_pattern(sla_csr A, const void** rowptr, const int32_t** col,
+                           const int64_t** perm) {
+  REQUIRE(A != nullptr, "sla_csr_pattern: NULL handle");
+  if (rowptr) *rowptr = A->rowptr;
+  if (col) *col = A->col;
+  if (perm) *perm = A->perm;
+  return SLA_OK;
+}
+
+sla_status sla_csr_copy_pattern(sla_csr A, void* rowptr_out, int32_t* col_out,
+                                int64_t* perm_out, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_copy_pattern: NULL handle");
+  REQUIRE(perm_out == nullptr || A->perm != nullptr,
+          "sla_csr_copy_pattern: handle was not built from COO (no perm)");
+  if (rowptr_out)
+    SLA_TRY_HIP(hipMemcpyAsync(rowptr_out, A->rowptr, size_t(A->n + 1) * A->rp_idx,
+                               hipMemcpyDeviceToDevice, stream));
+  if (col_out && A->nnz > 0)
+    SLA_TRY_HIP(hipMemcpyAsync(col_out, A->col, sizeof(int32_t) * A->nnz,
+                               hipMemcpyDeviceToDevice, stream));
+  if (perm_out && A->nnz_coo > 0)
+    SLA_TRY_HIP(hipMemcpyAsync(perm_out, A->perm, sizeof(int64_t) * A->nnz_coo,
+                               hipMemcpyDeviceToDevice, stream));
+  return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_values_from_coo(sla_csr A, const double* coo_val, double* vals,
+                                   int64_t batch, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_values_from_coo: NULL handle");
+  REQUIRE(A->perm != nullptr, "sla_csr_values_from_coo: handle was not built from COO");
+  REQUIRE(batch >= 1 && batch <= 65535, "sla_csr_values_from_coo: batch out of range");
+  REQUIRE(A->nnz == 0 || (coo_val != nullptr && vals != nullptr),
+          "sla_csr_values_from_coo: NULL array");
+  return launch_values_from_coo(A, coo_val, vals, batch, stream);
+  API_END
+}
+
+sla_status sla_csr_grad_to_coo(sla_csr A, const double* grad_vals, double* grad_coo,
+                               int64_t batch, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_grad_to_coo: NULL handle");
+  REQUIRE(A->perm != nullptr, "sla_csr_grad_to_coo: handle was not built from COO");
+  REQUIRE(batch >= 1 && batch <= 65535, "sla_csr_grad_to_coo: batch out of range");
+  REQUIRE(A->nnz_coo == 0 || (grad_vals != nullptr && grad_coo != nullptr),
+          "sla_csr_grad_to_coo: NULL array");
+  return launch_grad_to_coo(A, grad_vals, grad_coo, batch, stream);
+  API_END
+}
+
+sla_status sla_csr_set_values(sla_csr A, const double* vals, int64_t batch) {
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_set_values: NULL handle");
+  REQUIRE(batch >= 1 && batch <= 65535, "sla_csr_set_values: batch out of range");
+  REQUIRE(A->nnz == 0 || vals != nullptr, "sla_csr_set_values: NULL values");
+  A->vals = vals;
+  A->batch = batch;
+  return SLA_OK;
+}
+
+sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_spmv: NULL handle");
+  REQUIRE(A->batch >= 1, "sla_spmv: no values bound (sla_csr_set_values)");
+  REQUIRE(x != nullptr && y != nullptr, "sla_spmv: NULL vector");
+  return launch_spmv(A, A->vals, A->batch, x, y, stream);
+  API_END
+}
+
+static sla_status check_solve(sla_csr A, const void* b, const void* x, double tol,
+                              int64_t maxit, uint32_t flags, const char* who) {
+  REQUIRE(A != nullptr, "%s: NULL handle", who);
+  REQUIRE(A->batch >= 1, "%s: no values bound (sla_csr_set_values)", who);
+  REQUIRE(b != nullptr && x != nullptr, "%s: NULL vector", who);
+  REQUIRE(std::isfinite(tol) && tol >= 0.0, "%s: tol must be finite and >= 0", who);
+  REQUIRE(maxit >= 0, "%s: maxit must be >= 0", who);
+  REQUIRE((flags & ~uint32_t(SLA_FLAG_X0 | SLA_FLAG_HISTORY)) == 0, "%s: unknown flags", who);
+  return SLA_OK;
+}
+
+sla_status sla_cg_solve_batched(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                                uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_solve(A, b, x, tol, maxit, flags, "sla_cg_solve_batched"));
+  return run_cg(A, b, x, tol, maxit, flags, info, stream);
+  API_END
+}
+
+sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                        uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_solve(A, b, x, tol, maxit, flags, "sla_cg_solve"));
+  REQUIRE(A->batch == 1, "sla_cg_solve: %lld systems bound; use sla_cg_solve_batched",
+          (long long)A->batch);
+  return run_cg(A, b, x, tol, maxit, flags, info, stream);
+  API_END
+}
+
+sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad_x,
+                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_solve(A, grad_x, grad_b, tol, maxit, flags, "sla_cg_adjoint"));
+  REQUIRE((flags & SLA_FLAG_X0) == 0, "sla_cg_adjoint: SLA_FLAG_X0 is not supported");
+  REQUIRE(grad_vals == nullptr || x != nullptr, "sla_cg_adjoint: grad_vals needs x");
+  // A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix)
+  sla_status s = run_cg(A, grad_x, grad_b, tol, maxit, flags, info, stream);
+  if (grad_vals != nullptr && (s == SLA_OK || s == SLA_ERR_NOT_SPD || s == SLA_ERR_NONFINITE)) {
+    sla_status g = launch_pattern_grad(A, A->batch, grad_b, x, grad_vals, stream);
+    if (g != SLA_OK) return g;
+    if (hipStreamSynchronize(stream) != hipSuccess) {
+      set_error("sla_cg_adjoint: synchronisation failed");
+      return SLA_ERR_DEVICE;
+    }
+  }
+  return s;
+  API_END
+}
+
+sla_status sla_cg_adjoint(sla_csr A, const double* x, const double* grad_x, double* grad_b,
+                          double* grad_vals, double tol, int64_t maxit, uint32_t flags,
+                          sla_cg_info* info, hipStream_t stream) {
+  REQUIRE(A != nullptr, "sla_cg_adjoint: NULL handle");
+  REQUIRE(A->batch == 1, "sla_cg_adjoint: %lld systems bound; use sla_cg_adjoint_batched",
+          (long long)A->batch);
+  return sla_cg_adjoint_batched(A, x, grad_x, grad_b, grad_vals, tol, maxit, flags, info,
+                                stream);
+}
+
+sla_status sla_pattern_grad(sla_csr A, const double* lambda, const double* x, double* grad_vals,
+                            hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_pattern_grad: NULL handle");
+  REQUIRE(A->batch >= 1, "sla_pattern_grad: no batch bound (sla_csr_set_values)");
+  REQUIRE(lambda != nullptr && x != nullptr && (A->nnz == 0 || grad_vals != nullptr),
+          "sla_pattern_grad: NULL array");
+  return launch_pattern_grad(A, A->batch, lambda, x, grad_vals, stream);
+  API_END
+}
+
+sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha, double* beta, double* rr,
+                          int64_t cap, int64_t* count) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_cg_history: NULL handle");
+  REQUIRE(A->hist != nullptr && A->scal_host != nullptr,
+          "sla_cg_history: no solve with SLA_FLAG_HISTORY yet");
+  REQUIRE(system >= 0 && system < A->ws_batch, "sla_cg_history: system out of range");
+  REQUIRE(cap >= 0, "sla_cg_history: cap < 0");
+  const int64_t it = std::min<int64_t>(A->scal_host[system].it, A->hist_cap);
+  const int64_t k = std::min<int64_t>(it, cap);
+  if (count) *count = it;
+  if (k > 0) {
+    double* h = new double[size_t(k) * 3];
+    hipError_t e = hipMemcpy(h, A->hist + size_t(system) * A->hist_cap * 3,
+                             sizeof(double) * 3 * k, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+      delete[] h;
+      set_error("sla_cg_history: copy failed: %s", hipGetErrorString(e));
+      return SLA_ERR_DEVICE;
+    }
+    for (int64_t j = 0; j < k; ++j) {
+      if (alpha) alpha[j] = h[3 * j];
+      if (beta) beta[j] = h[3 * j + 1];
+      if (rr) rr[j] = h[3 * j + 2];
+    }
+    delete[] h;
+  }
+  return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_set_graph_block: NULL handle");
+  REQUIRE(iterations >= 0 && iterations <= 4096, "sla_csr_set_graph_block: out of range");
+  if (iterations != A->graph_block) {
+    (void)hipDeviceSynchronize();
+    release_workspace(A);  // drops the captured graphs with the workspace
+    A->graph_block = iterations;
+  }
+  return SLA_OK;
+  API_END
+}
+
+}  // extern "C"

@@ -1,0 +1,596 @@
+// Sparsity-pattern construction: COO -> CSR, CSR validation, value mapping.
+//
+// The pattern is the one a SparseTensor shares across a batch (torch-sla
+// explainer, technical summary, Methodology 1).  The result of the COO path
+// is unique: triplets ordered by (row, col), ties by input position, equal
+// (row, col) merged into one slot.  Integer atomics decide only where a
+// triplet lands before its row is sorted, and every row is then sorted by the
+// total order (col, input position), so the output is bit-identical on every
+// run whatever order the atomics took.
+#include <algorithm>
+#include <vector>
+
+#include "handle.h"
+
+namespace sla {
+namespace {
+
+constexpr int kScanItems = 16;
+constexpr int64_t kScanTile = int64_t(kBlock) * kScanItems;  // 4096
+constexpr int kSmallRow = 32;    // rows up to this length: one thread sorts
+constexpr int kMidRow = 4096;    // up to this: one workgroup sorts in LDS
+
+inline unsigned grid_for(int64_t work, int64_t per_block = kBlock) {
+  int64_t g = (work + per_block - 1) / per_block;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20));
+}
+
+// ---------------------------------------------------------------------------
+// Exclusive scan of non-negative integers into int64 (out has L+1 entries)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* lds) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int64_t t = lds[0] + lds[1] + lds[2] + lds[3];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ int64_t block_exclusive_i64(int64_t v, int64_t* lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  int64_t inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int64_t o = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += o;
+  }
+  if (lane == kWave - 1) lds[w] = inc;
+  __syncthreads();
+  int64_t before = 0;
+  for (int j = 0; j < w; ++j) before += lds[j];
+  __syncthreads();
+  return before + inc - v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_scan_reduce(const T* __restrict__ in, int64_t L,
+                                                        int64_t* __restrict__ bsum) {
+  __shared__ int64_t lds[4];
+  const int64_t base = int64_t(blockIdx.x) * kScanTile;
+  int64_t s = 0;
+  for (int j = 0; j < kScanItems; ++j) {
+    const int64_t i = base + int64_t(j) * kBlock + threadIdx.x;
+    if (i < L) s += int64_t(in[i]);
+  }
+  s = block_sum_i64(s, lds);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_scan_down(const T* __restrict__ in, int64_t L,
+                                                      const int64_t* __restrict__ boff,
+                                                      int64_t* __restrict__ out) {
+  __shared__ int64_t lds[4];
+  const int64_t base = int64_t(blockIdx.x) * kScanTile + int64_t(threadIdx.x) * kScanItems;
+  int64_t v[kScanItems];
+  int64_t tsum = 0;
+#pragma unroll
+  for (int j = 0; j < kScanItems; ++j) {
+    const int64_t i = base + j;
+    v[j] = i < L ? int64_t(in[i]) : 0;
+    tsum += v[j];
+  }
+  int64_t run = boff[blockIdx.x] + block_exclusive_i64(tsum, lds);
+#pragma unroll
+  for (int j = 0; j < kScanItems; ++j) {
+    const int64_t i = base + j;
+    if (i < L) out[i] = run;
+    run += v[j];
+    if (i == L - 1) out[L] = run;
+  }
+}
+
+__global__ void k_set_i64(int64_t* p, int64_t v) { *p = v; }
+
+template <typename T>
+sla_status exclusive_scan(const T* in, int64_t L, int64_t* out, hipStream_t st) {
+  if (L == 0) {
+    k_set_i64<<<1, 1, 0, st>>>(out, 0);
+    SLA_TRY_HIP(hipGetLastError());
+    return SLA_OK;
+  }
+  const int64_t nb = (L + kScanTile - 1) / kScanTile;
+  int64_t* bsum = nullptr;
+  int64_t* boff = nullptr;
+  SLA_TRY(dev_alloc(&bsum, nb, "scan block sums"));
+  sla_status s = dev_alloc(&boff, nb + 1, "scan block offsets");
+  if (s == SLA_OK) {
+    k_scan_reduce<T><<<(unsigned)nb, kBlock, 0, st>>>(in, L, bsum);
+    s = hipGetLastError() == hipSuccess ? SLA_OK : SLA_ERR_DEVICE;
+    if (s != SLA_OK) set_error("scan launch failed");
+  }
+  if (s == SLA_OK) {
+    if (nb == 1) {
+      // one tile: its offset is 0 (recursing would scan a 1-element array
+      // that is again one tile, forever)
+      k_set_i64<<<1, 1, 0, st>>>(boff, 0);
+      if (hipGetLastError() != hipSuccess) {
+        set_error("scan launch failed");
+        s = SLA_ERR_DEVICE;
+      }
+    } else {
+      s = exclusive_scan<int64_t>(bsum, nb, boff, st);
+    }
+  }
+  if (s == SLA_OK) {
+    k_scan_down<T><<<(unsigned)nb, kBlock, 0, st>>>(in, L, boff, out);
+    if (hipGetLastError() != hipSuccess) {
+      set_error("scan launch failed");
+      s = SLA_ERR_DEVICE;
+    }
+  }
+  (void)hipStreamSynchronize(st);
+  dev_free(bsum);
+  dev_free(boff);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// COO -> CSR kernels
+// ---------------------------------------------------------------------------
+template <typename CI>
+__global__ void k_coo_count(int64_t m, int64_t n, const CI* __restrict__ row,
+                            const CI* __restrict__ col, uint32_t* __restrict__ cnt,
+                            int* __restrict__ err) {
+  for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < m;
+       k += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = row[k];
+    const int64_t c = col[k];
+    if (r < 0 || r >= n || c < 0 || c >= n) {
+      atomicOr(err, 1);
+      continue;
+    }
+    atomicAdd(&cnt[r], 1u);
+  }
+}
+
+template <typename CI>
+__global__ void k_coo_scatter(int64_t m, const CI* __restrict__ row, const CI* __restrict__ col,
+                              const int64_t* __restrict__ start, uint32_t* __restrict__ fill,
+                              uint64_t* __restrict__ key, int32_t* __restrict__ rowid) {
+  for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < m;
+       k += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = row[k];
+    const int64_t pos = start[r] + atomicAdd(&fill[r], 1u);
+    key[pos] = (uint64_t(uint32_t(col[k])) << 32) | uint64_t(uint32_t(k));
+    rowid[pos] = int32_t(r);
+  }
+}
+
+// Rows of up to kSmallRow triplets are insertion-sorted by one thread; longer
+// rows are listed for the workgroup / global sorts.
+__global__ void k_sort_rows_small(int64_t n, const int64_t* __restrict__ start,
+                                  uint64_t* __restrict__ key, int32_t* __restrict__ mid_list,
+                                  int* __restrict__ n_mid, int32_t* __restrict__ long_list,
+                                  int* __restrict__ n_long) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t a = start[i];
+    const int64_t len = start[i + 1] - a;
+    if (len <= 1) continue;
+    if (len <= kSmallRow) {
+      uint64_t v[kSmallRow];
+      for (int j = 0; j < len; ++j) v[j] = key[a + j];
+      for (int j = 1; j < len; ++j) {
+        const uint64_t x = v[j];
+        int t = j - 1;
+        while (t >= 0 && v[t] > x) {
+          v[t + 1] = v[t];
+          --t;
+        }
+        v[t + 1] = x;
+      }
+      for (int j = 0; j < len; ++j) key[a + j] = v[j];
+    } else if (len <= kMidRow) {
+      mid_list[atomicAdd(n_mid, 1)] = int32_t(i);
+    } else {
+      long_list[atomicAdd(n_long, 1)] = int32_t(i);
+    }
+  }
+}
+
+__device__ __forceinline__ int64_t next_pow2(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// One workgroup per listed row: bitonic sort in LDS, padded with keys above
+// every real key (real keys have a column < 2^31 in the high word).
+__global__ __launch_bounds__(kBlock) void k_sort_rows_mid(const int32_t* __restrict__ list,
+                                                          const int64_t* __restrict__ start,
+                                                          uint64_t* __restrict__ key) {
+  __shared__ uint64_t s[kMidRow];
+  const int64_t row = list[blockIdx.x];
+  const int64_t a = start[row];
+  const int64_t len = start[row + 1] - a;
+  const int64_t P = next_pow2(len);
+  for (int64_t i = threadIdx.x; i < P; i += kBlock) s[i] = i < len ? key[a + i] : ~uint64_t(0);
+  __syncthreads();
+  for (int64_t k = 2; k <= P; k <<= 1) {
+    for (int64_t j = k >> 1; j > 0; j >>= 1) {
+      for (int64_t i = threadIdx.x; i < P; i += kBlock) {
+        const int64_t ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = (i & k) == 0;
+          const uint64_t x = s[i], y = s[ixj];
+          if ((x > y) == up) {
+            s[i] = y;
+            s[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int64_t i = threadIdx.x; i < len; i += kBlock) key[a + i] = s[i];
+}
+
+// Rows longer than kMidRow: bitonic network over a padded copy in memory.
+__global__ void k_long_fill(const uint64_t* __restrict__ key, int64_t a, int64_t len,
+                            uint64_t* __restrict__ tmp, int64_t P) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < P;
+       i += int64_t(gridDim.x) * blockDim.x)
+    tmp[i] = i < len ? key[a + i] : ~uint64_t(0);
+}
+__global__ void k_long_step(uint64_t* __restrict__ tmp, int64_t P, int64_t j, int64_t k) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < P;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t ixj = i ^ j;
+    if (ixj > i) {
+      const bool up = (i & k) == 0;
+      const uint64_t x = tmp[i], y = tmp[ixj];
+      if ((x > y) == up) {
+        tmp[i] = y;
+        tmp[ixj] = x;
+      }
+    }
+  }
+}
+__global__ void k_long_back(uint64_t* __restrict__ key, int64_t a, int64_t len,
+                            const uint64_t* __restrict__ tmp) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < len;
+       i += int64_t(gridDim.x) * blockDim.x)
+    key[a + i] = tmp[i];
+}
+
+__global__ void k_heads(int64_t m, const uint64_t* __restrict__ key,
+                        const int32_t* __restrict__ rowid, uint8_t* __restrict__ head) {
+  for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < m;
+       s += int64_t(gridDim.x) * blockDim.x) {
+    head[s] = (s == 0 || rowid[s] != rowid[s - 1] || (key[s] >> 32) != (key[s - 1] >> 32))
+                  ? 1 : 0;
+  }
+}
+
+__global__ void k_coo_emit(int64_t m, const uint64_t* __restrict__ key,
+                           const uint8_t* __restrict__ head, const int64_t* __restrict__ hscan,
+                           int32_t* __restrict__ col_out, int64_t* __restrict__ perm,
+                           uint32_t* __restrict__ sorted_idx, int64_t* __restrict__ grp) {
+  for (int64_t s = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; s < m;
+       s += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t slot = hscan[s] + head[s] - 1;
+    const uint64_t kv = key[s];
+    const uint32_t k = uint32_t(kv);
+    if (head[s]) {
+      col_out[slot] = int32_t(kv >> 32);
+      grp[slot] = s;
+    }
+    perm[k] = slot;
+    sorted_idx[s] = k;
+  }
+}
+
+template <typename RP>
+__global__ void k_coo_rowptr(int64_t n, const int64_t* __restrict__ start,
+                             const int64_t* __restrict__ hscan, RP* __restrict__ rowptr) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i <= n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    rowptr[i] = RP(hscan[start[i]]);
+}
+
+// vals[s][slot] = first COO value of the slot, then + the others in input order
+__global__ void k_values_from_coo(int64_t nnz, int64_t m, const int64_t* __restrict__ grp,
+                                  const uint32_t* __restrict__ sidx,
+                                  const double* __restrict__ coo_val, double* __restrict__ vals) {
+  const double* cv = coo_val + int64_t(blockIdx.y) * m;
+  double* out = vals + int64_t(blockIdx.y) * nnz;
+  for (int64_t slot = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; slot < nnz;
+       slot += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t g0 = grp[slot], g1 = grp[slot + 1];
+    double v = cv[sidx[g0]];
+    for (int64_t g = g0 + 1; g < g1; ++g) v = v + cv[sidx[g]];
+    out[slot] = v;
+  }
+}
+
+__global__ void k_grad_to_coo(int64_t m, int64_t nnz, const int64_t* __restrict__ perm,
+                              const double* __restrict__ gv, double* __restrict__ gc) {
+  const double* g = gv + int64_t(blockIdx.y) * nnz;
+  double* o = gc + int64_t(blockIdx.y) * m;
+  for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < m;
+       k += int64_t(gridDim.x) * blockDim.x)
+    o[k] = g[perm[k]];
+}
+
+// Every row pointer and column is range-checked before it is used as an
+// index, so malformed input becomes an error code, never a stray access.
+template <typename RP>
+__global__ void k_validate_csr(int64_t n, int64_t nnz, const RP* __restrict__ rowptr,
+                               const int32_t* __restrict__ col, int* __restrict__ err) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t a = rowptr[i], e = rowptr[i + 1];
+    if (i == 0 && a != 0) atomicOr(err, 1);
+    if (i == n - 1 && e != nnz) atomicOr(err, 2);
+    if (a < 0 || e > nnz || e < a) {
+      atomicOr(err, 4);
+      continue;
+    }
+    int64_t prev = -1;
+    for (int64_t k = a; k < e; ++k) {
+      const int64_t c = col[k];
+      if (c < 0 || c >= n) atomicOr(err, 8);
+      else if (c <= prev) atomicOr(err, 16);
+      prev = c;
+    }
+  }
+}
+
+template <typename RP>
+__global__ void k_tile_nnz_max(int64_t n, int64_t tiles, const RP* __restrict__ rowptr,
+                               unsigned long long* __restrict__ out) {
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < tiles;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t lo = t * kTileRows;
+    const int64_t hi = lo + kTileRows < n ? lo + kTileRows : n;
+    atomicMax(out, (unsigned long long)(int64_t(rowptr[hi]) - int64_t(rowptr[lo])));
+  }
+}
+
+#define LAUNCH_CHECK()                                                         \
+  do {                                                                         \
+    hipError_t e_ = hipGetLastError();                                         \
+    if (e_ != hipSuccess) {                                                    \
+      set_error("kernel launch failed: %s (%s:%d)", hipGetErrorString(e_),     \
+                __FILE__, __LINE__);                                           \
+      return SLA_ERR_DEVICE;                                                   \
+    }                                                                          \
+  } while (0)
+
+// RAII list of temporary device buffers for the build.
+struct Temps {
+  std::vector<void*> ptrs;
+  ~Temps() {
+    for (void* p : ptrs) dev_free(p);
+  }
+  template <typename T>
+  sla_status get(T** p, size_t count, const char* what) {
+    SLA_TRY(dev_alloc(p, count == 0 ? 1 : count, what));
+    ptrs.push_back(*p);
+    return SLA_OK;
+  }
+};
+
+template <typename CI>
+sla_status coo_build(sla_csr A, const CI* row, const CI* col, hipStream_t st) {
+  const int64_t n = A->n, m = A->nnz_coo;
+  Temps T;
+  uint32_t* cnt;
+  uint32_t* fill;
+  int64_t* start;
+  int* flags;  // [0] range error, [1] mid rows, [2] long rows
+  SLA_TRY(T.get(&cnt, n, "row counts"));
+  SLA_TRY(T.get(&fill, n, "row fill"));
+  SLA_TRY(T.get(&start, n + 1, "row starts"));
+  SLA_TRY(T.get(&flags, 4, "flags"));
+  SLA_TRY_HIP(hipMemsetAsync(cnt, 0, sizeof(uint32_t) * n, st));
+  SLA_TRY_HIP(hipMemsetAsync(fill, 0, sizeof(uint32_t) * n, st));
+  SLA_TRY_HIP(hipMemsetAsync(flags, 0, sizeof(int) * 4, st));
+
+  if (m > 0) {
+    k_coo_count<CI><<<grid_for(m), kBlock, 0, st>>>(m, n, row, col, cnt, flags);
+    LAUNCH_CHECK();
+  }
+  int hflags[4] = {0, 0, 0, 0};
+  SLA_TRY_HIP(hipMemcpyAsync(hflags, flags, sizeof(hflags), hipMemcpyDeviceToHost, st));
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  if (hflags[0]) {
+    set_error("sla_csr_create: a COO row or column index is outside [0, n)");
+    return SLA_ERR_CSR;
+  }
+  SLA_TRY(exclusive_scan<uint32_t>(cnt, n, start, st));
+
+  uint64_t* key;
+  int32_t* rowid;
+  uint8_t* head;
+  int64_t* hscan;
+  int32_t* mid_list;
+  int32_t* long_list;
+  SLA_TRY(T.get(&key, m, "sort keys"));
+  SLA_TRY(T.get(&rowid, m, "row ids"));
+  SLA_TRY(T.get(&head, m, "head flags"));
+  SLA_TRY(T.get(&hscan, m + 1, "head scan"));
+  SLA_TRY(T.get(&mid_list, n, "mid rows"));
+  SLA_TRY(T.get(&long_list, n, "long rows"));
+
+  if (m > 0) {
+    k_coo_scatter<CI><<<grid_for(m), kBlock, 0, st>>>(m, row, col, start, fill, key, rowid);
+    LAUNCH_CHECK();
+    k_sort_rows_small<<<grid_for(n), kBlock, 0, st>>>(n, start, key, mid_list, flags + 1,
+                                                       long_list, flags + 2);
+    LAUNCH_CHECK();
+    SLA_TRY_HIP(hipMemcpyAsync(hflags, flags, sizeof(hflags), hipMemcpyDeviceToHost, st));
+    SLA_TRY_HIP(hipStreamSynchronize(st));
+    if (hflags[1] > 0) {
+      k_sort_rows_mid<<<(unsigned)hflags[1], kBlock, 0, st>>>(mid_list, start, key);
+      LAUNCH_CHECK();
+    }
+    if (hflags[2] > 0) {
+      std::vector<int32_t> longs(hflags[2]);
+      std::vector<int64_t> hstart(n + 1);
+      SLA_TRY_HIP(hipMemcpyAsync(longs.data(), long_list, sizeof(int32_t) * longs.size(),
+                                 hipMemcpyDeviceToHost, st));
+      SLA_TRY_HIP(hipMemcpyAsync(hstart.data(), start, sizeof(int64_t) * (n + 1),
+                                 hipMemcpyDeviceToHost, st));
+      SLA_TRY_HIP(hipStreamSynchronize(st));
+      int64_t maxlen = 0;
+      for (int32_t r : longs) maxlen = std::max(maxlen, hstart[r + 1] - hstart[r]);
+      int64_t P = 1;
+      while (P < maxlen) P <<= 1;
+      uint64_t* tmp;
+      SLA_TRY(T.get(&tmp, P, "long row sort"));
+      for (int32_t r : longs) {
+        const int64_t a = hstart[r], len = hstart[r + 1] - a;
+        int64_t Pr = 1;
+        while (Pr < len) Pr <<= 1;
+        k_long_fill<<<grid_for(Pr), kBlock, 0, st>>>(key, a, len, tmp, Pr);
+        for (int64_t k = 2; k <= Pr; k <<= 1)
+          for (int64_t j = k >> 1; j > 0; j >>= 1)
+            k_long_step<<<grid_for(Pr), kBlock, 0, st>>>(tmp, Pr, j, k);
+        k_long_back<<<grid_for(len), kBlock, 0, st>>>(key, a, len, tmp);
+        LAUNCH_CHECK();
+      }
+    }
+    k_heads<<<grid_for(m), kBlock, 0, st>>>(m, key, rowid, head);
+    LAUNCH_CHECK();
+  }
+  SLA_TRY(exclusive_scan<uint8_t>(head, m, hscan, st));
+  int64_t nnz = 0;
+  SLA_TRY_HIP(hipMemcpyAsync(&nnz, hscan + m, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  if (A->rp_idx == SLA_I32 && nnz >= (int64_t(1) << 31)) {
+    set_error("sla_csr_create: %lld slots do not fit int32 row pointers", (long long)nnz);
+    return SLA_ERR_ARG;
+  }
+  A->nnz = nnz;
+  SLA_TRY(dev_alloc(&A->rowptr, size_t(n + 1) * A->rp_idx, "rowptr"));
+  SLA_TRY(dev_alloc(&A->col, nnz == 0 ? 1 : nnz, "col"));
+  SLA_TRY(dev_alloc(&A->perm, m == 0 ? 1 : m, "perm"));
+  SLA_TRY(dev_alloc(&A->sorted_idx, m == 0 ? 1 : m, "sorted index"));
+  SLA_TRY(dev_alloc(&A->grp, nnz + 1, "slot groups"));
+  if (m > 0) {
+    k_coo_emit<<<grid_for(m), kBlock, 0, st>>>(m, key, head, hscan, A->col, A->perm,
+                                                A->sorted_idx, A->grp);
+    LAUNCH_CHECK();
+  }
+  k_set_i64<<<1, 1, 0, st>>>(A->grp + nnz, m);
+  if (A->rp_idx == SLA_I32)
+    k_coo_rowptr<int32_t><<<grid_for(n + 1), kBlock, 0, st>>>(n, start, hscan,
+                                                              (int32_t*)A->rowptr);
+  else
+    k_coo_rowptr<int64_t><<<grid_for(n + 1), kBlock, 0, st>>>(n, start, hscan,
+                                                              (int64_t*)A->rowptr);
+  LAUNCH_CHECK();
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  return SLA_OK;
+}
+
+template <typename RP>
+sla_status tile_stats(sla_csr A, hipStream_t st) {
+  unsigned long long* d = nullptr;
+  SLA_TRY(dev_alloc(&d, 1, "tile stats"));
+  SLA_TRY_HIP(hipMemsetAsync(d, 0, sizeof(*d), st));
+  k_tile_nnz_max<RP><<<grid_for(A->tiles), kBlock, 0, st>>>(A->n, A->tiles,
+                                                            (const RP*)A->rowptr, d);
+  unsigned long long h = 0;
+  hipError_t e = hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  dev_free(d);
+  if (e != hipSuccess) {
+    set_error("pattern analysis failed: %s", hipGetErrorString(e));
+    return SLA_ERR_DEVICE;
+  }
+  A->max_tile_nnz = int64_t(h);
+  return SLA_OK;
+}
+
+}  // namespace
+
+sla_status analyse_pattern(sla_csr A, hipStream_t st) {
+  A->tiles = (A->n + kTileRows - 1) / kTileRows;
+  if (A->rp_idx == SLA_I32) SLA_TRY(tile_stats<int32_t>(A, st));
+  else SLA_TRY(tile_stats<int64_t>(A, st));
+  // stage a tile's slots in LDS when the largest tile fits; tiles above the
+  // cap read their slots straight from memory
+  A->lds_cap = int32_t(std::min<int64_t>(A->max_tile_nnz, kLdsCapNnz));
+  return SLA_OK;
+}
+
+sla_status build_from_coo(sla_csr A, sla_index coo_idx, const void* row, const void* col,
+                          hipStream_t st) {
+  if (coo_idx == SLA_I32)
+    return coo_build<int32_t>(A, (const int32_t*)row, (const int32_t*)col, st);
+  return coo_build<int64_t>(A, (const int64_t*)row, (const int64_t*)col, st);
+}
+
+sla_status build_from_csr(sla_csr A, const void* rowptr, const int32_t* col, hipStream_t st) {
+  const int64_t n = A->n, nnz = A->nnz;
+  SLA_TRY(dev_alloc(&A->rowptr, size_t(n + 1) * A->rp_idx, "rowptr"));
+  SLA_TRY(dev_alloc(&A->col, nnz == 0 ? 1 : nnz, "col"));
+  SLA_TRY_HIP(hipMemcpyAsync(A->rowptr, rowptr, size_t(n + 1) * A->rp_idx,
+                             hipMemcpyDeviceToDevice, st));
+  if (nnz > 0)
+    SLA_TRY_HIP(hipMemcpyAsync(A->col, col, sizeof(int32_t) * nnz, hipMemcpyDeviceToDevice, st));
+  int* err = nullptr;
+  SLA_TRY(dev_alloc(&err, 1, "validation flag"));
+  hipError_t e = hipMemsetAsync(err, 0, sizeof(int), st);
+  if (A->rp_idx == SLA_I32)
+    k_validate_csr<int32_t><<<grid_for(n), kBlock, 0, st>>>(n, nnz, (const int32_t*)A->rowptr,
+                                                            A->col, err);
+  else
+    k_validate_csr<int64_t><<<grid_for(n), kBlock, 0, st>>>(n, nnz, (const int64_t*)A->rowptr,
+                                                            A->col, err);
+  int h = 0;
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, err, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  dev_free(err);
+  if (e != hipSuccess) {
+    set_error("CSR validation failed: %s", hipGetErrorString(e));
+    return SLA_ERR_DEVICE;
+  }
+  if (h) {
+    set_error("sla_csr_create_from_csr: malformed CSR (%s%s%s%s%s)",
+              (h & 1) ? "rowptr[0] != 0; " : "", (h & 2) ? "rowptr[n] != nnz; " : "",
+              (h & 4) ? "row pointers out of order or range; " : "",
+              (h & 8) ? "column out of range; " : "",
+              (h & 16) ? "columns not strictly increasing in a row" : "");
+    return SLA_ERR_CSR;
+  }
+  return SLA_OK;
+}
+
+sla_status launch_values_from_coo(sla_csr A, const double* coo_val, double* vals, int64_t batch,
+                                  hipStream_t st) {
+  if (A->nnz == 0) return SLA_OK;
+  dim3 g(grid_for(A->nnz), (unsigned)batch);
+  k_values_from_coo<<<g, kBlock, 0, st>>>(A->nnz, A->nnz_coo, A->grp, A->sorted_idx, coo_val,
+                                           vals);
+  LAUNCH_CHECK();
+  return SLA_OK;
+}
+
+sla_status launch_grad_to_coo(sla_csr A, const double* grad_vals, double* grad_coo,
+                              int64_t batch, hipStream_t st) {
+  if (A->nnz_coo == 0) return SLA_OK;
+  dim3 g(grid_for(A->nnz_coo), (unsigned)batch);
+  k_grad_to_coo<<<g, kBlock, 0, st>>>(A->nnz_coo, A->nnz, A->perm, grad_vals, grad_coo);
+  LAUNCH_CHECK();
+  return SLA_OK;
+}
+
+}  // namespace sla

@@ -1,0 +1,81 @@
+// The matrix handle: pattern, bound values, and the solver workspace.
+#pragma once
+
+#include <map>
+#include <utility>
+
+#include "common.h"
+
+struct sla_csr_s {
+  int device = 0;
+  int64_t n = 0;
+  int64_t nnz = 0;
+  int64_t nnz_coo = 0;
+  sla_index rp_idx = SLA_I32;
+
+  // pattern (owned)
+  void* rowptr = nullptr;          // [n+1] int32 or int64
+  int32_t* col = nullptr;          // [nnz]
+  int64_t* perm = nullptr;         // [nnz_coo] COO triplet -> slot (COO only)
+  uint32_t* sorted_idx = nullptr;  // [nnz_coo] triplet of each sorted position
+  int64_t* grp = nullptr;          // [nnz+1] first sorted position of each slot
+
+  // pattern analysis
+  int64_t tiles = 0;           // ceil(n / kTileRows)
+  int64_t max_tile_nnz = 0;    // largest number of slots in one tile
+  int32_t lds_cap = 0;         // slots staged per tile (0 = none)
+
+  // bound values (borrowed)
+  const double* vals = nullptr;
+  int64_t batch = 0;
+
+  // workspace, sized for ws_batch systems
+  int64_t ws_batch = 0;
+  int32_t grid = 0;            // iteration workgroups per system
+  double* r = nullptr;
+  double* p0 = nullptr;
+  double* p1 = nullptr;
+  double* q = nullptr;
+  double* part = nullptr;      // 3 * ws_batch * grid
+  sla::Scal* scal = nullptr;   // [ws_batch]
+  int* n_running = nullptr;
+  sla::Ctx* ctx_dev = nullptr;
+  sla::Ctx* ctx_host = nullptr;      // pinned
+  sla::Scal* scal_host = nullptr;    // pinned [ws_batch]
+  int* poll_host = nullptr;          // pinned [2]
+  hipEvent_t poll_ev[2] = {nullptr, nullptr};
+  double* hist = nullptr;
+  int64_t hist_cap = 0;
+  int64_t hist_batch = 0;
+
+  // graphs of `graph_block` iterations, keyed by batch size
+  int64_t graph_block = 32;
+  hipStream_t capture_stream = nullptr;
+  std::map<int64_t, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
+};
+
+namespace sla {
+
+// Workspace and launch helpers implemented in cg.hip
+sla_status ensure_workspace(sla_csr A, int64_t batch);
+void release_workspace(sla_csr A);
+sla_status analyse_pattern(sla_csr A, hipStream_t stream);
+
+sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x,
+                       double* y, hipStream_t stream);
+sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda,
+                               const double* x, double* grad_vals, hipStream_t stream);
+sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                  uint32_t flags, sla_cg_info* info, hipStream_t stream);
+
+// COO / CSR construction implemented in csr_build.hip
+sla_status build_from_coo(sla_csr A, sla_index coo_idx, const void* row,
+                          const void* col, hipStream_t stream);
+sla_status build_from_csr(sla_csr A, const void* rowptr, const int32_t* col,
+                          hipStream_t stream);
+sla_status launch_values_from_coo(sla_csr A, const double* coo_val, double* vals,
+                                  int64_t batch, hipStream_t stream);
+sla_status launch_grad_to_coo(sla_csr A, const double* grad_vals, double* grad_coo,
+                              int64_t batch, hipStream_t stream);
+
+}  // namespace sla
