@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSR CG solve + adjoint on one MI355X.
+
+One step is the whole hot path on the 1000 x 1000 Poisson workload
+(n = 1e6, nnz = 4,996,000, int32 CSR, fp64): b = A u* with
+u* = sin(pi x) sin(pi y), a forward CG solve of exactly 1000 iterations
+(tol 0), then the adjoint solve of exactly 1000 iterations for
+grad_x ~ N(0,1) (seed 1) and the pattern gradient -lambda_i x_j.  Inputs are
+resident in HBM before timing starts.
+
+Printed: ONE JSON line.  ``value`` is CG iterations per second over the
+timed steps (forward + adjoint).  Extra fields: effective bandwidth on the
+canonical bytes of one iteration (12 nnz + 4 (n+1) + 88 n), the roofline of
+the dominant kernel (SpMV fused with the direction update, timed live per
+launch with HIP events), the same solve at 16M and 169M unknowns (500 fixed
+iterations each), and the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--sizes 16m,169m]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "CG solve ms & iterations/s at 1M/16M/169M DOF fp64; effective HBM GB/s vs peak"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def canonical_bytes(n: int, nnz: int, rp_bytes: int) -> int:
+    """Bytes one textbook CG iteration must move (matrix once; SpMV + p.Ap,
+    axpy + r.r and the direction update each touching their vectors once)."""
+    return 12 * nnz + rp_bytes * (n + 1) + 88 * n
+
+
+def spmv_step_bytes(n: int, nnz: int, rp_bytes: int) -> int:
+    """Algorithmic bytes of one launch of the fused SpMV step: the matrix
+    (values, columns, row pointers) once, reads of r, p_{k-1}, x and writes of
+    p_k, q, x."""
+    return 12 * nnz + rp_bytes * (n + 1) + 48 * n
+
+
+def pattern_grad_bytes(n: int, nnz: int, rp_bytes: int) -> int:
+    return 12 * nnz + rp_bytes * (n + 1) + 16 * n
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("cg.hip", "common.h"):
+        with open(os.path.join(ROOT, "krylov_solvers_adjoint_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"source digest:\s*([0-9a-f]+)", text)
+    m_t = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", text)
+    if not m_d or not m_t or m_d.group(1) != digest:
+        return None
+    return float(m_t.group(1))
+
+
+def gpu_setup(N: int, rp_dtype):
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    rowptr, col, vals = W.poisson_csr(N, rp_dtype)
+    log(f"[bench] generated Poisson {N}x{N}: n={N*N} nnz={len(col)} in {time.time()-t0:.1f}s")
+    free0 = torch.cuda.mem_get_info()[0]
+    P = K.sla_csr_create_from_csr(torch.from_numpy(rowptr).to(dev), torch.from_numpy(col).to(dev))
+    v = torch.from_numpy(vals).to(dev)
+    del rowptr, col
+    return P, v, vals, free0
+
+
+def bench_headline(args):
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    N = 1000
+    n = N * N
+    P, v, vals_np, free0 = gpu_setup(N, np.int32)
+    u, b_np = W.manufactured(N)
+    g_np = W.normal_rhs(n, 1)
+    b = torch.from_numpy(b_np).to(dev)
+    g = torch.from_numpy(g_np).to(dev)
+    nnz = P.nnz
+    its = 1000
+
+    def step():
+        x, fi = K.sla_cg_solve(P, v, b, 0.0, its)
+        gb, gv, ai = K.sla_cg_adjoint(P, v, x, g, 0.0, its)
+        return x, gb, gv, fi, ai
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        x, gb, gv, fi, ai = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    free1 = torch.cuda.mem_get_info()[0]
+    total_iters = (fi.iterations + ai.iterations) * args.steps
+    step_bytes = (fi.iterations + ai.iterations) * canonical_bytes(n, nnz, 4) + \
+        pattern_grad_bytes(n, nnz, 4)
+    ms_per_step = 1e3 * wall / args.steps
+    # sanity: the manufactured solution is recovered
+    err = float(torch.linalg.norm(x - torch.from_numpy(u).to(dev)) /
+                torch.linalg.norm(torch.from_numpy(u).to(dev)))
+    kern = K.sla_profile_iteration_kernels(P, v, b, reps=args.kernel_reps)
+    torch.cuda.synchronize()
+    res = dict(
+        n=n, nnz=nnz, iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
+        ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps,
+        it_per_s=total_iters / wall,
+        eff_GBps=step_bytes * args.steps / wall / 1e9,
+        solution_rel_error=err,
+        footprint_MB=(free0 - free1) / 2**20,
+        kernel_ms=kern,
+    )
+    res["pct_peak"] = 100.0 * res["eff_GBps"] / HBM_PEAK_GBPS
+    res["spmv_bytes"] = spmv_step_bytes(n, nnz, 4)
+    del P
+    torch.cuda.synchronize()
+    return res
+
+
+def bench_size(N: int, rp_dtype, its: int, kernel_reps: int):
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    n = N * N
+    P, v, _, free0 = gpu_setup(N, rp_dtype)
+    rp_bytes = 8 if rp_dtype == np.int64 else 4
+    b = torch.from_numpy(W.uniform_rhs(n, 0)).to(dev)
+    # warm-up: captures the iteration graph and touches the workspace
+    K.sla_cg_solve(P, v, b, 0.0, 40)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x, info = K.sla_cg_solve(P, v, b, 0.0, its)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    free1 = torch.cuda.mem_get_info()[0]
+    kern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
+    nnz = P.nnz
+    out = dict(n=n, nnz=nnz, rowptr="i64" if rp_bytes == 8 else "i32",
+               iterations=info.iterations, solve_ms=1e3 * wall,
+               ms_per_iteration=1e3 * wall / info.iterations,
+               it_per_s=info.iterations / wall,
+               eff_GBps=info.iterations * canonical_bytes(n, nnz, rp_bytes) / wall / 1e9,
+               rel_residual=info.rel_residual,
+               footprint_MB=(free0 - free1) / 2**20,
+               kernel_ms=kern,
+               spmv_GBps=spmv_step_bytes(n, nnz, rp_bytes) / (kern["spmv_step"] * 1e-3) / 1e9)
+    out["pct_peak"] = 100.0 * out["eff_GBps"] / HBM_PEAK_GBPS
+    del P, v, b, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(seconds: float):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    forward and adjoint CG on the 1000 x 1000 Poisson system, k fixed
+    iterations each, k chosen so that the run takes about `seconds`."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    threads = min(os.cpu_count() or 1, 16)
+    oracle.set_threads(threads)
+    N = 1000
+    n = N * N
+    rowptr, col, vals = W.poisson_csr(N, np.int64)
+    A = oracle.CSR(n, rowptr, col, vals)
+    _, b = W.manufactured(N)
+    g = W.normal_rhs(n, 1)
+    t0 = time.perf_counter()
+    oracle.cg(A, b, 0.0, 5)
+    per_it = (time.perf_counter() - t0) / 5
+    k = int(max(5, min(1000, seconds / 2 / per_it)))
+    t0 = time.perf_counter()
+    x, fi = oracle.cg(A, b, 0.0, k)
+    oracle.adjoint(A, x, g, 0.0, k)
+    dt = time.perf_counter() - t0
+    return dict(value=2 * k / dt, unit="CG iterations/s", cores=oracle.get_threads(),
+                kind="oracle",
+                sample=f"Poisson 1000x1000 (n=1e6): {k} forward + {k} adjoint CG iterations "
+                       f"with the pattern gradient, fp64, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--sizes", default="16m,169m",
+                    help="extra sizes solved for 500 fixed iterations ('' for none)")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--skip-headline", action="store_true",
+                    help="only the --sizes runs (for profiler passes); prints no JSON line")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the solver path "
+              "is single-GPU; multi-GPU sharding is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import krylov_solvers_adjoint_amd  # noqa: F401  (fails loudly without the HIP library)
+
+    if args.skip_headline:
+        for s in [s for s in args.sizes.split(",") if s]:
+            import numpy as np
+            N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
+                     "169m": (13000, np.int64)}[s.lower()]
+            out = bench_size(N, rp, 500, args.kernel_reps)
+            log(f"[bench] size {s}: {out['ms_per_iteration']:.3f} ms/it, "
+                f"{out['eff_GBps']:.0f} GB/s, kernels {out['kernel_ms']}")
+        return
+    log(f"[bench] headline: Poisson 1000x1000, 1000 fwd + 1000 adj iterations, "
+        f"{args.warmup} warm-up + {args.steps} timed steps")
+    head = bench_headline(args)
+    log(f"[bench] headline done: {head['ms_per_step']:.2f} ms/step, "
+        f"{head['it_per_s']:.0f} it/s, kernels {head['kernel_ms']}")
+    sizes = {}
+    for s in [s for s in args.sizes.split(",") if s]:
+        import numpy as np
+        N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
+                 "169m": (13000, np.int64)}[s.lower()]
+        log(f"[bench] size {s}: Poisson {N}x{N}, 500 fixed iterations")
+        sizes[s.lower()] = bench_size(N, rp, 500, args.kernel_reps)
+        log(f"[bench] size {s}: {sizes[s.lower()]['ms_per_iteration']:.3f} ms/it, "
+            f"{sizes[s.lower()]['eff_GBps']:.0f} GB/s")
+
+    digest = source_digest()
+    spmv_ms = head["kernel_ms"]["spmv_step"]
+    achieved = head["spmv_bytes"] / (spmv_ms * 1e-3) / 1e9
+    roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=achieved / HBM_PEAK_GBPS,
+                    traffic=traffic_from_profile("k_cg_spmv", "poisson1000", digest),
+                    kernel="k_cg_spmv (SpMV + direction update + deferred x update + p.Ap)",
+                    kernel_ms=spmv_ms, algorithmic_bytes=head["spmv_bytes"],
+                    source_digest=digest)
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": head["it_per_s"],
+        "unit": "CG iterations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "poisson1000_fixed1000_fwd_adj", "grid": "1000x1000",
+                   "n": head["n"], "nnz": head["nnz"], "index": "i32/i32",
+                   "iterations_fwd": head["iterations_fwd"],
+                   "iterations_adj": head["iterations_adj"], "parallelism": "none (1 GPU)"},
+        "eff_GBps": head["eff_GBps"],
+        "pct_peak": head["pct_peak"],
+        "solution_rel_error": head["solution_rel_error"],
+        "footprint_MB": head["footprint_MB"],
+        "kernel_ms": head["kernel_ms"],
+        "roofline": roofline,
+        "sizes": sizes,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -188,6 +188,22 @@ sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha_host,
                           double* beta_host, double* rr_host, int64_t cap,
                           int64_t* count_host);
 
+/*
+ * Instrumentation for benchmarks (batch 1): set up the solve of A x = b as
+ * sla_cg_solve does (tol 0) and run one iteration, then launch each of the
+ * two kernels of a CG iteration `reps` times on `stream`, each launch
+ * bracketed by start/stop events recorded around the kernel itself, and
+ * return the mean durations in milliseconds: avg_ms_host[0] the SpMV step
+ * (sum of the r.r partials, beta, stopping test, new search direction,
+ * deferred x update, q = A p, p.Ap partials); [1] the residual step (sum of
+ * the p.Ap partials, alpha, breakdown test, r -= alpha q, r.r partials).
+ * Repeated launches redo the same work, so x and the workspace hold
+ * meaningless values afterwards.  Synchronises `stream`.
+ */
+sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x,
+                                         int64_t reps, double* avg_ms_host,
+                                         hipStream_t stream);
+
 /* Iterations per captured HIP graph block (default 32; 0 = launch kernels
  * one by one without graphs).  Affects speed only, never results. */
 sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);

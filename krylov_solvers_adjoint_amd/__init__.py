@@ -41,7 +41,8 @@ EXPORTS = [
     "sla_csr_pattern", "sla_csr_copy_pattern", "sla_csr_values_from_coo",
     "sla_csr_grad_to_coo", "sla_csr_set_values", "sla_spmv", "sla_cg_solve",
     "sla_cg_adjoint", "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
-    "sla_cg_history", "sla_csr_set_graph_block", "sla_last_error", "sla_status_string",
+    "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_graph_block",
+    "sla_last_error", "sla_status_string",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -81,6 +82,7 @@ def _bind(lib):
         "sla_cg_adjoint_batched": [_P, _P, _P, _P, _P, _D, _I64, _U32, _P, _P],
         "sla_pattern_grad": [_P, _P, _P, _P, _P],
         "sla_cg_history": [_P, _I64, _P, _P, _P, _I64, ctypes.POINTER(_I64)],
+        "sla_profile_iteration_kernels": [_P, _P, _P, _I64, _P, _P],
         "sla_csr_set_graph_block": [_P, _I64],
     }
     for name, args in sig.items():
@@ -365,6 +367,21 @@ def sla_pattern_grad(A: CSRPattern, values_shape_ref: torch.Tensor, lam: torch.T
     _check(_lib.sla_pattern_grad(A.handle, _dev(lam, torch.float64, "lambda"),
                                  _dev(x, torch.float64, "x"), out.data_ptr(), _stream(stream)))
     return out
+
+
+def sla_profile_iteration_kernels(A: CSRPattern, values: torch.Tensor, b: torch.Tensor,
+                                  reps: int = 20, stream=None) -> dict:
+    """Mean duration (ms) of each CG iteration kernel, timed on its own."""
+    if A.bind(values) != 1:
+        raise ValueError("one system only")
+    _shape(b, (A.n,), "b")
+    x = torch.empty_like(b)
+    import numpy as np
+    out = np.zeros(2)
+    _check(_lib.sla_profile_iteration_kernels(A.handle, _dev(b, torch.float64, "b"),
+                                              x.data_ptr(), int(reps), out.ctypes.data,
+                                              _stream(stream)))
+    return dict(zip(("spmv_step", "residual_step"), out.tolist()))
 
 
 # ---------------------------------------------------------------------------

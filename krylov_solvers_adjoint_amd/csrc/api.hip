@@ -2,6 +2,7 @@
 // its arguments before launching anything, converts every failure into an
 // sla_status, and never lets a C++ exception escape.
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -363,6 +364,19 @@ sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha, double* beta
     delete[] h;
   }
   return SLA_OK;
+  API_END
+}
+
+sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x, int64_t reps,
+                                         double* avg_ms_host, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_profile_iteration_kernels: NULL handle");
+  REQUIRE(A->batch == 1, "sla_profile_iteration_kernels: bind exactly one system");
+  REQUIRE(b != nullptr && x != nullptr && avg_ms_host != nullptr,
+          "sla_profile_iteration_kernels: NULL pointer");
+  REQUIRE(reps >= 1 && reps <= 100000, "sla_profile_iteration_kernels: reps out of range");
+  return profile_kernels(A, b, x, reps, avg_ms_host, stream);
   API_END
 }
 

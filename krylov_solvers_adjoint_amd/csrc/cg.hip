@@ -11,33 +11,38 @@
 //
 // Layout and schedule (memory-bound: ~0.13 flop per byte, far below the fp64
 // ridge, so no matrix cores):
-//   * One iteration is four kernels, all reading the device-resident scalars
-//     of each system; nothing comes back to the host inside the loop.
-//       k_cg_spmv      p_k = r_k + beta p_{k-1}  (own rows, and recomputed at
-//                      each gathered column), x += alpha_{k-1} p_{k-1} (the
-//                      previous iteration's x update, deferred to this pass
-//                      where p_{k-1} is read anyway), q = A p_k, partial p.q
-//       k_cg_alpha     alpha = rr / sum(partials); breakdown checks
-//       k_cg_residual  r -= alpha q, partial r.r
-//       k_cg_beta      rr' = sum(partials); beta; stopping test; it++
-//     p is double-buffered because the SpMV reads p_{k-1} at other
-//     workgroups' rows while it writes p_k.  The arithmetic of every element
-//     is the textbook one (each * and + rounded separately), so only the
-//     order of the dot-product sums differs from a sequential CPU run.
-//   * Rows are cut into tiles of 256 (one row per thread).  A tile's slots
-//     [rowptr[r0], rowptr[r0+256]) are contiguous, so they are staged into LDS
-//     with coalesced loads and each thread then walks its own row there.
-//   * The iteration kernels run a fixed grid (8 workgroups per CU); each
-//     workgroup walks tiles inside its XCD's contiguous share of the rows,
-//     interleaved with the other workgroups of that XCD, so stencil
-//     neighbours (rows i +- N) are read while still in that XCD's L2, and the
-//     dot products have one partial per workgroup, summed in a fixed order:
-//     results are bitwise reproducible.
-//   * Blocks of iterations are captured once per handle as a HIP graph; each
+//   * One iteration k is two kernels; nothing returns to the host inside the
+//     loop.
+//       SpMV step k     rr_k = sum of the r.r partials; beta = rr_k / rr_{k-1};
+//                       stopping test; p_k = r_k + beta p_{k-1} (own rows, and
+//                       recomputed at each gathered column); the deferred
+//                       x += alpha_{k-1} p_{k-1}; q = A p_k; p.q partials
+//       residual step k alpha_k = rr_k / sum of the p.q partials; breakdown
+//                       test; r -= alpha_k q; r.r partials
+//     Each workgroup sums the (at most a few hundred) partials of the previous
+//     step itself, in one fixed order, so every workgroup obtains the same
+//     bits; no one-workgroup reduction kernel and no cross-workgroup signal
+//     inside a kernel is needed.  The x update is deferred by one step to the
+//     pass that reads p_{k-1} anyway; when the stopping test fires, that pass
+//     only applies it.  p is double-buffered because the SpMV reads p_{k-1}
+//     at other waves' rows while it writes p_k.  Each element's arithmetic is
+//     the textbook one (every * and + rounded on its own), so only the order
+//     of the dot-product sums differs from a sequential CPU run.
+//   * Rows are cut into 64-row wave tiles (one row per lane).  A tile's slots
+//     [rowptr[r0], rowptr[r0+64]) are contiguous: the wave stages them into
+//     its own LDS area with coalesced loads, then each lane walks its row.
+//     Only wave-level synchronisation is needed, so the 16 waves of a
+//     workgroup progress independently.
+//   * Fixed grid of two 1024-thread workgroups per CU; each wave walks tiles
+//     inside its XCD's contiguous share of the rows, interleaved with the
+//     other waves of that XCD, so stencil neighbours (rows i +- N) are read
+//     while still in that XCD's L2.
+//   * Blocks of iterations are captured once per handle as a HIP graph; a
 //     kernel returns at once when its system has stopped, and the host only
 //     polls the count of running systems between blocks.
 #include <algorithm>
 #include <cmath>
+#include <vector>
 
 #include "handle.h"
 
@@ -54,21 +59,22 @@ namespace {
     }                                                                          \
   } while (0)
 
-// Row sum of one tile row: acc = sum_k vals[k] * g(col[k]) in ascending slot
-// order, starting from 0.  `lv`/`lc` are LDS staging areas of lds_cap slots.
-// Returns false for threads past the last row.  Contains workgroup barriers:
-// every thread of the workgroup must call it for the same tile.
+// Row sum of one lane's row in a wave tile: acc = sum_k vals[k] * g(col[k])
+// in ascending slot order, starting from 0.  `lv`/`lc` are this wave's LDS
+// staging areas of `cap` slots.  Returns false for lanes past the last row.
+// Every lane of the wave must call it for the same tile.
 template <typename RP, typename G>
-__device__ __forceinline__ bool tile_row(const RP* __restrict__ rowptr,
-                                         const int32_t* __restrict__ col,
-                                         const double* __restrict__ vals, int64_t n,
-                                         int64_t tile, int lds_cap, double* lv, int32_t* lc,
-                                         G g, int64_t& row, double& acc) {
+__device__ __forceinline__ bool wave_tile_row(const RP* __restrict__ rowptr,
+                                              const int32_t* __restrict__ col,
+                                              const double* __restrict__ vals, int64_t n,
+                                              int64_t tile, int cap, double* lv, int32_t* lc,
+                                              G g, int64_t& row, double& acc) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int64_t r0 = tile * kTileRows;
   const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
   const int64_t s0 = rowptr[r0];
   const int64_t len = int64_t(rowptr[r1]) - s0;
-  row = r0 + threadIdx.x;
+  row = r0 + lane;
   const bool ok = row < r1;
   int64_t a = 0, e = 0;
   if (ok) {
@@ -76,42 +82,65 @@ __device__ __forceinline__ bool tile_row(const RP* __restrict__ rowptr,
     e = rowptr[row + 1];
   }
   acc = 0.0;
-  if (len <= lds_cap) {
-    for (int64_t k = threadIdx.x; k < len; k += kBlock) {
+  if (len <= cap) {
+    for (int64_t k = lane; k < len; k += kWave) {
       lv[k] = vals[s0 + k];
       lc[k] = col[s0 + k];
     }
-    __syncthreads();
+    wave_sync();
     for (int64_t k = a - s0; k < e - s0; ++k) acc = acc + lv[k] * g(lc[k]);
-    __syncthreads();
+    wave_sync();
   } else {
     for (int64_t k = a; k < e; ++k) acc = acc + vals[k] * g(col[k]);
   }
   return ok;
 }
 
+// This wave's LDS staging areas: 12 bytes per slot (value and column).
+__device__ __forceinline__ void wave_areas(double* lds_dyn, int cap, double*& lv, int32_t*& lc) {
+  const int w = threadIdx.x / kWave;
+  lv = lds_dyn + int64_t(w) * (cap + (cap + 1) / 2);
+  lc = reinterpret_cast<int32_t*>(lv + cap);
+}
+
+size_t solver_lds_bytes(int cap, int waves) {
+  return size_t(waves) * size_t(cap + (cap + 1) / 2) * sizeof(double);
+}
+
+// Sum of `count` partials, the same fixed order in every workgroup: thread t
+// adds part[t], part[t + 1024], ..., then the workgroup tree.  The result is
+// in every thread.
+__device__ __forceinline__ double sum_partials_all(const double* __restrict__ part, int count,
+                                                   double* red) {
+  double v = 0.0;
+  for (int i = threadIdx.x; i < count; i += kIterBlock) v = v + part[i];
+  return block_sum_all<kIterBlock>(v, red);
+}
+
 // ---------------------------------------------------------------------------
 // Standalone SpMV: y[s] = A_s x[s]
 // ---------------------------------------------------------------------------
 template <typename RP>
-__global__ __launch_bounds__(kBlock) void k_spmv(const RP* __restrict__ rowptr,
-                                                 const int32_t* __restrict__ col,
-                                                 const double* __restrict__ vals, int64_t n,
-                                                 int64_t nnz, int64_t tiles, int lds_cap,
-                                                 const double* __restrict__ x,
-                                                 double* __restrict__ y) {
+__global__ __launch_bounds__(kIterBlock) void k_spmv(const RP* __restrict__ rowptr,
+                                                     const int32_t* __restrict__ col,
+                                                     const double* __restrict__ vals, int64_t n,
+                                                     int64_t nnz, int64_t tiles, int cap,
+                                                     const double* __restrict__ x,
+                                                     double* __restrict__ y) {
   extern __shared__ double lds_dyn[];
-  double* lv = lds_dyn;
-  int32_t* lc = reinterpret_cast<int32_t*>(lds_dyn + lds_cap);
+  double* lv;
+  int32_t* lc;
+  wave_areas(lds_dyn, cap, lv, lc);
   const int64_t s = blockIdx.y;
   const double* v = vals + s * nnz;
   const double* xs = x + s * n;
   double* ys = y + s * n;
   auto g = [&](int64_t j) { return xs[j]; };
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+  const int w = threadIdx.x / kWave;
+  for (int64_t t = int64_t(blockIdx.x) * kWaves + w; t < tiles; t += int64_t(gridDim.x) * kWaves) {
     int64_t i;
     double acc;
-    if (tile_row<RP>(rowptr, col, v, n, t, lds_cap, lv, lc, g, i, acc)) ys[i] = acc;
+    if (wave_tile_row<RP>(rowptr, col, v, n, t, cap, lv, lc, g, i, acc)) ys[i] = acc;
   }
 }
 
@@ -119,19 +148,21 @@ __global__ __launch_bounds__(kBlock) void k_spmv(const RP* __restrict__ rowptr,
 // CG kernels
 // ---------------------------------------------------------------------------
 
-// r = b (x = 0) or r = b - q with q = A x0; p_{-1} = 0; partial b.b and r.r.
-__global__ __launch_bounds__(kBlock) void k_cg_init(const Ctx* __restrict__ c, int use_x0) {
-  __shared__ double red[4];
+// r = b (x = 0) or r = b - q with q = A x0; p_{-1} = 0; partials of b.b and
+// of r_0.r_0.
+__global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ c, int use_x0) {
+  __shared__ double red[kWaves];
   const int64_t s = blockIdx.y, n = c->n;
   const double* b = c->b + s * n;
   double* x = c->x + s * n;
   double* r = c->r + s * n;
   double* pm = c->p[1] + s * n;
   const double* q = c->q + s * n;
-  const TileWalk w = tile_walk(c->tiles, c->grid, blockIdx.x);
+  const int lane = threadIdx.x & (kWave - 1);
+  const TileWalk w = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, threadIdx.x / kWave);
   double bb = 0.0, rr = 0.0;
   for (int64_t t = w.first; t < w.end; t += w.stride) {
-    const int64_t i = t * kTileRows + threadIdx.x;
+    const int64_t i = t * kTileRows + lane;
     if (i < n) {
       const double bi = b[i];
       double ri;
@@ -147,76 +178,125 @@ __global__ __launch_bounds__(kBlock) void k_cg_init(const Ctx* __restrict__ c, i
       rr = rr + ri * ri;
     }
   }
-  bb = block_sum(bb, red);
-  rr = block_sum(rr, red);
+  bb = block_sum_all<kIterBlock>(bb, red);
+  rr = block_sum_all<kIterBlock>(rr, red);
   if (threadIdx.x == 0) {
-    c->part_c[s * c->grid + blockIdx.x] = bb;
-    c->part_b[s * c->grid + blockIdx.x] = rr;
+    double* part = c->part + s * kPartSets * c->grid;
+    part[4 * c->grid + blockIdx.x] = bb;
+    part[0 * c->grid + blockIdx.x] = rr;
     if (blockIdx.x == 0 && s == 0) *c->n_running = 0;
   }
 }
 
-__device__ __forceinline__ double sum_partials(const double* __restrict__ part, int count,
-                                               double* red) {
-  double v = 0.0;
-  for (int i = threadIdx.x; i < count; i += kBlock) v = v + part[i];
-  return block_sum(v, red);
-}
-
-__global__ __launch_bounds__(kBlock) void k_cg_init_scalars(const Ctx* __restrict__ c,
-                                                            double tol, int64_t maxit) {
-  __shared__ double red[4];
+__global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __restrict__ c,
+                                                                double tol, int64_t maxit) {
+  __shared__ double red[kWaves];
   const int64_t s = blockIdx.x;
-  const double bb = sum_partials(c->part_c + s * c->grid, c->grid, red);
-  const double rr = sum_partials(c->part_b + s * c->grid, c->grid, red);
+  const double* part = c->part + s * kPartSets * c->grid;
+  const double bb = sum_partials_all(part + 4 * c->grid, c->grid, red);
+  const double rr = sum_partials_all(part + 0 * c->grid, c->grid, red);
   if (threadIdx.x == 0) {
     Scal* sc = c->scal + s;
-    sc->rr = rr;
+    sc->rr[0] = rr;
+    sc->rr[1] = rr;
+    sc->alpha = 0.0;
     sc->bb = bb;
     sc->stop = (tol * tol) * bb;
-    sc->alpha = 0.0;
-    sc->beta = 0.0;
+    sc->rr_final = rr;
+    sc->ka = 0;
+    sc->kr = 0;
     sc->it = 0;
     sc->maxit = maxit;
-    sc->x_lag = 0;
-    sc->lag_buf = 0;
-    int32_t st = ST_RUNNING;
-    if (!isfinite(bb) || !isfinite(rr)) st = ST_NONFINITE;
-    else if (rr <= sc->stop) st = ST_CONVERGED;
-    else if (maxit <= 0) st = ST_MAXIT;
-    sc->state = st;
+    const int32_t st = (!isfinite(bb) || !isfinite(rr)) ? ST_NONFINITE : ST_RUNNING;
+    sc->state_a = st;
+    sc->state_r = st;
     if (st == ST_RUNNING) atomicAdd(c->n_running, 1);
   }
 }
 
+// SpMV step k (see the file comment).
 template <typename RP>
-__global__ __launch_bounds__(kBlock) void k_cg_spmv(const Ctx* __restrict__ c) {
+__global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ c) {
   extern __shared__ double lds_dyn[];
-  __shared__ double red[4];
+  __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
-  const Scal* sc = c->scal + s;
-  if (sc->state != ST_RUNNING) return;
+  Scal* sc = c->scal + s;
+  const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
+  const int32_t st_in = sc->state_r;
+  if (st_in != ST_RUNNING) {
+    if (lead) sc->state_a = st_in;
+    return;
+  }
+  const int G = c->grid;
+  double* part = c->part + s * kPartSets * G;
+  const int64_t k = sc->ka;
+  const double rr = sum_partials_all(part + (k & 1) * G, G, red);
+  const bool lag = k > 0;  // x still lacks alpha_{k-1} p_{k-1}
+  double alpha = 0.0, beta = 0.0;
+  int32_t stop = ST_RUNNING;
+  int64_t it_stop = k;
+  double rr_stop = rr;
+  if (lag) {
+    const double rr_prev = sc->rr[(k - 1) & 1];
+    alpha = sc->alpha;
+    if (!isfinite(rr)) {
+      stop = ST_NONFINITE;  // iteration k-1 did not complete
+      it_stop = k - 1;
+      rr_stop = rr_prev;
+    } else {
+      beta = rr / rr_prev;
+    }
+  }
+  if (stop == ST_RUNNING) {
+    if (rr <= sc->stop) stop = ST_CONVERGED;
+    else if (k >= sc->maxit) stop = ST_MAXIT;
+  }
+  if (lead) {
+    if (lag && stop != ST_NONFINITE && c->hist != nullptr && k - 1 < c->hist_cap) {
+      double* h = c->hist + (s * c->hist_cap + (k - 1)) * 3;
+      h[0] = alpha;
+      h[1] = beta;
+      h[2] = rr;
+    }
+    sc->rr[k & 1] = rr;
+    sc->kr = k;
+    if (stop != ST_RUNNING) {
+      sc->it = it_stop;
+      sc->rr_final = rr_stop;
+      sc->state_a = stop;
+      atomicSub(c->n_running, 1);
+    }
+  }
   const int64_t n = c->n;
-  const int64_t it = sc->it;
-  const double beta = sc->beta;
-  const double alpha = sc->alpha;
-  const bool lag = sc->x_lag != 0;
+  const double* pold = c->p[(k + 1) & 1] + s * n;
+  double* x = c->x + s * n;
+  const int w = threadIdx.x / kWave;
+  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, w);
+  if (stop != ST_RUNNING) {
+    // last pass: only the deferred x update
+    if (lag) {
+      const int lane = threadIdx.x & (kWave - 1);
+      for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
+        const int64_t i = t * kTileRows + lane;
+        if (i < n) x[i] = x[i] + alpha * pold[i];
+      }
+    }
+    return;
+  }
   const RP* rowptr = static_cast<const RP*>(c->rowptr);
   const double* vals = c->vals + s * c->nnz;
   const double* r = c->r + s * n;
-  const double* pold = c->p[(it + 1) & 1] + s * n;
-  double* pnew = c->p[it & 1] + s * n;
-  double* x = c->x + s * n;
+  double* pnew = c->p[k & 1] + s * n;
   double* q = c->q + s * n;
-  double* lv = lds_dyn;
-  int32_t* lc = reinterpret_cast<int32_t*>(lds_dyn + c->lds_cap);
+  double* lv;
+  int32_t* lc;
+  wave_areas(lds_dyn, c->wave_cap, lv, lc);
   auto g = [&](int64_t j) { return r[j] + beta * pold[j]; };
-  const TileWalk w = tile_walk(c->tiles, c->grid, blockIdx.x);
   double pq = 0.0;
-  for (int64_t t = w.first; t < w.end; t += w.stride) {
+  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
     int64_t i;
     double acc;
-    if (tile_row<RP>(rowptr, c->col, vals, n, t, c->lds_cap, lv, lc, g, i, acc)) {
+    if (wave_tile_row<RP>(rowptr, c->col, vals, n, t, c->wave_cap, lv, lc, g, i, acc)) {
       const double po = pold[i];
       const double pn = r[i] + beta * po;
       if (lag) x[i] = x[i] + alpha * po;
@@ -225,134 +305,111 @@ __global__ __launch_bounds__(kBlock) void k_cg_spmv(const Ctx* __restrict__ c) {
       pq = pq + pn * acc;
     }
   }
-  pq = block_sum(pq, red);
-  if (threadIdx.x == 0) c->part_a[s * c->grid + blockIdx.x] = pq;
+  pq = block_sum_all<kIterBlock>(pq, red);
+  if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
-__global__ __launch_bounds__(kBlock) void k_cg_alpha(const Ctx* __restrict__ c) {
-  __shared__ double red[4];
-  const int64_t s = blockIdx.x;
-  Scal* sc = c->scal + s;
-  if (sc->state != ST_RUNNING) return;
-  const double pq = sum_partials(c->part_a + s * c->grid, c->grid, red);
-  if (threadIdx.x == 0) {
-    if (!isfinite(pq)) {
-      sc->state = ST_NONFINITE;
-      sc->x_lag = 0;
-      atomicSub(c->n_running, 1);
-    } else if (!(pq > 0.0)) {
-      sc->state = ST_NOT_SPD;
-      sc->x_lag = 0;
-      atomicSub(c->n_running, 1);
-    } else {
-      sc->alpha = sc->rr / pq;
-      sc->x_lag = 1;
-      sc->lag_buf = int32_t(sc->it & 1);
-    }
-  }
-}
-
-__global__ __launch_bounds__(kBlock) void k_cg_residual(const Ctx* __restrict__ c) {
-  __shared__ double red[4];
+// Residual step k (see the file comment).
+__global__ __launch_bounds__(kIterBlock) void k_cg_residual(const Ctx* __restrict__ c) {
+  __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
-  const Scal* sc = c->scal + s;
-  if (sc->state != ST_RUNNING) return;
+  Scal* sc = c->scal + s;
+  const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
+  const int32_t st_in = sc->state_a;
+  if (st_in != ST_RUNNING) {
+    if (lead) sc->state_r = st_in;
+    return;
+  }
+  const int G = c->grid;
+  double* part = c->part + s * kPartSets * G;
+  const int64_t k = sc->kr;
+  const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
+  const double rr = sc->rr[k & 1];
+  int32_t stop = ST_RUNNING;
+  if (!isfinite(pq)) stop = ST_NONFINITE;
+  else if (!(pq > 0.0)) stop = ST_NOT_SPD;
+  if (stop != ST_RUNNING) {
+    // breakdown: x already holds x_k (the SpMV step applied the lagged update)
+    if (lead) {
+      sc->it = k;
+      sc->rr_final = rr;
+      sc->state_r = stop;
+      atomicSub(c->n_running, 1);
+    }
+    return;
+  }
+  const double alpha = rr / pq;
+  if (lead) {
+    sc->alpha = alpha;
+    sc->ka = k + 1;
+  }
   const int64_t n = c->n;
-  const double alpha = sc->alpha;
   double* r = c->r + s * n;
   const double* q = c->q + s * n;
-  const TileWalk w = tile_walk(c->tiles, c->grid, blockIdx.x);
-  double rr = 0.0;
-  for (int64_t t = w.first; t < w.end; t += w.stride) {
-    const int64_t i = t * kTileRows + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, threadIdx.x / kWave);
+  double rn = 0.0;
+  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
+    const int64_t i = t * kTileRows + lane;
     if (i < n) {
       const double ri = r[i] - alpha * q[i];
       r[i] = ri;
-      rr = rr + ri * ri;
+      rn = rn + ri * ri;
     }
   }
-  rr = block_sum(rr, red);
-  if (threadIdx.x == 0) c->part_b[s * c->grid + blockIdx.x] = rr;
+  rn = block_sum_all<kIterBlock>(rn, red);
+  if (threadIdx.x == 0) part[((k + 1) & 1) * G + blockIdx.x] = rn;
 }
 
-__global__ __launch_bounds__(kBlock) void k_cg_beta(const Ctx* __restrict__ c) {
-  __shared__ double red[4];
-  const int64_t s = blockIdx.x;
-  Scal* sc = c->scal + s;
-  if (sc->state != ST_RUNNING) return;
-  const double rr_new = sum_partials(c->part_b + s * c->grid, c->grid, red);
-  if (threadIdx.x == 0) {
-    if (!isfinite(rr_new)) {
-      sc->state = ST_NONFINITE;  // x still lacks alpha p: the finalize adds it
-      atomicSub(c->n_running, 1);
-      return;
-    }
-    const double beta = rr_new / sc->rr;
-    const int64_t it = sc->it;
-    if (c->hist != nullptr && it < c->hist_cap) {
-      double* h = c->hist + (s * c->hist_cap + it) * 3;
-      h[0] = sc->alpha;
-      h[1] = beta;
-      h[2] = rr_new;
-    }
-    sc->beta = beta;
-    sc->rr = rr_new;
-    sc->it = it + 1;
-    if (rr_new <= sc->stop) {
-      sc->state = ST_CONVERGED;
-      atomicSub(c->n_running, 1);
-    } else if (it + 1 >= sc->maxit) {
-      sc->state = ST_MAXIT;
-      atomicSub(c->n_running, 1);
-    }
-  }
-}
-
-// x += alpha p for the last iteration (deferred from the SpMV pass).
-__global__ __launch_bounds__(kBlock) void k_cg_finalize(const Ctx* __restrict__ c) {
-  const int64_t s = blockIdx.y;
-  const Scal* sc = c->scal + s;
-  if (sc->x_lag == 0) return;
-  const int64_t n = c->n;
-  const double alpha = sc->alpha;
-  const double* p = c->p[sc->lag_buf] + s * n;
-  double* x = c->x + s * n;
-  const TileWalk w = tile_walk(c->tiles, c->grid, blockIdx.x);
-  for (int64_t t = w.first; t < w.end; t += w.stride) {
-    const int64_t i = t * kTileRows + threadIdx.x;
-    if (i < n) x[i] = x[i] + alpha * p[i];
-  }
-}
-
-// grad_vals[s][k] = -lambda[s][i] * x[s][col[k]] for every stored slot k of row i
+// grad_vals[s][k] = -lambda[s][i] * x[s][col[k]] for every stored slot k of
+// row i.  The lanes of a wave walk the tile's slots in order (coalesced
+// column loads and gradient stores); each slot's row comes from an LDS map
+// the lanes fill for their own rows.
 template <typename RP>
-__global__ __launch_bounds__(kBlock) void k_pattern_grad(const RP* __restrict__ rowptr,
-                                                         const int32_t* __restrict__ col,
-                                                         int64_t n, int64_t nnz,
-                                                         const double* __restrict__ lambda,
-                                                         const double* __restrict__ x,
-                                                         double* __restrict__ grad) {
+__global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restrict__ rowptr,
+                                                             const int32_t* __restrict__ col,
+                                                             int64_t n, int64_t nnz, int64_t tiles,
+                                                             int cap,
+                                                             const double* __restrict__ lambda,
+                                                             const double* __restrict__ x,
+                                                             double* __restrict__ grad) {
+  extern __shared__ double lds_dyn[];
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint8_t* rowmap = reinterpret_cast<uint8_t*>(lds_dyn) + int64_t(w) * cap;
   const int64_t s = blockIdx.y;
   const double* l = lambda + s * n;
   const double* xs = x + s * n;
   double* gs = grad + s * nnz;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const double li = l[i];
-    const int64_t a = rowptr[i], e = rowptr[i + 1];
-    for (int64_t k = a; k < e; ++k) gs[k] = -(li * xs[col[k]]);
+  for (int64_t t = int64_t(blockIdx.x) * kWaves + w; t < tiles; t += int64_t(gridDim.x) * kWaves) {
+    const int64_t r0 = t * kTileRows;
+    const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
+    const int64_t s0 = rowptr[r0];
+    const int64_t len = int64_t(rowptr[r1]) - s0;
+    const int64_t i = r0 + lane;
+    if (len <= cap) {
+      if (i < r1) {
+        const int64_t a = rowptr[i] - s0, e = rowptr[i + 1] - s0;
+        for (int64_t k = a; k < e; ++k) rowmap[k] = uint8_t(lane);
+      }
+      wave_sync();
+      for (int64_t k = lane; k < len; k += kWave)
+        gs[s0 + k] = -(l[r0 + rowmap[k]] * xs[col[s0 + k]]);
+      wave_sync();
+    } else if (i < r1) {
+      const double li = l[i];
+      for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) gs[k] = -(li * xs[col[k]]);
+    }
   }
 }
 
-size_t lds_bytes(const sla_csr A) { return size_t(A->lds_cap) * (sizeof(double) + sizeof(int32_t)); }
+size_t lds_bytes(const sla_csr A) { return solver_lds_bytes(A->wave_cap, kWaves); }
 
 template <typename RP>
 sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
-  k_cg_spmv<RP><<<grid2, kBlock, lds_bytes(A), st>>>(A->ctx_dev);
-  k_cg_alpha<<<unsigned(batch), kBlock, 0, st>>>(A->ctx_dev);
-  k_cg_residual<<<grid2, kBlock, 0, st>>>(A->ctx_dev);
-  k_cg_beta<<<unsigned(batch), kBlock, 0, st>>>(A->ctx_dev);
+  k_cg_spmv<RP><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
   LAUNCH_CHECK();
   return SLA_OK;
 }
@@ -371,8 +428,8 @@ sla_status get_graph(sla_csr A, int64_t batch, hipGraphExec_t* exec) {
     *exec = it->second.second;
     return SLA_OK;
   }
-  if (A->capture_stream == nullptr) SLA_TRY_HIP(hipStreamCreateWithFlags(&A->capture_stream,
-                                                                         hipStreamNonBlocking));
+  if (A->capture_stream == nullptr)
+    SLA_TRY_HIP(hipStreamCreateWithFlags(&A->capture_stream, hipStreamNonBlocking));
   hipGraph_t g = nullptr;
   hipGraphExec_t e = nullptr;
   SLA_TRY_HIP(hipStreamBeginCapture(A->capture_stream, hipStreamCaptureModeThreadLocal));
@@ -403,6 +460,37 @@ void drop_graphs(sla_csr A) {
     (void)hipGraphDestroy(kv.second.first);
   }
   A->graphs.clear();
+}
+
+void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool hist) {
+  c = Ctx{};
+  c.rowptr = A->rowptr;
+  c.col = A->col;
+  c.vals = A->vals;
+  c.x = x;
+  c.b = b;
+  c.r = A->r;
+  c.p[0] = A->p0;
+  c.p[1] = A->p1;
+  c.q = A->q;
+  c.part = A->part;
+  c.scal = A->scal;
+  c.hist = hist ? A->hist : nullptr;
+  c.hist_cap = hist ? A->hist_cap : 0;
+  c.n_running = A->n_running;
+  c.n = A->n;
+  c.nnz = A->nnz;
+  c.batch = batch;
+  c.tiles = A->tiles;
+  c.grid = A->grid;
+  c.wave_cap = A->wave_cap;
+}
+
+// Workgroups for a one-pass kernel over `tiles` wave tiles and `batch` systems.
+unsigned plain_grid(int64_t tiles, int64_t batch) {
+  const int64_t need = (tiles + kWaves - 1) / kWaves;
+  const int64_t target = std::max<int64_t>(1, int64_t(device_cus()) * 2 / batch);
+  return unsigned(std::max<int64_t>(1, std::min(need, target)));
 }
 
 }  // namespace
@@ -444,10 +532,10 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   if (A->ws_batch == batch && A->r != nullptr) return SLA_OK;
   release_workspace(A);
   const int64_t n = A->n;
-  // iteration grid: about 8 workgroups per CU in total, a multiple of the
-  // XCD count per system, never more than the tiles need (rounded up)
-  const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * 8 / batch);
-  int64_t g = std::min<int64_t>(A->tiles, target);
+  // solver grid: two workgroups per CU in total, a multiple of the XCD count
+  // per system, never more than the wave tiles need (rounded up)
+  const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * 2 / batch);
+  int64_t g = std::min<int64_t>((A->tiles + kWaves - 1) / kWaves, target);
   g = (g + kXcds - 1) / kXcds * kXcds;
   A->grid = int32_t(std::max<int64_t>(g, kXcds));
   const size_t vec = size_t(batch) * size_t(n);
@@ -455,7 +543,7 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   SLA_TRY(dev_alloc(&A->p0, vec, "p"));
   SLA_TRY(dev_alloc(&A->p1, vec, "p"));
   SLA_TRY(dev_alloc(&A->q, vec, "q"));
-  SLA_TRY(dev_alloc(&A->part, size_t(3) * batch * A->grid, "partials"));
+  SLA_TRY(dev_alloc(&A->part, size_t(kPartSets) * batch * A->grid, "partials"));
   SLA_TRY(dev_alloc(&A->scal, batch, "scalars"));
   SLA_TRY(dev_alloc(&A->n_running, 1, "running count"));
   SLA_TRY(dev_alloc(&A->ctx_dev, 1, "context"));
@@ -472,31 +560,29 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
 // ---------------------------------------------------------------------------
 sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x, double* y,
                        hipStream_t st) {
-  if (A->n == 0) return SLA_OK;
-  const int64_t target = std::max<int64_t>(1, int64_t(device_cus()) * 8 / batch);
-  const dim3 grid(unsigned(std::min<int64_t>(A->tiles, std::max<int64_t>(target, 1))),
-                  unsigned(batch));
+  const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
+  const size_t lds = lds_bytes(A);
   if (A->rp_idx == SLA_I32)
-    k_spmv<int32_t><<<grid, kBlock, lds_bytes(A), st>>>(
-        (const int32_t*)A->rowptr, A->col, vals, A->n, A->nnz, A->tiles, A->lds_cap, x, y);
+    k_spmv<int32_t><<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, vals, A->n,
+                                                   A->nnz, A->tiles, A->wave_cap, x, y);
   else
-    k_spmv<int64_t><<<grid, kBlock, lds_bytes(A), st>>>(
-        (const int64_t*)A->rowptr, A->col, vals, A->n, A->nnz, A->tiles, A->lds_cap, x, y);
+    k_spmv<int64_t><<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, vals, A->n,
+                                                   A->nnz, A->tiles, A->wave_cap, x, y);
   LAUNCH_CHECK();
   return SLA_OK;
 }
 
 sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda, const double* x,
                                double* grad_vals, hipStream_t st) {
-  if (A->n == 0) return SLA_OK;
-  const dim3 grid(unsigned(std::min<int64_t>((A->n + kBlock - 1) / kBlock, 1 << 20)),
-                  unsigned(batch));
+  const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
+  const int cap = A->wave_cap;
+  const size_t lds = size_t(kWaves) * size_t(cap);
   if (A->rp_idx == SLA_I32)
-    k_pattern_grad<int32_t><<<grid, kBlock, 0, st>>>((const int32_t*)A->rowptr, A->col, A->n,
-                                                     A->nnz, lambda, x, grad_vals);
+    k_pattern_grad<int32_t><<<grid, kIterBlock, lds, st>>>(
+        (const int32_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles, cap, lambda, x, grad_vals);
   else
-    k_pattern_grad<int64_t><<<grid, kBlock, 0, st>>>((const int64_t*)A->rowptr, A->col, A->n,
-                                                     A->nnz, lambda, x, grad_vals);
+    k_pattern_grad<int64_t><<<grid, kIterBlock, lds, st>>>(
+        (const int64_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles, cap, lambda, x, grad_vals);
   LAUNCH_CHECK();
   return SLA_OK;
 }
@@ -516,44 +602,23 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
       A->hist_batch = batch;
     }
   }
-  Ctx& c = *A->ctx_host;
-  c.rowptr = A->rowptr;
-  c.col = A->col;
-  c.vals = A->vals;
-  c.x = x;
-  c.b = b;
-  c.r = A->r;
-  c.p[0] = A->p0;
-  c.p[1] = A->p1;
-  c.q = A->q;
-  c.part_a = A->part;
-  c.part_b = A->part + size_t(batch) * A->grid;
-  c.part_c = A->part + size_t(2) * batch * A->grid;
-  c.scal = A->scal;
-  c.hist = want_hist ? A->hist : nullptr;
-  c.hist_cap = want_hist ? A->hist_cap : 0;
-  c.n_running = A->n_running;
-  c.n = A->n;
-  c.nnz = A->nnz;
-  c.batch = batch;
-  c.tiles = A->tiles;
-  c.grid = A->grid;
-  c.lds_cap = A->lds_cap;
+  fill_ctx(A, *A->ctx_host, b, x, batch, want_hist);
   SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
 
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
   if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, A->q, st));  // q = A x0
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
-  k_cg_init<<<grid2, kBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
-  k_cg_init_scalars<<<unsigned(batch), kBlock, 0, st>>>(A->ctx_dev, tol, maxit);
+  k_cg_init<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
+  k_cg_init_scalars<<<unsigned(batch), kIterBlock, 0, st>>>(A->ctx_dev, tol, maxit);
   LAUNCH_CHECK();
   SLA_TRY_HIP(hipMemcpyAsync(A->poll_host, A->n_running, sizeof(int), hipMemcpyDeviceToHost,
                              st));
   SLA_TRY_HIP(hipStreamSynchronize(st));
 
   if (A->poll_host[0] > 0) {
+    // at most maxit + 1 SpMV steps: the last one only applies the x update
     const int64_t K = A->graph_block > 0 ? A->graph_block : 16;
-    const int64_t nblocks = (maxit + K - 1) / K;
+    const int64_t nblocks = (maxit + 1 + K - 1) / K;
     hipGraphExec_t exec = nullptr;
     if (A->graph_block > 0) SLA_TRY(get_graph(A, batch, &exec));
     for (int64_t j = 0; j < nblocks; ++j) {
@@ -569,8 +634,6 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
       }
     }
   }
-  k_cg_finalize<<<grid2, kBlock, 0, st>>>(A->ctx_dev);
-  LAUNCH_CHECK();
   SLA_TRY_HIP(hipMemcpyAsync(A->scal_host, A->scal, sizeof(Scal) * batch,
                              hipMemcpyDeviceToHost, st));
   SLA_TRY_HIP(hipStreamSynchronize(st));
@@ -578,19 +641,87 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
   sla_status first = SLA_OK;
   for (int64_t s = 0; s < batch; ++s) {
     const Scal& sc = A->scal_host[s];
-    const sla_status ss = sc.state >= SLA_ERR_NOT_SPD ? sla_status(sc.state) : SLA_OK;
+    const int32_t state = sc.state_a != ST_RUNNING ? sc.state_a : sc.state_r;
+    const sla_status ss = state >= SLA_ERR_NOT_SPD ? sla_status(state) : SLA_OK;
     if (info) {
       info[s].iterations = sc.it;
-      info[s].rel_residual = sc.bb > 0 ? std::sqrt(sc.rr / sc.bb) : 0.0;
-      info[s].converged = (ss == SLA_OK && sc.rr <= sc.stop) ? 1 : 0;
+      info[s].rel_residual = sc.bb > 0 ? std::sqrt(sc.rr_final / sc.bb) : 0.0;
+      info[s].converged = (ss == SLA_OK && sc.rr_final <= sc.stop) ? 1 : 0;
       info[s].status = ss;
+    }
+    if (state == ST_RUNNING && first == SLA_OK) {
+      set_error("CG loop ended with a system still running (internal error)");
+      first = SLA_ERR_DEVICE;
     }
     if (ss != SLA_OK && first == SLA_OK) first = ss;
   }
-  if (first != SLA_OK)
+  if (first == SLA_ERR_NOT_SPD || first == SLA_ERR_NONFINITE)
     set_error("CG stopped: %s", first == SLA_ERR_NOT_SPD ? "p.Ap <= 0 (matrix not SPD)"
                                                          : "non-finite value");
   return first;
+}
+
+// ---------------------------------------------------------------------------
+// Instrumentation: time each iteration kernel on its own
+// ---------------------------------------------------------------------------
+namespace {
+template <typename RP>
+sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st) {
+  const dim3 grid2(unsigned(A->grid), 1u);
+  const dim3 block(kIterBlock, 1u);
+  const void* fns[2] = {reinterpret_cast<const void*>(&k_cg_spmv<RP>),
+                        reinterpret_cast<const void*>(&k_cg_residual)};
+  const size_t ldss[2] = {lds_bytes(A), 0};
+  std::vector<hipEvent_t> ev(size_t(2 * reps), nullptr);
+  for (auto& e : ev) SLA_TRY_HIP(hipEventCreate(&e));
+  sla_status status = SLA_OK;
+  for (int k = 0; k < 2 && status == SLA_OK; ++k) {
+    void* args[1] = {&A->ctx_dev};
+    for (int64_t r = 0; r < reps; ++r) {
+      hipError_t e = hipExtLaunchKernel(fns[k], grid2, block, args, ldss[k], st, ev[2 * r],
+                                        ev[2 * r + 1], 0);
+      if (e != hipSuccess) {
+        set_error("timed launch failed: %s", hipGetErrorString(e));
+        status = SLA_ERR_DEVICE;
+        break;
+      }
+    }
+    if (status != SLA_OK) break;
+    if (hipStreamSynchronize(st) != hipSuccess) {
+      set_error("timed launch: synchronisation failed");
+      status = SLA_ERR_DEVICE;
+      break;
+    }
+    double total = 0.0;
+    for (int64_t r = 0; r < reps; ++r) {
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]);
+      total += ms;
+    }
+    avg_ms[k] = total / double(reps);
+  }
+  for (auto& e : ev)
+    if (e) (void)hipEventDestroy(e);
+  return status;
+}
+}  // namespace
+
+sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps, double* avg_ms,
+                           hipStream_t st) {
+  // a running solve (tol 0, no iteration limit in reach) advanced by one
+  // iteration, so that the timed SpMV steps include the deferred x update
+  const int64_t huge = int64_t(1) << 40;
+  SLA_TRY(ensure_workspace(A, 1));
+  fill_ctx(A, *A->ctx_host, b, x, 1, false);
+  SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
+  const dim3 grid2(unsigned(A->grid), 1u);
+  k_cg_init<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, 0);
+  k_cg_init_scalars<<<1u, kIterBlock, 0, st>>>(A->ctx_dev, 0.0, huge);
+  LAUNCH_CHECK();
+  if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, 1, st));
+  else SLA_TRY(enqueue_iteration<int64_t>(A, 1, st));
+  if (A->rp_idx == SLA_I32) return time_kernels<int32_t>(A, reps, avg_ms, st);
+  return time_kernels<int64_t>(A, reps, avg_ms, st);
 }
 
 }  // namespace sla

@@ -44,11 +44,17 @@ void dev_free(void* p);
 // ---------------------------------------------------------------------------
 // Launch geometry
 // ---------------------------------------------------------------------------
-constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
-constexpr int kTileRows = 256;   // rows per SpMV tile: one row per thread
 constexpr int kWave = 64;
-constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int64_t kLdsCapNnz = 4096;  // max staged slots per tile (48 KiB)
+constexpr int kBlock = 256;        // workgroup of the set-up kernels (4 waves)
+constexpr int kIterBlock = 1024;   // workgroup of the solver kernels (16 waves)
+constexpr int kWaves = kIterBlock / kWave;
+constexpr int kTileRows = 64;      // rows per wave tile: one row per lane
+constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
+// Staged (value, column) slots per wave tile: 16 waves x 336 slots x 12 B
+// stays under 64 KiB per workgroup, so two solver workgroups fit the LDS of a
+// CU; a 64-row tile of a 5-point stencil has at most 320 slots.
+constexpr int kWaveCap = 336;
+constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
 
 // Number of compute units of the current device (cached per device).
 int device_cus();
@@ -64,23 +70,27 @@ enum : int32_t {
   ST_NONFINITE = SLA_ERR_NONFINITE,
 };
 
-// Per-system CG scalars; they live on the device for the whole solve.
+// Per-system CG scalars, resident on the device for the whole solve.  An
+// iteration is two kernels, the SpMV step and the residual step.  Every field
+// is written by one of them (one thread of workgroup 0) and read only by the
+// other or by the host, so no workgroup ever reads a field that another
+// workgroup of the same launch may be writing.
 struct alignas(64) Scal {
-  double rr;      // r_k . r_k (recursive residual)
-  double bb;      // b . b
-  double stop;    // (tol * tol) * bb
-  double alpha;   // alpha of the last iteration whose SpMV phase finished
-  double beta;    // beta used to form the next search direction
-  int64_t it;     // completed iterations
-  int64_t maxit;
-  int32_t state;  // ST_*
-  int32_t x_lag;  // 1: x still lacks alpha * p(lag_buf)
-  int32_t lag_buf;
-  int32_t pad;
+  double rr[2];     // r_k . r_k, by parity of k          (SpMV step writes)
+  double alpha;     // alpha_k                              (residual step writes)
+  double bb;        // b . b                                (set-up)
+  double stop;      // (tol * tol) * bb                     (set-up)
+  double rr_final;  // r . r when the system stopped        (the stopping step)
+  int64_t ka;       // index of the next SpMV step          (residual step writes)
+  int64_t kr;       // index of the next residual step      (SpMV step writes)
+  int64_t it;       // completed iterations when stopped    (the stopping step)
+  int64_t maxit;    //                                      (set-up)
+  int32_t state_a;  // state as set by SpMV steps           (SpMV step writes)
+  int32_t state_r;  // state as set by residual steps       (residual step writes)
 };
 
-// Everything the iteration kernels touch, resident in device memory so that
-// a captured graph stays valid while the caller's x / b / values change.
+// Everything the solver kernels touch, resident in device memory so that a
+// captured graph stays valid while the caller's x / b / values change.
 struct Ctx {
   const void* rowptr;
   const int32_t* col;
@@ -90,9 +100,9 @@ struct Ctx {
   double* r;            // [batch][n]
   double* p[2];         // [batch][n] search direction, double-buffered
   double* q;            // [batch][n] A p
-  double* part_a;       // [batch][grid] partial p.q
-  double* part_b;       // [batch][grid] partial r.r
-  double* part_c;       // [batch][grid] partial b.b (set-up only)
+  // [batch][kPartSets][grid] one partial per workgroup:
+  //   set 0/1: r.r by parity of k, set 2/3: p.Ap by parity of k, set 4: b.b
+  double* part;
   Scal* scal;           // [batch]
   double* hist;         // [batch][hist_cap][3] alpha, beta, rr or nullptr
   int* n_running;       // systems still iterating
@@ -101,8 +111,8 @@ struct Ctx {
   int64_t nnz;
   int64_t batch;
   int64_t tiles;        // ceil(n / kTileRows)
-  int32_t grid;         // workgroups per system in the iteration kernels
-  int32_t lds_cap;      // staged slots per tile (0: read slots from memory)
+  int32_t grid;         // workgroups per system in the solver kernels
+  int32_t wave_cap;     // staged slots per wave tile (0: read slots from memory)
 };
 
 // ---------------------------------------------------------------------------
@@ -116,33 +126,43 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Sum over a workgroup of kBlock threads; valid in thread 0.  Fixed order.
-__device__ __forceinline__ double block_sum(double v, double* lds4) {
+// Sum over a workgroup of NT threads, fixed order, result in every thread.
+// `lds` holds NT / 64 doubles.
+template <int NT>
+__device__ __forceinline__ double block_sum_all(double v, double* lds) {
   v = wave_sum(v);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  if (lane == 0) lds4[w] = v;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = v;
   __syncthreads();
   double t = 0.0;
-  if (threadIdx.x == 0) t = (lds4[0] + lds4[1]) + (lds4[2] + lds4[3]);
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) t = t + lds[w];
   __syncthreads();
   return t;
 }
 
-// Tile range of workgroup `bid` of `grid`: the tiles are split into kXcds
-// contiguous ranges, one per XCD (workgroup i runs on XCD i % 8), and the
-// workgroups of one XCD interleave over its range, so that at any time the
-// workgroups of an XCD work on neighbouring rows and share its L2.
+// Make a wave's LDS writes visible to its other lanes (a wave tile is owned
+// by one wave, so no workgroup barrier is needed).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Tiles of wave `w` of workgroup `bid` (of `grid`, a multiple of kXcds): the
+// tiles are split into kXcds contiguous ranges, one per XCD (workgroup i runs
+// on XCD i % 8), and the waves of one XCD interleave over its range, so that
+// at any time they work on neighbouring rows and share that XCD's L2.
 struct TileWalk {
   int64_t first, stride, end;
 };
-__device__ __forceinline__ TileWalk tile_walk(int64_t tiles, int grid, int bid) {
+__device__ __forceinline__ TileWalk wave_walk(int64_t tiles, int grid, int bid, int waves,
+                                              int w) {
   const int xcd = bid % kXcds;
-  const int per_xcd = grid / kXcds;  // grid is a multiple of kXcds
+  const int per_xcd = grid / kXcds;
   const int slot = bid / kXcds;
   const int64_t lo = tiles * xcd / kXcds;
   const int64_t hi = tiles * (xcd + 1) / kXcds;
-  return TileWalk{lo + slot, per_xcd, hi};
+  return TileWalk{lo + int64_t(slot) * waves + w, int64_t(per_xcd) * waves, hi};
 }
 
 }  // namespace sla

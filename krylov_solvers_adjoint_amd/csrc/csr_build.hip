@@ -524,9 +524,9 @@ sla_status analyse_pattern(sla_csr A, hipStream_t st) {
   A->tiles = (A->n + kTileRows - 1) / kTileRows;
   if (A->rp_idx == SLA_I32) SLA_TRY(tile_stats<int32_t>(A, st));
   else SLA_TRY(tile_stats<int64_t>(A, st));
-  // stage a tile's slots in LDS when the largest tile fits; tiles above the
-  // cap read their slots straight from memory
-  A->lds_cap = int32_t(std::min<int64_t>(A->max_tile_nnz, kLdsCapNnz));
+  // stage a wave tile's slots in LDS up to the cap; tiles above it read
+  // their slots straight from memory
+  A->wave_cap = int32_t(std::min<int64_t>(A->max_tile_nnz, kWaveCap));
   return SLA_OK;
 }
 

@@ -21,9 +21,9 @@ struct sla_csr_s {
   int64_t* grp = nullptr;          // [nnz+1] first sorted position of each slot
 
   // pattern analysis
-  int64_t tiles = 0;           // ceil(n / kTileRows)
-  int64_t max_tile_nnz = 0;    // largest number of slots in one tile
-  int32_t lds_cap = 0;         // slots staged per tile (0 = none)
+  int64_t tiles = 0;           // ceil(n / kTileRows): 64-row wave tiles
+  int64_t max_tile_nnz = 0;    // largest number of slots in one wave tile
+  int32_t wave_cap = 0;        // slots staged per wave tile (0 = none)
 
   // bound values (borrowed)
   const double* vals = nullptr;
@@ -36,7 +36,7 @@ struct sla_csr_s {
   double* p0 = nullptr;
   double* p1 = nullptr;
   double* q = nullptr;
-  double* part = nullptr;      // 3 * ws_batch * grid
+  double* part = nullptr;      // kPartSets * ws_batch * grid
   sla::Scal* scal = nullptr;   // [ws_batch]
   int* n_running = nullptr;
   sla::Ctx* ctx_dev = nullptr;
@@ -67,6 +67,8 @@ sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda,
                                const double* x, double* grad_vals, hipStream_t stream);
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
                   uint32_t flags, sla_cg_info* info, hipStream_t stream);
+sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps,
+                           double* avg_ms, hipStream_t stream);
 
 // COO / CSR construction implemented in csr_build.hip
 sla_status build_from_coo(sla_csr A, sla_index coo_idx, const void* row,

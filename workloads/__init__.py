@@ -40,42 +40,63 @@ def poisson_nnz(N: int) -> int:
     return 5 * N * N - 4 * N
 
 
-def _poisson_slots(N: int):
-    """(n, 5) candidate columns and the mask of the ones inside the grid."""
-    n = N * N
-    idx_t = np.int64 if n >= 2**31 - N else np.int32
-    i = np.arange(n, dtype=idx_t)
-    a = i % N  # x position, 0-based
-    c = i // N  # y position, 0-based
-    cand = np.empty((n, 5), dtype=idx_t)
-    cand[:, 0] = i - N
-    cand[:, 1] = i - 1
-    cand[:, 2] = i
-    cand[:, 3] = i + 1
-    cand[:, 4] = i + N
-    mask = np.empty((n, 5), dtype=bool)
-    mask[:, 0] = c > 0
-    mask[:, 1] = a > 0
-    mask[:, 2] = True
-    mask[:, 3] = a < N - 1
-    mask[:, 4] = c < N - 1
-    return cand, mask
+def _grid_line(N: int, has_down: bool, has_up: bool, diag: float, off: float):
+    """Slots of one grid line of rows a = 0..N-1, in CSR order: column offsets
+    relative to the line's first unknown, values, and per-row counts."""
+    a = np.arange(N, dtype=np.int64)
+    kinds = []  # (present mask, column offset relative to the row, value)
+    if has_down:
+        kinds.append((np.ones(N, bool), -N, off))
+    kinds.append((a > 0, -1, off))
+    kinds.append((np.ones(N, bool), 0, diag))
+    kinds.append((a < N - 1, 1, off))
+    if has_up:
+        kinds.append((np.ones(N, bool), N, off))
+    counts = sum(m.astype(np.int64) for m, _, _ in kinds)
+    start = np.zeros(N, np.int64)
+    start[1:] = np.cumsum(counts)[:-1]
+    total = int(counts.sum())
+    col = np.empty(total, np.int64)
+    val = np.empty(total, np.float64)
+    pos = start.copy()
+    for m, o, v in kinds:
+        idx = pos[m]
+        col[idx] = a[m] + o
+        val[idx] = v
+        pos[m] += 1
+    return col, val, counts
 
 
 def poisson_csr(N: int, rowptr_dtype=np.int32, diag: float = 4.0, off: float = -1.0):
     """Closed-form CSR of the N x N 5-point Laplacian.
 
     Returns (rowptr[rowptr_dtype, n+1], col[int32, nnz], vals[float64, nnz]).
+    Every interior grid line has the same pattern relative to its first
+    unknown, so the matrix is assembled line by line from three templates.
     """
-    cand, mask = _poisson_slots(N)
-    counts = mask.sum(axis=1, dtype=np.int64)
-    rowptr = np.zeros(N * N + 1, dtype=np.int64)
-    np.cumsum(counts, out=rowptr[1:])
-    col = cand[mask].astype(np.int32, copy=False)
-    del cand
-    kind = np.broadcast_to(np.array([0, 0, 1, 0, 0], dtype=bool), mask.shape)[mask]
-    vals = np.where(kind, diag, off).astype(np.float64)
-    return rowptr.astype(rowptr_dtype), col, vals
+    n = N * N
+    if N == 1:
+        lines = [(_grid_line(1, False, False, diag, off), 1)]
+    else:
+        lines = [(_grid_line(N, False, True, diag, off), 1),
+                 (_grid_line(N, True, True, diag, off), N - 2),
+                 (_grid_line(N, True, False, diag, off), 1)]
+    cols, vals, counts = [], [], []
+    first = 0
+    for (c, v, k), reps in lines:
+        if reps == 0:
+            continue
+        bases = (np.arange(reps, dtype=np.int64) + first) * N
+        cols.append(np.add.outer(bases.astype(np.int32 if n < 2**31 else np.int64),
+                                 c.astype(np.int32 if n < 2**31 else np.int64)).ravel())
+        vals.append(np.tile(v, reps))
+        counts.append(np.tile(k, reps))
+        first += reps
+    col = np.concatenate(cols).astype(np.int32, copy=False)
+    vals = np.concatenate(vals)
+    rowptr = np.zeros(n + 1, dtype=np.int64)
+    np.cumsum(np.concatenate(counts), out=rowptr[1:])
+    return rowptr.astype(rowptr_dtype, copy=False), col, vals
 
 
 def poisson_coo(N: int):
