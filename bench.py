@@ -233,6 +233,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--skip-headline", action="store_true",
                     help="only the --sizes runs (for profiler passes); prints no JSON line")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy a 1 GiB fp64 tensor 5 times (a plain copy kernel of known "
+                         "size, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the solver path "
@@ -242,6 +245,18 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import krylov_solvers_adjoint_amd  # noqa: F401  (fails loudly without the HIP library)
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 27, dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        log(f"[bench] calibration copy: 1 GiB read + 1 GiB written per launch, "
+            f"{2 * src.numel() * 8 / dt / 1e9:.0f} GB/s")
+        del src, dst
     if args.skip_headline:
         for s in [s for s in args.sizes.split(",") if s]:
             import numpy as np
