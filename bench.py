@@ -53,6 +53,14 @@ def spmv_step_bytes(n: int, nnz: int, rp_bytes: int) -> int:
     return 12 * nnz + rp_bytes * (n + 1) + 48 * n
 
 
+def spmv_step_bytes_banded(n: int, nnz: int, rp_bytes: int) -> int:
+    """The same launch with the banded kernels: values once, one mask byte
+    per row and one row pointer per 64-row tile instead of the column array
+    and per-row row pointers."""
+    tiles = (n + 63) // 64
+    return 8 * nnz + n + rp_bytes * (tiles + 1) + 48 * n
+
+
 def pattern_grad_bytes(n: int, nnz: int, rp_bytes: int) -> int:
     return 12 * nnz + rp_bytes * (n + 1) + 16 * n
 
@@ -79,6 +87,9 @@ def traffic_from_profile(kernel: str, workload: str, digest: str):
     return float(m_t.group(1))
 
 
+CSR_ONLY = False  # --csr-only: force the plain CSR kernels
+
+
 def gpu_setup(N: int, rp_dtype):
     import numpy as np
     import torch
@@ -90,6 +101,8 @@ def gpu_setup(N: int, rp_dtype):
     log(f"[bench] generated Poisson {N}x{N}: n={N*N} nnz={len(col)} in {time.time()-t0:.1f}s")
     free0 = torch.cuda.mem_get_info()[0]
     P = K.sla_csr_create_from_csr(torch.from_numpy(rowptr).to(dev), torch.from_numpy(col).to(dev))
+    if CSR_ONLY:
+        P.set_spmv_variant("csr")
     v = torch.from_numpy(vals).to(dev)
     del rowptr, col
     return P, v, vals, free0
@@ -150,7 +163,8 @@ def bench_headline(args):
         kernel_ms=kern,
     )
     res["pct_peak"] = 100.0 * res["eff_GBps"] / HBM_PEAK_GBPS
-    res["spmv_bytes"] = spmv_step_bytes(n, nnz, 4)
+    res["banded"] = P.banded
+    res["spmv_bytes"] = (spmv_step_bytes_banded if res["banded"] else spmv_step_bytes)(n, nnz, 4)
     del P
     torch.cuda.synchronize()
     return res
@@ -176,7 +190,9 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int):
     free1 = torch.cuda.mem_get_info()[0]
     kern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
     nnz = P.nnz
-    out = dict(n=n, nnz=nnz, rowptr="i64" if rp_bytes == 8 else "i32",
+    banded = P.banded
+    sbytes = (spmv_step_bytes_banded if banded else spmv_step_bytes)(n, nnz, rp_bytes)
+    out = dict(n=n, nnz=nnz, rowptr="i64" if rp_bytes == 8 else "i32", banded=banded,
                iterations=info.iterations, solve_ms=1e3 * wall,
                ms_per_iteration=1e3 * wall / info.iterations,
                it_per_s=info.iterations / wall,
@@ -184,7 +200,7 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int):
                rel_residual=info.rel_residual,
                footprint_MB=(free0 - free1) / 2**20,
                kernel_ms=kern,
-               spmv_GBps=spmv_step_bytes(n, nnz, rp_bytes) / (kern["spmv_step"] * 1e-3) / 1e9)
+               spmv_GBps=sbytes / (kern["spmv_step"] * 1e-3) / 1e9)
     out["pct_peak"] = 100.0 * out["eff_GBps"] / HBM_PEAK_GBPS
     del P, v, b, x
     torch.cuda.synchronize()
@@ -233,6 +249,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--skip-headline", action="store_true",
                     help="only the --sizes runs (for profiler passes); prints no JSON line")
+    ap.add_argument("--csr-only", action="store_true",
+                    help="force the plain CSR kernels (no banded-pattern kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy a 1 GiB fp64 tensor 5 times (a plain copy kernel of known "
                          "size, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -241,6 +259,8 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the solver path "
               "is single-GPU; multi-GPU sharding is not part of this build.", file=sys.stderr)
         sys.exit(2)
+    global CSR_ONLY
+    CSR_ONLY = args.csr_only
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import krylov_solvers_adjoint_amd  # noqa: F401  (fails loudly without the HIP library)
@@ -287,7 +307,8 @@ def main():
     roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=achieved / HBM_PEAK_GBPS,
                     traffic=traffic_from_profile("k_cg_spmv", "poisson1000", digest),
-                    kernel="k_cg_spmv (SpMV + direction update + deferred x update + p.Ap)",
+                    kernel=("k_cg_spmv<banded> " if head["banded"] else "k_cg_spmv ") +
+                    "(SpMV + direction update + deferred x update + p.Ap)",
                     kernel_ms=spmv_ms, algorithmic_bytes=head["spmv_bytes"],
                     source_digest=digest)
     cpu = None
@@ -309,6 +330,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "poisson1000_fixed1000_fwd_adj", "grid": "1000x1000",
                    "n": head["n"], "nnz": head["nnz"], "index": "i32/i32",
+                   "spmv": "banded" if head["banded"] else "csr",
                    "iterations_fwd": head["iterations_fwd"],
                    "iterations_adj": head["iterations_adj"], "parallelism": "none (1 GPU)"},
         "eff_GBps": head["eff_GBps"],

@@ -204,6 +204,23 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x,
                                          int64_t reps, double* avg_ms_host,
                                          hipStream_t stream);
 
+/*
+ * SpMV kernel family.  At creation the pattern analysis checks whether every
+ * stored column j of every row i equals i + d for one of at most 8 fixed
+ * offsets d (a banded or stencil pattern such as the 5-point Laplacian); if
+ * so, the banded kernels can read a mask byte per row and one row pointer per
+ * 64 rows instead of the column array and per-row row pointers.
+ *   SLA_SPMV_AUTO (0, default): banded kernels when the pattern is banded and
+ *     its CSR arrays (12 bytes per slot) exceed the 256 MiB Infinity Cache, so
+ *     that the bytes saved are HBM bytes; otherwise the CSR kernels.
+ *   SLA_SPMV_CSR (1): always the CSR kernels.
+ *   SLA_SPMV_BANDED (2): the banded kernels whenever the pattern is banded.
+ * Results are bit-identical in every case.  *banded_host (may be NULL) tells
+ * whether the banded kernels are in use.
+ */
+enum { SLA_SPMV_AUTO = 0, SLA_SPMV_CSR = 1, SLA_SPMV_BANDED = 2 };
+sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* banded_host);
+
 /* Iterations per captured HIP graph block (default 32; 0 = launch kernels
  * one by one without graphs).  Affects speed only, never results. */
 sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);

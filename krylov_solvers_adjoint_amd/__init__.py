@@ -41,7 +41,8 @@ EXPORTS = [
     "sla_csr_pattern", "sla_csr_copy_pattern", "sla_csr_values_from_coo",
     "sla_csr_grad_to_coo", "sla_csr_set_values", "sla_spmv", "sla_cg_solve",
     "sla_cg_adjoint", "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
-    "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_graph_block",
+    "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_spmv_variant",
+    "sla_csr_set_graph_block",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -84,6 +85,7 @@ def _bind(lib):
         "sla_cg_history": [_P, _I64, _P, _P, _P, _I64, ctypes.POINTER(_I64)],
         "sla_profile_iteration_kernels": [_P, _P, _P, _I64, _P, _P],
         "sla_csr_set_graph_block": [_P, _I64],
+        "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -175,6 +177,7 @@ class CSRPattern:
         self.n, self.nnz, self.nnz_coo = n.value, nnz.value, m.value
         self.rowptr_dtype = torch.int32 if w.value == I32 else torch.int64
         self._bound = None
+        self._variant = 0
 
     @property
     def handle(self):
@@ -216,6 +219,21 @@ class CSRPattern:
 
     def set_graph_block(self, iterations: int):
         _check(_lib.sla_csr_set_graph_block(self._h, int(iterations)))
+
+    def set_spmv_variant(self, variant) -> bool:
+        """"auto" (default), "csr" or "banded" (see sla_csr_set_spmv_variant);
+        returns whether the banded kernels are now in use."""
+        b = _S()
+        self._variant = {"auto": 0, "csr": 1, "banded": 2}[variant]
+        _check(_lib.sla_csr_set_spmv_variant(self._h, self._variant, ctypes.byref(b)))
+        return bool(b.value)
+
+    @property
+    def banded(self) -> bool:
+        b = _S()
+        # query without changing: re-apply the current variant
+        _check(_lib.sla_csr_set_spmv_variant(self._h, self._variant, ctypes.byref(b)))
+        return bool(b.value)
 
     def history(self, system: int = 0, cap: int = 1 << 20):
         import numpy as np

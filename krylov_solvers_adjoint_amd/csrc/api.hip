@@ -88,6 +88,7 @@ static void destroy_handle(sla_csr A) {
   dev_free(A->perm);
   dev_free(A->sorted_idx);
   dev_free(A->grp);
+  dev_free(A->band_mask);
   delete A;
 }
 
@@ -377,6 +378,22 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x, 
           "sla_profile_iteration_kernels: NULL pointer");
   REQUIRE(reps >= 1 && reps <= 100000, "sla_profile_iteration_kernels: reps out of range");
   return profile_kernels(A, b, x, reps, avg_ms_host, stream);
+  API_END
+}
+
+sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* banded) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_set_spmv_variant: NULL handle");
+  REQUIRE(variant == SLA_SPMV_AUTO || variant == SLA_SPMV_CSR || variant == SLA_SPMV_BANDED,
+          "sla_csr_set_spmv_variant: unknown variant %d", variant);
+  if (variant != A->spmv_variant) {
+    (void)hipDeviceSynchronize();
+    release_workspace(A);  // the captured graphs hold the old kernels
+    A->spmv_variant = variant;
+  }
+  if (banded) *banded = use_band(A) ? 1 : 0;
+  return SLA_OK;
   API_END
 }
 

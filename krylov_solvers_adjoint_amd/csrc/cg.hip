@@ -64,11 +64,13 @@ namespace {
 // staging areas of `cap` slots.  Returns false for lanes past the last row.
 // Every lane of the wave must call it for the same tile.
 template <typename RP, typename G>
-__device__ __forceinline__ bool wave_tile_row(const RP* __restrict__ rowptr,
-                                              const int32_t* __restrict__ col,
-                                              const double* __restrict__ vals, int64_t n,
-                                              int64_t tile, int cap, double* lv, int32_t* lc,
-                                              G g, int64_t& row, double& acc) {
+__device__ __forceinline__ bool wave_tile_row(const RP* rowptr_, const int32_t* col_,
+                                              const double* vals_, int64_t n, int64_t tile,
+                                              int cap, double* lv, int32_t* lc, G g, int64_t& row,
+                                              double& acc) {
+  const SLA_GLOBAL RP* __restrict__ rowptr = gmem(rowptr_);
+  const SLA_GLOBAL int32_t* __restrict__ col = gmem(col_);
+  const SLA_GLOBAL double* __restrict__ vals = gmem(vals_);
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t r0 = tile * kTileRows;
   const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
@@ -83,12 +85,32 @@ __device__ __forceinline__ bool wave_tile_row(const RP* __restrict__ rowptr,
   }
   acc = 0.0;
   if (len <= cap) {
-    for (int64_t k = lane; k < len; k += kWave) {
-      lv[k] = vals[s0 + k];
-      lc[k] = col[s0 + k];
+    // a lane stages at most kStageLoads slots, in rounds of kStageRound
+    // whose loads are all issued before their LDS writes
+#pragma unroll
+    for (int j0 = 0; j0 < kStageLoads; j0 += kStageRound) {
+      double v[kStageRound];
+      int32_t cc[kStageRound];
+#pragma unroll
+      for (int j = 0; j < kStageRound; ++j) {
+        const int k = lane + (j0 + j) * kWave;
+        if (k < len) {
+          v[j] = vals[s0 + k];
+          cc[j] = col[s0 + k];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kStageRound; ++j) {
+        const int k = lane + (j0 + j) * kWave;
+        if (k < len) {
+          lv[k] = v[j];
+          lc[k] = cc[j];
+        }
+      }
     }
     wave_sync();
-    for (int64_t k = a - s0; k < e - s0; ++k) acc = acc + lv[k] * g(lc[k]);
+    const int k1 = int(e - s0);
+    for (int k = int(a - s0); k < k1; ++k) acc = acc + lv[k] * g(lc[k]);
     wave_sync();
   } else {
     for (int64_t k = a; k < e; ++k) acc = acc + vals[k] * g(col[k]);
@@ -96,22 +118,94 @@ __device__ __forceinline__ bool wave_tile_row(const RP* __restrict__ rowptr,
   return ok;
 }
 
-// This wave's LDS staging areas: 12 bytes per slot (value and column).
-__device__ __forceinline__ void wave_areas(double* lds_dyn, int cap, double*& lv, int32_t*& lc) {
+// Exclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_exclusive_sum(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += o;
+  }
+  return inc - v;
+}
+
+// The same row sum for a banded pattern: row i's slots are the columns
+// i + band.off[t] for the bits t of mask[i], in ascending t (= ascending
+// column, the CSR order).  The wave reads one row pointer per tile and one
+// mask byte per row instead of the column array and per-row row pointers;
+// slot positions come from a prefix sum of the rows' bit counts.  Only the
+// values are staged (8 bytes per slot).
+template <typename RP, typename G>
+__device__ __forceinline__ bool wave_tile_row_band(const RP* rowptr_, const uint8_t* mask_,
+                                                   const BandOffsets& band, const double* vals_,
+                                                   int64_t n, int64_t tile, int cap, double* lv,
+                                                   G g, int64_t& row, double& acc) {
+  const SLA_GLOBAL RP* __restrict__ rowptr = gmem(rowptr_);
+  const SLA_GLOBAL uint8_t* __restrict__ mask = gmem(mask_);
+  const SLA_GLOBAL double* __restrict__ vals = gmem(vals_);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r0 = tile * kTileRows;
+  const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
+  const int64_t s0 = rowptr[r0];
+  const int64_t len = int64_t(rowptr[r1]) - s0;
+  row = r0 + lane;
+  const bool ok = row < r1;
+  const unsigned m = ok ? unsigned(mask[row]) : 0u;
+  const int pre = wave_exclusive_sum(__builtin_popcount(m));
+  acc = 0.0;
+  if (len <= cap) {
+#pragma unroll
+    for (int j0 = 0; j0 < kStageLoads; j0 += kStageRound) {
+      double v[kStageRound];
+#pragma unroll
+      for (int j = 0; j < kStageRound; ++j) {
+        const int k = lane + (j0 + j) * kWave;
+        if (k < len) v[j] = vals[s0 + k];
+      }
+#pragma unroll
+      for (int j = 0; j < kStageRound; ++j) {
+        const int k = lane + (j0 + j) * kWave;
+        if (k < len) lv[k] = v[j];
+      }
+    }
+    wave_sync();
+    int k = pre;
+    for (int t = 0; t < band.count; ++t)
+      if ((m >> t) & 1u) {
+        acc = acc + lv[k] * g(row + band.off[t]);
+        ++k;
+      }
+    wave_sync();
+  } else {
+    int64_t k = s0 + pre;
+    for (int t = 0; t < band.count; ++t)
+      if ((m >> t) & 1u) {
+        acc = acc + vals[k] * g(row + band.off[t]);
+        ++k;
+      }
+  }
+  return ok;
+}
+
+// This wave's LDS staging areas: 12 bytes per slot (value and column), or 8
+// for a banded pattern (values only).
+__device__ __forceinline__ void wave_areas(double* lds_dyn, int cap, bool banded, double*& lv,
+                                           int32_t*& lc) {
   const int w = threadIdx.x / kWave;
-  lv = lds_dyn + int64_t(w) * (cap + (cap + 1) / 2);
+  lv = lds_dyn + int64_t(w) * (banded ? cap : cap + (cap + 1) / 2);
   lc = reinterpret_cast<int32_t*>(lv + cap);
 }
 
-size_t solver_lds_bytes(int cap, int waves) {
-  return size_t(waves) * size_t(cap + (cap + 1) / 2) * sizeof(double);
+size_t solver_lds_bytes(int cap, int waves, bool banded) {
+  return size_t(waves) * size_t(banded ? cap : cap + (cap + 1) / 2) * sizeof(double);
 }
 
 // Sum of `count` partials, the same fixed order in every workgroup: thread t
 // adds part[t], part[t + 1024], ..., then the workgroup tree.  The result is
 // in every thread.
-__device__ __forceinline__ double sum_partials_all(const double* __restrict__ part, int count,
-                                                   double* red) {
+__device__ __forceinline__ double sum_partials_all(const SLA_GLOBAL double* __restrict__ part,
+                                                   int count, double* red) {
   double v = 0.0;
   for (int i = threadIdx.x; i < count; i += kIterBlock) v = v + part[i];
   return block_sum_all<kIterBlock>(v, red);
@@ -120,9 +214,12 @@ __device__ __forceinline__ double sum_partials_all(const double* __restrict__ pa
 // ---------------------------------------------------------------------------
 // Standalone SpMV: y[s] = A_s x[s]
 // ---------------------------------------------------------------------------
-template <typename RP>
-__global__ __launch_bounds__(kIterBlock) void k_spmv(const RP* __restrict__ rowptr,
+template <typename RP, bool BANDED>
+__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+void k_spmv(const RP* __restrict__ rowptr,
                                                      const int32_t* __restrict__ col,
+                                                     const uint8_t* __restrict__ mask,
+                                                     BandOffsets band,
                                                      const double* __restrict__ vals, int64_t n,
                                                      int64_t nnz, int64_t tiles, int cap,
                                                      const double* __restrict__ x,
@@ -130,17 +227,19 @@ __global__ __launch_bounds__(kIterBlock) void k_spmv(const RP* __restrict__ rowp
   extern __shared__ double lds_dyn[];
   double* lv;
   int32_t* lc;
-  wave_areas(lds_dyn, cap, lv, lc);
+  wave_areas(lds_dyn, cap, BANDED, lv, lc);
   const int64_t s = blockIdx.y;
   const double* v = vals + s * nnz;
-  const double* xs = x + s * n;
-  double* ys = y + s * n;
+  const SLA_GLOBAL double* xs = gmem(x + s * n);
+  SLA_GLOBAL double* ys = gmem(y + s * n);
   auto g = [&](int64_t j) { return xs[j]; };
   const int w = threadIdx.x / kWave;
   for (int64_t t = int64_t(blockIdx.x) * kWaves + w; t < tiles; t += int64_t(gridDim.x) * kWaves) {
     int64_t i;
     double acc;
-    if (wave_tile_row<RP>(rowptr, col, v, n, t, cap, lv, lc, g, i, acc)) ys[i] = acc;
+    const bool ok = BANDED ? wave_tile_row_band<RP>(rowptr, mask, band, v, n, t, cap, lv, g, i, acc)
+                           : wave_tile_row<RP>(rowptr, col, v, n, t, cap, lv, lc, g, i, acc);
+    if (ok) ys[i] = acc;
   }
 }
 
@@ -153,11 +252,11 @@ __global__ __launch_bounds__(kIterBlock) void k_spmv(const RP* __restrict__ rowp
 __global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ c, int use_x0) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y, n = c->n;
-  const double* b = c->b + s * n;
-  double* x = c->x + s * n;
-  double* r = c->r + s * n;
-  double* pm = c->p[1] + s * n;
-  const double* q = c->q + s * n;
+  const SLA_GLOBAL double* b = gmem(c->b + s * n);
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
+  SLA_GLOBAL double* r = gmem(c->r + s * n);
+  SLA_GLOBAL double* pm = gmem(c->p[1] + s * n);
+  const SLA_GLOBAL double* q = gmem(c->q + s * n);
   const int lane = threadIdx.x & (kWave - 1);
   const TileWalk w = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, threadIdx.x / kWave);
   double bb = 0.0, rr = 0.0;
@@ -181,7 +280,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ 
   bb = block_sum_all<kIterBlock>(bb, red);
   rr = block_sum_all<kIterBlock>(rr, red);
   if (threadIdx.x == 0) {
-    double* part = c->part + s * kPartSets * c->grid;
+    SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * c->grid);
     part[4 * c->grid + blockIdx.x] = bb;
     part[0 * c->grid + blockIdx.x] = rr;
     if (blockIdx.x == 0 && s == 0) *c->n_running = 0;
@@ -192,7 +291,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
                                                                 double tol, int64_t maxit) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.x;
-  const double* part = c->part + s * kPartSets * c->grid;
+  const SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * c->grid);
   const double bb = sum_partials_all(part + 4 * c->grid, c->grid, red);
   const double rr = sum_partials_all(part + 0 * c->grid, c->grid, red);
   if (threadIdx.x == 0) {
@@ -215,8 +314,9 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
 }
 
 // SpMV step k (see the file comment).
-template <typename RP>
-__global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ c) {
+template <typename RP, bool BANDED>
+__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+void k_cg_spmv(const Ctx* __restrict__ c) {
   extern __shared__ double lds_dyn[];
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
@@ -228,7 +328,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ 
     return;
   }
   const int G = c->grid;
-  double* part = c->part + s * kPartSets * G;
+  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   const int64_t k = sc->ka;
   const double rr = sum_partials_all(part + (k & 1) * G, G, red);
   const bool lag = k > 0;  // x still lacks alpha_{k-1} p_{k-1}
@@ -253,7 +353,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ 
   }
   if (lead) {
     if (lag && stop != ST_NONFINITE && c->hist != nullptr && k - 1 < c->hist_cap) {
-      double* h = c->hist + (s * c->hist_cap + (k - 1)) * 3;
+      SLA_GLOBAL double* h = gmem(c->hist + (s * c->hist_cap + (k - 1)) * 3);
       h[0] = alpha;
       h[1] = beta;
       h[2] = rr;
@@ -268,8 +368,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ 
     }
   }
   const int64_t n = c->n;
-  const double* pold = c->p[(k + 1) & 1] + s * n;
-  double* x = c->x + s * n;
+  const SLA_GLOBAL double* pold = gmem(c->p[(k + 1) & 1] + s * n);
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
   const int w = threadIdx.x / kWave;
   const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, w);
   if (stop != ST_RUNNING) {
@@ -285,18 +385,30 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ 
   }
   const RP* rowptr = static_cast<const RP*>(c->rowptr);
   const double* vals = c->vals + s * c->nnz;
-  const double* r = c->r + s * n;
-  double* pnew = c->p[k & 1] + s * n;
-  double* q = c->q + s * n;
+  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  SLA_GLOBAL double* pnew = gmem(c->p[k & 1] + s * n);
+  SLA_GLOBAL double* q = gmem(c->q + s * n);
   double* lv;
   int32_t* lc;
-  wave_areas(lds_dyn, c->wave_cap, lv, lc);
+  wave_areas(lds_dyn, c->wave_cap, BANDED, lv, lc);
   auto g = [&](int64_t j) { return r[j] + beta * pold[j]; };
+  const BandOffsets band = c->band;
+  // plain row order, or the panel order for wide bands (see panel_tile)
+  const bool panels = c->panel > 0;
+  const int xcd = blockIdx.x % kXcds;
+  const int64_t lo = c->tiles * xcd / kXcds, hi = c->tiles * (xcd + 1) / kXcds;
+  const int64_t pend = panels ? panel_positions(hi - lo, c->panel, c->pblock) : wk.end - lo;
   double pq = 0.0;
-  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
+  for (int64_t pos = wk.first - lo; pos < pend; pos += wk.stride) {
+    const int64_t t = panels ? panel_tile(pos, lo, hi, c->panel, c->pblock) : lo + pos;
+    if (t < 0) continue;
     int64_t i;
     double acc;
-    if (wave_tile_row<RP>(rowptr, c->col, vals, n, t, c->wave_cap, lv, lc, g, i, acc)) {
+    const bool ok =
+        BANDED ? wave_tile_row_band<RP>(rowptr, c->mask, band, vals, n, t, c->wave_cap, lv, g, i,
+                                        acc)
+               : wave_tile_row<RP>(rowptr, c->col, vals, n, t, c->wave_cap, lv, lc, g, i, acc);
+    if (ok) {
       const double po = pold[i];
       const double pn = r[i] + beta * po;
       if (lag) x[i] = x[i] + alpha * po;
@@ -310,7 +422,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_spmv(const Ctx* __restrict__ 
 }
 
 // Residual step k (see the file comment).
-__global__ __launch_bounds__(kIterBlock) void k_cg_residual(const Ctx* __restrict__ c) {
+__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+void k_cg_residual(const Ctx* __restrict__ c) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
   Scal* sc = c->scal + s;
@@ -321,7 +434,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_residual(const Ctx* __restric
     return;
   }
   const int G = c->grid;
-  double* part = c->part + s * kPartSets * G;
+  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   const int64_t k = sc->kr;
   const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
   const double rr = sc->rr[k & 1];
@@ -344,8 +457,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_residual(const Ctx* __restric
     sc->ka = k + 1;
   }
   const int64_t n = c->n;
-  double* r = c->r + s * n;
-  const double* q = c->q + s * n;
+  SLA_GLOBAL double* r = gmem(c->r + s * n);
+  const SLA_GLOBAL double* q = gmem(c->q + s * n);
   const int lane = threadIdx.x & (kWave - 1);
   const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, threadIdx.x / kWave);
   double rn = 0.0;
@@ -378,9 +491,9 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
   const int lane = threadIdx.x & (kWave - 1);
   uint8_t* rowmap = reinterpret_cast<uint8_t*>(lds_dyn) + int64_t(w) * cap;
   const int64_t s = blockIdx.y;
-  const double* l = lambda + s * n;
-  const double* xs = x + s * n;
-  double* gs = grad + s * nnz;
+  const SLA_GLOBAL double* l = gmem(lambda + s * n);
+  const SLA_GLOBAL double* xs = gmem(x + s * n);
+  SLA_GLOBAL double* gs = gmem(grad + s * nnz);
   for (int64_t t = int64_t(blockIdx.x) * kWaves + w; t < tiles; t += int64_t(gridDim.x) * kWaves) {
     const int64_t r0 = t * kTileRows;
     const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
@@ -403,12 +516,13 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
   }
 }
 
-size_t lds_bytes(const sla_csr A) { return solver_lds_bytes(A->wave_cap, kWaves); }
+size_t lds_bytes(const sla_csr A) { return solver_lds_bytes(A->wave_cap, kWaves, use_band(A)); }
 
 template <typename RP>
 sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
-  k_cg_spmv<RP><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  if (use_band(A)) k_cg_spmv<RP, true><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  else k_cg_spmv<RP, false><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
   k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
   LAUNCH_CHECK();
   return SLA_OK;
@@ -484,6 +598,10 @@ void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool
   c.tiles = A->tiles;
   c.grid = A->grid;
   c.wave_cap = A->wave_cap;
+  c.mask = use_band(A) ? A->band_mask : nullptr;
+  c.band = A->band;
+  c.panel = A->panel;
+  c.pblock = A->pblock;
 }
 
 // Workgroups for a one-pass kernel over `tiles` wave tiles and `batch` systems.
@@ -494,6 +612,14 @@ unsigned plain_grid(int64_t tiles, int64_t batch) {
 }
 
 }  // namespace
+
+bool use_band(const sla_csr A) {
+  if (A->band_mask == nullptr || A->spmv_variant == SLA_SPMV_CSR) return false;
+  if (A->spmv_variant == SLA_SPMV_BANDED) return true;
+  // automatic: only when the CSR arrays stream from HBM rather than staying
+  // in the Infinity Cache, i.e. when the bytes saved are HBM bytes
+  return double(A->nnz) * 12.0 > double(kInfinityCacheBytes);
+}
 
 // ---------------------------------------------------------------------------
 // Workspace
@@ -562,12 +688,16 @@ sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const doubl
                        hipStream_t st) {
   const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
   const size_t lds = lds_bytes(A);
-  if (A->rp_idx == SLA_I32)
-    k_spmv<int32_t><<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, vals, A->n,
-                                                   A->nnz, A->tiles, A->wave_cap, x, y);
-  else
-    k_spmv<int64_t><<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, vals, A->n,
-                                                   A->nnz, A->tiles, A->wave_cap, x, y);
+  const bool bd = use_band(A);
+  if (A->rp_idx == SLA_I32) {
+    auto k = bd ? k_spmv<int32_t, true> : k_spmv<int32_t, false>;
+    k<<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->band_mask, A->band,
+                                     vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y);
+  } else {
+    auto k = bd ? k_spmv<int64_t, true> : k_spmv<int64_t, false>;
+    k<<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->band_mask, A->band,
+                                     vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y);
+  }
   LAUNCH_CHECK();
   return SLA_OK;
 }
@@ -669,7 +799,8 @@ template <typename RP>
 sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), 1u);
   const dim3 block(kIterBlock, 1u);
-  const void* fns[2] = {reinterpret_cast<const void*>(&k_cg_spmv<RP>),
+  const void* fns[2] = {use_band(A) ? reinterpret_cast<const void*>(&k_cg_spmv<RP, true>)
+                                    : reinterpret_cast<const void*>(&k_cg_spmv<RP, false>),
                         reinterpret_cast<const void*>(&k_cg_residual)};
   const size_t ldss[2] = {lds_bytes(A), 0};
   std::vector<hipEvent_t> ev(size_t(2 * reps), nullptr);

@@ -48,13 +48,28 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;        // workgroup of the set-up kernels (4 waves)
 constexpr int kIterBlock = 1024;   // workgroup of the solver kernels (16 waves)
 constexpr int kWaves = kIterBlock / kWave;
+// two solver workgroups per CU: 8 waves on each of its 4 SIMDs, which caps a
+// kernel at 64 VGPRs
+constexpr int kWavesPerEu = 2 * kWaves / 4;
 constexpr int kTileRows = 64;      // rows per wave tile: one row per lane
 constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
 // Staged (value, column) slots per wave tile: 16 waves x 336 slots x 12 B
 // stays under 64 KiB per workgroup, so two solver workgroups fit the LDS of a
 // CU; a 64-row tile of a 5-point stencil has at most 320 slots.
 constexpr int kWaveCap = 336;
+constexpr int kStageLoads = (kWaveCap + kWave - 1) / kWave;  // staged slots per lane
+constexpr int kStageRound = 3;     // staged slots whose loads are in flight together
 constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
+constexpr int kMaxBand = 8;        // most distinct column offsets of a banded pattern
+constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;  // MI355X last-level cache
+constexpr int kPanelTiles = 64;    // widest column block of the panel tile order
+
+// Column offsets j - i of a banded pattern, ascending: row i's slots are the
+// columns i + off[t] for the bits t set in its mask byte.
+struct BandOffsets {
+  int32_t count;
+  int32_t off[kMaxBand];
+};
 
 // Number of compute units of the current device (cached per device).
 int device_cus();
@@ -113,11 +128,25 @@ struct Ctx {
   int64_t tiles;        // ceil(n / kTileRows)
   int32_t grid;         // workgroups per system in the solver kernels
   int32_t wave_cap;     // staged slots per wave tile (0: read slots from memory)
+  const uint8_t* mask;  // [n] band masks, or nullptr (plain CSR)
+  BandOffsets band;
+  int32_t panel;        // tiles per band span (0: rows in plain order)
+  int32_t pblock;       // tiles per column block of the panel order
 };
 
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
+
+// Global-memory view of a pointer.  Pointers read from the device-resident
+// context are generic to the compiler, which then emits flat loads; a flat
+// load counts against both the vector-memory and the LDS counters, so every
+// LDS access after it waits for it.  All buffers here are global memory.
+#define SLA_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ SLA_GLOBAL T* gmem(T* p) {
+  return (SLA_GLOBAL T*)(p);
+}
 __device__ __forceinline__ double wave_sum(double v) {
   // butterfly over the 64 lanes; every lane ends with the same total, and
   // the association order is fixed, so results are reproducible
@@ -163,6 +192,32 @@ __device__ __forceinline__ TileWalk wave_walk(int64_t tiles, int grid, int bid, 
   const int64_t lo = tiles * xcd / kXcds;
   const int64_t hi = tiles * (xcd + 1) / kXcds;
   return TileWalk{lo + int64_t(slot) * waves + w, int64_t(per_xcd) * waves, hi};
+}
+
+// Tile order of one XCD's range [lo, hi) for a banded pattern whose
+// neighbours lie up to `panel` tiles away: the range is cut into panels of
+// `panel` tiles, and position p walks column blocks of `pblock` tiles down
+// all panels before moving to the next block, so a tile and its neighbours
+// one panel up and down are in flight together and share the L2.  Returns -1
+// for positions that fall past the end of a panel or of the range.
+__device__ __forceinline__ int64_t panel_tile(int64_t p, int64_t lo, int64_t hi, int panel,
+                                              int pblock) {
+  const int64_t V = (hi - lo + panel - 1) / panel;
+  const int64_t per_blk = V * pblock;
+  const int64_t blk = p / per_blk;
+  const int64_t rem = p - blk * per_blk;
+  const int64_t v = rem / pblock;
+  const int64_t u = blk * pblock + (rem - v * pblock);
+  if (u >= panel) return -1;
+  const int64_t t = lo + v * panel + u;
+  return t < hi ? t : -1;
+}
+
+// Number of positions panel_tile walks for a range of `cnt` tiles.
+__device__ __forceinline__ int64_t panel_positions(int64_t cnt, int panel, int pblock) {
+  const int64_t V = (cnt + panel - 1) / panel;
+  const int64_t nb = (panel + pblock - 1) / pblock;
+  return nb * V * pblock;
 }
 
 }  // namespace sla

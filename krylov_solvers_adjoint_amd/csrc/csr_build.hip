@@ -499,6 +499,118 @@ sla_status coo_build(sla_csr A, const CI* row, const CI* col, hipStream_t st) {
   return SLA_OK;
 }
 
+// Band verification: every slot (i, j) of row i must have j - i in the
+// candidate offsets off[0..noff) (ascending); mask[i] gets bit t for offset t.
+// Columns are strictly increasing inside a row (validated), so the slots of a
+// row are exactly its set bits in ascending order.  Any other slot clears
+// *ok, and the plain CSR kernels are used.
+template <typename RP>
+__global__ void k_band_masks(int64_t n, const RP* __restrict__ rowptr,
+                             const int32_t* __restrict__ col, BandOffsets bo,
+                             uint8_t* __restrict__ mask, int* __restrict__ ok) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    unsigned m = 0;
+    int prev = -1;
+    bool good = true;
+    for (int64_t k = rowptr[i]; k < int64_t(rowptr[i + 1]); ++k) {
+      const int64_t d = int64_t(col[k]) - i;
+      int t = -1;
+      for (int u = 0; u < bo.count; ++u)
+        if (int64_t(bo.off[u]) == d) t = u;
+      if (t <= prev) {
+        good = false;
+        break;
+      }
+      m |= 1u << t;
+      prev = t;
+    }
+    if (!good) atomicAnd(ok, 0);
+    mask[i] = uint8_t(m);
+  }
+}
+
+// Candidate band offsets from 64 samples of 64 consecutive rows spread over
+// the matrix (a heuristic: the device pass verifies every slot).  Returns
+// false when the samples already show more than kMaxBand offsets.
+template <typename RP>
+bool sample_offsets(sla_csr A, hipStream_t st, BandOffsets* bo) {
+  const int64_t n = A->n;
+  std::vector<int64_t> offs;
+  const int64_t samples = 64, rows = 64;
+  for (int64_t sidx = 0; sidx < samples; ++sidx) {
+    const int64_t r0 = std::min<int64_t>(n - 1, (n - 1) * sidx / std::max<int64_t>(1, samples - 1));
+    const int64_t r1 = std::min<int64_t>(n, r0 + rows);
+    std::vector<RP> rp(size_t(r1 - r0 + 1));
+    if (hipMemcpyAsync(rp.data(), (const RP*)A->rowptr + r0, sizeof(RP) * rp.size(),
+                       hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return false;
+    const int64_t k0 = rp.front(), k1 = rp.back();
+    if (k1 <= k0) continue;
+    std::vector<int32_t> cc(size_t(k1 - k0));
+    if (hipMemcpyAsync(cc.data(), A->col + k0, sizeof(int32_t) * cc.size(),
+                       hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return false;
+    for (int64_t i = r0; i < r1; ++i)
+      for (int64_t k = rp[i - r0]; k < int64_t(rp[i - r0 + 1]); ++k) {
+        const int64_t d = int64_t(cc[k - k0]) - i;
+        if (std::find(offs.begin(), offs.end(), d) == offs.end()) offs.push_back(d);
+        if (int(offs.size()) > kMaxBand) return false;
+      }
+  }
+  if (offs.empty()) return false;
+  std::sort(offs.begin(), offs.end());
+  bo->count = int32_t(offs.size());
+  for (int u = 0; u < bo->count; ++u) bo->off[u] = int32_t(offs[u]);
+  return true;
+}
+
+template <typename RP>
+sla_status detect_band(sla_csr A, hipStream_t st) {
+  A->band.count = 0;
+  BandOffsets bo{};
+  if (A->nnz == 0 || !sample_offsets<RP>(A, st, &bo)) return SLA_OK;
+  uint8_t* mask = nullptr;
+  int* ok = nullptr;
+  SLA_TRY(dev_alloc(&mask, A->n, "band masks"));
+  sla_status s = dev_alloc(&ok, 1, "band flag");
+  int h = 0;
+  if (s == SLA_OK) {
+    const int one = 1;
+    hipError_t e = hipMemcpyAsync(ok, &one, sizeof(int), hipMemcpyHostToDevice, st);
+    k_band_masks<RP><<<grid_for(A->n), kBlock, 0, st>>>(A->n, (const RP*)A->rowptr, A->col, bo,
+                                                         mask, ok);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(&h, ok, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      set_error("band detection failed: %s", hipGetErrorString(e));
+      s = SLA_ERR_DEVICE;
+    }
+  }
+  dev_free(ok);
+  if (s != SLA_OK || !h) {
+    dev_free(mask);
+    return s;
+  }
+  A->band_mask = mask;
+  A->band = bo;
+  // panel order when the band reaches further than kPanelTiles tiles: column
+  // blocks of at most kPanelTiles tiles (equal widths) across panels of
+  // ceil(span / 64) tiles
+  int64_t span = 0;
+  for (int u = 0; u < bo.count; ++u) span = std::max<int64_t>(span, std::abs(int64_t(bo.off[u])));
+  const int64_t P = (span + kTileRows - 1) / kTileRows;
+  if (P > kPanelTiles) {
+    const int64_t nb = (P + kPanelTiles - 1) / kPanelTiles;
+    A->panel = int32_t(P);
+    A->pblock = int32_t((P + nb - 1) / nb);
+  }
+  return SLA_OK;
+}
+
 template <typename RP>
 sla_status tile_stats(sla_csr A, hipStream_t st) {
   unsigned long long* d = nullptr;
@@ -527,6 +639,10 @@ sla_status analyse_pattern(sla_csr A, hipStream_t st) {
   // stage a wave tile's slots in LDS up to the cap; tiles above it read
   // their slots straight from memory
   A->wave_cap = int32_t(std::min<int64_t>(A->max_tile_nnz, kWaveCap));
+  if (!A->no_band) {
+    if (A->rp_idx == SLA_I32) SLA_TRY(detect_band<int32_t>(A, st));
+    else SLA_TRY(detect_band<int64_t>(A, st));
+  }
   return SLA_OK;
 }
 

@@ -24,6 +24,14 @@ struct sla_csr_s {
   int64_t tiles = 0;           // ceil(n / kTileRows): 64-row wave tiles
   int64_t max_tile_nnz = 0;    // largest number of slots in one wave tile
   int32_t wave_cap = 0;        // slots staged per wave tile (0 = none)
+  // banded patterns (every column j = i + one of a few offsets): a mask
+  // byte per row replaces the column array and per-row row pointers
+  uint8_t* band_mask = nullptr;  // [n] or nullptr
+  sla::BandOffsets band{};
+  bool no_band = false;          // pattern analysis skips band detection
+  int spmv_variant = SLA_SPMV_AUTO;  // SLA_SPMV_AUTO / _CSR / _BANDED
+  int32_t panel = 0;             // panel order of the SpMV tiles (0 = rows in order)
+  int32_t pblock = 0;
 
   // bound values (borrowed)
   const double* vals = nullptr;
@@ -58,6 +66,7 @@ namespace sla {
 
 // Workspace and launch helpers implemented in cg.hip
 sla_status ensure_workspace(sla_csr A, int64_t batch);
+bool use_band(const sla_csr A);  // banded SpMV kernels for this handle?
 void release_workspace(sla_csr A);
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 

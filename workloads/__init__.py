@@ -28,6 +28,7 @@ import numpy as np
 __all__ = [
     "poisson_n", "poisson_nnz", "poisson_csr", "poisson_coo", "manufactured",
     "uniform_rhs", "normal_rhs", "batched_poisson", "rgg_coo", "shuffled_coo",
+    "stencil_csr", "laplacian3d_csr", "nine_point_csr",
     "CONFIGS",
 ]
 
@@ -97,6 +98,53 @@ def poisson_csr(N: int, rowptr_dtype=np.int32, diag: float = 4.0, off: float = -
     rowptr = np.zeros(n + 1, dtype=np.int64)
     np.cumsum(np.concatenate(counts), out=rowptr[1:])
     return rowptr.astype(rowptr_dtype, copy=False), col, vals
+
+
+def stencil_csr(shape, stencil, rowptr_dtype=np.int32):
+    """CSR of a constant-coefficient stencil on a box grid with a zero
+    Dirichlet boundary: `stencil` maps a displacement tuple (x fastest) to
+    its value.  Columns come out ascending.  Small grids only (tests)."""
+    dims = len(shape)
+    n = int(np.prod(shape))
+    idx = np.arange(n)
+    coords = []
+    rem = idx.copy()
+    for d in range(dims):
+        coords.append(rem % shape[d])
+        rem //= shape[d]
+    strides = np.cumprod([1] + list(shape[:-1]))
+    entries = []
+    for disp, v in stencil.items():
+        ok = np.ones(n, bool)
+        for d in range(dims):
+            ok &= (coords[d] + disp[d] >= 0) & (coords[d] + disp[d] < shape[d])
+        off = int(sum(disp[d] * strides[d] for d in range(dims)))
+        entries.append((idx[ok], idx[ok] + off, np.full(ok.sum(), v, np.float64)))
+    row = np.concatenate([e[0] for e in entries])
+    col = np.concatenate([e[1] for e in entries])
+    val = np.concatenate([e[2] for e in entries])
+    order = np.lexsort((col, row))
+    row, col, val = row[order], col[order], val[order]
+    rowptr = np.zeros(n + 1, np.int64)
+    np.add.at(rowptr, row + 1, 1)
+    return np.cumsum(rowptr).astype(rowptr_dtype), col.astype(np.int32), val
+
+
+def laplacian3d_csr(N: int):
+    """7-point Laplacian on an N^3 grid: diagonal 6, neighbours -1."""
+    st = {(0, 0, 0): 6.0}
+    for d in range(3):
+        for s_ in (-1, 1):
+            disp = [0, 0, 0]
+            disp[d] = s_
+            st[tuple(disp)] = -1.0
+    return stencil_csr((N, N, N), st)
+
+
+def nine_point_csr(N: int):
+    """9-point Laplacian on an N^2 grid: diagonal 8, the 8 neighbours -1."""
+    st = {(a, b): (8.0 if a == 0 and b == 0 else -1.0) for a in (-1, 0, 1) for b in (-1, 0, 1)}
+    return stencil_csr((N, N), st)
 
 
 def poisson_coo(N: int):
