@@ -61,6 +61,17 @@ def spmv_step_bytes_banded(n: int, nnz: int, rp_bytes: int) -> int:
     return 8 * nnz + n + rp_bytes * (tiles + 1) + 48 * n
 
 
+def spmv_step_bytes_split(n: int, nnz: int, rp_bytes: int) -> int:
+    """The SpMV step as two launches for wide-column patterns: the direction
+    pass reads r, p_{k-1}, x and writes p_k, x (40 n); the product pass reads
+    the matrix once and p_k, and writes q."""
+    return 40 * n + 12 * nnz + rp_bytes * (n + 1) + 16 * n
+
+
+def spmv_variant(P) -> str:
+    return "split" if P.split else ("banded" if P.banded else "csr")
+
+
 def pattern_grad_bytes(n: int, nnz: int, rp_bytes: int) -> int:
     return 12 * nnz + rp_bytes * (n + 1) + 16 * n
 
@@ -208,6 +219,60 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int):
     return out
 
 
+def bench_rgg(n: int, kernel_reps: int):
+    """Random geometric graph Laplacian + 0.01 I (4M nodes, ~9 slots per row,
+    random node order): CSR built on the GPU from COO, then CG to 1e-8 and the
+    adjoint to 1e-8."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    row, col, val, _ = W.rgg_coo(n, 4, 5)
+    b = torch.from_numpy(W.normal_rhs(n, 6)).to(dev)
+    g = torch.from_numpy(W.normal_rhs(n, 7)).to(dev)
+    log(f"[bench] generated RGG n={n} triplets={row.shape[0]} in {time.time()-t0:.1f}s")
+    rt = torch.from_numpy(row.astype(np.int32)).to(dev)
+    ct = torch.from_numpy(col.astype(np.int32)).to(dev)
+    vt = torch.from_numpy(val).to(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    P = K.sla_csr_create(n, rt, ct)
+    v = K.sla_csr_values_from_coo(P, vt)
+    torch.cuda.synchronize()
+    build_ms = 1e3 * (time.perf_counter() - t0)
+    if CSR_ONLY:
+        P.set_spmv_variant("csr")
+    K.sla_cg_solve(P, v, b, 1e-8, 50)  # warm-up (graph capture)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x, fi = K.sla_cg_solve(P, v, b, 1e-8, 20000)
+    torch.cuda.synchronize()
+    fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    gb, gv, ai = K.sla_cg_adjoint(P, v, x, g, 1e-8, 20000)
+    torch.cuda.synchronize()
+    adj = time.perf_counter() - t0
+    kern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
+    nnz = P.nnz
+    its = fi.iterations + ai.iterations
+    step_bytes = (spmv_step_bytes_split if P.split else spmv_step_bytes)(n, nnz, 4)
+    out = dict(n=n, nnz=nnz, spmv=spmv_variant(P), csr_build_ms=build_ms,
+               iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
+               solve_ms=1e3 * fwd, adjoint_ms=1e3 * adj,
+               it_per_s=its / (fwd + adj),
+               eff_GBps=(its * canonical_bytes(n, nnz, 4) + pattern_grad_bytes(n, nnz, 4)) /
+               (fwd + adj) / 1e9,
+               kernel_ms=kern,
+               spmv_GBps=step_bytes / (kern["spmv_step"] * 1e-3) / 1e9)
+    out["pct_peak"] = 100.0 * out["eff_GBps"] / HBM_PEAK_GBPS
+    del P, v, b, g, x, gb, gv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(seconds: float):
     """The oracle as it stands, on a bounded sample of the same workload:
     forward and adjoint CG on the 1000 x 1000 Poisson system, k fixed
@@ -242,8 +307,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--sizes", default="16m,169m",
-                    help="extra sizes solved for 500 fixed iterations ('' for none)")
+    ap.add_argument("--sizes", default="16m,169m,rgg4m",
+                    help="extra workloads: 16m / 169m (Poisson, 500 fixed iterations), rgg4m "
+                         "(random geometric graph, tol 1e-8 forward + adjoint); '' for none")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -280,6 +346,10 @@ def main():
     if args.skip_headline:
         for s in [s for s in args.sizes.split(",") if s]:
             import numpy as np
+            if s.lower() == "rgg4m":
+                out = bench_rgg(4_000_000, args.kernel_reps)
+                log(f"[bench] rgg4m: {out}")
+                continue
             N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
                      "169m": (13000, np.int64)}[s.lower()]
             out = bench_size(N, rp, 500, args.kernel_reps)
@@ -294,6 +364,13 @@ def main():
     sizes = {}
     for s in [s for s in args.sizes.split(",") if s]:
         import numpy as np
+        if s.lower() == "rgg4m":
+            log("[bench] size rgg4m: random geometric graph, 4M nodes, tol 1e-8 fwd + adj")
+            sizes["rgg4m"] = bench_rgg(4_000_000, args.kernel_reps)
+            log(f"[bench] size rgg4m: {sizes['rgg4m']['iterations_fwd']}+"
+                f"{sizes['rgg4m']['iterations_adj']} iterations, "
+                f"{sizes['rgg4m']['it_per_s']:.0f} it/s, {sizes['rgg4m']['eff_GBps']:.0f} GB/s")
+            continue
         N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
                  "169m": (13000, np.int64)}[s.lower()]
         log(f"[bench] size {s}: Poisson {N}x{N}, 500 fixed iterations")

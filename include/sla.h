@@ -215,11 +215,17 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x,
  *     that the bytes saved are HBM bytes; otherwise the CSR kernels.
  *   SLA_SPMV_CSR (1): always the CSR kernels.
  *   SLA_SPMV_BANDED (2): the banded kernels whenever the pattern is banded.
- * Results are bit-identical in every case.  *banded_host (may be NULL) tells
- * whether the banded kernels are in use.
+ *   SLA_SPMV_SPLIT (3): the CSR kernels with the search-direction update in a
+ *     pass of its own, so that the SpMV gathers one vector instead of two;
+ *     AUTO picks it for non-banded patterns whose 64-row tiles reach columns
+ *     more than 2^17 apart (no reuse of gathered values from cache).
+ * SpMV results are bit-identical in every case; CG results are identical
+ * between AUTO, CSR and BANDED, and differ only in the order of the p.Ap
+ * partial sums under SPLIT.  *kernels_host (may be NULL) receives the family
+ * now in use: 0 CSR, 1 banded, 2 CSR with the separate direction pass.
  */
-enum { SLA_SPMV_AUTO = 0, SLA_SPMV_CSR = 1, SLA_SPMV_BANDED = 2 };
-sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* banded_host);
+enum { SLA_SPMV_AUTO = 0, SLA_SPMV_CSR = 1, SLA_SPMV_BANDED = 2, SLA_SPMV_SPLIT = 3 };
+sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels_host);
 
 /* Iterations per captured HIP graph block (default 32; 0 = launch kernels
  * one by one without graphs).  Affects speed only, never results. */

@@ -220,20 +220,26 @@ class CSRPattern:
     def set_graph_block(self, iterations: int):
         _check(_lib.sla_csr_set_graph_block(self._h, int(iterations)))
 
-    def set_spmv_variant(self, variant) -> bool:
-        """"auto" (default), "csr" or "banded" (see sla_csr_set_spmv_variant);
-        returns whether the banded kernels are now in use."""
+    def _kernels(self) -> int:
         b = _S()
-        self._variant = {"auto": 0, "csr": 1, "banded": 2}[variant]
         _check(_lib.sla_csr_set_spmv_variant(self._h, self._variant, ctypes.byref(b)))
-        return bool(b.value)
+        return b.value
+
+    def set_spmv_variant(self, variant) -> bool:
+        """"auto" (default), "csr", "banded" or "split" (see sla_csr_set_spmv_variant);
+        returns whether the banded kernels are now in use."""
+        self._variant = {"auto": 0, "csr": 1, "banded": 2, "split": 3}[variant]
+        return self._kernels() == 1
+
+    @property
+    def split(self) -> bool:
+        """Whether the separate search-direction pass is in use."""
+        return self._kernels() == 2
 
     @property
     def banded(self) -> bool:
-        b = _S()
-        # query without changing: re-apply the current variant
-        _check(_lib.sla_csr_set_spmv_variant(self._h, self._variant, ctypes.byref(b)))
-        return bool(b.value)
+        """Whether the banded kernels are in use."""
+        return self._kernels() == 1
 
     def history(self, system: int = 0, cap: int = 1 << 20):
         import numpy as np

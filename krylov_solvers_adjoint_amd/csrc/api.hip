@@ -381,18 +381,18 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x, 
   API_END
 }
 
-sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* banded) {
+sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels) {
   API_BEGIN
   clear_error();
   REQUIRE(A != nullptr, "sla_csr_set_spmv_variant: NULL handle");
-  REQUIRE(variant == SLA_SPMV_AUTO || variant == SLA_SPMV_CSR || variant == SLA_SPMV_BANDED,
+  REQUIRE(variant >= SLA_SPMV_AUTO && variant <= SLA_SPMV_SPLIT,
           "sla_csr_set_spmv_variant: unknown variant %d", variant);
   if (variant != A->spmv_variant) {
     (void)hipDeviceSynchronize();
     release_workspace(A);  // the captured graphs hold the old kernels
     A->spmv_variant = variant;
   }
-  if (banded) *banded = use_band(A) ? 1 : 0;
+  if (kernels) *kernels = use_split(A) ? 2 : (use_band(A) ? 1 : 0);
   return SLA_OK;
   API_END
 }

@@ -60,9 +60,13 @@ namespace {
   } while (0)
 
 // Row sum of one lane's row in a wave tile: acc = sum_k vals[k] * g(col[k])
-// in ascending slot order, starting from 0.  `lv`/`lc` are this wave's LDS
-// staging areas of `cap` slots.  Returns false for lanes past the last row.
-// Every lane of the wave must call it for the same tile.
+// in ascending slot order, starting from 0.  The tile's slots
+// [rowptr[r0], rowptr[r1]) are contiguous: the wave stages them into its LDS
+// areas `lv`/`lc` (`cap` slots) with coalesced loads, in as many chunks as
+// the tile needs, and each lane adds the slots of its row that fall into the
+// chunk; the ascending order of every row's sum is kept across chunks.
+// Returns false for lanes past the last row.  Every lane of the wave must
+// call it for the same tile.
 template <typename RP, typename G>
 __device__ __forceinline__ bool wave_tile_row(const RP* rowptr_, const int32_t* col_,
                                               const double* vals_, int64_t n, int64_t tile,
@@ -80,11 +84,12 @@ __device__ __forceinline__ bool wave_tile_row(const RP* rowptr_, const int32_t* 
   const bool ok = row < r1;
   int64_t a = 0, e = 0;
   if (ok) {
-    a = rowptr[row];
-    e = rowptr[row + 1];
+    a = rowptr[row] - s0;
+    e = rowptr[row + 1] - s0;
   }
   acc = 0.0;
-  if (len <= cap) {
+  for (int64_t c0 = 0; c0 < len; c0 += cap) {
+    const int clen = int(len - c0 < cap ? len - c0 : cap);
     // a lane stages at most kStageLoads slots, in rounds of kStageRound
     // whose loads are all issued before their LDS writes
 #pragma unroll
@@ -94,26 +99,25 @@ __device__ __forceinline__ bool wave_tile_row(const RP* rowptr_, const int32_t* 
 #pragma unroll
       for (int j = 0; j < kStageRound; ++j) {
         const int k = lane + (j0 + j) * kWave;
-        if (k < len) {
-          v[j] = vals[s0 + k];
-          cc[j] = col[s0 + k];
+        if (k < clen) {
+          v[j] = vals[s0 + c0 + k];
+          cc[j] = col[s0 + c0 + k];
         }
       }
 #pragma unroll
       for (int j = 0; j < kStageRound; ++j) {
         const int k = lane + (j0 + j) * kWave;
-        if (k < len) {
+        if (k < clen) {
           lv[k] = v[j];
           lc[k] = cc[j];
         }
       }
     }
     wave_sync();
-    const int k1 = int(e - s0);
-    for (int k = int(a - s0); k < k1; ++k) acc = acc + lv[k] * g(lc[k]);
+    const int k0 = int(a > c0 ? a - c0 : 0);
+    const int k1 = int(e - c0 < clen ? e - c0 : clen);
+    for (int k = k0; k < k1; ++k) acc = acc + lv[k] * g(lc[k]);
     wave_sync();
-  } else {
-    for (int64_t k = a; k < e; ++k) acc = acc + vals[k] * g(col[k]);
   }
   return ok;
 }
@@ -135,7 +139,7 @@ __device__ __forceinline__ int wave_exclusive_sum(int v) {
 // column, the CSR order).  The wave reads one row pointer per tile and one
 // mask byte per row instead of the column array and per-row row pointers;
 // slot positions come from a prefix sum of the rows' bit counts.  Only the
-// values are staged (8 bytes per slot).
+// values are staged (8 bytes per slot), chunked like the CSR form.
 template <typename RP, typename G>
 __device__ __forceinline__ bool wave_tile_row_band(const RP* rowptr_, const uint8_t* mask_,
                                                    const BandOffsets& band, const double* vals_,
@@ -154,36 +158,31 @@ __device__ __forceinline__ bool wave_tile_row_band(const RP* rowptr_, const uint
   const unsigned m = ok ? unsigned(mask[row]) : 0u;
   const int pre = wave_exclusive_sum(__builtin_popcount(m));
   acc = 0.0;
-  if (len <= cap) {
+  int t = 0;     // next offset index of this lane's row
+  int k = pre;   // its slot, relative to s0
+  for (int64_t c0 = 0; c0 < len; c0 += cap) {
+    const int clen = int(len - c0 < cap ? len - c0 : cap);
 #pragma unroll
     for (int j0 = 0; j0 < kStageLoads; j0 += kStageRound) {
       double v[kStageRound];
 #pragma unroll
       for (int j = 0; j < kStageRound; ++j) {
-        const int k = lane + (j0 + j) * kWave;
-        if (k < len) v[j] = vals[s0 + k];
+        const int kk = lane + (j0 + j) * kWave;
+        if (kk < clen) v[j] = vals[s0 + c0 + kk];
       }
 #pragma unroll
       for (int j = 0; j < kStageRound; ++j) {
-        const int k = lane + (j0 + j) * kWave;
-        if (k < len) lv[k] = v[j];
+        const int kk = lane + (j0 + j) * kWave;
+        if (kk < clen) lv[kk] = v[j];
       }
     }
     wave_sync();
-    int k = pre;
-    for (int t = 0; t < band.count; ++t)
+    for (; t < band.count && k - c0 < clen; ++t)
       if ((m >> t) & 1u) {
-        acc = acc + lv[k] * g(row + band.off[t]);
+        acc = acc + lv[k - c0] * g(row + band.off[t]);
         ++k;
       }
     wave_sync();
-  } else {
-    int64_t k = s0 + pre;
-    for (int t = 0; t < band.count; ++t)
-      if ((m >> t) & 1u) {
-        acc = acc + vals[k] * g(row + band.off[t]);
-        ++k;
-      }
   }
   return ok;
 }
@@ -313,7 +312,69 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
   }
 }
 
-// SpMV step k (see the file comment).
+// The scalar part of SpMV step k, in every workgroup: rr_k from the r.r
+// partials (the same bits everywhere), beta, the stopping test; workgroup 0
+// records the history, rr_k, the step index for the residual step and, when
+// the system stops, its final state.
+struct StepHead {
+  int64_t k;
+  double alpha, beta;
+  bool lag;      // x still lacks alpha_{k-1} p_{k-1}
+  int32_t stop;  // ST_RUNNING or the final state
+};
+
+__device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t s,
+                                              double* red) {
+  Scal* sc = c->scal + s;
+  const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
+  const int G = c->grid;
+  const SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
+  StepHead h;
+  h.k = sc->ka;
+  const int64_t k = h.k;
+  const double rr = sum_partials_all(part + (k & 1) * G, G, red);
+  h.lag = k > 0;
+  h.alpha = 0.0;
+  h.beta = 0.0;
+  h.stop = ST_RUNNING;
+  int64_t it_stop = k;
+  double rr_stop = rr;
+  if (h.lag) {
+    const double rr_prev = sc->rr[(k - 1) & 1];
+    h.alpha = sc->alpha;
+    if (!isfinite(rr)) {
+      h.stop = ST_NONFINITE;  // iteration k-1 did not complete
+      it_stop = k - 1;
+      rr_stop = rr_prev;
+    } else {
+      h.beta = rr / rr_prev;
+    }
+  }
+  if (h.stop == ST_RUNNING) {
+    if (rr <= sc->stop) h.stop = ST_CONVERGED;
+    else if (k >= sc->maxit) h.stop = ST_MAXIT;
+  }
+  if (lead) {
+    if (h.lag && h.stop != ST_NONFINITE && c->hist != nullptr && k - 1 < c->hist_cap) {
+      SLA_GLOBAL double* hh = gmem(c->hist + (s * c->hist_cap + (k - 1)) * 3);
+      hh[0] = h.alpha;
+      hh[1] = h.beta;
+      hh[2] = rr;
+    }
+    sc->rr[k & 1] = rr;
+    sc->kr = k;
+    if (h.stop != ST_RUNNING) {
+      sc->it = it_stop;
+      sc->rr_final = rr_stop;
+      sc->state_a = h.stop;
+      atomicSub(c->n_running, 1);
+    }
+  }
+  return h;
+}
+
+// SpMV step k (see the file comment): direction update, deferred x update,
+// q = A p_k with p_k recomputed at each gathered column, p.Ap partials.
 template <typename RP, bool BANDED>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_spmv(const Ctx* __restrict__ c) {
@@ -321,58 +382,22 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
   Scal* sc = c->scal + s;
-  const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
   const int32_t st_in = sc->state_r;
   if (st_in != ST_RUNNING) {
-    if (lead) sc->state_a = st_in;
+    if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
     return;
   }
+  const StepHead h = step_head(c, s, red);
+  const int64_t k = h.k;
+  const double alpha = h.alpha, beta = h.beta;
+  const bool lag = h.lag;
   const int G = c->grid;
-  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
-  const int64_t k = sc->ka;
-  const double rr = sum_partials_all(part + (k & 1) * G, G, red);
-  const bool lag = k > 0;  // x still lacks alpha_{k-1} p_{k-1}
-  double alpha = 0.0, beta = 0.0;
-  int32_t stop = ST_RUNNING;
-  int64_t it_stop = k;
-  double rr_stop = rr;
-  if (lag) {
-    const double rr_prev = sc->rr[(k - 1) & 1];
-    alpha = sc->alpha;
-    if (!isfinite(rr)) {
-      stop = ST_NONFINITE;  // iteration k-1 did not complete
-      it_stop = k - 1;
-      rr_stop = rr_prev;
-    } else {
-      beta = rr / rr_prev;
-    }
-  }
-  if (stop == ST_RUNNING) {
-    if (rr <= sc->stop) stop = ST_CONVERGED;
-    else if (k >= sc->maxit) stop = ST_MAXIT;
-  }
-  if (lead) {
-    if (lag && stop != ST_NONFINITE && c->hist != nullptr && k - 1 < c->hist_cap) {
-      SLA_GLOBAL double* h = gmem(c->hist + (s * c->hist_cap + (k - 1)) * 3);
-      h[0] = alpha;
-      h[1] = beta;
-      h[2] = rr;
-    }
-    sc->rr[k & 1] = rr;
-    sc->kr = k;
-    if (stop != ST_RUNNING) {
-      sc->it = it_stop;
-      sc->rr_final = rr_stop;
-      sc->state_a = stop;
-      atomicSub(c->n_running, 1);
-    }
-  }
   const int64_t n = c->n;
   const SLA_GLOBAL double* pold = gmem(c->p[(k + 1) & 1] + s * n);
   SLA_GLOBAL double* x = gmem(c->x + s * n);
   const int w = threadIdx.x / kWave;
   const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, w);
-  if (stop != ST_RUNNING) {
+  if (h.stop != ST_RUNNING) {
     // last pass: only the deferred x update
     if (lag) {
       const int lane = threadIdx.x & (kWave - 1);
@@ -418,7 +443,76 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
     }
   }
   pq = block_sum_all<kIterBlock>(pq, red);
-  if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
+  if (threadIdx.x == 0) gmem(c->part)[s * kPartSets * G + (2 + (k & 1)) * G + blockIdx.x] = pq;
+}
+
+// For patterns whose rows reach all over the matrix (no locality to reuse
+// r and p_{k-1} at gathered columns), SpMV step k is split in two passes so
+// that the SpMV gathers one vector instead of two:
+//   direction pass:  scalars as above, p_k = r_k + beta p_{k-1}, deferred
+//                    x update (own rows only, streaming);
+//   product pass:    q = A p_k, p.Ap partials.
+// The product pass reads the step index and state the direction pass
+// recorded and writes no scalar.
+__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+void k_cg_direction(const Ctx* __restrict__ c) {
+  __shared__ double red[kWaves];
+  const int64_t s = blockIdx.y;
+  Scal* sc = c->scal + s;
+  const int32_t st_in = sc->state_r;
+  if (st_in != ST_RUNNING) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
+    return;
+  }
+  const StepHead h = step_head(c, s, red);
+  const int64_t k = h.k, n = c->n;
+  const SLA_GLOBAL double* pold = gmem(c->p[(k + 1) & 1] + s * n);
+  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  SLA_GLOBAL double* pnew = gmem(c->p[k & 1] + s * n);
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
+  const int lane = threadIdx.x & (kWave - 1);
+  const TileWalk wk = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, threadIdx.x / kWave);
+  const bool run = h.stop == ST_RUNNING;
+  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
+    const int64_t i = t * kTileRows + lane;
+    if (i < n) {
+      const double po = pold[i];
+      if (h.lag) x[i] = x[i] + h.alpha * po;
+      if (run) pnew[i] = r[i] + h.beta * po;
+    }
+  }
+}
+
+template <typename RP>
+__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+void k_cg_product(const Ctx* __restrict__ c) {
+  extern __shared__ double lds_dyn[];
+  __shared__ double red[kWaves];
+  const int64_t s = blockIdx.y;
+  const Scal* sc = c->scal + s;
+  if (sc->state_a != ST_RUNNING) return;
+  const int64_t k = sc->kr, n = c->n;
+  const int G = c->grid;
+  const RP* rowptr = static_cast<const RP*>(c->rowptr);
+  const double* vals = c->vals + s * c->nnz;
+  const SLA_GLOBAL double* p = gmem(c->p[k & 1] + s * n);
+  SLA_GLOBAL double* q = gmem(c->q + s * n);
+  double* lv;
+  int32_t* lc;
+  wave_areas(lds_dyn, c->wave_cap, false, lv, lc);
+  auto g = [&](int64_t j) { return p[j]; };
+  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, threadIdx.x / kWave);
+  double pq = 0.0;
+  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
+    int64_t i;
+    double acc;
+    if (wave_tile_row<RP>(rowptr, c->col, vals, n, t, c->wave_cap, lv, lc, g, i, acc)) {
+      q[i] = acc;
+      pq = pq + p[i] * acc;
+    }
+  }
+  pq = block_sum_all<kIterBlock>(pq, red);
+  if (threadIdx.x == 0) gmem(c->part)[s * kPartSets * G + (2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
 // Residual step k (see the file comment).
@@ -500,18 +594,19 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
     const int64_t s0 = rowptr[r0];
     const int64_t len = int64_t(rowptr[r1]) - s0;
     const int64_t i = r0 + lane;
-    if (len <= cap) {
-      if (i < r1) {
-        const int64_t a = rowptr[i] - s0, e = rowptr[i + 1] - s0;
-        for (int64_t k = a; k < e; ++k) rowmap[k] = uint8_t(lane);
-      }
+    int64_t a = 0, e = 0;
+    if (i < r1) {
+      a = rowptr[i] - s0;
+      e = rowptr[i + 1] - s0;
+    }
+    for (int64_t c0 = 0; c0 < len; c0 += cap) {
+      const int64_t clen = len - c0 < cap ? len - c0 : cap;
+      for (int64_t k = (a > c0 ? a : c0); k < (e < c0 + clen ? e : c0 + clen); ++k)
+        rowmap[k - c0] = uint8_t(lane);
       wave_sync();
-      for (int64_t k = lane; k < len; k += kWave)
-        gs[s0 + k] = -(l[r0 + rowmap[k]] * xs[col[s0 + k]]);
+      for (int64_t k = lane; k < clen; k += kWave)
+        gs[s0 + c0 + k] = -(l[r0 + rowmap[k]] * xs[col[s0 + c0 + k]]);
       wave_sync();
-    } else if (i < r1) {
-      const double li = l[i];
-      for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) gs[k] = -(li * xs[col[k]]);
     }
   }
 }
@@ -521,8 +616,14 @@ size_t lds_bytes(const sla_csr A) { return solver_lds_bytes(A->wave_cap, kWaves,
 template <typename RP>
 sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
-  if (use_band(A)) k_cg_spmv<RP, true><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
-  else k_cg_spmv<RP, false><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  if (use_split(A)) {
+    k_cg_direction<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
+    k_cg_product<RP><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  } else if (use_band(A)) {
+    k_cg_spmv<RP, true><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  } else {
+    k_cg_spmv<RP, false><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+  }
   k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
   LAUNCH_CHECK();
   return SLA_OK;
@@ -613,8 +714,15 @@ unsigned plain_grid(int64_t tiles, int64_t batch) {
 
 }  // namespace
 
+bool use_split(const sla_csr A) {
+  if (A->spmv_variant == SLA_SPMV_SPLIT) return true;
+  return A->spmv_variant == SLA_SPMV_AUTO && !use_band(A) && A->wide_cols;
+}
+
 bool use_band(const sla_csr A) {
-  if (A->band_mask == nullptr || A->spmv_variant == SLA_SPMV_CSR) return false;
+  if (A->band_mask == nullptr || A->spmv_variant == SLA_SPMV_CSR ||
+      A->spmv_variant == SLA_SPMV_SPLIT)
+    return false;
   if (A->spmv_variant == SLA_SPMV_BANDED) return true;
   // automatic: only when the CSR arrays stream from HBM rather than staying
   // in the Infinity Cache, i.e. when the bytes saved are HBM bytes
@@ -799,14 +907,28 @@ template <typename RP>
 sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), 1u);
   const dim3 block(kIterBlock, 1u);
-  const void* fns[2] = {use_band(A) ? reinterpret_cast<const void*>(&k_cg_spmv<RP, true>)
-                                    : reinterpret_cast<const void*>(&k_cg_spmv<RP, false>),
-                        reinterpret_cast<const void*>(&k_cg_residual)};
-  const size_t ldss[2] = {lds_bytes(A), 0};
+  // the SpMV step is one kernel, or the direction and product passes
+  const bool split = use_split(A);
+  const void* fns[3];
+  size_t ldss[3];
+  int nk = 0;
+  if (split) {
+    fns[nk] = reinterpret_cast<const void*>(&k_cg_direction);
+    ldss[nk++] = 0;
+    fns[nk] = reinterpret_cast<const void*>(&k_cg_product<RP>);
+    ldss[nk++] = lds_bytes(A);
+  } else {
+    fns[nk] = use_band(A) ? reinterpret_cast<const void*>(&k_cg_spmv<RP, true>)
+                          : reinterpret_cast<const void*>(&k_cg_spmv<RP, false>);
+    ldss[nk++] = lds_bytes(A);
+  }
+  fns[nk] = reinterpret_cast<const void*>(&k_cg_residual);
+  ldss[nk++] = 0;
   std::vector<hipEvent_t> ev(size_t(2 * reps), nullptr);
   for (auto& e : ev) SLA_TRY_HIP(hipEventCreate(&e));
   sla_status status = SLA_OK;
-  for (int k = 0; k < 2 && status == SLA_OK; ++k) {
+  avg_ms[0] = avg_ms[1] = 0.0;
+  for (int k = 0; k < nk && status == SLA_OK; ++k) {
     void* args[1] = {&A->ctx_dev};
     for (int64_t r = 0; r < reps; ++r) {
       hipError_t e = hipExtLaunchKernel(fns[k], grid2, block, args, ldss[k], st, ev[2 * r],
@@ -829,7 +951,7 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
       (void)hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]);
       total += ms;
     }
-    avg_ms[k] = total / double(reps);
+    avg_ms[k == nk - 1 ? 1 : 0] += total / double(reps);
   }
   for (auto& e : ev)
     if (e) (void)hipEventDestroy(e);

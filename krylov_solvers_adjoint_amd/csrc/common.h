@@ -63,6 +63,9 @@ constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
 constexpr int kMaxBand = 8;        // most distinct column offsets of a banded pattern
 constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;  // MI355X last-level cache
 constexpr int kPanelTiles = 64;    // widest column block of the panel tile order
+// a 64-row tile whose columns span more than this is "wide" (the span of a
+// 5-point stencil tile on a 13000-point grid line is ~26000)
+constexpr int64_t kLocalSpan = int64_t(1) << 17;
 
 // Column offsets j - i of a banded pattern, ascending: row i's slots are the
 // columns i + off[t] for the bits t set in its mask byte.

@@ -567,6 +567,37 @@ bool sample_offsets(sla_csr A, hipStream_t st, BandOffsets* bo) {
   return true;
 }
 
+// Column locality: the median, over 64 sampled 64-row tiles, of the span
+// (largest - smallest column) of the tile.  A wide span means the gathers of
+// a tile land all over the vectors and are not reused from cache.
+template <typename RP>
+sla_status sample_locality(sla_csr A, hipStream_t st) {
+  const int64_t n = A->n;
+  std::vector<int64_t> spans;
+  for (int64_t sidx = 0; sidx < 64; ++sidx) {
+    const int64_t r0 = std::min<int64_t>(n - 1, (n - 1) * sidx / 63);
+    const int64_t r1 = std::min<int64_t>(n, r0 + kTileRows);
+    RP rp[2];
+    SLA_TRY_HIP(hipMemcpyAsync(&rp[0], (const RP*)A->rowptr + r0, sizeof(RP),
+                               hipMemcpyDeviceToHost, st));
+    SLA_TRY_HIP(hipMemcpyAsync(&rp[1], (const RP*)A->rowptr + r1, sizeof(RP),
+                               hipMemcpyDeviceToHost, st));
+    SLA_TRY_HIP(hipStreamSynchronize(st));
+    if (rp[1] <= rp[0]) continue;
+    std::vector<int32_t> cc(size_t(rp[1] - rp[0]));
+    SLA_TRY_HIP(hipMemcpyAsync(cc.data(), A->col + rp[0], sizeof(int32_t) * cc.size(),
+                               hipMemcpyDeviceToHost, st));
+    SLA_TRY_HIP(hipStreamSynchronize(st));
+    const auto mm = std::minmax_element(cc.begin(), cc.end());
+    spans.push_back(int64_t(*mm.second) - int64_t(*mm.first));
+  }
+  if (!spans.empty()) {
+    std::nth_element(spans.begin(), spans.begin() + spans.size() / 2, spans.end());
+    A->wide_cols = spans[spans.size() / 2] > kLocalSpan;
+  }
+  return SLA_OK;
+}
+
 template <typename RP>
 sla_status detect_band(sla_csr A, hipStream_t st) {
   A->band.count = 0;
@@ -636,12 +667,16 @@ sla_status analyse_pattern(sla_csr A, hipStream_t st) {
   A->tiles = (A->n + kTileRows - 1) / kTileRows;
   if (A->rp_idx == SLA_I32) SLA_TRY(tile_stats<int32_t>(A, st));
   else SLA_TRY(tile_stats<int64_t>(A, st));
-  // stage a wave tile's slots in LDS up to the cap; tiles above it read
-  // their slots straight from memory
-  A->wave_cap = int32_t(std::min<int64_t>(A->max_tile_nnz, kWaveCap));
+  // LDS stage per wave: the largest tile, up to kWaveCap slots (longer tiles
+  // are staged in several chunks)
+  A->wave_cap = int32_t(std::min<int64_t>(std::max<int64_t>(A->max_tile_nnz, 1), kWaveCap));
   if (!A->no_band) {
     if (A->rp_idx == SLA_I32) SLA_TRY(detect_band<int32_t>(A, st));
     else SLA_TRY(detect_band<int64_t>(A, st));
+  }
+  if (A->nnz > 0) {
+    if (A->rp_idx == SLA_I32) SLA_TRY(sample_locality<int32_t>(A, st));
+    else SLA_TRY(sample_locality<int64_t>(A, st));
   }
   return SLA_OK;
 }

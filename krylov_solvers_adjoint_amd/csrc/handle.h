@@ -31,6 +31,7 @@ struct sla_csr_s {
   bool no_band = false;          // pattern analysis skips band detection
   int spmv_variant = SLA_SPMV_AUTO;  // SLA_SPMV_AUTO / _CSR / _BANDED
   int32_t panel = 0;             // panel order of the SpMV tiles (0 = rows in order)
+  bool wide_cols = false;        // sampled tiles reach columns far apart
   int32_t pblock = 0;
 
   // bound values (borrowed)
@@ -66,7 +67,8 @@ namespace sla {
 
 // Workspace and launch helpers implemented in cg.hip
 sla_status ensure_workspace(sla_csr A, int64_t batch);
-bool use_band(const sla_csr A);  // banded SpMV kernels for this handle?
+bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
+bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
 void release_workspace(sla_csr A);
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 

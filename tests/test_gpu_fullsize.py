@@ -69,6 +69,9 @@ def test_rgg4m_csr_forward_adjoint():
     P = K.sla_csr_create(n, t(row.astype(np.int32)), t(col.astype(np.int32)))
     vt = K.sla_csr_values_from_coo(P, t(val))
     rp_g, c_g, perm_g = P.pattern()
+    # random node order: tiles span most of the columns, so the solver takes
+    # the split direction / product kernels
+    assert P.split and not P.banded
     x, info = K.sla_cg_solve(P, vt, t(b), 1e-8, 20000)
     gb, gv, ainfo = K.sla_cg_adjoint(P, vt, x, t(g), 1e-8, 20000)
     torch.cuda.synchronize()
