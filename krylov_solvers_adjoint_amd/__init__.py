@@ -43,6 +43,7 @@ EXPORTS = [
     "sla_cg_adjoint", "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
     "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_spmv_variant",
     "sla_csr_set_graph_block",
+    "sla_csr_set_workgroups_per_cu",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -85,6 +86,7 @@ def _bind(lib):
         "sla_cg_history": [_P, _I64, _P, _P, _P, _I64, ctypes.POINTER(_I64)],
         "sla_profile_iteration_kernels": [_P, _P, _P, _I64, _P, _P],
         "sla_csr_set_graph_block": [_P, _I64],
+        "sla_csr_set_workgroups_per_cu": [_P, _S],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
@@ -219,6 +221,9 @@ class CSRPattern:
 
     def set_graph_block(self, iterations: int):
         _check(_lib.sla_csr_set_graph_block(self._h, int(iterations)))
+
+    def set_workgroups_per_cu(self, workgroups: int):
+        _check(_lib.sla_csr_set_workgroups_per_cu(self._h, int(workgroups)))
 
     def _kernels(self) -> int:
         b = _S()

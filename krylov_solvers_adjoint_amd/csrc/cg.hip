@@ -59,67 +59,144 @@ namespace {
     }                                                                          \
   } while (0)
 
-// Row sum of one lane's row in a wave tile: acc = sum_k vals[k] * g(col[k])
+// Gathers a lane keeps in flight while walking its row (plain CSR rows).
+constexpr int kGather = 4;
+// Tiles a wave keeps in flight in the streaming passes.
+constexpr int kStreamTiles = 4;
+
+// The vector a row sum gathers: v[j] = a[j] (one vector), or, with TWO,
+// v[j] = a[j] + beta * b[j] (the new search direction, recomputed at each
+// gathered column from r and p_{k-1}).  Loads and arithmetic are separate so
+// that a row sum issues all its loads before it uses the first one.  WIDE
+// selects 64-bit addresses for columns of vectors of 4 GiB or more.
+template <bool TWO, bool WIDE>
+struct Gather {
+  const SLA_GLOBAL double* a;
+  const SLA_GLOBAL double* b;
+  double beta;
+  // column j of the whole vector
+  __device__ __forceinline__ void load(int32_t j, double& u, double& w) const {
+    if constexpr (WIDE) {
+      u = a[int64_t(j)];
+      if constexpr (TWO) w = b[int64_t(j)];
+    } else {
+      u = ld(a, uint32_t(j));
+      if constexpr (TWO) w = ld(b, uint32_t(j));
+    }
+  }
+  // column base + o: `base` wave-uniform, o below 2^28
+  __device__ __forceinline__ void load_at(int64_t base, uint32_t o, double& u, double& w) const {
+    u = ld(a + base, o);
+    if constexpr (TWO) w = ld(b + base, o);
+  }
+  __device__ __forceinline__ double value(double u, double w) const {
+    if constexpr (TWO) return u + beta * w;
+    else return u;
+  }
+};
+
+// The index data of a tile that the row sum's loads depend on.  The tile
+// loops load it one tile ahead, so that a tile's gathers and value loads
+// are all issued in one round trip.  Raw row pointers; differences are taken
+// at use.
+template <typename RP>
+struct TileIndex {
+  // row pointers in their stored type: widening them where they are loaded
+  // would wait for the load
+  RP s0;       // rowptr[r0]: the tile's first slot
+  RP s1;       // rowptr[r1]: one past its last slot (plain CSR)
+  RP a;        // rowptr of the lane's row (plain CSR)
+  RP e;        // rowptr of the next row (plain CSR)
+  unsigned m;  // mask byte of the lane's row (banded)
+};
+
+// Lane `lane`'s row in the tile starting at r0, clamped to the tile's last
+// row (lanes past the end compute that row again; see band_row).
+__device__ __forceinline__ uint32_t tile_lane(int64_t r0, int64_t n, uint32_t lane) {
+  const int64_t last = (r0 + kTileRows < n ? r0 + kTileRows : n) - 1 - r0;
+  return int64_t(lane) <= last ? lane : uint32_t(last);
+}
+
+template <int NB, typename RP>
+__device__ __forceinline__ TileIndex<RP> tile_index(const RP* rowptr_, const uint8_t* mask_,
+                                                    int64_t n, int64_t r0, uint32_t lr) {
+  const SLA_GLOBAL RP* rowptr = gmem(rowptr_);
+  TileIndex<RP> x{};
+  x.s0 = rowptr[r0];
+  if constexpr (NB > 0) {
+    x.m = unsigned(ld(gmem(mask_) + r0, lr));
+  } else {
+    x.s1 = rowptr[r0 + kTileRows < n ? r0 + kTileRows : n];
+    x.a = ld(rowptr + r0, lr);
+    x.e = ld(rowptr + r0 + 1, lr);
+  }
+  return x;
+}
+
+// Row sum of one lane's row in a wave tile: acc = sum_k vals[k] * v[col[k]]
 // in ascending slot order, starting from 0.  The tile's slots
 // [rowptr[r0], rowptr[r1]) are contiguous: the wave stages them into its LDS
 // areas `lv`/`lc` (`cap` slots) with coalesced loads, in as many chunks as
 // the tile needs, and each lane adds the slots of its row that fall into the
-// chunk; the ascending order of every row's sum is kept across chunks.
-// Returns false for lanes past the last row.  Every lane of the wave must
-// call it for the same tile.
-template <typename RP, typename G>
-__device__ __forceinline__ bool wave_tile_row(const RP* rowptr_, const int32_t* col_,
-                                              const double* vals_, int64_t n, int64_t tile,
-                                              int cap, double* lv, int32_t* lc, G g, int64_t& row,
-                                              double& acc) {
-  const SLA_GLOBAL RP* __restrict__ rowptr = gmem(rowptr_);
+// chunk, kGather at a time (loads at clamped slots first, then the adds of
+// the slots that exist); the ascending order of every row's sum is kept
+// across chunks.  The lane computes the row `ix` was loaded for; lanes past
+// the last row of the tile compute the tile's last row (see band_row).
+// Every lane of the wave must call it for the same tile.
+template <typename RP, typename GT>
+__device__ __forceinline__ double wave_tile_row(const int32_t* col_, const double* vals_,
+                                                const TileIndex<RP>& ix, int cap, double* lv,
+                                                int32_t* lc, const GT& g) {
   const SLA_GLOBAL int32_t* __restrict__ col = gmem(col_);
   const SLA_GLOBAL double* __restrict__ vals = gmem(vals_);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t r0 = tile * kTileRows;
-  const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
-  const int64_t s0 = rowptr[r0];
-  const int64_t len = int64_t(rowptr[r1]) - s0;
-  row = r0 + lane;
-  const bool ok = row < r1;
-  int64_t a = 0, e = 0;
-  if (ok) {
-    a = rowptr[row] - s0;
-    e = rowptr[row + 1] - s0;
-  }
-  acc = 0.0;
+  const uint32_t lane = lane_id();
+  const int64_t s0 = uniform(int64_t(ix.s0));
+  const int64_t len = uniform(int64_t(ix.s1)) - s0;
+  const int64_t a = int64_t(ix.a) - s0, e = int64_t(ix.e) - s0;
+  double acc = 0.0;
   for (int64_t c0 = 0; c0 < len; c0 += cap) {
     const int clen = int(len - c0 < cap ? len - c0 : cap);
-    // a lane stages at most kStageLoads slots, in rounds of kStageRound
-    // whose loads are all issued before their LDS writes
+    // a lane stages at most kStageLoads slots, all loads first; slots past
+    // the chunk are clamped to its last slot (those lanes store that slot's
+    // own value again), so no load or store needs a branch
+    const SLA_GLOBAL double* vb = vals + s0 + c0;
+    const SLA_GLOBAL int32_t* cb = col + s0 + c0;
+    double v[kStageLoads];
+    int32_t cc[kStageLoads];
 #pragma unroll
-    for (int j0 = 0; j0 < kStageLoads; j0 += kStageRound) {
-      double v[kStageRound];
-      int32_t cc[kStageRound];
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int k = int(lane) + j * kWave;
+      const uint32_t kc = uint32_t(k < clen ? k : clen - 1);
+      v[j] = ld(vb, kc);
+      cc[j] = ld(cb, kc);
+    }
 #pragma unroll
-      for (int j = 0; j < kStageRound; ++j) {
-        const int k = lane + (j0 + j) * kWave;
-        if (k < clen) {
-          v[j] = vals[s0 + c0 + k];
-          cc[j] = col[s0 + c0 + k];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kStageRound; ++j) {
-        const int k = lane + (j0 + j) * kWave;
-        if (k < clen) {
-          lv[k] = v[j];
-          lc[k] = cc[j];
-        }
-      }
+    for (int j = 0; j < kStageLoads; ++j) {
+      const int k = int(lane) + j * kWave;
+      const int kc = k < clen ? k : clen - 1;
+      lv[kc] = v[j];
+      lc[kc] = cc[j];
     }
     wave_sync();
     const int k0 = int(a > c0 ? a - c0 : 0);
     const int k1 = int(e - c0 < clen ? e - c0 : clen);
-    for (int k = k0; k < k1; ++k) acc = acc + lv[k] * g(lc[k]);
+    for (int k = k0; k < k1; k += kGather) {
+      double v[kGather], gu[kGather], gw[kGather];
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) {
+        const int kk = k + u < k1 ? k + u : k1 - 1;
+        v[u] = lv[kk];
+        g.load(lc[kk], gu[u], gw[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) {
+        const double sum = acc + v[u] * g.value(gu[u], gw[u]);
+        acc = k + u < k1 ? sum : acc;
+      }
+    }
     wave_sync();
   }
-  return ok;
+  return acc;
 }
 
 // Exclusive prefix sum over the 64 lanes of a wave.
@@ -136,68 +213,70 @@ __device__ __forceinline__ int wave_exclusive_sum(int v) {
 
 // The same row sum for a banded pattern: row i's slots are the columns
 // i + band.off[t] for the bits t of mask[i], in ascending t (= ascending
-// column, the CSR order).  The wave reads one row pointer per tile and one
-// mask byte per row instead of the column array and per-row row pointers;
-// slot positions come from a prefix sum of the rows' bit counts.  Only the
-// values are staged (8 bytes per slot), chunked like the CSR form.
-template <typename RP, typename G>
-__device__ __forceinline__ bool wave_tile_row_band(const RP* rowptr_, const uint8_t* mask_,
-                                                   const BandOffsets& band, const double* vals_,
-                                                   int64_t n, int64_t tile, int cap, double* lv,
-                                                   G g, int64_t& row, double& acc) {
-  const SLA_GLOBAL RP* __restrict__ rowptr = gmem(rowptr_);
-  const SLA_GLOBAL uint8_t* __restrict__ mask = gmem(mask_);
-  const SLA_GLOBAL double* __restrict__ vals = gmem(vals_);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t r0 = tile * kTileRows;
-  const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
-  const int64_t s0 = rowptr[r0];
-  const int64_t len = int64_t(rowptr[r1]) - s0;
-  row = r0 + lane;
-  const bool ok = row < r1;
-  const unsigned m = ok ? unsigned(mask[row]) : 0u;
-  const int pre = wave_exclusive_sum(__builtin_popcount(m));
-  acc = 0.0;
-  int t = 0;     // next offset index of this lane's row
-  int k = pre;   // its slot, relative to s0
-  for (int64_t c0 = 0; c0 < len; c0 += cap) {
-    const int clen = int(len - c0 < cap ? len - c0 : cap);
+// column, the CSR order).  Every load of the tile is issued before the first
+// one is used, at indices clamped into range so that no load needs a branch:
+// the gathered vector at all NB offsets of the band (columns clamped into
+// [0, n), addressed from a wave-uniform base row), the row's mask byte, one
+// row pointer per tile, and the row's values, read from the CSR array at the
+// positions a prefix sum of the rows' bit counts gives.  Terms of slots the
+// row does not have are dropped by a select.  No LDS and no per-row row
+// pointers or column indices.  band.count <= NB.
+//
+// Lanes past the last row of the tile compute the tile's last row again
+// (`lr`, the same bits as its own lane), so that the caller's stores need no
+// branch: a branch would let the compiler sink the loads into it.
+template <int NB, typename RP, typename GT>
+__device__ __forceinline__ double band_row(const BandOffsets& band, const double* vals_,
+                                           int64_t n, int64_t nnz, int64_t r0, uint32_t lr,
+                                           bool ok, const TileIndex<RP>& ix, const GT& g) {
+  const int64_t s0 = uniform(int64_t(ix.s0));
+  const unsigned m = ix.m;
+  // gathered columns relative to a wave-uniform base row; 32-bit arithmetic
+  const int64_t lo = r0 + (band.off[0] < 0 ? band.off[0] : 0);
+  const int64_t base = lo > 0 ? lo : 0;
+  const int32_t d = int32_t(r0 - base) + int32_t(lr);
+  const int32_t top = int32_t(n - 1 - base);
+  double gu[NB], gw[NB];
 #pragma unroll
-    for (int j0 = 0; j0 < kStageLoads; j0 += kStageRound) {
-      double v[kStageRound];
-#pragma unroll
-      for (int j = 0; j < kStageRound; ++j) {
-        const int kk = lane + (j0 + j) * kWave;
-        if (kk < clen) v[j] = vals[s0 + c0 + kk];
-      }
-#pragma unroll
-      for (int j = 0; j < kStageRound; ++j) {
-        const int kk = lane + (j0 + j) * kWave;
-        if (kk < clen) lv[kk] = v[j];
-      }
-    }
-    wave_sync();
-    for (; t < band.count && k - c0 < clen; ++t)
-      if ((m >> t) & 1u) {
-        acc = acc + lv[k - c0] * g(row + band.off[t]);
-        ++k;
-      }
-    wave_sync();
+  for (int t = 0; t < NB; ++t) {
+    int32_t j = t < band.count ? d + band.off[t] : d;
+    j = j < 0 ? 0 : (j > top ? top : j);
+    g.load_at(base, uint32_t(j), gu[t], gw[t]);
   }
-  return ok;
+  // slot of the row's first value: prefix sum over the tile's own rows, read
+  // from lane lr
+  const int kx = wave_exclusive_sum(ok ? __builtin_popcount(m) : 0);
+  uint32_t k = uint32_t(__shfl(kx, int(lr), kWave));
+  // a tile without slots starts at nnz (> 0 for a banded pattern): its
+  // unused loads read the last slot instead
+  const SLA_GLOBAL double* v = gmem(vals_) + (s0 < nnz ? s0 : nnz - 1);
+  double a[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const bool use = t < band.count && ((m >> t) & 1u);
+    a[t] = ld(v, use ? k : 0u);
+    k += use ? 1u : 0u;
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const bool use = t < band.count && ((m >> t) & 1u);
+    const double sum = acc + a[t] * g.value(gu[t], gw[t]);
+    acc = use ? sum : acc;
+  }
+  return acc;
 }
 
-// This wave's LDS staging areas: 12 bytes per slot (value and column), or 8
-// for a banded pattern (values only).
-__device__ __forceinline__ void wave_areas(double* lds_dyn, int cap, bool banded, double*& lv,
-                                           int32_t*& lc) {
-  const int w = threadIdx.x / kWave;
-  lv = lds_dyn + int64_t(w) * (banded ? cap : cap + (cap + 1) / 2);
+// This wave's LDS staging area for plain CSR rows: 12 bytes per slot (value
+// and column).
+__device__ __forceinline__ void wave_areas(double* lds_dyn, int cap, double*& lv, int32_t*& lc) {
+  const int w = wave_index();
+  lv = lds_dyn + int64_t(w) * (cap + (cap + 1) / 2);
   lc = reinterpret_cast<int32_t*>(lv + cap);
 }
 
-size_t solver_lds_bytes(int cap, int waves, bool banded) {
-  return size_t(waves) * size_t(banded ? cap : cap + (cap + 1) / 2) * sizeof(double);
+size_t solver_lds_bytes(int cap, int waves) {
+  return size_t(waves) * size_t(cap + (cap + 1) / 2) * sizeof(double);
 }
 
 // Sum of `count` partials, the same fixed order in every workgroup: thread t
@@ -213,32 +292,42 @@ __device__ __forceinline__ double sum_partials_all(const SLA_GLOBAL double* __re
 // ---------------------------------------------------------------------------
 // Standalone SpMV: y[s] = A_s x[s]
 // ---------------------------------------------------------------------------
-template <typename RP, bool BANDED>
+// NB > 0: banded rows with at most NB offsets; NB = 0: plain CSR rows
+// (staged through LDS) with vectors below 4 GiB, gathered with 32-bit
+// offsets; NB = -1: plain CSR rows with 64-bit gather addresses.
+template <typename RP, int NB>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
-void k_spmv(const RP* __restrict__ rowptr,
-                                                     const int32_t* __restrict__ col,
-                                                     const uint8_t* __restrict__ mask,
-                                                     BandOffsets band,
-                                                     const double* __restrict__ vals, int64_t n,
-                                                     int64_t nnz, int64_t tiles, int cap,
-                                                     const double* __restrict__ x,
-                                                     double* __restrict__ y) {
+void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
+            const uint8_t* __restrict__ mask, BandOffsets band, const double* __restrict__ vals,
+            int64_t n, int64_t nnz, int64_t tiles, int cap, const double* __restrict__ x,
+            double* __restrict__ y) {
   extern __shared__ double lds_dyn[];
   double* lv;
   int32_t* lc;
-  wave_areas(lds_dyn, cap, BANDED, lv, lc);
+  wave_areas(lds_dyn, cap, lv, lc);
   const int64_t s = blockIdx.y;
   const double* v = vals + s * nnz;
   const SLA_GLOBAL double* xs = gmem(x + s * n);
   SLA_GLOBAL double* ys = gmem(y + s * n);
-  auto g = [&](int64_t j) { return xs[j]; };
-  const int w = threadIdx.x / kWave;
-  for (int64_t t = int64_t(blockIdx.x) * kWaves + w; t < tiles; t += int64_t(gridDim.x) * kWaves) {
-    int64_t i;
+  const Gather<false, (NB < 0)> g{xs, nullptr, 0.0};
+  const int w = wave_index();
+  const uint32_t lane = lane_id();
+  const int64_t stride = int64_t(gridDim.x) * kWaves;
+  int64_t t = int64_t(blockIdx.x) * kWaves + w;
+  // each tile's index data is loaded one tile ahead
+  TileIndex<RP> ix{};
+  if (t < tiles) ix = tile_index<NB, RP>(rowptr, mask, n, t * kTileRows, tile_lane(t * kTileRows, n, lane));
+  for (; t < tiles; t += stride) {
+    const int64_t r0 = t * kTileRows;
+    const bool ok = r0 + lane < n;
+    const uint32_t lr = tile_lane(r0, n, lane);
+    const TileIndex<RP> cur = ix;
+    const int64_t tn = t + stride;
+    if (tn < tiles) ix = tile_index<NB, RP>(rowptr, mask, n, tn * kTileRows, tile_lane(tn * kTileRows, n, lane));
     double acc;
-    const bool ok = BANDED ? wave_tile_row_band<RP>(rowptr, mask, band, v, n, t, cap, lv, g, i, acc)
-                           : wave_tile_row<RP>(rowptr, col, v, n, t, cap, lv, lc, g, i, acc);
-    if (ok) ys[i] = acc;
+    if constexpr (NB > 0) acc = band_row<NB, RP>(band, v, n, nnz, r0, lr, ok, cur, g);
+    else acc = wave_tile_row<RP>(col, v, cur, cap, lv, lc, g);
+    st(ys + r0, lr, acc);
   }
 }
 
@@ -257,7 +346,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ 
   SLA_GLOBAL double* pm = gmem(c->p[1] + s * n);
   const SLA_GLOBAL double* q = gmem(c->q + s * n);
   const int lane = threadIdx.x & (kWave - 1);
-  const TileWalk w = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, threadIdx.x / kWave);
+  const TileWalk w = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, wave_index());
   double bb = 0.0, rr = 0.0;
   for (int64_t t = w.first; t < w.end; t += w.stride) {
     const int64_t i = t * kTileRows + lane;
@@ -375,12 +464,27 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
 
 // SpMV step k (see the file comment): direction update, deferred x update,
 // q = A p_k with p_k recomputed at each gathered column, p.Ap partials.
-template <typename RP, bool BANDED>
+template <typename RP, int NB>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_spmv(const Ctx* __restrict__ c) {
   extern __shared__ double lds_dyn[];
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
+  // context fields first: read before the kernel's first store, they come
+  // in through scalar loads
+  const int64_t n = c->n, nnz = c->nnz, tiles = c->tiles;
+  const int G = c->grid, cap = c->wave_cap, panel = c->panel, pblock = c->pblock;
+  const RP* rowptr = static_cast<const RP*>(c->rowptr);
+  const int32_t* col = c->col;
+  const uint8_t* mask = c->mask;
+  const BandOffsets band = c->band;
+  const double* vals = c->vals + s * nnz;
+  double* const p0 = c->p[0] + s * n;
+  double* const p1 = c->p[1] + s * n;
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
+  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  SLA_GLOBAL double* q = gmem(c->q + s * n);
+  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   Scal* sc = c->scal + s;
   const int32_t st_in = sc->state_r;
   if (st_in != ST_RUNNING) {
@@ -388,62 +492,75 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
     return;
   }
   const StepHead h = step_head(c, s, red);
-  const int64_t k = h.k;
-  const double alpha = h.alpha, beta = h.beta;
+  const int64_t k = uniform(h.k);
+  const double alpha = uniform(h.alpha), beta = uniform(h.beta);
   const bool lag = h.lag;
-  const int G = c->grid;
-  const int64_t n = c->n;
-  const SLA_GLOBAL double* pold = gmem(c->p[(k + 1) & 1] + s * n);
-  SLA_GLOBAL double* x = gmem(c->x + s * n);
-  const int w = threadIdx.x / kWave;
-  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, w);
+  // p_{k-1} and p_k
+  const SLA_GLOBAL double* pold = gmem((k & 1) ? p0 : p1);
+  SLA_GLOBAL double* pnew = gmem((k & 1) ? p1 : p0);
+  const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
   if (h.stop != ST_RUNNING) {
     // last pass: only the deferred x update
     if (lag) {
-      const int lane = threadIdx.x & (kWave - 1);
+      const uint32_t lane = lane_id();
       for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
-        const int64_t i = t * kTileRows + lane;
-        if (i < n) x[i] = x[i] + alpha * pold[i];
+        const int64_t i0 = t * kTileRows;
+        if (i0 + lane < n) st(x + i0, lane, ld(x + i0, lane) + alpha * ld(pold + i0, lane));
       }
     }
     return;
   }
-  const RP* rowptr = static_cast<const RP*>(c->rowptr);
-  const double* vals = c->vals + s * c->nnz;
-  const SLA_GLOBAL double* r = gmem(c->r + s * n);
-  SLA_GLOBAL double* pnew = gmem(c->p[k & 1] + s * n);
-  SLA_GLOBAL double* q = gmem(c->q + s * n);
   double* lv;
   int32_t* lc;
-  wave_areas(lds_dyn, c->wave_cap, BANDED, lv, lc);
-  auto g = [&](int64_t j) { return r[j] + beta * pold[j]; };
-  const BandOffsets band = c->band;
+  wave_areas(lds_dyn, cap, lv, lc);
+  const Gather<true, (NB < 0)> g{r, pold, beta};
+  const uint32_t lane = lane_id();
   // plain row order, or the panel order for wide bands (see panel_tile)
-  const bool panels = c->panel > 0;
+  const bool panels = panel > 0;
   const int xcd = blockIdx.x % kXcds;
-  const int64_t lo = c->tiles * xcd / kXcds, hi = c->tiles * (xcd + 1) / kXcds;
-  const int64_t pend = panels ? panel_positions(hi - lo, c->panel, c->pblock) : wk.end - lo;
-  double pq = 0.0;
-  for (int64_t pos = wk.first - lo; pos < pend; pos += wk.stride) {
-    const int64_t t = panels ? panel_tile(pos, lo, hi, c->panel, c->pblock) : lo + pos;
-    if (t < 0) continue;
-    int64_t i;
-    double acc;
-    const bool ok =
-        BANDED ? wave_tile_row_band<RP>(rowptr, c->mask, band, vals, n, t, c->wave_cap, lv, g, i,
-                                        acc)
-               : wave_tile_row<RP>(rowptr, c->col, vals, n, t, c->wave_cap, lv, lc, g, i, acc);
-    if (ok) {
-      const double po = pold[i];
-      const double pn = r[i] + beta * po;
-      if (lag) x[i] = x[i] + alpha * po;
-      pnew[i] = pn;
-      q[i] = acc;
-      pq = pq + pn * acc;
+  const int64_t lo = tiles * xcd / kXcds, hi = tiles * (xcd + 1) / kXcds;
+  const int64_t pend = panels ? panel_positions(hi - lo, panel, pblock) : wk.end - lo;
+  // the wave's next tile at or after position p (p moves to it), or -1
+  auto next_tile = [&](int64_t& p) -> int64_t {
+    for (; p < pend; p += wk.stride) {
+      const int64_t tt = panels ? panel_tile(p, lo, hi, panel, pblock) : lo + p;
+      if (tt >= 0) return tt;
     }
+    return -1;
+  };
+  double pq = 0.0;
+  int64_t pos = wk.first - lo;
+  int64_t t = next_tile(pos);
+  // each tile's index data is loaded one tile ahead
+  TileIndex<RP> ix{};
+  if (t >= 0) ix = tile_index<NB, RP>(rowptr, mask, n, t * kTileRows, tile_lane(t * kTileRows, n, lane));
+  while (t >= 0) {
+    const int64_t r0 = t * kTileRows;
+    const bool own = r0 + lane < n;
+    const uint32_t lr = tile_lane(r0, n, lane);
+    const TileIndex<RP> cur = ix;
+    pos += wk.stride;
+    const int64_t tn = next_tile(pos);
+    if (tn >= 0)
+      ix = tile_index<NB, RP>(rowptr, mask, n, tn * kTileRows, tile_lane(tn * kTileRows, n, lane));
+    // this row's own operands, loaded before the row sum's loads
+    const double po = ld(pold + r0, lr);
+    const double ro = ld(r + r0, lr);
+    const double xo = ld(x + r0, lr);
+    double acc;
+    if constexpr (NB > 0) acc = band_row<NB, RP>(band, vals, n, nnz, r0, lr, own, cur, g);
+    else acc = wave_tile_row<RP>(col, vals, cur, cap, lv, lc, g);
+    // lanes past the last row store the same bits as the row's own lane
+    const double pn = ro + beta * po;
+    if (lag) st(x + r0, lr, xo + alpha * po);
+    st(pnew + r0, lr, pn);
+    st(q + r0, lr, acc);
+    const double pq1 = pq + pn * acc;
+    pq = own ? pq1 : pq;
+    t = tn;
   }
   pq = block_sum_all<kIterBlock>(pq, red);
-  if (threadIdx.x == 0) gmem(c->part)[s * kPartSets * G + (2 + (k & 1)) * G + blockIdx.x] = pq;
+  if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
 // For patterns whose rows reach all over the matrix (no locality to reuse
@@ -458,6 +575,13 @@ __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWav
 void k_cg_direction(const Ctx* __restrict__ c) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
+  // context fields first (scalar loads, see k_cg_spmv)
+  const int64_t n = c->n, tiles = c->tiles;
+  const int G = c->grid;
+  double* const p0 = c->p[0] + s * n;
+  double* const p1 = c->p[1] + s * n;
+  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
   Scal* sc = c->scal + s;
   const int32_t st_in = sc->state_r;
   if (st_in != ST_RUNNING) {
@@ -465,25 +589,37 @@ void k_cg_direction(const Ctx* __restrict__ c) {
     return;
   }
   const StepHead h = step_head(c, s, red);
-  const int64_t k = h.k, n = c->n;
-  const SLA_GLOBAL double* pold = gmem(c->p[(k + 1) & 1] + s * n);
-  const SLA_GLOBAL double* r = gmem(c->r + s * n);
-  SLA_GLOBAL double* pnew = gmem(c->p[k & 1] + s * n);
-  SLA_GLOBAL double* x = gmem(c->x + s * n);
-  const int lane = threadIdx.x & (kWave - 1);
-  const TileWalk wk = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, threadIdx.x / kWave);
+  const int64_t k = uniform(h.k);
+  const double alpha = uniform(h.alpha), beta = uniform(h.beta);
+  const SLA_GLOBAL double* pold = gmem((k & 1) ? p0 : p1);
+  SLA_GLOBAL double* pnew = gmem((k & 1) ? p1 : p0);
+  const uint32_t lane = lane_id();
+  const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
   const bool run = h.stop == ST_RUNNING;
-  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
-    const int64_t i = t * kTileRows + lane;
-    if (i < n) {
-      const double po = pold[i];
-      if (h.lag) x[i] = x[i] + h.alpha * po;
-      if (run) pnew[i] = r[i] + h.beta * po;
+  // kStreamTiles tiles per round, all loads first
+  for (int64_t t0 = wk.first; t0 < wk.end; t0 += kStreamTiles * wk.stride) {
+    double po[kStreamTiles], xv[kStreamTiles], rv[kStreamTiles];
+#pragma unroll
+    for (int u = 0; u < kStreamTiles; ++u) {
+      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
+      if (t < wk.end && i0 + lane < n) {
+        po[u] = ld(pold + i0, lane);
+        if (h.lag) xv[u] = ld(x + i0, lane);
+        if (run) rv[u] = ld(r + i0, lane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamTiles; ++u) {
+      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
+      if (t < wk.end && i0 + lane < n) {
+        if (h.lag) st(x + i0, lane, xv[u] + alpha * po[u]);
+        if (run) st(pnew + i0, lane, rv[u] + beta * po[u]);
+      }
     }
   }
 }
 
-template <typename RP>
+template <typename RP, bool WIDE>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_product(const Ctx* __restrict__ c) {
   extern __shared__ double lds_dyn[];
@@ -492,27 +628,41 @@ void k_cg_product(const Ctx* __restrict__ c) {
   const Scal* sc = c->scal + s;
   if (sc->state_a != ST_RUNNING) return;
   const int64_t k = sc->kr, n = c->n;
-  const int G = c->grid;
+  const int G = c->grid, cap = c->wave_cap;
   const RP* rowptr = static_cast<const RP*>(c->rowptr);
+  const int32_t* col = c->col;
   const double* vals = c->vals + s * c->nnz;
   const SLA_GLOBAL double* p = gmem(c->p[k & 1] + s * n);
   SLA_GLOBAL double* q = gmem(c->q + s * n);
+  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   double* lv;
   int32_t* lc;
-  wave_areas(lds_dyn, c->wave_cap, false, lv, lc);
-  auto g = [&](int64_t j) { return p[j]; };
-  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, threadIdx.x / kWave);
+  wave_areas(lds_dyn, cap, lv, lc);
+  const Gather<false, WIDE> g{p, nullptr, 0.0};
+  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, wave_index());
+  const uint32_t lane = lane_id();
   double pq = 0.0;
+  // each tile's index data is loaded one tile ahead
+  TileIndex<RP> ix{};
+  if (wk.first < wk.end)
+    ix = tile_index<0, RP>(rowptr, nullptr, n, wk.first * kTileRows,
+                           tile_lane(wk.first * kTileRows, n, lane));
   for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
-    int64_t i;
-    double acc;
-    if (wave_tile_row<RP>(rowptr, c->col, vals, n, t, c->wave_cap, lv, lc, g, i, acc)) {
-      q[i] = acc;
-      pq = pq + p[i] * acc;
-    }
+    const int64_t r0 = t * kTileRows;
+    const bool own = r0 + lane < n;
+    const uint32_t lr = tile_lane(r0, n, lane);
+    const TileIndex<RP> cur = ix;
+    const int64_t tn = t + wk.stride;
+    if (tn < wk.end)
+      ix = tile_index<0, RP>(rowptr, nullptr, n, tn * kTileRows, tile_lane(tn * kTileRows, n, lane));
+    const double po = ld(p + r0, lr);
+    const double acc = wave_tile_row<RP>(col, vals, cur, cap, lv, lc, g);
+    st(q + r0, lr, acc);
+    const double pq1 = pq + po * acc;
+    pq = own ? pq1 : pq;
   }
   pq = block_sum_all<kIterBlock>(pq, red);
-  if (threadIdx.x == 0) gmem(c->part)[s * kPartSets * G + (2 + (k & 1)) * G + blockIdx.x] = pq;
+  if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
 // Residual step k (see the file comment).
@@ -520,6 +670,13 @@ __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWav
 void k_cg_residual(const Ctx* __restrict__ c) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
+  // context fields first (scalar loads, see k_cg_spmv)
+  const int64_t n = c->n, tiles = c->tiles;
+  const int G = c->grid;
+  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
+  SLA_GLOBAL double* r = gmem(c->r + s * n);
+  const SLA_GLOBAL double* q = gmem(c->q + s * n);
+  int* const n_running = c->n_running;
   Scal* sc = c->scal + s;
   const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
   const int32_t st_in = sc->state_a;
@@ -527,8 +684,6 @@ void k_cg_residual(const Ctx* __restrict__ c) {
     if (lead) sc->state_r = st_in;
     return;
   }
-  const int G = c->grid;
-  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   const int64_t k = sc->kr;
   const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
   const double rr = sc->rr[k & 1];
@@ -541,27 +696,38 @@ void k_cg_residual(const Ctx* __restrict__ c) {
       sc->it = k;
       sc->rr_final = rr;
       sc->state_r = stop;
-      atomicSub(c->n_running, 1);
+      atomicSub(n_running, 1);
     }
     return;
   }
-  const double alpha = rr / pq;
+  const double alpha = uniform(rr / pq);
   if (lead) {
     sc->alpha = alpha;
     sc->ka = k + 1;
   }
-  const int64_t n = c->n;
-  SLA_GLOBAL double* r = gmem(c->r + s * n);
-  const SLA_GLOBAL double* q = gmem(c->q + s * n);
-  const int lane = threadIdx.x & (kWave - 1);
-  const TileWalk wk = wave_walk(c->tiles, G, blockIdx.x, kWaves, threadIdx.x / kWave);
+  const uint32_t lane = lane_id();
+  const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
+  // kStreamTiles tiles per round, all loads first; the r.r terms are added
+  // in tile order
   double rn = 0.0;
-  for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
-    const int64_t i = t * kTileRows + lane;
-    if (i < n) {
-      const double ri = r[i] - alpha * q[i];
-      r[i] = ri;
-      rn = rn + ri * ri;
+  for (int64_t t0 = wk.first; t0 < wk.end; t0 += kStreamTiles * wk.stride) {
+    double rv[kStreamTiles], qv[kStreamTiles];
+#pragma unroll
+    for (int u = 0; u < kStreamTiles; ++u) {
+      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
+      if (t < wk.end && i0 + lane < n) {
+        rv[u] = ld(r + i0, lane);
+        qv[u] = ld(q + i0, lane);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamTiles; ++u) {
+      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
+      if (t < wk.end && i0 + lane < n) {
+        const double ri = rv[u] - alpha * qv[u];
+        st(r + i0, lane, ri);
+        rn = rn + ri * ri;
+      }
     }
   }
   rn = block_sum_all<kIterBlock>(rn, red);
@@ -581,7 +747,7 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
                                                              const double* __restrict__ x,
                                                              double* __restrict__ grad) {
   extern __shared__ double lds_dyn[];
-  const int w = threadIdx.x / kWave;
+  const int w = wave_index();
   const int lane = threadIdx.x & (kWave - 1);
   uint8_t* rowmap = reinterpret_cast<uint8_t*>(lds_dyn) + int64_t(w) * cap;
   const int64_t s = blockIdx.y;
@@ -611,18 +777,55 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
   }
 }
 
-size_t lds_bytes(const sla_csr A) { return solver_lds_bytes(A->wave_cap, kWaves, use_band(A)); }
+size_t lds_bytes(const sla_csr A) { return use_band(A) ? 0 : solver_lds_bytes(A->wave_cap, kWaves); }
+
+// Vectors of 4 GiB or more need 64-bit gather addresses.
+bool wide_vectors(const sla_csr A) { return uint64_t(A->n) * sizeof(double) >= (uint64_t(1) << 32); }
+
+// Kernel family of the row sums: the smallest of 3, 5, 8 offsets that holds
+// a band, else 0 (plain CSR) or -1 (plain CSR, vectors of 4 GiB or more).
+int band_class(const sla_csr A) {
+  if (!use_band(A)) return wide_vectors(A) ? -1 : 0;
+  return A->band.count <= 3 ? 3 : (A->band.count <= 5 ? 5 : 8);
+}
+
+template <typename RP>
+const void* spmv_step_kernel(int nb) {
+  switch (nb) {
+    case 3: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 3>);
+    case 5: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 5>);
+    case 8: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 8>);
+    case -1: return reinterpret_cast<const void*>(&k_cg_spmv<RP, -1>);
+    default: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 0>);
+  }
+}
+
+template <typename RP>
+const void* product_kernel(const sla_csr A) {
+  return wide_vectors(A) ? reinterpret_cast<const void*>(&k_cg_product<RP, true>)
+                         : reinterpret_cast<const void*>(&k_cg_product<RP, false>);
+}
+
+sla_status launch_ctx_kernel(const void* fn, dim3 grid, size_t lds, const Ctx* cd,
+                             hipStream_t st) {
+  void* args[1] = {&cd};
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(kIterBlock), args, lds, st);
+  if (e != hipSuccess) {
+    set_error("kernel launch failed: %s", hipGetErrorString(e));
+    return SLA_ERR_DEVICE;
+  }
+  return SLA_OK;
+}
 
 template <typename RP>
 sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
   if (use_split(A)) {
     k_cg_direction<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
-    k_cg_product<RP><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
-  } else if (use_band(A)) {
-    k_cg_spmv<RP, true><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+    SLA_TRY(launch_ctx_kernel(product_kernel<RP>(A), grid2, lds_bytes(A), A->ctx_dev, st));
   } else {
-    k_cg_spmv<RP, false><<<grid2, kIterBlock, lds_bytes(A), st>>>(A->ctx_dev);
+    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(band_class(A)), grid2, lds_bytes(A),
+                              A->ctx_dev, st));
   }
   k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
   LAUNCH_CHECK();
@@ -723,10 +926,9 @@ bool use_band(const sla_csr A) {
   if (A->band_mask == nullptr || A->spmv_variant == SLA_SPMV_CSR ||
       A->spmv_variant == SLA_SPMV_SPLIT)
     return false;
-  if (A->spmv_variant == SLA_SPMV_BANDED) return true;
-  // automatic: only when the CSR arrays stream from HBM rather than staying
-  // in the Infinity Cache, i.e. when the bytes saved are HBM bytes
-  return double(A->nnz) * 12.0 > double(kInfinityCacheBytes);
+  // automatic: whenever a band was detected (fewer bytes per slot, and no
+  // LDS staging between the index loads and the gathers)
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -766,9 +968,9 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   if (A->ws_batch == batch && A->r != nullptr) return SLA_OK;
   release_workspace(A);
   const int64_t n = A->n;
-  // solver grid: two workgroups per CU in total, a multiple of the XCD count
-  // per system, never more than the wave tiles need (rounded up)
-  const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * 2 / batch);
+  // solver grid: wg_per_cu workgroups per CU in total, a multiple of the XCD
+  // count per system, never more than the wave tiles need (rounded up)
+  const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * A->wg_per_cu / batch);
   int64_t g = std::min<int64_t>((A->tiles + kWaves - 1) / kWaves, target);
   g = (g + kXcds - 1) / kXcds * kXcds;
   A->grid = int32_t(std::max<int64_t>(g, kXcds));
@@ -796,13 +998,19 @@ sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const doubl
                        hipStream_t st) {
   const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
   const size_t lds = lds_bytes(A);
-  const bool bd = use_band(A);
+  const int nb = band_class(A);
   if (A->rp_idx == SLA_I32) {
-    auto k = bd ? k_spmv<int32_t, true> : k_spmv<int32_t, false>;
+    auto k = nb == 3 ? k_spmv<int32_t, 3>
+             : nb == 5 ? k_spmv<int32_t, 5>
+             : nb == 8 ? k_spmv<int32_t, 8>
+             : nb == 0 ? k_spmv<int32_t, 0> : k_spmv<int32_t, -1>;
     k<<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->band_mask, A->band,
                                      vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y);
   } else {
-    auto k = bd ? k_spmv<int64_t, true> : k_spmv<int64_t, false>;
+    auto k = nb == 3 ? k_spmv<int64_t, 3>
+             : nb == 5 ? k_spmv<int64_t, 5>
+             : nb == 8 ? k_spmv<int64_t, 8>
+             : nb == 0 ? k_spmv<int64_t, 0> : k_spmv<int64_t, -1>;
     k<<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->band_mask, A->band,
                                      vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y);
   }
@@ -915,11 +1123,10 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
   if (split) {
     fns[nk] = reinterpret_cast<const void*>(&k_cg_direction);
     ldss[nk++] = 0;
-    fns[nk] = reinterpret_cast<const void*>(&k_cg_product<RP>);
+    fns[nk] = product_kernel<RP>(A);
     ldss[nk++] = lds_bytes(A);
   } else {
-    fns[nk] = use_band(A) ? reinterpret_cast<const void*>(&k_cg_spmv<RP, true>)
-                          : reinterpret_cast<const void*>(&k_cg_spmv<RP, false>);
+    fns[nk] = spmv_step_kernel<RP>(band_class(A));
     ldss[nk++] = lds_bytes(A);
   }
   fns[nk] = reinterpret_cast<const void*>(&k_cg_residual);

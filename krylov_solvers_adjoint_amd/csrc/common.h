@@ -58,10 +58,9 @@ constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-rob
 // CU; a 64-row tile of a 5-point stencil has at most 320 slots.
 constexpr int kWaveCap = 336;
 constexpr int kStageLoads = (kWaveCap + kWave - 1) / kWave;  // staged slots per lane
-constexpr int kStageRound = 3;     // staged slots whose loads are in flight together
 constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
 constexpr int kMaxBand = 8;        // most distinct column offsets of a banded pattern
-constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;  // MI355X last-level cache
+constexpr int64_t kMaxBandSpan = int64_t(1) << 27;  // widest band (largest - smallest offset)
 constexpr int kPanelTiles = 64;    // widest column block of the panel tile order
 // a 64-row tile whose columns span more than this is "wide" (the span of a
 // 5-point stencil tile on a 13000-point grid line is ~26000)
@@ -150,6 +149,52 @@ template <typename T>
 __device__ __forceinline__ SLA_GLOBAL T* gmem(T* p) {
   return (SLA_GLOBAL T*)(p);
 }
+
+// A value that is the same in every lane, moved to scalar registers (values
+// that come from LDS or from vector loads live in vector registers).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ double uniform(double v) {
+  return __longlong_as_double(int64_t(uniform_u64(uint64_t(__double_as_longlong(v)))));
+}
+__device__ __forceinline__ int64_t uniform(int64_t v) { return int64_t(uniform_u64(uint64_t(v))); }
+
+// base[off] for a wave-uniform `base` and a non-negative offset whose byte
+// offset fits in 32 bits.  The base is moved to scalar registers (it may sit
+// in vector registers when the compiler cannot prove the context field it
+// came from unclobbered) and hidden from reassociation by an empty asm, so
+// the load takes the base in scalar registers and the offset in one vector
+// register; otherwise the compiler folds a tile's base into a 64-bit
+// per-lane address for every array and keeps those live across the loop.
+// Every caller passes a base that is the same in all lanes of the wave.
+template <typename T>
+__device__ __forceinline__ uint64_t scalar_base(const SLA_GLOBAL T* p) {
+  // readfirstlane returns int: both halves go through uint32_t before they
+  // are widened, so the low half is zero- and not sign-extended
+  uint64_t u = uniform_u64(reinterpret_cast<uint64_t>(p));
+  asm("" : "+s"(u));
+  return u;
+}
+template <typename T>
+__device__ __forceinline__ T ld(const SLA_GLOBAL T* base, uint32_t off) {
+  return *reinterpret_cast<const SLA_GLOBAL T*>(scalar_base(base) +
+                                                uint64_t(off * uint32_t(sizeof(T))));
+}
+template <typename T>
+__device__ __forceinline__ void st(SLA_GLOBAL T* base, uint32_t off, T v) {
+  *reinterpret_cast<SLA_GLOBAL T*>(scalar_base(base) + uint64_t(off * uint32_t(sizeof(T)))) = v;
+}
+
+// Index of this thread's wave in its workgroup, as a wave-uniform (scalar)
+// value, so that everything derived from it stays in scalar registers.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+}
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
 __device__ __forceinline__ double wave_sum(double v) {
   // butterfly over the 64 lanes; every lane ends with the same total, and
   // the association order is fixed, so results are reproducible
@@ -205,14 +250,16 @@ __device__ __forceinline__ TileWalk wave_walk(int64_t tiles, int grid, int bid, 
 // for positions that fall past the end of a panel or of the range.
 __device__ __forceinline__ int64_t panel_tile(int64_t p, int64_t lo, int64_t hi, int panel,
                                               int pblock) {
-  const int64_t V = (hi - lo + panel - 1) / panel;
-  const int64_t per_blk = V * pblock;
-  const int64_t blk = p / per_blk;
-  const int64_t rem = p - blk * per_blk;
-  const int64_t v = rem / pblock;
-  const int64_t u = blk * pblock + (rem - v * pblock);
-  if (u >= panel) return -1;
-  const int64_t t = lo + v * panel + u;
+  // every quantity is below 2^31 (tiles of an int32-column matrix)
+  const uint32_t V = uint32_t((hi - lo + panel - 1) / panel);
+  const uint32_t per_blk = V * uint32_t(pblock);
+  const uint32_t pp = uint32_t(p);
+  const uint32_t blk = pp / per_blk;
+  const uint32_t rem = pp - blk * per_blk;
+  const uint32_t v = rem / uint32_t(pblock);
+  const uint32_t u = blk * uint32_t(pblock) + (rem - v * uint32_t(pblock));
+  if (u >= uint32_t(panel)) return -1;
+  const int64_t t = lo + int64_t(v) * panel + u;
   return t < hi ? t : -1;
 }
 

@@ -603,6 +603,9 @@ sla_status detect_band(sla_csr A, hipStream_t st) {
   A->band.count = 0;
   BandOffsets bo{};
   if (A->nnz == 0 || !sample_offsets<RP>(A, st, &bo)) return SLA_OK;
+  // the banded kernels address a tile's gathers by 32-bit offsets from one
+  // base row, which holds for spans below kMaxBandSpan
+  if (int64_t(bo.off[bo.count - 1]) - int64_t(bo.off[0]) >= kMaxBandSpan) return SLA_OK;
   uint8_t* mask = nullptr;
   int* ok = nullptr;
   SLA_TRY(dev_alloc(&mask, A->n, "band masks"));

@@ -59,6 +59,8 @@ struct sla_csr_s {
 
   // graphs of `graph_block` iterations, keyed by batch size
   int64_t graph_block = 32;
+  // solver workgroups per compute unit (1 or 2)
+  int32_t wg_per_cu = 2;
   hipStream_t capture_stream = nullptr;
   std::map<int64_t, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
 };

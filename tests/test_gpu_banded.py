@@ -96,8 +96,7 @@ def test_laplacian3d_cg_against_oracle():
     n = len(rp) - 1
     b = W.uniform_rhs(n, 8)
     P = csr_handle(rp, c)
-    assert not P.banded  # small: the automatic choice keeps the CSR kernels
-    assert P.set_spmv_variant("banded")
+    assert P.banded  # seven offsets: the automatic choice is the banded kernels
     x, info = K.sla_cg_solve(P, t(v), t(b), 1e-10, 5000)
     torch.cuda.synchronize()
     xo, io = oracle.cg(oracle.CSR(n, rp.astype(np.int64), c, v), b, 1e-10, 5000)

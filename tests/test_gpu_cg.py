@@ -69,6 +69,38 @@ def test_graph_blocks_give_identical_bits(graph_block):
             assert np.array_equal(cur[0], ref[0]) and cur[1] == ref[1]
 
 
+def test_one_workgroup_per_cu():
+    """The one-workgroup-per-CU grid: CG and the adjoint still match the
+    oracle, two runs give the same bits, and the SpMV is unchanged."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    N = 150
+    rp, c, v, Ao = _poisson(N)
+    b = W.uniform_rhs(N * N, 5)
+    g = W.normal_rhs(N * N, 6)
+    runs = []
+    for _ in range(2):
+        P = csr_handle(rp, c)
+        P.set_workgroups_per_cu(1)
+        vt = t(v)
+        x, info = K.sla_cg_solve(P, vt, t(b), 1e-10, 5000)
+        gb, gv, ai = K.sla_cg_adjoint(P, vt, x, t(g), 1e-10, 5000)
+        y = K.sla_spmv(P, vt, t(b))
+        torch.cuda.synchronize()
+        runs.append((x.cpu().numpy(), gb.cpu().numpy(), gv.cpu().numpy(), y.cpu().numpy(),
+                     info.iterations, ai.iterations))
+    for u, w in zip(*runs):
+        assert np.array_equal(np.asarray(u), np.asarray(w))
+    xo, io = oracle.cg(Ao, b, 1e-10, 5000)
+    gbo, gvo, aio = oracle.adjoint(Ao, xo, g, 1e-10, 5000)
+    x, gb, gv, y, it, ait = runs[0]
+    assert np.array_equal(y, oracle.spmv(Ao, b))
+    assert iters_close(it, io.iterations) and iters_close(ait, aio.iterations)
+    assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+    with pytest.raises(K.SlaError):
+        P.set_workgroups_per_cu(3)
+
+
 def test_reproducible_bits_and_history():
     import torch
     import krylov_solvers_adjoint_amd as K
