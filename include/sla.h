@@ -209,22 +209,36 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x,
  * stored column j of every row i equals i + d for one of at most 8 fixed
  * offsets d (a banded or stencil pattern such as the 5-point Laplacian); if
  * so, the banded kernels can read a mask byte per row and one row pointer per
- * 64 rows instead of the column array and per-row row pointers.
- *   SLA_SPMV_AUTO (0, default): banded kernels when the pattern is banded and
- *     its CSR arrays (12 bytes per slot) exceed the 256 MiB Infinity Cache, so
- *     that the bytes saved are HBM bytes; otherwise the CSR kernels.
+ * 64 rows instead of the column array and per-row row pointers.  If moreover
+ * every offset of magnitude 64 or more is +-L for one L >= 961 (a stencil on
+ * a grid whose lines hold L points), the CG iteration can use the line walk:
+ * each wave walks a column of 64-point tiles down the grid lines and keeps
+ * the neighbouring lines' search direction in registers, so that r and
+ * p_{k-1} are read from memory once per row.
+ *   SLA_SPMV_AUTO (0, default): the line walk when it applies, else the
+ *     banded kernels when the pattern is banded, else the CSR kernels, or
+ *     the split form below for CSR patterns without column locality.
  *   SLA_SPMV_CSR (1): always the CSR kernels.
- *   SLA_SPMV_BANDED (2): the banded kernels whenever the pattern is banded.
+ *   SLA_SPMV_BANDED (2): the banded kernels whenever the pattern is banded
+ *     (never the line walk).
  *   SLA_SPMV_SPLIT (3): the CSR kernels with the search-direction update in a
  *     pass of its own, so that the SpMV gathers one vector instead of two;
  *     AUTO picks it for non-banded patterns whose 64-row tiles reach columns
  *     more than 2^17 apart (no reuse of gathered values from cache).
+ *   SLA_SPMV_LINES (4): the line walk when it applies, else as BANDED.
  * SpMV results are bit-identical in every case; CG results are identical
- * between AUTO, CSR and BANDED, and differ only in the order of the p.Ap
- * partial sums under SPLIT.  *kernels_host (may be NULL) receives the family
- * now in use: 0 CSR, 1 banded, 2 CSR with the separate direction pass.
+ * between CSR and BANDED, and differ only in the order of the p.Ap partial
+ * sums (each workgroup's share of rows) under SPLIT and LINES.  *kernels_host (may be NULL) receives the
+ * family now in use: 0 CSR, 1 banded, 2 CSR with the separate direction
+ * pass, 3 line walk.
  */
-enum { SLA_SPMV_AUTO = 0, SLA_SPMV_CSR = 1, SLA_SPMV_BANDED = 2, SLA_SPMV_SPLIT = 3 };
+enum {
+  SLA_SPMV_AUTO = 0,
+  SLA_SPMV_CSR = 1,
+  SLA_SPMV_BANDED = 2,
+  SLA_SPMV_SPLIT = 3,
+  SLA_SPMV_LINES = 4
+};
 sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels_host);
 
 /* Iterations per captured HIP graph block (default 32; 0 = launch kernels

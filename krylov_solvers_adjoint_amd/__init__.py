@@ -231,10 +231,11 @@ class CSRPattern:
         return b.value
 
     def set_spmv_variant(self, variant) -> bool:
-        """"auto" (default), "csr", "banded" or "split" (see sla_csr_set_spmv_variant);
-        returns whether the banded kernels are now in use."""
-        self._variant = {"auto": 0, "csr": 1, "banded": 2, "split": 3}[variant]
-        return self._kernels() == 1
+        """"auto" (default), "csr", "banded", "split" or "lines" (see
+        sla_csr_set_spmv_variant); returns whether mask-byte kernels (banded
+        or line walk) are now in use."""
+        self._variant = {"auto": 0, "csr": 1, "banded": 2, "split": 3, "lines": 4}[variant]
+        return self._kernels() in (1, 3)
 
     @property
     def split(self) -> bool:
@@ -243,8 +244,13 @@ class CSRPattern:
 
     @property
     def banded(self) -> bool:
-        """Whether the banded kernels are in use."""
-        return self._kernels() == 1
+        """Whether mask-byte kernels (banded or line walk) are in use."""
+        return self._kernels() in (1, 3)
+
+    @property
+    def lines(self) -> bool:
+        """Whether the CG iteration uses the line walk."""
+        return self._kernels() == 3
 
     def history(self, system: int = 0, cap: int = 1 << 20):
         import numpy as np

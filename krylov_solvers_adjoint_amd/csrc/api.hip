@@ -385,14 +385,14 @@ sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels) {
   API_BEGIN
   clear_error();
   REQUIRE(A != nullptr, "sla_csr_set_spmv_variant: NULL handle");
-  REQUIRE(variant >= SLA_SPMV_AUTO && variant <= SLA_SPMV_SPLIT,
+  REQUIRE(variant >= SLA_SPMV_AUTO && variant <= SLA_SPMV_LINES,
           "sla_csr_set_spmv_variant: unknown variant %d", variant);
   if (variant != A->spmv_variant) {
     (void)hipDeviceSynchronize();
     release_workspace(A);  // the captured graphs hold the old kernels
     A->spmv_variant = variant;
   }
-  if (kernels) *kernels = use_split(A) ? 2 : (use_band(A) ? 1 : 0);
+  if (kernels) *kernels = use_split(A) ? 2 : (use_lines(A) ? 3 : (use_band(A) ? 1 : 0));
   return SLA_OK;
   API_END
 }

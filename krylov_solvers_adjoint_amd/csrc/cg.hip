@@ -563,6 +563,179 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
+// SpMV step k for a band whose far offsets are +-L and whose other offsets
+// lie within +-63: the matrix of a stencil on a grid whose lines hold L
+// points (the 5-point Laplacian on an N x N grid: L = N).  Same arithmetic as
+// k_cg_spmv, different tiles and walk:
+//   * tile (u, v) is the points u*64 .. u*64+63 of grid line v (rows
+//     v*L + u*64 + lane; shorter at the end of a line and of the matrix), so
+//     the +-L neighbours of a tile are the tiles (u, v+-1), lane for lane;
+//   * each wave walks one tile column u down a chunk of lines.  It loads the
+//     next tile's r and p_{k-1} once, as the current tile's +L neighbours,
+//     and keeps them as that tile's own operands in the next step; the -L
+//     neighbours are the previous tile's p_k, still in registers.  r and
+//     p_{k-1} thus come from memory once per row (plus the tiles just above
+//     and below each chunk), whatever the line length;
+//   * offsets within +-63 are gathered as in band_row: they fall in the
+//     tile's own cache lines or the neighbouring columns', which the other
+//     waves of the workgroup (columns u - w .. u - w + 15) walk in step.
+// Lines are split into kXcds contiguous ranges, one per XCD; a range into
+// `chunks` chunks; a workgroup takes 16 adjacent columns of one chunk.
+template <typename RP, int NB>
+__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+void k_cg_spmv_lines(const Ctx* __restrict__ c) {
+  __shared__ double red[kWaves];
+  const int64_t s = blockIdx.y;
+  // context fields first (scalar loads, see k_cg_spmv)
+  const int64_t n = c->n, nnz = c->nnz, tiles = c->tiles, L = c->line;
+  const int G = c->grid, chunks = c->line_chunks;
+  const RP* rowptr = static_cast<const RP*>(c->rowptr);
+  const uint8_t* mask = c->mask;
+  const BandOffsets band = c->band;
+  const double* vals = c->vals + s * nnz;
+  double* const p0 = c->p[0] + s * n;
+  double* const p1 = c->p[1] + s * n;
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
+  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  SLA_GLOBAL double* q = gmem(c->q + s * n);
+  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
+  Scal* sc = c->scal + s;
+  const int32_t st_in = sc->state_r;
+  if (st_in != ST_RUNNING) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
+    return;
+  }
+  const StepHead h = step_head(c, s, red);
+  const int64_t k = uniform(h.k);
+  const double alpha = uniform(h.alpha), beta = uniform(h.beta);
+  const bool lag = h.lag;
+  const SLA_GLOBAL double* pold = gmem((k & 1) ? p0 : p1);
+  SLA_GLOBAL double* pnew = gmem((k & 1) ? p1 : p0);
+  const int w = wave_index();
+  const uint32_t lane = lane_id();
+  if (h.stop != ST_RUNNING) {
+    // last pass: only the deferred x update
+    if (lag) {
+      const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, w);
+      for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
+        const int64_t i0 = t * kTileRows;
+        if (i0 + lane < n) st(x + i0, lane, ld(x + i0, lane) + alpha * ld(pold + i0, lane));
+      }
+    }
+    return;
+  }
+  // offsets: off[0] = -L and off[count-1] = +L (from registers), 0 (the row
+  // itself), the others within +-63 (gathered)
+  const Gather<true, false> g{r, pold, beta};
+  const int64_t U = (L + kTileRows - 1) / kTileRows;  // tile columns per line
+  const int64_t V = (n + L - 1) / L;                  // lines
+  const int64_t groups = (U + kWaves - 1) / kWaves;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = G / kXcds;
+  const int64_t va = V * xcd / kXcds, vb = V * (xcd + 1) / kXcds;
+  double pq = 0.0;
+  for (int64_t unit = slot; unit < groups * chunks; unit += per_xcd) {
+    const int64_t u = (unit / chunks) * kWaves + w;
+    const int64_t ch = unit % chunks;
+    const int64_t v0 = va + (vb - va) * ch / chunks, v1 = va + (vb - va) * (ch + 1) / chunks;
+    const int64_t col0 = u * kTileRows;
+    if (u >= U || v0 >= v1 || v0 * L + col0 >= n) continue;
+    const int64_t lenu = L - col0 < kTileRows ? L - col0 : kTileRows;
+    // rows of tile v: v*L + col0 + [0, len(v)); lane clamped to the last one
+    auto tile_len = [&](int64_t v) -> int64_t {
+      const int64_t left = n - (v * L + col0);
+      return left < lenu ? left : lenu;
+    };
+    auto clamp_lane = [&](int64_t len) -> uint32_t {
+      return int64_t(lane) < len ? lane : uint32_t(len - 1);
+    };
+    // -L neighbours of the first tile
+    double pprev = 0.0;
+    if (v0 >= 1) {
+      const int64_t pr0 = (v0 - 1) * L + col0;
+      const uint32_t pl = clamp_lane(lenu);
+      pprev = ld(r + pr0, pl) + beta * ld(pold + pr0, pl);
+    }
+    int64_t len = tile_len(v0);
+    uint32_t lr = clamp_lane(len);
+    double rc = ld(r + v0 * L + col0, lr), pc = ld(pold + v0 * L + col0, lr);
+    TileIndex<RP> ix = tile_index<NB, RP>(rowptr, mask, n, v0 * L + col0, lr);
+    for (int64_t v = v0; v < v1; ++v) {
+      const int64_t r0 = v * L + col0;
+      const bool own = int64_t(lane) < len;
+      // the next tile: +L neighbours now, own operands in the next step
+      const int64_t lenn = v + 1 < V ? tile_len(v + 1) : 0;
+      const bool hasn = lenn > 0;
+      const int64_t rn0 = hasn ? r0 + L : r0;
+      const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
+      const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
+      const TileIndex<RP> cur = ix;
+      if (hasn && v + 1 < v1) ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
+      const double xo = ld(x + r0, lr);
+      // near offsets, gathered; the other kinds read the row itself (no
+      // branch; the value is not used)
+      const int64_t lo = r0 - kTileRows;
+      const int64_t base = lo > 0 ? lo : 0;
+      const int32_t d = int32_t(r0 - base) + int32_t(lr);
+      const int32_t top = int32_t(n - 1 - base);
+      // offsets are sorted: -L first, +L last, the near ones in between
+      double gu[NB], gw[NB];
+#pragma unroll
+      for (int t = 1; t < NB - 1; ++t) {
+        const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+        int32_t j = d + o;
+        j = j < 0 ? 0 : (j > top ? top : j);
+        g.load_at(base, uint32_t(j), gu[t], gw[t]);
+      }
+      // values at the slot positions of the row (see band_row)
+      const int64_t s0 = uniform(int64_t(cur.s0));
+      const unsigned m = cur.m;
+      const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
+      uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
+      const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+      double a[NB];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const bool use = t < band.count && ((m >> t) & 1u);
+        a[t] = ld(vb_, use ? kk : 0u);
+        kk += use ? 1u : 0u;
+      }
+      // p_k at the row, below (-L) and above (+L)
+      const double pcur = rc + beta * pc;
+      const double pnext = rn + beta * pn;
+      // lanes past the end of a short tile compute its last row: take that
+      // row's -L value (the previous tile was loaded lane for lane)
+      const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+      double acc = 0.0;
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const int32_t o = t < band.count ? band.off[t] : 0;
+        const bool use = t < band.count && ((m >> t) & 1u);
+        double gv;
+        if (t == 0) gv = pbelow;
+        else if (t == NB - 1) gv = pnext;
+        else gv = t == band.count - 1 ? pnext : (o == 0 ? pcur : g.value(gu[t], gw[t]));
+        const double sum = acc + a[t] * gv;
+        acc = use ? sum : acc;
+      }
+      // lanes past the last row store the same bits as the row's own lane
+      if (lag) st(x + r0, lr, xo + alpha * pc);
+      st(pnew + r0, lr, pcur);
+      st(q + r0, lr, acc);
+      const double pq1 = pq + pcur * acc;
+      pq = own ? pq1 : pq;
+      // shift the walk down one line
+      pprev = pcur;
+      rc = rn;
+      pc = pn;
+      len = lenn;
+      lr = lrn;
+      if (!hasn) break;
+    }
+  }
+  pq = block_sum_all<kIterBlock>(pq, red);
+  if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
+}
+
 // For patterns whose rows reach all over the matrix (no locality to reuse
 // r and p_{k-1} at gathered columns), SpMV step k is split in two passes so
 // that the SpMV gathers one vector instead of two:
@@ -790,7 +963,15 @@ int band_class(const sla_csr A) {
 }
 
 template <typename RP>
-const void* spmv_step_kernel(int nb) {
+const void* spmv_step_kernel(const sla_csr A) {
+  const int nb = band_class(A);
+  if (use_lines(A)) {
+    switch (nb) {
+      case 3: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3>);
+      case 5: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5>);
+      default: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 8>);
+    }
+  }
   switch (nb) {
     case 3: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 3>);
     case 5: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 5>);
@@ -824,7 +1005,7 @@ sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
     k_cg_direction<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
     SLA_TRY(launch_ctx_kernel(product_kernel<RP>(A), grid2, lds_bytes(A), A->ctx_dev, st));
   } else {
-    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(band_class(A)), grid2, lds_bytes(A),
+    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A), grid2, lds_bytes(A),
                               A->ctx_dev, st));
   }
   k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
@@ -906,6 +1087,22 @@ void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool
   c.band = A->band;
   c.panel = A->panel;
   c.pblock = A->pblock;
+  c.line = use_lines(A) ? A->line : 0;
+  c.line_chunks = 0;
+  if (c.line > 0) {
+    // chunks per XCD so that every workgroup of an XCD gets the same number
+    // of (16-column group, chunk) units: per_xcd / gcd(groups, per_xcd)
+    const int64_t per_xcd = A->grid / kXcds;
+    const int64_t U = (c.line + kTileRows - 1) / kTileRows;
+    const int64_t groups = (U + kWaves - 1) / kWaves;
+    int64_t a = per_xcd, b = groups;
+    while (b != 0) {
+      const int64_t t = a % b;
+      a = b;
+      b = t;
+    }
+    c.line_chunks = int32_t(per_xcd / a);
+  }
 }
 
 // Workgroups for a one-pass kernel over `tiles` wave tiles and `batch` systems.
@@ -920,6 +1117,11 @@ unsigned plain_grid(int64_t tiles, int64_t batch) {
 bool use_split(const sla_csr A) {
   if (A->spmv_variant == SLA_SPMV_SPLIT) return true;
   return A->spmv_variant == SLA_SPMV_AUTO && !use_band(A) && A->wide_cols;
+}
+
+bool use_lines(const sla_csr A) {
+  if (A->line <= 0 || !use_band(A)) return false;
+  return A->spmv_variant == SLA_SPMV_AUTO || A->spmv_variant == SLA_SPMV_LINES;
 }
 
 bool use_band(const sla_csr A) {
@@ -1126,7 +1328,7 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
     fns[nk] = product_kernel<RP>(A);
     ldss[nk++] = lds_bytes(A);
   } else {
-    fns[nk] = spmv_step_kernel<RP>(band_class(A));
+    fns[nk] = spmv_step_kernel<RP>(A);
     ldss[nk++] = lds_bytes(A);
   }
   fns[nk] = reinterpret_cast<const void*>(&k_cg_residual);

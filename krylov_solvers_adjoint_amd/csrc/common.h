@@ -62,6 +62,8 @@ constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
 constexpr int kMaxBand = 8;        // most distinct column offsets of a banded pattern
 constexpr int64_t kMaxBandSpan = int64_t(1) << 27;  // widest band (largest - smallest offset)
 constexpr int kPanelTiles = 64;    // widest column block of the panel tile order
+// a line walk needs at least one full workgroup of tile columns per line
+constexpr int64_t kMinWalkLine = int64_t(kIterBlock / kWave - 1) * kTileRows + 1;
 // a 64-row tile whose columns span more than this is "wide" (the span of a
 // 5-point stencil tile on a 13000-point grid line is ~26000)
 constexpr int64_t kLocalSpan = int64_t(1) << 17;
@@ -134,6 +136,8 @@ struct Ctx {
   BandOffsets band;
   int32_t panel;        // tiles per band span (0: rows in plain order)
   int32_t pblock;       // tiles per column block of the panel order
+  int64_t line;         // grid line length of a line-walk band (0: none)
+  int32_t line_chunks;  // line chunks per XCD in the line walk
 };
 
 // ---------------------------------------------------------------------------

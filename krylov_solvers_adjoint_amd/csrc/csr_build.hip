@@ -601,6 +601,7 @@ sla_status sample_locality(sla_csr A, hipStream_t st) {
 template <typename RP>
 sla_status detect_band(sla_csr A, hipStream_t st) {
   A->band.count = 0;
+  A->line = 0;
   BandOffsets bo{};
   if (A->nnz == 0 || !sample_offsets<RP>(A, st, &bo)) return SLA_OK;
   // the banded kernels address a tile's gathers by 32-bit offsets from one
@@ -642,6 +643,19 @@ sla_status detect_band(sla_csr A, hipStream_t st) {
     A->panel = int32_t(P);
     A->pblock = int32_t((P + nb - 1) / nb);
   }
+  // line walk: every offset of 64 or more in magnitude is +-L (one grid
+  // line), and both are present
+  int64_t L = 0;
+  bool lines = true;
+  for (int u = 0; u < bo.count; ++u) {
+    const int64_t a = std::abs(int64_t(bo.off[u]));
+    if (a < kTileRows) continue;
+    if (L == 0) L = a;
+    else if (a != L) lines = false;
+  }
+  // the walk takes -L and +L as the first and the last offset
+  lines = lines && bo.count >= 2 && bo.off[0] == -L && bo.off[bo.count - 1] == L;
+  A->line = (lines && L >= kMinWalkLine) ? L : 0;
   return SLA_OK;
 }
 

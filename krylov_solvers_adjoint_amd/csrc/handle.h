@@ -61,6 +61,9 @@ struct sla_csr_s {
   int64_t graph_block = 32;
   // solver workgroups per compute unit (1 or 2)
   int32_t wg_per_cu = 2;
+  // grid line length L of a band whose far offsets are +-L and whose other
+  // offsets lie within +-63 (0: the line walk does not apply)
+  int64_t line = 0;
   hipStream_t capture_stream = nullptr;
   std::map<int64_t, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
 };
@@ -71,6 +74,7 @@ namespace sla {
 sla_status ensure_workspace(sla_csr A, int64_t batch);
 bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
 bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
+bool use_lines(const sla_csr A);  // line-walk SpMV step (a banded pattern with far offsets +-L)?
 void release_workspace(sla_csr A);
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 

@@ -130,6 +130,27 @@ def stencil_csr(shape, stencil, rowptr_dtype=np.int32):
     return np.cumsum(rowptr).astype(rowptr_dtype), col.astype(np.int32), val
 
 
+def band_csr(n: int, offsets, diag: float, off: float = -1.0, rowptr_dtype=np.int32):
+    """CSR of the n x n band matrix with `diag` on the diagonal and `off` at
+    every column i + d (d in `offsets`, d != 0) that lies in [0, n).  Unlike
+    a grid stencil, couplings cross the ends of grid lines and n need not be
+    a multiple of the line length.  Columns come out ascending."""
+    ds = sorted(set(int(d) for d in offsets) | {0})
+    idx = np.arange(n)
+    entries = []
+    for d in ds:
+        ok = (idx + d >= 0) & (idx + d < n)
+        entries.append((idx[ok], idx[ok] + d, np.full(ok.sum(), diag if d == 0 else off)))
+    row = np.concatenate([e[0] for e in entries])
+    col = np.concatenate([e[1] for e in entries])
+    val = np.concatenate([e[2] for e in entries])
+    order = np.lexsort((col, row))
+    row, col, val = row[order], col[order], val[order]
+    rowptr = np.zeros(n + 1, np.int64)
+    np.add.at(rowptr, row + 1, 1)
+    return np.cumsum(rowptr).astype(rowptr_dtype), col.astype(np.int32), val
+
+
 def laplacian3d_csr(N: int):
     """7-point Laplacian on an N^3 grid: diagonal 6, neighbours -1."""
     st = {(0, 0, 0): 6.0}
