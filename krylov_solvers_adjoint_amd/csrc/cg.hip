@@ -279,14 +279,15 @@ size_t solver_lds_bytes(int cap, int waves) {
   return size_t(waves) * size_t(cap + (cap + 1) / 2) * sizeof(double);
 }
 
-// Sum of `count` partials, the same fixed order in every workgroup: thread t
-// adds part[t], part[t + 1024], ..., then the workgroup tree.  The result is
-// in every thread.
+// Sum of `count` partials, the same fixed order in every workgroup of NT
+// threads: thread t adds part[t], part[t + NT], ..., then the workgroup tree.
+// The result is in every thread.
+template <int NT = kIterBlock>
 __device__ __forceinline__ double sum_partials_all(const SLA_GLOBAL double* __restrict__ part,
                                                    int count, double* red) {
   double v = 0.0;
-  for (int i = threadIdx.x; i < count; i += kIterBlock) v = v + part[i];
-  return block_sum_all<kIterBlock>(v, red);
+  for (int i = threadIdx.x; i < count; i += NT) v = v + part[i];
+  return block_sum_all<NT>(v, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -323,7 +324,8 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
     const uint32_t lr = tile_lane(r0, n, lane);
     const TileIndex<RP> cur = ix;
     const int64_t tn = t + stride;
-    if (tn < tiles) ix = tile_index<NB, RP>(rowptr, mask, n, tn * kTileRows, tile_lane(tn * kTileRows, n, lane));
+    const int64_t tp = tn < tiles ? tn : t;  // unconditional load (see k_cg_spmv_lines)
+    ix = tile_index<NB, RP>(rowptr, mask, n, tp * kTileRows, tile_lane(tp * kTileRows, n, lane));
     double acc;
     if constexpr (NB > 0) acc = band_row<NB, RP>(band, v, n, nnz, r0, lr, ok, cur, g);
     else acc = wave_tile_row<RP>(col, v, cur, cap, lv, lc, g);
@@ -412,6 +414,7 @@ struct StepHead {
   int32_t stop;  // ST_RUNNING or the final state
 };
 
+template <int NT = kIterBlock>
 __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t s,
                                               double* red) {
   Scal* sc = c->scal + s;
@@ -421,7 +424,7 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
   StepHead h;
   h.k = sc->ka;
   const int64_t k = h.k;
-  const double rr = sum_partials_all(part + (k & 1) * G, G, red);
+  const double rr = sum_partials_all<NT>(part + (k & 1) * G, G, red);
   h.lag = k > 0;
   h.alpha = 0.0;
   h.beta = 0.0;
@@ -541,8 +544,8 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
     const TileIndex<RP> cur = ix;
     pos += wk.stride;
     const int64_t tn = next_tile(pos);
-    if (tn >= 0)
-      ix = tile_index<NB, RP>(rowptr, mask, n, tn * kTileRows, tile_lane(tn * kTileRows, n, lane));
+    const int64_t tp = tn >= 0 ? tn : t;  // unconditional load (see k_cg_spmv_lines)
+    ix = tile_index<NB, RP>(rowptr, mask, n, tp * kTileRows, tile_lane(tp * kTileRows, n, lane));
     // this row's own operands, loaded before the row sum's loads
     const double po = ld(pold + r0, lr);
     const double ro = ld(r + r0, lr);
@@ -576,15 +579,24 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
 //     neighbours are the previous tile's p_k, still in registers.  r and
 //     p_{k-1} thus come from memory once per row (plus the tiles just above
 //     and below each chunk), whatever the line length;
-//   * offsets within +-63 are gathered as in band_row: they fall in the
-//     tile's own cache lines or the neighbouring columns', which the other
-//     waves of the workgroup (columns u - w .. u - w + 15) walk in step.
+//   * NEAR1 (the offsets between -L and +L are -1, 0, +1): the +-1
+//     neighbours are the current tile's own p_k, moved across lanes, and at
+//     the two ends of the tile the rows just outside it, loaded (one address
+//     for the whole wave) together with the next tile, when the waves of the
+//     neighbouring columns load those rows' lines too;
+//   * otherwise offsets within +-63 are gathered as in band_row: they fall
+//     in the tile's own cache lines or the neighbouring columns'.
 // Lines are split into kXcds contiguous ranges, one per XCD; a range into
-// `chunks` chunks; a workgroup takes 16 adjacent columns of one chunk.
-template <typename RP, int NB>
-__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+// `chunks` chunks; a workgroup takes kLineWaves adjacent columns of one
+// chunk.  Workgroups of kLineWaves waves, two per CU: 16 waves per CU with
+// 128 registers each, enough to keep the next tile, its edge rows and the
+// current tile's values in flight together.
+template <typename RP, int NB, bool NEAR1>
+__global__ __launch_bounds__(kLineWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(kLineWavesPerEu)))
 void k_cg_spmv_lines(const Ctx* __restrict__ c) {
-  __shared__ double red[kWaves];
+  constexpr int NT = kLineWaves * kWave;
+  __shared__ double red[kLineWaves];
   const int64_t s = blockIdx.y;
   // context fields first (scalar loads, see k_cg_spmv)
   const int64_t n = c->n, nnz = c->nnz, tiles = c->tiles, L = c->line;
@@ -605,7 +617,7 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
     if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
     return;
   }
-  const StepHead h = step_head(c, s, red);
+  const StepHead h = step_head<NT>(c, s, red);
   const int64_t k = uniform(h.k);
   const double alpha = uniform(h.alpha), beta = uniform(h.beta);
   const bool lag = h.lag;
@@ -616,7 +628,7 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   if (h.stop != ST_RUNNING) {
     // last pass: only the deferred x update
     if (lag) {
-      const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, w);
+      const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kLineWaves, w);
       for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
         const int64_t i0 = t * kTileRows;
         if (i0 + lane < n) st(x + i0, lane, ld(x + i0, lane) + alpha * ld(pold + i0, lane));
@@ -629,12 +641,12 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   const Gather<true, false> g{r, pold, beta};
   const int64_t U = (L + kTileRows - 1) / kTileRows;  // tile columns per line
   const int64_t V = (n + L - 1) / L;                  // lines
-  const int64_t groups = (U + kWaves - 1) / kWaves;
+  const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = G / kXcds;
   const int64_t va = V * xcd / kXcds, vb = V * (xcd + 1) / kXcds;
   double pq = 0.0;
   for (int64_t unit = slot; unit < groups * chunks; unit += per_xcd) {
-    const int64_t u = (unit / chunks) * kWaves + w;
+    const int64_t u = (unit / chunks) * kLineWaves + w;
     const int64_t ch = unit % chunks;
     const int64_t v0 = va + (vb - va) * ch / chunks, v1 = va + (vb - va) * (ch + 1) / chunks;
     const int64_t col0 = u * kTileRows;
@@ -659,6 +671,27 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
     uint32_t lr = clamp_lane(len);
     double rc = ld(r + v0 * L + col0, lr), pc = ld(pold + v0 * L + col0, lr);
     TileIndex<RP> ix = tile_index<NB, RP>(rowptr, mask, n, v0 * L + col0, lr);
+    // rows just outside the tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
+    // clamped into [0, n)
+    auto edges = [&](int64_t e0, int64_t elen, double& rl, double& pl, double& rr, double& pr) {
+      const int64_t a = e0 > 0 ? e0 - 1 : 0;
+      const int64_t b = e0 + elen < n ? e0 + elen : n - 1;
+      rl = ld(r + a, 0u);
+      pl = ld(pold + a, 0u);
+      rr = ld(r + b, 0u);
+      pr = ld(pold + b, 0u);
+    };
+    // the current tile's edge rows live in scalar registers (the same value
+    // in every lane); the next tile's arrive in vector registers
+    double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
+    if constexpr (NEAR1) {
+      edges(v0 * L + col0, len, rl, pl, rr, pr);
+      rl = uniform(rl);
+      pl = uniform(pl);
+      rr = uniform(rr);
+      pr = uniform(pr);
+    }
+    wait_vmem();
     for (int64_t v = v0; v < v1; ++v) {
       const int64_t r0 = v * L + col0;
       const bool own = int64_t(lane) < len;
@@ -668,8 +701,13 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
       const int64_t rn0 = hasn ? r0 + L : r0;
       const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
       const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
+      double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+      if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
       const TileIndex<RP> cur = ix;
-      if (hasn && v + 1 < v1) ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
+      // unconditional (the current tile again when there is no next one): a
+      // conditional load would make the compiler copy the old value into its
+      // register first, which waits for older loads and stores
+      ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
       const double xo = ld(x + r0, lr);
       // near offsets, gathered; the other kinds read the row itself (no
       // branch; the value is not used)
@@ -679,12 +717,14 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
       const int32_t top = int32_t(n - 1 - base);
       // offsets are sorted: -L first, +L last, the near ones in between
       double gu[NB], gw[NB];
+      if constexpr (!NEAR1) {
 #pragma unroll
-      for (int t = 1; t < NB - 1; ++t) {
-        const int32_t o = t < band.count - 1 ? band.off[t] : 0;
-        int32_t j = d + o;
-        j = j < 0 ? 0 : (j > top ? top : j);
-        g.load_at(base, uint32_t(j), gu[t], gw[t]);
+        for (int t = 1; t < NB - 1; ++t) {
+          const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+          int32_t j = d + o;
+          j = j < 0 ? 0 : (j > top ? top : j);
+          g.load_at(base, uint32_t(j), gu[t], gw[t]);
+        }
       }
       // values at the slot positions of the row (see band_row)
       const int64_t s0 = uniform(int64_t(cur.s0));
@@ -705,6 +745,15 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
       // lanes past the end of a short tile compute its last row: take that
       // row's -L value (the previous tile was loaded lane for lane)
       const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+      // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+      // or, at the ends of the tile, from the rows just outside it
+      double pm1 = 0.0, pp1 = 0.0;
+      if constexpr (NEAR1) {
+        const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+        const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+        pm1 = lr == 0 ? rl + beta * pl : sm;
+        pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+      }
       double acc = 0.0;
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
@@ -713,7 +762,10 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
         double gv;
         if (t == 0) gv = pbelow;
         else if (t == NB - 1) gv = pnext;
-        else gv = t == band.count - 1 ? pnext : (o == 0 ? pcur : g.value(gu[t], gw[t]));
+        else if (t == band.count - 1) gv = pnext;
+        else if (o == 0) gv = pcur;
+        else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+        else gv = g.value(gu[t], gw[t]);
         const double sum = acc + a[t] * gv;
         acc = use ? sum : acc;
       }
@@ -727,12 +779,18 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
       pprev = pcur;
       rc = rn;
       pc = pn;
+      if constexpr (NEAR1) {
+        rl = uniform(rln);
+        pl = uniform(pln);
+        rr = uniform(rrn);
+        pr = uniform(prn);
+      }
       len = lenn;
       lr = lrn;
       if (!hasn) break;
     }
   }
-  pq = block_sum_all<kIterBlock>(pq, red);
+  pq = block_sum_all<NT>(pq, red);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
@@ -826,8 +884,8 @@ void k_cg_product(const Ctx* __restrict__ c) {
     const uint32_t lr = tile_lane(r0, n, lane);
     const TileIndex<RP> cur = ix;
     const int64_t tn = t + wk.stride;
-    if (tn < wk.end)
-      ix = tile_index<0, RP>(rowptr, nullptr, n, tn * kTileRows, tile_lane(tn * kTileRows, n, lane));
+    const int64_t tp = tn < wk.end ? tn : t;  // unconditional load (see k_cg_spmv_lines)
+    ix = tile_index<0, RP>(rowptr, nullptr, n, tp * kTileRows, tile_lane(tp * kTileRows, n, lane));
     const double po = ld(p + r0, lr);
     const double acc = wave_tile_row<RP>(col, vals, cur, cap, lv, lc, g);
     st(q + r0, lr, acc);
@@ -966,10 +1024,17 @@ template <typename RP>
 const void* spmv_step_kernel(const sla_csr A) {
   const int nb = band_class(A);
   if (use_lines(A)) {
+    // NEAR1: the offsets between -L and +L are only -1, 0, +1
+    bool near1 = true;
+    for (int t = 1; t + 1 < A->band.count; ++t)
+      near1 = near1 && A->band.off[t] >= -1 && A->band.off[t] <= 1;
+    if (near1 && nb <= 5)
+      return nb == 3 ? reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, true>)
+                     : reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, true>);
     switch (nb) {
-      case 3: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3>);
-      case 5: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5>);
-      default: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 8>);
+      case 3: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, false>);
+      case 5: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, false>);
+      default: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 8, false>);
     }
   }
   switch (nb) {
@@ -987,10 +1052,13 @@ const void* product_kernel(const sla_csr A) {
                          : reinterpret_cast<const void*>(&k_cg_product<RP, false>);
 }
 
-sla_status launch_ctx_kernel(const void* fn, dim3 grid, size_t lds, const Ctx* cd,
+// Threads per workgroup of the SpMV step kernel.
+unsigned spmv_step_block(const sla_csr A) { return use_lines(A) ? kLineWaves * kWave : kIterBlock; }
+
+sla_status launch_ctx_kernel(const void* fn, dim3 grid, unsigned block, size_t lds, const Ctx* cd,
                              hipStream_t st) {
   void* args[1] = {&cd};
-  const hipError_t e = hipLaunchKernel(fn, grid, dim3(kIterBlock), args, lds, st);
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(block), args, lds, st);
   if (e != hipSuccess) {
     set_error("kernel launch failed: %s", hipGetErrorString(e));
     return SLA_ERR_DEVICE;
@@ -1003,9 +1071,10 @@ sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
   if (use_split(A)) {
     k_cg_direction<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
-    SLA_TRY(launch_ctx_kernel(product_kernel<RP>(A), grid2, lds_bytes(A), A->ctx_dev, st));
+    SLA_TRY(launch_ctx_kernel(product_kernel<RP>(A), grid2, kIterBlock, lds_bytes(A), A->ctx_dev,
+                              st));
   } else {
-    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A), grid2, lds_bytes(A),
+    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A), grid2, spmv_step_block(A), lds_bytes(A),
                               A->ctx_dev, st));
   }
   k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
@@ -1094,7 +1163,7 @@ void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool
     // of (16-column group, chunk) units: per_xcd / gcd(groups, per_xcd)
     const int64_t per_xcd = A->grid / kXcds;
     const int64_t U = (c.line + kTileRows - 1) / kTileRows;
-    const int64_t groups = (U + kWaves - 1) / kWaves;
+    const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
     int64_t a = per_xcd, b = groups;
     while (b != 0) {
       const int64_t t = a % b;
@@ -1316,22 +1385,26 @@ namespace {
 template <typename RP>
 sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), 1u);
-  const dim3 block(kIterBlock, 1u);
   // the SpMV step is one kernel, or the direction and product passes
   const bool split = use_split(A);
   const void* fns[3];
   size_t ldss[3];
+  unsigned blocks[3];
   int nk = 0;
   if (split) {
     fns[nk] = reinterpret_cast<const void*>(&k_cg_direction);
+    blocks[nk] = kIterBlock;
     ldss[nk++] = 0;
     fns[nk] = product_kernel<RP>(A);
+    blocks[nk] = kIterBlock;
     ldss[nk++] = lds_bytes(A);
   } else {
     fns[nk] = spmv_step_kernel<RP>(A);
+    blocks[nk] = spmv_step_block(A);
     ldss[nk++] = lds_bytes(A);
   }
   fns[nk] = reinterpret_cast<const void*>(&k_cg_residual);
+  blocks[nk] = kIterBlock;
   ldss[nk++] = 0;
   std::vector<hipEvent_t> ev(size_t(2 * reps), nullptr);
   for (auto& e : ev) SLA_TRY_HIP(hipEventCreate(&e));
@@ -1340,8 +1413,8 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
   for (int k = 0; k < nk && status == SLA_OK; ++k) {
     void* args[1] = {&A->ctx_dev};
     for (int64_t r = 0; r < reps; ++r) {
-      hipError_t e = hipExtLaunchKernel(fns[k], grid2, block, args, ldss[k], st, ev[2 * r],
-                                        ev[2 * r + 1], 0);
+      hipError_t e = hipExtLaunchKernel(fns[k], grid2, dim3(blocks[k]), args, ldss[k], st,
+                                        ev[2 * r], ev[2 * r + 1], 0);
       if (e != hipSuccess) {
         set_error("timed launch failed: %s", hipGetErrorString(e));
         status = SLA_ERR_DEVICE;

@@ -62,7 +62,11 @@ constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
 constexpr int kMaxBand = 8;        // most distinct column offsets of a banded pattern
 constexpr int64_t kMaxBandSpan = int64_t(1) << 27;  // widest band (largest - smallest offset)
 constexpr int kPanelTiles = 64;    // widest column block of the panel tile order
-// a line walk needs at least one full workgroup of tile columns per line
+// line walk: workgroups of 8 waves, two per CU (4 waves per SIMD, 128
+// registers each)
+constexpr int kLineWaves = 8;
+constexpr int kLineWavesPerEu = 2 * kLineWaves / 4;
+// a line walk needs at least 16 tile columns per line
 constexpr int64_t kMinWalkLine = int64_t(kIterBlock / kWave - 1) * kTileRows + 1;
 // a 64-row tile whose columns span more than this is "wide" (the span of a
 // 5-point stencil tile on a 13000-point grid line is ~26000)
@@ -191,6 +195,13 @@ template <typename T>
 __device__ __forceinline__ void st(SLA_GLOBAL T* base, uint32_t off, T v) {
   *reinterpret_cast<SLA_GLOBAL T*>(scalar_base(base) + uint64_t(off * uint32_t(sizeof(T)))) = v;
 }
+
+// Wait until every vector memory operation of this wave has completed
+// (s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima).  Placed
+// after a loop's prologue loads, it keeps the compiler from merging those
+// pending loads into the loop head, where the wait for them would also wait
+// for the stores of the previous iteration.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Index of this thread's wave in its workgroup, as a wave-uniform (scalar)
 // value, so that everything derived from it stays in scalar registers.
