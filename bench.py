@@ -69,7 +69,27 @@ def spmv_step_bytes_split(n: int, nnz: int, rp_bytes: int) -> int:
 
 
 def spmv_variant(P) -> str:
-    return "split" if P.split else ("banded" if P.banded else "csr")
+    if P.split:
+        return "split"
+    if P.lines:
+        return "lines"
+    return "banded" if P.banded else "csr"
+
+
+# kernel that runs the SpMV step under each variant
+STEP_KERNEL = {"lines": "k_cg_spmv_lines", "banded": "k_cg_spmv", "csr": "k_cg_spmv",
+               "split": "k_cg_direction+k_cg_product"}
+
+
+def spmv_bytes_for(variant: str, n: int, nnz: int, rp_bytes: int) -> int:
+    """Algorithmic bytes of one SpMV step under `variant` (the line walk
+    moves the same arrays as the banded kernel: values, mask bytes, one row
+    pointer per tile, r, p_{k-1}, x read once, p_k, q, x written once)."""
+    if variant in ("lines", "banded"):
+        return spmv_step_bytes_banded(n, nnz, rp_bytes)
+    if variant == "split":
+        return spmv_step_bytes_split(n, nnz, rp_bytes)
+    return spmv_step_bytes(n, nnz, rp_bytes)
 
 
 def pattern_grad_bytes(n: int, nnz: int, rp_bytes: int) -> int:
@@ -174,8 +194,8 @@ def bench_headline(args):
         kernel_ms=kern,
     )
     res["pct_peak"] = 100.0 * res["eff_GBps"] / HBM_PEAK_GBPS
-    res["banded"] = P.banded
-    res["spmv_bytes"] = (spmv_step_bytes_banded if res["banded"] else spmv_step_bytes)(n, nnz, 4)
+    res["spmv"] = spmv_variant(P)
+    res["spmv_bytes"] = spmv_bytes_for(res["spmv"], n, nnz, 4)
     del P
     torch.cuda.synchronize()
     return res
@@ -201,9 +221,9 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int):
     free1 = torch.cuda.mem_get_info()[0]
     kern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
     nnz = P.nnz
-    banded = P.banded
-    sbytes = (spmv_step_bytes_banded if banded else spmv_step_bytes)(n, nnz, rp_bytes)
-    out = dict(n=n, nnz=nnz, rowptr="i64" if rp_bytes == 8 else "i32", banded=banded,
+    variant = spmv_variant(P)
+    sbytes = spmv_bytes_for(variant, n, nnz, rp_bytes)
+    out = dict(n=n, nnz=nnz, rowptr="i64" if rp_bytes == 8 else "i32", spmv=variant,
                iterations=info.iterations, solve_ms=1e3 * wall,
                ms_per_iteration=1e3 * wall / info.iterations,
                it_per_s=info.iterations / wall,
@@ -257,7 +277,7 @@ def bench_rgg(n: int, kernel_reps: int):
     kern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
     nnz = P.nnz
     its = fi.iterations + ai.iterations
-    step_bytes = (spmv_step_bytes_split if P.split else spmv_step_bytes)(n, nnz, 4)
+    sbytes = spmv_bytes_for(spmv_variant(P), n, nnz, 4)
     out = dict(n=n, nnz=nnz, spmv=spmv_variant(P), csr_build_ms=build_ms,
                iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
                solve_ms=1e3 * fwd, adjoint_ms=1e3 * adj,
@@ -265,7 +285,7 @@ def bench_rgg(n: int, kernel_reps: int):
                eff_GBps=(its * canonical_bytes(n, nnz, 4) + pattern_grad_bytes(n, nnz, 4)) /
                (fwd + adj) / 1e9,
                kernel_ms=kern,
-               spmv_GBps=step_bytes / (kern["spmv_step"] * 1e-3) / 1e9)
+               spmv_GBps=sbytes / (kern["spmv_step"] * 1e-3) / 1e9)
     out["pct_peak"] = 100.0 * out["eff_GBps"] / HBM_PEAK_GBPS
     del P, v, b, g, x, gb, gv
     torch.cuda.synchronize()
@@ -381,11 +401,12 @@ def main():
     digest = source_digest()
     spmv_ms = head["kernel_ms"]["spmv_step"]
     achieved = head["spmv_bytes"] / (spmv_ms * 1e-3) / 1e9
+    kname = STEP_KERNEL[head["spmv"]]
     roofline = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=achieved / HBM_PEAK_GBPS,
-                    traffic=traffic_from_profile("k_cg_spmv", "poisson1000", digest),
-                    kernel=("k_cg_spmv<banded> " if head["banded"] else "k_cg_spmv ") +
-                    "(SpMV + direction update + deferred x update + p.Ap)",
+                    traffic=traffic_from_profile(kname, "poisson1000", digest),
+                    kernel=f"{kname} ({head['spmv']}: SpMV + direction update + deferred x "
+                           "update + p.Ap partials)",
                     kernel_ms=spmv_ms, algorithmic_bytes=head["spmv_bytes"],
                     source_digest=digest)
     cpu = None
@@ -407,7 +428,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "poisson1000_fixed1000_fwd_adj", "grid": "1000x1000",
                    "n": head["n"], "nnz": head["nnz"], "index": "i32/i32",
-                   "spmv": "banded" if head["banded"] else "csr",
+                   "spmv": head["spmv"],
                    "iterations_fwd": head["iterations_fwd"],
                    "iterations_adj": head["iterations_adj"], "parallelism": "none (1 GPU)"},
         "eff_GBps": head["eff_GBps"],
