@@ -85,6 +85,14 @@ def _bind(lib):
                                    ctypes.POINTER(_Info)]
     lib.oracle_pattern_grad.restype = None
     lib.oracle_pattern_grad.argtypes = [_I64, _P, _P, _P, _P, _P]
+    lib.oracle_pcg_jacobi.restype = ctypes.c_int
+    lib.oracle_pcg_jacobi.argtypes = [_I64, _P, _P, _P, _P, _P, _D, _I64, ctypes.c_int,
+                                      ctypes.POINTER(_Info), _P, _P, _P, _P]
+    lib.oracle_adjoint_jacobi.restype = ctypes.c_int
+    lib.oracle_adjoint_jacobi.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P, _D, _I64,
+                                          ctypes.POINTER(_Info)]
+    lib.oracle_matvec_grad.restype = None
+    lib.oracle_matvec_grad.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
@@ -233,6 +241,56 @@ def adjoint(A: CSR, x, g, tol: float, maxit: int, lib=None):
                           _ptr(gv), float(tol), int(maxit), ctypes.byref(info))
     return gb, gv[:A.nnz].copy(), CGInfo(int(st), int(info.iterations), float(info.rr),
                                          float(info.bb), bool(info.converged))
+
+
+def pcg_jacobi(A: CSR, b, tol: float, maxit: int, x0=None, history: bool = False, lib=None):
+    """Jacobi-preconditioned CG (M = diag(A)): x, CGInfo[, (alpha, beta, rr,
+    rz) history arrays]."""
+    L = lib or _load()
+    b = _c(b, np.float64)
+    x = _c(x0, np.float64).copy() if x0 is not None else np.zeros(A.n, np.float64)
+    info = _Info()
+    ha = hb = hr = hz = None
+    if history:
+        ha, hb, hr, hz = (np.zeros(max(maxit, 1)) for _ in range(4))
+    st = L.oracle_pcg_jacobi(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                             _ptr(_c(A.vals, np.float64)), _ptr(b), _ptr(x), float(tol),
+                             int(maxit), 1 if x0 is not None else 0, ctypes.byref(info),
+                             _ptr(ha), _ptr(hb), _ptr(hr), _ptr(hz))
+    out = CGInfo(int(st), int(info.iterations), float(info.rr), float(info.bb),
+                 bool(info.converged))
+    if history:
+        k = out.iterations
+        return x, out, (ha[:k].copy(), hb[:k].copy(), hr[:k].copy(), hz[:k].copy())
+    return x, out
+
+
+def adjoint_jacobi(A: CSR, x, g, tol: float, maxit: int, lib=None):
+    """The adjoint of a Jacobi-PCG solve: (grad_b = lambda, grad_vals, CGInfo)."""
+    L = lib or _load()
+    x = _c(x, np.float64)
+    g = _c(g, np.float64)
+    gb = np.zeros(A.n, np.float64)
+    gv = np.zeros(max(A.nnz, 1), np.float64)
+    info = _Info()
+    st = L.oracle_adjoint_jacobi(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                                 _ptr(_c(A.vals, np.float64)), _ptr(x), _ptr(g), _ptr(gb),
+                                 _ptr(gv), float(tol), int(maxit), ctypes.byref(info))
+    return gb, gv[:A.nnz].copy(), CGInfo(int(st), int(info.iterations), float(info.rr),
+                                         float(info.bb), bool(info.converged))
+
+
+def matvec_grad(A: CSR, x, g, lib=None):
+    """Backward of y = A x for g = dL/dy: (grad_x = A^T g, grad_vals = g_i x_j
+    on the stored slots)."""
+    L = lib or _load()
+    x = _c(x, np.float64)
+    g = _c(g, np.float64)
+    gx = np.zeros(A.n, np.float64)
+    gv = np.zeros(max(A.nnz, 1), np.float64)
+    L.oracle_matvec_grad(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                         _ptr(_c(A.vals, np.float64)), _ptr(x), _ptr(g), _ptr(gx), _ptr(gv))
+    return gx, gv[:A.nnz].copy()
 
 
 def pattern_grad(A: CSR, lam, x, lib=None) -> np.ndarray:

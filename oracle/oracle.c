@@ -324,6 +324,166 @@ void oracle_pattern_grad(int64_t n, const int64_t* rowptr, const int32_t* col,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Jacobi-preconditioned CG                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Solve A x = b by CG preconditioned with M = diag(A), the preconditioner
+ * the pages name for the PyTorch-native backend (Significance / limitations).
+ * Textbook preconditioned CG, step by step:
+ *   r0 = b - A x0;  z0 = r0 / d (elementwise, d = the stored diagonal);
+ *   p0 = z0;  then per iteration
+ *   q = A p;  alpha = (r.z) / (p.q);  x += alpha p;  r -= alpha q;
+ *   z = r / d;  beta = (r.z)_new / (r.z);  p = z + beta p.
+ * The stopping test is the plain CG one, on the residual itself:
+ * r.r <= (tol*tol) * b.b before each iteration.  A missing or non-positive
+ * diagonal entry (impossible for an SPD matrix) returns ORACLE_ERR_NOT_SPD
+ * before any iteration.  hist_rr receives r.r after each iteration, hist_rz
+ * (optional) r.z.
+ */
+int oracle_pcg_jacobi(int64_t n, const int64_t* rowptr, const int32_t* col,
+                      const double* vals, const double* b, double* x, double tol,
+                      int64_t maxit, int use_x0, oracle_cg_info* info,
+                      double* hist_alpha, double* hist_beta, double* hist_rr,
+                      double* hist_rz) {
+  size_t bytes = sizeof(double) * (size_t)(n > 0 ? n : 1);
+  double* r = (double*)malloc(bytes);
+  double* z = (double*)malloc(bytes);
+  double* p = (double*)malloc(bytes);
+  double* q = (double*)malloc(bytes);
+  double* d = (double*)malloc(bytes);
+  int status = ORACLE_OK;
+  int64_t k = 0;
+  double bb = 0.0, rr = 0.0, rz = 0.0, stop = 0.0;
+
+  /* the diagonal: the stored slot (i, i) of each row */
+  for (int64_t i = 0; i < n; ++i) {
+    d[i] = 0.0;
+    for (int64_t s = rowptr[i]; s < rowptr[i + 1]; ++s)
+      if (col[s] == i) d[i] = vals[s];
+    if (!(d[i] > 0.0)) status = ORACLE_ERR_NOT_SPD;
+  }
+  if (status == ORACLE_OK) {
+    if (use_x0) {
+      oracle_spmv(n, rowptr, col, vals, x, q);
+      for (int64_t i = 0; i < n; ++i) r[i] = b[i] - q[i];
+    } else {
+      for (int64_t i = 0; i < n; ++i) {
+        x[i] = 0.0;
+        r[i] = b[i];
+      }
+    }
+    for (int64_t i = 0; i < n; ++i) {
+      z[i] = r[i] / d[i];
+      p[i] = z[i];
+    }
+    bb = oracle_dot(n, b, b);
+    rr = oracle_dot(n, r, r);
+    rz = oracle_dot(n, r, z);
+    stop = (tol * tol) * bb;
+    if (!isfinite(bb) || !isfinite(rr) || !isfinite(rz)) status = ORACLE_ERR_NONFINITE;
+  } else if (!use_x0) {
+    for (int64_t i = 0; i < n; ++i) x[i] = 0.0;
+  }
+  while (status == ORACLE_OK && k < maxit) {
+    if (rr <= stop) break;
+    oracle_spmv(n, rowptr, col, vals, p, q); /* q = A p */
+    double pq = oracle_dot(n, p, q);
+    if (!isfinite(pq)) {
+      status = ORACLE_ERR_NONFINITE;
+      break;
+    }
+    if (!(pq > 0.0)) {
+      status = ORACLE_ERR_NOT_SPD;
+      break;
+    }
+    double alpha = rz / pq;
+    for (int64_t i = 0; i < n; ++i) {
+      x[i] = x[i] + alpha * p[i];
+      r[i] = r[i] - alpha * q[i];
+    }
+    for (int64_t i = 0; i < n; ++i) z[i] = r[i] / d[i];
+    double rr_new = oracle_dot(n, r, r);
+    double rz_new = oracle_dot(n, r, z);
+    if (!isfinite(rr_new) || !isfinite(rz_new)) {
+      status = ORACLE_ERR_NONFINITE;
+      break;
+    }
+    double beta = rz_new / rz;
+    for (int64_t i = 0; i < n; ++i) p[i] = z[i] + beta * p[i];
+    if (hist_alpha) hist_alpha[k] = alpha;
+    if (hist_beta) hist_beta[k] = beta;
+    if (hist_rr) hist_rr[k] = rr_new;
+    if (hist_rz) hist_rz[k] = rz_new;
+    rr = rr_new;
+    rz = rz_new;
+    k = k + 1;
+  }
+  info->iterations = k;
+  info->rr = rr;
+  info->bb = bb;
+  info->converged = (status == ORACLE_OK && rr <= stop) ? 1 : 0;
+  free(r);
+  free(z);
+  free(p);
+  free(q);
+  free(d);
+  return status;
+}
+
+/* The adjoint of a Jacobi-PCG solve: the same steps as oracle_adjoint, with
+ * lambda from oracle_pcg_jacobi on the explicit A^T. */
+int oracle_adjoint_jacobi(int64_t n, const int64_t* rowptr, const int32_t* col,
+                          const double* vals, const double* x, const double* g,
+                          double* grad_b, double* grad_vals, double tol,
+                          int64_t maxit, oracle_cg_info* info) {
+  int64_t nnz = rowptr[n];
+  int64_t* rowptr_t = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int32_t* col_t = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+  double* vals_t = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
+  oracle_transpose(n, rowptr, col, vals, rowptr_t, col_t, vals_t);
+  int symmetric = 1;
+  for (int64_t i = 0; i <= n && symmetric; ++i)
+    if (rowptr_t[i] != rowptr[i]) symmetric = 0;
+  for (int64_t k = 0; k < nnz && symmetric; ++k)
+    if (col_t[k] != col[k] || memcmp(&vals_t[k], &vals[k], sizeof(double)) != 0)
+      symmetric = 0;
+  int status = oracle_pcg_jacobi(n, rowptr_t, col_t, vals_t, g, grad_b, tol, maxit, 0,
+                                 info, NULL, NULL, NULL, NULL);
+  oracle_pattern_grad(n, rowptr, col, grad_b, x, grad_vals);
+  free(rowptr_t);
+  free(col_t);
+  free(vals_t);
+  if (status == ORACLE_OK && !symmetric) status = ORACLE_ERR_NOT_SYMMETRIC;
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass of the product y = A x                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For a loss L with g = dL/dy (Methodology 1, the differentiable .matvec):
+ *   grad_x    = A^T g                   (explicit transpose, then SpMV)
+ *   grad_vals = g_i x_j on every stored slot (i, j), nothing else.
+ */
+void oracle_matvec_grad(int64_t n, const int64_t* rowptr, const int32_t* col,
+                        const double* vals, const double* x, const double* g,
+                        double* grad_x, double* grad_vals) {
+  int64_t nnz = rowptr[n];
+  int64_t* rowptr_t = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int32_t* col_t = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+  double* vals_t = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
+  oracle_transpose(n, rowptr, col, vals, rowptr_t, col_t, vals_t);
+  oracle_spmv(n, rowptr_t, col_t, vals_t, g, grad_x);
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) grad_vals[k] = g[i] * x[col[k]];
+  free(rowptr_t);
+  free(col_t);
+  free(vals_t);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Threads                                                                   */
 /* ------------------------------------------------------------------------ */
 #ifdef _OPENMP

@@ -460,6 +460,172 @@ def pin_batched_shift_spectrum(lib=None):
         assert np.linalg.norm(xs[s] - v / (lam + shifts[s])) <= 1e-12 * np.linalg.norm(v)
 
 
+# --------------------------------------------------------------------------
+# Jacobi-preconditioned CG
+# --------------------------------------------------------------------------
+
+def _scaled_spd(n, seed, spread=2.0):
+    """S M S for a random diagonally dominant SPD M and S = diag(10^U(-spread, spread)):
+    SPD, with a diagonal spanning many orders of magnitude."""
+    A0, M = _random_spd_csr(n, 0.15, seed)
+    rng = np.random.default_rng(seed + 100)
+    sd = 10.0 ** rng.uniform(-spread, spread, n)
+    rows = np.repeat(np.arange(n), np.diff(A0.rowptr))
+    # s_i s_j first: the product commutes exactly, so A stays bitwise symmetric
+    vals = A0.vals * (sd[rows] * sd[A0.col])
+    return oracle.CSR(n, A0.rowptr, A0.col, vals), M * np.outer(sd, sd)
+
+
+def pin_pcg_uniform_diagonal(lib=None):
+    """With M = 4 I (the Poisson diagonal) the preconditioner only rescales
+    z, p and q by powers of two: the iterates, beta and r.r are CG's bit for
+    bit, and alpha is exactly 4 times CG's."""
+    for N in (16, 40):
+        A = _poisson(N)
+        b = W.uniform_rhs(N * N, 3)
+        x1, i1, (a1, b1, r1) = oracle.cg(A, b, 1e-12, 5000, history=True, lib=lib)
+        x2, i2, (a2, b2, r2, z2) = oracle.pcg_jacobi(A, b, 1e-12, 5000, history=True, lib=lib)
+        assert i1.iterations == i2.iterations and i2.converged
+        assert np.array_equal(x1, x2) and np.array_equal(b1, b2) and np.array_equal(r1, r2)
+        assert np.array_equal(4.0 * a1, a2) and np.array_equal(r1 / 4.0, z2)
+
+
+def pin_pcg_scaled_equivalence(lib=None):
+    """Jacobi PCG on A is CG on D^-1/2 A D^-1/2 (b -> D^-1/2 b): PCG's r.z
+    after each iteration equals that CG's r.r, and x = D^-1/2 x_hat."""
+    n = 60
+    A, M = _scaled_spd(n, 7)
+    d = np.diag(M).copy()
+    h = 1.0 / np.sqrt(d)
+    Ah = M * np.outer(h, h)
+    rows, cols = np.nonzero(Ah)
+    rp = np.zeros(n + 1, np.int64)
+    np.add.at(rp, rows + 1, 1)
+    Ahc = oracle.CSR(n, np.cumsum(rp), cols.astype(np.int32), Ah[rows, cols].copy())
+    b = W.normal_rhs(n, 8)
+    x, info, (al, be, rr, rz) = oracle.pcg_jacobi(A, b, 1e-13, 500, history=True, lib=lib)
+    xh, ih, (alh, beh, rrh) = oracle.cg(Ahc, h * b, 1e-30, len(rz), history=True, lib=lib)
+    k = min(12, len(rz))
+    assert np.allclose(rz[:k], rrh[:k], rtol=1e-8, atol=0)
+    assert np.allclose(be[:k], beh[:k], rtol=1e-8, atol=0)
+    assert np.allclose(al[:k], alh[:k], rtol=1e-8, atol=0)
+    assert info.converged and np.linalg.norm(x - h * xh) <= 1e-8 * np.linalg.norm(x)
+
+
+def pin_pcg_diagonal_one_step(lib=None):
+    """A diagonal A: z0 is already the solution, so PCG stops after one step."""
+    n = 50
+    rng = np.random.default_rng(11)
+    d = 10.0 ** rng.uniform(-3, 3, n)
+    A = oracle.CSR(n, np.arange(n + 1, dtype=np.int64), np.arange(n, dtype=np.int32), d)
+    b = rng.uniform(-1, 1, n)
+    x, info = oracle.pcg_jacobi(A, b, 1e-12, 100, lib=lib)
+    assert info.iterations == 1 and info.converged
+    assert np.max(np.abs(x - b / d) / np.abs(b / d)) <= 8 * EPS
+
+
+def pin_pcg_dense_lu(lib=None):
+    """Against dense LU on a badly scaled SPD matrix, where Jacobi also needs
+    fewer iterations than plain CG."""
+    n = 80
+    A, M = _scaled_spd(n, 12, spread=2.5)
+    b = W.normal_rhs(n, 13)
+    xl = np.linalg.solve(M, b)
+    x, info = oracle.pcg_jacobi(A, b, 1e-13, 5000, lib=lib)
+    x_cg, info_cg = oracle.cg(A, b, 1e-13, 5000, lib=lib)
+    assert info.converged
+    assert np.linalg.norm(x - xl) <= 1e-8 * np.linalg.norm(xl)
+    assert info.iterations < info_cg.iterations
+
+
+def pin_pcg_statuses(lib=None):
+    """A missing, zero or negative diagonal entry is NOT_SPD before any step;
+    b = 0 converges in 0 steps."""
+    n = 4
+    rp = np.array([0, 2, 4, 6, 8], np.int64)
+    col = np.array([0, 1, 0, 1, 2, 3, 2, 3], np.int32)
+    for bad in (0.0, -1.0):
+        vals = np.array([2.0, -1.0, -1.0, 2.0, bad, 0.5, 0.5, 2.0])
+        x, info = oracle.pcg_jacobi(oracle.CSR(n, rp, col, vals), np.ones(n), 1e-10, 10, lib=lib)
+        assert info.status == oracle.ERR_NOT_SPD and info.iterations == 0
+    col2 = np.array([0, 1, 0, 1, 3, 3, 2, 3], np.int32)   # row 2 has no diagonal slot
+    vals = np.array([2.0, -1.0, -1.0, 2.0, 0.5, 0.0, 0.5, 2.0])
+    rp2 = np.array([0, 2, 4, 5, 8], np.int64)
+    x, info = oracle.pcg_jacobi(oracle.CSR(n, rp2, np.array([0, 1, 0, 1, 3, 1, 2, 3], np.int32), vals),
+                                np.ones(n), 1e-10, 10, lib=lib)
+    assert info.status == oracle.ERR_NOT_SPD
+    A = _poisson(5)
+    x, info = oracle.pcg_jacobi(A, np.zeros(25), 1e-10, 10, lib=lib)
+    assert info.status == oracle.OK and info.iterations == 0 and not np.any(x)
+
+
+def pin_adjoint_jacobi(lib=None):
+    """The adjoint of the Jacobi-PCG solve: g.x = lambda.b, the slot identity,
+    lambda against dense LU on A^T, and central differences over the slots."""
+    n = 40
+    A, M = _scaled_spd(n, 21, spread=1.5)
+    b = W.normal_rhs(n, 22)
+    g = W.normal_rhs(n, 23)
+    x, _ = oracle.pcg_jacobi(A, b, 1e-14, 2000, lib=lib)
+    gb, gv, info = oracle.adjoint_jacobi(A, x, g, 1e-14, 2000, lib=lib)
+    assert info.status == oracle.OK and info.converged
+    assert abs(g @ x - gb @ b) <= 1e-9 * abs(g @ x)
+    assert abs(A.vals @ gv + gb @ b) <= 1e-9 * abs(gb @ b)
+    assert np.linalg.norm(gb - np.linalg.solve(M.T, g)) <= 1e-8 * np.linalg.norm(gb)
+    rows = np.repeat(np.arange(n), np.diff(A.rowptr))
+    for k in range(0, A.nnz, max(1, A.nnz // 25)):
+        dlt = 1e-6 * max(1.0, abs(A.vals[k]))
+        Mp, Mm = M.copy(), M.copy()
+        Mp[rows[k], A.col[k]] += dlt
+        Mm[rows[k], A.col[k]] -= dlt
+        fd = (_dense_loss(Mp, b, g) - _dense_loss(Mm, b, g)) / (2 * dlt)
+        assert abs(fd - gv[k]) <= 1e-5 * np.max(np.abs(gv)), k
+
+
+# --------------------------------------------------------------------------
+# Backward of the SpMV
+# --------------------------------------------------------------------------
+
+def _random_nonsym_csr(n, density, seed):
+    rng = np.random.default_rng(seed)
+    M = np.where(rng.random((n, n)) < density, rng.uniform(-2, 2, (n, n)), 0.0)
+    M[3, 7] = 0.0
+    rows, cols = np.nonzero(M)
+    rows = np.append(rows, 3)
+    cols = np.append(cols, 7)   # a stored explicit zero
+    order = np.lexsort((cols, rows))
+    rows, cols = rows[order], cols[order]
+    rp = np.zeros(n + 1, np.int64)
+    np.add.at(rp, rows + 1, 1)
+    return oracle.CSR(n, np.cumsum(rp), cols.astype(np.int32), M[rows, cols].copy()), M, rows, cols
+
+
+def pin_matvec_grad(lib=None):
+    """y = A x with L = g.y: grad_x = A^T g (dense, within the summation
+    bound), g.(A x) = (A^T g).x = sum_k vals_k grad_k, central differences in
+    the slots, and a stored zero still gets g_i x_j."""
+    n = 50
+    A, M, rows, cols = _random_nonsym_csr(n, 0.1, 31)
+    x = W.normal_rhs(n, 32)
+    g = W.normal_rhs(n, 33)
+    gx, gv = oracle.matvec_grad(A, x, g, lib=lib)
+    dense = M.T @ g
+    bound = 4 * n * EPS * (np.abs(M.T) @ np.abs(g))
+    assert np.all(np.abs(gx - dense) <= bound + 1e-300)
+    y = oracle.spmv(A, x, lib=lib)
+    assert abs(g @ y - gx @ x) <= 1e-12 * (np.abs(g) @ np.abs(y) + 1)
+    assert abs(g @ y - A.vals @ gv) <= 1e-12 * (np.abs(g) @ np.abs(y) + 1)
+    k37 = [k for k in range(A.nnz) if rows[k] == 3 and cols[k] == 7][0]
+    assert A.vals[k37] == 0.0 and gv[k37] == g[3] * x[7] != 0.0
+    for k in range(0, A.nnz, 17):
+        dlt = 1e-3
+        Mp, Mm = M.copy(), M.copy()
+        Mp[rows[k], cols[k]] += dlt
+        Mm[rows[k], cols[k]] -= dlt
+        fd = (g @ (Mp @ x) - g @ (Mm @ x)) / (2 * dlt)
+        assert abs(fd - gv[k]) <= 1e-9 * max(1.0, abs(gv[k])), k
+
+
 ALL_PINS = [
     pin_csr_poisson_closed_form, pin_csr_brute_force, pin_csr_rgg_symmetric,
     pin_spmv_eigenpairs, pin_spmv_dense, pin_dot,
@@ -467,4 +633,6 @@ ALL_PINS = [
     pin_cg_ritz, pin_cg_energy, pin_cg_statuses, pin_cg_warm_start,
     pin_adjoint_identities, pin_adjoint_fd, pin_adjoint_support, pin_adjoint_golden,
     pin_adjoint_nonsymmetric_flag, pin_batched_shift_spectrum,
+    pin_pcg_uniform_diagonal, pin_pcg_scaled_equivalence, pin_pcg_diagonal_one_step,
+    pin_pcg_dense_lu, pin_pcg_statuses, pin_adjoint_jacobi, pin_matvec_grad,
 ]

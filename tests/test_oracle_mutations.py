@@ -33,6 +33,17 @@ MUTATIONS = {
     "rowptr_shifted": ("rowptr[keys[s].row + 1] += 1;", "rowptr[keys[s].row] += 1;"),
     "warm_start_sign": ("r[i] = b[i] - q[i];", "r[i] = q[i] - b[i];"),
     "transpose_keeps_rows": ("col_t[dst] = (int32_t)i;", "col_t[dst] = (int32_t)j;"),
+    "pcg_beta_uses_rr": ("double beta = rz_new / rz;", "double beta = rr_new / rr;"),
+    "pcg_alpha_uses_rr": ("double alpha = rz / pq;", "double alpha = rr / pq;"),
+    "pcg_z_times_d": ("z[i] = r[i] / d[i];", "z[i] = r[i] * d[i];"),
+    "pcg_p_from_r": ("p[i] = z[i] + beta * p[i];", "p[i] = r[i] + beta * p[i];"),
+    "pcg_diag_from_row_start": ("if (col[s] == i) d[i] = vals[s];", "d[i] = vals[rowptr[i]];"),
+    "pcg_adjoint_rhs_is_x": ("oracle_pcg_jacobi(n, rowptr_t, col_t, vals_t, g, grad_b",
+                             "oracle_pcg_jacobi(n, rowptr_t, col_t, vals_t, x, grad_b"),
+    "matvec_grad_sign": ("grad_vals[k] = g[i] * x[col[k]];", "grad_vals[k] = -(g[i] * x[col[k]]);"),
+    "matvec_grad_no_transpose": ("oracle_spmv(n, rowptr_t, col_t, vals_t, g, grad_x);",
+                                 "oracle_spmv(n, rowptr, col, vals, g, grad_x);"),
+    "matvec_grad_swapped": ("grad_vals[k] = g[i] * x[col[k]];", "grad_vals[k] = g[col[k]] * x[i];"),
 }
 
 CHILD = r"""
