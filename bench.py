@@ -274,6 +274,17 @@ def bench_rgg(n: int, kernel_reps: int):
     gb, gv, ai = K.sla_cg_adjoint(P, v, x, g, 1e-8, 20000)
     torch.cuda.synchronize()
     adj = time.perf_counter() - t0
+    # the same solve and adjoint preconditioned with diag(A) (the pages' Jacobi)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    xj, fj = K.sla_cg_solve(P, v, b, 1e-8, 20000, jacobi=True)
+    gbj, gvj, aj = K.sla_cg_adjoint(P, v, xj, g, 1e-8, 20000, jacobi=True)
+    torch.cuda.synchronize()
+    jac_s = time.perf_counter() - t0
+    jacobi = dict(iterations_fwd=fj.iterations, iterations_adj=aj.iterations,
+                  solve_adjoint_ms=1e3 * jac_s,
+                  it_per_s=(fj.iterations + aj.iterations) / jac_s)
+    del xj, gbj, gvj
     kern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
     nnz = P.nnz
     its = fi.iterations + ai.iterations
@@ -285,7 +296,8 @@ def bench_rgg(n: int, kernel_reps: int):
                eff_GBps=(its * canonical_bytes(n, nnz, 4) + pattern_grad_bytes(n, nnz, 4)) /
                (fwd + adj) / 1e9,
                kernel_ms=kern,
-               spmv_GBps=sbytes / (kern["spmv_step"] * 1e-3) / 1e9)
+               spmv_GBps=sbytes / (kern["spmv_step"] * 1e-3) / 1e9,
+               jacobi=jacobi)
     out["pct_peak"] = 100.0 * out["eff_GBps"] / HBM_PEAK_GBPS
     del P, v, b, g, x, gb, gv
     torch.cuda.synchronize()

@@ -62,7 +62,8 @@ typedef struct {
 
 enum {
   SLA_FLAG_X0 = 1,      /* x holds the start vector (default: x0 = 0)        */
-  SLA_FLAG_HISTORY = 2  /* record alpha, beta, rr of every iteration         */
+  SLA_FLAG_HISTORY = 2, /* record alpha, beta, rr of every iteration         */
+  SLA_FLAG_JACOBI = 4   /* Jacobi preconditioning, M = diag(A) (see below)   */
 };
 
 /* Opaque matrix handle: the sparsity pattern (owned by the library, copied
@@ -146,6 +147,14 @@ sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream);
  * iterate in x.  The loop runs on the device (alpha, beta and the stopping
  * test never leave it); the host polls a small status word between blocks
  * of iterations.  info_host may be NULL.  Synchronises `stream`.
+ *
+ * SLA_FLAG_JACOBI: preconditioned CG with M = diag(A), the preconditioner the
+ * pages name for the PyTorch-native backend (Significance / limitations):
+ * z = r / d elementwise (d = the stored diagonal entries), alpha = r.z / p.Ap,
+ * beta = r.z (new) / r.z, p = z + beta p; the stopping test stays on r.r.
+ * A missing or non-positive diagonal entry returns SLA_ERR_NOT_SPD before
+ * any iteration.  Needs 2 n + 1 more workspace doubles per system.  The flag
+ * applies to the adjoint solve in the same way.
  */
 sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol,
                         int64_t maxit, uint32_t flags, sla_cg_info* info_host,

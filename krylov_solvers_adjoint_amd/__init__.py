@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 
 OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE = range(7)
 I32, I64 = 4, 8
-FLAG_X0, FLAG_HISTORY = 1, 2
+FLAG_X0, FLAG_HISTORY, FLAG_JACOBI = 1, 2, 4
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_create_from_csr", "sla_csr_destroy", "sla_csr_get_info",
@@ -331,27 +331,33 @@ def _solve_call(fn, A, b, x, tol, maxit, flags, batch, stream, check):
     return st, _infos(infos)
 
 
+def _flags(x0, history, jacobi):
+    return ((FLAG_X0 if x0 is not None else 0) | (FLAG_HISTORY if history else 0) |
+            (FLAG_JACOBI if jacobi else 0))
+
+
 def sla_cg_solve(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: float, maxit: int,
                  x0: torch.Tensor | None = None, history: bool = False, stream=None,
-                 check: bool = True):
-    """x, CGInfo.  Raises SlaError on breakdown unless check=False."""
+                 check: bool = True, jacobi: bool = False):
+    """x, CGInfo.  Raises SlaError on breakdown unless check=False.  jacobi:
+    preconditioned with M = diag(A)."""
     batch = A.bind(values)
     if batch != 1:
         raise ValueError("sla_cg_solve takes one system; use sla_cg_solve_batched")
     x = x0.clone() if x0 is not None else torch.empty_like(b)
-    flags = (FLAG_X0 if x0 is not None else 0) | (FLAG_HISTORY if history else 0)
+    flags = _flags(x0, history, jacobi)
     st, infos = _solve_call(_lib.sla_cg_solve, A, b, x, tol, maxit, flags, 1, stream, check)
     return x, infos[0]
 
 
 def sla_cg_solve_batched(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: float,
                          maxit: int, x0: torch.Tensor | None = None, history: bool = False,
-                         stream=None, check: bool = True):
+                         stream=None, check: bool = True, jacobi: bool = False):
     batch = A.bind(values)
     if b.shape[0] != batch:
         raise ValueError("b must be [batch, n]")
     x = x0.clone() if x0 is not None else torch.empty_like(b)
-    flags = (FLAG_X0 if x0 is not None else 0) | (FLAG_HISTORY if history else 0)
+    flags = _flags(x0, history, jacobi)
     st, infos = _solve_call(_lib.sla_cg_solve_batched, A, b, x, tol, maxit, flags, batch,
                             stream, check)
     return x, infos
@@ -374,21 +380,22 @@ def _adjoint_call(fn, A, x, grad_x, tol, maxit, want_vals, flags, batch, stream,
 
 def sla_cg_adjoint(A: CSRPattern, values: torch.Tensor, x: torch.Tensor, grad_x: torch.Tensor,
                    tol: float, maxit: int, want_vals: bool = True, history: bool = False,
-                   stream=None, check: bool = True):
+                   stream=None, check: bool = True, jacobi: bool = False):
     """(grad_b = lambda, grad_vals or None, CGInfo)."""
     if A.bind(values) != 1:
         raise ValueError("sla_cg_adjoint takes one system; use sla_cg_adjoint_batched")
     gb, gv, infos = _adjoint_call(_lib.sla_cg_adjoint, A, x, grad_x, tol, maxit, want_vals,
-                                  FLAG_HISTORY if history else 0, 1, stream, check)
+                                  _flags(None, history, jacobi), 1, stream, check)
     return gb, gv, infos[0]
 
 
 def sla_cg_adjoint_batched(A: CSRPattern, values: torch.Tensor, x: torch.Tensor,
                            grad_x: torch.Tensor, tol: float, maxit: int,
-                           want_vals: bool = True, stream=None, check: bool = True):
+                           want_vals: bool = True, stream=None, check: bool = True,
+                           jacobi: bool = False):
     batch = A.bind(values)
-    return _adjoint_call(_lib.sla_cg_adjoint_batched, A, x, grad_x, tol, maxit, want_vals, 0,
-                         batch, stream, check)
+    return _adjoint_call(_lib.sla_cg_adjoint_batched, A, x, grad_x, tol, maxit, want_vals,
+                         _flags(None, False, jacobi), batch, stream, check)
 
 
 def sla_pattern_grad(A: CSRPattern, values_shape_ref: torch.Tensor, lam: torch.Tensor,
@@ -424,14 +431,16 @@ def sla_profile_iteration_kernels(A: CSRPattern, values: torch.Tensor, b: torch.
 # ---------------------------------------------------------------------------
 class _CGSolve(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, values, b, pattern, tol, maxit):
+    def forward(ctx, values, b, pattern, tol, maxit, jacobi=False):
         batched = b.dim() == 2
         if batched:
-            x, infos = sla_cg_solve_batched(pattern, values, b.contiguous(), tol, maxit)
+            x, infos = sla_cg_solve_batched(pattern, values, b.contiguous(), tol, maxit,
+                                            jacobi=jacobi)
         else:
-            x, info = sla_cg_solve(pattern, values, b.contiguous(), tol, maxit)
+            x, info = sla_cg_solve(pattern, values, b.contiguous(), tol, maxit, jacobi=jacobi)
             infos = [info]
         ctx.pattern, ctx.tol, ctx.maxit, ctx.batched = pattern, tol, maxit, batched
+        ctx.jacobi = jacobi
         ctx.infos = infos
         ctx.save_for_backward(values, x)
         return x
@@ -443,10 +452,11 @@ class _CGSolve(torch.autograd.Function):
         g = grad_x.contiguous()
         if ctx.batched:
             gb, gv, _ = sla_cg_adjoint_batched(ctx.pattern, values, x, g, ctx.tol, ctx.maxit,
-                                               want_vals)
+                                               want_vals, jacobi=ctx.jacobi)
         else:
-            gb, gv, _ = sla_cg_adjoint(ctx.pattern, values, x, g, ctx.tol, ctx.maxit, want_vals)
-        return gv, gb, None, None, None
+            gb, gv, _ = sla_cg_adjoint(ctx.pattern, values, x, g, ctx.tol, ctx.maxit, want_vals,
+                                       jacobi=ctx.jacobi)
+        return gv, gb, None, None, None, None
 
 
 class SparseTensor:
@@ -466,14 +476,20 @@ class SparseTensor:
     def shape(self):
         return (self.pattern.n, self.pattern.n)
 
-    def solve(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000) -> torch.Tensor:
-        return _CGSolve.apply(self.values, b, self.pattern, float(tol), int(maxit))
+    def solve(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
+              precond: str | None = None) -> torch.Tensor:
+        """x = A^{-1} b by CG (precond="jacobi": preconditioned with diag(A))."""
+        if precond not in (None, "jacobi"):
+            raise ValueError(f"unknown preconditioner {precond!r}")
+        return _CGSolve.apply(self.values, b, self.pattern, float(tol), int(maxit),
+                              precond == "jacobi")
 
     def matvec(self, x: torch.Tensor) -> torch.Tensor:
         """y = A x (forward only; its own backward is not built)."""
         return sla_spmv(self.pattern, self.values.detach().contiguous(), x.contiguous())
 
 
-def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000):
+def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
+          precond: str | None = None):
     """x = A^{-1} b with the adjoint backward pass."""
-    return A.solve(b, tol, maxit)
+    return A.solve(b, tol, maxit, precond)

@@ -268,7 +268,8 @@ static sla_status check_solve(sla_csr A, const void* b, const void* x, double to
   REQUIRE(b != nullptr && x != nullptr, "%s: NULL vector", who);
   REQUIRE(std::isfinite(tol) && tol >= 0.0, "%s: tol must be finite and >= 0", who);
   REQUIRE(maxit >= 0, "%s: maxit must be >= 0", who);
-  REQUIRE((flags & ~uint32_t(SLA_FLAG_X0 | SLA_FLAG_HISTORY)) == 0, "%s: unknown flags", who);
+  REQUIRE((flags & ~uint32_t(SLA_FLAG_X0 | SLA_FLAG_HISTORY | SLA_FLAG_JACOBI)) == 0,
+          "%s: unknown flags", who);
   return SLA_OK;
 }
 

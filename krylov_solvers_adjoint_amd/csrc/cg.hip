@@ -339,6 +339,7 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
 
 // r = b (x = 0) or r = b - q with q = A x0; p_{-1} = 0; partials of b.b and
 // of r_0.r_0.
+template <typename RP>
 __global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ c, int use_x0) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y, n = c->n;
@@ -347,9 +348,14 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ 
   SLA_GLOBAL double* r = gmem(c->r + s * n);
   SLA_GLOBAL double* pm = gmem(c->p[1] + s * n);
   const SLA_GLOBAL double* q = gmem(c->q + s * n);
+  const bool jac = c->jacobi != 0;
+  const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(c->rowptr));
+  const SLA_GLOBAL int32_t* col = gmem(c->col);
+  const SLA_GLOBAL double* vals = gmem(c->vals + s * c->nnz);
   const int lane = threadIdx.x & (kWave - 1);
   const TileWalk w = wave_walk(c->tiles, c->grid, blockIdx.x, kWaves, wave_index());
-  double bb = 0.0, rr = 0.0;
+  double bb = 0.0, rr = 0.0, rz = 0.0;
+  bool bad = false;
   for (int64_t t = w.first; t < w.end; t += w.stride) {
     const int64_t i = t * kTileRows + lane;
     if (i < n) {
@@ -365,14 +371,28 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init(const Ctx* __restrict__ 
       pm[i] = 0.0;
       bb = bb + bi * bi;
       rr = rr + ri * ri;
+      if (jac) {
+        // the stored diagonal entry of row i (0 when the row has none)
+        double d = 0.0;
+        for (int64_t k = rowptr[i]; k < int64_t(rowptr[i + 1]); ++k)
+          if (col[k] == i) d = vals[k];
+        bad = bad || !(d > 0.0);
+        const double zi = ri / d;
+        gmem(const_cast<double*>(c->diag) + s * n)[i] = d;
+        gmem(c->z + s * n)[i] = zi;
+        rz = rz + ri * zi;
+      }
     }
   }
+  if (bad) c->bad[s] = 1;  // every writer stores the same value
   bb = block_sum_all<kIterBlock>(bb, red);
   rr = block_sum_all<kIterBlock>(rr, red);
+  if (jac) rz = block_sum_all<kIterBlock>(rz, red);
   if (threadIdx.x == 0) {
     SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * c->grid);
     part[4 * c->grid + blockIdx.x] = bb;
     part[0 * c->grid + blockIdx.x] = rr;
+    if (jac) part[5 * c->grid + blockIdx.x] = rz;
     if (blockIdx.x == 0 && s == 0) *c->n_running = 0;
   }
 }
@@ -381,13 +401,17 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
                                                                 double tol, int64_t maxit) {
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.x;
+  const bool jac = c->jacobi != 0;
   const SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * c->grid);
   const double bb = sum_partials_all(part + 4 * c->grid, c->grid, red);
   const double rr = sum_partials_all(part + 0 * c->grid, c->grid, red);
+  const double rz = jac ? sum_partials_all(part + 5 * c->grid, c->grid, red) : 0.0;
   if (threadIdx.x == 0) {
     Scal* sc = c->scal + s;
     sc->rr[0] = rr;
     sc->rr[1] = rr;
+    sc->rz[0] = rz;
+    sc->rz[1] = rz;
     sc->alpha = 0.0;
     sc->bb = bb;
     sc->stop = (tol * tol) * bb;
@@ -396,7 +420,11 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
     sc->kr = 0;
     sc->it = 0;
     sc->maxit = maxit;
-    const int32_t st = (!isfinite(bb) || !isfinite(rr)) ? ST_NONFINITE : ST_RUNNING;
+    int32_t st = (!isfinite(bb) || !isfinite(rr) || !isfinite(rz)) ? ST_NONFINITE : ST_RUNNING;
+    if (jac && c->bad[s] != 0) {
+      st = ST_NOT_SPD;  // a diagonal entry is not > 0: before any iteration
+      c->bad[s] = 0;    // cleared for the next solve
+    }
     sc->state_a = st;
     sc->state_r = st;
     if (st == ST_RUNNING) atomicAdd(c->n_running, 1);
@@ -425,6 +453,9 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
   h.k = sc->ka;
   const int64_t k = h.k;
   const double rr = sum_partials_all<NT>(part + (k & 1) * G, G, red);
+  // Jacobi: beta from r.z, the stopping test still on r.r
+  const bool jac = c->jacobi != 0;
+  const double rz = jac ? sum_partials_all<NT>(part + (5 + (k & 1)) * G, G, red) : 0.0;
   h.lag = k > 0;
   h.alpha = 0.0;
   h.beta = 0.0;
@@ -434,12 +465,12 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
   if (h.lag) {
     const double rr_prev = sc->rr[(k - 1) & 1];
     h.alpha = sc->alpha;
-    if (!isfinite(rr)) {
+    if (!isfinite(rr) || !isfinite(rz)) {
       h.stop = ST_NONFINITE;  // iteration k-1 did not complete
       it_stop = k - 1;
       rr_stop = rr_prev;
     } else {
-      h.beta = rr / rr_prev;
+      h.beta = jac ? rz / sc->rz[(k - 1) & 1] : rr / rr_prev;
     }
   }
   if (h.stop == ST_RUNNING) {
@@ -454,6 +485,7 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
       hh[2] = rr;
     }
     sc->rr[k & 1] = rr;
+    sc->rz[k & 1] = rz;
     sc->kr = k;
     if (h.stop != ST_RUNNING) {
       sc->it = it_stop;
@@ -485,7 +517,7 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
   double* const p0 = c->p[0] + s * n;
   double* const p1 = c->p[1] + s * n;
   SLA_GLOBAL double* x = gmem(c->x + s * n);
-  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  const SLA_GLOBAL double* r = gmem(c->rd + s * n);  // r, or z with Jacobi
   SLA_GLOBAL double* q = gmem(c->q + s * n);
   SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   Scal* sc = c->scal + s;
@@ -608,7 +640,7 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   double* const p0 = c->p[0] + s * n;
   double* const p1 = c->p[1] + s * n;
   SLA_GLOBAL double* x = gmem(c->x + s * n);
-  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  const SLA_GLOBAL double* r = gmem(c->rd + s * n);  // r, or z with Jacobi
   SLA_GLOBAL double* q = gmem(c->q + s * n);
   SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   Scal* sc = c->scal + s;
@@ -811,7 +843,7 @@ void k_cg_direction(const Ctx* __restrict__ c) {
   const int G = c->grid;
   double* const p0 = c->p[0] + s * n;
   double* const p1 = c->p[1] + s * n;
-  const SLA_GLOBAL double* r = gmem(c->r + s * n);
+  const SLA_GLOBAL double* r = gmem(c->rd + s * n);  // r, or z with Jacobi
   SLA_GLOBAL double* x = gmem(c->x + s * n);
   Scal* sc = c->scal + s;
   const int32_t st_in = sc->state_r;
@@ -896,7 +928,9 @@ void k_cg_product(const Ctx* __restrict__ c) {
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
-// Residual step k (see the file comment).
+// Residual step k (see the file comment).  JAC: Jacobi preconditioning, so
+// alpha = r.z / p.Ap, and the step also writes z = r / d and the r.z partials.
+template <bool JAC>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_residual(const Ctx* __restrict__ c) {
   __shared__ double red[kWaves];
@@ -907,6 +941,8 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   SLA_GLOBAL double* r = gmem(c->r + s * n);
   const SLA_GLOBAL double* q = gmem(c->q + s * n);
+  const SLA_GLOBAL double* dg = gmem(c->diag + s * n);
+  SLA_GLOBAL double* z = gmem(c->z + s * n);
   int* const n_running = c->n_running;
   Scal* sc = c->scal + s;
   const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
@@ -918,6 +954,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   const int64_t k = sc->kr;
   const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
   const double rr = sc->rr[k & 1];
+  const double num = JAC ? sc->rz[k & 1] : rr;
   int32_t stop = ST_RUNNING;
   if (!isfinite(pq)) stop = ST_NONFINITE;
   else if (!(pq > 0.0)) stop = ST_NOT_SPD;
@@ -931,38 +968,50 @@ void k_cg_residual(const Ctx* __restrict__ c) {
     }
     return;
   }
-  const double alpha = uniform(rr / pq);
+  const double alpha = uniform(num / pq);
   if (lead) {
     sc->alpha = alpha;
     sc->ka = k + 1;
   }
   const uint32_t lane = lane_id();
   const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
-  // kStreamTiles tiles per round, all loads first; the r.r terms are added
-  // in tile order
-  double rn = 0.0;
-  for (int64_t t0 = wk.first; t0 < wk.end; t0 += kStreamTiles * wk.stride) {
-    double rv[kStreamTiles], qv[kStreamTiles];
+  // kStreamTiles tiles per round, all loads first; the r.r (and r.z) terms
+  // are added in tile order
+  // (two tiles in flight with Jacobi: the divisions need the registers)
+  constexpr int U = JAC ? 2 : kStreamTiles;
+  double rn = 0.0, rzn = 0.0;
+  for (int64_t t0 = wk.first; t0 < wk.end; t0 += U * wk.stride) {
+    double rv[U], qv[U], dv[U];
 #pragma unroll
-    for (int u = 0; u < kStreamTiles; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
       if (t < wk.end && i0 + lane < n) {
         rv[u] = ld(r + i0, lane);
         qv[u] = ld(q + i0, lane);
+        if constexpr (JAC) dv[u] = ld(dg + i0, lane);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kStreamTiles; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
       if (t < wk.end && i0 + lane < n) {
         const double ri = rv[u] - alpha * qv[u];
         st(r + i0, lane, ri);
         rn = rn + ri * ri;
+        if constexpr (JAC) {
+          const double zi = ri / dv[u];
+          st(z + i0, lane, zi);
+          rzn = rzn + ri * zi;
+        }
       }
     }
   }
   rn = block_sum_all<kIterBlock>(rn, red);
-  if (threadIdx.x == 0) part[((k + 1) & 1) * G + blockIdx.x] = rn;
+  if constexpr (JAC) rzn = block_sum_all<kIterBlock>(rzn, red);
+  if (threadIdx.x == 0) {
+    part[((k + 1) & 1) * G + blockIdx.x] = rn;
+    if constexpr (JAC) part[(5 + ((k + 1) & 1)) * G + blockIdx.x] = rzn;
+  }
 }
 
 // grad_vals[s][k] = -lambda[s][i] * x[s][col[k]] for every stored slot k of
@@ -1067,7 +1116,7 @@ sla_status launch_ctx_kernel(const void* fn, dim3 grid, unsigned block, size_t l
 }
 
 template <typename RP>
-sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
+sla_status enqueue_iteration(sla_csr A, int64_t batch, bool jacobi, hipStream_t st) {
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
   if (use_split(A)) {
     k_cg_direction<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
@@ -1077,21 +1126,24 @@ sla_status enqueue_iteration(sla_csr A, int64_t batch, hipStream_t st) {
     SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A), grid2, spmv_step_block(A), lds_bytes(A),
                               A->ctx_dev, st));
   }
-  k_cg_residual<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
+  if (jacobi) k_cg_residual<true><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
+  else k_cg_residual<false><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
   LAUNCH_CHECK();
   return SLA_OK;
 }
 
-sla_status enqueue_block(sla_csr A, int64_t batch, int64_t iters, hipStream_t st) {
+sla_status enqueue_block(sla_csr A, int64_t batch, bool jacobi, int64_t iters, hipStream_t st) {
   for (int64_t k = 0; k < iters; ++k) {
-    if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, batch, st));
-    else SLA_TRY(enqueue_iteration<int64_t>(A, batch, st));
+    if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, batch, jacobi, st));
+    else SLA_TRY(enqueue_iteration<int64_t>(A, batch, jacobi, st));
   }
   return SLA_OK;
 }
 
-sla_status get_graph(sla_csr A, int64_t batch, hipGraphExec_t* exec) {
-  auto it = A->graphs.find(batch);
+sla_status get_graph(sla_csr A, int64_t batch, bool jacobi, hipGraphExec_t* exec) {
+  // one graph per (batch, preconditioner): the kernels differ
+  const int64_t key = batch * 2 + (jacobi ? 1 : 0);
+  auto it = A->graphs.find(key);
   if (it != A->graphs.end()) {
     *exec = it->second.second;
     return SLA_OK;
@@ -1101,7 +1153,7 @@ sla_status get_graph(sla_csr A, int64_t batch, hipGraphExec_t* exec) {
   hipGraph_t g = nullptr;
   hipGraphExec_t e = nullptr;
   SLA_TRY_HIP(hipStreamBeginCapture(A->capture_stream, hipStreamCaptureModeThreadLocal));
-  sla_status s = enqueue_block(A, batch, A->graph_block, A->capture_stream);
+  sla_status s = enqueue_block(A, batch, jacobi, A->graph_block, A->capture_stream);
   hipError_t he = hipStreamEndCapture(A->capture_stream, &g);
   if (s != SLA_OK) {
     if (g) (void)hipGraphDestroy(g);
@@ -1117,7 +1169,7 @@ sla_status get_graph(sla_csr A, int64_t batch, hipGraphExec_t* exec) {
     set_error("graph instantiation failed: %s", hipGetErrorString(he));
     return SLA_ERR_DEVICE;
   }
-  A->graphs[batch] = {g, e};
+  A->graphs[key] = {g, e};
   *exec = e;
   return SLA_OK;
 }
@@ -1130,7 +1182,8 @@ void drop_graphs(sla_csr A) {
   A->graphs.clear();
 }
 
-void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool hist) {
+void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool hist,
+              bool jacobi = false) {
   c = Ctx{};
   c.rowptr = A->rowptr;
   c.col = A->col;
@@ -1138,6 +1191,11 @@ void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool
   c.x = x;
   c.b = b;
   c.r = A->r;
+  c.jacobi = jacobi ? 1 : 0;
+  c.diag = jacobi ? A->jdiag : nullptr;
+  c.z = jacobi ? A->jz : nullptr;
+  c.bad = jacobi ? A->jbad : nullptr;
+  c.rd = jacobi ? A->jz : A->r;
   c.p[0] = A->p0;
   c.p[1] = A->p1;
   c.q = A->q;
@@ -1216,6 +1274,11 @@ void release_workspace(sla_csr A) {
   dev_free(A->n_running);
   dev_free(A->ctx_dev);
   dev_free(A->hist);
+  dev_free(A->jz);
+  dev_free(A->jdiag);
+  dev_free(A->jbad);
+  A->jz = A->jdiag = nullptr;
+  A->jbad = nullptr;
   if (A->ctx_host) (void)hipHostFree(A->ctx_host);
   if (A->scal_host) (void)hipHostFree(A->scal_host);
   if (A->poll_host) (void)hipHostFree(A->poll_host);
@@ -1319,13 +1382,24 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
       A->hist_batch = batch;
     }
   }
-  fill_ctx(A, *A->ctx_host, b, x, batch, want_hist);
+  const bool jacobi = (flags & SLA_FLAG_JACOBI) != 0;
+  if (jacobi && A->jz == nullptr) {
+    // Jacobi workspace: z and the diagonal [batch][n], a flag per system
+    // (zero here, and cleared again by every solve that sets it)
+    const size_t vec = size_t(batch) * size_t(A->n);
+    SLA_TRY(dev_alloc(&A->jz, vec, "z"));
+    SLA_TRY(dev_alloc(&A->jdiag, vec, "diagonal"));
+    SLA_TRY(dev_alloc(&A->jbad, size_t(batch), "diagonal flags"));
+    SLA_TRY_HIP(hipMemsetAsync(A->jbad, 0, sizeof(int) * size_t(batch), st));
+  }
+  fill_ctx(A, *A->ctx_host, b, x, batch, want_hist, jacobi);
   SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
 
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
   if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, A->q, st));  // q = A x0
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
-  k_cg_init<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
+  if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
+  else k_cg_init<int64_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
   k_cg_init_scalars<<<unsigned(batch), kIterBlock, 0, st>>>(A->ctx_dev, tol, maxit);
   LAUNCH_CHECK();
   SLA_TRY_HIP(hipMemcpyAsync(A->poll_host, A->n_running, sizeof(int), hipMemcpyDeviceToHost,
@@ -1337,10 +1411,10 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
     const int64_t K = A->graph_block > 0 ? A->graph_block : 16;
     const int64_t nblocks = (maxit + 1 + K - 1) / K;
     hipGraphExec_t exec = nullptr;
-    if (A->graph_block > 0) SLA_TRY(get_graph(A, batch, &exec));
+    if (A->graph_block > 0) SLA_TRY(get_graph(A, batch, jacobi, &exec));
     for (int64_t j = 0; j < nblocks; ++j) {
       if (exec) SLA_TRY_HIP(hipGraphLaunch(exec, st));
-      else SLA_TRY(enqueue_block(A, batch, K, st));
+      else SLA_TRY(enqueue_block(A, batch, jacobi, K, st));
       SLA_TRY_HIP(hipMemcpyAsync(A->poll_host + (j & 1), A->n_running, sizeof(int),
                                  hipMemcpyDeviceToHost, st));
       SLA_TRY_HIP(hipEventRecord(A->poll_ev[j & 1], st));
@@ -1403,7 +1477,7 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
     blocks[nk] = spmv_step_block(A);
     ldss[nk++] = lds_bytes(A);
   }
-  fns[nk] = reinterpret_cast<const void*>(&k_cg_residual);
+  fns[nk] = reinterpret_cast<const void*>(&k_cg_residual<false>);
   blocks[nk] = kIterBlock;
   ldss[nk++] = 0;
   std::vector<hipEvent_t> ev(size_t(2 * reps), nullptr);
@@ -1450,11 +1524,12 @@ sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps, 
   fill_ctx(A, *A->ctx_host, b, x, 1, false);
   SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
   const dim3 grid2(unsigned(A->grid), 1u);
-  k_cg_init<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, 0);
+  if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, 0);
+  else k_cg_init<int64_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, 0);
   k_cg_init_scalars<<<1u, kIterBlock, 0, st>>>(A->ctx_dev, 0.0, huge);
   LAUNCH_CHECK();
-  if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, 1, st));
-  else SLA_TRY(enqueue_iteration<int64_t>(A, 1, st));
+  if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, 1, false, st));
+  else SLA_TRY(enqueue_iteration<int64_t>(A, 1, false, st));
   if (A->rp_idx == SLA_I32) return time_kernels<int32_t>(A, reps, avg_ms, st);
   return time_kernels<int64_t>(A, reps, avg_ms, st);
 }

@@ -58,7 +58,7 @@ constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-rob
 // CU; a 64-row tile of a 5-point stencil has at most 320 slots.
 constexpr int kWaveCap = 336;
 constexpr int kStageLoads = (kWaveCap + kWave - 1) / kWave;  // staged slots per lane
-constexpr int kPartSets = 5;       // partial-sum arrays per system (see Ctx)
+constexpr int kPartSets = 7;       // partial-sum arrays per system (see Ctx)
 constexpr int kMaxBand = 8;        // most distinct column offsets of a banded pattern
 constexpr int64_t kMaxBandSpan = int64_t(1) << 27;  // widest band (largest - smallest offset)
 constexpr int kPanelTiles = 64;    // widest column block of the panel tile order
@@ -100,6 +100,7 @@ enum : int32_t {
 // workgroup of the same launch may be writing.
 struct alignas(64) Scal {
   double rr[2];     // r_k . r_k, by parity of k          (SpMV step writes)
+  double rz[2];     // r_k . z_k (Jacobi), by parity of k  (SpMV step writes)
   double alpha;     // alpha_k                              (residual step writes)
   double bb;        // b . b                                (set-up)
   double stop;      // (tol * tol) * bb                     (set-up)
@@ -121,10 +122,18 @@ struct Ctx {
   double* x;            // [batch][n] solution (lambda for the adjoint)
   const double* b;      // [batch][n] right-hand side
   double* r;            // [batch][n]
+  // Jacobi preconditioning (M = diag(A)): z = r / d, the search direction is
+  // built from z; without it `rd` is r and `diag`, `z`, `bad` are unused
+  const double* diag;   // [batch][n] the diagonal d, extracted at set-up
+  double* z;            // [batch][n]
+  const double* rd;     // [batch][n] source of the search direction: z or r
+  int* bad;             // [batch] set when a diagonal entry is not > 0
+  int32_t jacobi;
   double* p[2];         // [batch][n] search direction, double-buffered
   double* q;            // [batch][n] A p
   // [batch][kPartSets][grid] one partial per workgroup:
-  //   set 0/1: r.r by parity of k, set 2/3: p.Ap by parity of k, set 4: b.b
+  //   set 0/1: r.r by parity of k, set 2/3: p.Ap by parity of k, set 4: b.b,
+  //   set 5/6: r.z by parity of k (Jacobi)
   double* part;
   Scal* scal;           // [batch]
   double* hist;         // [batch][hist_cap][3] alpha, beta, rr or nullptr

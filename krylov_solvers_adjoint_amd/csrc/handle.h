@@ -54,6 +54,10 @@ struct sla_csr_s {
   int* poll_host = nullptr;          // pinned [2]
   hipEvent_t poll_ev[2] = {nullptr, nullptr};
   double* hist = nullptr;
+  // Jacobi workspace (allocated by the first preconditioned solve)
+  double* jz = nullptr;
+  double* jdiag = nullptr;
+  int* jbad = nullptr;
   int64_t hist_cap = 0;
   int64_t hist_batch = 0;
 
