@@ -139,6 +139,26 @@ sla_status sla_csr_set_values(sla_csr A, const double* vals, int64_t batch);
 sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream);
 
 /*
+ * y[s] = A_s^T x[s] for every system s of the bound batch: the transposed
+ * product the backward pass of .matvec needs (Methodology 1).  The first call
+ * builds the transposed pattern and keeps it with the handle (a COO -> CSR
+ * build of the slots with rows and columns swapped; about 24 more bytes per
+ * slot); every call gathers the bound values into its slot order.  Row j of
+ * A^T is summed in ascending original row i, as an explicit transpose
+ * followed by sla_spmv would.  x, y [batch][n], device memory.
+ */
+sla_status sla_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t stream);
+
+/*
+ * Backward pass of y = A x (Methodology 1, the differentiable .matvec) for a
+ * loss L with grad_y = dL/dy: grad_x = A^T grad_y [batch][n] (may be NULL:
+ * not computed) and grad_vals[k] = grad_y_i x_j for every stored slot
+ * k = (i, j) [batch][nnz] (may be NULL), nothing for absent entries.
+ */
+sla_status sla_matvec_grad(sla_csr A, const double* x, const double* grad_y, double* grad_x,
+                           double* grad_vals, hipStream_t stream);
+
+/*
  * Solve A x = b by CG (bound batch must be 1).  x0 = 0 unless SLA_FLAG_X0.
  * Stops when rr <= (tol*tol)*bb with rr the recursive residual norm squared
  * and bb = b.b (checked before each iteration), or after maxit iterations;

@@ -43,7 +43,7 @@ EXPORTS = [
     "sla_cg_adjoint", "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
     "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_spmv_variant",
     "sla_csr_set_graph_block",
-    "sla_csr_set_workgroups_per_cu",
+    "sla_csr_set_workgroups_per_cu", "sla_spmv_transpose", "sla_matvec_grad",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -87,6 +87,8 @@ def _bind(lib):
         "sla_profile_iteration_kernels": [_P, _P, _P, _I64, _P, _P],
         "sla_csr_set_graph_block": [_P, _I64],
         "sla_csr_set_workgroups_per_cu": [_P, _S],
+        "sla_spmv_transpose": [_P, _P, _P, _P],
+        "sla_matvec_grad": [_P, _P, _P, _P, _P, _P],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
@@ -320,6 +322,33 @@ def sla_spmv(A: CSRPattern, values: torch.Tensor, x: torch.Tensor, stream=None) 
     return y
 
 
+def sla_spmv_transpose(A: CSRPattern, values: torch.Tensor, x: torch.Tensor,
+                       stream=None) -> torch.Tensor:
+    """y = A^T x (every system of the batch)."""
+    batch = A.bind(values)
+    _shape(x, _vec_shape(A, batch, x), "x")
+    y = torch.empty_like(x)
+    _check(_lib.sla_spmv_transpose(A.handle, _dev(x, torch.float64, "x"), y.data_ptr(),
+                                   _stream(stream)))
+    return y
+
+
+def sla_matvec_grad(A: CSRPattern, values: torch.Tensor, x: torch.Tensor, grad_y: torch.Tensor,
+                    want_x: bool = True, want_vals: bool = True, stream=None):
+    """Backward of y = A x: (grad_x = A^T grad_y or None, grad_vals = grad_y_i x_j or None)."""
+    batch = A.bind(values)
+    _shape(grad_y, _vec_shape(A, batch, grad_y), "grad_y")
+    _shape(x, _vec_shape(A, batch, grad_y), "x")
+    gx = torch.empty_like(grad_y) if want_x else None
+    gv = (torch.empty((batch, A.nnz) if grad_y.dim() == 2 else (A.nnz,), dtype=torch.float64,
+                      device=grad_y.device) if want_vals else None)
+    _check(_lib.sla_matvec_grad(A.handle, _dev(x, torch.float64, "x"),
+                                _dev(grad_y, torch.float64, "grad_y"),
+                                gx.data_ptr() if gx is not None else None,
+                                gv.data_ptr() if gv is not None else None, _stream(stream)))
+    return gx, gv
+
+
 def _solve_call(fn, A, b, x, tol, maxit, flags, batch, stream, check):
     _shape(b, _vec_shape(A, batch, b), "b")
     _shape(x, _vec_shape(A, batch, b), "x")
@@ -459,6 +488,25 @@ class _CGSolve(torch.autograd.Function):
         return gv, gb, None, None, None, None
 
 
+class _MatVec(torch.autograd.Function):
+    """y = A x; backward grad_x = A^T g, grad_vals = g_i x_j on the pattern."""
+
+    @staticmethod
+    def forward(ctx, values, x, pattern):
+        ctx.pattern = pattern
+        ctx.save_for_backward(values, x)
+        return sla_spmv(pattern, values.detach().contiguous(), x.detach().contiguous())
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        values, x = ctx.saved_tensors
+        gx, gv = sla_matvec_grad(ctx.pattern, values.detach().contiguous(),
+                                 x.detach().contiguous(), grad_y.contiguous(),
+                                 want_x=ctx.needs_input_grad[1],
+                                 want_vals=ctx.needs_input_grad[0])
+        return gv, gx, None
+
+
 class SparseTensor:
     """A sparse matrix (or a batch sharing one pattern) with .solve / .matvec.
 
@@ -485,8 +533,8 @@ class SparseTensor:
                               precond == "jacobi")
 
     def matvec(self, x: torch.Tensor) -> torch.Tensor:
-        """y = A x (forward only; its own backward is not built)."""
-        return sla_spmv(self.pattern, self.values.detach().contiguous(), x.contiguous())
+        """y = A x, differentiable in the values and in x (one graph node)."""
+        return _MatVec.apply(self.values, x, self.pattern)
 
 
 def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,

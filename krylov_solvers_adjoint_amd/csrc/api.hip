@@ -80,9 +80,12 @@ using namespace sla;
 
 static bool valid_index(sla_index v) { return v == SLA_I32 || v == SLA_I64; }
 
-static void destroy_handle(sla_csr A) {
+namespace sla {
+void free_handle(sla_csr A) {
   if (!A) return;
   release_workspace(A);
+  free_handle(A->trans);
+  dev_free(A->trans_vals);
   dev_free(A->rowptr);
   dev_free(A->col);
   dev_free(A->perm);
@@ -91,6 +94,9 @@ static void destroy_handle(sla_csr A) {
   dev_free(A->band_mask);
   delete A;
 }
+}  // namespace sla
+
+static void destroy_handle(sla_csr A) { free_handle(A); }
 
 extern "C" {
 
@@ -258,6 +264,31 @@ sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream) {
   REQUIRE(A->batch >= 1, "sla_spmv: no values bound (sla_csr_set_values)");
   REQUIRE(x != nullptr && y != nullptr, "sla_spmv: NULL vector");
   return launch_spmv(A, A->vals, A->batch, x, y, stream);
+  API_END
+}
+
+sla_status sla_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_spmv_transpose: NULL handle");
+  REQUIRE(A->batch >= 1, "sla_spmv_transpose: no values bound (sla_csr_set_values)");
+  REQUIRE(x != nullptr && y != nullptr, "sla_spmv_transpose: NULL vector");
+  return launch_spmv_transpose(A, x, y, stream);
+  API_END
+}
+
+sla_status sla_matvec_grad(sla_csr A, const double* x, const double* grad_y, double* grad_x,
+                           double* grad_vals, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_matvec_grad: NULL handle");
+  REQUIRE(A->batch >= 1, "sla_matvec_grad: no values bound (sla_csr_set_values)");
+  REQUIRE(grad_y != nullptr, "sla_matvec_grad: NULL grad_y");
+  REQUIRE(grad_vals == nullptr || A->nnz == 0 || x != nullptr, "sla_matvec_grad: grad_vals needs x");
+  if (grad_x != nullptr) SLA_TRY(launch_spmv_transpose(A, grad_y, grad_x, stream));
+  if (grad_vals != nullptr && A->nnz > 0)
+    SLA_TRY(launch_slot_products(A, A->batch, grad_y, x, grad_vals, false, stream));
+  return SLA_OK;
   API_END
 }
 

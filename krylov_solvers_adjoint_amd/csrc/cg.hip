@@ -1015,10 +1015,10 @@ void k_cg_residual(const Ctx* __restrict__ c) {
 }
 
 // grad_vals[s][k] = -lambda[s][i] * x[s][col[k]] for every stored slot k of
-// row i.  The lanes of a wave walk the tile's slots in order (coalesced
+// row i (NEG; without it the product itself, the .matvec backward).  The lanes of a wave walk the tile's slots in order (coalesced
 // column loads and gradient stores); each slot's row comes from an LDS map
 // the lanes fill for their own rows.
-template <typename RP>
+template <typename RP, bool NEG>
 __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restrict__ rowptr,
                                                              const int32_t* __restrict__ col,
                                                              int64_t n, int64_t nnz, int64_t tiles,
@@ -1050,8 +1050,10 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
       for (int64_t k = (a > c0 ? a : c0); k < (e < c0 + clen ? e : c0 + clen); ++k)
         rowmap[k - c0] = uint8_t(lane);
       wave_sync();
-      for (int64_t k = lane; k < clen; k += kWave)
-        gs[s0 + c0 + k] = -(l[r0 + rowmap[k]] * xs[col[s0 + c0 + k]]);
+      for (int64_t k = lane; k < clen; k += kWave) {
+        const double pr = l[r0 + rowmap[k]] * xs[col[s0 + c0 + k]];
+        gs[s0 + c0 + k] = NEG ? -pr : pr;
+      }
       wave_sync();
     }
   }
@@ -1352,19 +1354,27 @@ sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const doubl
   return SLA_OK;
 }
 
-sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda, const double* x,
-                               double* grad_vals, hipStream_t st) {
+sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const double* x,
+                                double* out, bool negate, hipStream_t st) {
   const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
   const int cap = A->wave_cap;
   const size_t lds = size_t(kWaves) * size_t(cap);
-  if (A->rp_idx == SLA_I32)
-    k_pattern_grad<int32_t><<<grid, kIterBlock, lds, st>>>(
-        (const int32_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles, cap, lambda, x, grad_vals);
-  else
-    k_pattern_grad<int64_t><<<grid, kIterBlock, lds, st>>>(
-        (const int64_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles, cap, lambda, x, grad_vals);
+  if (A->rp_idx == SLA_I32) {
+    auto k = negate ? k_pattern_grad<int32_t, true> : k_pattern_grad<int32_t, false>;
+    k<<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles,
+                                     cap, g, x, out);
+  } else {
+    auto k = negate ? k_pattern_grad<int64_t, true> : k_pattern_grad<int64_t, false>;
+    k<<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles,
+                                     cap, g, x, out);
+  }
   LAUNCH_CHECK();
   return SLA_OK;
+}
+
+sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda, const double* x,
+                               double* grad_vals, hipStream_t st) {
+  return launch_slot_products(A, batch, lambda, x, grad_vals, true, st);
 }
 
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,

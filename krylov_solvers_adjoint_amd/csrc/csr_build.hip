@@ -678,6 +678,14 @@ sla_status tile_stats(sla_csr A, hipStream_t st) {
   return SLA_OK;
 }
 
+// rows[k] = the row of slot k (the row index of every stored entry)
+template <typename RP>
+__global__ void k_expand_rows(int64_t n, const RP* __restrict__ rowptr, int32_t* __restrict__ rows) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  for (int64_t k = rowptr[i]; k < int64_t(rowptr[i + 1]); ++k) rows[k] = int32_t(i);
+}
+
 }  // namespace
 
 sla_status analyse_pattern(sla_csr A, hipStream_t st) {
@@ -740,6 +748,63 @@ sla_status build_from_csr(sla_csr A, const void* rowptr, const int32_t* col, hip
     return SLA_ERR_CSR;
   }
   return SLA_OK;
+}
+
+// The transposed pattern as a handle of its own: its COO triplets are our
+// slots k = 0 .. nnz-1 with row col[k] and column row(k), so the ordinary
+// COO build sorts each transposed row by original row (ascending) and its
+// perm maps our slots to its slots.
+sla_status build_transpose(sla_csr A, hipStream_t st) {
+  if (A->trans != nullptr) return SLA_OK;
+  int32_t* rows = nullptr;
+  SLA_TRY(dev_alloc(&rows, size_t(A->nnz > 0 ? A->nnz : 1), "row of each slot"));
+  if (A->rp_idx == SLA_I32)
+    k_expand_rows<int32_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, (const int32_t*)A->rowptr, rows);
+  else
+    k_expand_rows<int64_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, (const int64_t*)A->rowptr, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    dev_free(rows);
+    set_error("transpose: kernel launch failed: %s", hipGetErrorString(e));
+    return SLA_ERR_DEVICE;
+  }
+  sla_csr T = new sla_csr_s();
+  T->device = A->device;
+  T->n = A->n;
+  T->nnz_coo = A->nnz;
+  T->rp_idx = A->rp_idx;
+  sla_status s = build_from_coo(T, SLA_I32, A->col, rows, st);
+  if (s == SLA_OK) s = analyse_pattern(T, st);
+  if (s == SLA_OK) {
+    e = hipStreamSynchronize(st);  // `rows` is freed below
+    if (e != hipSuccess) {
+      set_error("transpose: %s", hipGetErrorString(e));
+      s = SLA_ERR_DEVICE;
+    }
+  }
+  dev_free(rows);
+  if (s != SLA_OK) {
+    free_handle(T);
+    return s;
+  }
+  A->trans = T;
+  return SLA_OK;
+}
+
+sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t st) {
+  SLA_TRY(build_transpose(A, st));
+  sla_csr T = A->trans;
+  const int64_t batch = A->batch;
+  if (A->trans_vals == nullptr || A->trans_batch < batch) {
+    dev_free(A->trans_vals);
+    A->trans_vals = nullptr;
+    SLA_TRY(dev_alloc(&A->trans_vals, size_t(batch) * size_t(A->nnz > 0 ? A->nnz : 1),
+                      "transposed values"));
+    A->trans_batch = batch;
+  }
+  // our values in the transposed slot order (a copy: one slot per triplet)
+  if (A->nnz > 0) SLA_TRY(launch_values_from_coo(T, A->vals, A->trans_vals, batch, st));
+  return launch_spmv(T, A->trans_vals, batch, x, y, st);
 }
 
 sla_status launch_values_from_coo(sla_csr A, const double* coo_val, double* vals, int64_t batch,

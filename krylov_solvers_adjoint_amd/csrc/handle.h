@@ -38,6 +38,14 @@ struct sla_csr_s {
   const double* vals = nullptr;
   int64_t batch = 0;
 
+  // the transposed pattern, built on first use by the transposed product:
+  // a handle of its own whose COO triplets are this pattern's slots with
+  // rows and columns swapped (so its perm maps our slots to its slots), and
+  // its values [batch][nnz] gathered from ours on each call
+  sla_csr_s* trans = nullptr;
+  double* trans_vals = nullptr;
+  int64_t trans_batch = 0;
+
   // workspace, sized for ws_batch systems
   int64_t ws_batch = 0;
   int32_t grid = 0;            // iteration workgroups per system
@@ -79,7 +87,13 @@ sla_status ensure_workspace(sla_csr A, int64_t batch);
 bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
 bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
 bool use_lines(const sla_csr A);  // line-walk SpMV step (a banded pattern with far offsets +-L)?
+// y[s] = A_s^T x[s] (builds the transposed pattern on first use)
+sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t st);
+// grad_vals[s][k] = sign * g[s][i] * x[s][col[k]] on every stored slot
+sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const double* x,
+                                double* out, bool negate, hipStream_t st);
 void release_workspace(sla_csr A);
+void free_handle(sla_csr A);  // the handle, its workspace and its transposed pattern
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 
 sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x,
