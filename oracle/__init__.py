@@ -93,6 +93,10 @@ def _bind(lib):
                                           ctypes.POINTER(_Info)]
     lib.oracle_matvec_grad.restype = None
     lib.oracle_matvec_grad.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_lanczos.restype = _I64
+    lib.oracle_lanczos.argtypes = [_I64, _P, _P, _P, _P, _I64, _P, _P, _P]
+    lib.oracle_eig_grad.restype = None
+    lib.oracle_eig_grad.argtypes = [_I64, _P, _P, _P, _P]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
@@ -291,6 +295,46 @@ def matvec_grad(A: CSR, x, g, lib=None):
     L.oracle_matvec_grad(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
                          _ptr(_c(A.vals, np.float64)), _ptr(x), _ptr(g), _ptr(gx), _ptr(gv))
     return gx, gv[:A.nnz].copy()
+
+
+def lanczos(A: CSR, v0, m: int, lib=None):
+    """m Lanczos steps with full reorthogonalisation (classical Gram-Schmidt
+    twice) from v0: (alpha[steps], beta[steps], V[steps+1, n])."""
+    L = lib or _load()
+    v0 = _c(v0, np.float64)
+    alpha = np.zeros(max(m, 1))
+    beta = np.zeros(max(m, 1))
+    V = np.zeros((m + 1, A.n))
+    steps = int(L.oracle_lanczos(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                                 _ptr(_c(A.vals, np.float64)), _ptr(v0), int(m), _ptr(alpha),
+                                 _ptr(beta), _ptr(V)))
+    return alpha[:steps].copy(), beta[:steps].copy(), V[:steps + 1].copy()
+
+
+def eigsh(A: CSR, k: int, which: str, v0, m: int, lib=None):
+    """The .eigsh: k Ritz pairs of the m-step Lanczos process, the largest
+    (which="LA") or the smallest ("SA") algebraic ones, ascending.  The
+    tridiagonal eigenproblem is solved by a library routine (LAPACK stevr via
+    scipy).  Returns (theta[k], X[k, n] unit Ritz vectors, residual
+    estimates |beta_m y_m|[k])."""
+    from scipy.linalg import eigh_tridiagonal
+    alpha, beta, V = lanczos(A, v0, m, lib=lib)
+    steps = alpha.shape[0]
+    theta, Y = eigh_tridiagonal(alpha, beta[:steps - 1])
+    sel = np.arange(steps - k, steps) if which == "LA" else np.arange(k)
+    X = (V[:steps].T @ Y[:, sel]).T
+    res = np.abs(beta[steps - 1] * Y[steps - 1, sel])
+    return theta[sel], X, res
+
+
+def eig_grad(A: CSR, v, lib=None) -> np.ndarray:
+    """d lambda / d vals[k] = v_i v_j on every stored slot (Hellmann-Feynman)."""
+    L = lib or _load()
+    v = _c(v, np.float64)
+    gv = np.zeros(max(A.nnz, 1), np.float64)
+    L.oracle_eig_grad(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)), _ptr(v),
+                      _ptr(gv))
+    return gv[:A.nnz].copy()
 
 
 def pattern_grad(A: CSR, lam, x, lib=None) -> np.ndarray:

@@ -15,6 +15,10 @@
  *     solves A^T lambda = dL/dx and the matrix gradient is -lambda_i x_j,
  *     only on the sparsity pattern.
  *   - Methodology 2, complexity: O(1) graph nodes, O(n + nnz) memory.
+ *   - Methodology 1 (.eigsh) and Methodology 2, eigenvalue problems: the
+ *     eigenvalue gradient d lambda / d A_ij = v_i v_j on the pattern
+ *     (Hellmann-Feynman); the Lanczos process below is this oracle's reading
+ *     of .eigsh.
  * The CG steps themselves are the textbook Hestenes-Stiefel method that the
  * pages call "CG"; the pages fix no variant, so the plain one is used.
  *
@@ -481,6 +485,71 @@ void oracle_matvec_grad(int64_t n, const int64_t* rowptr, const int32_t* col,
   free(rowptr_t);
   free(col_t);
   free(vals_t);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lanczos (the .eigsh of Methodology 1)                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages name .eigsh (Methodology 1) but not its algorithm; the reading
+ * taken is the textbook one for a few extreme eigenpairs of a sparse
+ * symmetric matrix through products with A alone:
+ * m steps of the Lanczos process for symmetric A from the start vector v0,
+ * with full reorthogonalisation by classical Gram-Schmidt applied twice:
+ *   v_0 = v0 / |v0|;  for j = 0 .. m-1:
+ *     w = A v_j;
+ *     h = V_j^T w, w = w - V_j h;  h' = V_j^T w, w = w - V_j h'
+ *       (V_j = [v_0 .. v_j]; dot products and updates in index order);
+ *     alpha_j = h_j + h'_j;  beta_j = |w|;  v_{j+1} = w / beta_j.
+ * T = tridiag(beta, alpha, beta) is then the matrix of A in the orthonormal
+ * Krylov basis; its eigenpairs give the Ritz pairs (done by the caller).
+ * Stops after step j when beta_j <= 1e-10 |A v_j| (the Krylov space is an
+ * invariant subspace: what is left of w is rounding); returns the number of
+ * completed steps.  V receives v_0 .. v_steps, row-major [steps+1][n] (room
+ * for m+1 vectors).
+ */
+int64_t oracle_lanczos(int64_t n, const int64_t* rowptr, const int32_t* col,
+                       const double* vals, const double* v0, int64_t m, double* alpha,
+                       double* beta, double* V) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(m > 0 ? m + 1 : 1));
+  double nv = sqrt(oracle_dot(n, v0, v0));
+  for (int64_t i = 0; i < n; ++i) V[i] = v0[i] / nv;
+  int64_t steps = 0;
+  for (int64_t j = 0; j < m; ++j) {
+    const double* vj = V + j * n;
+    oracle_spmv(n, rowptr, col, vals, vj, w);
+    double wn = sqrt(oracle_dot(n, w, w));
+    double a = 0.0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int64_t l = 0; l <= j; ++l) h[l] = oracle_dot(n, V + l * n, w);
+      for (int64_t i = 0; i < n; ++i) {
+        double s = w[i];
+        for (int64_t l = 0; l <= j; ++l) s = s - V[l * n + i] * h[l];
+        w[i] = s;
+      }
+      a = a + h[j];
+    }
+    alpha[j] = a;
+    double b = sqrt(oracle_dot(n, w, w));
+    beta[j] = b;
+    steps = j + 1;
+    if (!(b > 1e-10 * wn)) break;
+    for (int64_t i = 0; i < n; ++i) V[(j + 1) * n + i] = w[i] / b;
+  }
+  free(w);
+  free(h);
+  return steps;
+}
+
+/* Hellmann-Feynman (Methodology 2, eigenvalue problems): for a simple
+ * eigenvalue with unit eigenvector v, d lambda / d A_ij = v_i v_j, on every
+ * stored slot (i, j) and nothing else. */
+void oracle_eig_grad(int64_t n, const int64_t* rowptr, const int32_t* col, const double* v,
+                     double* grad_vals) {
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) grad_vals[k] = v[i] * v[col[k]];
 }
 
 /* ------------------------------------------------------------------------ */

@@ -626,6 +626,99 @@ def pin_matvec_grad(lib=None):
         assert abs(fd - gv[k]) <= 1e-9 * max(1.0, abs(gv[k])), k
 
 
+# --------------------------------------------------------------------------
+# Lanczos eigsh and the Hellmann-Feynman gradient
+# --------------------------------------------------------------------------
+
+def _poisson_spectrum(N):
+    return np.sort([eigval(N, i, j) for i in range(1, N + 1) for j in range(1, N + 1)])
+
+
+def pin_eigsh_poisson(lib=None):
+    """Ritz values of the Poisson matrix against the closed-form spectrum
+    (multiple eigenvalues counted with multiplicity): the 4 largest after 300
+    steps, the 4 smallest when the Krylov space is exhausted; the Ritz vector
+    of the simple top eigenvalue is the closed-form v_NN."""
+    N = 24
+    A = _poisson(N)
+    lam = _poisson_spectrum(N)
+    v0 = W.normal_rhs(N * N, 70)
+    th, X, res = oracle.eigsh(A, 4, "LA", v0, 150, lib=lib)
+    # the residual estimate |beta_m y_m| is the true residual ||A v - theta v||
+    for l in range(4):
+        true = np.linalg.norm(oracle.spmv(A, X[l], lib=lib) - th[l] * X[l])
+        assert abs(res[l] - true) <= 1e-13 + 1e-6 * true, (l, res[l], true)
+    th, X, res = oracle.eigsh(A, 4, "LA", v0, 300, lib=lib)
+    assert np.allclose(th, lam[-4:], rtol=0, atol=1e-10), (th, lam[-4:])
+    assert np.all(res <= 1e-8)
+    v = eigvec(N, N, N)
+    v = v / np.linalg.norm(v)
+    assert abs(abs(X[-1] @ v) - 1.0) <= 1e-10
+    th, X, res = oracle.eigsh(A, 4, "SA", v0, N * N, lib=lib)
+    assert np.allclose(th, lam[:4], rtol=0, atol=1e-10), (th, lam[:4])
+
+
+def pin_eigsh_dense(lib=None):
+    """A random sparse symmetric matrix with distinct eigenvalues: every Ritz
+    value of the full-dimension process against dense eigh, an orthonormal
+    basis, and V^T A V = T (tridiagonal)."""
+    n = 120
+    rng = np.random.default_rng(71)
+    M = np.where(rng.random((n, n)) < 0.06, rng.uniform(-1, 1, (n, n)), 0.0)
+    M = np.triu(M, 1)
+    M = M + M.T + np.diag(rng.uniform(-2, 2, n))
+    rows, cols = np.nonzero(M)
+    rp = np.zeros(n + 1, np.int64)
+    np.add.at(rp, rows + 1, 1)
+    A = oracle.CSR(n, np.cumsum(rp), cols.astype(np.int32), M[rows, cols].copy())
+    alpha, beta, V = oracle.lanczos(A, rng.standard_normal(n), n, lib=lib)
+    k = alpha.shape[0]
+    Vk = V[:k]
+    assert np.max(np.abs(Vk @ Vk.T - np.eye(k))) <= 1e-12
+    T = np.diag(alpha) + np.diag(beta[:k - 1], 1) + np.diag(beta[:k - 1], -1)
+    assert np.max(np.abs(Vk @ M @ Vk.T - T)) <= 1e-10 * np.abs(M).sum(axis=1).max()
+    if k == n:
+        from scipy.linalg import eigh_tridiagonal
+        th = eigh_tridiagonal(alpha, beta[:k - 1], eigvals_only=True)
+        assert np.allclose(np.sort(th), np.linalg.eigvalsh(M), rtol=0, atol=1e-10)
+    th, X, res = oracle.eigsh(A, 3, "SA", rng.standard_normal(n), n, lib=lib)
+    ev, EV = np.linalg.eigh(M)
+    assert np.allclose(th, ev[:3], rtol=0, atol=1e-10)
+    for l in range(3):
+        assert abs(abs(X[l] @ EV[:, l]) - 1.0) <= 1e-9
+
+
+def pin_eig_grad(lib=None):
+    """d lambda_max / d vals[k] against central differences of the perturbed
+    (non-symmetric) matrix's largest eigenvalue; sum_k vals_k grad_k =
+    v^T A v = lambda; a stored zero gets v_i v_j."""
+    n = 30
+    rng = np.random.default_rng(72)
+    M = np.where(rng.random((n, n)) < 0.2, rng.uniform(-1, 1, (n, n)), 0.0)
+    M = np.triu(M, 1)
+    M = M + M.T + np.diag(np.linspace(-3, 3, n))
+    M[2, 9] = M[9, 2] = 0.0
+    mask = M != 0
+    mask[2, 9] = mask[9, 2] = True   # stored zeros
+    rows, cols = np.nonzero(mask)
+    rp = np.zeros(n + 1, np.int64)
+    np.add.at(rp, rows + 1, 1)
+    A = oracle.CSR(n, np.cumsum(rp), cols.astype(np.int32), M[rows, cols].copy())
+    th, X, _ = oracle.eigsh(A, 1, "LA", rng.standard_normal(n), n, lib=lib)
+    v = X[0]
+    gv = oracle.eig_grad(A, v, lib=lib)
+    assert abs(A.vals @ gv - th[0]) <= 1e-12 * max(1.0, abs(th[0]))
+    k29 = [k for k in range(A.nnz) if rows[k] == 2 and cols[k] == 9][0]
+    assert A.vals[k29] == 0.0 and gv[k29] != 0.0
+    for k in range(0, A.nnz, 7):
+        d = 1e-6
+        Mp, Mm = M.copy(), M.copy()
+        Mp[rows[k], cols[k]] += d
+        Mm[rows[k], cols[k]] -= d
+        fd = (np.max(np.linalg.eigvals(Mp).real) - np.max(np.linalg.eigvals(Mm).real)) / (2 * d)
+        assert abs(fd - gv[k]) <= 1e-6, (k, fd, gv[k])
+
+
 ALL_PINS = [
     pin_csr_poisson_closed_form, pin_csr_brute_force, pin_csr_rgg_symmetric,
     pin_spmv_eigenpairs, pin_spmv_dense, pin_dot,
@@ -635,4 +728,5 @@ ALL_PINS = [
     pin_adjoint_nonsymmetric_flag, pin_batched_shift_spectrum,
     pin_pcg_uniform_diagonal, pin_pcg_scaled_equivalence, pin_pcg_diagonal_one_step,
     pin_pcg_dense_lu, pin_pcg_statuses, pin_adjoint_jacobi, pin_matvec_grad,
+    pin_eigsh_poisson, pin_eigsh_dense, pin_eig_grad,
 ]

@@ -44,6 +44,10 @@ MUTATIONS = {
     "matvec_grad_no_transpose": ("oracle_spmv(n, rowptr_t, col_t, vals_t, g, grad_x);",
                                  "oracle_spmv(n, rowptr, col, vals, g, grad_x);"),
     "matvec_grad_swapped": ("grad_vals[k] = g[i] * x[col[k]];", "grad_vals[k] = g[col[k]] * x[i];"),
+    "lanczos_one_pass": ("for (int pass = 0; pass < 2; ++pass) {", "for (int pass = 0; pass < 1; ++pass) {"),
+    "lanczos_alpha_second_pass_only": ("a = a + h[j];", "a = h[j];"),
+    "lanczos_beta_squared": ("double b = sqrt(oracle_dot(n, w, w));", "double b = oracle_dot(n, w, w);"),
+    "eig_grad_diagonal_only": ("grad_vals[k] = v[i] * v[col[k]];", "grad_vals[k] = v[i] * v[i];"),
 }
 
 CHILD = r"""
