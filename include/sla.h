@@ -47,7 +47,9 @@ typedef enum {
   SLA_ERR_OOM = 3,        /* device allocation failed                          */
   SLA_ERR_DEVICE = 4,     /* a HIP call failed                                  */
   SLA_ERR_NOT_SPD = 5,    /* CG breakdown: p.Ap <= 0                            */
-  SLA_ERR_NONFINITE = 6   /* b.b, p.Ap or r.r is not finite                     */
+  SLA_ERR_NONFINITE = 6,  /* b.b, p.Ap or r.r is not finite                     */
+  SLA_ERR_KRYLOV = 7      /* eigsh: the Lanczos process ended (an invariant
+                             subspace was reached) after fewer than k steps   */
 } sla_status;
 
 typedef enum { SLA_I32 = 4, SLA_I64 = 8 } sla_index;
@@ -232,6 +234,58 @@ sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha_host,
 sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x,
                                          int64_t reps, double* avg_ms_host,
                                          hipStream_t stream);
+
+/*
+ * The .eigsh of Methodology 1 ("torch-sla" summary): the k extreme eigenpairs
+ * of each bound system by m steps of the Lanczos process from the start
+ * vector v0.  A must be symmetric (not checked; for a non-symmetric A the
+ * results mean nothing).  The pages name the operation
+ * but not its algorithm; this library takes the textbook one:
+ *   v_0 = v0 / |v0|; for j = 0 .. m-1:
+ *     w = A v_j; h = V_j^T w, w -= V_j h; h' = V_j^T w, w -= V_j h'
+ *     (full reorthogonalisation: classical Gram-Schmidt applied twice);
+ *     alpha_j = h_j + h'_j, beta_j = |w|, v_{j+1} = w / beta_j;
+ *   the process ends early when beta_j <= 1e-10 |A v_j| (an invariant
+ *   subspace).  The eigenpairs (theta, y) of the tridiagonal T =
+ *   tridiag(beta, alpha, beta) over the completed steps give the Ritz pairs
+ *   (theta, V y).
+ *   which   SLA_EIG_SMALLEST (0): the k smallest algebraic Ritz values;
+ *           SLA_EIG_LARGEST (1): the k largest.  Ascending in both cases.
+ *   m       Lanczos steps, k <= m <= n.
+ *   v0      [batch][n] start vectors (device); must not be zero.
+ *   theta   [batch][k] Ritz values (device), ascending.
+ *   X       [batch][k][n] unit Ritz vectors (device); the sign of each is
+ *           fixed by making the largest component of y positive.
+ *   resid   [batch][k] |beta_{steps-1} y_{steps-1}| = |A x - theta x|
+ *           (device): how far each pair is from an eigenpair of A.
+ *   info_host [batch] steps completed and status per system (may be NULL).
+ * Returns the first non-OK system status: SLA_ERR_ARG for a zero v0,
+ * SLA_ERR_NONFINITE, SLA_ERR_KRYLOV when fewer than k steps completed; a
+ * failed system's theta, X and resid are left untouched.  Workspace of
+ * (m + 1) n doubles is kept with the handle.  Synchronises `stream`.
+ */
+enum { SLA_EIG_SMALLEST = 0, SLA_EIG_LARGEST = 1 };
+typedef struct {
+  int64_t steps;    /* Lanczos steps completed                             */
+  int32_t status;   /* sla_status of this system                           */
+  int32_t reserved;
+} sla_eig_info;
+sla_status sla_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v0,
+                     double* theta, double* X, double* resid, sla_eig_info* info_host,
+                     hipStream_t stream);
+
+/*
+ * Gradient of the eigenvalues (Methodology 2, eigenvalue problems: the
+ * Hellmann-Feynman relation d lambda / d A_ij = v_i v_j for a simple
+ * eigenvalue with unit eigenvector v, on the sparsity pattern only): for a
+ * loss with grad_theta = dL/dtheta [batch][k],
+ *   grad_vals[s][slot (i, j)] = sum_t grad_theta[s][t] X[s][t][i] X[s][t][j]
+ * on every stored slot [batch][nnz], the terms added in ascending t.
+ * X [batch][k][n] unit eigenvectors (as sla_eigsh returns them).  All
+ * device memory.
+ */
+sla_status sla_eig_grad(sla_csr A, int64_t k, const double* X, const double* grad_theta,
+                        double* grad_vals, hipStream_t stream);
 
 /*
  * SpMV kernel family.  At creation the pattern analysis checks whether every

@@ -27,12 +27,14 @@ __all__ = [
     "sla_csr_create", "sla_csr_create_from_csr", "sla_csr_values_from_coo",
     "sla_csr_grad_to_coo", "sla_spmv", "sla_cg_solve", "sla_cg_adjoint",
     "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
+    "sla_spmv_transpose", "sla_matvec_grad", "sla_eigsh", "sla_eig_grad", "EigInfo",
     "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 
-OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE = range(7)
+OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE, ERR_KRYLOV = range(8)
+EIG_SMALLEST, EIG_LARGEST = 0, 1
 I32, I64 = 4, 8
 FLAG_X0, FLAG_HISTORY, FLAG_JACOBI = 1, 2, 4
 
@@ -44,6 +46,7 @@ EXPORTS = [
     "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_spmv_variant",
     "sla_csr_set_graph_block",
     "sla_csr_set_workgroups_per_cu", "sla_spmv_transpose", "sla_matvec_grad",
+    "sla_eigsh", "sla_eig_grad",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -56,6 +59,11 @@ if not os.path.exists(LIB_PATH):
 class _Info(ctypes.Structure):
     _fields_ = [("iterations", ctypes.c_int64), ("rel_residual", ctypes.c_double),
                 ("converged", ctypes.c_int32), ("status", ctypes.c_int32)]
+
+
+class _EigInfo(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("status", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -89,6 +97,8 @@ def _bind(lib):
         "sla_csr_set_workgroups_per_cu": [_P, _S],
         "sla_spmv_transpose": [_P, _P, _P, _P],
         "sla_matvec_grad": [_P, _P, _P, _P, _P, _P],
+        "sla_eigsh": [_P, _I64, _S, _I64, _P, _P, _P, _P, _P, _P],
+        "sla_eig_grad": [_P, _I64, _P, _P, _P, _P],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
@@ -349,6 +359,55 @@ def sla_matvec_grad(A: CSRPattern, values: torch.Tensor, x: torch.Tensor, grad_y
     return gx, gv
 
 
+@dataclass
+class EigInfo:
+    steps: int
+    status: int
+
+
+_WHICH = {"SA": EIG_SMALLEST, "LA": EIG_LARGEST}
+
+
+def sla_eigsh(A: CSRPattern, values: torch.Tensor, k: int, which: str, m: int,
+              v0: torch.Tensor, stream=None, check: bool = True):
+    """k extreme Ritz pairs by m Lanczos steps (full reorthogonalisation).
+
+    which "LA" (largest) or "SA" (smallest); v0 [n] or [batch, n].  Returns
+    (theta [.., k] ascending, X [.., k, n] unit vectors, resid [.., k], infos).
+    """
+    batch = A.bind(values)
+    if which not in _WHICH:
+        raise ValueError(f"which must be 'LA' or 'SA', not {which!r}")
+    _shape(v0, _vec_shape(A, batch, v0), "v0")
+    lead = (batch,) if v0.dim() == 2 else ()
+    theta = torch.empty(lead + (k,), dtype=torch.float64, device=v0.device)
+    X = torch.empty(lead + (k, A.n), dtype=torch.float64, device=v0.device)
+    resid = torch.empty(lead + (k,), dtype=torch.float64, device=v0.device)
+    infos = (_EigInfo * batch)()
+    st = _lib.sla_eigsh(A.handle, int(k), _WHICH[which], int(m), _dev(v0, torch.float64, "v0"),
+                        theta.data_ptr(), X.data_ptr(), resid.data_ptr(), infos,
+                        _stream(stream))
+    if check:
+        _check(st)
+    return theta, X, resid, [EigInfo(int(i.steps), int(i.status)) for i in infos]
+
+
+def sla_eig_grad(A: CSRPattern, values: torch.Tensor, X: torch.Tensor, grad_theta: torch.Tensor,
+                 stream=None) -> torch.Tensor:
+    """grad_vals[slot (i, j)] = sum_t grad_theta[t] X[t, i] X[t, j] (Hellmann-Feynman)."""
+    batch = A.bind(values)
+    k = grad_theta.shape[-1]
+    want = (batch, k, A.n) if grad_theta.dim() == 2 else (k, A.n)
+    _shape(X, want, "X")
+    _shape(grad_theta, want[:-1], "grad_theta")
+    gv = torch.empty((batch, A.nnz) if grad_theta.dim() == 2 else (A.nnz,), dtype=torch.float64,
+                     device=X.device)
+    _check(_lib.sla_eig_grad(A.handle, int(k), _dev(X, torch.float64, "X"),
+                             _dev(grad_theta, torch.float64, "grad_theta"), gv.data_ptr(),
+                             _stream(stream)))
+    return gv
+
+
 def _solve_call(fn, A, b, x, tol, maxit, flags, batch, stream, check):
     _shape(b, _vec_shape(A, batch, b), "b")
     _shape(x, _vec_shape(A, batch, b), "x")
@@ -507,6 +566,29 @@ class _MatVec(torch.autograd.Function):
         return gv, gx, None
 
 
+class _EigSH(torch.autograd.Function):
+    """theta, X = eigsh(A); backward d theta_t / d A_ij = X_ti X_tj on the
+    pattern (Hellmann-Feynman).  X carries no gradient."""
+
+    @staticmethod
+    def forward(ctx, values, pattern, k, which, m, v0):
+        theta, X, _, _ = sla_eigsh(pattern, values.detach().contiguous(), k, which, m,
+                                   v0.contiguous())
+        ctx.pattern = pattern
+        ctx.save_for_backward(values, X)
+        ctx.mark_non_differentiable(X)
+        return theta, X
+
+    @staticmethod
+    def backward(ctx, grad_theta, grad_X):
+        values, X = ctx.saved_tensors
+        gv = None
+        if ctx.needs_input_grad[0]:
+            gv = sla_eig_grad(ctx.pattern, values.detach().contiguous(), X,
+                              grad_theta.contiguous())
+        return gv, None, None, None, None, None
+
+
 class SparseTensor:
     """A sparse matrix (or a batch sharing one pattern) with .solve / .matvec.
 
@@ -535,6 +617,20 @@ class SparseTensor:
     def matvec(self, x: torch.Tensor) -> torch.Tensor:
         """y = A x, differentiable in the values and in x (one graph node)."""
         return _MatVec.apply(self.values, x, self.pattern)
+
+    def eigsh(self, k: int = 6, which: str = "LA", m: int | None = None,
+              v0: torch.Tensor | None = None):
+        """(theta, X): the k largest ("LA") or smallest ("SA") eigenpairs of the
+        symmetric matrix by m Lanczos steps (default min(n, max(2k + 1, 64)));
+        theta is differentiable in the values (Hellmann-Feynman)."""
+        n = self.pattern.n
+        if m is None:
+            m = min(n, max(2 * k + 1, 64))
+        if v0 is None:
+            g = torch.Generator().manual_seed(0)
+            shape = (self.values.shape[0], n) if self.values.dim() == 2 else (n,)
+            v0 = torch.randn(shape, generator=g, dtype=torch.float64).to(self.values.device)
+        return _EigSH.apply(self.values, self.pattern, int(k), which, int(m), v0)
 
 
 def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,

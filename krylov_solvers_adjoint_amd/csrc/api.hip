@@ -84,6 +84,7 @@ namespace sla {
 void free_handle(sla_csr A) {
   if (!A) return;
   release_workspace(A);
+  release_eig_work(A);
   free_handle(A->trans);
   dev_free(A->trans_vals);
   dev_free(A->rowptr);
@@ -111,6 +112,7 @@ const char* sla_status_string(sla_status s) {
     case SLA_ERR_DEVICE: return "SLA_ERR_DEVICE";
     case SLA_ERR_NOT_SPD: return "SLA_ERR_NOT_SPD";
     case SLA_ERR_NONFINITE: return "SLA_ERR_NONFINITE";
+    case SLA_ERR_KRYLOV: return "SLA_ERR_KRYLOV";
   }
   return "SLA_UNKNOWN";
 }
@@ -289,6 +291,37 @@ sla_status sla_matvec_grad(sla_csr A, const double* x, const double* grad_y, dou
   if (grad_vals != nullptr && A->nnz > 0)
     SLA_TRY(launch_slot_products(A, A->batch, grad_y, x, grad_vals, false, stream));
   return SLA_OK;
+  API_END
+}
+
+sla_status sla_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v0,
+                     double* theta, double* X, double* resid, sla_eig_info* info_host,
+                     hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_eigsh: NULL handle");
+  REQUIRE(A->batch >= 1, "sla_eigsh: no values bound (sla_csr_set_values)");
+  REQUIRE(v0 != nullptr && theta != nullptr && X != nullptr && resid != nullptr,
+          "sla_eigsh: NULL vector");
+  REQUIRE(which == SLA_EIG_SMALLEST || which == SLA_EIG_LARGEST, "sla_eigsh: bad `which` %d",
+          which);
+  REQUIRE(k >= 1 && k <= m && m <= A->n, "sla_eigsh: need 1 <= k <= m <= n (k=%lld m=%lld n=%lld)",
+          (long long)k, (long long)m, (long long)A->n);
+  return run_eigsh(A, k, which, m, v0, theta, X, resid, info_host, stream);
+  API_END
+}
+
+sla_status sla_eig_grad(sla_csr A, int64_t k, const double* X, const double* grad_theta,
+                        double* grad_vals, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_eig_grad: NULL handle");
+  REQUIRE(A->batch >= 1, "sla_eig_grad: no values bound (sla_csr_set_values)");
+  REQUIRE(k >= 1, "sla_eig_grad: k must be >= 1");
+  REQUIRE(X != nullptr && grad_theta != nullptr && grad_vals != nullptr,
+          "sla_eig_grad: NULL vector");
+  if (A->nnz == 0) return SLA_OK;
+  return launch_eig_grad(A, k, X, grad_theta, grad_vals, stream);
   API_END
 }
 

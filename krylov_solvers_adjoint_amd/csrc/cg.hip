@@ -49,16 +49,6 @@
 namespace sla {
 namespace {
 
-#define LAUNCH_CHECK()                                                         \
-  do {                                                                         \
-    hipError_t e_ = hipGetLastError();                                         \
-    if (e_ != hipSuccess) {                                                    \
-      set_error("kernel launch failed: %s (%s:%d)", hipGetErrorString(e_),     \
-                __FILE__, __LINE__);                                           \
-      return SLA_ERR_DEVICE;                                                   \
-    }                                                                          \
-  } while (0)
-
 // Gathers a lane keeps in flight while walking its row (plain CSR rows).
 constexpr int kGather = 4;
 // Tiles a wave keeps in flight in the streaming passes.

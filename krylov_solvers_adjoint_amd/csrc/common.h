@@ -33,6 +33,18 @@ void clear_error();
     if (s_ != SLA_OK) return s_;                                               \
   } while (0)
 
+// Report a failed kernel launch (call after launching, inside a function
+// that returns sla_status).
+#define LAUNCH_CHECK()                                                         \
+  do {                                                                         \
+    hipError_t e_ = hipGetLastError();                                         \
+    if (e_ != hipSuccess) {                                                    \
+      ::sla::set_error("kernel launch failed: %s (%s:%d)",                     \
+                       hipGetErrorString(e_), __FILE__, __LINE__);             \
+      return SLA_ERR_DEVICE;                                                   \
+    }                                                                          \
+  } while (0)
+
 // Device allocation that reports SLA_ERR_OOM.
 sla_status dev_alloc(void** p, size_t bytes, const char* what);
 template <typename T>

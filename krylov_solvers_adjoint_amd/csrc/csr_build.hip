@@ -361,16 +361,6 @@ __global__ void k_tile_nnz_max(int64_t n, int64_t tiles, const RP* __restrict__ 
   }
 }
 
-#define LAUNCH_CHECK()                                                         \
-  do {                                                                         \
-    hipError_t e_ = hipGetLastError();                                         \
-    if (e_ != hipSuccess) {                                                    \
-      set_error("kernel launch failed: %s (%s:%d)", hipGetErrorString(e_),     \
-                __FILE__, __LINE__);                                           \
-      return SLA_ERR_DEVICE;                                                   \
-    }                                                                          \
-  } while (0)
-
 // RAII list of temporary device buffers for the build.
 struct Temps {
   std::vector<void*> ptrs;

@@ -6,6 +6,10 @@
 
 #include "common.h"
 
+namespace sla {
+struct EigWork;  // Lanczos workspace (lanczos.hip)
+}
+
 struct sla_csr_s {
   int device = 0;
   int64_t n = 0;
@@ -77,6 +81,8 @@ struct sla_csr_s {
   // offsets lie within +-63 (0: the line walk does not apply)
   int64_t line = 0;
   hipStream_t capture_stream = nullptr;
+  // Lanczos basis and scratch, allocated by the first eigsh call
+  sla::EigWork* eig = nullptr;
   std::map<int64_t, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
 };
 
@@ -102,6 +108,14 @@ sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda,
                                const double* x, double* grad_vals, hipStream_t stream);
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
                   uint32_t flags, sla_cg_info* info, hipStream_t stream);
+// Lanczos eigenpairs of every bound system (lanczos.hip)
+sla_status run_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v0,
+                     double* theta, double* X, double* resid, sla_eig_info* info,
+                     hipStream_t stream);
+// grad[s][slot (i, j)] = sum_t g[s][t] X[s][t][i] X[s][t][j]
+sla_status launch_eig_grad(sla_csr A, int64_t k, const double* X, const double* g,
+                           double* grad, hipStream_t stream);
+void release_eig_work(sla_csr A);
 sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps,
                            double* avg_ms, hipStream_t stream);
 
