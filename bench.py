@@ -305,6 +305,111 @@ def bench_rgg(n: int, kernel_reps: int):
     return out
 
 
+def spmv_bytes(variant: str, n: int, nnz: int, rp_bytes: int) -> int:
+    """Algorithmic bytes of y = A x: the matrix once (banded: values, a mask
+    byte per row, a row pointer per 64 rows; else values, columns, row
+    pointers), x read once, y written once."""
+    if variant in ("lines", "banded"):
+        return 8 * nnz + n + rp_bytes * ((n + 63) // 64 + 1) + 16 * n
+    return 12 * nnz + rp_bytes * (n + 1) + 16 * n
+
+
+def _event_ms(fn, reps: int) -> float:
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_matvec(reps: int):
+    """The differentiable .matvec on the 1000 x 1000 Poisson matrix: y = A x,
+    y = A^T x (values gathered into the transposed pattern's order on each
+    call) and the backward pass (grad_x = A^T g plus grad_vals = g_i x_j)."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    N = 1000
+    n = N * N
+    P, v, _, _ = gpu_setup(N, np.int32)
+    x = torch.from_numpy(W.normal_rhs(n, 2)).to(dev)
+    g = torch.from_numpy(W.normal_rhs(n, 3)).to(dev)
+    nnz = P.nnz
+    variant = "banded" if P.banded else "csr"
+    fwd = _event_ms(lambda: K.sla_spmv(P, v, x), reps)
+    trn = _event_ms(lambda: K.sla_spmv_transpose(P, v, x), reps)
+    bwd = _event_ms(lambda: K.sla_matvec_grad(P, v, x, g), reps)
+    b_fwd = spmv_bytes(variant, n, nnz, 4)
+    # A^T x through the transposed pattern: its columns and its map to A's
+    # slots (4 B each per slot), A's values (8 B per slot), its row pointers,
+    # x read and y written once
+    b_trn = 16 * nnz + 4 * (n + 1) + 16 * n
+    # plus grad_vals = g_i x_j: row pointers, columns, g and x read, 8 B
+    # written per slot
+    b_bwd = b_trn + 12 * nnz + 4 * (n + 1) + 16 * n
+    out = dict(n=n, nnz=nnz, spmv=variant,
+               spmv_ms=fwd, spmv_GBps=b_fwd / (fwd * 1e-3) / 1e9,
+               transpose_ms=trn, transpose_GBps=b_trn / (trn * 1e-3) / 1e9,
+               backward_ms=bwd, backward_GBps=b_bwd / (bwd * 1e-3) / 1e9,
+               bytes=dict(spmv=b_fwd, transpose=b_trn, backward=b_bwd))
+    del P, v, x, g
+    torch.cuda.synchronize()
+    return out
+
+
+def lanczos_bytes(n: int, steps: int, k: int, spmv: int) -> int:
+    """Algorithmic bytes of `steps` Lanczos steps with two Gram-Schmidt passes
+    (step j reads the j + 1 basis vectors four times: two dot passes, two
+    updates; w is read 4 times and written twice, v_{j+1} read and written
+    once) plus the start and the k Ritz vectors."""
+    gs = 8 * n * (2 * steps * (steps + 1) + 8 * steps)
+    return gs + steps * spmv + 24 * n + 8 * n * (steps + k)
+
+
+def bench_eigsh(m: int, k: int):
+    """The .eigsh on the 1000 x 1000 Poisson matrix: the k largest
+    eigenvalues by m Lanczos steps with full reorthogonalisation."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    N = 1000
+    n = N * N
+    P, v, _, free0 = gpu_setup(N, np.int32)
+    v0 = torch.from_numpy(W.normal_rhs(n, 72)).to(dev)
+    K.sla_eigsh(P, v, k, "LA", m, v0)  # workspace, warm caches
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    t0 = time.perf_counter()
+    th, X, res, infos = K.sla_eigsh(P, v, k, "LA", m, v0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    steps = infos[0].steps
+    nbytes = lanczos_bytes(n, steps, k, spmv_bytes("banded" if P.banded else "csr", n, P.nnz, 4))
+    grad_ms = _event_ms(lambda: K.sla_eig_grad(P, v, X, torch.ones(k, dtype=torch.float64,
+                                                                   device=dev)), 10)
+    out = dict(n=n, nnz=P.nnz, k=k, m=m, steps=steps, ms=1e3 * wall,
+               steps_per_s=steps / wall, eff_GBps=nbytes / wall / 1e9,
+               algorithmic_bytes=nbytes, basis_MB=(free0 - free1) / 2**20,
+               theta=th.cpu().tolist(), resid=res.cpu().tolist(),
+               # largest eigenvalue of the 5-point Laplacian, 4 + 4 cos(pi / (N + 1))
+               theta_top_exact=4.0 + 4.0 * float(np.cos(np.pi / (N + 1))),
+               eig_grad_ms=grad_ms)
+    del P, v, v0, th, X, res
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(seconds: float):
     """The oracle as it stands, on a bounded sample of the same workload:
     forward and adjoint CG on the 1000 x 1000 Poisson system, k fixed
@@ -341,10 +446,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--sizes", default="16m,169m,rgg4m",
                     help="extra workloads: 16m / 169m (Poisson, 500 fixed iterations), rgg4m "
-                         "(random geometric graph, tol 1e-8 forward + adjoint); '' for none")
+                         "(random geometric graph, tol 1e-8 forward + adjoint); '' for none; "
+                         "with --skip-headline also matvec and eigsh")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the .matvec and .eigsh measurements")
+    ap.add_argument("--eig-steps", type=int, default=300,
+                    help="Lanczos steps of the .eigsh measurement")
     ap.add_argument("--skip-headline", action="store_true",
                     help="only the --sizes runs (for profiler passes); prints no JSON line")
     ap.add_argument("--csr-only", action="store_true",
@@ -382,6 +492,13 @@ def main():
                 out = bench_rgg(4_000_000, args.kernel_reps)
                 log(f"[bench] rgg4m: {out}")
                 continue
+            if s.lower() == "matvec":
+                log(f"[bench] matvec: {bench_matvec(args.kernel_reps)}")
+                continue
+            if s.lower() == "eigsh":
+                out = bench_eigsh(args.eig_steps, 4)
+                log(f"[bench] eigsh: {out['ms']:.1f} ms, {out['eff_GBps']:.0f} GB/s")
+                continue
             N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
                      "169m": (13000, np.int64)}[s.lower()]
             out = bench_size(N, rp, 500, args.kernel_reps)
@@ -409,6 +526,16 @@ def main():
         sizes[s.lower()] = bench_size(N, rp, 500, args.kernel_reps)
         log(f"[bench] size {s}: {sizes[s.lower()]['ms_per_iteration']:.3f} ms/it, "
             f"{sizes[s.lower()]['eff_GBps']:.0f} GB/s")
+
+    nxt = {}
+    if not args.no_next:
+        log("[bench] .matvec on Poisson 1000x1000")
+        nxt["matvec"] = bench_matvec(args.kernel_reps)
+        log(f"[bench] .matvec: {nxt['matvec']}")
+        log(f"[bench] .eigsh on Poisson 1000x1000: k=4 largest, {args.eig_steps} Lanczos steps")
+        nxt["eigsh"] = bench_eigsh(args.eig_steps, 4)
+        log(f"[bench] .eigsh: {nxt['eigsh']['ms']:.1f} ms, "
+            f"{nxt['eigsh']['eff_GBps']:.0f} GB/s")
 
     digest = source_digest()
     spmv_ms = head["kernel_ms"]["spmv_step"]
@@ -450,6 +577,7 @@ def main():
         "kernel_ms": head["kernel_ms"],
         "roofline": roofline,
         "sizes": sizes,
+        "next": nxt,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

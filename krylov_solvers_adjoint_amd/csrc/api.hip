@@ -86,7 +86,6 @@ void free_handle(sla_csr A) {
   release_workspace(A);
   release_eig_work(A);
   free_handle(A->trans);
-  dev_free(A->trans_vals);
   dev_free(A->rowptr);
   dev_free(A->col);
   dev_free(A->perm);

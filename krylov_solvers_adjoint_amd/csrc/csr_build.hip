@@ -676,6 +676,54 @@ __global__ void k_expand_rows(int64_t n, const RP* __restrict__ rowptr, int32_t*
   for (int64_t k = rowptr[i]; k < int64_t(rowptr[i + 1]); ++k) rows[k] = int32_t(i);
 }
 
+// y[s][j] = (A_s^T x_s)_j from the transposed pattern T: row j of T holds
+// the slots of column j of A in ascending row i, and src maps each slot of T
+// to the slot of A it came from, so A's values are read in place.  One wave
+// per 64-row tile of T: its lanes form the products a x of consecutive slots
+// (`cap` at a time) in LDS, then each lane adds its row's products in slot
+// order, y = 0, then y = y + a x: an explicit transpose followed by a CSR
+// product, bit for bit.
+template <typename RP>
+__global__ __launch_bounds__(kIterBlock) void k_spmv_transpose(
+    int64_t n, int64_t nnz, int64_t tiles, int cap, const RP* __restrict__ rowptr_t,
+    const int32_t* __restrict__ col_t, const uint32_t* __restrict__ src,
+    const double* __restrict__ vals, const double* __restrict__ x, double* __restrict__ y) {
+  extern __shared__ double prod_lds[];
+  constexpr int kW = kIterBlock / kWave;
+  const int wv = wave_index();
+  const int lane = int(lane_id());
+  double* pr = prod_lds + int64_t(wv) * cap;
+  const int64_t s = blockIdx.y;
+  const double* v = vals + s * nnz;
+  const double* xs = x + s * n;
+  double* ys = y + s * n;
+  for (int64_t t = int64_t(blockIdx.x) * kW + wv; t < tiles; t += int64_t(gridDim.x) * kW) {
+    const int64_t r0 = t * kTileRows;
+    const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
+    const int64_t s0 = rowptr_t[r0];
+    const int64_t len = int64_t(rowptr_t[r1]) - s0;
+    const int64_t i = r0 + lane;
+    int64_t a = 0, e = 0;
+    if (i < r1) {
+      a = int64_t(rowptr_t[i]) - s0;
+      e = int64_t(rowptr_t[i + 1]) - s0;
+    }
+    double acc = 0.0;
+    for (int64_t c0 = 0; c0 < len; c0 += cap) {
+      const int64_t clen = len - c0 < cap ? len - c0 : cap;
+      for (int64_t q = lane; q < clen; q += kWave) {
+        const int64_t k = s0 + c0 + q;
+        pr[q] = v[src[k]] * xs[col_t[k]];
+      }
+      wave_sync();
+      const int64_t qa = a > c0 ? a : c0, qe = e < c0 + clen ? e : c0 + clen;
+      for (int64_t q = qa; q < qe; ++q) acc = acc + pr[q - c0];
+      wave_sync();
+    }
+    if (i < r1) ys[i] = acc;
+  }
+}
+
 }  // namespace
 
 sla_status analyse_pattern(sla_csr A, hipStream_t st) {
@@ -773,6 +821,11 @@ sla_status build_transpose(sla_csr A, hipStream_t st) {
     }
   }
   dev_free(rows);
+  if (s == SLA_OK && T->nnz != A->nnz) {
+    // the slots of A are distinct (row, column) pairs, so none may merge
+    set_error("transpose: %lld slots became %lld", (long long)A->nnz, (long long)T->nnz);
+    s = SLA_ERR_CSR;
+  }
   if (s != SLA_OK) {
     free_handle(T);
     return s;
@@ -784,17 +837,24 @@ sla_status build_transpose(sla_csr A, hipStream_t st) {
 sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t st) {
   SLA_TRY(build_transpose(A, st));
   sla_csr T = A->trans;
-  const int64_t batch = A->batch;
-  if (A->trans_vals == nullptr || A->trans_batch < batch) {
-    dev_free(A->trans_vals);
-    A->trans_vals = nullptr;
-    SLA_TRY(dev_alloc(&A->trans_vals, size_t(batch) * size_t(A->nnz > 0 ? A->nnz : 1),
-                      "transposed values"));
-    A->trans_batch = batch;
-  }
-  // our values in the transposed slot order (a copy: one slot per triplet)
-  if (A->nnz > 0) SLA_TRY(launch_values_from_coo(T, A->vals, A->trans_vals, batch, st));
-  return launch_spmv(T, A->trans_vals, batch, x, y, st);
+  // the transposed pattern was built from one COO triplet per slot of A, in
+  // slot order: the triplet of each of its slots is the slot of A
+  constexpr int64_t kW = kIterBlock / kWave;
+  int64_t blocks = (T->tiles + kW - 1) / kW;
+  blocks = blocks < 1 ? 1 : (blocks > 65535 ? 65535 : blocks);
+  const int cap = T->wave_cap;  // >= 1 once the pattern is analysed
+  const dim3 g(unsigned(blocks), unsigned(A->batch));
+  const size_t lds = size_t(kW) * size_t(cap) * sizeof(double);
+  if (T->rp_idx == SLA_I32)
+    k_spmv_transpose<int32_t><<<g, kIterBlock, lds, st>>>(
+        A->n, A->nnz, T->tiles, cap, (const int32_t*)T->rowptr, T->col, T->sorted_idx, A->vals,
+        x, y);
+  else
+    k_spmv_transpose<int64_t><<<g, kIterBlock, lds, st>>>(
+        A->n, A->nnz, T->tiles, cap, (const int64_t*)T->rowptr, T->col, T->sorted_idx, A->vals,
+        x, y);
+  LAUNCH_CHECK();
+  return SLA_OK;
 }
 
 sla_status launch_values_from_coo(sla_csr A, const double* coo_val, double* vals, int64_t batch,

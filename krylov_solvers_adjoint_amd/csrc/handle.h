@@ -44,11 +44,9 @@ struct sla_csr_s {
 
   // the transposed pattern, built on first use by the transposed product:
   // a handle of its own whose COO triplets are this pattern's slots with
-  // rows and columns swapped (so its perm maps our slots to its slots), and
-  // its values [batch][nnz] gathered from ours on each call
+  // rows and columns swapped, so that its sorted_idx maps each of its slots
+  // to the slot of ours it transposes
   sla_csr_s* trans = nullptr;
-  double* trans_vals = nullptr;
-  int64_t trans_batch = 0;
 
   // workspace, sized for ws_batch systems
   int64_t ws_batch = 0;

@@ -28,9 +28,12 @@
 namespace sla {
 
 constexpr int kLzBlock = 256;   // workgroup of the Lanczos kernels (4 waves)
-constexpr int kLzDotVecs = 8;   // basis vectors per block sum of the dot pass
+constexpr int kLzDotVecs = 8;   // basis vectors per workgroup of the dot pass
+constexpr int64_t kLzChunk = 2048;  // rows per workgroup of the dot pass
+constexpr int kLzDotRows = 4;   // rows per thread and loop trip of the dot pass
 constexpr int kLzRitz = 8;      // Ritz vectors accumulated per pass over V
 constexpr int kInvIters = 3;    // inverse-iteration solves per eigenvector
+constexpr int64_t kTriLdsMax = 960;  // largest m whose tridiagonal work fits in LDS
 constexpr double kBreakdown = 1e-10;
 
 struct alignas(64) LzState {
@@ -62,54 +65,62 @@ struct EigWork {
 // Gram-Schmidt passes
 // ---------------------------------------------------------------------------
 
-// part[l][g] = sum over the rows of workgroup g of src_l[i] w[i], where src_l
-// is basis vector l for l < nvec and w itself for l == nvec (when with_ww).
-// R rows per thread, strided by the workgroup size.
-template <int R>
+// part[l][g] = sum over the rows of chunk g of src_l[i] w[i], where src_l is
+// basis vector l for l < nvec and w itself for l == nvec (when with_ww).
+// A workgroup takes one chunk of kLzChunk rows and a block of kLzDotVecs
+// vectors and reduces its sums once, at the end.  Workgroups are numbered so
+// that those sharing a chunk run on one XCD one after another (workgroup i
+// runs on XCD i % 8): the chunk of w they all read then comes from that
+// XCD's L2 after the first.
 __global__ __launch_bounds__(kLzBlock) void k_lz_dot(const double* __restrict__ V, int64_t n,
                                                      int64_t nvec, const double* __restrict__ w,
                                                      int with_ww, double* __restrict__ part,
-                                                     int64_t G, const LzState* __restrict__ st) {
+                                                     int64_t G, int64_t nblk,
+                                                     const LzState* __restrict__ st) {
   if (st->stop) return;
   __shared__ double red[kLzBlock / kWave][kLzDotVecs];
-  const int64_t base = int64_t(blockIdx.x) * (kLzBlock * R) + threadIdx.x;
-  double wv[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t i = base + int64_t(r) * kLzBlock;
-    wv[r] = i < n ? w[i] : 0.0;
-  }
+  const int64_t xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int64_t g = (slot / nblk) * kXcds + xcd;
+  const int64_t l0 = (slot % nblk) * kLzDotVecs;
+  if (g >= G) return;
   const int64_t total = nvec + (with_ww ? 1 : 0);
-  const int wave = wave_index();
-  for (int64_t l0 = 0; l0 < total; l0 += kLzDotVecs) {
-    double acc[kLzDotVecs];
+  double acc[kLzDotVecs];
+#pragma unroll
+  for (int q = 0; q < kLzDotVecs; ++q) acc[q] = 0.0;
+  const int64_t r1 = (g + 1) * kLzChunk < n ? (g + 1) * kLzChunk : n;
+  for (int64_t i0 = g * kLzChunk + threadIdx.x; i0 < r1; i0 += kLzBlock * kLzDotRows) {
+    double wi[kLzDotRows];
+#pragma unroll
+    for (int r = 0; r < kLzDotRows; ++r) {
+      const int64_t i = i0 + r * kLzBlock;
+      wi[r] = i < r1 ? w[i] : 0.0;
+    }
 #pragma unroll
     for (int q = 0; q < kLzDotVecs; ++q) {
-      acc[q] = 0.0;
       const int64_t l = l0 + q;
       if (l < total) {
         const double* src = l < nvec ? V + l * n : w;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int64_t i = base + int64_t(r) * kLzBlock;
-          if (i < n) acc[q] = fma(src[i], wv[r], acc[q]);
+        for (int r = 0; r < kLzDotRows; ++r) {
+          const int64_t i = i0 + r * kLzBlock;
+          if (i < r1) acc[q] = fma(src[i], wi[r], acc[q]);
         }
       }
     }
+  }
 #pragma unroll
-    for (int q = 0; q < kLzDotVecs; ++q) acc[q] = wave_sum(acc[q]);
-    if (lane_id() == 0) {
+  for (int q = 0; q < kLzDotVecs; ++q) acc[q] = wave_sum(acc[q]);
+  const int wave = wave_index();
+  if (lane_id() == 0) {
 #pragma unroll
-      for (int q = 0; q < kLzDotVecs; ++q) red[wave][q] = acc[q];
-    }
-    __syncthreads();
-    if (threadIdx.x < kLzDotVecs && l0 + threadIdx.x < total) {
-      double s = 0.0;
+    for (int q = 0; q < kLzDotVecs; ++q) red[wave][q] = acc[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < kLzDotVecs && l0 + threadIdx.x < total) {
+    double s = 0.0;
 #pragma unroll
-      for (int v = 0; v < kLzBlock / kWave; ++v) s = s + red[v][threadIdx.x];
-      part[(l0 + threadIdx.x) * G + blockIdx.x] = s;
-    }
-    __syncthreads();
+    for (int v = 0; v < kLzBlock / kWave; ++v) s = s + red[v][threadIdx.x];
+    part[(l0 + threadIdx.x) * G + g] = s;
   }
 }
 
@@ -330,19 +341,38 @@ __device__ void tri_shifted_solve(const double* a, const double* b, int64_t m, d
 // (which = SLA_EIG_LARGEST: the k largest, else the k smallest), ascending;
 // Y[t][0 .. steps) their unit eigenvectors (largest component positive),
 // resid[t] = |beta_{steps-1} Y[t][steps-1]|, the residual norm of the Ritz pair.
-__global__ __launch_bounds__(kWave) void k_tri_eig(const double* __restrict__ alpha,
-                                                   const double* __restrict__ beta, int64_t k,
+// With use_lds, T and the inverse-iteration arrays live in LDS (8 ldy
+// doubles of dynamic LDS): the LU recurrences then wait on LDS, not on
+// global memory, at every step.
+__global__ __launch_bounds__(kWave) void k_tri_eig(const double* __restrict__ alpha_g,
+                                                   const double* __restrict__ beta_g, int64_t k,
                                                    int which, double* __restrict__ theta,
                                                    double* __restrict__ Y, int64_t ldy,
                                                    double* __restrict__ resid,
-                                                   double* __restrict__ scratch,
+                                                   double* __restrict__ scratch_g, int use_lds,
                                                    LzState* __restrict__ st) {
   __shared__ double bounds[4];
+  extern __shared__ double tri_lds[];
   if (st->status != SLA_OK) return;
   const int64_t m = st->steps;
   if (m < k) {
     if (threadIdx.x == 0) st->status = SLA_ERR_KRYLOV;
     return;
+  }
+  const double* alpha = alpha_g;
+  const double* beta = beta_g;
+  double* scratch = scratch_g;
+  if (use_lds) {
+    double* a_s = tri_lds;
+    double* b_s = tri_lds + ldy;
+    for (int64_t i = threadIdx.x; i < m; i += kWave) {
+      a_s[i] = alpha_g[i];
+      b_s[i] = beta_g[i];
+    }
+    __syncthreads();
+    alpha = a_s;
+    beta = b_s;
+    scratch = tri_lds + 2 * ldy;
   }
   if (threadIdx.x == 0) {
     double lo = INFINITY, hi = -INFINITY, nrm = 0.0, bmax = 0.0;
@@ -453,26 +483,52 @@ __global__ __launch_bounds__(kLzBlock) void k_lz_ritz(const double* __restrict__
 }
 
 // grad[s][slot (i, j)] = sum_t g[s][t] X[s][t][i] X[s][t][j] on every stored
-// slot: the Hellmann-Feynman gradient of sum_t g_t theta_t.
+// slot: the Hellmann-Feynman gradient of sum_t g_t theta_t.  One wave per
+// 64-row tile; its lanes take consecutive slots (coalesced column reads and
+// gradient writes), each slot's row read from a map of the tile's slots to
+// their rows, built in LDS `cap` slots at a time.
 template <typename RP>
-__global__ __launch_bounds__(kBlock) void k_eig_grad(const RP* __restrict__ rowptr,
-                                                     const int32_t* __restrict__ col, int64_t n,
-                                                     int64_t nnz, int64_t k,
-                                                     const double* __restrict__ X,
-                                                     const double* __restrict__ g,
-                                                     double* __restrict__ grad) {
+__global__ __launch_bounds__(kIterBlock) void k_eig_grad(const RP* __restrict__ rowptr,
+                                                         const int32_t* __restrict__ col,
+                                                         int64_t n, int64_t nnz, int64_t tiles,
+                                                         int cap, int64_t k,
+                                                         const double* __restrict__ X,
+                                                         const double* __restrict__ g,
+                                                         double* __restrict__ grad) {
+  extern __shared__ uint8_t slot_rows[];
+  const int wv = wave_index();
+  const int lane = int(lane_id());
+  uint8_t* rowmap = slot_rows + int64_t(wv) * cap;
   const int64_t s = blockIdx.y;
   const double* Xs = X + s * k * n;
   const double* gs = g + s * k;
   double* out = grad + s * nnz;
-  for (int64_t i = int64_t(blockIdx.x) * (kBlock / kWave) + threadIdx.x / kWave; i < n;
-       i += int64_t(gridDim.x) * (kBlock / kWave)) {
-    const int64_t a = rowptr[i], e = rowptr[i + 1];
-    for (int64_t slot = a + lane_id(); slot < e; slot += kWave) {
-      const int64_t j = col[slot];
-      double acc = 0.0;
-      for (int64_t t = 0; t < k; ++t) acc = acc + gs[t] * (Xs[t * n + i] * Xs[t * n + j]);
-      out[slot] = acc;
+  for (int64_t t = int64_t(blockIdx.x) * kWaves + wv; t < tiles;
+       t += int64_t(gridDim.x) * kWaves) {
+    const int64_t r0 = t * kTileRows;
+    const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
+    const int64_t s0 = rowptr[r0];
+    const int64_t len = int64_t(rowptr[r1]) - s0;
+    const int64_t i = r0 + lane;
+    int64_t a = 0, e = 0;
+    if (i < r1) {
+      a = int64_t(rowptr[i]) - s0;
+      e = int64_t(rowptr[i + 1]) - s0;
+    }
+    for (int64_t c0 = 0; c0 < len; c0 += cap) {
+      const int64_t clen = len - c0 < cap ? len - c0 : cap;
+      const int64_t qa = a > c0 ? a : c0, qe = e < c0 + clen ? e : c0 + clen;
+      for (int64_t q = qa; q < qe; ++q) rowmap[q - c0] = uint8_t(lane);
+      wave_sync();
+      for (int64_t q = lane; q < clen; q += kWave) {
+        const int64_t row = r0 + rowmap[q];
+        const int64_t slot = s0 + c0 + q;
+        const int64_t j = col[slot];
+        double acc = 0.0;
+        for (int64_t u = 0; u < k; ++u) acc = acc + gs[u] * (Xs[u * n + row] * Xs[u * n + j]);
+        out[slot] = acc;
+      }
+      wave_sync();
     }
   }
 }
@@ -488,6 +544,8 @@ static int64_t lz_groups(int64_t n) {
   const int64_t rows = int64_t(kLzBlock) * lz_rows_per_thread(n);
   return (n + rows - 1) / rows;
 }
+
+static int64_t lz_dot_chunks(int64_t n);
 
 void release_eig_work(sla_csr A) {
   EigWork* e = A->eig;
@@ -511,7 +569,8 @@ void release_eig_work(sla_csr A) {
 }
 
 static sla_status ensure_eig_work(sla_csr A, int64_t m, int64_t k) {
-  const int64_t n = A->n, G = lz_groups(n);
+  const int64_t n = A->n;
+  const int64_t G = lz_groups(n) > lz_dot_chunks(n) ? lz_groups(n) : lz_dot_chunks(n);
   EigWork* e = A->eig;
   if (e && e->cap_n == n && e->cap_m >= m && e->cap_k >= k && e->cap_g >= G) return SLA_OK;
   release_eig_work(A);
@@ -538,10 +597,15 @@ static sla_status ensure_eig_work(sla_csr A, int64_t m, int64_t k) {
   return SLA_OK;
 }
 
-template <int R>
+static int64_t lz_dot_chunks(int64_t n) { return (n + kLzChunk - 1) / kLzChunk; }
+
 static void lz_launch_dot(EigWork* e, int64_t n, int64_t nvec, const double* w, int with_ww,
-                          int64_t G, hipStream_t st) {
-  k_lz_dot<R><<<unsigned(G), kLzBlock, 0, st>>>(e->V, n, nvec, w, with_ww, e->part, G, e->st);
+                          hipStream_t st) {
+  const int64_t G = lz_dot_chunks(n);
+  const int64_t nblk = (nvec + (with_ww ? 1 : 0) + kLzDotVecs - 1) / kLzDotVecs;
+  const int64_t groups = (G + kXcds - 1) / kXcds * kXcds * nblk;
+  k_lz_dot<<<unsigned(groups), kLzBlock, 0, st>>>(e->V, n, nvec, w, with_ww, e->part, G, nblk,
+                                                  e->st);
 }
 
 template <int R>
@@ -561,8 +625,9 @@ static sla_status lanczos_system(sla_csr A, const double* vals, const double* v0
   const unsigned G2 = unsigned((n + kLzBlock - 1) / kLzBlock);
   const unsigned Gs = G2 < 4096u ? G2 : 4096u;
   k_lz_reset<<<1, 1, 0, st>>>(e->st);
-  lz_launch_dot<R>(e, n, 0, v0, 1, G, st);
-  k_lz_begin<<<1, kLzBlock, 0, st>>>(e->part, G, e->st);
+  const int64_t Gd = lz_dot_chunks(n);
+  lz_launch_dot(e, n, 0, v0, 1, st);
+  k_lz_begin<<<1, kLzBlock, 0, st>>>(e->part, Gd, e->st);
   k_lz_scale<<<Gs, kLzBlock, 0, st>>>(v0, e->V, n, &e->st->norm0, e->st);
   LAUNCH_CHECK();
   constexpr int64_t kPoll = 8;
@@ -573,11 +638,11 @@ static sla_status lanczos_system(sla_csr A, const double* vals, const double* v0
       if (*e->poll_host) break;
     }
     SLA_TRY(launch_spmv(A, vals, 1, e->V + j * n, e->w, st));
-    lz_launch_dot<R>(e, n, j + 1, e->w, 1, G, st);
-    k_lz_reduce<<<unsigned(j + 2), kLzBlock, 0, st>>>(e->part, G, e->h1, e->st);
+    lz_launch_dot(e, n, j + 1, e->w, 1, st);
+    k_lz_reduce<<<unsigned(j + 2), kLzBlock, 0, st>>>(e->part, Gd, e->h1, e->st);
     lz_launch_update<R>(e, n, j + 1, e->h1, nullptr, G, st);
-    lz_launch_dot<R>(e, n, j + 1, e->w, 0, G, st);
-    k_lz_reduce<<<unsigned(j + 1), kLzBlock, 0, st>>>(e->part, G, e->h2, e->st);
+    lz_launch_dot(e, n, j + 1, e->w, 0, st);
+    k_lz_reduce<<<unsigned(j + 1), kLzBlock, 0, st>>>(e->part, Gd, e->h2, e->st);
     lz_launch_update<R>(e, n, j + 1, e->h2, e->pww, G, st);
     k_lz_finish<<<1, kLzBlock, 0, st>>>(e->pww, G, e->h1, e->h2, j, m, e->alpha, e->beta,
                                          e->st);
@@ -590,8 +655,9 @@ static sla_status lanczos_system(sla_csr A, const double* vals, const double* v0
       polled = true;
     }
   }
-  k_tri_eig<<<1, kWave, 0, st>>>(e->alpha, e->beta, k, which, theta, e->Y, m, resid, e->tri,
-                                 e->st);
+  const int tri_lds = m <= kTriLdsMax ? 1 : 0;
+  k_tri_eig<<<1, kWave, tri_lds ? size_t(8) * size_t(m) * sizeof(double) : 0, st>>>(
+      e->alpha, e->beta, k, which, theta, e->Y, m, resid, e->tri, tri_lds, e->st);
   for (int64_t t0 = 0; t0 < k; t0 += kLzRitz)
     k_lz_ritz<kLzRitz><<<G2, kLzBlock, 0, st>>>(e->V, n, e->Y, m, t0, k, X, e->st);
   LAUNCH_CHECK();
@@ -633,17 +699,18 @@ sla_status run_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v
 
 sla_status launch_eig_grad(sla_csr A, int64_t k, const double* X, const double* g,
                            double* grad, hipStream_t st) {
-  const int64_t rows_per_block = kBlock / kWave;
-  int64_t blocks = (A->n + rows_per_block - 1) / rows_per_block;
-  if (blocks > 65536) blocks = 65536;
+  int64_t blocks = (A->tiles + kWaves - 1) / kWaves;
+  if (blocks > 65535) blocks = 65535;
   if (blocks < 1) blocks = 1;
+  const int cap = A->wave_cap;  // >= 1 once the pattern is analysed
   const dim3 grid(unsigned(blocks), unsigned(A->batch));
+  const size_t lds = size_t(kWaves) * size_t(cap);
   if (A->rp_idx == SLA_I32)
-    k_eig_grad<int32_t><<<grid, kBlock, 0, st>>>((const int32_t*)A->rowptr, A->col, A->n,
-                                                  A->nnz, k, X, g, grad);
+    k_eig_grad<int32_t><<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->n,
+                                                        A->nnz, A->tiles, cap, k, X, g, grad);
   else
-    k_eig_grad<int64_t><<<grid, kBlock, 0, st>>>((const int64_t*)A->rowptr, A->col, A->n,
-                                                  A->nnz, k, X, g, grad);
+    k_eig_grad<int64_t><<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->n,
+                                                        A->nnz, A->tiles, cap, k, X, g, grad);
   LAUNCH_CHECK();
   return SLA_OK;
 }

@@ -115,6 +115,7 @@ def test_poisson_closed_form():
     (3000, 3, 5, "SA", 120, 2),
     (700, 4, 3, "LA", 700, 3),     # to the end of the Krylov space
     (97, 2, 1, "SA", 40, 4),       # one partial tile
+    (1200, 3, 2, "LA", 1000, 5),   # a tridiagonal too large for LDS
 ])
 def test_random_symmetric(n, per_row, k, which, m, seed):
     rp, c, v = _sym_csr(n, per_row, seed, empty_diag_rows={0, n // 2})
