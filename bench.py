@@ -104,6 +104,14 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def lanczos_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("lanczos.hip", "common.h"):
+        with open(os.path.join(ROOT, "krylov_solvers_adjoint_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profile(kernel: str, workload: str, digest: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
@@ -397,6 +405,17 @@ def bench_eigsh(m: int, k: int):
     nbytes = lanczos_bytes(n, steps, k, spmv_bytes("banded" if P.banded else "csr", n, P.nnz, 4))
     grad_ms = _event_ms(lambda: K.sla_eig_grad(P, v, X, torch.ones(k, dtype=torch.float64,
                                                                    device=dev)), 10)
+    # the Gram-Schmidt passes at the mean basis size of the run (step j
+    # passes over j + 1 vectors): timed live with HIP events on the stream
+    # they run on
+    nvec = max(1, (steps + 1) // 2)
+    gs = K.sla_profile_lanczos_kernels(P, nvec, reps=10)
+    dot_bytes = 8 * n * (nvec + 1)        # nvec basis vectors and w read once
+    upd_bytes = 8 * n * (nvec + 2)        # nvec basis vectors and w read, w written
+    gs_roof = dict(nvec=nvec, dot_ms=gs["dot"], update_ms=gs["update"],
+                   dot_GBps=dot_bytes / (gs["dot"] * 1e-3) / 1e9,
+                   update_GBps=upd_bytes / (gs["update"] * 1e-3) / 1e9,
+                   dot_bytes=dot_bytes, update_bytes=upd_bytes)
     out = dict(n=n, nnz=P.nnz, k=k, m=m, steps=steps, ms=1e3 * wall,
                steps_per_s=steps / wall, eff_GBps=nbytes / wall / 1e9,
                algorithmic_bytes=nbytes, basis_MB=(free0 - free1) / 2**20,
@@ -404,6 +423,12 @@ def bench_eigsh(m: int, k: int):
                # largest eigenvalue of the 5-point Laplacian, 4 + 4 cos(pi / (N + 1))
                theta_top_exact=4.0 + 4.0 * float(np.cos(np.pi / (N + 1))),
                eig_grad_ms=grad_ms)
+    out["roofline"] = dict(
+        bound="hbm", kernel="k_lz_dot (Gram-Schmidt dot pass)",
+        achieved=gs_roof["dot_GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
+        frac=gs_roof["dot_GBps"] / HBM_PEAK_GBPS,
+        traffic=traffic_from_profile("k_lz_dot", "poisson1000_m300", lanczos_digest()),
+        **{k_: v_ for k_, v_ in gs_roof.items()})
     del P, v, v0, th, X, res
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -288,6 +288,18 @@ sla_status sla_eig_grad(sla_csr A, int64_t k, const double* X, const double* gra
                         double* grad_vals, hipStream_t stream);
 
 /*
+ * Measurement aid for sla_eigsh: after an sla_eigsh call on this handle with
+ * m >= nvec, launch the Gram-Schmidt dot pass (V_nvec^T w plus w.w) and the
+ * update pass (w -= V_nvec h) over the first nvec basis vectors `reps`
+ * times each on `stream` and return their mean durations in milliseconds:
+ * avg_ms_host[0] dot, [1] update.  The Lanczos workspace holds meaningless
+ * values afterwards (earlier results in the caller's buffers are not
+ * touched).  SLA_ERR_ARG without such a call.  Synchronises `stream`.
+ */
+sla_status sla_profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps,
+                                      double* avg_ms_host, hipStream_t stream);
+
+/*
  * SpMV kernel family.  At creation the pattern analysis checks whether every
  * stored column j of every row i equals i + d for one of at most 8 fixed
  * offsets d (a banded or stencil pattern such as the 5-point Laplacian); if

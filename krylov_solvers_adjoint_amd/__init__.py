@@ -46,7 +46,7 @@ EXPORTS = [
     "sla_cg_history", "sla_profile_iteration_kernels", "sla_csr_set_spmv_variant",
     "sla_csr_set_graph_block",
     "sla_csr_set_workgroups_per_cu", "sla_spmv_transpose", "sla_matvec_grad",
-    "sla_eigsh", "sla_eig_grad",
+    "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -99,6 +99,7 @@ def _bind(lib):
         "sla_matvec_grad": [_P, _P, _P, _P, _P, _P],
         "sla_eigsh": [_P, _I64, _S, _I64, _P, _P, _P, _P, _P, _P],
         "sla_eig_grad": [_P, _I64, _P, _P, _P, _P],
+        "sla_profile_lanczos_kernels": [_P, _I64, _I64, _P, _P],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
@@ -406,6 +407,16 @@ def sla_eig_grad(A: CSRPattern, values: torch.Tensor, X: torch.Tensor, grad_thet
                              _dev(grad_theta, torch.float64, "grad_theta"), gv.data_ptr(),
                              _stream(stream)))
     return gv
+
+
+def sla_profile_lanczos_kernels(A: CSRPattern, nvec: int, reps: int = 10, stream=None) -> dict:
+    """Mean ms of the Gram-Schmidt dot and update passes over nvec basis
+    vectors (after an sla_eigsh call on A with m >= nvec)."""
+    import numpy as np
+    out = np.zeros(2, np.float64)
+    _check(_lib.sla_profile_lanczos_kernels(A.handle, int(nvec), int(reps), out.ctypes.data,
+                                            _stream(stream)))
+    return dict(zip(("dot", "update"), out.tolist()))
 
 
 def _solve_call(fn, A, b, x, tol, maxit, flags, batch, stream, check):

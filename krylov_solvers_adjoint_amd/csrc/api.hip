@@ -445,6 +445,17 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x, 
   API_END
 }
 
+sla_status sla_profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps,
+                                      double* avg_ms_host, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_profile_lanczos_kernels: NULL handle");
+  REQUIRE(avg_ms_host != nullptr, "sla_profile_lanczos_kernels: NULL pointer");
+  REQUIRE(reps >= 1 && reps <= 100000, "sla_profile_lanczos_kernels: reps out of range");
+  return profile_lanczos_kernels(A, nvec, reps, avg_ms_host, stream);
+  API_END
+}
+
 sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels) {
   API_BEGIN
   clear_error();

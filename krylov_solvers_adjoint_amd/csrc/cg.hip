@@ -1024,7 +1024,10 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
   const SLA_GLOBAL double* l = gmem(lambda + s * n);
   const SLA_GLOBAL double* xs = gmem(x + s * n);
   SLA_GLOBAL double* gs = gmem(grad + s * nnz);
-  for (int64_t t = int64_t(blockIdx.x) * kWaves + w; t < tiles; t += int64_t(gridDim.x) * kWaves) {
+  // contiguous tile ranges per XCD (the grid is a multiple of kXcds): tiles
+  // that gather the same entries of x run close together on one L2
+  const TileWalk walk = wave_walk(tiles, int(gridDim.x), int(blockIdx.x), kWaves, w);
+  for (int64_t t = walk.first; t < walk.end; t += walk.stride) {
     const int64_t r0 = t * kTileRows;
     const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
     const int64_t s0 = rowptr[r0];
@@ -1346,7 +1349,8 @@ sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const doubl
 
 sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const double* x,
                                 double* out, bool negate, hipStream_t st) {
-  const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
+  const unsigned per_xcd = std::max(1u, plain_grid(A->tiles, batch) / unsigned(kXcds));
+  const dim3 grid(per_xcd * kXcds, unsigned(batch));
   const int cap = A->wave_cap;
   const size_t lds = size_t(kWaves) * size_t(cap);
   if (A->rp_idx == SLA_I32) {

@@ -697,7 +697,11 @@ __global__ __launch_bounds__(kIterBlock) void k_spmv_transpose(
   const double* v = vals + s * nnz;
   const double* xs = x + s * n;
   double* ys = y + s * n;
-  for (int64_t t = int64_t(blockIdx.x) * kW + wv; t < tiles; t += int64_t(gridDim.x) * kW) {
+  // each XCD walks a contiguous range of tiles, so the tiles that read the
+  // same lines of A's values (rows i and i +- the band's reach) run close
+  // together in time on one L2
+  const TileWalk walk = wave_walk(tiles, int(gridDim.x), int(blockIdx.x), kW, wv);
+  for (int64_t t = walk.first; t < walk.end; t += walk.stride) {
     const int64_t r0 = t * kTileRows;
     const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
     const int64_t s0 = rowptr_t[r0];
@@ -840,8 +844,10 @@ sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStrea
   // the transposed pattern was built from one COO triplet per slot of A, in
   // slot order: the triplet of each of its slots is the slot of A
   constexpr int64_t kW = kIterBlock / kWave;
-  int64_t blocks = (T->tiles + kW - 1) / kW;
-  blocks = blocks < 1 ? 1 : (blocks > 65535 ? 65535 : blocks);
+  // a multiple of kXcds workgroups (the tile walk splits the tiles by XCD)
+  int64_t per_xcd = (T->tiles + kW * kXcds - 1) / (kW * kXcds);
+  per_xcd = per_xcd < 1 ? 1 : (per_xcd > 8191 ? 8191 : per_xcd);
+  const int64_t blocks = per_xcd * kXcds;
   const int cap = T->wave_cap;  // >= 1 once the pattern is analysed
   const dim3 g(unsigned(blocks), unsigned(A->batch));
   const size_t lds = size_t(kW) * size_t(cap) * sizeof(double);

@@ -114,6 +114,10 @@ sla_status run_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v
 sla_status launch_eig_grad(sla_csr A, int64_t k, const double* X, const double* g,
                            double* grad, hipStream_t stream);
 void release_eig_work(sla_csr A);
+// mean durations of the Gram-Schmidt dot and update passes over nvec basis
+// vectors, on the basis an earlier eigsh left in the workspace
+sla_status profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps, double* avg_ms,
+                                   hipStream_t stream);
 sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps,
                            double* avg_ms, hipStream_t stream);
 

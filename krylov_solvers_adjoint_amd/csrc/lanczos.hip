@@ -503,8 +503,10 @@ __global__ __launch_bounds__(kIterBlock) void k_eig_grad(const RP* __restrict__ 
   const double* Xs = X + s * k * n;
   const double* gs = g + s * k;
   double* out = grad + s * nnz;
-  for (int64_t t = int64_t(blockIdx.x) * kWaves + wv; t < tiles;
-       t += int64_t(gridDim.x) * kWaves) {
+  // contiguous tile ranges per XCD: the tiles that gather the same entries
+  // of X run close together on one L2
+  const TileWalk walk = wave_walk(tiles, int(gridDim.x), int(blockIdx.x), kWaves, wv);
+  for (int64_t t = walk.first; t < walk.end; t += walk.stride) {
     const int64_t r0 = t * kTileRows;
     const int64_t r1 = r0 + kTileRows < n ? r0 + kTileRows : n;
     const int64_t s0 = rowptr[r0];
@@ -697,11 +699,45 @@ sla_status run_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v
   return first;
 }
 
+sla_status profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps, double* avg_ms,
+                                   hipStream_t st) {
+  EigWork* e = A->eig;
+  if (e == nullptr || nvec < 1 || nvec > e->cap_m) {
+    set_error("sla_profile_lanczos_kernels: needs an earlier sla_eigsh with m >= nvec = %lld",
+              (long long)nvec);
+    return SLA_ERR_ARG;
+  }
+  const int64_t n = A->n, G = lz_groups(n);
+  // the kernels return at once once the process has stopped: clear the flag
+  k_lz_reset<<<1, 1, 0, st>>>(e->st);
+  LAUNCH_CHECK();
+  hipEvent_t ev[4];
+  for (auto& x : ev) SLA_TRY_HIP(hipEventCreate(&x));
+  SLA_TRY_HIP(hipEventRecord(ev[0], st));
+  for (int64_t r = 0; r < reps; ++r) lz_launch_dot(e, n, nvec, e->w, 1, st);
+  SLA_TRY_HIP(hipEventRecord(ev[1], st));
+  for (int64_t r = 0; r < reps; ++r) {
+    if (lz_rows_per_thread(n) == 4) lz_launch_update<4>(e, n, nvec, e->h1, nullptr, G, st);
+    else lz_launch_update<1>(e, n, nvec, e->h1, nullptr, G, st);
+  }
+  SLA_TRY_HIP(hipEventRecord(ev[2], st));
+  LAUNCH_CHECK();
+  SLA_TRY_HIP(hipEventSynchronize(ev[2]));
+  float t0 = 0.f, t1 = 0.f;
+  SLA_TRY_HIP(hipEventElapsedTime(&t0, ev[0], ev[1]));
+  SLA_TRY_HIP(hipEventElapsedTime(&t1, ev[1], ev[2]));
+  for (auto& x : ev) (void)hipEventDestroy(x);
+  avg_ms[0] = double(t0) / double(reps);
+  avg_ms[1] = double(t1) / double(reps);
+  return SLA_OK;
+}
+
 sla_status launch_eig_grad(sla_csr A, int64_t k, const double* X, const double* g,
                            double* grad, hipStream_t st) {
-  int64_t blocks = (A->tiles + kWaves - 1) / kWaves;
-  if (blocks > 65535) blocks = 65535;
-  if (blocks < 1) blocks = 1;
+  // a multiple of kXcds workgroups (the tile walk splits the tiles by XCD)
+  int64_t per_xcd = (A->tiles + int64_t(kWaves) * kXcds - 1) / (int64_t(kWaves) * kXcds);
+  per_xcd = per_xcd < 1 ? 1 : (per_xcd > 8191 ? 8191 : per_xcd);
+  const int64_t blocks = per_xcd * kXcds;
   const int cap = A->wave_cap;  // >= 1 once the pattern is analysed
   const dim3 grid(unsigned(blocks), unsigned(A->batch));
   const size_t lds = size_t(kWaves) * size_t(cap);
