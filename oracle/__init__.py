@@ -31,6 +31,7 @@ ERR_CSR = 2
 ERR_NOT_SPD = 5
 ERR_NONFINITE = 6
 ERR_NOT_SYMMETRIC = 7
+ERR_BREAKDOWN = 8
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
@@ -97,6 +98,12 @@ def _bind(lib):
     lib.oracle_lanczos.argtypes = [_I64, _P, _P, _P, _P, _I64, _P, _P, _P]
     lib.oracle_eig_grad.restype = None
     lib.oracle_eig_grad.argtypes = [_I64, _P, _P, _P, _P]
+    lib.oracle_bicgstab.restype = ctypes.c_int
+    lib.oracle_bicgstab.argtypes = [_I64, _P, _P, _P, _P, _P, _D, _I64, ctypes.c_int,
+                                    ctypes.POINTER(_Info), _P, _P, _P, _P]
+    lib.oracle_adjoint_bicgstab.restype = ctypes.c_int
+    lib.oracle_adjoint_bicgstab.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P, _D, _I64,
+                                            ctypes.POINTER(_Info)]
     lib.oracle_set_threads.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
@@ -243,6 +250,42 @@ def adjoint(A: CSR, x, g, tol: float, maxit: int, lib=None):
     st = L.oracle_adjoint(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
                           _ptr(_c(A.vals, np.float64)), _ptr(x), _ptr(g), _ptr(gb),
                           _ptr(gv), float(tol), int(maxit), ctypes.byref(info))
+    return gb, gv[:A.nnz].copy(), CGInfo(int(st), int(info.iterations), float(info.rr),
+                                         float(info.bb), bool(info.converged))
+
+
+def bicgstab(A: CSR, b, tol: float, maxit: int, x0=None, history: bool = False, lib=None):
+    """BiCGStab for a general A: x, CGInfo[, (rho, alpha, omega, rr) history]."""
+    L = lib or _load()
+    b = _c(b, np.float64)
+    x = _c(x0, np.float64).copy() if x0 is not None else np.zeros(A.n, np.float64)
+    info = _Info()
+    hs = [None] * 4
+    if history:
+        hs = [np.zeros(max(maxit, 1)) for _ in range(4)]
+    st = L.oracle_bicgstab(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                           _ptr(_c(A.vals, np.float64)), _ptr(b), _ptr(x), float(tol),
+                           int(maxit), 1 if x0 is not None else 0, ctypes.byref(info),
+                           *[_ptr(h) for h in hs])
+    out = CGInfo(int(st), int(info.iterations), float(info.rr), float(info.bb),
+                 bool(info.converged))
+    if history:
+        k = out.iterations
+        return x, out, tuple(h[:k].copy() for h in hs)
+    return x, out
+
+
+def adjoint_bicgstab(A: CSR, x, g, tol: float, maxit: int, lib=None):
+    """(grad_b = lambda solving A^T lambda = g by BiCGStab, grad_vals, CGInfo)."""
+    L = lib or _load()
+    x = _c(x, np.float64)
+    g = _c(g, np.float64)
+    gb = np.zeros(A.n, np.float64)
+    gv = np.zeros(max(A.nnz, 1), np.float64)
+    info = _Info()
+    st = L.oracle_adjoint_bicgstab(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                                   _ptr(_c(A.vals, np.float64)), _ptr(x), _ptr(g), _ptr(gb),
+                                   _ptr(gv), float(tol), int(maxit), ctypes.byref(info))
     return gb, gv[:A.nnz].copy(), CGInfo(int(st), int(info.iterations), float(info.rr),
                                          float(info.bb), bool(info.converged))
 

@@ -50,6 +50,7 @@
 #define ORACLE_ERR_NOT_SPD 5
 #define ORACLE_ERR_NONFINITE 6
 #define ORACLE_ERR_NOT_SYMMETRIC 7
+#define ORACLE_ERR_BREAKDOWN 8
 
 #define DOT_BLOCK 4096
 
@@ -550,6 +551,143 @@ void oracle_eig_grad(int64_t n, const int64_t* rowptr, const int32_t* col, const
                      double* grad_vals) {
   for (int64_t i = 0; i < n; ++i)
     for (int64_t k = rowptr[i]; k < rowptr[i + 1]; ++k) grad_vals[k] = v[i] * v[col[k]];
+}
+
+/* ------------------------------------------------------------------------ */
+/* BiCGStab (a CPU backend solver of Methodology 1) and its adjoint          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Solve A x = b for a general (non-symmetric) A by BiCGStab (van der Vorst),
+ * without preconditioner.  The pages name the solver (SciPy and Eigen CPU
+ * backends) but not its variant; the reading taken is the textbook one:
+ *   r = b - A x0 (x0 = 0 unless use_x0), rhat = r, p = v = 0,
+ *   rho_prev = alpha = omega = 1;  each iteration:
+ *     rho = rhat . r                       (zero: breakdown)
+ *     beta = (rho / rho_prev) (alpha / omega)
+ *     p = r + beta (p - omega v)
+ *     v = A p ; alpha = rho / (rhat . v)   (rhat . v zero: breakdown)
+ *     s = r - alpha v
+ *     if s . s <= tol^2 b . b: x = x + alpha p, done (a counted iteration)
+ *     t = A s ; omega = (t . s) / (t . t)  (t . t or omega zero: breakdown)
+ *     x = (x + alpha p) + omega s ; r = s - omega t
+ * and it stops, as CG, when the recursive residual satisfies
+ * r . r <= tol^2 b . b before an iteration, or after maxit iterations.
+ * Returns ORACLE_OK (converged or not), ORACLE_ERR_BREAKDOWN or
+ * ORACLE_ERR_NONFINITE; x holds the last iterate.  hist_* (may be NULL,
+ * length >= maxit): rho, alpha, omega and the residual norm squared after
+ * each iteration (s . s and omega = 0 for a half-step finish).
+ */
+int oracle_bicgstab(int64_t n, const int64_t* rowptr, const int32_t* col,
+                    const double* vals, const double* b, double* x, double tol,
+                    int64_t maxit, int use_x0, oracle_cg_info* info, double* hist_rho,
+                    double* hist_alpha, double* hist_omega, double* hist_rr) {
+  size_t bytes = sizeof(double) * (size_t)(n > 0 ? n : 1);
+  double* r = (double*)malloc(bytes);
+  double* rh = (double*)malloc(bytes);
+  double* p = (double*)malloc(bytes);
+  double* v = (double*)malloc(bytes);
+  double* sv = (double*)malloc(bytes);
+  double* t = (double*)malloc(bytes);
+  int status = ORACLE_OK;
+  if (use_x0) {
+    oracle_spmv(n, rowptr, col, vals, x, v);
+    for (int64_t i = 0; i < n; ++i) r[i] = b[i] - v[i];
+  } else {
+    for (int64_t i = 0; i < n; ++i) {
+      x[i] = 0.0;
+      r[i] = b[i];
+    }
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    rh[i] = r[i];
+    p[i] = 0.0;
+    v[i] = 0.0;
+  }
+  double bb = oracle_dot(n, b, b);
+  double rr = oracle_dot(n, r, r);
+  double stop = (tol * tol) * bb;
+  double rho_prev = 1.0, alpha = 1.0, omega = 1.0;
+  int64_t k = 0;
+  int done = 0;
+  if (!isfinite(bb) || !isfinite(rr)) status = ORACLE_ERR_NONFINITE;
+  while (status == ORACLE_OK && !done && k < maxit && rr > stop) {
+    double rho = oracle_dot(n, rh, r);
+    if (!isfinite(rho)) { status = ORACLE_ERR_NONFINITE; break; }
+    if (rho == 0.0) { status = ORACLE_ERR_BREAKDOWN; break; }
+    double beta = (rho / rho_prev) * (alpha / omega);
+    for (int64_t i = 0; i < n; ++i) p[i] = r[i] + beta * (p[i] - omega * v[i]);
+    oracle_spmv(n, rowptr, col, vals, p, v);
+    double rv = oracle_dot(n, rh, v);
+    if (!isfinite(rv)) { status = ORACLE_ERR_NONFINITE; break; }
+    if (rv == 0.0) { status = ORACLE_ERR_BREAKDOWN; break; }
+    alpha = rho / rv;
+    for (int64_t i = 0; i < n; ++i) sv[i] = r[i] - alpha * v[i];
+    double ss = oracle_dot(n, sv, sv);
+    if (!isfinite(ss)) { status = ORACLE_ERR_NONFINITE; break; }
+    if (hist_rho) hist_rho[k] = rho;
+    if (hist_alpha) hist_alpha[k] = alpha;
+    if (ss <= stop) {
+      for (int64_t i = 0; i < n; ++i) x[i] = x[i] + alpha * p[i];
+      if (hist_omega) hist_omega[k] = 0.0;
+      if (hist_rr) hist_rr[k] = ss;
+      rr = ss;
+      k = k + 1;
+      done = 1;
+      break;
+    }
+    oracle_spmv(n, rowptr, col, vals, sv, t);
+    double tt = oracle_dot(n, t, t);
+    double ts = oracle_dot(n, t, sv);
+    if (!isfinite(tt) || !isfinite(ts)) { status = ORACLE_ERR_NONFINITE; break; }
+    if (tt == 0.0) { status = ORACLE_ERR_BREAKDOWN; break; }
+    omega = ts / tt;
+    for (int64_t i = 0; i < n; ++i) {
+      x[i] = (x[i] + alpha * p[i]) + omega * sv[i];
+      r[i] = sv[i] - omega * t[i];
+    }
+    rr = oracle_dot(n, r, r);
+    if (hist_omega) hist_omega[k] = omega;
+    if (hist_rr) hist_rr[k] = rr;
+    k = k + 1;
+    if (!isfinite(rr)) { status = ORACLE_ERR_NONFINITE; break; }
+    if (omega == 0.0) { status = ORACLE_ERR_BREAKDOWN; break; }
+    rho_prev = rho;
+  }
+  info->iterations = k;
+  info->rr = rr;
+  info->bb = bb;
+  info->converged = (status == ORACLE_OK && rr <= stop) ? 1 : 0;
+  free(r);
+  free(rh);
+  free(p);
+  free(v);
+  free(sv);
+  free(t);
+  return status;
+}
+
+/*
+ * Backward pass of x = A^{-1} b (Methodology 2, linear systems) for a
+ * general A: A^T lambda = g solved by the same BiCGStab on an explicit A^T;
+ * grad_b = lambda, grad_vals[k] = -lambda_i x_j on the stored slots.
+ */
+int oracle_adjoint_bicgstab(int64_t n, const int64_t* rowptr, const int32_t* col,
+                            const double* vals, const double* x, const double* g,
+                            double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                            oracle_cg_info* info) {
+  int64_t nnz = rowptr[n];
+  int64_t* rowptr_t = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int32_t* col_t = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+  double* vals_t = (double*)malloc(sizeof(double) * (size_t)(nnz > 0 ? nnz : 1));
+  oracle_transpose(n, rowptr, col, vals, rowptr_t, col_t, vals_t);
+  int status = oracle_bicgstab(n, rowptr_t, col_t, vals_t, g, grad_b, tol, maxit, 0, info,
+                               NULL, NULL, NULL, NULL);
+  oracle_pattern_grad(n, rowptr, col, grad_b, x, grad_vals);
+  free(rowptr_t);
+  free(col_t);
+  free(vals_t);
+  return status;
 }
 
 /* ------------------------------------------------------------------------ */

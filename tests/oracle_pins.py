@@ -719,6 +719,139 @@ def pin_eig_grad(lib=None):
         assert abs(fd - gv[k]) <= 1e-6, (k, fd, gv[k])
 
 
+# --------------------------------------------------------------------------
+# BiCGStab and its adjoint
+# --------------------------------------------------------------------------
+
+def _csr_of(M):
+    rows, cols = np.nonzero(M)
+    rp = np.zeros(M.shape[0] + 1, np.int64)
+    np.add.at(rp, rows + 1, 1)
+    return oracle.CSR(M.shape[0], np.cumsum(rp), cols.astype(np.int32), M[rows, cols].copy())
+
+
+def _convection_diffusion(N, eps=0.05):
+    """2D upwind convection-diffusion on an N x N grid (flow along the grid
+    lines): a non-symmetric M-matrix, dense for the LU check."""
+    h = 1.0 / (N + 1)
+    n = N * N
+    M = np.zeros((n, n))
+    for c in range(N):
+        for a in range(N):
+            i = c * N + a
+            M[i, i] = 4 * eps / h ** 2 + 1 / h
+            if a > 0:
+                M[i, i - 1] = -eps / h ** 2 - 1 / h
+            if a + 1 < N:
+                M[i, i + 1] = -eps / h ** 2
+            if c > 0:
+                M[i, i - N] = -eps / h ** 2
+            if c + 1 < N:
+                M[i, i + N] = -eps / h ** 2
+    return M
+
+
+def pin_bicgstab_dense_lu(lib=None):
+    """Converged BiCGStab against dense LU: convection-diffusion, a random
+    non-symmetric diagonally dominant matrix, and the SPD Poisson matrix;
+    the recursive residual agrees with the true residual b - A x."""
+    rng = np.random.default_rng(80)
+    R = np.where(rng.random((60, 60)) < 0.1, rng.uniform(-1, 1, (60, 60)), 0.0)
+    R += np.diag(np.abs(R).sum(axis=1) + 1.0)
+    cases = [_convection_diffusion(12), R, _poisson(10).to_dense()]
+    for M in cases:
+        A = _csr_of(M)
+        b = rng.standard_normal(A.n)
+        x, info = oracle.bicgstab(A, b, 1e-12, 2000, lib=lib)
+        assert info.status == oracle.OK and info.converged, info
+        xe = np.linalg.solve(M, b)
+        assert np.linalg.norm(x - xe) <= 1e-9 * np.linalg.norm(xe)
+        true = np.linalg.norm(b - M @ x) ** 2
+        assert abs(true - info.rr) <= 1e-6 * max(true, info.rr) + 1e-26 * info.bb
+
+
+def pin_bicgstab_scaling(lib=None):
+    """(2A) x = b: rho is unchanged, alpha and omega halve, x halves -- all
+    exactly, since every step only rescales by powers of two."""
+    M = _convection_diffusion(9)
+    A = _csr_of(M)
+    A2 = oracle.CSR(A.n, A.rowptr, A.col, 2.0 * A.vals)
+    b = W.uniform_rhs(A.n, 4)
+    x1, i1, h1 = oracle.bicgstab(A, b, 1e-10, 500, history=True, lib=lib)
+    x2, i2, h2 = oracle.bicgstab(A2, b, 1e-10, 500, history=True, lib=lib)
+    assert i1.iterations == i2.iterations and i1.iterations > 3
+    assert np.array_equal(x2, 0.5 * x1)
+    assert np.array_equal(h2[0], h1[0])
+    assert np.array_equal(h2[1], 0.5 * h1[1])
+    assert np.array_equal(h2[2], 0.5 * h1[2])
+    assert np.array_equal(h2[3], h1[3])
+
+
+def pin_bicgstab_finite_termination(lib=None):
+    """BiCG terminates in n steps, so for n = 2 and 3 BiCGStab's s vanishes
+    (to rounding) in iteration n and it finishes there, on the half step,
+    with the LU solution; for A = 2 I it finishes in iteration 1 with x = b/2
+    exactly."""
+    rng = np.random.default_rng(81)
+    for n in (2, 3):
+        for _ in range(5):
+            M = rng.uniform(-1, 1, (n, n)) + 3 * np.eye(n)
+            A = _csr_of(M)
+            b = rng.standard_normal(n)
+            x, info, h = oracle.bicgstab(A, b, 1e-10, 10, history=True, lib=lib)
+            assert info.converged and info.iterations <= n, (n, info)
+            assert h[2][info.iterations - 1] == 0.0   # ended on the half step
+            assert np.allclose(x, np.linalg.solve(M, b), rtol=1e-12, atol=1e-14)
+    A = _csr_of(2.0 * np.eye(7))
+    b = W.uniform_rhs(7, 5)
+    x, info = oracle.bicgstab(A, b, 1e-10, 10, lib=lib)
+    assert info.iterations == 1 and np.array_equal(x, 0.5 * b)
+
+
+def pin_bicgstab_statuses(lib=None):
+    """b = 0: converged in 0 iterations with x = 0; a skew-symmetric rotation
+    gives rhat . v = 0 at once (breakdown); a NaN value is non-finite; tol = 0
+    runs exactly maxit iterations."""
+    A = _csr_of(_convection_diffusion(5))
+    x, info = oracle.bicgstab(A, np.zeros(A.n), 1e-8, 50, lib=lib)
+    assert info.status == oracle.OK and info.iterations == 0 and not np.any(x)
+    R = _csr_of(np.array([[0.0, 1.0], [-1.0, 0.0]]))
+    x, info = oracle.bicgstab(R, np.array([1.0, 0.0]), 1e-8, 50, lib=lib)
+    assert info.status == oracle.ERR_BREAKDOWN and info.iterations == 0
+    Bad = oracle.CSR(A.n, A.rowptr, A.col, A.vals.copy())
+    Bad.vals[4] = np.nan
+    _, info = oracle.bicgstab(Bad, W.uniform_rhs(A.n, 6), 1e-8, 50, lib=lib)
+    assert info.status == oracle.ERR_NONFINITE
+    _, info = oracle.bicgstab(A, W.uniform_rhs(A.n, 6), 0.0, 7, lib=lib)
+    assert info.status == oracle.OK and info.iterations == 7
+
+
+def pin_adjoint_bicgstab(lib=None):
+    """A^T lambda = g by BiCGStab on a non-symmetric matrix: lambda against
+    LU of A^T; g.x = lambda.b; sum vals.grad = -lambda.b; central
+    differences of L = g.x over stored slots (perturbed systems by LU)."""
+    M = _convection_diffusion(7)
+    A = _csr_of(M)
+    rng = np.random.default_rng(82)
+    b = rng.standard_normal(A.n)
+    g = rng.standard_normal(A.n)
+    x, info = oracle.bicgstab(A, b, 1e-13, 2000, lib=lib)
+    lam, gv, ainfo = oracle.adjoint_bicgstab(A, x, g, 1e-13, 2000, lib=lib)
+    assert ainfo.status == oracle.OK and ainfo.converged
+    le = np.linalg.solve(M.T, g)
+    assert np.linalg.norm(lam - le) <= 1e-9 * np.linalg.norm(le)
+    assert abs(g @ x - lam @ b) <= 1e-9 * abs(g @ x)
+    assert abs(A.vals @ gv + lam @ b) <= 1e-9 * abs(lam @ b)
+    rows = np.repeat(np.arange(A.n), np.diff(A.rowptr))
+    for k in range(0, A.nnz, 11):
+        d = 1e-6
+        Mp, Mm = M.copy(), M.copy()
+        Mp[rows[k], A.col[k]] += d
+        Mm[rows[k], A.col[k]] -= d
+        fd = (g @ np.linalg.solve(Mp, b) - g @ np.linalg.solve(Mm, b)) / (2 * d)
+        assert abs(fd - gv[k]) <= 1e-6 * max(1.0, abs(fd)), (k, fd, gv[k])
+
+
 ALL_PINS = [
     pin_csr_poisson_closed_form, pin_csr_brute_force, pin_csr_rgg_symmetric,
     pin_spmv_eigenpairs, pin_spmv_dense, pin_dot,
@@ -729,4 +862,6 @@ ALL_PINS = [
     pin_pcg_uniform_diagonal, pin_pcg_scaled_equivalence, pin_pcg_diagonal_one_step,
     pin_pcg_dense_lu, pin_pcg_statuses, pin_adjoint_jacobi, pin_matvec_grad,
     pin_eigsh_poisson, pin_eigsh_dense, pin_eig_grad,
+    pin_bicgstab_dense_lu, pin_bicgstab_scaling, pin_bicgstab_finite_termination,
+    pin_bicgstab_statuses, pin_adjoint_bicgstab,
 ]

@@ -21,7 +21,8 @@ MUTATIONS = {
     "beta_inverted": ("double beta = rr_new / rr;", "double beta = rr / rr_new;"),
     "alpha_inverted": ("double alpha = rr / pq;", "double alpha = pq / rr;"),
     "residual_sign": ("r[i] = r[i] - alpha * q[i];", "r[i] = r[i] + alpha * q[i];"),
-    "x_uses_q": ("x[i] = x[i] + alpha * p[i];", "x[i] = x[i] + alpha * q[i];"),
+    "x_uses_q": ("x[i] = x[i] + alpha * p[i];\n        r[i] = r[i] - alpha * q[i];",
+                 "x[i] = x[i] + alpha * q[i];\n        r[i] = r[i] - alpha * q[i];"),
     "p_drops_old_p": ("p[i] = r[i] + beta * p[i];", "p[i] = r[i] + beta * r[i];"),
     "dot_drops_last_block": ("for (int64_t b = 0; b < nb; ++b) total = total + part[b];",
                              "for (int64_t b = 0; b + 1 < nb; ++b) total = total + part[b];"),
@@ -48,6 +49,21 @@ MUTATIONS = {
     "lanczos_alpha_second_pass_only": ("a = a + h[j];", "a = h[j];"),
     "lanczos_beta_squared": ("double b = sqrt(oracle_dot(n, w, w));", "double b = oracle_dot(n, w, w);"),
     "eig_grad_diagonal_only": ("grad_vals[k] = v[i] * v[col[k]];", "grad_vals[k] = v[i] * v[i];"),
+    "bicgstab_p_sign": ("p[i] = r[i] + beta * (p[i] - omega * v[i]);",
+                        "p[i] = r[i] + beta * (p[i] + omega * v[i]);"),
+    "bicgstab_omega_inverted": ("omega = ts / tt;", "omega = tt / ts;"),
+    "bicgstab_beta_swapped": ("double beta = (rho / rho_prev) * (alpha / omega);",
+                              "double beta = (rho / rho_prev) * (omega / alpha);"),
+    "bicgstab_x_drops_omega_s": ("x[i] = (x[i] + alpha * p[i]) + omega * sv[i];",
+                                 "x[i] = x[i] + alpha * p[i];"),
+    "bicgstab_r_sign": ("r[i] = sv[i] - omega * t[i];", "r[i] = sv[i] + omega * t[i];"),
+    "bicgstab_s_uses_p": ("sv[i] = r[i] - alpha * v[i];", "sv[i] = r[i] - alpha * p[i];"),
+    "bicgstab_rho_prev_stale": ("    rho_prev = rho;\n  }\n  info->iterations = k;",
+                                "  }\n  info->iterations = k;"),
+    "bicgstab_half_step_no_x": ("      for (int64_t i = 0; i < n; ++i) x[i] = x[i] + alpha * p[i];\n      if (hist_omega) hist_omega[k] = 0.0;",
+                                "      if (hist_omega) hist_omega[k] = 0.0;"),
+    "bicgstab_adjoint_on_A": ("  int status = oracle_bicgstab(n, rowptr_t, col_t, vals_t, g, grad_b,",
+                              "  int status = oracle_bicgstab(n, rowptr, col, vals, g, grad_b,"),
 }
 
 CHILD = r"""
