@@ -48,8 +48,9 @@ typedef enum {
   SLA_ERR_DEVICE = 4,     /* a HIP call failed                                  */
   SLA_ERR_NOT_SPD = 5,    /* CG breakdown: p.Ap <= 0                            */
   SLA_ERR_NONFINITE = 6,  /* b.b, p.Ap or r.r is not finite                     */
-  SLA_ERR_KRYLOV = 7      /* eigsh: the Lanczos process ended (an invariant
+  SLA_ERR_KRYLOV = 7,     /* eigsh: the Lanczos process ended (an invariant
                              subspace was reached) after fewer than k steps   */
+  SLA_ERR_BREAKDOWN = 8   /* BiCGStab: rhat.r, rhat.v or t.t became 0          */
 } sla_status;
 
 typedef enum { SLA_I32 = 4, SLA_I64 = 8 } sla_index;
@@ -286,6 +287,54 @@ sla_status sla_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v
  */
 sla_status sla_eig_grad(sla_csr A, int64_t k, const double* X, const double* grad_theta,
                         double* grad_vals, hipStream_t stream);
+
+/*
+ * Solve A x = b for a general (non-symmetric) A by BiCGStab, one of the
+ * solvers the torch-sla summary lists for its CPU backends (Methodology 1),
+ * here on the GPU, for every system of the bound batch (shared pattern).
+ * The pages name the solver, not its variant; this is the textbook
+ * unpreconditioned method:
+ *   r = b - A x0 (x0 = 0 unless SLA_FLAG_X0), rhat = r, p = v = 0,
+ *   rho_prev = alpha = omega = 1; each iteration:
+ *     rho = rhat.r, beta = (rho / rho_prev)(alpha / omega),
+ *     p = r + beta (p - omega v), v = A p, alpha = rho / rhat.v,
+ *     s = r - alpha v; if s.s <= tol^2 b.b: x += alpha p and stop (the
+ *     iteration counts); t = A s, omega = t.s / t.t,
+ *     x = (x + alpha p) + omega s, r = s - omega t.
+ * Stops, as the CG solve, when the recursive residual has r.r <= tol^2 b.b
+ * before an iteration, or after maxit iterations (SLA_OK, converged = 0).
+ * rhat.r, rhat.v or t.t equal to 0, or omega = 0, is SLA_ERR_BREAKDOWN;
+ * a non-finite dot product SLA_ERR_NONFINITE (x holds the last iterate).
+ * flags: SLA_FLAG_X0, SLA_FLAG_HISTORY (rho, alpha, omega, r.r per
+ * iteration, read with sla_bicgstab_history).  b, x [batch][n] device
+ * memory; info_host [batch] (may be NULL).  Returns the first non-OK system
+ * status.  Synchronises `stream`.
+ */
+sla_status sla_bicgstab_solve(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                              uint32_t flags, sla_cg_info* info_host, hipStream_t stream);
+
+/*
+ * Backward pass of x = A^{-1} b solved by BiCGStab (Methodology 2, linear
+ * systems): A^T lambda = grad_x by the same BiCGStab on the transposed
+ * pattern (built once per handle; the values are gathered into its slot
+ * order on each call), grad_b = lambda [batch][n], and
+ * grad_vals[k] = -lambda_i x_j on every stored slot [batch][nnz] (may be
+ * NULL; computed also after a breakdown, from the last iterate).  flags:
+ * SLA_FLAG_HISTORY only.  Synchronises `stream`.
+ */
+sla_status sla_bicgstab_adjoint(sla_csr A, const double* x, const double* grad_x,
+                                double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                                uint32_t flags, sla_cg_info* info_host, hipStream_t stream);
+
+/*
+ * rho, alpha, omega (0 for a half-step finish) and the residual norm squared
+ * after each iteration of system `system` of the last BiCGStab solve or
+ * adjoint run with SLA_FLAG_HISTORY.  Host arrays of length cap (each may be
+ * NULL); *count_host = the iterations recorded.
+ */
+sla_status sla_bicgstab_history(sla_csr A, int64_t system, double* rho_host,
+                                double* alpha_host, double* omega_host, double* rr_host,
+                                int64_t cap, int64_t* count_host);
 
 /*
  * Measurement aid for sla_eigsh: after an sla_eigsh call on this handle with

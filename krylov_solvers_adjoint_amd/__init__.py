@@ -28,12 +28,14 @@ __all__ = [
     "sla_csr_grad_to_coo", "sla_spmv", "sla_cg_solve", "sla_cg_adjoint",
     "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
     "sla_spmv_transpose", "sla_matvec_grad", "sla_eigsh", "sla_eig_grad", "EigInfo",
+    "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 
-OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE, ERR_KRYLOV = range(8)
+(OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE, ERR_KRYLOV,
+ ERR_BREAKDOWN) = range(9)
 EIG_SMALLEST, EIG_LARGEST = 0, 1
 I32, I64 = 4, 8
 FLAG_X0, FLAG_HISTORY, FLAG_JACOBI = 1, 2, 4
@@ -47,6 +49,7 @@ EXPORTS = [
     "sla_csr_set_graph_block",
     "sla_csr_set_workgroups_per_cu", "sla_spmv_transpose", "sla_matvec_grad",
     "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
+    "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -100,6 +103,9 @@ def _bind(lib):
         "sla_eigsh": [_P, _I64, _S, _I64, _P, _P, _P, _P, _P, _P],
         "sla_eig_grad": [_P, _I64, _P, _P, _P, _P],
         "sla_profile_lanczos_kernels": [_P, _I64, _I64, _P, _P],
+        "sla_bicgstab_solve": [_P, _P, _P, _D, _I64, _U32, _P, _P],
+        "sla_bicgstab_adjoint": [_P, _P, _P, _P, _P, _D, _I64, _U32, _P, _P],
+        "sla_bicgstab_history": [_P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64)],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
@@ -462,6 +468,40 @@ def sla_cg_solve_batched(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, t
     return x, infos
 
 
+def sla_bicgstab_solve(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: float,
+                       maxit: int, x0: torch.Tensor | None = None, history: bool = False,
+                       stream=None, check: bool = True):
+    """BiCGStab for a general A: (x, [CGInfo per system]).  b [n] or [batch, n]."""
+    batch = A.bind(values)
+    x = x0.clone() if x0 is not None else torch.empty_like(b)
+    st, infos = _solve_call(_lib.sla_bicgstab_solve, A, b, x, tol, maxit,
+                            _flags(x0, history, False), batch, stream, check)
+    return x, infos
+
+
+def sla_bicgstab_adjoint(A: CSRPattern, values: torch.Tensor, x: torch.Tensor,
+                         grad_x: torch.Tensor, tol: float, maxit: int, want_vals: bool = True,
+                         history: bool = False, stream=None, check: bool = True):
+    """(grad_b = lambda solving A^T lambda = grad_x, grad_vals = -lambda_i x_j or None,
+    [CGInfo per system])."""
+    batch = A.bind(values)
+    return _adjoint_call(_lib.sla_bicgstab_adjoint, A, x, grad_x, tol, maxit, want_vals,
+                         _flags(None, history, False), batch, stream, check)
+
+
+def sla_bicgstab_history(A: CSRPattern, system: int = 0, cap: int = 1 << 20):
+    """(rho, alpha, omega, rr) per iteration of the last BiCGStab run with history."""
+    import numpy as np
+    cnt = _I64()
+    _check(_lib.sla_bicgstab_history(A.handle, system, None, None, None, None, 0,
+                                     ctypes.byref(cnt)))
+    k = min(cnt.value, cap)
+    out = [np.zeros(max(k, 1)) for _ in range(4)]
+    _check(_lib.sla_bicgstab_history(A.handle, system, *[o.ctypes.data for o in out], k,
+                                     ctypes.byref(cnt)))
+    return tuple(o[:k] for o in out)
+
+
 def _adjoint_call(fn, A, x, grad_x, tol, maxit, want_vals, flags, batch, stream, check):
     _shape(grad_x, _vec_shape(A, batch, grad_x), "grad_x")
     _shape(x, _vec_shape(A, batch, grad_x), "x")
@@ -558,6 +598,28 @@ class _CGSolve(torch.autograd.Function):
         return gv, gb, None, None, None, None
 
 
+class _BiCGStabSolve(torch.autograd.Function):
+    """x = A^{-1} b by BiCGStab (general A); backward: A^T lambda = g by
+    BiCGStab, grad_b = lambda, grad_vals = -lambda_i x_j on the pattern."""
+
+    @staticmethod
+    def forward(ctx, values, b, pattern, tol, maxit):
+        x, infos = sla_bicgstab_solve(pattern, values.detach().contiguous(), b.contiguous(), tol,
+                                      maxit)
+        ctx.pattern, ctx.tol, ctx.maxit = pattern, tol, maxit
+        ctx.infos = infos
+        ctx.save_for_backward(values, x)
+        return x
+
+    @staticmethod
+    def backward(ctx, grad_x):
+        values, x = ctx.saved_tensors
+        gb, gv, _ = sla_bicgstab_adjoint(ctx.pattern, values.detach().contiguous(), x,
+                                         grad_x.contiguous(), ctx.tol, ctx.maxit,
+                                         want_vals=ctx.needs_input_grad[0])
+        return gv, gb, None, None, None
+
+
 class _MatVec(torch.autograd.Function):
     """y = A x; backward grad_x = A^T g, grad_vals = g_i x_j on the pattern."""
 
@@ -618,8 +680,15 @@ class SparseTensor:
         return (self.pattern.n, self.pattern.n)
 
     def solve(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
-              precond: str | None = None) -> torch.Tensor:
-        """x = A^{-1} b by CG (precond="jacobi": preconditioned with diag(A))."""
+              precond: str | None = None, method: str = "cg") -> torch.Tensor:
+        """x = A^{-1} b: method "cg" (symmetric positive definite A; precond
+        "jacobi" for diag(A)) or "bicgstab" (general A, no preconditioner)."""
+        if method == "bicgstab":
+            if precond is not None:
+                raise ValueError("BiCGStab runs without a preconditioner")
+            return _BiCGStabSolve.apply(self.values, b, self.pattern, float(tol), int(maxit))
+        if method != "cg":
+            raise ValueError(f"unknown method {method!r}")
         if precond not in (None, "jacobi"):
             raise ValueError(f"unknown preconditioner {precond!r}")
         return _CGSolve.apply(self.values, b, self.pattern, float(tol), int(maxit),
@@ -645,6 +714,6 @@ class SparseTensor:
 
 
 def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
-          precond: str | None = None):
+          precond: str | None = None, method: str = "cg"):
     """x = A^{-1} b with the adjoint backward pass."""
-    return A.solve(b, tol, maxit, precond)
+    return A.solve(b, tol, maxit, precond, method)

@@ -85,6 +85,7 @@ void free_handle(sla_csr A) {
   if (!A) return;
   release_workspace(A);
   release_eig_work(A);
+  release_bs_work(A);
   free_handle(A->trans);
   dev_free(A->rowptr);
   dev_free(A->col);
@@ -112,6 +113,7 @@ const char* sla_status_string(sla_status s) {
     case SLA_ERR_NOT_SPD: return "SLA_ERR_NOT_SPD";
     case SLA_ERR_NONFINITE: return "SLA_ERR_NONFINITE";
     case SLA_ERR_KRYLOV: return "SLA_ERR_KRYLOV";
+    case SLA_ERR_BREAKDOWN: return "SLA_ERR_BREAKDOWN";
   }
   return "SLA_UNKNOWN";
 }
@@ -375,6 +377,39 @@ sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad
     }
   }
   return s;
+  API_END
+}
+
+sla_status sla_bicgstab_solve(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                              uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_solve(A, b, x, tol, maxit, flags & ~uint32_t(SLA_FLAG_JACOBI), "sla_bicgstab_solve"));
+  REQUIRE((flags & SLA_FLAG_JACOBI) == 0, "sla_bicgstab_solve: no preconditioner is supported");
+  return run_bicgstab(A, b, x, tol, maxit, flags, info, stream);
+  API_END
+}
+
+sla_status sla_bicgstab_adjoint(sla_csr A, const double* x, const double* grad_x,
+                                double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                                uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_solve(A, grad_x, grad_b, tol, maxit, flags, "sla_bicgstab_adjoint"));
+  REQUIRE((flags & ~uint32_t(SLA_FLAG_HISTORY)) == 0,
+          "sla_bicgstab_adjoint: only SLA_FLAG_HISTORY is supported");
+  REQUIRE(grad_vals == nullptr || x != nullptr, "sla_bicgstab_adjoint: grad_vals needs x");
+  return run_bicgstab_adjoint(A, x, grad_x, grad_b, grad_vals, tol, maxit, flags, info, stream);
+  API_END
+}
+
+sla_status sla_bicgstab_history(sla_csr A, int64_t system, double* rho, double* alpha,
+                                double* omega, double* rr, int64_t cap, int64_t* count) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_bicgstab_history: NULL handle");
+  REQUIRE(cap >= 0, "sla_bicgstab_history: cap < 0");
+  return bicgstab_history(A, system, rho, alpha, omega, rr, cap, count);
   API_END
 }
 

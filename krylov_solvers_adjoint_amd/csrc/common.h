@@ -103,6 +103,7 @@ enum : int32_t {
   ST_MAXIT = 2,
   ST_NOT_SPD = SLA_ERR_NOT_SPD,
   ST_NONFINITE = SLA_ERR_NONFINITE,
+  ST_BREAKDOWN = SLA_ERR_BREAKDOWN,
 };
 
 // Per-system CG scalars, resident on the device for the whole solve.  An

@@ -8,6 +8,7 @@
 
 namespace sla {
 struct EigWork;  // Lanczos workspace (lanczos.hip)
+struct BsWork;   // BiCGStab workspace (bicgstab.hip)
 }
 
 struct sla_csr_s {
@@ -81,6 +82,9 @@ struct sla_csr_s {
   hipStream_t capture_stream = nullptr;
   // Lanczos basis and scratch, allocated by the first eigsh call
   sla::EigWork* eig = nullptr;
+  // BiCGStab vectors, partials and scalars, allocated by the first solve
+  sla::BsWork* bs = nullptr;
+  bool bs_hist_valid = false;
   std::map<int64_t, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
 };
 
@@ -114,6 +118,15 @@ sla_status run_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v
 sla_status launch_eig_grad(sla_csr A, int64_t k, const double* X, const double* g,
                            double* grad, hipStream_t stream);
 void release_eig_work(sla_csr A);
+// BiCGStab (bicgstab.hip)
+sla_status run_bicgstab(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                        uint32_t flags, sla_cg_info* info, hipStream_t stream);
+sla_status run_bicgstab_adjoint(sla_csr A, const double* x, const double* grad_x,
+                                double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                                uint32_t flags, sla_cg_info* info, hipStream_t stream);
+sla_status bicgstab_history(sla_csr A, int64_t system, double* rho, double* alpha,
+                            double* omega, double* rr, int64_t cap, int64_t* count);
+void release_bs_work(sla_csr A);
 // mean durations of the Gram-Schmidt dot and update passes over nvec basis
 // vectors, on the basis an earlier eigsh left in the workspace
 sla_status profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps, double* avg_ms,
@@ -126,6 +139,8 @@ sla_status build_from_coo(sla_csr A, sla_index coo_idx, const void* row,
                           const void* col, hipStream_t stream);
 sla_status build_from_csr(sla_csr A, const void* rowptr, const int32_t* col,
                           hipStream_t stream);
+// the transposed pattern A->trans (built once; csr_build.hip)
+sla_status build_transpose(sla_csr A, hipStream_t stream);
 sla_status launch_values_from_coo(sla_csr A, const double* coo_val, double* vals,
                                   int64_t batch, hipStream_t stream);
 sla_status launch_grad_to_coo(sla_csr A, const double* grad_vals, double* grad_coo,

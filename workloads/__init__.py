@@ -100,6 +100,34 @@ def poisson_csr(N: int, rowptr_dtype=np.int32, diag: float = 4.0, off: float = -
     return rowptr.astype(rowptr_dtype, copy=False), col, vals
 
 
+def convection_diffusion_csr(N: int, eps: float = 0.05, wind: float = 1.0,
+                             rowptr_dtype=np.int32):
+    """CSR of the N x N upwind convection-diffusion operator
+    -eps Laplace(u) + wind du/da with h = 1/(N+1), zero Dirichlet boundary and
+    the flow along the grid lines (+a): row i = (c-1) N + (a-1) holds
+    -eps/h^2 (south, north, east), -eps/h^2 - wind/h (west, upwind) and
+    4 eps/h^2 + wind/h (diagonal), columns ascending.  A non-symmetric
+    M-matrix with the Poisson pattern.  Returns (rowptr, col, vals)."""
+    n = N * N
+    h = 1.0 / (N + 1)
+    d, w = eps / h ** 2, wind / h
+    i = np.arange(n, dtype=np.int64)
+    a, c = i % N, i // N
+    parts = [(i - N, -d, c > 0), (i - 1, -d - w, a > 0), (i, 4 * d + w, np.ones(n, bool)),
+             (i + 1, -d, a < N - 1), (i + N, -d, c < N - 1)]
+    counts = sum(m.astype(np.int64) for _, _, m in parts)
+    rowptr = np.zeros(n + 1, np.int64)
+    np.cumsum(counts, out=rowptr[1:])
+    col = np.empty(rowptr[-1], np.int32)
+    val = np.empty(rowptr[-1], np.float64)
+    pos = rowptr[:-1].copy()
+    for cols, v, m in parts:   # in ascending column order
+        col[pos[m]] = cols[m]
+        val[pos[m]] = v
+        pos[m] += 1
+    return rowptr.astype(rowptr_dtype, copy=False), col, val
+
+
 def stencil_csr(shape, stencil, rowptr_dtype=np.int32):
     """CSR of a constant-coefficient stencil on a box grid with a zero
     Dirichlet boundary: `stencil` maps a displacement tuple (x fastest) to
