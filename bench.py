@@ -435,6 +435,56 @@ def bench_eigsh(m: int, k: int):
     return out
 
 
+def bicgstab_bytes(n: int, nnz: int, variant: str) -> int:
+    """Algorithmic bytes of one BiCGStab iteration: two SpMVs (A p, A s),
+    which also read rhat and s for their dot products, and the vector passes:
+    p = r + beta (p - omega v) reads r, p, v and writes p; s = r - alpha v
+    reads 2, writes 1; the update reads s, x, p, t, rhat and writes x, r
+    (16 vectors in all besides the SpMVs' own)."""
+    return 2 * spmv_bytes(variant, n, nnz, 4) + 16 * 8 * n
+
+
+def bench_bicgstab():
+    """BiCGStab forward + adjoint on the 1000 x 1000 upwind
+    convection-diffusion matrix (non-symmetric, 10^6 unknowns) to tol 1e-8."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    N = 1000
+    n = N * N
+    rp, c, v = W.convection_diffusion_csr(N)
+    P = K.sla_csr_create_from_csr(torch.from_numpy(rp).to(dev), torch.from_numpy(c).to(dev))
+    vt = torch.from_numpy(v).to(dev)
+    b = torch.from_numpy(W.normal_rhs(n, 90)).to(dev)
+    g = torch.from_numpy(W.normal_rhs(n, 91)).to(dev)
+    K.sla_bicgstab_solve(P, vt, b, 1e-8, 40)  # workspace, transposed pattern below
+    K.sla_bicgstab_adjoint(P, vt, b, g, 1e-8, 40)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x, fi = K.sla_bicgstab_solve(P, vt, b, 1e-8, 10000)
+    torch.cuda.synchronize()
+    fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    gb, gv, ai = K.sla_bicgstab_adjoint(P, vt, x, g, 1e-8, 10000)
+    torch.cuda.synchronize()
+    adj = time.perf_counter() - t0
+    variant = "banded" if P.banded else "csr"
+    its = fi[0].iterations + ai[0].iterations
+    nb = its * bicgstab_bytes(n, P.nnz, variant)
+    out = dict(n=n, nnz=P.nnz, spmv=variant, iterations_fwd=fi[0].iterations,
+               iterations_adj=ai[0].iterations, solve_ms=1e3 * fwd, adjoint_ms=1e3 * adj,
+               it_per_s=its / (fwd + adj), us_per_iteration=1e6 * (fwd + adj) / its,
+               eff_GBps=nb / (fwd + adj) / 1e9, bytes_per_iteration=bicgstab_bytes(n, P.nnz,
+                                                                                    variant),
+               rel_residual=fi[0].rel_residual)
+    del P, vt, b, g, x, gb, gv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(seconds: float):
     """The oracle as it stands, on a bounded sample of the same workload:
     forward and adjoint CG on the 1000 x 1000 Poisson system, k fixed
@@ -520,6 +570,9 @@ def main():
             if s.lower() == "matvec":
                 log(f"[bench] matvec: {bench_matvec(args.kernel_reps)}")
                 continue
+            if s.lower() == "bicgstab":
+                log(f"[bench] bicgstab: {bench_bicgstab()}")
+                continue
             if s.lower() == "eigsh":
                 out = bench_eigsh(args.eig_steps, 4)
                 log(f"[bench] eigsh: {out['ms']:.1f} ms, {out['eff_GBps']:.0f} GB/s")
@@ -561,6 +614,9 @@ def main():
         nxt["eigsh"] = bench_eigsh(args.eig_steps, 4)
         log(f"[bench] .eigsh: {nxt['eigsh']['ms']:.1f} ms, "
             f"{nxt['eigsh']['eff_GBps']:.0f} GB/s")
+        log("[bench] BiCGStab on convection-diffusion 1000x1000, tol 1e-8, fwd + adj")
+        nxt["bicgstab"] = bench_bicgstab()
+        log(f"[bench] BiCGStab: {nxt['bicgstab']}")
 
     digest = source_digest()
     spmv_ms = head["kernel_ms"]["spmv_step"]

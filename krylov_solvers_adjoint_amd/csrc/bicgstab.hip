@@ -7,12 +7,10 @@
 //   each iteration j:
 //     rho = rhat.r; beta = (rho / rho_prev)(alpha / omega)
 //     p = r + beta (p - omega v)                      k_bs_direction
-//     v = A p                                          the library's SpMV
-//     partials of rhat.v                               k_bs_rv
+//     v = A p and the rhat.v partials                  the library's SpMV
 //     alpha = rho / rhat.v; s = r - alpha v, s.s       k_bs_s
-//     t = A s                                          the library's SpMV
-//     s.s <= tol^2 b.b: x += alpha p, done; else t.t, t.s partials
-//                                                      k_bs_half
+//     t = A s and the t.s, t.t partials                the library's SpMV
+//     s.s <= tol^2 b.b: x += alpha p, done; else
 //     omega = t.s / t.t; x = (x + alpha p) + omega s; r = s - omega t;
 //     rhat.r and r.r partials                          k_bs_update
 // Every kernel's workgroups first sum the previous kernel's partials (one
@@ -20,11 +18,16 @@
 // same decisions from the same bits, and no reduction kernel or
 // cross-workgroup signal is needed.
 //
-// Stopping: a kernel that ends the solve stores its position 8 j + phase in
-// the system's scalars; a kernel at a later position returns at once.  The
-// workgroups of the stopping launch itself read their own position there,
-// not a later one, so they all still finish that kernel's work (the x
-// update of a half-step finish, the update before an omega = 0 breakdown).
+// Iteration index and stopping live in device memory, so a block of
+// iterations can be captured once as a HIP graph and replayed.
+// k_bs_direction reads the next iteration's index jn (written only by
+// k_bs_update) and publishes it as jc for the other kernels of the
+// iteration.  A kernel that ends the solve stores its position 8 jc + phase;
+// a later kernel of the same iteration sees a smaller position and returns,
+// while the workgroups of the stopping launch itself see their own position
+// and still finish its work (the x update of a half-step finish, the update
+// before an omega = 0 breakdown).  The next k_bs_direction that finds a stop
+// raises `halted`, which every later kernel checks first.
 #include <cmath>
 #include <vector>
 
@@ -36,7 +39,7 @@ namespace {
 
 constexpr int kBsBlock = kIterBlock;  // 16 waves
 enum : int { P_RHR = 0, P_RR, P_RV, P_SS, P_TT, P_TS, P_BB, kBsSets };
-enum : int { PH_DIR = 0, PH_S = 1, PH_HALF = 2, PH_UPD = 3 };
+enum : int { PH_DIR = 0, PH_S = 1, PH_UPD = 2 };
 constexpr int64_t kNoStop = INT64_MAX;
 
 struct alignas(64) BsScal {
@@ -46,10 +49,14 @@ struct alignas(64) BsScal {
   double omega;     //                                          (k_bs_update)
   double bb;        // b.b                                      (set-up)
   double stop;      // tol^2 b.b                                (set-up)
-  double rr;        // residual norm squared, last known        (k_bs_direction, k_bs_half)
-  int64_t it;       // completed iterations                     (k_bs_half, k_bs_update)
-  int64_t stop_pos; // 8 j + phase of the stopping kernel, or kNoStop
+  double rr;        // residual norm squared, last known        (k_bs_direction, k_bs_update)
+  int64_t it;       // completed iterations                     (k_bs_update)
+  int64_t stop_pos; // 8 jc + phase of the stopping kernel, or kNoStop
+  int64_t jn;       // index of the next iteration              (k_bs_update)
+  int64_t jc;       // index of the current iteration           (k_bs_direction)
+  int64_t maxit;    //                                          (set-up)
   int32_t status;   // ST_* of the stop
+  int32_t halted;   // a stop was seen by a later iteration     (k_bs_direction)
 };
 
 struct BsArgs {
@@ -68,8 +75,16 @@ struct BsArgs {
   int64_t hist_cap;
 };
 
-__device__ __forceinline__ bool skip(const BsScal* sc, int64_t pos) {
-  return __hip_atomic_load(&sc->stop_pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < pos;
+__device__ __forceinline__ int64_t stop_pos_of(const BsScal* sc) {
+  return __hip_atomic_load(&sc->stop_pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Kernels after the head of an iteration: return when the solve has halted
+// or stopped at an earlier position of this iteration.
+__device__ __forceinline__ bool skip(const BsScal* sc, int phase, int64_t* j) {
+  if (sc->halted) return true;
+  *j = sc->jc;
+  return stop_pos_of(sc) < 8 * *j + phase;
 }
 
 // Workgroup stop: one thread records the position and status.
@@ -140,22 +155,32 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_init_scalars(BsArgs a, double t
     sc->stop = (tol * tol) * bb;
     sc->rr = rr;
     sc->it = 0;
+    sc->jn = 0;
+    sc->jc = 0;
+    sc->maxit = maxit;
+    sc->halted = 0;
     sc->status = ST_RUNNING;
     sc->stop_pos = kNoStop;
-    (void)maxit;
     if (!isfinite(bb) || !isfinite(rr)) set_stop(sc, -1, ST_NONFINITE);
   }
 }
 
-// Head of iteration j: the stopping tests on r.r, rho = rhat.r, beta and
-// p = r + beta (p - omega v).  Launched once more with j = maxit to close
-// the solve (it then only tests).
-__global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a, int64_t j, int64_t maxit) {
+// Head of iteration j = jn: the stopping tests on r.r, rho = rhat.r, beta
+// and p = r + beta (p - omega v).  Launched once more after the last
+// iteration to close the solve (it then only tests).
+__global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a) {
   __shared__ double red[kBsBlock / kWave];
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
+  if (sc->halted) return;
+  if (stop_pos_of(sc) != kNoStop) {
+    // stopped in an earlier iteration (or by workgroup 0 of this launch,
+    // after the same tests this workgroup would make)
+    if (blockIdx.x == 0 && threadIdx.x == 0) sc->halted = 1;
+    return;
+  }
+  const int64_t j = sc->jn, maxit = sc->maxit;
   const int64_t pos = 8 * j + PH_DIR;
-  if (skip(sc, pos)) return;
   const double* part = a.part + sys * kBsSets * a.G;
   const double rho = sum_set(part + P_RHR * a.G, a.G, red);
   const double rr = sum_set(part + P_RR * a.G, a.G, red);
@@ -167,6 +192,7 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a, int64_t j, 
   else if (rho == 0.0) st = ST_BREAKDOWN;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     sc->rr = rr;
+    sc->jc = j;
     double* h = hist_of(a, sys);
     if (h && j >= 1 && j - 1 < a.hist_cap) h[(j - 1) * 4 + 3] = rr;
     if (st != ST_RUNNING) set_stop(sc, pos, st);
@@ -180,25 +206,14 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a, int64_t j, 
     a.p[o + i] = a.r[o + i] + beta * (a.p[o + i] - om * a.v[o + i]);
 }
 
-// Partials of rhat.v after v = A p.
-__global__ __launch_bounds__(kBsBlock) void k_bs_rv(BsArgs a, int64_t j) {
-  __shared__ double red[kBsBlock / kWave];
-  const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
-  if (skip(a.scal + sys, 8 * j + PH_S)) return;
-  double acc = 0.0;
-  for (int64_t i = int64_t(blockIdx.x) * kBsBlock + threadIdx.x; i < n;
-       i += a.G * kBsBlock)
-    acc = acc + a.rh[o + i] * a.v[o + i];
-  put_partial(a.part + (sys * kBsSets + P_RV) * a.G, acc, red);
-}
-
 // alpha = rho / rhat.v; s = r - alpha v and the s.s partials.
-__global__ __launch_bounds__(kBsBlock) void k_bs_s(BsArgs a, int64_t j) {
+__global__ __launch_bounds__(kBsBlock) void k_bs_s(BsArgs a) {
   __shared__ double red[kBsBlock / kWave];
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
+  int64_t j;
+  if (skip(sc, PH_S, &j)) return;
   const int64_t pos = 8 * j + PH_S;
-  if (skip(sc, pos)) return;
   const double* part = a.part + sys * kBsSets * a.G;
   const double rv = sum_set(part + P_RV * a.G, a.G, red);
   int32_t st = ST_RUNNING;
@@ -228,15 +243,18 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_s(BsArgs a, int64_t j) {
   put_partial(a.part + (sys * kBsSets + P_SS) * a.G, ss, red);
 }
 
-// After t = A s: the half-step finish (s.s <= tol^2 b.b: x += alpha p),
-// else the t.t and t.s partials.
-__global__ __launch_bounds__(kBsBlock) void k_bs_half(BsArgs a, int64_t j) {
+// After t = A s: the half-step finish (s.s <= tol^2 b.b: x += alpha p), else
+// omega = t.s / t.t; x = (x + alpha p) + omega s; r = s - omega t; the
+// rhat.r and r.r partials of the next iteration.
+__global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a) {
   __shared__ double red[kBsBlock / kWave];
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
-  const int64_t pos = 8 * j + PH_HALF;
-  if (skip(sc, pos)) return;
-  const double ss = sum_set(a.part + (sys * kBsSets + P_SS) * a.G, a.G, red);
+  int64_t j;
+  if (skip(sc, PH_UPD, &j)) return;
+  const int64_t pos = 8 * j + PH_UPD;
+  const double* part = a.part + sys * kBsSets * a.G;
+  const double ss = sum_set(part + P_SS * a.G, a.G, red);
   if (!isfinite(ss)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) set_stop(sc, pos, ST_NONFINITE);
     return;
@@ -258,27 +276,6 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_half(BsArgs a, int64_t j) {
     }
     return;
   }
-  double tt = 0.0, ts = 0.0;
-  for (int64_t i = int64_t(blockIdx.x) * kBsBlock + threadIdx.x; i < n;
-       i += a.G * kBsBlock) {
-    const double ti = a.t[o + i];
-    tt = tt + ti * ti;
-    ts = ts + ti * a.s[o + i];
-  }
-  double* part = a.part + sys * kBsSets * a.G;
-  put_partial(part + P_TT * a.G, tt, red);
-  put_partial(part + P_TS * a.G, ts, red);
-}
-
-// omega = t.s / t.t; x = (x + alpha p) + omega s; r = s - omega t; the
-// rhat.r and r.r partials of the next iteration.
-__global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a, int64_t j) {
-  __shared__ double red[kBsBlock / kWave];
-  const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
-  BsScal* sc = a.scal + sys;
-  const int64_t pos = 8 * j + PH_UPD;
-  if (skip(sc, pos)) return;
-  const double* part = a.part + sys * kBsSets * a.G;
   const double tt = sum_set(part + P_TT * a.G, a.G, red);
   const double ts = sum_set(part + P_TS * a.G, a.G, red);
   int32_t st = ST_RUNNING;
@@ -311,6 +308,7 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a, int64_t j) {
     } else {
       sc->omega = omega;
       sc->rho_prev = sc->rho;
+      sc->jn = j + 1;
     }
   }
 }
@@ -321,13 +319,25 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a, int64_t j) {
 // Host side
 // ---------------------------------------------------------------------------
 
+// iterations per captured graph
+constexpr int64_t kBsGraphIters = 16;
+
 struct BsWork {
   int64_t cap_n = 0, cap_batch = 0, cap_g = 0;
   double* vec = nullptr;    // [6][batch][n]: r, rhat, p, v, s, t
   double* part = nullptr;   // [batch][kBsSets][G]
   BsScal* scal = nullptr;   // [batch]
-  BsScal* scal_host = nullptr;  // pinned [batch]
-  hipEvent_t poll_ev = nullptr;
+  BsScal* scal_host = nullptr;  // pinned [3][batch]: final copy, two poll copies
+  hipEvent_t poll_ev[2] = {nullptr, nullptr};
+  // the captured block of iterations and what its kernel arguments bake in
+  hipStream_t capture_stream = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  const void* key_pattern = nullptr;
+  const void* key_vals = nullptr;
+  const void* key_x = nullptr;
+  const void* key_hist = nullptr;
+  int64_t key_batch = 0, key_g = 0, key_hcap = 0;
   double* hist = nullptr;   // [batch][hist_cap][4]
   int64_t hist_cap = 0, hist_batch = 0;
   double* tvals = nullptr;  // [batch][nnz] values of A^T (adjoint)
@@ -343,20 +353,21 @@ void release_bs_work(sla_csr A) {
   dev_free(w->hist);
   dev_free(w->tvals);
   if (w->scal_host) (void)hipHostFree(w->scal_host);
-  if (w->poll_ev) (void)hipEventDestroy(w->poll_ev);
+  for (auto& e : w->poll_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (w->exec) (void)hipGraphExecDestroy(w->exec);
+  if (w->graph) (void)hipGraphDestroy(w->graph);
+  if (w->capture_stream) (void)hipStreamDestroy(w->capture_stream);
   delete w;
   A->bs = nullptr;
 }
 
-static int64_t bs_groups(int64_t n, int64_t batch) {
-  const int64_t need = (n + kBsBlock - 1) / kBsBlock;
-  int64_t target = int64_t(device_cus()) * 2 / (batch > 0 ? batch : 1);
-  if (target < 1) target = 1;
-  return need < target ? (need > 0 ? need : 1) : target;
-}
+// Workgroups per system of the vector kernels: the SpMV's, so that the
+// partial sums the SpMV leaves line up with the vector kernels' own.
+static int64_t bs_groups(sla_csr P, int64_t batch) { return spmv_groups(P, batch); }
 
 static sla_status ensure_bs_work(sla_csr A, int64_t batch) {
-  const int64_t n = A->n, G = bs_groups(n, 1);
+  const int64_t n = A->n, G = bs_groups(A, 1);
   BsWork* w = A->bs;
   if (w && w->cap_n == n && w->cap_batch >= batch && w->cap_g >= G) return SLA_OK;
   release_bs_work(A);
@@ -368,9 +379,74 @@ static sla_status ensure_bs_work(sla_csr A, int64_t batch) {
   SLA_TRY(dev_alloc(&w->vec, size_t(6) * size_t(batch) * size_t(n), "BiCGStab vectors"));
   SLA_TRY(dev_alloc(&w->part, size_t(batch) * kBsSets * size_t(G), "BiCGStab partials"));
   SLA_TRY(dev_alloc(&w->scal, size_t(batch), "BiCGStab scalars"));
-  SLA_TRY_HIP(hipHostMalloc((void**)&w->scal_host, sizeof(BsScal) * size_t(batch),
+  SLA_TRY_HIP(hipHostMalloc((void**)&w->scal_host, sizeof(BsScal) * 3 * size_t(batch),
                             hipHostMallocDefault));
-  SLA_TRY_HIP(hipEventCreateWithFlags(&w->poll_ev, hipEventDisableTiming));
+  for (auto& e : w->poll_ev) SLA_TRY_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  return SLA_OK;
+}
+
+// One iteration: three vector kernels around the two SpMVs, which leave the
+// rhat.v and the t.s, t.t partials (their grid is the vector kernels').
+static sla_status bs_enqueue_iteration(const BsArgs& a, sla_csr P, const double* vals,
+                                       int64_t batch, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.G), static_cast<unsigned>(batch));
+  const int64_t ps = kBsSets * a.G;
+  k_bs_direction<<<grid, kBsBlock, 0, st>>>(a);
+  SLA_TRY(launch_spmv_dots(P, vals, batch, a.p, a.v, a.rh, 1, a.part, ps, P_RV, 0, st));
+  k_bs_s<<<grid, kBsBlock, 0, st>>>(a);
+  SLA_TRY(launch_spmv_dots(P, vals, batch, a.s, a.t, a.s, 2, a.part, ps, P_TS, P_TT, st));
+  k_bs_update<<<grid, kBsBlock, 0, st>>>(a);
+  LAUNCH_CHECK();
+  return SLA_OK;
+}
+
+// The graph of kBsGraphIters iterations for these arguments: reused while
+// the pointers it bakes in are unchanged, else captured anew.
+static sla_status bs_graph(BsWork* w, const BsArgs& a, sla_csr P, const double* vals,
+                           int64_t batch, hipGraphExec_t* exec) {
+  if (w->exec && w->key_pattern == P && w->key_vals == vals && w->key_x == a.x &&
+      w->key_hist == a.hist && w->key_batch == batch && w->key_g == a.G &&
+      w->key_hcap == a.hist_cap) {
+    *exec = w->exec;
+    return SLA_OK;
+  }
+  if (w->exec) (void)hipGraphExecDestroy(w->exec);
+  if (w->graph) (void)hipGraphDestroy(w->graph);
+  w->exec = nullptr;
+  w->graph = nullptr;
+  if (w->capture_stream == nullptr)
+    SLA_TRY_HIP(hipStreamCreateWithFlags(&w->capture_stream, hipStreamNonBlocking));
+  hipGraph_t g = nullptr;
+  SLA_TRY_HIP(hipStreamBeginCapture(w->capture_stream, hipStreamCaptureModeThreadLocal));
+  sla_status s = SLA_OK;
+  for (int64_t k = 0; k < kBsGraphIters && s == SLA_OK; ++k)
+    s = bs_enqueue_iteration(a, P, vals, batch, w->capture_stream);
+  hipError_t he = hipStreamEndCapture(w->capture_stream, &g);
+  if (s != SLA_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return s;
+  }
+  if (he != hipSuccess) {
+    set_error("BiCGStab graph capture failed: %s", hipGetErrorString(he));
+    return SLA_ERR_DEVICE;
+  }
+  hipGraphExec_t e = nullptr;
+  he = hipGraphInstantiate(&e, g, nullptr, nullptr, 0);
+  if (he != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    set_error("BiCGStab graph instantiation failed: %s", hipGetErrorString(he));
+    return SLA_ERR_DEVICE;
+  }
+  w->graph = g;
+  w->exec = e;
+  w->key_pattern = P;
+  w->key_vals = vals;
+  w->key_x = a.x;
+  w->key_hist = a.hist;
+  w->key_batch = batch;
+  w->key_g = a.G;
+  w->key_hcap = a.hist_cap;
+  *exec = e;
   return SLA_OK;
 }
 
@@ -382,7 +458,7 @@ static sla_status bs_run(sla_csr A, sla_csr P, const double* vals, int64_t batch
   SLA_TRY(ensure_bs_work(A, batch));
   BsWork* w = A->bs;
   const int64_t n = A->n;
-  const int64_t G = bs_groups(n, batch);
+  const int64_t G = bs_groups(P, batch);
   const bool want_hist = (flags & SLA_FLAG_HISTORY) != 0;
   if (want_hist) {
     const int64_t cap = maxit > 0 ? maxit : 1;
@@ -417,36 +493,36 @@ static sla_status bs_run(sla_csr A, sla_csr P, const double* vals, int64_t batch
   k_bs_init<<<grid, kBsBlock, 0, st>>>(a, a.v, x0 ? 1 : 0);
   k_bs_init_scalars<<<unsigned(batch), kBsBlock, 0, st>>>(a, tol, maxit);
   LAUNCH_CHECK();
-  // every kPoll iterations the scalars are copied to pinned memory behind
-  // the queued work; once a copy has landed and no system is running, the
-  // host stops launching (the kernels of stopped systems return at once, so
-  // the iterations queued meanwhile cost only their launches and SpMVs)
-  constexpr int64_t kPoll = 16;
-  bool polled = false;
-  for (int64_t j = 0; j < maxit; ++j) {
-    if (polled && hipEventQuery(w->poll_ev) == hipSuccess) {
-      polled = false;
-      int64_t running = 0;
-      for (int64_t s = 0; s < batch; ++s) running += w->scal_host[s].stop_pos == kNoStop;
-      if (running == 0) break;
-    }
-    k_bs_direction<<<grid, kBsBlock, 0, st>>>(a, j, maxit);
-    SLA_TRY(launch_spmv(P, vals, batch, a.p, a.v, st));
-    k_bs_rv<<<grid, kBsBlock, 0, st>>>(a, j);
-    k_bs_s<<<grid, kBsBlock, 0, st>>>(a, j);
-    SLA_TRY(launch_spmv(P, vals, batch, a.s, a.t, st));
-    k_bs_half<<<grid, kBsBlock, 0, st>>>(a, j);
-    k_bs_update<<<grid, kBsBlock, 0, st>>>(a, j);
-    LAUNCH_CHECK();
-    if (!polled && (j + 1) % kPoll == 0) {
-      SLA_TRY_HIP(hipMemcpyAsync(w->scal_host, w->scal, sizeof(BsScal) * size_t(batch),
-                                 hipMemcpyDeviceToHost, st));
-      SLA_TRY_HIP(hipEventRecord(w->poll_ev, st));
-      polled = true;
+  if (maxit < 2 * kBsGraphIters) {
+    // short runs: every iteration launched directly (kernels of a stopped
+    // system return at once)
+    for (int64_t j = 0; j < maxit; ++j) SLA_TRY(bs_enqueue_iteration(a, P, vals, batch, st));
+  } else {
+    // blocks of kBsGraphIters iterations replayed from one captured graph;
+    // after each block the scalars are copied to pinned memory, and before
+    // block k is launched the host waits for the copy behind block k - 2,
+    // so one block is always queued while the host can still stop early
+    hipGraphExec_t exec = nullptr;
+    SLA_TRY(bs_graph(w, a, P, vals, batch, &exec));
+    const int64_t blocks = (maxit + kBsGraphIters - 1) / kBsGraphIters;
+    for (int64_t k = 0; k < blocks; ++k) {
+      if (k >= 2) {
+        const int q = int(k & 1);
+        SLA_TRY_HIP(hipEventSynchronize(w->poll_ev[q]));
+        const BsScal* h = w->scal_host + (1 + q) * batch;
+        int64_t running = 0;
+        for (int64_t s = 0; s < batch; ++s) running += h[s].stop_pos == kNoStop;
+        if (running == 0) break;
+      }
+      SLA_TRY_HIP(hipGraphLaunch(exec, st));
+      const int q = int(k & 1);
+      SLA_TRY_HIP(hipMemcpyAsync(w->scal_host + (1 + q) * batch, w->scal,
+                                 sizeof(BsScal) * size_t(batch), hipMemcpyDeviceToHost, st));
+      SLA_TRY_HIP(hipEventRecord(w->poll_ev[q], st));
     }
   }
   // close: the stopping tests of the state after the last iteration
-  k_bs_direction<<<grid, kBsBlock, 0, st>>>(a, maxit, maxit);
+  k_bs_direction<<<grid, kBsBlock, 0, st>>>(a);
   LAUNCH_CHECK();
   SLA_TRY_HIP(hipMemcpyAsync(w->scal_host, w->scal, sizeof(BsScal) * size_t(batch),
                              hipMemcpyDeviceToHost, st));

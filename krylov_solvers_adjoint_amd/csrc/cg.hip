@@ -286,12 +286,18 @@ __device__ __forceinline__ double sum_partials_all(const SLA_GLOBAL double* __re
 // NB > 0: banded rows with at most NB offsets; NB = 0: plain CSR rows
 // (staged through LDS) with vectors below 4 GiB, gathered with 32-bit
 // offsets; NB = -1: plain CSR rows with 64-bit gather addresses.
-template <typename RP, int NB>
+//
+// ND > 0 also leaves per-workgroup partial dot products for a caller's
+// iteration (BiCGStab): ND = 1 the partial of wdot.y at part[set0], ND = 2 in
+// addition that of y.y at part[set1] (part[set][blockIdx.x] for system
+// blockIdx.y, `pstride` doubles per system).
+template <typename RP, int NB, int ND = 0>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
             const uint8_t* __restrict__ mask, BandOffsets band, const double* __restrict__ vals,
             int64_t n, int64_t nnz, int64_t tiles, int cap, const double* __restrict__ x,
-            double* __restrict__ y) {
+            double* __restrict__ y, const double* __restrict__ wdot,
+            double* __restrict__ part, int64_t pstride, int set0, int set1) {
   extern __shared__ double lds_dyn[];
   double* lv;
   int32_t* lc;
@@ -300,11 +306,13 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
   const double* v = vals + s * nnz;
   const SLA_GLOBAL double* xs = gmem(x + s * n);
   SLA_GLOBAL double* ys = gmem(y + s * n);
+  const SLA_GLOBAL double* wd = gmem(wdot + s * n);
   const Gather<false, (NB < 0)> g{xs, nullptr, 0.0};
   const int w = wave_index();
   const uint32_t lane = lane_id();
   const int64_t stride = int64_t(gridDim.x) * kWaves;
   int64_t t = int64_t(blockIdx.x) * kWaves + w;
+  double d0 = 0.0, d1 = 0.0;
   // each tile's index data is loaded one tile ahead
   TileIndex<RP> ix{};
   if (t < tiles) ix = tile_index<NB, RP>(rowptr, mask, n, t * kTileRows, tile_lane(t * kTileRows, n, lane));
@@ -320,6 +328,21 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
     if constexpr (NB > 0) acc = band_row<NB, RP>(band, v, n, nnz, r0, lr, ok, cur, g);
     else acc = wave_tile_row<RP>(col, v, cur, cap, lv, lc, g);
     st(ys + r0, lr, acc);
+    if constexpr (ND > 0) {
+      // lanes past the last row repeat the tile's last row: counted once
+      const double wi = ld(wd + r0, lr);
+      d0 = d0 + (ok ? wi * acc : 0.0);
+      if constexpr (ND > 1) d1 = d1 + (ok ? acc * acc : 0.0);
+    }
+  }
+  if constexpr (ND > 0) {
+    __shared__ double red[kWaves];
+    d0 = block_sum_all<kIterBlock>(d0, red);
+    if constexpr (ND > 1) d1 = block_sum_all<kIterBlock>(d1, red);
+    if (threadIdx.x == 0) {
+      part[s * pstride + int64_t(set0) * gridDim.x + blockIdx.x] = d0;
+      if constexpr (ND > 1) part[s * pstride + int64_t(set1) * gridDim.x + blockIdx.x] = d1;
+    }
   }
 }
 
@@ -1323,28 +1346,47 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x, double* y,
-                       hipStream_t st) {
+template <int ND>
+static sla_status launch_spmv_nd(sla_csr A, const double* vals, int64_t batch, const double* x,
+                                 double* y, const double* wdot, double* part, int64_t pstride,
+                                 int set0, int set1, hipStream_t st) {
   const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
   const size_t lds = lds_bytes(A);
   const int nb = band_class(A);
   if (A->rp_idx == SLA_I32) {
-    auto k = nb == 3 ? k_spmv<int32_t, 3>
-             : nb == 5 ? k_spmv<int32_t, 5>
-             : nb == 8 ? k_spmv<int32_t, 8>
-             : nb == 0 ? k_spmv<int32_t, 0> : k_spmv<int32_t, -1>;
+    auto k = nb == 3 ? k_spmv<int32_t, 3, ND>
+             : nb == 5 ? k_spmv<int32_t, 5, ND>
+             : nb == 8 ? k_spmv<int32_t, 8, ND>
+             : nb == 0 ? k_spmv<int32_t, 0, ND> : k_spmv<int32_t, -1, ND>;
     k<<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->band_mask, A->band,
-                                     vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y);
+                                     vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y, wdot, part,
+                                     pstride, set0, set1);
   } else {
-    auto k = nb == 3 ? k_spmv<int64_t, 3>
-             : nb == 5 ? k_spmv<int64_t, 5>
-             : nb == 8 ? k_spmv<int64_t, 8>
-             : nb == 0 ? k_spmv<int64_t, 0> : k_spmv<int64_t, -1>;
+    auto k = nb == 3 ? k_spmv<int64_t, 3, ND>
+             : nb == 5 ? k_spmv<int64_t, 5, ND>
+             : nb == 8 ? k_spmv<int64_t, 8, ND>
+             : nb == 0 ? k_spmv<int64_t, 0, ND> : k_spmv<int64_t, -1, ND>;
     k<<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->band_mask, A->band,
-                                     vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y);
+                                     vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y, wdot, part,
+                                     pstride, set0, set1);
   }
   LAUNCH_CHECK();
   return SLA_OK;
+}
+
+sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x, double* y,
+                       hipStream_t st) {
+  return launch_spmv_nd<0>(A, vals, batch, x, y, nullptr, nullptr, 0, 0, 0, st);
+}
+
+int64_t spmv_groups(const sla_csr A, int64_t batch) { return plain_grid(A->tiles, batch); }
+
+sla_status launch_spmv_dots(sla_csr A, const double* vals, int64_t batch, const double* x,
+                            double* y, const double* wdot, int nd, double* part, int64_t pstride,
+                            int set0, int set1, hipStream_t st) {
+  if (nd == 1)
+    return launch_spmv_nd<1>(A, vals, batch, x, y, wdot, part, pstride, set0, set1, st);
+  return launch_spmv_nd<2>(A, vals, batch, x, y, wdot, part, pstride, set0, set1, st);
 }
 
 sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const double* x,

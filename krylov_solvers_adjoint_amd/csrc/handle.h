@@ -106,6 +106,13 @@ sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 
 sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x,
                        double* y, hipStream_t stream);
+// y = A x plus per-workgroup partials of wdot.y (nd = 1) and of y.y (nd = 2)
+// in part[system * pstride + set * groups + workgroup], groups =
+// spmv_groups(A, batch)
+sla_status launch_spmv_dots(sla_csr A, const double* vals, int64_t batch, const double* x,
+                            double* y, const double* wdot, int nd, double* part, int64_t pstride,
+                            int set0, int set1, hipStream_t stream);
+int64_t spmv_groups(const sla_csr A, int64_t batch);
 sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda,
                                const double* x, double* grad_vals, hipStream_t stream);
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,

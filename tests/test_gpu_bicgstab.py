@@ -118,9 +118,22 @@ def test_fixed_iterations_and_warm_start():
     N = 64
     rp, c, v = W.convection_diffusion_csr(N)
     b = W.normal_rhs(N * N, 92)
-    _, _, x, info, xo, io, _ = _solve_both(rp, c, v, b, 0.0, 20)
+    # 20 iterations are launched one by one: x against the oracle
+    P, _, x, info, xo, io, _ = _solve_both(rp, c, v, b, 0.0, 20)
     assert info.iterations == 20 == io.iterations and not info.converged
     assert rel(x, xo) <= TOL_X
+    h20 = K.sla_bicgstab_history(P)
+    # 40 and 45 run as graph-captured blocks of 16 iterations, the last block
+    # cut short by the limit: the same kernels in the same order, so the
+    # first 20 iterations' scalars are the direct launches' bit for bit (past
+    # ~30 iterations rounding alone separates BiCGStab trajectories, so the
+    # unconverged x is not compared with the oracle there)
+    for m in (40, 45):
+        P, _, x, info, xo, io, _ = _solve_both(rp, c, v, b, 0.0, m)
+        assert info.iterations == m == io.iterations and not info.converged
+        h = K.sla_bicgstab_history(P)
+        for a_, b_ in zip(h, h20):
+            assert len(a_) == m and np.array_equal(a_[:20], b_)
     x0 = W.uniform_rhs(N * N, 93)
     _, _, x, info, xo, io, _ = _solve_both(rp, c, v, b, 1e-9, 1000, x0=x0)
     assert info.converged and iters_close(info.iterations, io.iterations)
