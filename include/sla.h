@@ -337,6 +337,38 @@ sla_status sla_bicgstab_history(sla_csr A, int64_t system, double* rho_host,
                                 int64_t cap, int64_t* count_host);
 
 /*
+ * Lists of independent systems, each with its own pattern and size (the
+ * SparseTensorList of Methodology 1: distinct patterns per batch item).
+ * A[i] is a handle with exactly one system bound; no handle may appear
+ * twice.  method SLA_METHOD_CG (SPD systems; flags as sla_cg_solve, so
+ * SLA_FLAG_JACOBI too) or SLA_METHOD_BICGSTAB (flags as sla_bicgstab_solve).
+ * Every system is solved exactly as by the single-system call on its
+ * handle (the same kernels and bits); up to 8 systems run at once, each on
+ * a worker stream of the library's (created once per device, default
+ * priority) that first waits for the work already queued on `stream`.
+ * Host arrays of device pointers: b[i], x[i] [n_i].  info_host [count]
+ * (may be NULL).  Returns the first failing system's status (its message
+ * names the system).  Returns when every system is done.
+ */
+enum { SLA_METHOD_CG = 0, SLA_METHOD_BICGSTAB = 1 };
+sla_status sla_solve_list(int64_t count, const sla_csr* A, const double* const* b,
+                          double* const* x, double tol, int64_t maxit, uint32_t flags, int method,
+                          sla_cg_info* info_host, hipStream_t stream);
+
+/*
+ * Backward pass of sla_solve_list (Methodology 2, linear systems, per
+ * system): grad_b[i] = lambda_i solving A_i^T lambda_i = grad_x[i], and
+ * grad_vals[i][k] = -lambda_i x_j on the stored slots of A_i.  grad_vals
+ * (the array) may be NULL, and so may any of its entries (that system's
+ * values gradient is then not formed).  flags: SLA_FLAG_HISTORY, and
+ * SLA_FLAG_JACOBI for CG.
+ */
+sla_status sla_adjoint_list(int64_t count, const sla_csr* A, const double* const* x,
+                            const double* const* grad_x, double* const* grad_b,
+                            double* const* grad_vals, double tol, int64_t maxit, uint32_t flags,
+                            int method, sla_cg_info* info_host, hipStream_t stream);
+
+/*
  * Measurement aid for sla_eigsh: after an sla_eigsh call on this handle with
  * m >= nvec, launch the Gram-Schmidt dot pass (V_nvec^T w plus w.w) and the
  * update pass (w -= V_nvec h) over the first nvec basis vectors `reps`

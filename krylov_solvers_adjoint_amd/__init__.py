@@ -29,6 +29,7 @@ __all__ = [
     "sla_cg_solve_batched", "sla_cg_adjoint_batched", "sla_pattern_grad",
     "sla_spmv_transpose", "sla_matvec_grad", "sla_eigsh", "sla_eig_grad", "EigInfo",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
+    "sla_solve_list", "sla_adjoint_list", "SparseTensorList",
     "LIB_PATH", "EXPORTS",
 ]
 
@@ -37,6 +38,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 (OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE, ERR_KRYLOV,
  ERR_BREAKDOWN) = range(9)
 EIG_SMALLEST, EIG_LARGEST = 0, 1
+METHOD_CG, METHOD_BICGSTAB = 0, 1
 I32, I64 = 4, 8
 FLAG_X0, FLAG_HISTORY, FLAG_JACOBI = 1, 2, 4
 
@@ -50,6 +52,7 @@ EXPORTS = [
     "sla_csr_set_workgroups_per_cu", "sla_spmv_transpose", "sla_matvec_grad",
     "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
+    "sla_solve_list", "sla_adjoint_list",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -106,6 +109,8 @@ def _bind(lib):
         "sla_bicgstab_solve": [_P, _P, _P, _D, _I64, _U32, _P, _P],
         "sla_bicgstab_adjoint": [_P, _P, _P, _P, _P, _D, _I64, _U32, _P, _P],
         "sla_bicgstab_history": [_P, _I64, _P, _P, _P, _P, _I64, ctypes.POINTER(_I64)],
+        "sla_solve_list": [_I64, _P, _P, _P, _D, _I64, _U32, _S, _P, _P],
+        "sla_adjoint_list": [_I64, _P, _P, _P, _P, _P, _D, _I64, _U32, _S, _P, _P],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
     }
     for name, args in sig.items():
@@ -502,6 +507,77 @@ def sla_bicgstab_history(A: CSRPattern, system: int = 0, cap: int = 1 << 20):
     return tuple(o[:k] for o in out)
 
 
+_METHODS = {"cg": METHOD_CG, "bicgstab": METHOD_BICGSTAB}
+
+
+def _ptr_array(items):
+    arr = (_P * len(items))()
+    for i, it in enumerate(items):
+        arr[i] = it
+    return arr
+
+
+def _list_prepare(patterns, values, method):
+    if method not in _METHODS:
+        raise ValueError(f"unknown method {method!r}")
+    if not (len(patterns) == len(values)) or not patterns:
+        raise ValueError("patterns and values must be non-empty lists of one length")
+    if len({id(P) for P in patterns}) != len(patterns):
+        raise ValueError("a pattern appears twice in the list (use a batched SparseTensor)")
+    for P, v in zip(patterns, values):
+        if v.dim() != 1 or P.bind(v) != 1:
+            raise ValueError("each list item binds exactly one system ([nnz] values)")
+    return _ptr_array([P.handle for P in patterns])
+
+
+def sla_solve_list(patterns: list, values: list, bs: list, tol: float, maxit: int,
+                   method: str = "cg", jacobi: bool = False, stream=None, check: bool = True):
+    """Solve a list of systems with distinct patterns (SparseTensorList):
+    ([x_i], [CGInfo_i]).  Every system runs exactly as its single solve."""
+    handles = _list_prepare(patterns, values, method)
+    xs = []
+    for P, b in zip(patterns, bs):
+        _shape(b, (P.n,), "b")
+        _dev(b, torch.float64, "b")
+        xs.append(torch.empty_like(b))
+    infos = (_Info * len(patterns))()
+    st = _lib.sla_solve_list(len(patterns), handles, _ptr_array([b.data_ptr() for b in bs]),
+                             _ptr_array([x.data_ptr() for x in xs]), float(tol), int(maxit),
+                             _flags(None, False, jacobi), _METHODS[method], infos,
+                             _stream(stream))
+    if check:
+        _check(st)
+    return xs, _infos(infos)
+
+
+def sla_adjoint_list(patterns: list, values: list, xs: list, grad_xs: list, tol: float,
+                     maxit: int, method: str = "cg", want_vals=True, jacobi: bool = False,
+                     stream=None, check: bool = True):
+    """Backward of sla_solve_list: ([grad_b_i], [grad_vals_i or None], [CGInfo_i]).
+    want_vals: one bool for all systems or a list of bools."""
+    handles = _list_prepare(patterns, values, method)
+    count = len(patterns)
+    wv = want_vals if isinstance(want_vals, (list, tuple)) else [want_vals] * count
+    gbs, gvs = [], []
+    for P, x, g, w in zip(patterns, xs, grad_xs, wv):
+        _shape(g, (P.n,), "grad_x")
+        _shape(x, (P.n,), "x")
+        _dev(g, torch.float64, "grad_x")
+        _dev(x, torch.float64, "x")
+        gbs.append(torch.empty_like(g))
+        gvs.append(torch.empty(P.nnz, dtype=torch.float64, device=g.device) if w else None)
+    infos = (_Info * count)()
+    st = _lib.sla_adjoint_list(count, handles, _ptr_array([x.data_ptr() for x in xs]),
+                               _ptr_array([g.data_ptr() for g in grad_xs]),
+                               _ptr_array([g.data_ptr() for g in gbs]),
+                               _ptr_array([g.data_ptr() if g is not None else None for g in gvs]),
+                               float(tol), int(maxit), _flags(None, False, jacobi),
+                               _METHODS[method], infos, _stream(stream))
+    if check:
+        _check(st)
+    return gbs, gvs, _infos(infos)
+
+
 def _adjoint_call(fn, A, x, grad_x, tol, maxit, want_vals, flags, batch, stream, check):
     _shape(grad_x, _vec_shape(A, batch, grad_x), "grad_x")
     _shape(x, _vec_shape(A, batch, grad_x), "x")
@@ -620,6 +696,36 @@ class _BiCGStabSolve(torch.autograd.Function):
         return gv, gb, None, None, None
 
 
+class _ListSolve(torch.autograd.Function):
+    """[x_i = A_i^{-1} b_i] for a list of systems with distinct patterns; one
+    graph node; backward solves every adjoint system in one list call."""
+
+    @staticmethod
+    def forward(ctx, meta, *tensors):
+        patterns, tol, maxit, method, jacobi = meta
+        count = len(patterns)
+        values = [t.detach().contiguous() for t in tensors[:count]]
+        bs = [t.detach().contiguous() for t in tensors[count:]]
+        xs, infos = sla_solve_list(patterns, values, bs, tol, maxit, method, jacobi)
+        ctx.meta = meta
+        ctx.infos = infos
+        ctx.save_for_backward(*values, *xs)
+        return tuple(xs)
+
+    @staticmethod
+    def backward(ctx, *grad_xs):
+        patterns, tol, maxit, method, jacobi = ctx.meta
+        count = len(patterns)
+        saved = ctx.saved_tensors
+        values, xs = list(saved[:count]), list(saved[count:])
+        gx = [g.contiguous() if g is not None else torch.zeros_like(x)
+              for g, x in zip(grad_xs, xs)]
+        want = [ctx.needs_input_grad[1 + i] for i in range(count)]
+        gbs, gvs, _ = sla_adjoint_list(patterns, values, xs, gx, tol, maxit, method, want,
+                                       jacobi)
+        return (None, *gvs, *gbs)
+
+
 class _MatVec(torch.autograd.Function):
     """y = A x; backward grad_x = A^T g, grad_vals = g_i x_j on the pattern."""
 
@@ -711,6 +817,39 @@ class SparseTensor:
             shape = (self.values.shape[0], n) if self.values.dim() == 2 else (n,)
             v0 = torch.randn(shape, generator=g, dtype=torch.float64).to(self.values.device)
         return _EigSH.apply(self.values, self.pattern, int(k), which, int(m), v0)
+
+
+class SparseTensorList:
+    """A list of sparse matrices with distinct patterns (and sizes): the
+    ragged counterpart of a batched SparseTensor.  ``.solve`` solves all of
+    them in one call of the library (up to 8 at once on the GPU) and is one
+    autograd node; each item's values and right-hand side get gradients."""
+
+    def __init__(self, tensors: list):
+        if not tensors:
+            raise ValueError("empty list")
+        if len({id(t.pattern) for t in tensors}) != len(tensors):
+            raise ValueError("every item needs a pattern of its own")
+        self.tensors = list(tensors)
+
+    def __len__(self):
+        return len(self.tensors)
+
+    def __getitem__(self, i):
+        return self.tensors[i]
+
+    def solve(self, bs: list, tol: float = 1e-10, maxit: int = 10000, method: str = "cg",
+              precond: str | None = None) -> list:
+        if len(bs) != len(self.tensors):
+            raise ValueError("one right-hand side per matrix")
+        if precond not in (None, "jacobi") or (precond and method != "cg"):
+            raise ValueError(f"preconditioner {precond!r} not available for {method}")
+        meta = ([t.pattern for t in self.tensors], float(tol), int(maxit), method,
+                precond == "jacobi")
+        return list(_ListSolve.apply(meta, *[t.values for t in self.tensors], *bs))
+
+    def matvec(self, xs: list) -> list:
+        return [t.matvec(x) for t, x in zip(self.tensors, xs)]
 
 
 def solve(A: SparseTensor, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,

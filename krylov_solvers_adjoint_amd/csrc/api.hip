@@ -4,9 +4,14 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <new>
+#include <set>
+#include <string>
+#include <thread>
+#include <vector>
 
 #include "handle.h"
 
@@ -358,15 +363,11 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol, int64
   API_END
 }
 
-sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad_x,
-                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
-                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
-  API_BEGIN
-  clear_error();
-  SLA_TRY(check_solve(A, grad_x, grad_b, tol, maxit, flags, "sla_cg_adjoint"));
-  REQUIRE((flags & SLA_FLAG_X0) == 0, "sla_cg_adjoint: SLA_FLAG_X0 is not supported");
-  REQUIRE(grad_vals == nullptr || x != nullptr, "sla_cg_adjoint: grad_vals needs x");
-  // A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix)
+// A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix), then
+// the pattern gradient (also from the last iterate after a breakdown).
+static sla_status run_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
+                                 double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                                 uint32_t flags, sla_cg_info* info, hipStream_t stream) {
   sla_status s = run_cg(A, grad_x, grad_b, tol, maxit, flags, info, stream);
   if (grad_vals != nullptr && (s == SLA_OK || s == SLA_ERR_NOT_SPD || s == SLA_ERR_NONFINITE)) {
     sla_status g = launch_pattern_grad(A, A->batch, grad_b, x, grad_vals, stream);
@@ -377,6 +378,159 @@ sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad
     }
   }
   return s;
+}
+
+sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad_x,
+                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
+                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_solve(A, grad_x, grad_b, tol, maxit, flags, "sla_cg_adjoint"));
+  REQUIRE((flags & SLA_FLAG_X0) == 0, "sla_cg_adjoint: SLA_FLAG_X0 is not supported");
+  REQUIRE(grad_vals == nullptr || x != nullptr, "sla_cg_adjoint: grad_vals needs x");
+  return run_cg_adjoint(A, x, grad_x, grad_b, grad_vals, tol, maxit, flags, info, stream);
+  API_END
+}
+
+// ---------------------------------------------------------------------------
+// Lists of systems with their own patterns (SparseTensorList)
+// ---------------------------------------------------------------------------
+
+extern "C++" {
+// Worker streams, created once per device and kept for the process.
+static constexpr int kListWorkers = 8;
+static sla_status list_streams(int device, hipStream_t* out) {
+  static std::mutex mu;
+  static std::map<int, std::vector<hipStream_t>> pools;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& v = pools[device];
+  while (int(v.size()) < kListWorkers) {
+    hipStream_t st = nullptr;
+    SLA_TRY_HIP(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    v.push_back(st);
+  }
+  for (int i = 0; i < kListWorkers; ++i) out[i] = v[size_t(i)];
+  return SLA_OK;
+}
+
+// Runs one(i, stream, &info[i]) for i < count on up to kListWorkers host
+// threads, each with a stream of its own that first waits for the work
+// queued on `stream`; returns when every system is done.  A failing system's
+// status and message are reported for the first such i.
+template <typename F>
+static sla_status run_list(int64_t count, sla_cg_info* info, hipStream_t stream, F&& one) {
+  int device = 0;
+  SLA_TRY_HIP(hipGetDevice(&device));
+  hipStream_t streams[kListWorkers];
+  SLA_TRY(list_streams(device, streams));
+  hipEvent_t ready = nullptr;
+  SLA_TRY_HIP(hipEventCreateWithFlags(&ready, hipEventDisableTiming));
+  if (hipEventRecord(ready, stream) != hipSuccess) {
+    (void)hipEventDestroy(ready);
+    set_error("solve list: event record failed");
+    return SLA_ERR_DEVICE;
+  }
+  const int workers = int(count < kListWorkers ? count : kListWorkers);
+  std::atomic<int64_t> next{0};
+  const size_t cnt = static_cast<size_t>(count);
+  std::vector<sla_status> status(cnt, SLA_OK);
+  std::vector<std::string> message(cnt);
+  std::vector<sla_cg_info> local(cnt);
+  std::vector<std::thread> pool;
+  for (int w = 0; w < workers; ++w) {
+    pool.emplace_back([&, w]() {
+      hipStream_t st = streams[w];
+      bool ok = hipSetDevice(device) == hipSuccess && hipStreamWaitEvent(st, ready, 0) == hipSuccess;
+      for (;;) {
+        const int64_t i = next.fetch_add(1);
+        if (i >= count) break;
+        if (!ok) {
+          status[size_t(i)] = SLA_ERR_DEVICE;
+          message[size_t(i)] = "worker stream set-up failed";
+          continue;
+        }
+        clear_error();
+        sla_status s = SLA_ERR_DEVICE;
+        try {
+          s = one(i, st, &local[size_t(i)]);
+        } catch (...) {
+          set_error("unexpected exception");
+        }
+        status[size_t(i)] = s;
+        if (s != SLA_OK) message[size_t(i)] = sla_last_error();
+      }
+      (void)hipStreamSynchronize(st);
+    });
+  }
+  for (auto& t : pool) t.join();
+  (void)hipEventDestroy(ready);
+  if (info)
+    for (int64_t i = 0; i < count; ++i) info[i] = local[size_t(i)];
+  for (int64_t i = 0; i < count; ++i)
+    if (status[size_t(i)] != SLA_OK) {
+      set_error("system %lld: %s", (long long)i, message[size_t(i)].c_str());
+      return status[size_t(i)];
+    }
+  clear_error();
+  return SLA_OK;
+}
+
+static sla_status check_list(int64_t count, const sla_csr* A, int method, uint32_t flags,
+                             const char* who) {
+  REQUIRE(count >= 1 && A != nullptr, "%s: empty list", who);
+  REQUIRE(method == SLA_METHOD_CG || method == SLA_METHOD_BICGSTAB, "%s: unknown method %d", who,
+          method);
+  REQUIRE(method == SLA_METHOD_CG || (flags & SLA_FLAG_JACOBI) == 0,
+          "%s: BiCGStab takes no preconditioner", who);
+  std::set<const void*> seen;
+  for (int64_t i = 0; i < count; ++i) {
+    REQUIRE(A[i] != nullptr, "%s: handle %lld is NULL", who, (long long)i);
+    REQUIRE(A[i]->batch == 1, "%s: handle %lld must have exactly one system bound", who,
+            (long long)i);
+    REQUIRE(seen.insert(A[i]).second, "%s: handle %lld appears twice", who, (long long)i);
+  }
+  return SLA_OK;
+}
+}  // extern "C++"
+
+sla_status sla_solve_list(int64_t count, const sla_csr* A, const double* const* b,
+                          double* const* x, double tol, int64_t maxit, uint32_t flags, int method,
+                          sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_list(count, A, method, flags, "sla_solve_list"));
+  REQUIRE(b != nullptr && x != nullptr, "sla_solve_list: NULL vector array");
+  for (int64_t i = 0; i < count; ++i)
+    SLA_TRY(check_solve(A[i], b[i], x[i], tol, maxit, flags, "sla_solve_list"));
+  return run_list(count, info, stream, [&](int64_t i, hipStream_t st, sla_cg_info* in) {
+    return method == SLA_METHOD_CG ? run_cg(A[i], b[i], x[i], tol, maxit, flags, in, st)
+                                   : run_bicgstab(A[i], b[i], x[i], tol, maxit, flags, in, st);
+  });
+  API_END
+}
+
+sla_status sla_adjoint_list(int64_t count, const sla_csr* A, const double* const* x,
+                            const double* const* grad_x, double* const* grad_b,
+                            double* const* grad_vals, double tol, int64_t maxit, uint32_t flags,
+                            int method, sla_cg_info* info, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  SLA_TRY(check_list(count, A, method, flags, "sla_adjoint_list"));
+  REQUIRE((flags & SLA_FLAG_X0) == 0, "sla_adjoint_list: SLA_FLAG_X0 is not supported");
+  REQUIRE(grad_x != nullptr && grad_b != nullptr, "sla_adjoint_list: NULL vector array");
+  for (int64_t i = 0; i < count; ++i) {
+    SLA_TRY(check_solve(A[i], grad_x[i], grad_b[i], tol, maxit, flags, "sla_adjoint_list"));
+    REQUIRE(grad_vals == nullptr || grad_vals[i] == nullptr || (x != nullptr && x[i] != nullptr),
+            "sla_adjoint_list: grad_vals needs x");
+  }
+  return run_list(count, info, stream, [&](int64_t i, hipStream_t st, sla_cg_info* in) {
+    double* gv = grad_vals ? grad_vals[i] : nullptr;
+    const double* xi = x ? x[i] : nullptr;
+    return method == SLA_METHOD_CG
+               ? run_cg_adjoint(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in, st)
+               : run_bicgstab_adjoint(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in,
+                                      st);
+  });
   API_END
 }
 

@@ -61,6 +61,9 @@ def test_argument_errors_need_no_gpu():
                                     None) == K.ERR_ARG
     assert lib.sla_bicgstab_history(None, 0, None, None, None, None, 0, None) == K.ERR_ARG
     assert lib.sla_status_string(K.ERR_BREAKDOWN) == b"SLA_ERR_BREAKDOWN"
+    assert lib.sla_solve_list(0, None, None, None, 1e-8, 10, 0, 0, None, None) == K.ERR_ARG
+    assert lib.sla_adjoint_list(0, None, None, None, None, None, 1e-8, 10, 0, 0, None,
+                                None) == K.ERR_ARG
     assert lib.sla_csr_set_graph_block(None, 32) == K.ERR_ARG
     assert lib.sla_status_string(K.ERR_NOT_SPD) == b"SLA_ERR_NOT_SPD"
     assert lib.sla_csr_destroy(None) == K.OK
