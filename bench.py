@@ -485,6 +485,45 @@ def bench_bicgstab():
     return out
 
 
+def bench_list(count: int = 32):
+    """SparseTensorList: `count` Poisson systems with distinct grids (N = 100,
+    110, ..., 410: distinct patterns and sizes), CG to tol 1e-8, solved as one
+    list call (up to 8 at once) and one after another."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    Ps, vals, bs = [], [], []
+    for i in range(count):
+        N = 100 + 10 * i
+        rp, c, v = W.poisson_csr(N)
+        Ps.append(K.sla_csr_create_from_csr(torch.from_numpy(rp).to(dev),
+                                            torch.from_numpy(c).to(dev)))
+        vals.append(torch.from_numpy(v).to(dev))
+        bs.append(torch.from_numpy(W.uniform_rhs(N * N, i)).to(dev))
+    K.sla_solve_list(Ps, vals, bs, 1e-8, 20000)  # workspaces, graphs
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    xs, infos = K.sla_solve_list(Ps, vals, bs, 1e-8, 20000)
+    torch.cuda.synchronize()
+    t_list = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for P, v, b in zip(Ps, vals, bs):
+        K.sla_cg_solve(P, v, b, 1e-8, 20000)
+    torch.cuda.synchronize()
+    t_seq = time.perf_counter() - t0
+    its = sum(i.iterations for i in infos)
+    out = dict(systems=count, unknowns=int(sum(P.n for P in Ps)), iterations=its,
+               list_ms=1e3 * t_list, sequential_ms=1e3 * t_seq,
+               systems_per_s=count / t_list, speedup=t_seq / t_list,
+               all_converged=all(i.converged for i in infos))
+    del Ps, vals, bs, xs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(seconds: float):
     """The oracle as it stands, on a bounded sample of the same workload:
     forward and adjoint CG on the 1000 x 1000 Poisson system, k fixed
@@ -570,6 +609,9 @@ def main():
             if s.lower() == "matvec":
                 log(f"[bench] matvec: {bench_matvec(args.kernel_reps)}")
                 continue
+            if s.lower() == "list":
+                log(f"[bench] list: {bench_list()}")
+                continue
             if s.lower() == "bicgstab":
                 log(f"[bench] bicgstab: {bench_bicgstab()}")
                 continue
@@ -617,6 +659,9 @@ def main():
         log("[bench] BiCGStab on convection-diffusion 1000x1000, tol 1e-8, fwd + adj")
         nxt["bicgstab"] = bench_bicgstab()
         log(f"[bench] BiCGStab: {nxt['bicgstab']}")
+        log("[bench] SparseTensorList: 32 Poisson grids 100^2 .. 410^2, CG tol 1e-8")
+        nxt["list"] = bench_list()
+        log(f"[bench] list: {nxt['list']}")
 
     digest = source_digest()
     spmv_ms = head["kernel_ms"]["spmv_step"]
