@@ -473,8 +473,15 @@ def bench_bicgstab():
     variant = "banded" if P.banded else "csr"
     its = fi[0].iterations + ai[0].iterations
     nb = its * bicgstab_bytes(n, P.nnz, variant)
+    bpi = bicgstab_bytes(n, P.nnz, variant)
+    achieved = bpi / ((fwd + adj) / its) / 1e9
     out = dict(n=n, nnz=P.nnz, spmv=variant, iterations_fwd=fi[0].iterations,
                iterations_adj=ai[0].iterations, solve_ms=1e3 * fwd, adjoint_ms=1e3 * adj,
+               roofline=dict(bound="hbm", kernel="the whole iteration (2 SpMVs with fused dot "
+                             "partials + 3 vector kernels, graph-replayed)",
+                             achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                             frac=achieved / HBM_PEAK_GBPS, traffic=None,
+                             algorithmic_bytes=bpi),
                it_per_s=its / (fwd + adj), us_per_iteration=1e6 * (fwd + adj) / its,
                eff_GBps=nb / (fwd + adj) / 1e9, bytes_per_iteration=bicgstab_bytes(n, P.nnz,
                                                                                     variant),
@@ -521,6 +528,75 @@ def bench_list(count: int = 32):
     del Ps, vals, bs, xs
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return out
+
+
+def _oracle_threads():
+    import oracle
+    threads = min(os.cpu_count() or 1, 16)
+    oracle.set_threads(threads)
+    return oracle.get_threads()
+
+
+def oracle_next(nxt: dict):
+    """The oracle beside each NEXT leg, on bounded samples of the same
+    workloads (a few seconds each), in the legs' own units."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    cores = _oracle_threads()
+    N = 1000
+    n = N * N
+    out = {}
+    if "matvec" in nxt:
+        rp, c, v = W.poisson_csr(N, np.int64)
+        A = oracle.CSR(n, rp, c, v)
+        x = W.normal_rhs(n, 2)
+        t0 = time.perf_counter()
+        for _ in range(100):
+            oracle.spmv(A, x)
+        fwd = (time.perf_counter() - t0) / 100
+        t0 = time.perf_counter()
+        for _ in range(20):
+            oracle.matvec_grad(A, x, x)
+        bwd = (time.perf_counter() - t0) / 20
+        out["matvec"] = dict(spmv_ms=1e3 * fwd, backward_ms=1e3 * bwd, cores=cores,
+                             kind="oracle", sample="100 y = A x and 20 backward passes "
+                             "(explicit transpose each), Poisson 1000^2")
+    if "eigsh" in nxt:
+        rp, c, v = W.poisson_csr(N, np.int64)
+        A = oracle.CSR(n, rp, c, v)
+        m = 60
+        t0 = time.perf_counter()
+        oracle.lanczos(A, W.normal_rhs(n, 72), m)
+        dt = time.perf_counter() - t0
+        out["eigsh"] = dict(steps_per_s=m / dt, cores=cores, kind="oracle",
+                            sample=f"{m} Lanczos steps (two Gram-Schmidt passes), Poisson "
+                                   f"1000^2, {dt:.1f} s; the cost per step grows with the "
+                                   "step index, so the 300-step rate is lower still")
+    if "bicgstab" in nxt:
+        rp, c, v = W.convection_diffusion_csr(N, rowptr_dtype=np.int64)
+        A = oracle.CSR(n, rp, c, v)
+        k = 500
+        t0 = time.perf_counter()
+        oracle.bicgstab(A, W.normal_rhs(n, 90), 0.0, k)
+        dt = time.perf_counter() - t0
+        out["bicgstab"] = dict(it_per_s=k / dt, cores=cores, kind="oracle",
+                               sample=f"{k} BiCGStab iterations, convection-diffusion 1000^2, "
+                                      f"{dt:.1f} s")
+    if "list" in nxt:
+        t0 = time.perf_counter()
+        its = 0
+        for i in range(8):
+            Nl = 100 + 10 * i
+            rp, c, v = W.poisson_csr(Nl, np.int64)
+            _, info = oracle.cg(oracle.CSR(Nl * Nl, rp, c, v), W.uniform_rhs(Nl * Nl, i), 1e-8,
+                                20000)
+            its += info.iterations
+        dt = time.perf_counter() - t0
+        out["list"] = dict(systems_per_s=8 / dt, cores=cores, kind="oracle",
+                           sample=f"the first 8 systems of the list (100^2 .. 170^2), "
+                                  f"{its} CG iterations, {dt:.2f} s")
     return out
 
 
@@ -678,6 +754,10 @@ def main():
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         cpu = cpu_baseline(args.cpu_seconds)
+        if nxt:
+            log("[bench] CPU oracle beside the NEXT legs")
+            for key, val in oracle_next(nxt).items():
+                nxt[key]["cpu_oracle"] = val
     line = {
         "metric": METRIC,
         "value": head["it_per_s"],

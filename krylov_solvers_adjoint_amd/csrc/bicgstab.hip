@@ -105,13 +105,67 @@ __device__ __forceinline__ void put_partial(double* part, double v, double* red)
   if (threadIdx.x == 0) part[blockIdx.x] = v;
 }
 
+constexpr int kBsWaves = kBsBlock / kWave;
+
+// K sets of G partials summed in one pass: the same order as K calls of
+// sum_set (each thread's strided terms, a wave butterfly, the waves in
+// order).  Thread k adds set k's wave sums and broadcasts the total through
+// LDS.  red holds K * (kBsWaves + 1) doubles.
+template <int K>
+__device__ __forceinline__ void sum_sets(const double* const (&p)[K], int64_t G, double* red,
+                                         double (&out)[K]) {
+  double a[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) a[k] = 0.0;
+  for (int64_t g = threadIdx.x; g < G; g += kBsBlock) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) a[k] = a[k] + p[k][g];
+  }
+  const int wave = int(threadIdx.x) / kWave;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    a[k] = wave_sum(a[k]);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[k * kBsWaves + wave] = a[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int k = int(threadIdx.x);
+    double t = 0.0;
+    for (int q = 0; q < kBsWaves; ++q) t = t + red[k * kBsWaves + q];
+    red[K * kBsWaves + k] = t;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) out[k] = red[K * kBsWaves + k];
+  __syncthreads();
+}
+
+// K per-workgroup partials written in one pass (same order as put_partial).
+template <int K>
+__device__ __forceinline__ void put_partials(double* const (&part)[K], const double (&v)[K],
+                                             double* red) {
+  const int wave = int(threadIdx.x) / kWave;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const double a = wave_sum(v[k]);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[k * kBsWaves + wave] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    const int k = int(threadIdx.x);
+    double t = 0.0;
+    for (int q = 0; q < kBsWaves; ++q) t = t + red[k * kBsWaves + q];
+    part[k][blockIdx.x] = t;
+  }
+}
+
 __device__ __forceinline__ double* hist_of(const BsArgs& a, int64_t sys) {
   return a.hist ? a.hist + sys * a.hist_cap * 4 : nullptr;
 }
 
 // r = b - A x0 (q holds A x0) or r = b with x = 0; rhat = r; p = v = 0;
 // partials of b.b, rhat.r, r.r.
-__global__ __launch_bounds__(kBsBlock) void k_bs_init(BsArgs a, const double* __restrict__ q,
+__global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) void k_bs_init(BsArgs a, const double* __restrict__ q,
                                                       int use_x0) {
   __shared__ double red[kBsBlock / kWave];
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
@@ -168,8 +222,7 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_init_scalars(BsArgs a, double t
 // Head of iteration j = jn: the stopping tests on r.r, rho = rhat.r, beta
 // and p = r + beta (p - omega v).  Launched once more after the last
 // iteration to close the solve (it then only tests).
-__global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a) {
-  __shared__ double red[kBsBlock / kWave];
+__global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) void k_bs_direction(BsArgs a) {
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
   if (sc->halted) return;
@@ -182,8 +235,10 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a) {
   const int64_t j = sc->jn, maxit = sc->maxit;
   const int64_t pos = 8 * j + PH_DIR;
   const double* part = a.part + sys * kBsSets * a.G;
-  const double rho = sum_set(part + P_RHR * a.G, a.G, red);
-  const double rr = sum_set(part + P_RR * a.G, a.G, red);
+  __shared__ double red2[2 * (kBsWaves + 1)];
+  double sums[2];
+  sum_sets<2>({part + P_RHR * a.G, part + P_RR * a.G}, a.G, red2, sums);
+  const double rho = sums[0], rr = sums[1];
   int32_t st = ST_RUNNING;
   if (!isfinite(rr)) st = ST_NONFINITE;
   else if (rr <= sc->stop) st = ST_CONVERGED;
@@ -207,7 +262,7 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_direction(BsArgs a) {
 }
 
 // alpha = rho / rhat.v; s = r - alpha v and the s.s partials.
-__global__ __launch_bounds__(kBsBlock) void k_bs_s(BsArgs a) {
+__global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) void k_bs_s(BsArgs a) {
   __shared__ double red[kBsBlock / kWave];
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
@@ -246,15 +301,17 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_s(BsArgs a) {
 // After t = A s: the half-step finish (s.s <= tol^2 b.b: x += alpha p), else
 // omega = t.s / t.t; x = (x + alpha p) + omega s; r = s - omega t; the
 // rhat.r and r.r partials of the next iteration.
-__global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a) {
-  __shared__ double red[kBsBlock / kWave];
+__global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) void k_bs_update(BsArgs a) {
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
   int64_t j;
   if (skip(sc, PH_UPD, &j)) return;
   const int64_t pos = 8 * j + PH_UPD;
   const double* part = a.part + sys * kBsSets * a.G;
-  const double ss = sum_set(part + P_SS * a.G, a.G, red);
+  __shared__ double red3[3 * (kBsWaves + 1)];
+  double sums[3];
+  sum_sets<3>({part + P_SS * a.G, part + P_TT * a.G, part + P_TS * a.G}, a.G, red3, sums);
+  const double ss = sums[0];
   if (!isfinite(ss)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) set_stop(sc, pos, ST_NONFINITE);
     return;
@@ -276,8 +333,7 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a) {
     }
     return;
   }
-  const double tt = sum_set(part + P_TT * a.G, a.G, red);
-  const double ts = sum_set(part + P_TS * a.G, a.G, red);
+  const double tt = sums[1], ts = sums[2];
   int32_t st = ST_RUNNING;
   if (!isfinite(tt) || !isfinite(ts)) st = ST_NONFINITE;
   else if (tt == 0.0) st = ST_BREAKDOWN;
@@ -297,8 +353,8 @@ __global__ __launch_bounds__(kBsBlock) void k_bs_update(BsArgs a) {
     rhr = rhr + a.rh[o + i] * ri;
     rr = rr + ri * ri;
   }
-  put_partial(a.part + (sys * kBsSets + P_RHR) * a.G, rhr, red);
-  put_partial(a.part + (sys * kBsSets + P_RR) * a.G, rr, red);
+  double* wpart = a.part + sys * kBsSets * a.G;
+  put_partials<2>({wpart + P_RHR * a.G, wpart + P_RR * a.G}, {rhr, rr}, red3);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     sc->it = j + 1;
     double* h = hist_of(a, sys);

@@ -336,12 +336,24 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
     }
   }
   if constexpr (ND > 0) {
-    __shared__ double red[kWaves];
-    d0 = block_sum_all<kIterBlock>(d0, red);
-    if constexpr (ND > 1) d1 = block_sum_all<kIterBlock>(d1, red);
+    // both sums in one pass: a wave sum each, one barrier, then thread 0
+    // adds the waves' sums in wave order
+    __shared__ double red[2][kWaves];
+    d0 = wave_sum(d0);
+    if constexpr (ND > 1) d1 = wave_sum(d1);
+    if (lane == 0) {
+      red[0][w] = d0;
+      if constexpr (ND > 1) red[1][w] = d1;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-      part[s * pstride + int64_t(set0) * gridDim.x + blockIdx.x] = d0;
-      if constexpr (ND > 1) part[s * pstride + int64_t(set1) * gridDim.x + blockIdx.x] = d1;
+      double a = 0.0, b = 0.0;
+      for (int q = 0; q < kWaves; ++q) {
+        a = a + red[0][q];
+        if constexpr (ND > 1) b = b + red[1][q];
+      }
+      part[s * pstride + int64_t(set0) * gridDim.x + blockIdx.x] = a;
+      if constexpr (ND > 1) part[s * pstride + int64_t(set1) * gridDim.x + blockIdx.x] = b;
     }
   }
 }
