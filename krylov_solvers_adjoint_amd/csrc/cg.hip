@@ -310,19 +310,21 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
   const Gather<false, (NB < 0)> g{xs, nullptr, 0.0};
   const int w = wave_index();
   const uint32_t lane = lane_id();
-  const int64_t stride = int64_t(gridDim.x) * kWaves;
-  int64_t t = int64_t(blockIdx.x) * kWaves + w;
+  // each XCD walks a contiguous eighth of the tiles (the grid is a multiple
+  // of kXcds), so a tile and the tiles its band reaches share one L2
+  const TileWalk walk = wave_walk(tiles, int(gridDim.x), int(blockIdx.x), kWaves, w);
+  int64_t t = walk.first;
   double d0 = 0.0, d1 = 0.0;
   // each tile's index data is loaded one tile ahead
   TileIndex<RP> ix{};
-  if (t < tiles) ix = tile_index<NB, RP>(rowptr, mask, n, t * kTileRows, tile_lane(t * kTileRows, n, lane));
-  for (; t < tiles; t += stride) {
+  if (t < walk.end) ix = tile_index<NB, RP>(rowptr, mask, n, t * kTileRows, tile_lane(t * kTileRows, n, lane));
+  for (; t < walk.end; t += walk.stride) {
     const int64_t r0 = t * kTileRows;
     const bool ok = r0 + lane < n;
     const uint32_t lr = tile_lane(r0, n, lane);
     const TileIndex<RP> cur = ix;
-    const int64_t tn = t + stride;
-    const int64_t tp = tn < tiles ? tn : t;  // unconditional load (see k_cg_spmv_lines)
+    const int64_t tn = t + walk.stride;
+    const int64_t tp = tn < walk.end ? tn : t;  // unconditional load (see k_cg_spmv_lines)
     ix = tile_index<NB, RP>(rowptr, mask, n, tp * kTileRows, tile_lane(tp * kTileRows, n, lane));
     double acc;
     if constexpr (NB > 0) acc = band_row<NB, RP>(band, v, n, nnz, r0, lr, ok, cur, g);
@@ -1358,11 +1360,18 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Workgroups per system of the plain SpMV: a multiple of kXcds (its tile
+// walk splits the tiles by XCD).
+static unsigned spmv_grid(int64_t tiles, int64_t batch) {
+  const unsigned g = plain_grid(tiles, batch);
+  return (g + kXcds - 1) / kXcds * kXcds;
+}
+
 template <int ND>
 static sla_status launch_spmv_nd(sla_csr A, const double* vals, int64_t batch, const double* x,
                                  double* y, const double* wdot, double* part, int64_t pstride,
                                  int set0, int set1, hipStream_t st) {
-  const dim3 grid(plain_grid(A->tiles, batch), unsigned(batch));
+  const dim3 grid(spmv_grid(A->tiles, batch), unsigned(batch));
   const size_t lds = lds_bytes(A);
   const int nb = band_class(A);
   if (A->rp_idx == SLA_I32) {
@@ -1391,7 +1400,7 @@ sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const doubl
   return launch_spmv_nd<0>(A, vals, batch, x, y, nullptr, nullptr, 0, 0, 0, st);
 }
 
-int64_t spmv_groups(const sla_csr A, int64_t batch) { return plain_grid(A->tiles, batch); }
+int64_t spmv_groups(const sla_csr A, int64_t batch) { return spmv_grid(A->tiles, batch); }
 
 sla_status launch_spmv_dots(sla_csr A, const double* vals, int64_t batch, const double* x,
                             double* y, const double* wdot, int nd, double* part, int64_t pstride,
