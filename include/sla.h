@@ -421,11 +421,13 @@ sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels_host);
  * one by one without graphs).  Affects speed only, never results. */
 sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
 
-/* Solver workgroups (1024 threads each) per compute unit: 2 (default, 32
- * waves per CU) or 1 (16 waves per CU, fewer DRAM pages open at once).
- * The grid sets the number and order of the dot-product partial sums, so
- * CG results differ in the last bits between the two settings; each setting
- * is reproducible.  SpMV results do not change. */
+/* Solver workgroups (1024 threads each) per compute unit: 0 (default:
+ * automatic, 1 for solves of at most 2^21 unknowns over the batch, where the
+ * kernels' fixed costs dominate, else 2), 1 (16 waves per CU, fewer DRAM
+ * pages open at once) or 2 (32 waves per CU).  The grid sets the number and
+ * order of the dot-product partial sums, so CG results differ in the last
+ * bits between grids; each setting is reproducible.  SpMV results do not
+ * change. */
 sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -679,7 +679,7 @@ sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups) {
   API_BEGIN
   clear_error();
   REQUIRE(A != nullptr, "sla_csr_set_workgroups_per_cu: NULL handle");
-  REQUIRE(workgroups == 1 || workgroups == 2, "sla_csr_set_workgroups_per_cu: must be 1 or 2");
+  REQUIRE(workgroups >= 0 && workgroups <= 2, "sla_csr_set_workgroups_per_cu: must be 0, 1 or 2");
   if (workgroups != A->wg_per_cu) {
     (void)hipDeviceSynchronize();
     release_workspace(A);  // the grid sizes the partial-sum arrays and the graphs

@@ -1336,7 +1336,11 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   const int64_t n = A->n;
   // solver grid: wg_per_cu workgroups per CU in total, a multiple of the XCD
   // count per system, never more than the wave tiles need (rounded up)
-  const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * A->wg_per_cu / batch);
+  // (automatic: one per CU up to kSmallSolve unknowns over the batch, where
+  // the kernels' fixed costs -- each workgroup summing the partials of the
+  // previous kernel -- weigh more than the latency hiding of a second one)
+  const int wg = A->wg_per_cu > 0 ? A->wg_per_cu : (A->n * batch <= kSmallSolve ? 1 : 2);
+  const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * wg / batch);
   int64_t g = std::min<int64_t>((A->tiles + kWaves - 1) / kWaves, target);
   g = (g + kXcds - 1) / kXcds * kXcds;
   A->grid = int32_t(std::max<int64_t>(g, kXcds));

@@ -83,6 +83,9 @@ constexpr int64_t kMinWalkLine = int64_t(kIterBlock / kWave - 1) * kTileRows + 1
 // a 64-row tile whose columns span more than this is "wide" (the span of a
 // 5-point stencil tile on a 13000-point grid line is ~26000)
 constexpr int64_t kLocalSpan = int64_t(1) << 17;
+// solves of at most this many unknowns (over the batch) run one solver
+// workgroup per CU unless the handle asks otherwise
+constexpr int64_t kSmallSolve = int64_t(1) << 21;
 
 // Column offsets j - i of a banded pattern, ascending: row i's slots are the
 // columns i + off[t] for the bits t set in its mask byte.

@@ -74,8 +74,8 @@ struct sla_csr_s {
 
   // graphs of `graph_block` iterations, keyed by batch size
   int64_t graph_block = 32;
-  // solver workgroups per compute unit (1 or 2)
-  int32_t wg_per_cu = 2;
+  // solver workgroups per compute unit: 1, 2, or 0 (by problem size)
+  int32_t wg_per_cu = 0;
   // grid line length L of a band whose far offsets are +-L and whose other
   // offsets lie within +-63 (0: the line walk does not apply)
   int64_t line = 0;

@@ -97,6 +97,13 @@ def test_one_workgroup_per_cu():
     assert np.array_equal(y, oracle.spmv(Ao, b))
     assert iters_close(it, io.iterations) and iters_close(ait, aio.iterations)
     assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+    # automatic (the default): one workgroup per CU at this size, so the
+    # same bits as the explicit setting
+    Q = csr_handle(rp, c)
+    Q.set_workgroups_per_cu(0)
+    xa, ia = K.sla_cg_solve(Q, t(v), t(b), 1e-10, 5000)
+    torch.cuda.synchronize()
+    assert np.array_equal(xa.cpu().numpy(), x) and ia.iterations == it
     with pytest.raises(K.SlaError):
         P.set_workgroups_per_cu(3)
 
