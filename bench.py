@@ -96,20 +96,25 @@ def pattern_grad_bytes(n: int, nnz: int, rp_bytes: int) -> int:
     return 12 * nnz + rp_bytes * (n + 1) + 16 * n
 
 
-def source_digest() -> str:
+def code_digest(files) -> str:
+    """sha256/16 of the kernel sources with comments and blank space removed:
+    a profile summary stays valid across edits of the comments only."""
     h = hashlib.sha256()
-    for f in ("cg.hip", "common.h"):
-        with open(os.path.join(ROOT, "krylov_solvers_adjoint_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in files:
+        with open(os.path.join(ROOT, "krylov_solvers_adjoint_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def source_digest() -> str:
+    return code_digest(("cg.hip", "common.h"))
 
 
 def lanczos_digest() -> str:
-    h = hashlib.sha256()
-    for f in ("lanczos.hip", "common.h"):
-        with open(os.path.join(ROOT, "krylov_solvers_adjoint_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    return code_digest(("lanczos.hip", "common.h"))
 
 
 def traffic_from_profile(kernel: str, workload: str, digest: str):

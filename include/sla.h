@@ -145,10 +145,11 @@ sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream);
  * y[s] = A_s^T x[s] for every system s of the bound batch: the transposed
  * product the backward pass of .matvec needs (Methodology 1).  The first call
  * builds the transposed pattern and keeps it with the handle (a COO -> CSR
- * build of the slots with rows and columns swapped; about 24 more bytes per
- * slot); every call gathers the bound values into its slot order.  Row j of
- * A^T is summed in ascending original row i, as an explicit transpose
- * followed by sla_spmv would.  x, y [batch][n], device memory.
+ * build of the slots with rows and columns swapped, with a map from each of
+ * its slots to the slot of A it transposes; about 24 more bytes per slot);
+ * the bound values are read in place through that map.  Row j of A^T is
+ * summed in ascending original row i, as an explicit transpose followed by
+ * sla_spmv would, bit for bit.  x, y [batch][n], device memory.
  */
 sla_status sla_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t stream);
 

@@ -160,7 +160,7 @@ struct Ctx {
   int64_t batch;
   int64_t tiles;        // ceil(n / kTileRows)
   int32_t grid;         // workgroups per system in the solver kernels
-  int32_t wave_cap;     // staged slots per wave tile (0: read slots from memory)
+  int32_t wave_cap;     // staged slots per wave tile (>= 1)
   const uint8_t* mask;  // [n] band masks, or nullptr (plain CSR)
   BandOffsets band;
   int32_t panel;        // tiles per band span (0: rows in plain order)

@@ -28,13 +28,13 @@ struct sla_csr_s {
   // pattern analysis
   int64_t tiles = 0;           // ceil(n / kTileRows): 64-row wave tiles
   int64_t max_tile_nnz = 0;    // largest number of slots in one wave tile
-  int32_t wave_cap = 0;        // slots staged per wave tile (0 = none)
+  int32_t wave_cap = 0;        // slots staged per wave tile (>= 1 once analysed)
   // banded patterns (every column j = i + one of a few offsets): a mask
   // byte per row replaces the column array and per-row row pointers
   uint8_t* band_mask = nullptr;  // [n] or nullptr
   sla::BandOffsets band{};
   bool no_band = false;          // pattern analysis skips band detection
-  int spmv_variant = SLA_SPMV_AUTO;  // SLA_SPMV_AUTO / _CSR / _BANDED
+  int spmv_variant = SLA_SPMV_AUTO;  // SLA_SPMV_AUTO / _CSR / _BANDED / _SPLIT / _LINES
   int32_t panel = 0;             // panel order of the SpMV tiles (0 = rows in order)
   bool wide_cols = false;        // sampled tiles reach columns far apart
   int32_t pblock = 0;
