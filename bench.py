@@ -252,6 +252,47 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int):
     return out
 
 
+def bench_batch64(kernel_reps: int):
+    """The shared-pattern batch: 64 Poisson 128 x 128 systems (diagonal
+    4 + c_s), CG to tol 1e-8 forward and adjoint; iteration time while all
+    64 are active, from the per-kernel timing launches."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    N, B = 128, 64
+    rp, c, vals, b, _ = W.batched_poisson(N, B, 2, 3)
+    g = W.normal_rhs(N * N, 4, shape=(B, N * N))
+    P = K.sla_csr_create_from_csr(torch.from_numpy(rp).to(dev), torch.from_numpy(c).to(dev))
+    vt = torch.from_numpy(vals).to(dev)
+    bt = torch.from_numpy(b).to(dev)
+    gt = torch.from_numpy(g).to(dev)
+    K.sla_cg_solve_batched(P, vt, bt, 1e-8, 50)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    x, fi = K.sla_cg_solve_batched(P, vt, bt, 1e-8, 10000)
+    gb, gv, ai = K.sla_cg_adjoint_batched(P, vt, x, gt, 1e-8, 10000)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n, nnz = N * N, P.nnz
+    its_f = [i.iterations for i in fi]
+    its_a = [i.iterations for i in ai]
+    # canonical bytes of one iteration of all 64 systems: the pattern read
+    # once, the values and vectors per system
+    b_it = B * (8 * nnz + 88 * n) + 4 * nnz + 4 * (n + 1)
+    out = dict(systems=B, n=n, nnz=nnz, iterations_fwd=[min(its_f), max(its_f)],
+               iterations_adj=[min(its_a), max(its_a)], solve_adjoint_ms=1e3 * wall,
+               steps=max(its_f) + max(its_a),
+               us_per_step=1e6 * wall / (max(its_f) + max(its_a)),
+               canonical_bytes_all_active=b_it,
+               eff_GBps_upper=b_it * (max(its_f) + max(its_a)) / wall / 1e9)
+    del P, vt, bt, gt, x, gb, gv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_rgg(n: int, kernel_reps: int):
     """Random geometric graph Laplacian + 0.01 I (4M nodes, ~9 slots per row,
     random node order): CSR built on the GPU from COO, then CG to 1e-8 and the
@@ -639,10 +680,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--sizes", default="16m,169m,rgg4m",
+    ap.add_argument("--sizes", default="16m,169m,rgg4m,batch64",
                     help="extra workloads: 16m / 169m (Poisson, 500 fixed iterations), rgg4m "
-                         "(random geometric graph, tol 1e-8 forward + adjoint); '' for none; "
-                         "with --skip-headline also matvec and eigsh")
+                         "(random geometric graph, tol 1e-8 forward + adjoint), batch64 (64 "
+                         "Poisson 128^2 systems on one pattern); '' for none; with "
+                         "--skip-headline also matvec, eigsh, bicgstab and list")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -693,6 +735,9 @@ def main():
             if s.lower() == "list":
                 log(f"[bench] list: {bench_list()}")
                 continue
+            if s.lower() == "batch64":
+                log(f"[bench] batch64: {bench_batch64(args.kernel_reps)}")
+                continue
             if s.lower() == "bicgstab":
                 log(f"[bench] bicgstab: {bench_bicgstab()}")
                 continue
@@ -714,6 +759,11 @@ def main():
     sizes = {}
     for s in [s for s in args.sizes.split(",") if s]:
         import numpy as np
+        if s.lower() == "batch64":
+            log("[bench] size batch64: 64 Poisson 128x128 systems, shared pattern, tol 1e-8")
+            sizes["batch64"] = bench_batch64(args.kernel_reps)
+            log(f"[bench] size batch64: {sizes['batch64']['us_per_step']:.1f} us per step")
+            continue
         if s.lower() == "rgg4m":
             log("[bench] size rgg4m: random geometric graph, 4M nodes, tol 1e-8 fwd + adj")
             sizes["rgg4m"] = bench_rgg(4_000_000, args.kernel_reps)
