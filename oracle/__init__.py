@@ -105,6 +105,10 @@ def _bind(lib):
     lib.oracle_adjoint_bicgstab.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P, _D, _I64,
                                             ctypes.POINTER(_Info)]
     lib.oracle_set_threads.restype = None
+    lib.oracle_bfs_order.argtypes = [_I64, _P, _P, _P]
+    lib.oracle_bfs_order.restype = None
+    lib.oracle_permute.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_permute.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_get_threads.restype = ctypes.c_int
     lib.oracle_get_threads.argtypes = []
@@ -198,6 +202,31 @@ def transpose(A: CSR, lib=None) -> CSR:
     vt = np.zeros(max(A.nnz, 1), np.float64)
     L.oracle_transpose(A.n, _ptr(rp), _ptr(c), _ptr(v), _ptr(rpt), _ptr(ct), _ptr(vt))
     return CSR(A.n, rpt, ct[:A.nnz].copy(), vt[:A.nnz].copy())
+
+
+def bfs_order(A: CSR, lib=None) -> np.ndarray:
+    """Breadth-first (Cuthill-McKee level) order of the unknowns from a
+    pseudo-peripheral node; order[t] = original index at position t."""
+    L = lib or _load()
+    order = np.zeros(max(A.n, 1), np.int64)
+    L.oracle_bfs_order(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                       _ptr(order))
+    return order[:A.n].copy()
+
+
+def permute(A: CSR, order, lib=None):
+    """(P A P^T, src): the matrix with unknown order[t] at position t, rows'
+    columns ascending; src[s] = slot of A held by slot s."""
+    L = lib or _load()
+    o = _c(order, np.int64)
+    rp = np.zeros(A.n + 1, np.int64)
+    c = np.zeros(max(A.nnz, 1), np.int32)
+    v = np.zeros(max(A.nnz, 1), np.float64)
+    src = np.zeros(max(A.nnz, 1), np.int64)
+    L.oracle_permute(A.n, _ptr(_c(A.rowptr, np.int64)), _ptr(_c(A.col, np.int32)),
+                     _ptr(_c(A.vals, np.float64)), _ptr(o), _ptr(rp), _ptr(c), _ptr(v),
+                     _ptr(src))
+    return CSR(A.n, rp, c[:A.nnz].copy(), v[:A.nnz].copy()), src[:A.nnz].copy()
 
 
 def spmv(A: CSR, x, lib=None) -> np.ndarray:

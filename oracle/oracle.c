@@ -691,6 +691,102 @@ int oracle_adjoint_bicgstab(int64_t n, const int64_t* rowptr, const int32_t* col
 }
 
 /* ------------------------------------------------------------------------ */
+/* Locality ordering of the unknowns (not from the pages)                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Breadth-first visit of the pattern's graph (an edge i -> j for every
+ * stored slot (i, j), j != i) from `start`, restricted to unvisited nodes:
+ * nodes are appended to order[] at *len in the order they are first reached,
+ * each node's neighbours taken in its row's (ascending) column order.
+ * dist[v] receives the number of edges from start.  Returns the last node
+ * appended's distance (the depth of the visit).
+ */
+static int64_t bfs_visit(const int64_t* rowptr, const int32_t* col, int64_t start,
+                         int64_t* order, int64_t* len, int64_t* dist) {
+  int64_t head = *len;
+  order[(*len)++] = start;
+  dist[start] = 0;
+  int64_t depth = 0;
+  while (head < *len) {
+    int64_t v = order[head++];
+    for (int64_t k = rowptr[v]; k < rowptr[v + 1]; ++k) {
+      int64_t u = col[k];
+      if (dist[u] >= 0) continue;
+      dist[u] = dist[v] + 1;
+      if (dist[u] > depth) depth = dist[u];
+      order[(*len)++] = u;
+    }
+  }
+  return depth;
+}
+
+/*
+ * A bandwidth-reducing order of the unknowns: the breadth-first order of the
+ * pattern's graph (Cuthill-McKee's level structure, with each node's
+ * children in column order instead of by degree) from a pseudo-peripheral
+ * start node.
+ *   s0 = the smallest index of largest row length (stored slots);
+ *   s1 = the smallest index among the nodes farthest from s0 (in edges);
+ *   a visit from s1, then from the smallest unvisited index while nodes
+ *   remain (every connected piece in turn).
+ * order[t] = the original index of the unknown at position t.
+ */
+void oracle_bfs_order(int64_t n, const int64_t* rowptr, const int32_t* col, int64_t* order) {
+  if (n <= 0) return;
+  int64_t* dist = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t s0 = 0;
+  for (int64_t i = 1; i < n; ++i)
+    if (rowptr[i + 1] - rowptr[i] > rowptr[s0 + 1] - rowptr[s0]) s0 = i;
+  for (int64_t i = 0; i < n; ++i) dist[i] = -1;
+  int64_t len = 0;
+  int64_t depth = bfs_visit(rowptr, col, s0, order, &len, dist);
+  int64_t s1 = -1;
+  for (int64_t t = 0; t < len; ++t)
+    if (dist[order[t]] == depth && (s1 < 0 || order[t] < s1)) s1 = order[t];
+  for (int64_t i = 0; i < n; ++i) dist[i] = -1;
+  len = 0;
+  bfs_visit(rowptr, col, s1, order, &len, dist);
+  for (int64_t i = 0; i < n; ++i)
+    if (dist[i] < 0) bfs_visit(rowptr, col, i, order, &len, dist);
+  free(dist);
+}
+
+/*
+ * The symmetrically permuted matrix B = P A P^T of an order (B's row t is
+ * A's row order[t], its columns renumbered by pos[order[t]] = t and sorted
+ * ascending).  src[s] receives the slot of A that B's slot s holds.
+ */
+void oracle_permute(int64_t n, const int64_t* rowptr, const int32_t* col, const double* vals,
+                    const int64_t* order, int64_t* rowptr_p, int32_t* col_p, double* vals_p,
+                    int64_t* src) {
+  int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  for (int64_t t = 0; t < n; ++t) pos[order[t]] = t;
+  rowptr_p[0] = 0;
+  for (int64_t t = 0; t < n; ++t)
+    rowptr_p[t + 1] = rowptr_p[t] + (rowptr[order[t] + 1] - rowptr[order[t]]);
+  for (int64_t t = 0; t < n; ++t) {
+    int64_t i = order[t], a = rowptr_p[t];
+    int64_t len = rowptr[i + 1] - rowptr[i];
+    /* insertion sort of the row's slots by new column */
+    for (int64_t q = 0; q < len; ++q) {
+      int64_t k = rowptr[i] + q;
+      int64_t c = pos[col[k]];
+      int64_t w = a + q;
+      while (w > a && col_p[w - 1] > c) {
+        col_p[w] = col_p[w - 1];
+        src[w] = src[w - 1];
+        --w;
+      }
+      col_p[w] = (int32_t)c;
+      src[w] = k;
+    }
+    for (int64_t q = 0; q < len; ++q) vals_p[a + q] = vals[src[a + q]];
+  }
+  free(pos);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Threads                                                                   */
 /* ------------------------------------------------------------------------ */
 #ifdef _OPENMP

@@ -852,6 +852,88 @@ def pin_adjoint_bicgstab(lib=None):
         assert abs(fd - gv[k]) <= 1e-6 * max(1.0, abs(fd)), (k, fd, gv[k])
 
 
+# --------------------------------------------------------------------------
+# Locality ordering (breadth-first order of the pattern's graph)
+# --------------------------------------------------------------------------
+
+def _pattern_csr(n, edges, diag=True):
+    """Symmetric pattern of an undirected edge list (values: a Laplacian +
+    I, so that the matrix is SPD), rows' columns ascending."""
+    M = np.zeros((n, n))
+    for i, j in edges:
+        M[i, j] = M[j, i] = -1.0
+    M += np.diag(np.abs(M).sum(axis=1) + (1.0 if diag else 0.0))
+    return _csr_of(M), M
+
+
+def pin_bfs_order_hand(lib=None):
+    """Orders worked out by hand.  A path 3-0-4-1-2: the longest rows (3
+    slots) are 0, 4, 1, so the first visit starts at 0; the farthest nodes
+    from 0 are {2} (3 edges); the visit from 2 lists 2, 1, 4, 0, 3.  Two
+    pieces and an isolated node (edges 0-3, 3-5, 5-1, 2-6; 4 alone): start 3;
+    farthest {1}; 1, 5, 3, 0, then the smallest unvisited index 2 (2, 6),
+    then 4."""
+    A, _ = _pattern_csr(5, [(3, 0), (0, 4), (4, 1), (1, 2)])
+    assert oracle.bfs_order(A, lib=lib).tolist() == [2, 1, 4, 0, 3]
+    A, _ = _pattern_csr(7, [(0, 3), (3, 5), (5, 1), (2, 6)])
+    assert oracle.bfs_order(A, lib=lib).tolist() == [1, 5, 3, 0, 2, 6, 4]
+    A, _ = _pattern_csr(1, [])
+    assert oracle.bfs_order(A, lib=lib).tolist() == [0]
+    # a star: centre 4 has the longest row; every leaf is 1 edge away, the
+    # smallest is 0; from 0: 0, 4, then the other leaves ascending
+    A, _ = _pattern_csr(6, [(4, 0), (4, 1), (4, 2), (4, 3), (4, 5)])
+    assert oracle.bfs_order(A, lib=lib).tolist() == [0, 4, 1, 2, 3, 5]
+
+
+def _scipy_bfs_order(A):
+    """The same order from scipy's graph routines: distances from the start
+    by unweighted shortest paths, each piece by breadth_first_order."""
+    import scipy.sparse as sp
+    from scipy.sparse.csgraph import breadth_first_order, shortest_path
+    G = sp.csr_matrix((np.ones(A.nnz), A.col, A.rowptr), shape=(A.n, A.n))
+    s0 = int(np.argmax(np.diff(A.rowptr)))
+    d = shortest_path(G, directed=True, unweighted=True, indices=s0)
+    far = np.max(d[np.isfinite(d)])
+    s1 = int(np.flatnonzero(d == far).min())
+    out = list(breadth_first_order(G, s1, directed=True, return_predecessors=False))
+    seen = np.zeros(A.n, bool)
+    seen[out] = True
+    for i in range(A.n):
+        if not seen[i]:
+            piece = breadth_first_order(G, i, directed=True, return_predecessors=False)
+            out += list(piece)
+            seen[piece] = True
+    return np.array(out)
+
+
+def pin_bfs_order_scipy(lib=None):
+    """Symmetric patterns with several pieces (a random geometric graph with
+    isolated nodes, a grid, a random sparse matrix): the oracle's order is
+    scipy's breadth-first order from the same start, piece by piece, and a
+    permutation of 0..n-1."""
+    row, col, val, _ = W.rgg_coo(3000, 11, 12, degree=4.0)
+    rp, c, perm = oracle.csr_from_coo(3000, row, col)
+    A = oracle.CSR(3000, rp, c, oracle.values_from_coo(perm, c.shape[0], val))
+    cases = [A, _poisson(17), _random_spd_csr(300, 0.01, 5)[0]]
+    for A in cases:
+        o = oracle.bfs_order(A, lib=lib)
+        assert np.array_equal(np.sort(o), np.arange(A.n))
+        assert np.array_equal(o, _scipy_bfs_order(A))
+
+
+def pin_permute_dense(lib=None):
+    """P A P^T against the dense matrix indexed by the order; every row's
+    columns ascending; src maps each new slot to the slot of A it holds."""
+    A, M = _random_spd_csr(60, 0.08, 9)
+    order = np.random.default_rng(3).permutation(60)
+    B, src = oracle.permute(A, order, lib=lib)
+    assert np.array_equal(B.to_dense(), M[np.ix_(order, order)])
+    for t in range(B.n):
+        assert np.all(np.diff(B.col[B.rowptr[t]:B.rowptr[t + 1]]) > 0)
+    assert np.array_equal(B.vals, A.vals[src])
+    assert np.array_equal(np.sort(src), np.arange(A.nnz))
+
+
 ALL_PINS = [
     pin_csr_poisson_closed_form, pin_csr_brute_force, pin_csr_rgg_symmetric,
     pin_spmv_eigenpairs, pin_spmv_dense, pin_dot,
@@ -864,4 +946,5 @@ ALL_PINS = [
     pin_eigsh_poisson, pin_eigsh_dense, pin_eig_grad,
     pin_bicgstab_dense_lu, pin_bicgstab_scaling, pin_bicgstab_finite_termination,
     pin_bicgstab_statuses, pin_adjoint_bicgstab,
+    pin_bfs_order_hand, pin_bfs_order_scipy, pin_permute_dense,
 ]

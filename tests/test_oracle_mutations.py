@@ -62,6 +62,14 @@ MUTATIONS = {
                                 "  }\n  info->iterations = k;"),
     "bicgstab_half_step_no_x": ("      for (int64_t i = 0; i < n; ++i) x[i] = x[i] + alpha * p[i];\n      if (hist_omega) hist_omega[k] = 0.0;",
                                 "      if (hist_omega) hist_omega[k] = 0.0;"),
+    "bfs_far_node_largest": ("if (dist[order[t]] == depth && (s1 < 0 || order[t] < s1)) s1 = order[t];",
+                             "if (dist[order[t]] == depth && (s1 < 0 || order[t] > s1)) s1 = order[t];"),
+    "bfs_start_last_longest": ("if (rowptr[i + 1] - rowptr[i] > rowptr[s0 + 1] - rowptr[s0]) s0 = i;",
+                               "if (rowptr[i + 1] - rowptr[i] >= rowptr[s0 + 1] - rowptr[s0]) s0 = i;"),
+    "bfs_no_restart": ("if (dist[i] < 0) bfs_visit(rowptr, col, i, order, &len, dist);", ""),
+    "bfs_start_is_s0": ("  bfs_visit(rowptr, col, s1, order, &len, dist);\n",
+                        "  bfs_visit(rowptr, col, s0, order, &len, dist);\n"),
+    "permute_unsorted": ("while (w > a && col_p[w - 1] > c) {", "while (0) {"),
     "bicgstab_adjoint_on_A": ("  int status = oracle_bicgstab(n, rowptr_t, col_t, vals_t, g, grad_b,",
                               "  int status = oracle_bicgstab(n, rowptr, col, vals, g, grad_b,"),
 }
