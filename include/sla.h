@@ -431,6 +431,44 @@ sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
  * change. */
 sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups);
 
+/*
+ * Locality ordering of the unknowns for CG.  The pages fix no storage order;
+ * this is the library's own remedy for patterns whose unknowns come in an
+ * order unrelated to the graph (the random geometric graph of the
+ * explainer's benchmark set, Performance / benchmarks: nodes in sampling
+ * order), where every gathered vector entry of the SpMV misses the caches.
+ *
+ * SLA_ORDER_BFS renumbers the unknowns in the breadth-first order of the
+ * pattern's graph (an edge i -> j for every stored slot (i, j), j != i):
+ * from s1, the smallest index among the nodes farthest (in edges) from s0,
+ * the smallest index of largest row length; each node's unvisited
+ * neighbours are appended in ascending column order; when a visit ends and
+ * nodes remain, the next starts at the smallest unvisited index.  Computed on
+ * the device (integer work, the same order on every run), together with
+ * B = P A P^T (pattern, slot map and solver workspace: about 12 bytes per
+ * slot + 8 per slot and system for B's values + 20 bytes per unknown and
+ * system).  Synchronises `stream`.  Needs nnz < 2^32.
+ *
+ * Afterwards sla_cg_solve, sla_cg_solve_batched, sla_cg_adjoint,
+ * sla_cg_adjoint_batched, the CG calls of sla_solve_list / sla_adjoint_list,
+ * sla_cg_history and sla_profile_iteration_kernels run on B: every call
+ * gathers the bound values into B's slot order and b (or grad_x, and x
+ * under SLA_FLAG_X0) into B's unknown order, and scatters x (or grad_b) back;
+ * grad_vals is formed on A's own slots.  Inputs and outputs keep A's
+ * numbering.  CG's iterates are A's, permuted, in exact arithmetic; in
+ * floating point the row sums and dot products are taken in another order,
+ * so results differ from the unordered solve by rounding.  Every other call
+ * (spmv, eigsh, BiCGStab, ...) still uses A as it is.
+ * SLA_ORDER_NONE drops the ordering and its memory.
+ */
+enum { SLA_ORDER_NONE = 0, SLA_ORDER_BFS = 1 };
+sla_status sla_csr_reorder(sla_csr A, int ordering, hipStream_t stream);
+
+/* The ordering of a reordered handle: order_out [n] (int32, device) receives
+ * the original index of the unknown at each position.  Asynchronous on
+ * `stream`.  SLA_ERR_ARG if the handle is not reordered. */
+sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* sla_last_error(void);
 

@@ -30,6 +30,7 @@ __all__ = [
     "sla_spmv_transpose", "sla_matvec_grad", "sla_eigsh", "sla_eig_grad", "EigInfo",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_solve_list", "sla_adjoint_list", "SparseTensorList",
+    "sla_csr_reorder", "sla_csr_ordering",
     "LIB_PATH", "EXPORTS",
 ]
 
@@ -41,6 +42,7 @@ EIG_SMALLEST, EIG_LARGEST = 0, 1
 METHOD_CG, METHOD_BICGSTAB = 0, 1
 I32, I64 = 4, 8
 FLAG_X0, FLAG_HISTORY, FLAG_JACOBI = 1, 2, 4
+ORDER_NONE, ORDER_BFS = 0, 1
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_create_from_csr", "sla_csr_destroy", "sla_csr_get_info",
@@ -52,7 +54,7 @@ EXPORTS = [
     "sla_csr_set_workgroups_per_cu", "sla_spmv_transpose", "sla_matvec_grad",
     "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
-    "sla_solve_list", "sla_adjoint_list",
+    "sla_solve_list", "sla_adjoint_list", "sla_csr_reorder", "sla_csr_ordering",
     "sla_last_error", "sla_status_string",
 ]
 
@@ -112,6 +114,8 @@ def _bind(lib):
         "sla_solve_list": [_I64, _P, _P, _P, _D, _I64, _U32, _S, _P, _P],
         "sla_adjoint_list": [_I64, _P, _P, _P, _P, _P, _D, _I64, _U32, _S, _P, _P],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
+        "sla_csr_reorder": [_P, _S, _P],
+        "sla_csr_ordering": [_P, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -204,6 +208,7 @@ class CSRPattern:
         self.rowptr_dtype = torch.int32 if w.value == I32 else torch.int64
         self._bound = None
         self._variant = 0
+        self._reordered = False
 
     @property
     def handle(self):
@@ -276,6 +281,16 @@ class CSRPattern:
         """Whether the CG iteration uses the line walk."""
         return self._kernels() == 3
 
+    def reorder(self, ordering: str = "bfs", stream=None) -> "CSRPattern":
+        """Renumber the unknowns for the CG calls (sla_csr_reorder): "bfs"
+        (breadth-first order of the pattern's graph) or "none"."""
+        sla_csr_reorder(self, ordering, stream)
+        return self
+
+    @property
+    def reordered(self) -> bool:
+        return self._reordered
+
     def history(self, system: int = 0, cap: int = 1 << 20):
         import numpy as np
         cnt = _I64()
@@ -312,6 +327,22 @@ def sla_csr_create_from_csr(rowptr: torch.Tensor, col: torch.Tensor, stream=None
         _dev(col, torch.int32, "col") if col.numel() else None, _stream(stream),
         ctypes.byref(h)))
     return CSRPattern(h.value)
+
+
+def sla_csr_reorder(A: CSRPattern, ordering: str = "bfs", stream=None) -> None:
+    """CG solves and adjoints on A run on P A P^T, P the breadth-first order
+    of the pattern's graph ("bfs"), or on A as it is again ("none")."""
+    code = {"none": ORDER_NONE, "bfs": ORDER_BFS}[ordering]
+    _check(_lib.sla_csr_reorder(A.handle, code, _stream(stream)))
+    A._reordered = code != ORDER_NONE
+
+
+def sla_csr_ordering(A: CSRPattern, stream=None) -> torch.Tensor:
+    """The ordering of a reordered handle: out[t] = original index of the
+    unknown at position t (int32, on the device)."""
+    out = torch.empty(A.n, dtype=torch.int32, device=torch.device("cuda", torch.cuda.current_device()))
+    _check(_lib.sla_csr_ordering(A.handle, out.data_ptr() if A.n else None, _stream(stream)))
+    return out
 
 
 def sla_csr_values_from_coo(A: CSRPattern, coo_val: torch.Tensor, stream=None) -> torch.Tensor:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsla.so")
-SOURCES = ["api.hip", "csr_build.hip", "cg.hip", "lanczos.hip", "bicgstab.hip"]
+SOURCES = ["api.hip", "csr_build.hip", "cg.hip", "lanczos.hip", "bicgstab.hip", "reorder.hip"]
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -91,6 +91,7 @@ void free_handle(sla_csr A) {
   release_workspace(A);
   release_eig_work(A);
   release_bs_work(A);
+  release_reorder(A);
   free_handle(A->trans);
   dev_free(A->rowptr);
   dev_free(A->col);
@@ -348,7 +349,7 @@ sla_status sla_cg_solve_batched(sla_csr A, const double* b, double* x, double to
   API_BEGIN
   clear_error();
   SLA_TRY(check_solve(A, b, x, tol, maxit, flags, "sla_cg_solve_batched"));
-  return run_cg(A, b, x, tol, maxit, flags, info, stream);
+  return run_cg_any(A, b, x, tol, maxit, flags, info, stream);
   API_END
 }
 
@@ -359,16 +360,17 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol, int64
   SLA_TRY(check_solve(A, b, x, tol, maxit, flags, "sla_cg_solve"));
   REQUIRE(A->batch == 1, "sla_cg_solve: %lld systems bound; use sla_cg_solve_batched",
           (long long)A->batch);
-  return run_cg(A, b, x, tol, maxit, flags, info, stream);
+  return run_cg_any(A, b, x, tol, maxit, flags, info, stream);
   API_END
 }
 
 // A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix), then
-// the pattern gradient (also from the last iterate after a breakdown).
+// the pattern gradient (also from the last iterate after a breakdown), on
+// A's own slots whether or not the solve ran on a reordered copy.
 static sla_status run_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
-  sla_status s = run_cg(A, grad_x, grad_b, tol, maxit, flags, info, stream);
+  sla_status s = run_cg_any(A, grad_x, grad_b, tol, maxit, flags, info, stream);
   if (grad_vals != nullptr && (s == SLA_OK || s == SLA_ERR_NOT_SPD || s == SLA_ERR_NONFINITE)) {
     sla_status g = launch_pattern_grad(A, A->batch, grad_b, x, grad_vals, stream);
     if (g != SLA_OK) return g;
@@ -503,7 +505,7 @@ sla_status sla_solve_list(int64_t count, const sla_csr* A, const double* const* 
   for (int64_t i = 0; i < count; ++i)
     SLA_TRY(check_solve(A[i], b[i], x[i], tol, maxit, flags, "sla_solve_list"));
   return run_list(count, info, stream, [&](int64_t i, hipStream_t st, sla_cg_info* in) {
-    return method == SLA_METHOD_CG ? run_cg(A[i], b[i], x[i], tol, maxit, flags, in, st)
+    return method == SLA_METHOD_CG ? run_cg_any(A[i], b[i], x[i], tol, maxit, flags, in, st)
                                    : run_bicgstab(A[i], b[i], x[i], tol, maxit, flags, in, st);
   });
   API_END
@@ -594,6 +596,7 @@ sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha, double* beta
   API_BEGIN
   clear_error();
   REQUIRE(A != nullptr, "sla_cg_history: NULL handle");
+  A = solver_handle(A);
   REQUIRE(A->hist != nullptr && A->scal_host != nullptr,
           "sla_cg_history: no solve with SLA_FLAG_HISTORY yet");
   REQUIRE(system >= 0 && system < A->ws_batch, "sla_cg_history: system out of range");
@@ -630,7 +633,7 @@ sla_status sla_profile_iteration_kernels(sla_csr A, const double* b, double* x, 
   REQUIRE(b != nullptr && x != nullptr && avg_ms_host != nullptr,
           "sla_profile_iteration_kernels: NULL pointer");
   REQUIRE(reps >= 1 && reps <= 100000, "sla_profile_iteration_kernels: reps out of range");
-  return profile_kernels(A, b, x, reps, avg_ms_host, stream);
+  return profile_kernels_any(A, b, x, reps, avg_ms_host, stream);
   API_END
 }
 
@@ -651,12 +654,16 @@ sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels) {
   REQUIRE(A != nullptr, "sla_csr_set_spmv_variant: NULL handle");
   REQUIRE(variant >= SLA_SPMV_AUTO && variant <= SLA_SPMV_LINES,
           "sla_csr_set_spmv_variant: unknown variant %d", variant);
-  if (variant != A->spmv_variant) {
-    (void)hipDeviceSynchronize();
-    release_workspace(A);  // the captured graphs hold the old kernels
-    A->spmv_variant = variant;
+  for (sla_csr H : {A, solver_handle(A)}) {
+    if (variant != H->spmv_variant) {
+      (void)hipDeviceSynchronize();
+      release_workspace(H);  // the captured graphs hold the old kernels
+      H->spmv_variant = variant;
+    }
   }
-  if (kernels) *kernels = use_split(A) ? 2 : (use_lines(A) ? 3 : (use_band(A) ? 1 : 0));
+  // the family the CG solves use (those of the reordered copy, if any)
+  const sla_csr K = solver_handle(A);
+  if (kernels) *kernels = use_split(K) ? 2 : (use_lines(K) ? 3 : (use_band(K) ? 1 : 0));
   return SLA_OK;
   API_END
 }
@@ -666,10 +673,12 @@ sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations) {
   clear_error();
   REQUIRE(A != nullptr, "sla_csr_set_graph_block: NULL handle");
   REQUIRE(iterations >= 0 && iterations <= 4096, "sla_csr_set_graph_block: out of range");
-  if (iterations != A->graph_block) {
-    (void)hipDeviceSynchronize();
-    release_workspace(A);  // drops the captured graphs with the workspace
-    A->graph_block = iterations;
+  for (sla_csr H : {A, solver_handle(A)}) {
+    if (iterations != H->graph_block) {
+      (void)hipDeviceSynchronize();
+      release_workspace(H);  // drops the captured graphs with the workspace
+      H->graph_block = iterations;
+    }
   }
   return SLA_OK;
   API_END
@@ -680,12 +689,43 @@ sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups) {
   clear_error();
   REQUIRE(A != nullptr, "sla_csr_set_workgroups_per_cu: NULL handle");
   REQUIRE(workgroups >= 0 && workgroups <= 2, "sla_csr_set_workgroups_per_cu: must be 0, 1 or 2");
-  if (workgroups != A->wg_per_cu) {
-    (void)hipDeviceSynchronize();
-    release_workspace(A);  // the grid sizes the partial-sum arrays and the graphs
-    A->wg_per_cu = workgroups;
+  for (sla_csr H : {A, solver_handle(A)}) {
+    if (workgroups != H->wg_per_cu) {
+      (void)hipDeviceSynchronize();
+      release_workspace(H);  // the grid sizes the partial-sum arrays and the graphs
+      H->wg_per_cu = workgroups;
+    }
   }
   return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_reorder(sla_csr A, int ordering, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_reorder: NULL handle");
+  REQUIRE(ordering == SLA_ORDER_NONE || ordering == SLA_ORDER_BFS,
+          "sla_csr_reorder: unknown ordering %d", ordering);
+  if (ordering == SLA_ORDER_NONE) {
+    if (A->ro != nullptr) {
+      SLA_TRY_HIP(hipStreamSynchronize(stream));
+      (void)hipDeviceSynchronize();
+      release_reorder(A);
+    }
+    return SLA_OK;
+  }
+  if (A->ro != nullptr) return SLA_OK;  // the order is a function of the pattern
+  return make_reorder(A, stream);
+  API_END
+}
+
+sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_ordering: NULL handle");
+  REQUIRE(A->ro != nullptr, "sla_csr_ordering: the handle is not reordered (sla_csr_reorder)");
+  REQUIRE(order_out != nullptr || A->n == 0, "sla_csr_ordering: NULL output");
+  return copy_order(A, order_out, stream);
   API_END
 }
 

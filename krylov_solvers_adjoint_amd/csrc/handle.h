@@ -9,6 +9,7 @@
 namespace sla {
 struct EigWork;  // Lanczos workspace (lanczos.hip)
 struct BsWork;   // BiCGStab workspace (bicgstab.hip)
+struct Reorder;  // locality ordering and the permuted matrix (reorder.hip)
 }
 
 struct sla_csr_s {
@@ -85,6 +86,8 @@ struct sla_csr_s {
   // BiCGStab vectors, partials and scalars, allocated by the first solve
   sla::BsWork* bs = nullptr;
   bool bs_hist_valid = false;
+  // sla_csr_reorder: CG solves and adjoints run on P A P^T (its own handle)
+  sla::Reorder* ro = nullptr;
   std::map<int64_t, std::pair<hipGraph_t, hipGraphExec_t>> graphs;
 };
 
@@ -140,6 +143,19 @@ sla_status profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps, double
                                    hipStream_t stream);
 sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps,
                            double* avg_ms, hipStream_t stream);
+
+// Locality ordering (reorder.hip): A->ro with the breadth-first order of the
+// pattern's graph and the handle of P A P^T
+sla_status make_reorder(sla_csr A, hipStream_t stream);
+void release_reorder(sla_csr A);
+// CG on A, or on P A P^T with b, x permuted in and out when A is reordered
+sla_status run_cg_any(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                      uint32_t flags, sla_cg_info* info, hipStream_t stream);
+sla_status profile_kernels_any(sla_csr A, const double* b, double* x, int64_t reps,
+                               double* avg_ms, hipStream_t stream);
+sla_status copy_order(sla_csr A, int32_t* out, hipStream_t stream);
+// the handle whose kernels and CG state a solve on A uses
+sla_csr solver_handle(sla_csr A);
 
 // COO / CSR construction implemented in csr_build.hip
 sla_status build_from_coo(sla_csr A, sla_index coo_idx, const void* row,

@@ -65,5 +65,7 @@ def test_argument_errors_need_no_gpu():
     assert lib.sla_adjoint_list(0, None, None, None, None, None, 1e-8, 10, 0, 0, None,
                                 None) == K.ERR_ARG
     assert lib.sla_csr_set_graph_block(None, 32) == K.ERR_ARG
+    assert lib.sla_csr_reorder(None, K.ORDER_BFS, None) == K.ERR_ARG
+    assert lib.sla_csr_ordering(None, None, None) == K.ERR_ARG
     assert lib.sla_status_string(K.ERR_NOT_SPD) == b"SLA_ERR_NOT_SPD"
     assert lib.sla_csr_destroy(None) == K.OK

@@ -94,6 +94,22 @@ def test_rgg4m_csr_forward_adjoint():
     assert iters_close(info.iterations, io.iterations)
     assert iters_close(ainfo.iterations, aio.iterations)
     assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+    # the same solves on the breadth-first reordering: the order bit-exact,
+    # the results against the same oracle solves
+    say("rgg4m: reordering")
+    P.reorder()
+    order = K.sla_csr_ordering(P).cpu().numpy().astype(np.int64)
+    assert np.array_equal(order, oracle.bfs_order(Ao))
+    xr, ri = K.sla_cg_solve(P, vt, t(b), 1e-8, 20000)
+    gbr, gvr, rai = K.sla_cg_adjoint(P, vt, xr, t(g), 1e-8, 20000)
+    torch.cuda.synchronize()
+    xr, gbr, gvr = xr.cpu().numpy(), gbr.cpu().numpy(), gvr.cpu().numpy()
+    say(f"rgg4m reordered: iterations {ri.iterations}/{rai.iterations}; x {rel(xr, xo):.2e} "
+        f"lam {rel(gbr, gbo):.2e} gv {rel(gvr, gvo):.2e}")
+    assert ri.converged and rai.converged
+    assert iters_close(ri.iterations, io.iterations)
+    assert iters_close(rai.iterations, aio.iterations)
+    assert rel(xr, xo) <= TOL_X and rel(gbr, gbo) <= TOL_X and rel(gvr, gvo) <= TOL_GRAD
 
 
 def _properties(N, rp_dtype, maxit=500):

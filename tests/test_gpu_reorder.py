@@ -1,0 +1,218 @@
+"""Locality ordering (sla_csr_reorder): the device's breadth-first order is
+the oracle's bit for bit (integer work) on patterns with several pieces,
+isolated nodes, directed edges, empty rows and long rows; CG solves,
+adjoints, batches and lists on a reordered handle match the oracle's solve
+of the original system; inputs and outputs keep the caller's numbering."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import TOL_GRAD, TOL_X, csr_handle, iters_close, rel, say, t
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_A(rp, c, v):
+    return oracle.CSR(len(rp) - 1, np.asarray(rp, np.int64), np.asarray(c, np.int32),
+                      np.asarray(v, np.float64))
+
+
+def _rgg(n, seed, degree=8.0):
+    row, col, val, _ = W.rgg_coo(n, seed, seed + 1, degree=degree)
+    rp, c, perm = oracle.csr_from_coo(n, row, col)
+    return rp, c, oracle.values_from_coo(perm, c.shape[0], val)
+
+
+def _directed(n, per_row, seed):
+    """A pattern with one-way edges (no diagonal in some rows, some rows
+    empty), columns ascending."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(n):
+        k = int(rng.integers(0, per_row + 1))
+        rows.append(np.unique(rng.integers(0, n, k)))
+    rp = np.zeros(n + 1, np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    c = np.concatenate(rows).astype(np.int32) if rp[-1] else np.zeros(0, np.int32)
+    return rp, c, np.ones(c.shape[0])
+
+
+def _star(n):
+    """Node 0 linked to every other node (a row of n slots), plus a path."""
+    M = {(0, j) for j in range(n)} | {(j, 0) for j in range(n)}
+    M |= {(j, j) for j in range(n)} | {(j, j + 1) for j in range(1, n - 1)}
+    M |= {(j + 1, j) for j in range(1, n - 1)}
+    e = np.array(sorted(M))
+    rp = np.zeros(n + 1, np.int64)
+    np.add.at(rp, e[:, 0] + 1, 1)
+    return np.cumsum(rp), e[:, 1].astype(np.int32), np.ones(len(e))
+
+
+def _patterns():
+    rp, c, v = W.poisson_csr(37)
+    yield "poisson37", rp, c
+    rp, c, v = _rgg(20000, 21)
+    yield "rgg20k", rp, c
+    rp, c, v = _rgg(30000, 23, degree=2.0)   # many pieces and isolated nodes
+    yield "rgg30k-sparse", rp, c
+    rp, c, _ = _directed(3000, 5, 4)
+    yield "directed3k", rp, c
+    rp, c, _ = _star(9000)                   # one row longer than 4096 slots
+    yield "star9k", rp, c
+    n = 5000                                 # diagonal only: every node alone
+    yield "diag5k", np.arange(n + 1, dtype=np.int64), np.arange(n, dtype=np.int32)
+    yield "one", np.array([0, 1]), np.array([0], np.int32)
+    yield "empty-rows", np.zeros(7, np.int64), np.zeros(0, np.int32)
+
+
+@pytest.mark.parametrize("case", [p[0] for p in _patterns()])
+def test_order_matches_oracle(case):
+    import krylov_solvers_adjoint_amd as K
+    name, rp, c = next(p for p in _patterns() if p[0] == case)
+    n = len(rp) - 1
+    say(f"ordering {name}: n={n} nnz={c.shape[0]}")
+    P = csr_handle(rp, c)
+    P.reorder()
+    o = K.sla_csr_ordering(P).cpu().numpy()
+    oo = oracle.bfs_order(_oracle_A(rp, c, np.ones(c.shape[0])))
+    assert np.array_equal(o.astype(np.int64), oo)
+    # idempotent, and dropped by "none"
+    P.reorder()
+    assert np.array_equal(K.sla_csr_ordering(P).cpu().numpy(), o)
+    P.reorder("none")
+    with pytest.raises(K.SlaError):
+        K.sla_csr_ordering(P)
+
+
+def test_reordered_cg_and_adjoint():
+    """RGG 20k (+0.01 I), tol 1e-10: plain CG and Jacobi CG, forward and
+    adjoint, on the reordered handle against the oracle on the original
+    matrix; the result is in the caller's numbering."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    rp, c, v = _rgg(20000, 31)
+    n = len(rp) - 1
+    A = _oracle_A(rp, c, v)
+    b = W.normal_rhs(n, 32)
+    g = W.normal_rhs(n, 33)
+    P = csr_handle(rp, c)
+    P.reorder()
+    vt = t(v)
+    for jac in (False, True):
+        solve = oracle.pcg_jacobi if jac else oracle.cg
+        adj = oracle.adjoint_jacobi if jac else oracle.adjoint
+        x, info = K.sla_cg_solve(P, vt, t(b), 1e-10, 20000, jacobi=jac)
+        gb, gv, ainfo = K.sla_cg_adjoint(P, vt, x, t(g), 1e-10, 20000, jacobi=jac)
+        torch.cuda.synchronize()
+        xo, io = solve(A, b, 1e-10, 20000)
+        gbo, gvo, aio = adj(A, xo, g, 1e-10, 20000)
+        x, gb, gv = x.cpu().numpy(), gb.cpu().numpy(), gv.cpu().numpy()
+        say(f"reordered rgg20k jacobi={jac}: it {info.iterations}/{io.iterations} "
+            f"adj {ainfo.iterations}/{aio.iterations} x {rel(x, xo):.1e} "
+            f"lam {rel(gb, gbo):.1e} gv {rel(gv, gvo):.1e}")
+        assert info.converged and ainfo.converged
+        assert iters_close(info.iterations, io.iterations)
+        assert iters_close(ainfo.iterations, aio.iterations)
+        assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+
+
+def test_reordered_matches_oracle_on_permuted_system():
+    """The reordered solve is CG on P A P^T: the oracle's CG on the permuted
+    matrix (built by the oracle from the oracle's own order) gives the same
+    iteration count and iterates to within the tolerance, and the history's
+    scalars follow the oracle's on that system."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    rp, c, v = _rgg(20000, 41)
+    n = len(rp) - 1
+    A = _oracle_A(rp, c, v)
+    order = oracle.bfs_order(A)
+    B, _ = oracle.permute(A, order)
+    b = W.normal_rhs(n, 42)
+    P = csr_handle(rp, c)
+    P.reorder()
+    x, info = K.sla_cg_solve(P, t(v), t(b), 1e-10, 20000, history=True)
+    torch.cuda.synchronize()
+    al, be, rr = P.history()
+    xb, ib, hist = oracle.cg(B, b[order], 1e-10, 20000, history=True)
+    assert iters_close(info.iterations, ib.iterations)
+    assert rel(x.cpu().numpy()[order], xb) <= TOL_X
+    k = min(len(al), len(hist[0]), 50)
+    assert rel(al[:k], hist[0][:k]) <= 1e-9 and rel(be[:k], hist[1][:k]) <= 1e-9
+
+
+def test_reordered_batched_and_warm_start():
+    """Shared-pattern batch of shifted Laplacians on a reordered handle
+    against the oracle's batched CG and adjoint; a warm start (x0 given)
+    lands on the same solution."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    N, B = 40, 5
+    rp, c, vals_b, b_b, _ = W.batched_poisson(N, B, 2, 3)
+    n = N * N
+    P = csr_handle(rp, c)
+    P.reorder()
+    vt = t(vals_b)
+    x, infos = K.sla_cg_solve_batched(P, vt, t(b_b), 1e-10, 5000)
+    g_b = W.normal_rhs(n, 9, shape=(B, n))
+    gb, gv, ainf = K.sla_cg_adjoint_batched(P, vt, x, t(g_b), 1e-10, 5000)
+    torch.cuda.synchronize()
+    xo, io = oracle.cg_batched(rp, c, vals_b, b_b, 1e-10, 5000)
+    gbo, gvo, aio = oracle.adjoint_batched(rp, c, vals_b, xo, g_b, 1e-10, 5000)
+    for s in range(B):
+        assert iters_close(infos[s].iterations, io[s].iterations)
+        assert rel(x[s].cpu().numpy(), xo[s]) <= TOL_X
+        assert rel(gb[s].cpu().numpy(), gbo[s]) <= TOL_X
+        assert rel(gv[s].cpu().numpy(), gvo[s]) <= TOL_GRAD
+    # warm start from a perturbed solution of system 0
+    P1 = csr_handle(rp, c)
+    P1.reorder()
+    x0 = xo[0] + 1e-3 * W.normal_rhs(n, 11)
+    xw, iw = K.sla_cg_solve(P1, t(vals_b[0]), t(b_b[0]), 1e-10, 5000, x0=t(x0))
+    torch.cuda.synchronize()
+    xwo, iwo = oracle.cg(_oracle_A(rp, c, vals_b[0]), b_b[0], 1e-10, 5000, x0=x0)
+    assert iters_close(iw.iterations, iwo.iterations)
+    assert rel(xw.cpu().numpy(), xwo) <= TOL_X
+
+
+def test_reordered_list_and_settings():
+    """A list whose items are reordered or not; the variant and workgroup
+    settings reach the reordered copy; a breakdown (negative definite)
+    reports NOT_SPD and leaves x in the caller's numbering."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    sys_ = [_rgg(8000, 51), W.poisson_csr(30), _rgg(12000, 53)]
+    Ps = [csr_handle(rp, c) for rp, c, _ in sys_]
+    Ps[0].reorder()
+    Ps[2].reorder()
+    vals = [t(v) for _, _, v in sys_]
+    bs = [t(W.normal_rhs(len(rp) - 1, 60 + i)) for i, (rp, _, _) in enumerate(sys_)]
+    xs, infos = K.sla_solve_list(Ps, vals, bs, 1e-10, 20000)
+    torch.cuda.synchronize()
+    for i, (rp, c, v) in enumerate(sys_):
+        x1, _ = K.sla_cg_solve(Ps[i], vals[i], bs[i], 1e-10, 20000)
+        torch.cuda.synchronize()
+        assert np.array_equal(xs[i].cpu().numpy(), x1.cpu().numpy())
+        xo, io = oracle.cg(_oracle_A(rp, c, v), bs[i].cpu().numpy(), 1e-10, 20000)
+        assert iters_close(infos[i].iterations, io.iterations)
+        assert rel(xs[i].cpu().numpy(), xo) <= TOL_X
+    # settings: the same answer under every SpMV family and grid
+    rp, c, v = sys_[0]
+    ref = xs[0].cpu().numpy()
+    for var, wg in (("csr", 1), ("split", 2), ("auto", 0)):
+        Ps[0].set_spmv_variant(var)
+        Ps[0].set_workgroups_per_cu(wg)
+        x1, i1 = K.sla_cg_solve(Ps[0], vals[0], bs[0], 1e-10, 20000)
+        torch.cuda.synchronize()
+        assert rel(x1.cpu().numpy(), ref) <= 1e-9
+    # breakdown on -A: NOT_SPD at the first iteration, the same iterate as
+    # the unordered handle's (x0 = 0)
+    neg = t(-v)
+    Q = csr_handle(rp, c)
+    xr, ir = K.sla_cg_solve(Ps[0], neg, bs[0], 1e-10, 100, check=False)
+    xq, iq = K.sla_cg_solve(Q, neg, bs[0], 1e-10, 100, check=False)
+    torch.cuda.synchronize()
+    assert ir.status == K.ERR_NOT_SPD and iq.status == K.ERR_NOT_SPD
+    assert ir.iterations == iq.iterations
+    assert rel(xr.cpu().numpy(), xq.cpu().numpy()) <= 1e-12
