@@ -49,8 +49,10 @@
 namespace sla {
 namespace {
 
-// Gathers a lane keeps in flight while walking its row (plain CSR rows).
-constexpr int kGather = 4;
+// Slots a lane gathers at a time in a plain CSR tile (two rounds cover the
+// kStageLoads slots per lane of a full chunk).
+constexpr int kSlotGather = 3;
+static_assert(kStageLoads % kSlotGather == 0, "whole rounds per chunk");
 // Tiles a wave keeps in flight in the streaming passes.
 constexpr int kStreamTiles = 4;
 
@@ -125,18 +127,23 @@ __device__ __forceinline__ TileIndex<RP> tile_index(const RP* rowptr_, const uin
 
 // Row sum of one lane's row in a wave tile: acc = sum_k vals[k] * v[col[k]]
 // in ascending slot order, starting from 0.  The tile's slots
-// [rowptr[r0], rowptr[r1]) are contiguous: the wave stages them into its LDS
-// areas `lv`/`lc` (`cap` slots) with coalesced loads, in as many chunks as
-// the tile needs, and each lane adds the slots of its row that fall into the
-// chunk, kGather at a time (loads at clamped slots first, then the adds of
-// the slots that exist); the ascending order of every row's sum is kept
-// across chunks.  The lane computes the row `ix` was loaded for; lanes past
-// the last row of the tile compute the tile's last row (see band_row).
-// Every lane of the wave must call it for the same tile.
+// [rowptr[r0], rowptr[r1]) are contiguous; the wave takes them in chunks of
+// `cap`, lane l handling slots l, l + 64, ... of a chunk: it loads their
+// values and columns (coalesced), gathers v at those columns (every lane
+// busy, whatever the row lengths) and stores each product into the wave's
+// LDS area `lv`.  Each lane then adds the products of its own row in slot
+// order.  Every product and sum is rounded on its own, so the row sum has
+// the bits of the sequential sum of vals[k] * v[col[k]].  Slots past the
+// chunk are clamped to its last slot (those lanes store that slot's product
+// again), so no load or store needs a branch.  The lane computes the row
+// `ix` was loaded for; lanes past the last row of the tile compute the
+// tile's last row (see band_row).  Every lane of the wave must call it for
+// the same tile.
 template <typename RP, typename GT>
 __device__ __forceinline__ double wave_tile_row(const int32_t* col_, const double* vals_,
                                                 const TileIndex<RP>& ix, int cap, double* lv,
                                                 int32_t* lc, const GT& g) {
+  (void)lc;
   const SLA_GLOBAL int32_t* __restrict__ col = gmem(col_);
   const SLA_GLOBAL double* __restrict__ vals = gmem(vals_);
   const uint32_t lane = lane_id();
@@ -146,44 +153,34 @@ __device__ __forceinline__ double wave_tile_row(const int32_t* col_, const doubl
   double acc = 0.0;
   for (int64_t c0 = 0; c0 < len; c0 += cap) {
     const int clen = int(len - c0 < cap ? len - c0 : cap);
-    // a lane stages at most kStageLoads slots, all loads first; slots past
-    // the chunk are clamped to its last slot (those lanes store that slot's
-    // own value again), so no load or store needs a branch
     const SLA_GLOBAL double* vb = vals + s0 + c0;
     const SLA_GLOBAL int32_t* cb = col + s0 + c0;
-    double v[kStageLoads];
-    int32_t cc[kStageLoads];
+    // kSlotGather slots per lane at a time: values and columns, then the
+    // gathers, then the products into LDS
+    for (int j0 = 0; j0 < kStageLoads; j0 += kSlotGather) {
+      double v[kSlotGather], gu[kSlotGather], gw[kSlotGather];
+      int32_t cc[kSlotGather];
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
-      const int k = int(lane) + j * kWave;
-      const uint32_t kc = uint32_t(k < clen ? k : clen - 1);
-      v[j] = ld(vb, kc);
-      cc[j] = ld(cb, kc);
-    }
+      for (int j = 0; j < kSlotGather; ++j) {
+        const int k = int(lane) + (j0 + j) * kWave;
+        const uint32_t kc = uint32_t(k < clen ? k : clen - 1);
+        v[j] = ld(vb, kc);
+        cc[j] = ld(cb, kc);
+      }
 #pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
-      const int k = int(lane) + j * kWave;
-      const int kc = k < clen ? k : clen - 1;
-      lv[kc] = v[j];
-      lc[kc] = cc[j];
+      for (int j = 0; j < kSlotGather; ++j) g.load(cc[j], gu[j], gw[j]);
+#pragma unroll
+      for (int j = 0; j < kSlotGather; ++j) {
+        const int k = int(lane) + (j0 + j) * kWave;
+        const int kc = k < clen ? k : clen - 1;
+        lv[kc] = v[j] * g.value(gu[j], gw[j]);
+      }
+      if ((j0 + kSlotGather) * kWave >= clen) break;
     }
     wave_sync();
     const int k0 = int(a > c0 ? a - c0 : 0);
     const int k1 = int(e - c0 < clen ? e - c0 : clen);
-    for (int k = k0; k < k1; k += kGather) {
-      double v[kGather], gu[kGather], gw[kGather];
-#pragma unroll
-      for (int u = 0; u < kGather; ++u) {
-        const int kk = k + u < k1 ? k + u : k1 - 1;
-        v[u] = lv[kk];
-        g.load(lc[kk], gu[u], gw[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kGather; ++u) {
-        const double sum = acc + v[u] * g.value(gu[u], gw[u]);
-        acc = k + u < k1 ? sum : acc;
-      }
-    }
+    for (int k = k0; k < k1; ++k) acc = acc + lv[k];
     wave_sync();
   }
   return acc;
