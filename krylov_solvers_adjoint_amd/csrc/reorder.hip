@@ -16,12 +16,15 @@
 //   s1 = the smallest index among the nodes farthest from s0 (in edges);
 //   a visit from s1, each node's neighbours taken in ascending column order,
 //   then from the smallest unvisited index while nodes remain.
-// It is computed on the device by one workgroup, level by level: every node
-// reached from the current level is claimed by its earliest parent (an
-// atomic minimum of parent positions), each parent counts its claims, a
-// block scan of the counts gives each parent its place, and each parent
+// It is computed on the device level by level, four kernels per level: every
+// node reached from the current level is claimed by its earliest parent (an
+// atomic minimum of parent positions, over the whole grid), each parent
+// counts its claims, one workgroup scans the counts into each parent's place
+// (and starts the next piece when a level claims nothing), and each parent
 // writes its claimed nodes in its row's column order.  The result does not
-// depend on the timing of the atomics, so the order is reproducible.
+// depend on the timing of the atomics, so the order is reproducible.  The
+// level bounds live on the device; the host enqueues blocks of levels and
+// polls a done flag between blocks, as the CG loop does.
 #include <algorithm>
 #include <climits>
 
@@ -47,15 +50,6 @@ constexpr int kBfsWaves = kBfsThreads / kWave;
 inline unsigned blocks_for(int64_t work) {
   const int64_t g = (work + kBlock - 1) / kBlock;
   return unsigned(std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20)));
-}
-
-// Every global write of the workgroup is complete and every wave sees it:
-// agent-scope release, barrier, agent-scope acquire (the acquire drops the
-// CU's vector L1, so later loads read what other waves wrote or claimed).
-__device__ __forceinline__ void bfs_sync() {
-  __threadfence();
-  __syncthreads();
-  __threadfence();
 }
 
 // Exclusive prefix sum of v over the workgroup (thread order); *total gets
@@ -97,172 +91,249 @@ __device__ __forceinline__ int64_t bfs_min(int64_t v, int64_t* lds) {
   return m;
 }
 
-// Largest v over the workgroup.  Every thread must call it.
-__device__ __forceinline__ int64_t bfs_max(int64_t v, int64_t* lds) {
-  return -bfs_min(-v, lds);
+constexpr int kBfsParents = 2;  // parents a thread works on at once
+constexpr int kBfsSlots = 8;    // slots of each parent loaded at once
+constexpr int kBfsLevels = 32;  // levels enqueued between two polls of the host (even)
+
+// Device state of one visit.  The parents of level L are the positions
+// [a[L & 1], b[L & 1]) of the order; the scan of level L writes the bounds of
+// level L + 1 into the other parity.
+struct BfsState {
+  int64_t a[2], b[2];
+  int64_t cursor;  // every index below it is placed (where restarts look)
+  int32_t done;    // the visit is complete: later level kernels return at once
+  int32_t err;     // the bookkeeping disagreed with n (never, for a valid pattern)
+  int32_t s0, s1;
+};
+
+enum : int { kClaim = 0, kCount = 1, kPlace = 2 };
+
+// One pass over the parents q in [a, b) of a level, by every thread of the
+// grid, each taking kBfsParents of them at a time with their row loads issued
+// together:
+//   kClaim: every unplaced neighbour u gets key[u] = min(key[u], q);
+//   kCount: cnt[q - a] = the number of u with key[u] == q still unplaced;
+//   kPlace: those u are written at b + cnt[q - a], b + cnt[q - a] + 1, ...
+//           in column order (cnt holding the scanned counts).
+// A node passes the kCount / kPlace test only for its one claiming parent,
+// so the placements of different parents never touch the same node.
+template <int PH, typename RP>
+__global__ __launch_bounds__(kBlock) void k_bfs_pass(int64_t n, const RP* __restrict__ rowptr,
+                                                     const int32_t* __restrict__ col,
+                                                     int32_t* pos, int32_t* key, int32_t* order,
+                                                     int32_t* cnt, const BfsState* st,
+                                                     int parity) {
+  if (st->done) return;
+  const int64_t a = st->a[parity], b = st->b[parity];
+  constexpr int R = kBfsParents, C = kBfsSlots;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t q0 = a + int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q0 < b;
+       q0 += stride * R) {
+    int64_t q[R], p[R], s[R], e[R], t[R];
+    bool ok[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      q[r] = q0 + int64_t(r) * stride;
+      ok[r] = q[r] < b;
+      p[r] = ok[r] ? order[q[r]] : 0;
+    }
+    int64_t len = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s[r] = int64_t(rowptr[p[r]]);
+      e[r] = ok[r] ? int64_t(rowptr[p[r] + 1]) : s[r];
+      len = e[r] - s[r] > len ? e[r] - s[r] : len;
+      if constexpr (PH == kPlace) t[r] = ok[r] ? b + cnt[q[r] - a] : n;
+    }
+    int32_t c[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) c[r] = 0;
+    for (int64_t k0 = 0; k0 < len; k0 += C) {
+      int32_t u[R][C], pu[R][C], ku[R][C];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const int64_t k = s[r] + k0 + j;
+          u[r][j] = k < e[r] ? col[k] : -1;
+        }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          pu[r][j] = u[r][j] >= 0 ? pos[u[r][j]] : 0;
+          if constexpr (PH != kClaim) ku[r][j] = u[r][j] >= 0 ? key[u[r][j]] : -1;
+        }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const int32_t uu = u[r][j];
+          if constexpr (PH == kClaim) {
+            if (uu >= 0 && pu[r][j] < 0) atomicMin(&key[uu], int32_t(q[r]));
+          } else {
+            const bool f = uu >= 0 && pu[r][j] < 0 && ku[r][j] == int32_t(q[r]);
+            if constexpr (PH == kCount) {
+              c[r] += f ? 1 : 0;
+            } else if (f && t[r] < n) {
+              order[t[r]] = uu;
+              pos[uu] = int32_t(t[r]);
+              ++t[r];
+            }
+          }
+        }
+    }
+    if constexpr (PH == kCount) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (ok[r]) cnt[q[r] - a] = c[r];
+    }
+  }
 }
 
-// One visit structure of the pattern's graph, by one workgroup of
-// kBfsThreads threads.  pos [n] must hold -1 and key [n] INT_MAX on entry;
-// cnt [n] is scratch.
-//   full == 0: start at s0 (found here, written to io[0]), visit the start's
-//              piece only and write s1, the smallest index of its last level,
-//              to io[1];
-//   full == 1: start at io[1] and visit every piece: order [n] receives the
-//              original index of each position.
-// io[2] is set to 1 if the bookkeeping ever disagrees with n (never, for a
-// validated pattern); the kernel then stops.
+// s0: the longest row, smallest index among equals, as the largest key
+// (length << 32) | (INT32_MAX - i) (rows cannot be longer than n < 2^31).
 template <typename RP>
-__global__ __launch_bounds__(kBfsThreads) void k_bfs_order(int64_t n,
-                                                           const RP* __restrict__ rowptr,
-                                                           const int32_t* __restrict__ col,
-                                                           int32_t* pos, int32_t* key,
-                                                           int32_t* order, int32_t* cnt,
-                                                           int32_t* io, int full) {
+__global__ __launch_bounds__(kBlock) void k_bfs_longest(int64_t n, const RP* __restrict__ rowptr,
+                                                        unsigned long long* best) {
+  __shared__ int64_t s_i64[kBlock / kWave];
+  int64_t m = -1;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t len = int64_t(rowptr[i + 1] - rowptr[i]);
+    const int64_t k = (len << 32) | int64_t(INT32_MAX - int32_t(i));
+    m = k > m ? k : m;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const int64_t o = __shfl_xor(m, off, kWave);
+    m = o > m ? o : m;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) s_i64[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int j = 1; j < kBlock / kWave; ++j) m = s_i64[j] > m ? s_i64[j] : m;
+    if (m >= 0) atomicMax(best, (unsigned long long)m);
+  }
+}
+
+// The first node of a visit: s0 (full == 0, from the longest-row key) or s1.
+__global__ void k_bfs_start(BfsState* st, const unsigned long long* best, int32_t* pos,
+                            int32_t* order, int full) {
+  int32_t s;
+  if (!full) {
+    s = INT32_MAX - int32_t(*best & 0xffffffffull);
+    st->s0 = s;
+  } else {
+    s = st->s1;
+  }
+  order[0] = s;
+  pos[s] = 0;
+  st->a[0] = 0;
+  st->b[0] = 1;
+  st->cursor = 0;
+  st->done = 0;
+}
+
+// The end of level `parity`, by one workgroup of kBfsThreads threads: the
+// exclusive scan of the claim counts (cnt, in place) and the bounds of the
+// next level.  When the level claimed nothing, its piece is complete:
+//   full == 0: s1 = the smallest index of the piece's last level; done;
+//   full == 1: the next piece starts at the smallest unplaced index.
+//              Unplaced nodes whose neighbours are all placed are pieces of
+//              their own: they are placed in index order up to the first
+//              node that has an unplaced neighbour, which starts the next
+//              piece; done when every node is placed.
+template <typename RP>
+__global__ __launch_bounds__(kBfsThreads) void k_bfs_scan(int64_t n,
+                                                          const RP* __restrict__ rowptr,
+                                                          const int32_t* __restrict__ col,
+                                                          int32_t* pos, int32_t* order,
+                                                          int32_t* cnt, BfsState* st,
+                                                          int parity, int full) {
   __shared__ int32_t s_i32[kBfsWaves];
   __shared__ int64_t s_i64[kBfsWaves];
+  if (st->done) return;
   const int tid = threadIdx.x;
-  int64_t start;
+  const int64_t a = st->a[parity];
+  int64_t b = st->b[parity];
+  int64_t total = 0;
+  for (int64_t c0 = a; c0 < b; c0 += kBfsThreads) {
+    const int64_t q = c0 + tid;
+    const int32_t v = q < b ? cnt[q - a] : 0;
+    int32_t chunk = 0;
+    const int32_t ex = bfs_scan(v, s_i32, &chunk);
+    if (q < b) cnt[q - a] = int32_t(total) + ex;
+    total += chunk;
+  }
+  if (b + total > n) {
+    if (tid == 0) {
+      st->err = 1;
+      st->done = 1;
+    }
+    return;
+  }
+  if (total > 0) {
+    if (tid == 0) {
+      st->a[parity ^ 1] = b;
+      st->b[parity ^ 1] = b + total;
+    }
+    return;
+  }
   if (!full) {
-    // s0: the longest row, smallest index among equals (rows longer than
-    // 2^31 slots cannot occur: columns in a row are distinct and below n)
-    int64_t best = -1;
-    for (int64_t i = tid; i < n; i += kBfsThreads) {
-      const int64_t len = int64_t(rowptr[i + 1] - rowptr[i]);
-      const int64_t k = (len << 32) | int64_t(INT32_MAX - int32_t(i));
-      best = k > best ? k : best;
+    int64_t m = INT64_MAX;
+    for (int64_t q = a + tid; q < b; q += kBfsThreads) m = order[q] < m ? order[q] : m;
+    m = bfs_min(m, s_i64);
+    if (tid == 0) {
+      st->s1 = int32_t(m);
+      st->done = 1;
     }
-    best = bfs_max(best, s_i64);
-    start = int64_t(INT32_MAX - int32_t(best & 0xffffffff));
-    if (tid == 0) io[0] = int32_t(start);
-  } else {
-    start = io[1];
+    return;
   }
-  if (tid == 0) {
-    order[0] = int32_t(start);
-    pos[start] = 0;
-  }
-  bfs_sync();
-  int64_t a = 0, b = 1, cursor = 0;
-  // each pass of the loop places at least one node or returns
-  for (int64_t guard = 0; guard <= n + 1; ++guard) {
-    // claims: every unplaced neighbour of the level gets its earliest parent
-    for (int64_t q = a + tid; q < b; q += kBfsThreads) {
-      const int64_t p = order[q];
-      const int64_t e = int64_t(rowptr[p + 1]);
-      for (int64_t k = int64_t(rowptr[p]); k < e; ++k) {
+  int64_t cursor = st->cursor;
+  while (b < n && cursor < n) {
+    const int64_t i = cursor + tid;
+    bool un = false, alone = false;
+    if (i < n && pos[i] < 0) {
+      un = true;
+      alone = true;
+      const int64_t e = int64_t(rowptr[i + 1]);
+      for (int64_t k = int64_t(rowptr[i]); k < e; ++k) {
         const int32_t u = col[k];
-        if (pos[u] < 0) atomicMin(&key[u], int32_t(q));
+        if (u != int32_t(i) && pos[u] < 0) alone = false;
       }
     }
-    bfs_sync();
-    // counts of claims per parent
-    for (int64_t q = a + tid; q < b; q += kBfsThreads) {
-      const int64_t p = order[q];
-      const int64_t e = int64_t(rowptr[p + 1]);
-      int32_t c = 0;
-      for (int64_t k = int64_t(rowptr[p]); k < e; ++k) {
-        const int32_t u = col[k];
-        c += (pos[u] < 0 && key[u] == int32_t(q)) ? 1 : 0;
-      }
-      cnt[q - a] = c;
+    const int64_t f = bfs_min(un && !alone ? i : INT64_MAX, s_i64);
+    const bool place = un && alone && i < f;
+    int32_t placed = 0;
+    const int32_t rk = bfs_scan(place ? 1 : 0, s_i32, &placed);
+    if (place && b + rk < n) {
+      order[b + rk] = int32_t(i);
+      pos[i] = int32_t(b + rk);
     }
-    bfs_sync();
-    // exclusive scan of the counts, in chunks of the workgroup's size
-    int64_t total = 0;
-    for (int64_t c0 = a; c0 < b; c0 += kBfsThreads) {
-      const int64_t q = c0 + tid;
-      const int32_t v = q < b ? cnt[q - a] : 0;
-      int32_t chunk = 0;
-      const int32_t ex = bfs_scan(v, s_i32, &chunk);
-      if (q < b) cnt[q - a] = int32_t(total) + ex;
-      total += chunk;
-    }
-    if (b + total > n) {
-      if (tid == 0) io[2] = 1;
-      return;
-    }
-    bfs_sync();
-    // placement: each parent writes its claims in column order
-    for (int64_t q = a + tid; q < b; q += kBfsThreads) {
-      const int64_t p = order[q];
-      const int64_t e = int64_t(rowptr[p + 1]);
-      int64_t t = b + cnt[q - a];
-      for (int64_t k = int64_t(rowptr[p]); k < e; ++k) {
-        const int32_t u = col[k];
-        if (pos[u] < 0 && key[u] == int32_t(q) && t < n) {
-          order[t] = u;
-          pos[u] = int32_t(t);
-          ++t;
-        }
-      }
-    }
-    bfs_sync();
-    if (total > 0) {
-      a = b;
-      b += total;
-      continue;
-    }
-    // the piece is complete; [a, b) is its last level
-    if (!full) {
-      int64_t m = INT64_MAX;
-      for (int64_t q = a + tid; q < b; q += kBfsThreads) m = order[q] < m ? order[q] : m;
-      m = bfs_min(m, s_i64);
-      if (tid == 0) io[1] = int32_t(m);
-      return;
-    }
-    if (b >= n) return;
-    // the next piece starts at the smallest unplaced index.  Unplaced nodes
-    // whose neighbours are all placed are pieces of their own: they are
-    // placed in index order up to the first node that has an unplaced
-    // neighbour, which starts the next visit.
-    bool started = false;
-    while (cursor < n) {
-      const int64_t i = cursor + tid;
-      bool un = false, alone = false;
-      if (i < n && pos[i] < 0) {
-        un = true;
-        alone = true;
-        const int64_t e = int64_t(rowptr[i + 1]);
-        for (int64_t k = int64_t(rowptr[i]); k < e; ++k) {
-          const int32_t u = col[k];
-          if (u != int32_t(i) && pos[u] < 0) alone = false;
-        }
-      }
-      const int64_t f = bfs_min(un && !alone ? i : INT64_MAX, s_i64);
-      const bool place = un && alone && i < f;
-      int32_t placed = 0;
-      const int32_t rk = bfs_scan(place ? 1 : 0, s_i32, &placed);
-      if (place && b + rk < n) {
-        order[b + rk] = int32_t(i);
-        pos[i] = int32_t(b + rk);
-      }
-      b += placed;
-      if (f != INT64_MAX) {
-        if (b >= n) {
-          if (tid == 0) io[2] = 1;
-          return;
-        }
-        if (tid == 0) {
+    b += placed;
+    if (f != INT64_MAX) {
+      if (tid == 0) {
+        if (b < n) {
           order[b] = int32_t(f);
           pos[f] = int32_t(b);
+          st->a[parity ^ 1] = b;
+          st->b[parity ^ 1] = b + 1;
+          st->cursor = f + 1;
+        } else {
+          st->err = 1;
+          st->done = 1;
         }
-        a = b;
-        b += 1;
-        cursor = f + 1;
-        started = true;
-        bfs_sync();
-        break;
       }
-      cursor += kBfsThreads;
-      bfs_sync();
-    }
-    if (!started) {
-      if (b != n && tid == 0) io[2] = 1;
       return;
     }
+    cursor += kBfsThreads;
+    __syncthreads();  // the placements above before the next chunk's tests
   }
-  if (tid == 0) io[2] = 1;
+  if (tid == 0) {
+    if (b != n) st->err = 1;
+    st->done = 1;
+  }
 }
 
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
@@ -321,37 +392,76 @@ __global__ void k_scatter_vec(int64_t n, const int32_t* __restrict__ order,
 template <typename RP>
 sla_status compute_order(sla_csr A, int32_t* order, int32_t* pos, hipStream_t st) {
   const int64_t n = A->n;
+  const RP* rp = static_cast<const RP*>(A->rowptr);
   int32_t* key = nullptr;
   int32_t* cnt = nullptr;
-  int32_t* io = nullptr;
+  BfsState* state = nullptr;
+  unsigned long long* best = nullptr;
+  int32_t* poll = nullptr;  // pinned: the done flag after each block of levels
+  hipEvent_t ev[2] = {nullptr, nullptr};
   sla_status s = dev_alloc(&key, size_t(n), "ordering keys");
   if (s == SLA_OK) s = dev_alloc(&cnt, size_t(n), "ordering counts");
-  if (s == SLA_OK) s = dev_alloc(&io, 4, "ordering scalars");
-  int32_t hio[4] = {0, 0, 0, 0};
+  if (s == SLA_OK) s = dev_alloc(&state, 1, "ordering state");
+  if (s == SLA_OK) s = dev_alloc(&best, 1, "longest row");
   hipError_t e = hipSuccess;
-  if (s == SLA_OK) {
-    const RP* rp = static_cast<const RP*>(A->rowptr);
-    k_fill_i32<<<blocks_for(4), kBlock, 0, st>>>(io, 4, 0);
-    for (int full = 0; full <= 1 && e == hipSuccess; ++full) {
-      k_fill_i32<<<blocks_for(n), kBlock, 0, st>>>(pos, n, -1);
-      k_fill_i32<<<blocks_for(n), kBlock, 0, st>>>(key, n, INT32_MAX);
-      // every position holds a valid node before it is written
-      k_fill_i32<<<blocks_for(n), kBlock, 0, st>>>(order, n, 0);
-      k_bfs_order<RP><<<1, kBfsThreads, 0, st>>>(n, rp, A->col, pos, key, order, cnt, io, full);
-      e = hipGetLastError();
+  if (s == SLA_OK) e = hipHostMalloc(reinterpret_cast<void**>(&poll), 2 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev[0], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev[1], hipEventDisableTiming);
+  BfsState hs{};
+  const unsigned pass_grid = unsigned(std::max(1, device_cus()));
+  // every level places at least one node or ends the visit
+  const int64_t max_blocks = (n + 1) / kBfsLevels + 2;
+  for (int full = 0; full <= 1 && s == SLA_OK && e == hipSuccess; ++full) {
+    k_fill_i32<<<blocks_for(n), kBlock, 0, st>>>(pos, n, -1);
+    k_fill_i32<<<blocks_for(n), kBlock, 0, st>>>(key, n, INT32_MAX);
+    // every position holds a valid node before it is written
+    k_fill_i32<<<blocks_for(n), kBlock, 0, st>>>(order, n, 0);
+    if (!full) {
+      e = hipMemsetAsync(state, 0, sizeof(BfsState), st);
+      if (e == hipSuccess) e = hipMemsetAsync(best, 0, sizeof(unsigned long long), st);
+      if (e == hipSuccess) k_bfs_longest<RP><<<blocks_for(n), kBlock, 0, st>>>(n, rp, best);
     }
-    if (e == hipSuccess) e = hipMemcpyAsync(hio, io, sizeof(hio), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) k_bfs_start<<<1, 1, 0, st>>>(state, best, pos, order, full);
+    for (int64_t blk = 0; blk < max_blocks && e == hipSuccess; ++blk) {
+      for (int j = 0; j < kBfsLevels; ++j) {
+        const int par = j & 1;
+        k_bfs_pass<kClaim, RP><<<pass_grid, kBlock, 0, st>>>(n, rp, A->col, pos, key, order, cnt,
+                                                             state, par);
+        k_bfs_pass<kCount, RP><<<pass_grid, kBlock, 0, st>>>(n, rp, A->col, pos, key, order, cnt,
+                                                             state, par);
+        k_bfs_scan<RP><<<1, kBfsThreads, 0, st>>>(n, rp, A->col, pos, order, cnt, state, par,
+                                                   full);
+        k_bfs_pass<kPlace, RP><<<pass_grid, kBlock, 0, st>>>(n, rp, A->col, pos, key, order, cnt,
+                                                             state, par);
+      }
+      e = hipGetLastError();
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(poll + (blk & 1), &state->done, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, st);
+      if (e == hipSuccess) e = hipEventRecord(ev[blk & 1], st);
+      // wait for the previous block only, so that one block is always queued
+      if (e == hipSuccess && blk >= 1) {
+        e = hipEventSynchronize(ev[(blk - 1) & 1]);
+        if (e == hipSuccess && poll[(blk - 1) & 1]) break;
+      }
+    }
+    if (e == hipSuccess) e = hipMemcpyAsync(&hs, state, sizeof(hs), hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess && (!hs.done || hs.err)) break;
   }
+  if (ev[0]) (void)hipEventDestroy(ev[0]);
+  if (ev[1]) (void)hipEventDestroy(ev[1]);
+  if (poll) (void)hipHostFree(poll);
   dev_free(key);
   dev_free(cnt);
-  dev_free(io);
+  dev_free(state);
+  dev_free(best);
   if (s != SLA_OK) return s;
   if (e != hipSuccess) {
     set_error("ordering: %s", hipGetErrorString(e));
     return SLA_ERR_DEVICE;
   }
-  if (hio[2] != 0) {
+  if (!hs.done || hs.err) {
     set_error("ordering: inconsistent visit (internal error)");
     return SLA_ERR_DEVICE;
   }
