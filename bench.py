@@ -293,6 +293,56 @@ def bench_batch64(kernel_reps: int):
     return out
 
 
+def bench_poisson32():
+    """The 32 x 32 Poisson workload (tol 1e-10, forward + adjoint; b ~ U(-1,1)
+    seed 0, g ~ N(0,1) seed 1) and a batch of 256 shifted 32 x 32 systems,
+    each through the one-workgroup CG loop (the default at this size) and the
+    two-kernel loop; median of 20 timed calls."""
+    import numpy as np
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    rp, c, v = W.poisson_csr(32)
+    rpt, ct = torch.from_numpy(rp).to(dev), torch.from_numpy(c).to(dev)
+    vt = torch.from_numpy(v).to(dev)
+    bt = torch.from_numpy(W.uniform_rhs(1024, 0)).to(dev)
+    gt = torch.from_numpy(W.normal_rhs(1024, 1)).to(dev)
+    rpb, cb, vals_b, b_b, _ = W.batched_poisson(32, 256, 2, 3)
+    vbt = torch.from_numpy(vals_b).to(dev)
+    bbt = torch.from_numpy(b_b).to(dev)
+    gbt = torch.from_numpy(W.normal_rhs(1024, 4, shape=(256, 1024))).to(dev)
+    out = {}
+    for mode, key in (("auto", "one_group"), ("off", "two_kernel")):
+        P = K.sla_csr_create_from_csr(rpt, ct)
+        P.set_one_group(mode)
+        times, btimes = [], []
+        for rep in range(22):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            x, fi = K.sla_cg_solve(P, vt, bt, 1e-10, 10000)
+            gb, gv, ai = K.sla_cg_adjoint(P, vt, x, gt, 1e-10, 10000)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            xb, fb = K.sla_cg_solve_batched(P, vbt, bbt, 1e-10, 10000)
+            gbb, gvb, ab = K.sla_cg_adjoint_batched(P, vbt, xb, gbt, 1e-10, 10000)
+            torch.cuda.synchronize()
+            btimes.append(time.perf_counter() - t0)
+        ms = 1e3 * float(np.median(times[2:]))
+        bms = 1e3 * float(np.median(btimes[2:]))
+        its = fi.iterations + ai.iterations
+        steps = max(i.iterations for i in fb) + max(i.iterations for i in ab)
+        out[key] = dict(iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
+                        solve_adjoint_ms=ms, us_per_iteration=1e3 * ms / its,
+                        batch256_ms=bms, batch256_us_per_step=1e3 * bms / steps)
+        del P
+    out["speedup"] = out["two_kernel"]["solve_adjoint_ms"] / out["one_group"]["solve_adjoint_ms"]
+    out["batch256_speedup"] = out["two_kernel"]["batch256_ms"] / out["one_group"]["batch256_ms"]
+    torch.cuda.synchronize()
+    return out
+
+
 def bench_rgg(n: int, kernel_reps: int):
     """Random geometric graph Laplacian + 0.01 I (4M nodes, ~9 slots per row,
     random node order): CSR built on the GPU from COO, then CG to 1e-8 and the
@@ -704,10 +754,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--sizes", default="16m,169m,rgg4m,batch64",
+    ap.add_argument("--sizes", default="16m,169m,rgg4m,batch64,poisson32",
                     help="extra workloads: 16m / 169m (Poisson, 500 fixed iterations), rgg4m "
                          "(random geometric graph, tol 1e-8 forward + adjoint), batch64 (64 "
-                         "Poisson 128^2 systems on one pattern); '' for none; with "
+                         "Poisson 128^2 systems on one pattern), poisson32 (32^2, tol 1e-10, "
+                         "and 256 such systems); '' for none; with "
                          "--skip-headline also matvec, eigsh, bicgstab and list")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -762,6 +813,9 @@ def main():
             if s.lower() == "batch64":
                 log(f"[bench] batch64: {bench_batch64(args.kernel_reps)}")
                 continue
+            if s.lower() == "poisson32":
+                log(f"[bench] poisson32: {bench_poisson32()}")
+                continue
             if s.lower() == "bicgstab":
                 log(f"[bench] bicgstab: {bench_bicgstab()}")
                 continue
@@ -783,6 +837,14 @@ def main():
     sizes = {}
     for s in [s for s in args.sizes.split(",") if s]:
         import numpy as np
+        if s.lower() == "poisson32":
+            log("[bench] size poisson32: 32x32 Poisson, tol 1e-10, forward + adjoint")
+            sizes["poisson32"] = bench_poisson32()
+            og, tk = sizes["poisson32"]["one_group"], sizes["poisson32"]["two_kernel"]
+            log(f"[bench] size poisson32: {og['solve_adjoint_ms']:.3f} ms one workgroup, "
+                f"{tk['solve_adjoint_ms']:.3f} ms two-kernel loop; 256 systems "
+                f"{og['batch256_ms']:.3f} / {tk['batch256_ms']:.3f} ms")
+            continue
         if s.lower() == "batch64":
             log("[bench] size batch64: 64 Poisson 128x128 systems, shared pattern, tol 1e-8")
             sizes["batch64"] = bench_batch64(args.kernel_reps)

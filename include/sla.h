@@ -469,6 +469,21 @@ sla_status sla_csr_reorder(sla_csr A, int ordering, hipStream_t stream);
  * `stream`.  SLA_ERR_ARG if the handle is not reordered. */
 sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
 
+/*
+ * CG loop of small systems.  SLA_ONE_GROUP_AUTO (default): a system of at
+ * most 16384 unknowns runs its whole CG loop in one workgroup (one launch per
+ * solve, one workgroup per system of the batch, workgroup barriers only),
+ * instead of two kernels over the whole GPU per iteration, whose launch gaps
+ * and partial sums dominate at such sizes (Problem statement: launch costs
+ * of iterative solvers on small problems).  The same steps, stopping rule,
+ * statuses and history; the dot products are summed in another order, so the
+ * results differ from the two-kernel loop's in the last bits.
+ * SLA_ONE_GROUP_OFF: always the two-kernel loop.  Applies to sla_cg_solve /
+ * _batched, the adjoint solves and the CG lists.
+ */
+enum { SLA_ONE_GROUP_AUTO = 0, SLA_ONE_GROUP_OFF = 1 };
+sla_status sla_csr_set_one_group(sla_csr A, int mode);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* sla_last_error(void);
 

@@ -43,6 +43,7 @@ METHOD_CG, METHOD_BICGSTAB = 0, 1
 I32, I64 = 4, 8
 FLAG_X0, FLAG_HISTORY, FLAG_JACOBI = 1, 2, 4
 ORDER_NONE, ORDER_BFS = 0, 1
+ONE_GROUP_AUTO, ONE_GROUP_OFF = 0, 1
 
 EXPORTS = [
     "sla_csr_create", "sla_csr_create_from_csr", "sla_csr_destroy", "sla_csr_get_info",
@@ -55,7 +56,7 @@ EXPORTS = [
     "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_solve_list", "sla_adjoint_list", "sla_csr_reorder", "sla_csr_ordering",
-    "sla_last_error", "sla_status_string",
+    "sla_csr_set_one_group", "sla_last_error", "sla_status_string",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -115,6 +116,7 @@ def _bind(lib):
         "sla_adjoint_list": [_I64, _P, _P, _P, _P, _P, _D, _I64, _U32, _S, _P, _P],
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
         "sla_csr_reorder": [_P, _S, _P],
+        "sla_csr_set_one_group": [_P, _S],
         "sla_csr_ordering": [_P, _P, _P],
     }
     for name, args in sig.items():
@@ -253,6 +255,12 @@ class CSRPattern:
 
     def set_workgroups_per_cu(self, workgroups: int):
         _check(_lib.sla_csr_set_workgroups_per_cu(self._h, int(workgroups)))
+
+    def set_one_group(self, mode: str = "auto"):
+        """"auto": systems of up to 16384 unknowns run the CG loop in one
+        workgroup per system; "off": always the two-kernel loop."""
+        _check(_lib.sla_csr_set_one_group(self._h, {"auto": ONE_GROUP_AUTO,
+                                                    "off": ONE_GROUP_OFF}[mode]))
 
     def _kernels(self) -> int:
         b = _S()

@@ -700,6 +700,17 @@ sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups) {
   API_END
 }
 
+sla_status sla_csr_set_one_group(sla_csr A, int mode) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_set_one_group: NULL handle");
+  REQUIRE(mode == SLA_ONE_GROUP_AUTO || mode == SLA_ONE_GROUP_OFF,
+          "sla_csr_set_one_group: unknown mode %d", mode);
+  for (sla_csr H : {A, solver_handle(A)}) H->one_group = mode;
+  return SLA_OK;
+  API_END
+}
+
 sla_status sla_csr_reorder(sla_csr A, int ordering, hipStream_t stream) {
   API_BEGIN
   clear_error();

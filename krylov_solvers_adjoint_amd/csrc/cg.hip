@@ -952,6 +952,236 @@ void k_cg_product(const Ctx* __restrict__ c) {
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
+// ---------------------------------------------------------------------------
+// Small systems: one workgroup per system, the whole CG loop in one launch
+// ---------------------------------------------------------------------------
+// For a system of at most kOneGroupRows * kIterBlock unknowns whose 64-row
+// tiles hold at most kWaveCap slots each, the two-kernel iteration is bound
+// by launch gaps and by every workgroup summing partials.  Here one workgroup
+// owns a system and iterates with workgroup barriers only (no cross-workgroup
+// signal exists), with nothing in memory but LDS:
+//   * thread t owns rows t + j * kIterBlock (j < R) and keeps their r, x, p
+//     (and the Jacobi diagonal) in registers;
+//   * wave w owns tiles w + j * kWaves; lane l holds the values and columns
+//     of slots l, l + 64, ... of each of its tiles in registers, loaded once;
+//   * p is published in LDS; an SpMV gathers p from LDS at the held columns,
+//     stores the products in the wave's LDS area and each lane adds its own
+//     row's products in slot order (the bits of the sequential row sum).
+// Same steps, stopping rule, statuses and history as the two-kernel loop; the
+// x update is applied at once rather than one step late (the same
+// expression); the dot products are summed in another fixed order.
+
+// Two sums over the workgroup at once, fixed order, results in every thread.
+__device__ __forceinline__ void block_sum2(double& u, double& v, double* lds) {
+  u = wave_sum(u);
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds[threadIdx.x / kWave] = u;
+    lds[kWaves + threadIdx.x / kWave] = v;
+  }
+  __syncthreads();
+  double a = 0.0, b = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    a = a + lds[w];
+    b = b + lds[kWaves + w];
+  }
+  __syncthreads();
+  u = a;
+  v = b;
+}
+
+// LDS of the small-system kernel: p [n rounded up to the workgroup] and one
+// product area of kWaveCap doubles per wave.
+size_t one_group_lds_bytes(int64_t n) {
+  const int64_t rows = (n + kIterBlock - 1) / kIterBlock * kIterBlock;
+  return size_t(rows + int64_t(kWaves) * kWaveCap) * sizeof(double);
+}
+
+template <typename RP, int R, bool JAC>
+__global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restrict__ c,
+                                                            double tol, int64_t maxit,
+                                                            int use_x0) {
+  extern __shared__ double lds_dyn[];
+  __shared__ double red[2 * kWaves];
+  const int64_t s = blockIdx.x;
+  const int64_t n = c->n, nnz = c->nnz;
+  const int64_t npad = (n + kIterBlock - 1) / kIterBlock * kIterBlock;
+  double* pl = lds_dyn;                                         // p, or x0 at set-up
+  double* prod = lds_dyn + npad + int64_t(wave_index()) * kWaveCap;  // this wave's products
+  const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(c->rowptr));
+  const SLA_GLOBAL int32_t* col = gmem(c->col);
+  const SLA_GLOBAL double* vals = gmem(c->vals + s * nnz);
+  const SLA_GLOBAL double* b = gmem(c->b + s * n);
+  SLA_GLOBAL double* x = gmem(c->x + s * n);
+  SLA_GLOBAL double* hist = c->hist != nullptr ? gmem(c->hist + s * c->hist_cap * 3) : nullptr;
+  const int64_t hist_cap = c->hist_cap;
+  const int t = threadIdx.x;
+  const int lane = int(lane_id());
+  // this thread's rows and tiles; the held slots of each tile
+  int64_t row[R];
+  int rlen[R], ra[R], re[R];   // tile length; the row's slots [ra, re) in the tile
+  double hv[R][kStageLoads];
+  int32_t hc[R][kStageLoads];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int64_t r0 = (int64_t(j) * kWaves + wave_index()) * kTileRows;
+    row[j] = r0 + lane;
+    rlen[j] = ra[j] = re[j] = 0;
+    if (r0 < n) {
+      const int64_t last = (r0 + kTileRows < n ? r0 + kTileRows : n);
+      const int64_t s0 = int64_t(rowptr[r0]);
+      rlen[j] = int(int64_t(rowptr[last]) - s0);
+      if (row[j] < n) {
+        ra[j] = int(int64_t(rowptr[row[j]]) - s0);
+        re[j] = int(int64_t(rowptr[row[j] + 1]) - s0);
+      }
+#pragma unroll
+      for (int m = 0; m < kStageLoads; ++m) {
+        const int k = lane + m * kWave;
+        const int kc = k < rlen[j] ? k : (rlen[j] > 0 ? rlen[j] - 1 : 0);
+        hv[j][m] = rlen[j] > 0 ? vals[s0 + kc] : 0.0;
+        hc[j][m] = rlen[j] > 0 ? col[s0 + kc] : 0;
+      }
+    }
+  }
+  // q = A v for this thread's rows, v published in pl (every wave works on
+  // its own tiles; the caller has made pl visible)
+  auto spmv = [&](double (&q)[R]) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      q[j] = 0.0;
+      if (rlen[j] > 0) {  // wave-uniform
+#pragma unroll
+        for (int m = 0; m < kStageLoads; ++m) {
+          const int k = lane + m * kWave;
+          if (k < rlen[j]) prod[k] = hv[j][m] * pl[hc[j][m]];
+        }
+        wave_sync();
+        double acc = 0.0;
+        for (int k = ra[j]; k < re[j]; ++k) acc = acc + prod[k];
+        q[j] = acc;
+        wave_sync();  // the area is reused by the next tile
+      }
+    }
+  };
+  double r[R], xv[R], pv[R], dv[R], q[R];
+  // r0 = b - A x0 (or b, x0 = 0); the Jacobi diagonal
+  if (use_x0) {
+    for (int64_t i = t; i < npad; i += kIterBlock) pl[i] = i < n ? x[i] : 0.0;
+    __syncthreads();
+    spmv(q);
+    __syncthreads();
+  }
+  double bb = 0.0, rr = 0.0, rz = 0.0, bad = 0.0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int64_t i = t + int64_t(j) * kIterBlock;
+    r[j] = xv[j] = pv[j] = 0.0;
+    dv[j] = 1.0;
+    if (i < n) {
+      const double bi = b[i];
+      xv[j] = use_x0 ? x[i] : 0.0;
+      r[j] = use_x0 ? bi - q[j] : bi;
+      bb = bb + bi * bi;
+      rr = rr + r[j] * r[j];
+      if constexpr (JAC) {
+        double d = 0.0;  // the stored diagonal entry (0 when the row has none)
+        for (int64_t k = int64_t(rowptr[i]); k < int64_t(rowptr[i + 1]); ++k)
+          if (col[k] == i) d = vals[k];
+        dv[j] = d;
+        bad = (d > 0.0) ? bad : 1.0;
+        rz = rz + r[j] * (r[j] / d);
+      }
+    }
+  }
+  block_sum2(bb, rr, red);
+  if constexpr (JAC) block_sum2(rz, bad, red);
+  const double stop = (tol * tol) * bb;
+  int32_t state = (!isfinite(bb) || !isfinite(rr) || !isfinite(rz)) ? ST_NONFINITE : ST_RUNNING;
+  if (JAC && bad != 0.0) state = ST_NOT_SPD;  // a diagonal entry is not > 0
+  int64_t it = 0;
+  double rr_final = rr;
+  double alpha = 0.0, rr_prev = rr, rz_prev = rz;
+  // every thread holds the same scalars, so every branch below is uniform
+  for (int64_t k = 0; state == ST_RUNNING; ++k) {
+    double beta = 0.0;
+    if (k > 0) {
+      if (!isfinite(rr) || !isfinite(rz)) {
+        state = ST_NONFINITE;  // iteration k-1 did not complete
+        it = k - 1;
+        rr_final = rr_prev;
+        break;
+      }
+      beta = JAC ? rz / rz_prev : rr / rr_prev;
+      if (hist != nullptr && t == 0 && k - 1 < hist_cap) {
+        hist[(k - 1) * 3 + 0] = alpha;
+        hist[(k - 1) * 3 + 1] = beta;
+        hist[(k - 1) * 3 + 2] = rr;
+      }
+    }
+    if (rr <= stop || k >= maxit) {
+      state = rr <= stop ? ST_CONVERGED : ST_MAXIT;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    // p_k = r_k (z_k) + beta p_{k-1}, published in LDS for the gathers
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const double src = JAC ? r[j] / dv[j] : r[j];
+      pv[j] = src + beta * pv[j];
+      const int64_t i = t + int64_t(j) * kIterBlock;
+      if (i < npad) pl[i] = pv[j];
+    }
+    __syncthreads();
+    spmv(q);
+    double pq = 0.0, zero = 0.0;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (t + int64_t(j) * kIterBlock < n) pq = pq + pv[j] * q[j];
+    // (the barriers of the sum also end every wave's gathers of p_k)
+    block_sum2(pq, zero, red);
+    if (!isfinite(pq) || !(pq > 0.0)) {
+      state = !isfinite(pq) ? ST_NONFINITE : ST_NOT_SPD;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    alpha = (JAC ? rz : rr) / pq;
+    double rn = 0.0, rzn = 0.0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (t + int64_t(j) * kIterBlock < n) {
+        xv[j] = xv[j] + alpha * pv[j];
+        r[j] = r[j] - alpha * q[j];
+        rn = rn + r[j] * r[j];
+        if constexpr (JAC) rzn = rzn + r[j] * (r[j] / dv[j]);
+      }
+    }
+    block_sum2(rn, rzn, red);
+    rr_prev = rr;
+    rz_prev = rz;
+    rr = rn;
+    rz = rzn;
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int64_t i = t + int64_t(j) * kIterBlock;
+    if (i < n) x[i] = xv[j];
+  }
+  if (t == 0) {
+    Scal* sc = c->scal + s;
+    sc->bb = bb;
+    sc->stop = stop;
+    sc->maxit = maxit;
+    sc->it = it;
+    sc->rr_final = rr_final;
+    sc->state_a = state;
+    sc->state_r = state;
+  }
+}
+
 // Residual step k (see the file comment).  JAC: Jacobi preconditioning, so
 // alpha = r.z / p.Ap, and the step also writes z = r / d and the r.z partials.
 template <bool JAC>
@@ -1435,6 +1665,45 @@ sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda, c
   return launch_slot_products(A, batch, lambda, x, grad_vals, true, st);
 }
 
+static sla_status finish_cg(sla_csr A, int64_t batch, sla_cg_info* info, hipStream_t st);
+
+// Rows per thread of the small-system kernel (1 or 2), 0 when it does not
+// apply: more than kOneGroupRows * kIterBlock unknowns, a 64-row tile with
+// more slots than a wave holds, or LDS beyond the device's limit.
+static int one_group_rows(const sla_csr A) {
+  if (A->n <= 0 || A->n > int64_t(kOneGroupRows) * kIterBlock) return 0;
+  if (A->max_tile_nnz > kWaveCap) return 0;
+  int lim = 0;
+  if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, A->device) !=
+          hipSuccess ||
+      one_group_lds_bytes(A->n) + 2 * kWaves * sizeof(double) > size_t(lim))
+    return 0;
+  return A->n <= kIterBlock ? 1 : 2;
+}
+
+bool use_one_group(const sla_csr A) {
+  return A->one_group == SLA_ONE_GROUP_AUTO && one_group_rows(A) > 0;
+}
+
+static sla_status launch_one_group(sla_csr A, int64_t batch, bool jac, double tol,
+                                   int64_t maxit, bool x0, hipStream_t st) {
+  const size_t lds = one_group_lds_bytes(A->n);
+  const unsigned g = unsigned(batch);
+  const int u = x0 ? 1 : 0;
+  const bool two = one_group_rows(A) == 2;
+  if (A->rp_idx == SLA_I32) {
+    auto k = two ? (jac ? k_cg_onegroup<int32_t, 2, true> : k_cg_onegroup<int32_t, 2, false>)
+                 : (jac ? k_cg_onegroup<int32_t, 1, true> : k_cg_onegroup<int32_t, 1, false>);
+    k<<<g, kIterBlock, lds, st>>>(A->ctx_dev, tol, maxit, u);
+  } else {
+    auto k = two ? (jac ? k_cg_onegroup<int64_t, 2, true> : k_cg_onegroup<int64_t, 2, false>)
+                 : (jac ? k_cg_onegroup<int64_t, 1, true> : k_cg_onegroup<int64_t, 1, false>);
+    k<<<g, kIterBlock, lds, st>>>(A->ctx_dev, tol, maxit, u);
+  }
+  LAUNCH_CHECK();
+  return SLA_OK;
+}
+
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
                   uint32_t flags, sla_cg_info* info, hipStream_t st) {
   const int64_t batch = A->batch;
@@ -1464,6 +1733,10 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
   SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
 
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
+  if (use_one_group(A)) {
+    SLA_TRY(launch_one_group(A, batch, jacobi, tol, maxit, x0, st));
+    return finish_cg(A, batch, info, st);
+  }
   if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, A->q, st));  // q = A x0
   const dim3 grid2(unsigned(A->grid), unsigned(batch));
   if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
@@ -1493,6 +1766,12 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
       }
     }
   }
+  return finish_cg(A, batch, info, st);
+}
+
+// The per-system scalars back to the host, the infos and the status of the
+// solve (the first failing system's).
+static sla_status finish_cg(sla_csr A, int64_t batch, sla_cg_info* info, hipStream_t st) {
   SLA_TRY_HIP(hipMemcpyAsync(A->scal_host, A->scal, sizeof(Scal) * batch,
                              hipMemcpyDeviceToHost, st));
   SLA_TRY_HIP(hipStreamSynchronize(st));

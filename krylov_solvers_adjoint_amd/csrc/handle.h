@@ -77,6 +77,9 @@ struct sla_csr_s {
   int64_t graph_block = 32;
   // solver workgroups per compute unit: 1, 2, or 0 (by problem size)
   int32_t wg_per_cu = 0;
+  // SLA_ONE_GROUP_AUTO: systems of up to 16384 unknowns run the CG loop in
+  // one workgroup per system; SLA_ONE_GROUP_OFF: always the two-kernel loop
+  int32_t one_group = SLA_ONE_GROUP_AUTO;
   // grid line length L of a band whose far offsets are +-L and whose other
   // offsets lie within +-63 (0: the line walk does not apply)
   int64_t line = 0;
@@ -98,6 +101,7 @@ sla_status ensure_workspace(sla_csr A, int64_t batch);
 bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
 bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
 bool use_lines(const sla_csr A);  // line-walk SpMV step (a banded pattern with far offsets +-L)?
+bool use_one_group(const sla_csr A);  // the one-workgroup-per-system CG loop?
 // y[s] = A_s^T x[s] (builds the transposed pattern on first use)
 sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t st);
 // grad_vals[s][k] = sign * g[s][i] * x[s][col[k]] on every stored slot

@@ -565,6 +565,7 @@ static sla_status prepare(sla_csr A, hipStream_t st) {
   Reorder* R = A->ro;
   sla_csr B = R->B;
   const int64_t batch = A->batch;
+  B->one_group = A->one_group;
   if (B->spmv_variant != A->spmv_variant || B->graph_block != A->graph_block ||
       B->wg_per_cu != A->wg_per_cu) {
     SLA_TRY_HIP(hipStreamSynchronize(st));

@@ -40,6 +40,11 @@ def iters_close(a: int, b: int) -> bool:
     return abs(a - b) <= max(1, ITER_FRAC * max(a, b))
 
 
-def csr_handle(rowptr, col):
+def csr_handle(rowptr, col, one_group="auto"):
+    """A pattern handle; one_group="off" keeps small systems on the two-kernel
+    CG loop (for tests of its kernel families)."""
     import krylov_solvers_adjoint_amd as K
-    return K.sla_csr_create_from_csr(t(rowptr), t(col.astype(np.int32)))
+    P = K.sla_csr_create_from_csr(t(rowptr), t(col.astype(np.int32)))
+    if one_group != "auto":
+        P.set_one_group(one_group)
+    return P

@@ -67,5 +67,6 @@ def test_argument_errors_need_no_gpu():
     assert lib.sla_csr_set_graph_block(None, 32) == K.ERR_ARG
     assert lib.sla_csr_reorder(None, K.ORDER_BFS, None) == K.ERR_ARG
     assert lib.sla_csr_ordering(None, None, None) == K.ERR_ARG
+    assert lib.sla_csr_set_one_group(None, K.ONE_GROUP_AUTO) == K.ERR_ARG
     assert lib.sla_status_string(K.ERR_NOT_SPD) == b"SLA_ERR_NOT_SPD"
     assert lib.sla_csr_destroy(None) == K.OK

@@ -17,10 +17,10 @@ def _poisson(N, rp_dtype=np.int32):
     return rp, c, v, oracle.CSR(N * N, rp.astype(np.int64), c, v)
 
 
-def _solve_pair(rp, c, v, Ao, b, g, tol, maxit, graph_block=None):
+def _solve_pair(rp, c, v, Ao, b, g, tol, maxit, graph_block=None, one_group="auto"):
     import torch
     import krylov_solvers_adjoint_amd as K
-    P = csr_handle(rp, c)
+    P = csr_handle(rp, c, one_group=one_group)
     if graph_block is not None:
         P.set_graph_block(graph_block)
     vt = t(v)
@@ -33,14 +33,17 @@ def _solve_pair(rp, c, v, Ao, b, g, tol, maxit, graph_block=None):
             xo, io, gbo, gvo, aio)
 
 
-def test_poisson32_forward_and_adjoint():
+@pytest.mark.parametrize("one_group", ["auto", "off"])
+def test_poisson32_forward_and_adjoint(one_group):
     """The 32 x 32 Poisson workload: b ~ U(-1,1) seed 0, g ~ N(0,1) seed 1,
-    tol 1e-10 forward and adjoint."""
+    tol 1e-10 forward and adjoint (the one-workgroup loop and the two-kernel
+    loop)."""
     rp, c, v, Ao = _poisson(32)
     b = W.uniform_rhs(1024, 0)
     g = W.normal_rhs(1024, 1)
-    x, info, gb, gv, ainfo, xo, io, gbo, gvo, aio = _solve_pair(rp, c, v, Ao, b, g, 1e-10, 10000)
-    say(f"poisson32: iters gpu {info.iterations} oracle {io.iterations}; adjoint gpu "
+    x, info, gb, gv, ainfo, xo, io, gbo, gvo, aio = _solve_pair(rp, c, v, Ao, b, g, 1e-10, 10000,
+                                                                one_group=one_group)
+    say(f"poisson32 {one_group}: iters gpu {info.iterations} oracle {io.iterations}; adjoint gpu "
         f"{ainfo.iterations} oracle {aio.iterations}; x {rel(x, xo):.2e} lam {rel(gb, gbo):.2e} "
         f"gv {rel(gv, gvo):.2e}")
     assert info.converged and ainfo.converged
@@ -58,7 +61,7 @@ def test_graph_blocks_give_identical_bits(graph_block):
     b = W.uniform_rhs(45 * 45, 3)
     ref = None
     for gbk in (32, graph_block):
-        P = csr_handle(rp, c)
+        P = csr_handle(rp, c, one_group="off")  # 2025 unknowns: keep the graph loop
         P.set_graph_block(gbk)
         x, info = K.sla_cg_solve(P, t(v), t(b), 1e-9, 5000)
         torch.cuda.synchronize()
@@ -178,13 +181,14 @@ def test_eigenvector_rhs_one_iteration():
     assert rel(x.cpu().numpy(), vec / eigval(N, 3, 5)) <= 1e-12
 
 
-def test_degenerate_cases():
+@pytest.mark.parametrize("one_group", ["auto", "off"])
+def test_degenerate_cases(one_group):
     import torch
     import krylov_solvers_adjoint_amd as K
     N = 10
     rp, c, v, Ao = _poisson(N)
     n = N * N
-    P = csr_handle(rp, c)
+    P = csr_handle(rp, c, one_group=one_group)
     # b = 0: no iteration, x = 0
     x, info = K.sla_cg_solve(P, t(v), t(np.zeros(n)), 1e-10, 100)
     assert info.iterations == 0 and info.converged and float(x.abs().max()) == 0.0
@@ -211,7 +215,7 @@ def test_degenerate_cases():
     xo, io = oracle.cg(Ao, b, 1e-12, 1000, x0=x0)
     assert iters_close(info.iterations, io.iterations) and rel(x.cpu().numpy(), xo) <= TOL_X
     # n = 1
-    P1 = csr_handle(np.array([0, 1], np.int32), np.array([0], np.int32))
+    P1 = csr_handle(np.array([0, 1], np.int32), np.array([0], np.int32), one_group=one_group)
     x, info = K.sla_cg_solve(P1, t(np.array([2.5])), t(np.array([3.0])), 1e-12, 10)
     gb, gv, _ = K.sla_cg_adjoint(P1, t(np.array([2.5])), x, t(np.array([-1.5])), 1e-12, 10)
     torch.cuda.synchronize()

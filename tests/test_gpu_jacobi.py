@@ -64,16 +64,16 @@ def _check_vs_oracle(name, rp, c, v, b, g, tol, maxit, variant="auto"):
     return x, info
 
 
-@pytest.mark.parametrize("N", [40, 1000])
-def test_uniform_diagonal_is_cg_bit_for_bit(N):
+@pytest.mark.parametrize("N,one_group", [(40, "off"), (40, "auto"), (1000, "auto")])
+def test_uniform_diagonal_is_cg_bit_for_bit(N, one_group):
     """Diagonal 4: z = r/4 rescales everything by powers of two, so the
     preconditioned iterates, beta and r.r are CG's exactly (row-order kernel
-    at 40^2, line walk at 1000^2)."""
+    and the one-workgroup loop at 40^2, line walk at 1000^2)."""
     import torch
     import krylov_solvers_adjoint_amd as K
     rp, c, v = W.poisson_csr(N, np.int32)
     b = W.uniform_rhs(N * N, 40)
-    P = csr_handle(rp, c)
+    P = csr_handle(rp, c, one_group=one_group)
     vt = t(v)
     x1, i1 = K.sla_cg_solve(P, vt, t(b), 1e-10, 3000, history=True)
     h1 = P.history()
