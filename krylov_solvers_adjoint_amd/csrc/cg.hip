@@ -883,25 +883,32 @@ void k_cg_direction(const Ctx* __restrict__ c) {
   const uint32_t lane = lane_id();
   const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
   const bool run = h.stop == ST_RUNNING;
-  // kStreamTiles tiles per round, all loads first
+  // kStreamTiles tiles per round, all loads first and unconditional (rows
+  // past the range read a valid row whose value is not used: a conditional
+  // load would make the compiler keep the old register value, which waits
+  // for every older load)
   for (int64_t t0 = wk.first; t0 < wk.end; t0 += kStreamTiles * wk.stride) {
     double po[kStreamTiles], xv[kStreamTiles], rv[kStreamTiles];
 #pragma unroll
     for (int u = 0; u < kStreamTiles; ++u) {
-      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
-      if (t < wk.end && i0 + lane < n) {
-        po[u] = ld(pold + i0, lane);
-        if (h.lag) xv[u] = ld(x + i0, lane);
-        if (run) rv[u] = ld(r + i0, lane);
-      }
+      const int64_t t = t0 + u * wk.stride;
+      const int64_t i0 = (t < wk.end ? t : t0) * kTileRows;
+      const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
+      po[u] = ld(pold + i0, li);
+      xv[u] = ld(x + i0, li);
+      rv[u] = ld(r + i0, li);
     }
+    // unconditional stores too (see k_cg_residual): a lane past the range
+    // stores what its loaded row's own lane stores; without the lagged
+    // update x is stored back unchanged, and in the last pass p_k is not
+    // formed (the buffer gets p_{k-1}, unused afterwards)
 #pragma unroll
     for (int u = 0; u < kStreamTiles; ++u) {
-      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
-      if (t < wk.end && i0 + lane < n) {
-        if (h.lag) st(x + i0, lane, xv[u] + alpha * po[u]);
-        if (run) st(pnew + i0, lane, rv[u] + beta * po[u]);
-      }
+      const int64_t t = t0 + u * wk.stride;
+      const int64_t i0 = (t < wk.end ? t : t0) * kTileRows;
+      const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
+      st(x + i0, li, h.lag ? xv[u] + alpha * po[u] : xv[u]);
+      st(pnew + i0, li, run ? rv[u] + beta * po[u] : po[u]);
     }
   }
 }
@@ -1205,10 +1212,39 @@ void k_cg_residual(const Ctx* __restrict__ c) {
     if (lead) sc->state_r = st_in;
     return;
   }
-  const int64_t k = sc->kr;
+  // (read through the global address space: a flat load would make the
+  // first wait below cover the tile loads issued after it)
+  const SLA_GLOBAL Scal* scg = gmem(static_cast<const Scal*>(sc));
+  const int64_t k = scg->kr;
+  const uint32_t lane = lane_id();
+  // rounds of U consecutive tiles (a wave's loads of a round fall in a few
+  // DRAM pages), walked like single tiles: each XCD owns a contiguous range
+  // of rounds; all loads first, the r.r (and r.z) terms added in tile order
+  // (two tiles in flight with Jacobi: the divisions need the registers)
+  constexpr int U = JAC ? 2 : kStreamTiles;
+  const TileWalk wk = wave_walk((tiles + U - 1) / U, G, blockIdx.x, kWaves, wave_index());
+  double rv[U], qv[U], dv[U];
+  // unconditional loads (rows past the range read a valid row whose value is
+  // not used: a conditional load would make the compiler keep the old
+  // register value, which waits for every older load)
+  auto load_round = [&](int64_t bk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t t = bk * U + u;
+      t = bk < wk.end && t < tiles ? t : (bk < wk.end ? bk * U : tiles - 1);
+      const int64_t i0 = t * kTileRows;
+      const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
+      rv[u] = ld(r + i0, li);
+      qv[u] = ld(q + i0, li);
+      if constexpr (JAC) dv[u] = ld(dg + i0, li);
+    }
+  };
+  // the first round's loads need no scalar: issued before the p.Ap partials
+  // are summed, so that the two latencies overlap
+  load_round(wk.first);
   const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
-  const double rr = sc->rr[k & 1];
-  const double num = JAC ? sc->rz[k & 1] : rr;
+  const double rr = scg->rr[k & 1];
+  const double num = JAC ? scg->rz[k & 1] : rr;
   int32_t stop = ST_RUNNING;
   if (!isfinite(pq)) stop = ST_NONFINITE;
   else if (!(pq > 0.0)) stop = ST_NOT_SPD;
@@ -1227,36 +1263,28 @@ void k_cg_residual(const Ctx* __restrict__ c) {
     sc->alpha = alpha;
     sc->ka = k + 1;
   }
-  const uint32_t lane = lane_id();
-  const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
-  // kStreamTiles tiles per round, all loads first; the r.r (and r.z) terms
-  // are added in tile order
-  // (two tiles in flight with Jacobi: the divisions need the registers)
-  constexpr int U = JAC ? 2 : kStreamTiles;
   double rn = 0.0, rzn = 0.0;
-  for (int64_t t0 = wk.first; t0 < wk.end; t0 += U * wk.stride) {
-    double rv[U], qv[U], dv[U];
+  for (int64_t bk = wk.first; bk < wk.end; bk += wk.stride) {
+    if (bk != wk.first) load_round(bk);
+    // no branch around the stores either (a branch makes the compiler wait
+    // for every older store before the next one): a lane past the range
+    // stores the value its loaded row's own lane stores, and only owned
+    // rows enter the sums, in tile order
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
-      if (t < wk.end && i0 + lane < n) {
-        rv[u] = ld(r + i0, lane);
-        qv[u] = ld(q + i0, lane);
-        if constexpr (JAC) dv[u] = ld(dg + i0, lane);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = t0 + u * wk.stride, i0 = t * kTileRows;
-      if (t < wk.end && i0 + lane < n) {
-        const double ri = rv[u] - alpha * qv[u];
-        st(r + i0, lane, ri);
-        rn = rn + ri * ri;
-        if constexpr (JAC) {
-          const double zi = ri / dv[u];
-          st(z + i0, lane, zi);
-          rzn = rzn + ri * zi;
-        }
+      const int64_t t = bk * U + u;
+      const int64_t i0 = (t < tiles ? t : bk * U) * kTileRows;
+      const bool own = t < tiles && i0 + lane < n;
+      const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
+      const double ri = rv[u] - alpha * qv[u];
+      st(r + i0, li, ri);
+      const double rn1 = rn + ri * ri;
+      rn = own ? rn1 : rn;
+      if constexpr (JAC) {
+        const double zi = ri / dv[u];
+        st(z + i0, li, zi);
+        const double rzn1 = rzn + ri * zi;
+        rzn = own ? rzn1 : rzn;
       }
     }
   }
