@@ -1217,21 +1217,26 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   const SLA_GLOBAL Scal* scg = gmem(static_cast<const Scal*>(sc));
   const int64_t k = scg->kr;
   const uint32_t lane = lane_id();
-  // rounds of U consecutive tiles (a wave's loads of a round fall in a few
+  // blocks of kStreamTiles consecutive tiles (a wave's loads fall in a few
   // DRAM pages), walked like single tiles: each XCD owns a contiguous range
-  // of rounds; all loads first, the r.r (and r.z) terms added in tile order
-  // (two tiles in flight with Jacobi: the divisions need the registers)
+  // of blocks; a block is loaded in rounds of U tiles, all loads of a round
+  // first (two tiles with Jacobi: the divisions need the registers); the
+  // r.r (and r.z) terms are added in tile order, the same order with and
+  // without Jacobi
+  constexpr int B = kStreamTiles;
   constexpr int U = JAC ? 2 : kStreamTiles;
-  const TileWalk wk = wave_walk((tiles + U - 1) / U, G, blockIdx.x, kWaves, wave_index());
+  static_assert(B % U == 0, "whole rounds per block");
+  const TileWalk wk = wave_walk((tiles + B - 1) / B, G, blockIdx.x, kWaves, wave_index());
   double rv[U], qv[U], dv[U];
-  // unconditional loads (rows past the range read a valid row whose value is
-  // not used: a conditional load would make the compiler keep the old
-  // register value, which waits for every older load)
-  auto load_round = [&](int64_t bk) {
+  // unconditional loads: tiles past the matrix read the round's first tile
+  // and lanes past the last row read that row (their values are not used,
+  // or give the same stores; a conditional load would make the compiler
+  // keep the old register value, which waits for every older load)
+  auto load_round = [&](int64_t t0) {
+    const int64_t tf = t0 < tiles ? t0 : tiles - 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int64_t t = bk * U + u;
-      t = bk < wk.end && t < tiles ? t : (bk < wk.end ? bk * U : tiles - 1);
+      const int64_t t = t0 + u < tiles ? t0 + u : tf;
       const int64_t i0 = t * kTileRows;
       const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
       rv[u] = ld(r + i0, li);
@@ -1241,7 +1246,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   };
   // the first round's loads need no scalar: issued before the p.Ap partials
   // are summed, so that the two latencies overlap
-  load_round(wk.first);
+  load_round(wk.first * B);
   const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
   const double rr = scg->rr[k & 1];
   const double num = JAC ? scg->rz[k & 1] : rr;
@@ -1265,26 +1270,32 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   }
   double rn = 0.0, rzn = 0.0;
   for (int64_t bk = wk.first; bk < wk.end; bk += wk.stride) {
-    if (bk != wk.first) load_round(bk);
-    // no branch around the stores either (a branch makes the compiler wait
-    // for every older store before the next one): a lane past the range
-    // stores the value its loaded row's own lane stores, and only owned
-    // rows enter the sums, in tile order
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = bk * U + u;
-      const int64_t i0 = (t < tiles ? t : bk * U) * kTileRows;
-      const bool own = t < tiles && i0 + lane < n;
-      const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
-      const double ri = rv[u] - alpha * qv[u];
-      st(r + i0, li, ri);
-      const double rn1 = rn + ri * ri;
-      rn = own ? rn1 : rn;
-      if constexpr (JAC) {
-        const double zi = ri / dv[u];
-        st(z + i0, li, zi);
-        const double rzn1 = rzn + ri * zi;
-        rzn = own ? rzn1 : rzn;
+    for (int h = 0; h < B; h += U) {
+      const int64_t t0 = bk * B + h;  // the round's first tile
+      if (h > 0 && t0 >= tiles) break;  // (wave-uniform) the block ends early
+      if (bk != wk.first || h != 0) load_round(t0);
+      // no branch around the stores either (a branch makes the compiler wait
+      // for every older store before the next one): a lane past the range
+      // stores what the loaded row's own lane stores (from the same values,
+      // loaded before this round's stores), and only owned rows enter the
+      // sums, in tile order
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + u;
+        const int64_t i0 = (t < tiles ? t : t0) * kTileRows;
+        const bool own = t < tiles && i0 + lane < n;
+        const uint32_t li = i0 + lane < n ? lane : uint32_t(n - 1 - i0);
+        const double ri = rv[u] - alpha * qv[u];
+        st(r + i0, li, ri);
+        const double rn1 = rn + ri * ri;
+        rn = own ? rn1 : rn;
+        if constexpr (JAC) {
+          const double zi = ri / dv[u];
+          st(z + i0, li, zi);
+          const double rzn1 = rzn + ri * zi;
+          rzn = own ? rzn1 : rzn;
+        }
       }
     }
   }
