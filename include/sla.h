@@ -449,16 +449,19 @@ sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups);
  * slot + 8 per slot and system for B's values + 20 bytes per unknown and
  * system).  Synchronises `stream`.  Needs nnz < 2^32.
  *
- * Afterwards sla_cg_solve, sla_cg_solve_batched, sla_cg_adjoint,
- * sla_cg_adjoint_batched, the CG calls of sla_solve_list / sla_adjoint_list,
- * sla_cg_history and sla_profile_iteration_kernels run on B: every call
- * gathers the bound values into B's slot order and b (or grad_x, and x
- * under SLA_FLAG_X0) into B's unknown order, and scatters x (or grad_b) back;
- * grad_vals is formed on A's own slots.  Inputs and outputs keep A's
- * numbering.  CG's iterates are A's, permuted, in exact arithmetic; in
- * floating point the row sums and dot products are taken in another order,
- * so results differ from the unordered solve by rounding.  Every other call
- * (spmv, eigsh, BiCGStab, ...) still uses A as it is.
+ * Afterwards the CG and BiCGStab solves and adjoints (sla_cg_solve,
+ * sla_cg_solve_batched, sla_cg_adjoint, sla_cg_adjoint_batched,
+ * sla_bicgstab_solve, sla_bicgstab_adjoint, and those of sla_solve_list /
+ * sla_adjoint_list), sla_cg_history, sla_bicgstab_history and
+ * sla_profile_iteration_kernels run on B: every call gathers the bound values
+ * into B's slot order and b (or grad_x, and x under SLA_FLAG_X0) into B's
+ * unknown order, and scatters x (or grad_b) back; grad_vals is formed on A's
+ * own slots.  Inputs and outputs keep A's numbering.  The iterates are A's,
+ * permuted, in exact arithmetic (the BiCGStab adjoint runs on
+ * (P A P^T)^T = P A^T P^T); in floating point the row sums and dot products
+ * are taken in another order, so results differ from the unordered solve by
+ * rounding.  Every other call (spmv, the transposed product, eigsh, ...)
+ * still uses A as it is.
  * SLA_ORDER_NONE drops the ordering and its memory.
  */
 enum { SLA_ORDER_NONE = 0, SLA_ORDER_BFS = 1 };

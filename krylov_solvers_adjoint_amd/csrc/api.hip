@@ -506,7 +506,7 @@ sla_status sla_solve_list(int64_t count, const sla_csr* A, const double* const* 
     SLA_TRY(check_solve(A[i], b[i], x[i], tol, maxit, flags, "sla_solve_list"));
   return run_list(count, info, stream, [&](int64_t i, hipStream_t st, sla_cg_info* in) {
     return method == SLA_METHOD_CG ? run_cg_any(A[i], b[i], x[i], tol, maxit, flags, in, st)
-                                   : run_bicgstab(A[i], b[i], x[i], tol, maxit, flags, in, st);
+                                   : run_bicgstab_any(A[i], b[i], x[i], tol, maxit, flags, in, st);
   });
   API_END
 }
@@ -530,7 +530,7 @@ sla_status sla_adjoint_list(int64_t count, const sla_csr* A, const double* const
     const double* xi = x ? x[i] : nullptr;
     return method == SLA_METHOD_CG
                ? run_cg_adjoint(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in, st)
-               : run_bicgstab_adjoint(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in,
+               : run_bicgstab_adjoint_any(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in,
                                       st);
   });
   API_END
@@ -542,7 +542,7 @@ sla_status sla_bicgstab_solve(sla_csr A, const double* b, double* x, double tol,
   clear_error();
   SLA_TRY(check_solve(A, b, x, tol, maxit, flags & ~uint32_t(SLA_FLAG_JACOBI), "sla_bicgstab_solve"));
   REQUIRE((flags & SLA_FLAG_JACOBI) == 0, "sla_bicgstab_solve: no preconditioner is supported");
-  return run_bicgstab(A, b, x, tol, maxit, flags, info, stream);
+  return run_bicgstab_any(A, b, x, tol, maxit, flags, info, stream);
   API_END
 }
 
@@ -555,7 +555,8 @@ sla_status sla_bicgstab_adjoint(sla_csr A, const double* x, const double* grad_x
   REQUIRE((flags & ~uint32_t(SLA_FLAG_HISTORY)) == 0,
           "sla_bicgstab_adjoint: only SLA_FLAG_HISTORY is supported");
   REQUIRE(grad_vals == nullptr || x != nullptr, "sla_bicgstab_adjoint: grad_vals needs x");
-  return run_bicgstab_adjoint(A, x, grad_x, grad_b, grad_vals, tol, maxit, flags, info, stream);
+  return run_bicgstab_adjoint_any(A, x, grad_x, grad_b, grad_vals, tol, maxit, flags, info,
+                                  stream);
   API_END
 }
 
@@ -565,7 +566,7 @@ sla_status sla_bicgstab_history(sla_csr A, int64_t system, double* rho, double* 
   clear_error();
   REQUIRE(A != nullptr, "sla_bicgstab_history: NULL handle");
   REQUIRE(cap >= 0, "sla_bicgstab_history: cap < 0");
-  return bicgstab_history(A, system, rho, alpha, omega, rr, cap, count);
+  return bicgstab_history(solver_handle(A), system, rho, alpha, omega, rr, cap, count);
   API_END
 }
 

@@ -155,6 +155,13 @@ void release_reorder(sla_csr A);
 // CG on A, or on P A P^T with b, x permuted in and out when A is reordered
 sla_status run_cg_any(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
                       uint32_t flags, sla_cg_info* info, hipStream_t stream);
+// BiCGStab on A, or on P A P^T (the adjoint on its transpose, P A^T P^T)
+sla_status run_bicgstab_any(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                            uint32_t flags, sla_cg_info* info, hipStream_t stream);
+sla_status run_bicgstab_adjoint_any(sla_csr A, const double* x, const double* grad_x,
+                                    double* grad_b, double* grad_vals, double tol,
+                                    int64_t maxit, uint32_t flags, sla_cg_info* info,
+                                    hipStream_t stream);
 sla_status profile_kernels_any(sla_csr A, const double* b, double* x, int64_t reps,
                                double* avg_ms, hipStream_t stream);
 sla_status copy_order(sla_csr A, int32_t* out, hipStream_t stream);

@@ -634,6 +634,41 @@ sla_status run_cg_any(sla_csr A, const double* b, double* x, double tol, int64_t
   return s;
 }
 
+sla_status run_bicgstab_any(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
+                            uint32_t flags, sla_cg_info* info, hipStream_t st) {
+  if (A->ro == nullptr) return run_bicgstab(A, b, x, tol, maxit, flags, info, st);
+  Reorder* R = A->ro;
+  SLA_TRY(prepare(A, st));
+  SLA_TRY(permute_in(A, b, R->vin, st));
+  if (flags & SLA_FLAG_X0) SLA_TRY(permute_in(A, x, R->vout, st));
+  const sla_status s = run_bicgstab(R->B, R->vin, R->vout, tol, maxit, flags, info, st);
+  if (s != SLA_OK && s != SLA_ERR_BREAKDOWN && s != SLA_ERR_NONFINITE) return s;
+  SLA_TRY(permute_out(A, R->vout, x, st));
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  return s;
+}
+
+// (P A P^T)^T = P A^T P^T: the adjoint of the permuted system with P g is
+// P lambda; the slot gradient is formed on A's own slots.
+sla_status run_bicgstab_adjoint_any(sla_csr A, const double* x, const double* grad_x,
+                                    double* grad_b, double* grad_vals, double tol,
+                                    int64_t maxit, uint32_t flags, sla_cg_info* info,
+                                    hipStream_t st) {
+  if (A->ro == nullptr)
+    return run_bicgstab_adjoint(A, x, grad_x, grad_b, grad_vals, tol, maxit, flags, info, st);
+  Reorder* R = A->ro;
+  SLA_TRY(prepare(A, st));
+  SLA_TRY(permute_in(A, grad_x, R->vin, st));
+  const sla_status s = run_bicgstab_adjoint(R->B, nullptr, R->vin, R->vout, nullptr, tol, maxit,
+                                            flags, info, st);
+  if (s != SLA_OK && s != SLA_ERR_BREAKDOWN && s != SLA_ERR_NONFINITE) return s;
+  SLA_TRY(permute_out(A, R->vout, grad_b, st));
+  if (grad_vals != nullptr && A->nnz > 0)
+    SLA_TRY(launch_slot_products(A, A->batch, grad_b, x, grad_vals, true, st));
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  return s;
+}
+
 sla_status profile_kernels_any(sla_csr A, const double* b, double* x, int64_t reps,
                                double* avg_ms, hipStream_t st) {
   if (A->ro == nullptr) return profile_kernels(A, b, x, reps, avg_ms, st);

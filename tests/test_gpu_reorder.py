@@ -216,3 +216,42 @@ def test_reordered_list_and_settings():
     assert ir.status == K.ERR_NOT_SPD and iq.status == K.ERR_NOT_SPD
     assert ir.iterations == iq.iterations
     assert rel(xr.cpu().numpy(), xq.cpu().numpy()) <= 1e-12
+
+
+def test_reordered_bicgstab():
+    """BiCGStab on a non-symmetric system in random order (convection-
+    diffusion 40^2 with its unknowns shuffled), reordered: forward and
+    adjoint against the oracle on the shuffled matrix, the history's length,
+    and a BiCGStab list holding the reordered handle equal to its single
+    solve bit for bit."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    rp, c, v = W.convection_diffusion_csr(40)
+    n = len(rp) - 1
+    shuffle = np.random.default_rng(5).permutation(n)
+    A, _ = oracle.permute(_oracle_A(rp, c, v), shuffle)
+    b = W.normal_rhs(n, 6)
+    g = W.normal_rhs(n, 7)
+    P = csr_handle(A.rowptr, A.col)
+    P.reorder()
+    vt = t(A.vals)
+    x, (info,) = K.sla_bicgstab_solve(P, vt, t(b), 1e-12, 5000, history=True)
+    hist_len = len(K.sla_bicgstab_history(P)[0])
+    gb, gv, (ai,) = K.sla_bicgstab_adjoint(P, vt, x, t(g), 1e-12, 5000)
+    torch.cuda.synchronize()
+    xo, io = oracle.bicgstab(A, b, 1e-12, 5000)
+    gbo, gvo, aio = oracle.adjoint_bicgstab(A, xo, g, 1e-12, 5000)
+    x, gb, gv = x.cpu().numpy(), gb.cpu().numpy(), gv.cpu().numpy()
+    say(f"reordered bicgstab: it {info.iterations}/{io.iterations} adj {ai.iterations}/"
+        f"{aio.iterations} x {rel(x, xo):.1e} lam {rel(gb, gbo):.1e} gv {rel(gv, gvo):.1e}")
+    assert info.converged and ai.converged
+    assert hist_len == info.iterations
+    # BiCGStab's count moves with rounding (the residual oscillates)
+    assert abs(info.iterations - io.iterations) <= 0.25 * io.iterations
+    assert abs(ai.iterations - aio.iterations) <= 0.25 * aio.iterations
+    assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+    xs, infos = K.sla_solve_list([P], [vt], [t(b)], 1e-12, 5000, method="bicgstab")
+    x1, (i1,) = K.sla_bicgstab_solve(P, vt, t(b), 1e-12, 5000)
+    torch.cuda.synchronize()
+    assert np.array_equal(xs[0].cpu().numpy(), x1.cpu().numpy())
+    assert infos[0].iterations == i1.iterations
