@@ -420,12 +420,23 @@ def bench_rgg(n: int, kernel_reps: int):
     rs = time.perf_counter() - t0
     rkern = K.sla_profile_iteration_kernels(P, v, b, reps=kernel_reps)
     rits = ri.iterations + rai.iterations
+    # Jacobi preconditioning on the reordered copy
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    xrj, rj = K.sla_cg_solve(P, v, b, 1e-8, 20000, jacobi=True)
+    gbrj, gvrj, raj = K.sla_cg_adjoint(P, v, xrj, g, 1e-8, 20000, jacobi=True)
+    torch.cuda.synchronize()
+    rjs = time.perf_counter() - t0
+    del xrj, gbrj, gvrj
     out["reordered"] = dict(
         order_ms=order_ms, spmv=spmv_variant(P), iterations_fwd=ri.iterations,
         iterations_adj=rai.iterations, solve_adjoint_ms=1e3 * rs, it_per_s=rits / rs,
         eff_GBps=(rits * canonical_bytes(n, nnz, 4) + pattern_grad_bytes(n, nnz, 4)) / rs / 1e9,
         kernel_ms=rkern,
-        spmv_GBps=spmv_bytes_for(spmv_variant(P), n, nnz, 4) / (rkern["spmv_step"] * 1e-3) / 1e9)
+        spmv_GBps=spmv_bytes_for(spmv_variant(P), n, nnz, 4) / (rkern["spmv_step"] * 1e-3) / 1e9,
+        jacobi=dict(iterations_fwd=rj.iterations, iterations_adj=raj.iterations,
+                    solve_adjoint_ms=1e3 * rjs,
+                    it_per_s=(rj.iterations + raj.iterations) / rjs))
     out["reordered"]["pct_peak"] = 100.0 * out["reordered"]["eff_GBps"] / HBM_PEAK_GBPS
     del P, v, b, g, x, gb, gv, xr, gbr, gvr
     torch.cuda.synchronize()

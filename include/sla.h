@@ -432,11 +432,11 @@ sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
 sla_status sla_csr_set_workgroups_per_cu(sla_csr A, int workgroups);
 
 /*
- * Locality ordering of the unknowns for CG.  The pages fix no storage order;
- * this is the library's own remedy for patterns whose unknowns come in an
- * order unrelated to the graph (the random geometric graph of the
- * explainer's benchmark set, Performance / benchmarks: nodes in sampling
- * order), where every gathered vector entry of the SpMV misses the caches.
+ * Locality ordering of the unknowns for the iterative solvers.  The pages fix
+ * no storage order; this is the library's own remedy for patterns whose
+ * unknowns come in an order unrelated to the graph (a random geometric graph
+ * whose nodes are numbered in the order the points were drawn, say), where
+ * every gathered vector entry of the SpMV misses the caches.
  *
  * SLA_ORDER_BFS renumbers the unknowns in the breadth-first order of the
  * pattern's graph (an edge i -> j for every stored slot (i, j), j != i):

@@ -1,9 +1,8 @@
 // Locality ordering of the unknowns for the iterative solvers.
 //
-// A pattern whose unknowns come in an order unrelated to its graph (the
-// random geometric graph of the torch-sla explainer's benchmark set, whose
-// nodes are numbered in sampling order) makes every gathered p[col] of the
-// SpMV a miss in every cache.  Renumbering the unknowns in the breadth-first
+// A pattern whose unknowns come in an order unrelated to its graph (a random
+// geometric graph whose nodes are numbered in the order the points were
+// drawn, say) makes every gathered p[col] of the SpMV a miss in every cache.  Renumbering the unknowns in the breadth-first
 // order of the pattern's graph (Cuthill-McKee's level structure) puts the
 // neighbours of consecutive rows within a narrow window of indices, so the
 // gathers hit L2.  The solvers then run on B = P A P^T with b and x permuted

@@ -68,6 +68,15 @@ def test_ragged_sizes_against_oracle(n):
         assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
 
 
+def test_mode_argument():
+    import krylov_solvers_adjoint_amd as K
+    rp, c, v = W.poisson_csr(8)
+    P = csr_handle(rp, c)
+    assert K._lib.sla_csr_set_one_group(P.handle, 7) == K.ERR_ARG
+    assert K._lib.sla_csr_set_one_group(P.handle, K.ONE_GROUP_OFF) == K.OK
+    assert K._lib.sla_csr_set_one_group(P.handle, K.ONE_GROUP_AUTO) == K.OK
+
+
 def test_outside_the_range_takes_the_two_kernel_loop():
     """2049 unknowns, or tiles of more than 336 slots (7 per row): the
     automatic mode gives the two-kernel loop's bits."""
