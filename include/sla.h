@@ -423,8 +423,9 @@ sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels_host);
 sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
 
 /* Solver workgroups (1024 threads each) per compute unit: 0 (default:
- * automatic, 1 for solves of at most 2^21 unknowns over the batch, where the
- * kernels' fixed costs dominate, else 2), 1 (16 waves per CU, fewer DRAM
+ * automatic: 1 for solves of at most 2^21 unknowns over the batch, where the
+ * kernels' fixed costs dominate, and for line-walk patterns (2D stencils),
+ * whose waves then walk longer chunks; else 2), 1 (16 waves per CU, fewer DRAM
  * pages open at once) or 2 (32 waves per CU).  The grid sets the number and
  * order of the dot-product partial sums, so CG results differ in the last
  * bits between grids; each setting is reproducible.  SpMV results do not

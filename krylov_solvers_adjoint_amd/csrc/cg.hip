@@ -647,7 +647,7 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
 // chunk.  Workgroups of kLineWaves waves, two per CU: 16 waves per CU with
 // 128 registers each, enough to keep the next tile, its edge rows and the
 // current tile's values in flight together.
-template <typename RP, int NB, bool NEAR1>
+template <typename RP, int NB, bool NEAR1, bool PIPE>
 __global__ __launch_bounds__(kLineWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(kLineWavesPerEu)))
 void k_cg_spmv_lines(const Ctx* __restrict__ c) {
@@ -716,134 +716,308 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
     auto clamp_lane = [&](int64_t len) -> uint32_t {
       return int64_t(lane) < len ? lane : uint32_t(len - 1);
     };
-    // -L neighbours of the first tile
-    double pprev = 0.0;
-    if (v0 >= 1) {
-      const int64_t pr0 = (v0 - 1) * L + col0;
-      const uint32_t pl = clamp_lane(lenu);
-      pprev = ld(r + pr0, pl) + beta * ld(pold + pr0, pl);
-    }
-    int64_t len = tile_len(v0);
-    uint32_t lr = clamp_lane(len);
-    double rc = ld(r + v0 * L + col0, lr), pc = ld(pold + v0 * L + col0, lr);
-    TileIndex<RP> ix = tile_index<NB, RP>(rowptr, mask, n, v0 * L + col0, lr);
-    // rows just outside the tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
-    // clamped into [0, n)
-    auto edges = [&](int64_t e0, int64_t elen, double& rl, double& pl, double& rr, double& pr) {
-      const int64_t a = e0 > 0 ? e0 - 1 : 0;
-      const int64_t b = e0 + elen < n ? e0 + elen : n - 1;
-      rl = ld(r + a, 0u);
-      pl = ld(pold + a, 0u);
-      rr = ld(r + b, 0u);
-      pr = ld(pold + b, 0u);
-    };
-    // the current tile's edge rows live in scalar registers (the same value
-    // in every lane); the next tile's arrive in vector registers
-    double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
-    if constexpr (NEAR1) {
-      edges(v0 * L + col0, len, rl, pl, rr, pr);
-      rl = uniform(rl);
-      pl = uniform(pl);
-      rr = uniform(rr);
-      pr = uniform(pr);
-    }
-    wait_vmem();
-    for (int64_t v = v0; v < v1; ++v) {
-      const int64_t r0 = v * L + col0;
-      const bool own = int64_t(lane) < len;
-      // the next tile: +L neighbours now, own operands in the next step
-      const int64_t lenn = v + 1 < V ? tile_len(v + 1) : 0;
-      const bool hasn = lenn > 0;
-      const int64_t rn0 = hasn ? r0 + L : r0;
-      const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
-      const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
-      double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
-      if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
-      const TileIndex<RP> cur = ix;
-      // unconditional (the current tile again when there is no next one): a
-      // conditional load would make the compiler copy the old value into its
-      // register first, which waits for older loads and stores
-      ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
-      const double xo = ld(x + r0, lr);
-      // near offsets, gathered; the other kinds read the row itself (no
-      // branch; the value is not used)
-      const int64_t lo = r0 - kTileRows;
-      const int64_t base = lo > 0 ? lo : 0;
-      const int32_t d = int32_t(r0 - base) + int32_t(lr);
-      const int32_t top = int32_t(n - 1 - base);
-      // offsets are sorted: -L first, +L last, the near ones in between
-      double gu[NB], gw[NB];
-      if constexpr (!NEAR1) {
-#pragma unroll
-        for (int t = 1; t < NB - 1; ++t) {
-          const int32_t o = t < band.count - 1 ? band.off[t] : 0;
-          int32_t j = d + o;
-          j = j < 0 ? 0 : (j > top ? top : j);
-          g.load_at(base, uint32_t(j), gu[t], gw[t]);
+    if constexpr (PIPE) {
+      // -L neighbours of the first tile
+      double pprev = 0.0;
+      if (v0 >= 1) {
+        const int64_t pr0 = (v0 - 1) * L + col0;
+        const uint32_t pl = clamp_lane(lenu);
+        pprev = ld(r + pr0, pl) + beta * ld(pold + pr0, pl);
+      }
+      // A tile of the walk: first row, the lane's (clamped) row, its length;
+      // a line past the matrix stands for the tile before it (its loads repeat
+      // that tile's, unconditionally, and nothing of them is used).
+      struct TileRef {
+        int64_t r0;
+        int64_t len;
+        uint32_t lr;
+        bool has;
+      };
+      auto tile_ref = [&](int64_t v, const TileRef& before) -> TileRef {
+        const int64_t lv = v < V ? tile_len(v) : 0;
+        if (lv > 0) return TileRef{v * L + col0, lv, clamp_lane(lv), true};
+        return TileRef{before.r0, before.len, before.lr, false};
+      };
+      // nothing past the chunk is loaded but the +L neighbours of its last
+      // tile: later tiles' loads repeat the tile before (cache hits)
+      auto pick = [&](bool c, const TileRef& a_, const TileRef& b_) -> TileRef {
+        return TileRef{c ? a_.r0 : b_.r0, c ? a_.len : b_.len, c ? a_.lr : b_.lr, c ? a_.has : b_.has};
+      };
+      // rows just outside the tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
+      // clamped into [0, n); the same value in every lane
+      auto edges = [&](const TileRef& tr, double& rl, double& pl, double& rr, double& pr) {
+        const int64_t a = tr.r0 > 0 ? tr.r0 - 1 : 0;
+        const int64_t b = tr.r0 + tr.len < n ? tr.r0 + tr.len : n - 1;
+        rl = ld(r + a, 0u);
+        pl = ld(pold + a, 0u);
+        rr = ld(r + b, 0u);
+        pr = ld(pold + b, 0u);
+      };
+      // the tile's values at the slot positions of the lane's row (see
+      // band_row): issued from index data loaded a step earlier
+      auto load_values = [&](const TileIndex<RP>& ixv, const TileRef& tr, double (&a)[NB],
+                             unsigned& m) {
+        const int64_t s0 = uniform(int64_t(ixv.s0));
+        m = ixv.m;
+        const bool ownv = int64_t(lane) < tr.len;
+        const int kx = wave_exclusive_sum(ownv ? __builtin_popcount(m) : 0);
+        uint32_t kk = uint32_t(__shfl(kx, int(tr.lr), kWave));
+        const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+  #pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const bool use = t < band.count && ((m >> t) & 1u);
+          a[t] = ld(vb_, use ? kk : 0u);
+          kk += use ? 1u : 0u;
         }
-      }
-      // values at the slot positions of the row (see band_row)
-      const int64_t s0 = uniform(int64_t(cur.s0));
-      const unsigned m = cur.m;
-      const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
-      uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
-      const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+      };
+      // The walk is a pipeline two tiles deep: step v computes tile v from
+      // data issued in the steps before, and issues r, p_{k-1} and the index
+      // data of tile v + 2, and the values, x and edge rows of tile v + 1.
+      TileRef tc{v0 * L + col0, tile_len(v0), 0u, true};
+      tc.lr = clamp_lane(tc.len);
+      TileRef t1 = tile_ref(v0 + 1, tc);
+      double rc = ld(r + tc.r0, tc.lr), pc = ld(pold + tc.r0, tc.lr);
+      double rn = ld(r + t1.r0, t1.lr), pn = ld(pold + t1.r0, t1.lr);
+      TileIndex<RP> ixc = tile_index<NB, RP>(rowptr, mask, n, tc.r0, tc.lr);
+      TileIndex<RP> ix1 = tile_index<NB, RP>(rowptr, mask, n, t1.r0, t1.lr);
+      double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
+      if constexpr (NEAR1) edges(tc, rl, pl, rr, pr);
+      wait_vmem();
       double a[NB];
-#pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const bool use = t < band.count && ((m >> t) & 1u);
-        a[t] = ld(vb_, use ? kk : 0u);
-        kk += use ? 1u : 0u;
+      unsigned m = 0;
+      load_values(ixc, tc, a, m);
+      double xo = ld(x + tc.r0, tc.lr);
+      for (int64_t v = v0; v < v1; ++v) {
+        const int64_t r0 = tc.r0;
+        const uint32_t lr = tc.lr;
+        const int64_t len = tc.len;
+        const bool own = int64_t(lane) < len;
+        // tile v + 2: r, p_{k-1} and index data (the +L neighbours of tile
+        // v + 1, read in the next step; needed up to tile v1)
+        const TileRef t2 = pick(v + 2 <= v1, tile_ref(v + 2, t1), t1);
+        const double rn2 = ld(r + t2.r0, t2.lr), pn2 = ld(pold + t2.r0, t2.lr);
+        const TileIndex<RP> ix2 = tile_index<NB, RP>(rowptr, mask, n, t2.r0, t2.lr);
+        // tile v + 1: x and edge rows, then its values (inside the chunk only)
+        const bool in1 = v + 1 < v1;
+        const TileRef tv = pick(in1, t1, tc);
+        const double xn = ld(x + tv.r0, tv.lr);
+        double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+        if constexpr (NEAR1) edges(tv, rln, pln, rrn, prn);
+        double an[NB];
+        unsigned mn = 0;
+        TileIndex<RP> ixv = ixc;
+        ixv.s0 = in1 ? ix1.s0 : ixc.s0;
+        ixv.m = in1 ? ix1.m : ixc.m;
+        load_values(ixv, tv, an, mn);
+        // near offsets of tile v, gathered; the other kinds read the row
+        // itself (no branch; the value is not used)
+        const int64_t lo = r0 - kTileRows;
+        const int64_t base = lo > 0 ? lo : 0;
+        const int32_t d = int32_t(r0 - base) + int32_t(lr);
+        const int32_t top = int32_t(n - 1 - base);
+        // offsets are sorted: -L first, +L last, the near ones in between
+        double gu[NB], gw[NB];
+        if constexpr (!NEAR1) {
+  #pragma unroll
+          for (int t = 1; t < NB - 1; ++t) {
+            const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+            int32_t j = d + o;
+            j = j < 0 ? 0 : (j > top ? top : j);
+            g.load_at(base, uint32_t(j), gu[t], gw[t]);
+          }
+        }
+        // p_k at the row, below (-L) and above (+L)
+        const double pcur = rc + beta * pc;
+        const double pnext = rn + beta * pn;
+        // lanes past the end of a short tile compute its last row: take that
+        // row's -L value (the previous tile was loaded lane for lane)
+        const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+        // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+        // or, at the ends of the tile, from the rows just outside it
+        double pm1 = 0.0, pp1 = 0.0;
+        if constexpr (NEAR1) {
+          const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+          const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+          pm1 = lr == 0 ? rl + beta * pl : sm;
+          pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+        }
+        double acc = 0.0;
+  #pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const int32_t o = t < band.count ? band.off[t] : 0;
+          const bool use = t < band.count && ((m >> t) & 1u);
+          double gv;
+          if (t == 0) gv = pbelow;
+          else if (t == NB - 1) gv = pnext;
+          else if (t == band.count - 1) gv = pnext;
+          else if (o == 0) gv = pcur;
+          else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+          else gv = g.value(gu[t], gw[t]);
+          const double sum = acc + a[t] * gv;
+          acc = use ? sum : acc;
+        }
+        // lanes past the last row store the same bits as the row's own lane;
+        // x is stored back unchanged when there is no lagged update (no branch
+        // around a store: it would make the compiler wait for older stores)
+        st(x + r0, lr, lag ? xo + alpha * pc : xo);
+        st(pnew + r0, lr, pcur);
+        st(q + r0, lr, acc);
+        const double pq1 = pq + pcur * acc;
+        pq = own ? pq1 : pq;
+        // shift the walk down one line
+        if (!t1.has) break;
+        pprev = pcur;
+        rc = rn;
+        pc = pn;
+        rn = rn2;
+        pn = pn2;
+  #pragma unroll
+        for (int t = 0; t < NB; ++t) a[t] = an[t];
+        m = mn;
+        xo = xn;
+        if constexpr (NEAR1) {
+          rl = rln;
+          pl = pln;
+          rr = rrn;
+          pr = prn;
+        }
+        ixc = ix1;
+        ix1 = ix2;
+        tc = t1;
+        t1 = t2;
       }
-      // p_k at the row, below (-L) and above (+L)
-      const double pcur = rc + beta * pc;
-      const double pnext = rn + beta * pn;
-      // lanes past the end of a short tile compute its last row: take that
-      // row's -L value (the previous tile was loaded lane for lane)
-      const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
-      // NEAR1: p_k at the rows before and after, from the neighbouring lanes
-      // or, at the ends of the tile, from the rows just outside it
-      double pm1 = 0.0, pp1 = 0.0;
+    } else {
+      // the walk with one tile of look-ahead (r, p_{k-1} and index data of
+      // the next tile); shorter chunks run faster this way
+      // -L neighbours of the first tile
+      double pprev = 0.0;
+      if (v0 >= 1) {
+        const int64_t pr0 = (v0 - 1) * L + col0;
+        const uint32_t pl = clamp_lane(lenu);
+        pprev = ld(r + pr0, pl) + beta * ld(pold + pr0, pl);
+      }
+      int64_t len = tile_len(v0);
+      uint32_t lr = clamp_lane(len);
+      double rc = ld(r + v0 * L + col0, lr), pc = ld(pold + v0 * L + col0, lr);
+      TileIndex<RP> ix = tile_index<NB, RP>(rowptr, mask, n, v0 * L + col0, lr);
+      // rows just outside the tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
+      // clamped into [0, n)
+      auto edges = [&](int64_t e0, int64_t elen, double& rl, double& pl, double& rr, double& pr) {
+        const int64_t a = e0 > 0 ? e0 - 1 : 0;
+        const int64_t b = e0 + elen < n ? e0 + elen : n - 1;
+        rl = ld(r + a, 0u);
+        pl = ld(pold + a, 0u);
+        rr = ld(r + b, 0u);
+        pr = ld(pold + b, 0u);
+      };
+      // the current tile's edge rows live in scalar registers (the same value
+      // in every lane); the next tile's arrive in vector registers
+      double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
       if constexpr (NEAR1) {
-        const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
-        const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
-        pm1 = lr == 0 ? rl + beta * pl : sm;
-        pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+        edges(v0 * L + col0, len, rl, pl, rr, pr);
+        rl = uniform(rl);
+        pl = uniform(pl);
+        rr = uniform(rr);
+        pr = uniform(pr);
       }
-      double acc = 0.0;
-#pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const int32_t o = t < band.count ? band.off[t] : 0;
-        const bool use = t < band.count && ((m >> t) & 1u);
-        double gv;
-        if (t == 0) gv = pbelow;
-        else if (t == NB - 1) gv = pnext;
-        else if (t == band.count - 1) gv = pnext;
-        else if (o == 0) gv = pcur;
-        else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
-        else gv = g.value(gu[t], gw[t]);
-        const double sum = acc + a[t] * gv;
-        acc = use ? sum : acc;
+      wait_vmem();
+      for (int64_t v = v0; v < v1; ++v) {
+        const int64_t r0 = v * L + col0;
+        const bool own = int64_t(lane) < len;
+        // the next tile: +L neighbours now, own operands in the next step
+        const int64_t lenn = v + 1 < V ? tile_len(v + 1) : 0;
+        const bool hasn = lenn > 0;
+        const int64_t rn0 = hasn ? r0 + L : r0;
+        const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
+        const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
+        double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+        if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
+        const TileIndex<RP> cur = ix;
+        // unconditional (the current tile again when there is no next one): a
+        // conditional load would make the compiler copy the old value into its
+        // register first, which waits for older loads and stores
+        ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
+        const double xo = ld(x + r0, lr);
+        // near offsets, gathered; the other kinds read the row itself (no
+        // branch; the value is not used)
+        const int64_t lo = r0 - kTileRows;
+        const int64_t base = lo > 0 ? lo : 0;
+        const int32_t d = int32_t(r0 - base) + int32_t(lr);
+        const int32_t top = int32_t(n - 1 - base);
+        // offsets are sorted: -L first, +L last, the near ones in between
+        double gu[NB], gw[NB];
+        if constexpr (!NEAR1) {
+  #pragma unroll
+          for (int t = 1; t < NB - 1; ++t) {
+            const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+            int32_t j = d + o;
+            j = j < 0 ? 0 : (j > top ? top : j);
+            g.load_at(base, uint32_t(j), gu[t], gw[t]);
+          }
+        }
+        // values at the slot positions of the row (see band_row)
+        const int64_t s0 = uniform(int64_t(cur.s0));
+        const unsigned m = cur.m;
+        const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
+        uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
+        const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+        double a[NB];
+  #pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const bool use = t < band.count && ((m >> t) & 1u);
+          a[t] = ld(vb_, use ? kk : 0u);
+          kk += use ? 1u : 0u;
+        }
+        // p_k at the row, below (-L) and above (+L)
+        const double pcur = rc + beta * pc;
+        const double pnext = rn + beta * pn;
+        // lanes past the end of a short tile compute its last row: take that
+        // row's -L value (the previous tile was loaded lane for lane)
+        const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+        // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+        // or, at the ends of the tile, from the rows just outside it
+        double pm1 = 0.0, pp1 = 0.0;
+        if constexpr (NEAR1) {
+          const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+          const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+          pm1 = lr == 0 ? rl + beta * pl : sm;
+          pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+        }
+        double acc = 0.0;
+  #pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const int32_t o = t < band.count ? band.off[t] : 0;
+          const bool use = t < band.count && ((m >> t) & 1u);
+          double gv;
+          if (t == 0) gv = pbelow;
+          else if (t == NB - 1) gv = pnext;
+          else if (t == band.count - 1) gv = pnext;
+          else if (o == 0) gv = pcur;
+          else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+          else gv = g.value(gu[t], gw[t]);
+          const double sum = acc + a[t] * gv;
+          acc = use ? sum : acc;
+        }
+        // lanes past the last row store the same bits as the row's own lane
+        if (lag) st(x + r0, lr, xo + alpha * pc);
+        st(pnew + r0, lr, pcur);
+        st(q + r0, lr, acc);
+        const double pq1 = pq + pcur * acc;
+        pq = own ? pq1 : pq;
+        // shift the walk down one line
+        pprev = pcur;
+        rc = rn;
+        pc = pn;
+        if constexpr (NEAR1) {
+          rl = uniform(rln);
+          pl = uniform(pln);
+          rr = uniform(rrn);
+          pr = uniform(prn);
+        }
+        len = lenn;
+        lr = lrn;
+        if (!hasn) break;
       }
-      // lanes past the last row store the same bits as the row's own lane
-      if (lag) st(x + r0, lr, xo + alpha * pc);
-      st(pnew + r0, lr, pcur);
-      st(q + r0, lr, acc);
-      const double pq1 = pq + pcur * acc;
-      pq = own ? pq1 : pq;
-      // shift the walk down one line
-      pprev = pcur;
-      rc = rn;
-      pc = pn;
-      if constexpr (NEAR1) {
-        rl = uniform(rln);
-        pl = uniform(pln);
-        rr = uniform(rrn);
-        pr = uniform(prn);
-      }
-      len = lenn;
-      lr = lrn;
-      if (!hasn) break;
     }
   }
   pq = block_sum_all<NT>(pq, red);
@@ -1362,6 +1536,28 @@ bool wide_vectors(const sla_csr A) { return uint64_t(A->n) * sizeof(double) >= (
 
 // Kernel family of the row sums: the smallest of 3, 5, 8 offsets that holds
 // a band, else 0 (plain CSR) or -1 (plain CSR, vectors of 4 GiB or more).
+// Line-walk chunks per XCD, so that every workgroup of an XCD gets the same
+// number of (kLineWaves-column group, chunk) units: per_xcd / gcd(groups,
+// per_xcd).
+int64_t line_chunks(const sla_csr A) {
+  const int64_t per_xcd = A->grid / kXcds;
+  const int64_t U = (A->line + kTileRows - 1) / kTileRows;
+  const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
+  int64_t a = per_xcd, b = groups;
+  while (b != 0) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return per_xcd / a;
+}
+
+// Lines a wave walks in one chunk (about).
+int64_t line_chunk_lines(const sla_csr A) {
+  const int64_t V = (A->n + A->line - 1) / A->line;
+  return V / kXcds / std::max<int64_t>(1, line_chunks(A));
+}
+
 int band_class(const sla_csr A) {
   if (!use_band(A)) return wide_vectors(A) ? -1 : 0;
   return A->band.count <= 3 ? 3 : (A->band.count <= 5 ? 5 : 8);
@@ -1375,13 +1571,25 @@ const void* spmv_step_kernel(const sla_csr A) {
     bool near1 = true;
     for (int t = 1; t + 1 < A->band.count; ++t)
       near1 = near1 && A->band.off[t] >= -1 && A->band.off[t] <= 1;
+    // the two-deep pipeline pays off once a wave walks a dozen lines or more,
+    // on matrices whose vectors stay partly in the Infinity Cache
+    if (line_chunk_lines(A) >= kPipeLines && A->n <= kPipeMaxRows) {
+      if (near1 && nb <= 5)
+        return nb == 3 ? reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, true, true>)
+                       : reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, true, true>);
+      switch (nb) {
+        case 3: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, false, true>);
+        case 5: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, false, true>);
+        default: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 8, false, true>);
+      }
+    }
     if (near1 && nb <= 5)
-      return nb == 3 ? reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, true>)
-                     : reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, true>);
+      return nb == 3 ? reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, true, false>)
+                     : reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, true, false>);
     switch (nb) {
-      case 3: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, false>);
-      case 5: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, false>);
-      default: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 8, false>);
+      case 3: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, false, false>);
+      case 5: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, false, false>);
+      default: return reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 8, false, false>);
     }
   }
   switch (nb) {
@@ -1513,21 +1721,7 @@ void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool
   c.panel = A->panel;
   c.pblock = A->pblock;
   c.line = use_lines(A) ? A->line : 0;
-  c.line_chunks = 0;
-  if (c.line > 0) {
-    // chunks per XCD so that every workgroup of an XCD gets the same number
-    // of (16-column group, chunk) units: per_xcd / gcd(groups, per_xcd)
-    const int64_t per_xcd = A->grid / kXcds;
-    const int64_t U = (c.line + kTileRows - 1) / kTileRows;
-    const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
-    int64_t a = per_xcd, b = groups;
-    while (b != 0) {
-      const int64_t t = a % b;
-      a = b;
-      b = t;
-    }
-    c.line_chunks = int32_t(per_xcd / a);
-  }
+  c.line_chunks = c.line > 0 ? line_chunks(A) : 0;
 }
 
 // Workgroups for a one-pass kernel over `tiles` wave tiles and `batch` systems.
@@ -1605,7 +1799,10 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   // (automatic: one per CU up to kSmallSolve unknowns over the batch, where
   // the kernels' fixed costs -- each workgroup summing the partials of the
   // previous kernel -- weigh more than the latency hiding of a second one)
-  const int wg = A->wg_per_cu > 0 ? A->wg_per_cu : (A->n * batch <= kSmallSolve ? 1 : 2);
+  // (and for line walks at any size: their waves stream long chunks, and
+  // with half the workgroups each chunk is twice as long)
+  const int wg = A->wg_per_cu > 0 ? A->wg_per_cu
+                                  : (A->n * batch <= kSmallSolve || use_lines(A) ? 1 : 2);
   const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * wg / batch);
   int64_t g = std::min<int64_t>((A->tiles + kWaves - 1) / kWaves, target);
   g = (g + kXcds - 1) / kXcds * kXcds;

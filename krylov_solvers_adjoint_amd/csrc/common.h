@@ -78,6 +78,12 @@ constexpr int kPanelTiles = 64;    // widest column block of the panel tile orde
 // registers each)
 constexpr int kLineWaves = 8;
 constexpr int kLineWavesPerEu = 2 * kLineWaves / 4;
+// a line walk whose waves walk at least this many lines per chunk keeps two
+// tiles of loads in flight (shorter walks do better with one)
+constexpr int64_t kPipeLines = 12;
+// ... on matrices of at most this many rows (beyond, the walk streams from
+// HBM and the simpler loop is as fast)
+constexpr int64_t kPipeMaxRows = int64_t(1) << 26;
 // a line walk needs at least 16 tile columns per line
 constexpr int64_t kMinWalkLine = int64_t(kIterBlock / kWave - 1) * kTileRows + 1;
 // a 64-row tile whose columns span more than this is "wide" (the span of a

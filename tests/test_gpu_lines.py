@@ -94,3 +94,22 @@ def test_line_walk_vs_banded_same_iterates():
     ba = _solve(rp, c, v, b, g, 0.0, 200, variant="banded")
     assert la[0] and not ba[0]
     assert rel(la[1], ba[1]) <= 1e-11 and rel(la[2], ba[2]) <= 1e-11
+
+
+@pytest.mark.parametrize("n,L,wg", [(1000 * 1599 + 371, 1000, 1), (961 * 3200 + 5, 961, 2)])
+def test_long_chunks_short_last_line(n, L, wg):
+    """Walks of a dozen lines or more per chunk (1600 lines over 8 XCDs x 16
+    chunks; 3201 lines over 8 x 32), which keep two tiles of loads in flight,
+    with a short last line and couplings across line ends."""
+    rp, c, v = W.band_csr(n, [-L, -1, 1, L], 4.5)
+    b = W.uniform_rhs(n, 27)
+    g = W.normal_rhs(n, 28)
+    _check(f"band n={n} L={L} wg={wg}", rp, c, v, b, g, 1e-10, 5000, wg=wg)
+
+
+def test_poisson_long_chunks():
+    """Poisson 1700^2 with one workgroup per CU: 26 lines per chunk."""
+    rp, c, v = W.poisson_csr(1700, np.int32)
+    b = W.uniform_rhs(1700 * 1700, 29)
+    g = W.normal_rhs(1700 * 1700, 30)
+    _check("poisson1700 wg1", rp, c, v, b, g, 0.0, 40, wg=1)
