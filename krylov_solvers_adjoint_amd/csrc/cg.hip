@@ -431,7 +431,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
   const double rr = sum_partials_all(part + 0 * c->grid, c->grid, red);
   const double rz = jac ? sum_partials_all(part + 5 * c->grid, c->grid, red) : 0.0;
   if (threadIdx.x == 0) {
-    Scal* sc = c->scal + s;
+    Scal* sc = scal_of(c, s);
     sc->rr[0] = rr;
     sc->rr[1] = rr;
     sc->rz[0] = rz;
@@ -466,19 +466,55 @@ struct StepHead {
   int32_t stop;  // ST_RUNNING or the final state
 };
 
+// What an SpMV step reads of its system's record and of the context's
+// scalars, loaded at the top of the kernel and pinned (with the kernel's
+// own context fields) before its first branch.  The record's fields are
+// written by earlier launches only (this one writes rr[k & 1], rz[k & 1] and
+// the fields after alpha); both parities are loaded, since an index from k
+// would wait for k.
+struct StepIn {
+  int64_t k;      // index of this SpMV step (ka)
+  int32_t state;  // state_r
+  int32_t jacobi, grid;
+  double rr0, rr1, rz0, rz1, alpha, stop;
+  int64_t maxit;
+};
+
+__device__ __forceinline__ StepIn step_in(const Ctx* __restrict__ c, int64_t s) {
+  const SLA_GLOBAL Scal* scg = gmem(static_cast<const Scal*>(scal_of(c, s)));
+  StepIn in;
+  in.k = scg->ka;
+  in.state = scg->state_r;
+  in.jacobi = c->jacobi;
+  in.grid = c->grid;
+  in.rr0 = scg->rr[0];
+  in.rr1 = scg->rr[1];
+  in.rz0 = scg->rz[0];
+  in.rz1 = scg->rz[1];
+  in.alpha = scg->alpha;
+  in.stop = scg->stop;
+  in.maxit = scg->maxit;
+  pin(in.k, in.state, in.jacobi, in.grid, in.rr0, in.rr1, in.rz0, in.rz1, in.alpha, in.stop,
+      in.maxit);
+  return in;
+}
+
 template <int NT = kIterBlock>
 __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t s,
-                                              double* red) {
-  Scal* sc = c->scal + s;
+                                              const StepIn& in, double* red) {
+  Scal* sc = scal_of(c, s);
+  const int64_t k = in.k;
+  const double rr_prev = (k & 1) ? in.rr0 : in.rr1, rz_prev = (k & 1) ? in.rz0 : in.rz1;
+  const double alpha_in = in.alpha, stop_at = in.stop;
+  const int64_t maxit = in.maxit;
   const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
-  const int G = c->grid;
+  const int G = in.grid;
   const SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   StepHead h;
-  h.k = sc->ka;
-  const int64_t k = h.k;
+  h.k = k;
   const double rr = sum_partials_all<NT>(part + (k & 1) * G, G, red);
   // Jacobi: beta from r.z, the stopping test still on r.r
-  const bool jac = c->jacobi != 0;
+  const bool jac = in.jacobi != 0;
   const double rz = jac ? sum_partials_all<NT>(part + (5 + (k & 1)) * G, G, red) : 0.0;
   h.lag = k > 0;
   h.alpha = 0.0;
@@ -487,19 +523,18 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
   int64_t it_stop = k;
   double rr_stop = rr;
   if (h.lag) {
-    const double rr_prev = sc->rr[(k - 1) & 1];
-    h.alpha = sc->alpha;
+    h.alpha = alpha_in;
     if (!isfinite(rr) || !isfinite(rz)) {
       h.stop = ST_NONFINITE;  // iteration k-1 did not complete
       it_stop = k - 1;
       rr_stop = rr_prev;
     } else {
-      h.beta = jac ? rz / sc->rz[(k - 1) & 1] : rr / rr_prev;
+      h.beta = jac ? rz / rz_prev : rr / rr_prev;
     }
   }
   if (h.stop == ST_RUNNING) {
-    if (rr <= sc->stop) h.stop = ST_CONVERGED;
-    else if (k >= sc->maxit) h.stop = ST_MAXIT;
+    if (rr <= stop_at) h.stop = ST_CONVERGED;
+    else if (k >= maxit) h.stop = ST_MAXIT;
   }
   if (lead) {
     if (h.lag && h.stop != ST_NONFINITE && c->hist != nullptr && k - 1 < c->hist_cap) {
@@ -544,13 +579,14 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
   const SLA_GLOBAL double* r = gmem(c->rd + s * n);  // r, or z with Jacobi
   SLA_GLOBAL double* q = gmem(c->q + s * n);
   SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
-  Scal* sc = c->scal + s;
-  const int32_t st_in = sc->state_r;
+  Scal* sc = scal_of(c, s);
+  const StepIn in = step_in(c, s);
+  const int32_t st_in = in.state;
   if (st_in != ST_RUNNING) {
     if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
     return;
   }
-  const StepHead h = step_head(c, s, red);
+  const StepHead h = step_head(c, s, in, red);
   const int64_t k = uniform(h.k);
   const double alpha = uniform(h.alpha), beta = uniform(h.beta);
   const bool lag = h.lag;
@@ -667,20 +703,112 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   const SLA_GLOBAL double* r = gmem(c->rd + s * n);  // r, or z with Jacobi
   SLA_GLOBAL double* q = gmem(c->q + s * n);
   SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
-  Scal* sc = c->scal + s;
-  const int32_t st_in = sc->state_r;
+  Scal* sc = scal_of(c, s);
+  const StepIn in = step_in(c, s);
+  pin(n, nnz, tiles, L, G, chunks, rowptr, mask, band.count, vals, p0, p1, x, r, q, part);
+  const int64_t k = in.k;
+  const int32_t st_in = in.state;
   if (st_in != ST_RUNNING) {
     if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
     return;
   }
-  const StepHead h = step_head<NT>(c, s, red);
-  const int64_t k = uniform(h.k);
-  const double alpha = uniform(h.alpha), beta = uniform(h.beta);
-  const bool lag = h.lag;
   const SLA_GLOBAL double* pold = gmem((k & 1) ? p0 : p1);
   SLA_GLOBAL double* pnew = gmem((k & 1) ? p1 : p0);
   const int w = wave_index();
   const uint32_t lane = lane_id();
+  const int64_t U = (L + kTileRows - 1) / kTileRows;  // tile columns per line
+  const int64_t V = (n + L - 1) / L;                  // lines
+  const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
+  const int64_t units = groups * chunks;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = G / kXcds;
+  const int64_t va = V * xcd / kXcds, vb = V * (xcd + 1) / kXcds;
+  // A unit of the walk: tile column u over the lines [v0, v1).  A unit with
+  // no rows (past the last unit, a column past the line, an empty chunk)
+  // stands for column 0 on line 0: its loads stay in the matrix, and it is
+  // not walked.
+  struct Unit {
+    int64_t v0, v1, col0, lenu;
+    bool ok;
+  };
+  auto unit_at = [&](int64_t unit) -> Unit {
+    const int64_t u = (unit / chunks) * kLineWaves + w;
+    const int64_t ch = unit % chunks;
+    const int64_t v0 = va + (vb - va) * ch / chunks, v1 = va + (vb - va) * (ch + 1) / chunks;
+    const int64_t col0 = u * kTileRows;
+    if (unit >= units || u >= U || v0 >= v1 || v0 * L + col0 >= n)
+      return Unit{0, 1, 0, L < kTileRows ? L : kTileRows, false};
+    return Unit{v0, v1, col0, L - col0 < kTileRows ? L - col0 : kTileRows, true};
+  };
+  // rows of tile v: v*L + col0 + [0, len(v)); lane clamped to the last one
+  auto tile_len = [&](const Unit& ug, int64_t v) -> int64_t {
+    const int64_t left = n - (v * L + ug.col0);
+    return left < ug.lenu ? left : ug.lenu;
+  };
+  auto clamp_lane = [&](int64_t len) -> uint32_t {
+    return int64_t(lane) < len ? lane : uint32_t(len - 1);
+  };
+  // A tile of the walk: first row, the lane's (clamped) row, its length; a
+  // line past the matrix stands for the tile before it (its loads repeat
+  // that tile's, unconditionally, and nothing of them is used).
+  struct TileRef {
+    int64_t r0;
+    int64_t len;
+    uint32_t lr;
+    bool has;
+  };
+  auto tile_ref = [&](const Unit& ug, int64_t v, const TileRef& before) -> TileRef {
+    const int64_t lv = v < V ? tile_len(ug, v) : 0;
+    if (lv > 0) return TileRef{v * L + ug.col0, lv, clamp_lane(lv), true};
+    return TileRef{before.r0, before.len, before.lr, false};
+  };
+  // rows just outside a tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
+  // clamped into [0, n); the same value in every lane
+  auto edges = [&](int64_t e0, int64_t elen, double& rl, double& pl, double& rr, double& pr) {
+    const int64_t a = e0 > 0 ? e0 - 1 : 0;
+    const int64_t b = e0 + elen < n ? e0 + elen : n - 1;
+    rl = ld(r + a, 0u);
+    pl = ld(pold + a, 0u);
+    rr = ld(r + b, 0u);
+    pr = ld(pold + b, 0u);
+  };
+  // A unit's loads that need no scalar of the step: r and p_{k-1} of the
+  // tile below the first (the -L neighbours; the first tile itself on the
+  // first line, not used), of the first tile and (PIPE) the second, their
+  // index data, the first tile's edge rows and (PIPE) its x.
+  struct Pre {
+    double rb, pb, rc, pc, rn, pn;
+    TileIndex<RP> ix0, ix1;
+    double rl, pl, rr, pr, x0;
+  };
+  auto issue = [&](const Unit& ug) -> Pre {
+    Pre e{};
+    const int64_t first = ug.v0 * L + ug.col0;
+    const int64_t len0 = tile_len(ug, ug.v0);
+    const uint32_t l0 = clamp_lane(len0);
+    const int64_t b0 = ug.v0 >= 1 ? first - L : first;
+    const uint32_t lb = ug.v0 >= 1 ? clamp_lane(ug.lenu) : l0;
+    e.rb = ld(r + b0, lb);
+    e.pb = ld(pold + b0, lb);
+    e.rc = ld(r + first, l0);
+    e.pc = ld(pold + first, l0);
+    if constexpr (PIPE) {
+      const TileRef t0{first, len0, l0, true};
+      const TileRef t1 = tile_ref(ug, ug.v0 + 1, t0);
+      e.rn = ld(r + t1.r0, t1.lr);
+      e.pn = ld(pold + t1.r0, t1.lr);
+      e.ix0 = tile_index<NB, RP>(rowptr, mask, n, first, l0);
+      e.ix1 = tile_index<NB, RP>(rowptr, mask, n, t1.r0, t1.lr);
+    } else {
+      e.ix0 = tile_index<NB, RP>(rowptr, mask, n, first, l0);
+    }
+    if constexpr (NEAR1) edges(first, len0, e.rl, e.pl, e.rr, e.pr);
+    if constexpr (PIPE) e.x0 = ld(x + first, l0);
+    return e;
+  };
+  Pre pre = issue(unit_at(slot));
+  const StepHead h = step_head<NT>(c, s, in, red);
+  const double alpha = uniform(h.alpha), beta = uniform(h.beta);
+  const bool lag = h.lag;
   if (h.stop != ST_RUNNING) {
     // last pass: only the deferred x update
     if (lag) {
@@ -695,330 +823,267 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   // offsets: off[0] = -L and off[count-1] = +L (from registers), 0 (the row
   // itself), the others within +-63 (gathered)
   const Gather<true, false> g{r, pold, beta};
-  const int64_t U = (L + kTileRows - 1) / kTileRows;  // tile columns per line
-  const int64_t V = (n + L - 1) / L;                  // lines
-  const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = G / kXcds;
-  const int64_t va = V * xcd / kXcds, vb = V * (xcd + 1) / kXcds;
   double pq = 0.0;
-  for (int64_t unit = slot; unit < groups * chunks; unit += per_xcd) {
-    const int64_t u = (unit / chunks) * kLineWaves + w;
-    const int64_t ch = unit % chunks;
-    const int64_t v0 = va + (vb - va) * ch / chunks, v1 = va + (vb - va) * (ch + 1) / chunks;
-    const int64_t col0 = u * kTileRows;
-    if (u >= U || v0 >= v1 || v0 * L + col0 >= n) continue;
-    const int64_t lenu = L - col0 < kTileRows ? L - col0 : kTileRows;
-    // rows of tile v: v*L + col0 + [0, len(v)); lane clamped to the last one
-    auto tile_len = [&](int64_t v) -> int64_t {
-      const int64_t left = n - (v * L + col0);
-      return left < lenu ? left : lenu;
-    };
-    auto clamp_lane = [&](int64_t len) -> uint32_t {
-      return int64_t(lane) < len ? lane : uint32_t(len - 1);
-    };
-    if constexpr (PIPE) {
-      // -L neighbours of the first tile
-      double pprev = 0.0;
-      if (v0 >= 1) {
-        const int64_t pr0 = (v0 - 1) * L + col0;
-        const uint32_t pl = clamp_lane(lenu);
-        pprev = ld(r + pr0, pl) + beta * ld(pold + pr0, pl);
-      }
-      // A tile of the walk: first row, the lane's (clamped) row, its length;
-      // a line past the matrix stands for the tile before it (its loads repeat
-      // that tile's, unconditionally, and nothing of them is used).
-      struct TileRef {
-        int64_t r0;
-        int64_t len;
-        uint32_t lr;
-        bool has;
-      };
-      auto tile_ref = [&](int64_t v, const TileRef& before) -> TileRef {
-        const int64_t lv = v < V ? tile_len(v) : 0;
-        if (lv > 0) return TileRef{v * L + col0, lv, clamp_lane(lv), true};
-        return TileRef{before.r0, before.len, before.lr, false};
-      };
-      // nothing past the chunk is loaded but the +L neighbours of its last
-      // tile: later tiles' loads repeat the tile before (cache hits)
-      auto pick = [&](bool c, const TileRef& a_, const TileRef& b_) -> TileRef {
-        return TileRef{c ? a_.r0 : b_.r0, c ? a_.len : b_.len, c ? a_.lr : b_.lr, c ? a_.has : b_.has};
-      };
-      // rows just outside the tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
-      // clamped into [0, n); the same value in every lane
-      auto edges = [&](const TileRef& tr, double& rl, double& pl, double& rr, double& pr) {
-        const int64_t a = tr.r0 > 0 ? tr.r0 - 1 : 0;
-        const int64_t b = tr.r0 + tr.len < n ? tr.r0 + tr.len : n - 1;
-        rl = ld(r + a, 0u);
-        pl = ld(pold + a, 0u);
-        rr = ld(r + b, 0u);
-        pr = ld(pold + b, 0u);
-      };
-      // the tile's values at the slot positions of the lane's row (see
-      // band_row): issued from index data loaded a step earlier
-      auto load_values = [&](const TileIndex<RP>& ixv, const TileRef& tr, double (&a)[NB],
-                             unsigned& m) {
-        const int64_t s0 = uniform(int64_t(ixv.s0));
-        m = ixv.m;
-        const bool ownv = int64_t(lane) < tr.len;
-        const int kx = wave_exclusive_sum(ownv ? __builtin_popcount(m) : 0);
-        uint32_t kk = uint32_t(__shfl(kx, int(tr.lr), kWave));
-        const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
-  #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const bool use = t < band.count && ((m >> t) & 1u);
-          a[t] = ld(vb_, use ? kk : 0u);
-          kk += use ? 1u : 0u;
-        }
-      };
-      // The walk is a pipeline two tiles deep: step v computes tile v from
-      // data issued in the steps before, and issues r, p_{k-1} and the index
-      // data of tile v + 2, and the values, x and edge rows of tile v + 1.
-      TileRef tc{v0 * L + col0, tile_len(v0), 0u, true};
-      tc.lr = clamp_lane(tc.len);
-      TileRef t1 = tile_ref(v0 + 1, tc);
-      double rc = ld(r + tc.r0, tc.lr), pc = ld(pold + tc.r0, tc.lr);
-      double rn = ld(r + t1.r0, t1.lr), pn = ld(pold + t1.r0, t1.lr);
-      TileIndex<RP> ixc = tile_index<NB, RP>(rowptr, mask, n, tc.r0, tc.lr);
-      TileIndex<RP> ix1 = tile_index<NB, RP>(rowptr, mask, n, t1.r0, t1.lr);
-      double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
-      if constexpr (NEAR1) edges(tc, rl, pl, rr, pr);
+  for (int64_t unit = slot; unit < units; unit += per_xcd) {
+    const Unit ug = unit_at(unit);
+    if (ug.ok) {
+      const int64_t v0 = ug.v0, v1 = ug.v1, col0 = ug.col0, lenu = ug.lenu;
       wait_vmem();
-      double a[NB];
-      unsigned m = 0;
-      load_values(ixc, tc, a, m);
-      double xo = ld(x + tc.r0, tc.lr);
-      for (int64_t v = v0; v < v1; ++v) {
-        const int64_t r0 = tc.r0;
-        const uint32_t lr = tc.lr;
-        const int64_t len = tc.len;
-        const bool own = int64_t(lane) < len;
-        // tile v + 2: r, p_{k-1} and index data (the +L neighbours of tile
-        // v + 1, read in the next step; needed up to tile v1)
-        const TileRef t2 = pick(v + 2 <= v1, tile_ref(v + 2, t1), t1);
-        const double rn2 = ld(r + t2.r0, t2.lr), pn2 = ld(pold + t2.r0, t2.lr);
-        const TileIndex<RP> ix2 = tile_index<NB, RP>(rowptr, mask, n, t2.r0, t2.lr);
-        // tile v + 1: x and edge rows, then its values (inside the chunk only)
-        const bool in1 = v + 1 < v1;
-        const TileRef tv = pick(in1, t1, tc);
-        const double xn = ld(x + tv.r0, tv.lr);
-        double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
-        if constexpr (NEAR1) edges(tv, rln, pln, rrn, prn);
-        double an[NB];
-        unsigned mn = 0;
-        TileIndex<RP> ixv = ixc;
-        ixv.s0 = in1 ? ix1.s0 : ixc.s0;
-        ixv.m = in1 ? ix1.m : ixc.m;
-        load_values(ixv, tv, an, mn);
-        // near offsets of tile v, gathered; the other kinds read the row
-        // itself (no branch; the value is not used)
-        const int64_t lo = r0 - kTileRows;
-        const int64_t base = lo > 0 ? lo : 0;
-        const int32_t d = int32_t(r0 - base) + int32_t(lr);
-        const int32_t top = int32_t(n - 1 - base);
-        // offsets are sorted: -L first, +L last, the near ones in between
-        double gu[NB], gw[NB];
-        if constexpr (!NEAR1) {
-  #pragma unroll
-          for (int t = 1; t < NB - 1; ++t) {
-            const int32_t o = t < band.count - 1 ? band.off[t] : 0;
-            int32_t j = d + o;
-            j = j < 0 ? 0 : (j > top ? top : j);
-            g.load_at(base, uint32_t(j), gu[t], gw[t]);
-          }
-        }
-        // p_k at the row, below (-L) and above (+L)
-        const double pcur = rc + beta * pc;
-        const double pnext = rn + beta * pn;
-        // lanes past the end of a short tile compute its last row: take that
-        // row's -L value (the previous tile was loaded lane for lane)
-        const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
-        // NEAR1: p_k at the rows before and after, from the neighbouring lanes
-        // or, at the ends of the tile, from the rows just outside it
-        double pm1 = 0.0, pp1 = 0.0;
-        if constexpr (NEAR1) {
-          const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
-          const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
-          pm1 = lr == 0 ? rl + beta * pl : sm;
-          pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
-        }
-        double acc = 0.0;
-  #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const int32_t o = t < band.count ? band.off[t] : 0;
-          const bool use = t < band.count && ((m >> t) & 1u);
-          double gv;
-          if (t == 0) gv = pbelow;
-          else if (t == NB - 1) gv = pnext;
-          else if (t == band.count - 1) gv = pnext;
-          else if (o == 0) gv = pcur;
-          else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
-          else gv = g.value(gu[t], gw[t]);
-          const double sum = acc + a[t] * gv;
-          acc = use ? sum : acc;
-        }
-        // lanes past the last row store the same bits as the row's own lane;
-        // x is stored back unchanged when there is no lagged update (no branch
-        // around a store: it would make the compiler wait for older stores)
-        st(x + r0, lr, lag ? xo + alpha * pc : xo);
-        st(pnew + r0, lr, pcur);
-        st(q + r0, lr, acc);
-        const double pq1 = pq + pcur * acc;
-        pq = own ? pq1 : pq;
-        // shift the walk down one line
-        if (!t1.has) break;
-        pprev = pcur;
-        rc = rn;
-        pc = pn;
-        rn = rn2;
-        pn = pn2;
-  #pragma unroll
-        for (int t = 0; t < NB; ++t) a[t] = an[t];
-        m = mn;
-        xo = xn;
-        if constexpr (NEAR1) {
-          rl = rln;
-          pl = pln;
-          rr = rrn;
-          pr = prn;
-        }
-        ixc = ix1;
-        ix1 = ix2;
-        tc = t1;
-        t1 = t2;
-      }
-    } else {
-      // the walk with one tile of look-ahead (r, p_{k-1} and index data of
-      // the next tile); shorter chunks run faster this way
       // -L neighbours of the first tile
-      double pprev = 0.0;
-      if (v0 >= 1) {
-        const int64_t pr0 = (v0 - 1) * L + col0;
-        const uint32_t pl = clamp_lane(lenu);
-        pprev = ld(r + pr0, pl) + beta * ld(pold + pr0, pl);
-      }
-      int64_t len = tile_len(v0);
-      uint32_t lr = clamp_lane(len);
-      double rc = ld(r + v0 * L + col0, lr), pc = ld(pold + v0 * L + col0, lr);
-      TileIndex<RP> ix = tile_index<NB, RP>(rowptr, mask, n, v0 * L + col0, lr);
-      // rows just outside the tile (NEAR1): r and p_{k-1} at r0 - 1 and r0 + len,
-      // clamped into [0, n)
-      auto edges = [&](int64_t e0, int64_t elen, double& rl, double& pl, double& rr, double& pr) {
-        const int64_t a = e0 > 0 ? e0 - 1 : 0;
-        const int64_t b = e0 + elen < n ? e0 + elen : n - 1;
-        rl = ld(r + a, 0u);
-        pl = ld(pold + a, 0u);
-        rr = ld(r + b, 0u);
-        pr = ld(pold + b, 0u);
-      };
-      // the current tile's edge rows live in scalar registers (the same value
-      // in every lane); the next tile's arrive in vector registers
-      double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
-      if constexpr (NEAR1) {
-        edges(v0 * L + col0, len, rl, pl, rr, pr);
-        rl = uniform(rl);
-        pl = uniform(pl);
-        rr = uniform(rr);
-        pr = uniform(pr);
-      }
-      wait_vmem();
-      for (int64_t v = v0; v < v1; ++v) {
-        const int64_t r0 = v * L + col0;
-        const bool own = int64_t(lane) < len;
-        // the next tile: +L neighbours now, own operands in the next step
-        const int64_t lenn = v + 1 < V ? tile_len(v + 1) : 0;
-        const bool hasn = lenn > 0;
-        const int64_t rn0 = hasn ? r0 + L : r0;
-        const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
-        const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
-        double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
-        if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
-        const TileIndex<RP> cur = ix;
-        // unconditional (the current tile again when there is no next one): a
-        // conditional load would make the compiler copy the old value into its
-        // register first, which waits for older loads and stores
-        ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
-        const double xo = ld(x + r0, lr);
-        // near offsets, gathered; the other kinds read the row itself (no
-        // branch; the value is not used)
-        const int64_t lo = r0 - kTileRows;
-        const int64_t base = lo > 0 ? lo : 0;
-        const int32_t d = int32_t(r0 - base) + int32_t(lr);
-        const int32_t top = int32_t(n - 1 - base);
-        // offsets are sorted: -L first, +L last, the near ones in between
-        double gu[NB], gw[NB];
-        if constexpr (!NEAR1) {
+      double pprev = v0 >= 1 ? pre.rb + beta * pre.pb : 0.0;
+      if constexpr (PIPE) {
+        // the tile's values at the slot positions of the lane's row (see
+        // band_row): issued from index data loaded a step earlier
+        auto load_values = [&](const TileIndex<RP>& ixv, const TileRef& tr, double (&a)[NB],
+                               unsigned& m) {
+          const int64_t s0 = uniform(int64_t(ixv.s0));
+          m = ixv.m;
+          const bool ownv = int64_t(lane) < tr.len;
+          const int kx = wave_exclusive_sum(ownv ? __builtin_popcount(m) : 0);
+          uint32_t kk = uint32_t(__shfl(kx, int(tr.lr), kWave));
+          const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
   #pragma unroll
-          for (int t = 1; t < NB - 1; ++t) {
-            const int32_t o = t < band.count - 1 ? band.off[t] : 0;
-            int32_t j = d + o;
-            j = j < 0 ? 0 : (j > top ? top : j);
-            g.load_at(base, uint32_t(j), gu[t], gw[t]);
+          for (int t = 0; t < NB; ++t) {
+            const bool use = t < band.count && ((m >> t) & 1u);
+            a[t] = ld(vb_, use ? kk : 0u);
+            kk += use ? 1u : 0u;
           }
-        }
-        // values at the slot positions of the row (see band_row)
-        const int64_t s0 = uniform(int64_t(cur.s0));
-        const unsigned m = cur.m;
-        const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
-        uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
-        const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+        };
+        // nothing past the chunk is loaded but the +L neighbours of its last
+        // tile: later tiles' loads repeat the tile before (cache hits)
+        auto pick = [&](bool c, const TileRef& a_, const TileRef& b_) -> TileRef {
+          return TileRef{c ? a_.r0 : b_.r0, c ? a_.len : b_.len, c ? a_.lr : b_.lr,
+                         c ? a_.has : b_.has};
+        };
+        // The walk is a pipeline two tiles deep: step v computes tile v from
+        // data issued in the steps before, and issues r, p_{k-1} and the index
+        // data of tile v + 2, and the values, x and edge rows of tile v + 1.
+        TileRef tc{v0 * L + col0, tile_len(ug, v0), 0u, true};
+        tc.lr = clamp_lane(tc.len);
+        TileRef t1 = tile_ref(ug, v0 + 1, tc);
+        double rc = pre.rc, pc = pre.pc, rn = pre.rn, pn = pre.pn;
+        TileIndex<RP> ixc = pre.ix0, ix1 = pre.ix1;
+        double rl = pre.rl, pl = pre.pl, rr = pre.rr, pr = pre.pr;
         double a[NB];
-  #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const bool use = t < band.count && ((m >> t) & 1u);
-          a[t] = ld(vb_, use ? kk : 0u);
-          kk += use ? 1u : 0u;
+        unsigned m = 0;
+        load_values(ixc, tc, a, m);
+        double xo = pre.x0;
+        for (int64_t v = v0; v < v1; ++v) {
+          const int64_t r0 = tc.r0;
+          const uint32_t lr = tc.lr;
+          const int64_t len = tc.len;
+          const bool own = int64_t(lane) < len;
+          // tile v + 2: r, p_{k-1} and index data (the +L neighbours of tile
+          // v + 1, read in the next step; needed up to tile v1)
+          const TileRef t2 = pick(v + 2 <= v1, tile_ref(ug, v + 2, t1), t1);
+          const double rn2 = ld(r + t2.r0, t2.lr), pn2 = ld(pold + t2.r0, t2.lr);
+          const TileIndex<RP> ix2 = tile_index<NB, RP>(rowptr, mask, n, t2.r0, t2.lr);
+          // tile v + 1: x and edge rows, then its values (inside the chunk only)
+          const bool in1 = v + 1 < v1;
+          const TileRef tv = pick(in1, t1, tc);
+          const double xn = ld(x + tv.r0, tv.lr);
+          double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+          if constexpr (NEAR1) edges(tv.r0, tv.len, rln, pln, rrn, prn);
+          double an[NB];
+          unsigned mn = 0;
+          TileIndex<RP> ixv = ixc;
+          ixv.s0 = in1 ? ix1.s0 : ixc.s0;
+          ixv.m = in1 ? ix1.m : ixc.m;
+          load_values(ixv, tv, an, mn);
+          // near offsets of tile v, gathered; the other kinds read the row
+          // itself (no branch; the value is not used)
+          const int64_t lo = r0 - kTileRows;
+          const int64_t base = lo > 0 ? lo : 0;
+          const int32_t d = int32_t(r0 - base) + int32_t(lr);
+          const int32_t top = int32_t(n - 1 - base);
+          // offsets are sorted: -L first, +L last, the near ones in between
+          double gu[NB], gw[NB];
+          if constexpr (!NEAR1) {
+    #pragma unroll
+            for (int t = 1; t < NB - 1; ++t) {
+              const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+              int32_t j = d + o;
+              j = j < 0 ? 0 : (j > top ? top : j);
+              g.load_at(base, uint32_t(j), gu[t], gw[t]);
+            }
+          }
+          // p_k at the row, below (-L) and above (+L)
+          const double pcur = rc + beta * pc;
+          const double pnext = rn + beta * pn;
+          // lanes past the end of a short tile compute its last row: take that
+          // row's -L value (the previous tile was loaded lane for lane)
+          const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+          // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+          // or, at the ends of the tile, from the rows just outside it
+          double pm1 = 0.0, pp1 = 0.0;
+          if constexpr (NEAR1) {
+            const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+            const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+            pm1 = lr == 0 ? rl + beta * pl : sm;
+            pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+          }
+          double acc = 0.0;
+    #pragma unroll
+          for (int t = 0; t < NB; ++t) {
+            const int32_t o = t < band.count ? band.off[t] : 0;
+            const bool use = t < band.count && ((m >> t) & 1u);
+            double gv;
+            if (t == 0) gv = pbelow;
+            else if (t == NB - 1) gv = pnext;
+            else if (t == band.count - 1) gv = pnext;
+            else if (o == 0) gv = pcur;
+            else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+            else gv = g.value(gu[t], gw[t]);
+            const double sum = acc + a[t] * gv;
+            acc = use ? sum : acc;
+          }
+          // lanes past the last row store the same bits as the row's own lane;
+          // x is stored back unchanged when there is no lagged update (no branch
+          // around a store: it would make the compiler wait for older stores)
+          st(x + r0, lr, lag ? xo + alpha * pc : xo);
+          st(pnew + r0, lr, pcur);
+          st(q + r0, lr, acc);
+          const double pq1 = pq + pcur * acc;
+          pq = own ? pq1 : pq;
+          // shift the walk down one line
+          if (!t1.has) break;
+          pprev = pcur;
+          rc = rn;
+          pc = pn;
+          rn = rn2;
+          pn = pn2;
+    #pragma unroll
+          for (int t = 0; t < NB; ++t) a[t] = an[t];
+          m = mn;
+          xo = xn;
+          if constexpr (NEAR1) {
+            rl = rln;
+            pl = pln;
+            rr = rrn;
+            pr = prn;
+          }
+          ixc = ix1;
+          ix1 = ix2;
+          tc = t1;
+          t1 = t2;
         }
-        // p_k at the row, below (-L) and above (+L)
-        const double pcur = rc + beta * pc;
-        const double pnext = rn + beta * pn;
-        // lanes past the end of a short tile compute its last row: take that
-        // row's -L value (the previous tile was loaded lane for lane)
-        const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
-        // NEAR1: p_k at the rows before and after, from the neighbouring lanes
-        // or, at the ends of the tile, from the rows just outside it
-        double pm1 = 0.0, pp1 = 0.0;
+      } else {
+        // the walk with one tile of look-ahead (r, p_{k-1} and index data of
+        // the next tile); shorter chunks run faster this way
+        int64_t len = tile_len(ug, v0);
+        uint32_t lr = clamp_lane(len);
+        double rc = pre.rc, pc = pre.pc;
+        TileIndex<RP> ix = pre.ix0;
+        // the current tile's edge rows live in scalar registers (the same value
+        // in every lane); the next tile's arrive in vector registers
+        double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
         if constexpr (NEAR1) {
-          const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
-          const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
-          pm1 = lr == 0 ? rl + beta * pl : sm;
-          pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+          rl = uniform(pre.rl);
+          pl = uniform(pre.pl);
+          rr = uniform(pre.rr);
+          pr = uniform(pre.pr);
         }
-        double acc = 0.0;
-  #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const int32_t o = t < band.count ? band.off[t] : 0;
-          const bool use = t < band.count && ((m >> t) & 1u);
-          double gv;
-          if (t == 0) gv = pbelow;
-          else if (t == NB - 1) gv = pnext;
-          else if (t == band.count - 1) gv = pnext;
-          else if (o == 0) gv = pcur;
-          else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
-          else gv = g.value(gu[t], gw[t]);
-          const double sum = acc + a[t] * gv;
-          acc = use ? sum : acc;
+        for (int64_t v = v0; v < v1; ++v) {
+          const int64_t r0 = v * L + col0;
+          const bool own = int64_t(lane) < len;
+          // the next tile: +L neighbours now, own operands in the next step
+          const int64_t lenn = v + 1 < V ? tile_len(ug, v + 1) : 0;
+          const bool hasn = lenn > 0;
+          const int64_t rn0 = hasn ? r0 + L : r0;
+          const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
+          const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
+          double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+          if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
+          const TileIndex<RP> cur = ix;
+          // unconditional (the current tile again when there is no next one): a
+          // conditional load would make the compiler copy the old value into its
+          // register first, which waits for older loads and stores
+          ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
+          const double xo = ld(x + r0, lr);
+          // near offsets, gathered; the other kinds read the row itself (no
+          // branch; the value is not used)
+          const int64_t lo = r0 - kTileRows;
+          const int64_t base = lo > 0 ? lo : 0;
+          const int32_t d = int32_t(r0 - base) + int32_t(lr);
+          const int32_t top = int32_t(n - 1 - base);
+          // offsets are sorted: -L first, +L last, the near ones in between
+          double gu[NB], gw[NB];
+          if constexpr (!NEAR1) {
+    #pragma unroll
+            for (int t = 1; t < NB - 1; ++t) {
+              const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+              int32_t j = d + o;
+              j = j < 0 ? 0 : (j > top ? top : j);
+              g.load_at(base, uint32_t(j), gu[t], gw[t]);
+            }
+          }
+          // values at the slot positions of the row (see band_row)
+          const int64_t s0 = uniform(int64_t(cur.s0));
+          const unsigned m = cur.m;
+          const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
+          uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
+          const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+          double a[NB];
+    #pragma unroll
+          for (int t = 0; t < NB; ++t) {
+            const bool use = t < band.count && ((m >> t) & 1u);
+            a[t] = ld(vb_, use ? kk : 0u);
+            kk += use ? 1u : 0u;
+          }
+          // p_k at the row, below (-L) and above (+L)
+          const double pcur = rc + beta * pc;
+          const double pnext = rn + beta * pn;
+          // lanes past the end of a short tile compute its last row: take that
+          // row's -L value (the previous tile was loaded lane for lane)
+          const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+          // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+          // or, at the ends of the tile, from the rows just outside it
+          double pm1 = 0.0, pp1 = 0.0;
+          if constexpr (NEAR1) {
+            const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+            const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+            pm1 = lr == 0 ? rl + beta * pl : sm;
+            pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+          }
+          double acc = 0.0;
+    #pragma unroll
+          for (int t = 0; t < NB; ++t) {
+            const int32_t o = t < band.count ? band.off[t] : 0;
+            const bool use = t < band.count && ((m >> t) & 1u);
+            double gv;
+            if (t == 0) gv = pbelow;
+            else if (t == NB - 1) gv = pnext;
+            else if (t == band.count - 1) gv = pnext;
+            else if (o == 0) gv = pcur;
+            else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+            else gv = g.value(gu[t], gw[t]);
+            const double sum = acc + a[t] * gv;
+            acc = use ? sum : acc;
+          }
+          // lanes past the last row store the same bits as the row's own lane
+          if (lag) st(x + r0, lr, xo + alpha * pc);
+          st(pnew + r0, lr, pcur);
+          st(q + r0, lr, acc);
+          const double pq1 = pq + pcur * acc;
+          pq = own ? pq1 : pq;
+          // shift the walk down one line
+          pprev = pcur;
+          rc = rn;
+          pc = pn;
+          if constexpr (NEAR1) {
+            rl = uniform(rln);
+            pl = uniform(pln);
+            rr = uniform(rrn);
+            pr = uniform(prn);
+          }
+          len = lenn;
+          lr = lrn;
+          if (!hasn) break;
         }
-        // lanes past the last row store the same bits as the row's own lane
-        if (lag) st(x + r0, lr, xo + alpha * pc);
-        st(pnew + r0, lr, pcur);
-        st(q + r0, lr, acc);
-        const double pq1 = pq + pcur * acc;
-        pq = own ? pq1 : pq;
-        // shift the walk down one line
-        pprev = pcur;
-        rc = rn;
-        pc = pn;
-        if constexpr (NEAR1) {
-          rl = uniform(rln);
-          pl = uniform(pln);
-          rr = uniform(rrn);
-          pr = uniform(prn);
-        }
-        len = lenn;
-        lr = lrn;
-        if (!hasn) break;
       }
     }
+    // the next unit's first loads
+    if (unit + per_xcd < units) pre = issue(unit_at(unit + per_xcd));
   }
   pq = block_sum_all<NT>(pq, red);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
@@ -1043,13 +1108,14 @@ void k_cg_direction(const Ctx* __restrict__ c) {
   double* const p1 = c->p[1] + s * n;
   const SLA_GLOBAL double* r = gmem(c->rd + s * n);  // r, or z with Jacobi
   SLA_GLOBAL double* x = gmem(c->x + s * n);
-  Scal* sc = c->scal + s;
-  const int32_t st_in = sc->state_r;
+  Scal* sc = scal_of(c, s);
+  const StepIn in = step_in(c, s);
+  const int32_t st_in = in.state;
   if (st_in != ST_RUNNING) {
     if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
     return;
   }
-  const StepHead h = step_head(c, s, red);
+  const StepHead h = step_head(c, s, in, red);
   const int64_t k = uniform(h.k);
   const double alpha = uniform(h.alpha), beta = uniform(h.beta);
   const SLA_GLOBAL double* pold = gmem((k & 1) ? p0 : p1);
@@ -1093,7 +1159,7 @@ void k_cg_product(const Ctx* __restrict__ c) {
   extern __shared__ double lds_dyn[];
   __shared__ double red[kWaves];
   const int64_t s = blockIdx.y;
-  const Scal* sc = c->scal + s;
+  const Scal* sc = scal_of(c, s);
   if (sc->state_a != ST_RUNNING) return;
   const int64_t k = sc->kr, n = c->n;
   const int G = c->grid, cap = c->wave_cap;
@@ -1352,7 +1418,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
     if (i < n) x[i] = xv[j];
   }
   if (t == 0) {
-    Scal* sc = c->scal + s;
+    Scal* sc = scal_of(c, s);
     sc->bb = bb;
     sc->stop = stop;
     sc->maxit = maxit;
@@ -1379,17 +1445,19 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   const SLA_GLOBAL double* dg = gmem(c->diag + s * n);
   SLA_GLOBAL double* z = gmem(c->z + s * n);
   int* const n_running = c->n_running;
-  Scal* sc = c->scal + s;
+  Scal* sc = scal_of(c, s);
   const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
-  const int32_t st_in = sc->state_a;
-  if (st_in != ST_RUNNING) {
-    if (lead) sc->state_r = st_in;
-    return;
-  }
-  // (read through the global address space: a flat load would make the
-  // first wait below cover the tile loads issued after it)
+  // the step index and state come in the context's round trip (read through
+  // the global address space: a flat load would make the first wait below
+  // cover the tile loads issued after it)
   const SLA_GLOBAL Scal* scg = gmem(static_cast<const Scal*>(sc));
   const int64_t k = scg->kr;
+  const int32_t st_in = scg->state_a;
+  // (both parities: an index from k would wait for k)
+  const double rr0 = scg->rr[0], rr1 = scg->rr[1], rz0 = scg->rz[0], rz1 = scg->rz[1];
+  pin(n, tiles, G, part, r, q, dg, z, k, st_in, rr0, rr1, rz0, rz1);
+  const double rr = (k & 1) ? rr1 : rr0;
+  const double num = JAC ? ((k & 1) ? rz1 : rz0) : rr;
   const uint32_t lane = lane_id();
   // blocks of kStreamTiles consecutive tiles (a wave's loads fall in a few
   // DRAM pages), walked like single tiles: each XCD owns a contiguous range
@@ -1418,12 +1486,14 @@ void k_cg_residual(const Ctx* __restrict__ c) {
       if constexpr (JAC) dv[u] = ld(dg + i0, li);
     }
   };
-  // the first round's loads need no scalar: issued before the p.Ap partials
-  // are summed, so that the two latencies overlap
+  // the first round's loads need no scalar: issued before the state is
+  // known and the p.Ap partials are summed, so that the latencies overlap
   load_round(wk.first * B);
+  if (st_in != ST_RUNNING) {
+    if (lead) sc->state_r = st_in;
+    return;
+  }
   const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
-  const double rr = scg->rr[k & 1];
-  const double num = JAC ? scg->rz[k & 1] : rr;
   int32_t stop = ST_RUNNING;
   if (!isfinite(pq)) stop = ST_NONFINITE;
   else if (!(pq > 0.0)) stop = ST_NOT_SPD;
@@ -1762,7 +1832,6 @@ void release_workspace(sla_csr A) {
   dev_free(A->p1);
   dev_free(A->q);
   dev_free(A->part);
-  dev_free(A->scal);
   dev_free(A->n_running);
   dev_free(A->ctx_dev);
   dev_free(A->hist);
@@ -1813,9 +1882,11 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   SLA_TRY(dev_alloc(&A->p1, vec, "p"));
   SLA_TRY(dev_alloc(&A->q, vec, "q"));
   SLA_TRY(dev_alloc(&A->part, size_t(kPartSets) * batch * A->grid, "partials"));
-  SLA_TRY(dev_alloc(&A->scal, batch, "scalars"));
   SLA_TRY(dev_alloc(&A->n_running, 1, "running count"));
-  SLA_TRY(dev_alloc(&A->ctx_dev, 1, "context"));
+  // the context, then the systems' scalars (scal_of)
+  SLA_TRY(dev_alloc(reinterpret_cast<void**>(&A->ctx_dev), sizeof(Ctx) + sizeof(Scal) * batch,
+                    "context and scalars"));
+  A->scal = scal_of(A->ctx_dev, 0);
   SLA_TRY_HIP(hipHostMalloc(reinterpret_cast<void**>(&A->ctx_host), sizeof(Ctx)));
   SLA_TRY_HIP(hipHostMalloc(reinterpret_cast<void**>(&A->scal_host), sizeof(Scal) * batch));
   SLA_TRY_HIP(hipHostMalloc(reinterpret_cast<void**>(&A->poll_host), sizeof(int) * 2));

@@ -139,8 +139,9 @@ struct alignas(64) Scal {
 };
 
 // Everything the solver kernels touch, resident in device memory so that a
-// captured graph stays valid while the caller's x / b / values change.
-struct Ctx {
+// captured graph stays valid while the caller's x / b / values change.  The
+// systems' Scal records follow it in the same allocation (see scal_of).
+struct alignas(64) Ctx {
   const void* rowptr;
   const int32_t* col;
   const double* vals;   // [batch][nnz]
@@ -177,6 +178,14 @@ struct Ctx {
   int64_t line;         // grid line length of a line-walk band (0: none)
   int32_t line_chunks;  // line chunks per XCD in the line walk
 };
+static_assert(sizeof(Ctx) % alignof(Scal) == 0, "Scal records follow the context");
+
+// System s's scalars: the records right after the context, so that a kernel
+// can load them in the same round trip as the context's own fields (through
+// `scal` it would wait for the context first).
+__host__ __device__ __forceinline__ Scal* scal_of(const Ctx* c, int64_t s) {
+  return reinterpret_cast<Scal*>(const_cast<Ctx*>(c) + 1) + s;
+}
 
 // ---------------------------------------------------------------------------
 // Device helpers
@@ -199,6 +208,20 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
   return (uint64_t(hi) << 32) | lo;
 }
+// Ties uniform values to this point of the kernel: their scalar loads are
+// issued before it.  Pinning all the context and record fields a kernel
+// needs ahead of its first branch puts those loads under one wait; left to
+// itself the compiler issues them a round trip apart, or sinks them past the
+// branch, and each round trip costs the latency of the memory-side cache.
+template <typename T>
+__device__ __forceinline__ void pin1(const T& v) {
+  __asm__ __volatile__("" : : "s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void pin(const T&... v) {
+  (pin1(v), ...);
+}
+
 __device__ __forceinline__ double uniform(double v) {
   return __longlong_as_double(int64_t(uniform_u64(uint64_t(__double_as_longlong(v)))));
 }
