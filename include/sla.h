@@ -422,11 +422,12 @@ sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels_host);
  * one by one without graphs).  Affects speed only, never results. */
 sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
 
-/* Solver workgroups (1024 threads each) per compute unit: 0 (default:
- * automatic: 1 for solves of at most 2^21 unknowns over the batch, where the
- * kernels' fixed costs dominate, and for line-walk patterns (2D stencils),
- * whose waves then walk longer chunks; else 2), 1 (16 waves per CU, fewer DRAM
- * pages open at once) or 2 (32 waves per CU).  The grid sets the number and
+/* Solver workgroups per compute unit (1024 threads each; 512 in the line
+ * walk): 0 (default: automatic: 1 for solves of at most 2^21 unknowns over
+ * the batch, where the kernels' fixed costs dominate, and for line-walk
+ * patterns (2D stencils), whose waves then walk longer chunks; else 2), 1
+ * (fewer DRAM pages open at once) or 2 (twice the waves to hide latency).
+ * The grid sets the number and
  * order of the dot-product partial sums, so CG results differ in the last
  * bits between grids; each setting is reproducible.  SpMV results do not
  * change. */
@@ -475,8 +476,10 @@ sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
 
 /*
  * CG loop of small systems.  SLA_ONE_GROUP_AUTO (default): a system of at
- * most 16384 unknowns runs its whole CG loop in one workgroup (one launch per
- * solve, one workgroup per system of the batch, workgroup barriers only),
+ * most 2048 unknowns whose 64-row tiles hold at most 336 stored entries each
+ * (and whose vectors fit one workgroup's LDS) runs its whole CG loop in one
+ * workgroup (one launch per solve, one workgroup per system of the batch,
+ * workgroup barriers only),
  * instead of two kernels over the whole GPU per iteration, whose launch gaps
  * and partial sums dominate at such sizes (Problem statement: launch costs
  * of iterative solvers on small problems).  The same steps, stopping rule,

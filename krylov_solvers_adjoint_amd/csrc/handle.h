@@ -77,8 +77,9 @@ struct sla_csr_s {
   int64_t graph_block = 32;
   // solver workgroups per compute unit: 1, 2, or 0 (by problem size)
   int32_t wg_per_cu = 0;
-  // SLA_ONE_GROUP_AUTO: systems of up to 16384 unknowns run the CG loop in
-  // one workgroup per system; SLA_ONE_GROUP_OFF: always the two-kernel loop
+  // SLA_ONE_GROUP_AUTO: systems of up to 2048 unknowns (tiles of at most
+  // kWaveCap slots) run the CG loop in one workgroup per system;
+  // SLA_ONE_GROUP_OFF: always the two-kernel loop
   int32_t one_group = SLA_ONE_GROUP_AUTO;
   // grid line length L of a band whose far offsets are +-L and whose other
   // offsets lie within +-63 (0: the line walk does not apply)
