@@ -180,21 +180,35 @@ __device__ __forceinline__ double wave_tile_row(const int32_t* col_, const doubl
     wave_sync();
     const int k0 = int(a > c0 ? a - c0 : 0);
     const int k1 = int(e - c0 < clen ? e - c0 : clen);
-    for (int k = k0; k < k1; ++k) acc = acc + lv[k];
+    // the row's products in slot order; four LDS reads in flight at a time
+    // (one round trip per four slots instead of one per slot)
+    int k = k0;
+    for (; k + 4 <= k1; k += 4) {
+      const double p0 = lv[k], p1 = lv[k + 1], p2 = lv[k + 2], p3 = lv[k + 3];
+      acc = acc + p0;
+      acc = acc + p1;
+      acc = acc + p2;
+      acc = acc + p3;
+    }
+    for (; k < k1; ++k) acc = acc + lv[k];
     wave_sync();
   }
   return acc;
 }
 
-// Exclusive prefix sum over the 64 lanes of a wave.
+// Exclusive prefix sum over the 64 lanes of a wave, by data-parallel
+// primitives (DPP) instead of lane permutes through the LDS crossbar: shifts
+// by 1, 2, 4 and 8 lanes within each 16-lane row, then lane 15's total
+// broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.  Lanes with no
+// source lane add 0.  Integer sums: exact in any order.
 __device__ __forceinline__ int wave_exclusive_sum(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
   int inc = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x111, 0xF, 0xF, false);  // row_shr:1
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x112, 0xF, 0xF, false);  // row_shr:2
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x114, 0xF, 0xF, false);  // row_shr:4
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x118, 0xF, 0xF, false);  // row_shr:8
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return inc - v;
 }
 
