@@ -267,12 +267,34 @@ __device__ __forceinline__ int wave_index() {
 }
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// A double moved across lanes by a DPP pattern (two 32-bit moves); lanes
+// without a source lane, or in rows the mask leaves out, read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
-  // butterfly over the 64 lanes; every lane ends with the same total, and
-  // the association order is fixed, so results are reproducible
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  // Sum over the 64 lanes by DPP moves (no lane permutes through LDS), one
+  // fixed association order, the total in every lane: pairs (quad_perm
+  // 1,0,3,2), quads (2,3,0,1), half rows (half mirror) and rows (mirror)
+  // leave every lane of a 16-lane row with the row's sum; row 1 adds row 0's
+  // and row 3 row 2's (broadcast of lane 15), rows 2 and 3 add lane 31's;
+  // lane 63 then holds (r3 + r2) + (r1 + r0), read back into every lane.
+  const int row = int(threadIdx.x & (kWave - 1)) >> 4;
+  v = v + dpp_f64<0xB1>(v);
+  v = v + dpp_f64<0x4E>(v);
+  v = v + dpp_f64<0x141>(v);
+  v = v + dpp_f64<0x140>(v);
+  const double b15 = dpp_f64<0x142, 0xA>(v);
+  v = (row & 1) ? v + b15 : v;
+  const double b31 = dpp_f64<0x143, 0xC>(v);
+  v = (row >= 2) ? v + b31 : v;
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), kWave - 1);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), kWave - 1);
+  return __hiloint2double(hi, lo);
 }
 
 // Sum over a workgroup of NT threads, fixed order, result in every thread.

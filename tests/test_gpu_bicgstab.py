@@ -143,7 +143,10 @@ def test_fixed_iterations_and_warm_start():
 def test_half_step_finish_and_statuses():
     import torch
     import krylov_solvers_adjoint_amd as K
-    # A = 2 I: one iteration, finished on the half step, x = b / 2 exactly
+    # A = 2 I: one iteration, finished on the half step, x = alpha b with
+    # alpha = rhat.r / rhat.v = 1/2 up to one rounding: the two dot products
+    # are summed by different kernels along different trees, so exact halving
+    # holds for some right-hand sides only
     n = 1000
     rp = np.arange(n + 1, dtype=np.int32)
     c = np.arange(n, dtype=np.int32)
@@ -152,7 +155,8 @@ def test_half_step_finish_and_statuses():
     x, infos = K.sla_bicgstab_solve(P, t(np.full(n, 2.0)), t(b), 1e-10, 10)
     torch.cuda.synchronize()
     assert infos[0].iterations == 1 and infos[0].converged
-    assert np.array_equal(x.cpu().numpy(), 0.5 * b)
+    xh = x.cpu().numpy()
+    assert np.all(np.abs(xh - 0.5 * b) <= 2.0 ** -51 * np.abs(0.5 * b))
     # b = 0: converged before the first iteration, x = 0
     rp, c, v = W.convection_diffusion_csr(12)
     P = csr_handle(rp, c)
