@@ -291,6 +291,15 @@ __device__ __forceinline__ double sum_partials_all(const SLA_GLOBAL double* __re
   return block_sum_all<NT>(v, red);
 }
 
+// The same sum into an LDS area of its own (see block_sum_once).
+template <int NT = kIterBlock>
+__device__ __forceinline__ double sum_partials_once(const SLA_GLOBAL double* __restrict__ part,
+                                                    int count, double* red) {
+  double v = 0.0;
+  for (int i = threadIdx.x; i < count; i += NT) v = v + part[i];
+  return block_sum_once<NT>(v, red);
+}
+
 // ---------------------------------------------------------------------------
 // Standalone SpMV: y[s] = A_s x[s]
 // ---------------------------------------------------------------------------
@@ -513,6 +522,8 @@ __device__ __forceinline__ StepIn step_in(const Ctx* __restrict__ c, int64_t s) 
   return in;
 }
 
+// `red`: two LDS areas of NT / 64 doubles that the launch uses for no
+// other sum.
 template <int NT = kIterBlock>
 __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t s,
                                               const StepIn& in, double* red) {
@@ -526,10 +537,11 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
   const SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
   StepHead h;
   h.k = k;
-  const double rr = sum_partials_all<NT>(part + (k & 1) * G, G, red);
+  const double rr = sum_partials_once<NT>(part + (k & 1) * G, G, red);
   // Jacobi: beta from r.z, the stopping test still on r.r
   const bool jac = in.jacobi != 0;
-  const double rz = jac ? sum_partials_all<NT>(part + (5 + (k & 1)) * G, G, red) : 0.0;
+  const double rz =
+      jac ? sum_partials_once<NT>(part + (5 + (k & 1)) * G, G, red + NT / kWave) : 0.0;
   h.lag = k > 0;
   h.alpha = 0.0;
   h.beta = 0.0;
@@ -576,7 +588,7 @@ template <typename RP, int NB>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_spmv(const Ctx* __restrict__ c) {
   extern __shared__ double lds_dyn[];
-  __shared__ double red[kWaves];
+  __shared__ double red[3 * kWaves];  // step head (2 areas), the p.Ap partial
   const int64_t s = blockIdx.y;
   // context fields first: read before the kernel's first store, they come
   // in through scalar loads
@@ -668,7 +680,7 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
     pq = own ? pq1 : pq;
     t = tn;
   }
-  pq = block_sum_all<kIterBlock>(pq, red);
+  pq = block_sum_once<kIterBlock>(pq, red + 2 * kWaves);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
@@ -702,7 +714,7 @@ __global__ __launch_bounds__(kLineWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(kLineWavesPerEu)))
 void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   constexpr int NT = kLineWaves * kWave;
-  __shared__ double red[kLineWaves];
+  __shared__ double red[3 * kLineWaves];  // step head (2 areas), the p.Ap partial
   const int64_t s = blockIdx.y;
   // context fields first (scalar loads, see k_cg_spmv)
   const int64_t n = c->n, nnz = c->nnz, tiles = c->tiles, L = c->line;
@@ -1099,7 +1111,7 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
     // the next unit's first loads
     if (unit + per_xcd < units) pre = issue(unit_at(unit + per_xcd));
   }
-  pq = block_sum_all<NT>(pq, red);
+  pq = block_sum_once<NT>(pq, red + 2 * kLineWaves);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
@@ -1113,7 +1125,7 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
 // recorded and writes no scalar.
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_direction(const Ctx* __restrict__ c) {
-  __shared__ double red[kWaves];
+  __shared__ double red[2 * kWaves];  // step head
   const int64_t s = blockIdx.y;
   // context fields first (scalar loads, see k_cg_spmv)
   const int64_t n = c->n, tiles = c->tiles;
@@ -1209,7 +1221,7 @@ void k_cg_product(const Ctx* __restrict__ c) {
     const double pq1 = pq + po * acc;
     pq = own ? pq1 : pq;
   }
-  pq = block_sum_all<kIterBlock>(pq, red);
+  pq = block_sum_once<kIterBlock>(pq, red);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
@@ -1252,6 +1264,36 @@ __device__ __forceinline__ void block_sum2(double& u, double& v, double* lds) {
   v = b;
 }
 
+// The same sums without the closing barrier, for a loop that alternates two
+// `lds` areas: the next use of an area comes after another sum's barrier, by
+// which every thread has read it.  sum1 is the one-value form.
+__device__ __forceinline__ void block_sum2_open(double& u, double& v, double* lds) {
+  u = wave_sum(u);
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds[threadIdx.x / kWave] = u;
+    lds[kWaves + threadIdx.x / kWave] = v;
+  }
+  __syncthreads();
+  double a = 0.0, b = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    a = a + lds[w];
+    b = b + lds[kWaves + w];
+  }
+  u = a;
+  v = b;
+}
+__device__ __forceinline__ double block_sum1_open(double u, double* lds) {
+  u = wave_sum(u);
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = u;
+  __syncthreads();
+  double a = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) a = a + lds[w];
+  return a;
+}
+
 // LDS of the small-system kernel: p [n rounded up to the workgroup] and one
 // product area of kWaveCap doubles per wave.
 size_t one_group_lds_bytes(int64_t n) {
@@ -1265,6 +1307,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
                                                             int use_x0) {
   extern __shared__ double lds_dyn[];
   __shared__ double red[2 * kWaves];
+  __shared__ double red_a[kWaves], red_b[2 * kWaves];  // the loop's two areas
   const int64_t s = blockIdx.x;
   const int64_t n = c->n, nnz = c->nnz;
   const int64_t npad = (n + kIterBlock - 1) / kIterBlock * kIterBlock;
@@ -1319,8 +1362,17 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
           if (k < rlen[j]) prod[k] = hv[j][m] * pl[hc[j][m]];
         }
         wave_sync();
+        // slot order, four LDS reads in flight at a time
         double acc = 0.0;
-        for (int k = ra[j]; k < re[j]; ++k) acc = acc + prod[k];
+        int k = ra[j];
+        for (; k + 4 <= re[j]; k += 4) {
+          const double p0 = prod[k], p1 = prod[k + 1], p2 = prod[k + 2], p3 = prod[k + 3];
+          acc = acc + p0;
+          acc = acc + p1;
+          acc = acc + p2;
+          acc = acc + p3;
+        }
+        for (; k < re[j]; ++k) acc = acc + prod[k];
         q[j] = acc;
         wave_sync();  // the area is reused by the next tile
       }
@@ -1397,12 +1449,13 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
     }
     __syncthreads();
     spmv(q);
-    double pq = 0.0, zero = 0.0;
+    double pq = 0.0;
 #pragma unroll
     for (int j = 0; j < R; ++j)
       if (t + int64_t(j) * kIterBlock < n) pq = pq + pv[j] * q[j];
-    // (the barriers of the sum also end every wave's gathers of p_k)
-    block_sum2(pq, zero, red);
+    // (the barrier of the sum also ends every wave's gathers of p_k; red_a
+    // was last read before the previous iteration's second sum)
+    pq = block_sum1_open(pq, red_a);
     if (!isfinite(pq) || !(pq > 0.0)) {
       state = !isfinite(pq) ? ST_NONFINITE : ST_NOT_SPD;
       it = k;
@@ -1420,7 +1473,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
         if constexpr (JAC) rzn = rzn + r[j] * (r[j] / dv[j]);
       }
     }
-    block_sum2(rn, rzn, red);
+    // (red_b was last read before this iteration's first sum)
+    block_sum2_open(rn, rzn, red_b);
     rr_prev = rr;
     rz_prev = rz;
     rr = rn;
@@ -1448,7 +1502,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
 template <bool JAC>
 __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 void k_cg_residual(const Ctx* __restrict__ c) {
-  __shared__ double red[kWaves];
+  __shared__ double red[3 * kWaves];  // p.Ap sum, r.r and r.z partials
   const int64_t s = blockIdx.y;
   // context fields first (scalar loads, see k_cg_spmv)
   const int64_t n = c->n, tiles = c->tiles;
@@ -1507,7 +1561,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
     if (lead) sc->state_r = st_in;
     return;
   }
-  const double pq = sum_partials_all(part + (2 + (k & 1)) * G, G, red);
+  const double pq = sum_partials_once(part + (2 + (k & 1)) * G, G, red);
   int32_t stop = ST_RUNNING;
   if (!isfinite(pq)) stop = ST_NONFINITE;
   else if (!(pq > 0.0)) stop = ST_NOT_SPD;
@@ -1557,8 +1611,8 @@ void k_cg_residual(const Ctx* __restrict__ c) {
       }
     }
   }
-  rn = block_sum_all<kIterBlock>(rn, red);
-  if constexpr (JAC) rzn = block_sum_all<kIterBlock>(rzn, red);
+  rn = block_sum_once<kIterBlock>(rn, red + kWaves);
+  if constexpr (JAC) rzn = block_sum_once<kIterBlock>(rzn, red + 2 * kWaves);
   if (threadIdx.x == 0) {
     part[((k + 1) & 1) * G + blockIdx.x] = rn;
     if constexpr (JAC) part[(5 + ((k + 1) & 1)) * G + blockIdx.x] = rzn;
@@ -1997,7 +2051,7 @@ static int one_group_rows(const sla_csr A) {
   int lim = 0;
   if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, A->device) !=
           hipSuccess ||
-      one_group_lds_bytes(A->n) + 2 * kWaves * sizeof(double) > size_t(lim))
+      one_group_lds_bytes(A->n) + 5 * kWaves * sizeof(double) > size_t(lim))  // + red*
     return 0;
   return A->n <= kIterBlock ? 1 : 2;
 }

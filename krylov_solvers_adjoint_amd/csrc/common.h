@@ -311,6 +311,19 @@ __device__ __forceinline__ double block_sum_all(double v, double* lds) {
   return t;
 }
 
+// The same sum without the closing barrier, for an `lds` area that the
+// launch uses for no other sum (the barrier only protects an area's reuse).
+template <int NT>
+__device__ __forceinline__ double block_sum_once(double v, double* lds) {
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) t = t + lds[w];
+  return t;
+}
+
 // Make a wave's LDS writes visible to its other lanes (a wave tile is owned
 // by one wave, so no workgroup barrier is needed).
 __device__ __forceinline__ void wave_sync() {
