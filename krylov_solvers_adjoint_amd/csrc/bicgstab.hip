@@ -105,12 +105,26 @@ __device__ __forceinline__ void put_partial(double* part, double v, double* red)
   if (threadIdx.x == 0) part[blockIdx.x] = v;
 }
 
+// One-shot forms for an LDS area that the launch uses for no other sum: no
+// closing barrier (see block_sum_once).
+__device__ __forceinline__ double sum_set_once(const double* part, int64_t G, double* red) {
+  double a = 0.0;
+  for (int64_t g = threadIdx.x; g < G; g += kBsBlock) a = a + part[g];
+  return block_sum_once<kBsBlock>(a, red);
+}
+
+__device__ __forceinline__ void put_partial_once(double* part, double v, double* red) {
+  v = block_sum_once<kBsBlock>(v, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = v;
+}
+
 constexpr int kBsWaves = kBsBlock / kWave;
 
 // K sets of G partials summed in one pass: the same order as K calls of
 // sum_set (each thread's strided terms, a wave butterfly, the waves in
 // order).  Thread k adds set k's wave sums and broadcasts the total through
-// LDS.  red holds K * (kBsWaves + 1) doubles.
+// LDS.  red holds K * (kBsWaves + 1) doubles, an area that the launch uses
+// for no other sum (there is no closing barrier).
 template <int K>
 __device__ __forceinline__ void sum_sets(const double* const (&p)[K], int64_t G, double* red,
                                          double (&out)[K]) {
@@ -137,7 +151,6 @@ __device__ __forceinline__ void sum_sets(const double* const (&p)[K], int64_t G,
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < K; ++k) out[k] = red[K * kBsWaves + k];
-  __syncthreads();
 }
 
 // K per-workgroup partials written in one pass (same order as put_partial).
@@ -263,14 +276,14 @@ __global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWaves
 
 // alpha = rho / rhat.v; s = r - alpha v and the s.s partials.
 __global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) void k_bs_s(BsArgs a) {
-  __shared__ double red[kBsBlock / kWave];
+  __shared__ double red[2 * kBsWaves];  // the rhat.v sum, the s.s partial
   const int64_t sys = blockIdx.y, n = a.n, o = sys * n;
   BsScal* sc = a.scal + sys;
   int64_t j;
   if (skip(sc, PH_S, &j)) return;
   const int64_t pos = 8 * j + PH_S;
   const double* part = a.part + sys * kBsSets * a.G;
-  const double rv = sum_set(part + P_RV * a.G, a.G, red);
+  const double rv = sum_set_once(part + P_RV * a.G, a.G, red);
   int32_t st = ST_RUNNING;
   if (!isfinite(rv)) st = ST_NONFINITE;
   else if (rv == 0.0) st = ST_BREAKDOWN;
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWaves
     a.s[o + i] = si;
     ss = ss + si * si;
   }
-  put_partial(a.part + (sys * kBsSets + P_SS) * a.G, ss, red);
+  put_partial_once(a.part + (sys * kBsSets + P_SS) * a.G, ss, red + kBsWaves);
 }
 
 // After t = A s: the half-step finish (s.s <= tol^2 b.b: x += alpha p), else
@@ -308,7 +321,7 @@ __global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWaves
   if (skip(sc, PH_UPD, &j)) return;
   const int64_t pos = 8 * j + PH_UPD;
   const double* part = a.part + sys * kBsSets * a.G;
-  __shared__ double red3[3 * (kBsWaves + 1)];
+  __shared__ double red3[3 * (kBsWaves + 1)], redp[2 * kBsWaves];
   double sums[3];
   sum_sets<3>({part + P_SS * a.G, part + P_TT * a.G, part + P_TS * a.G}, a.G, red3, sums);
   const double ss = sums[0];
@@ -354,7 +367,7 @@ __global__ __launch_bounds__(kBsBlock) __attribute__((amdgpu_waves_per_eu(kWaves
     rr = rr + ri * ri;
   }
   double* wpart = a.part + sys * kBsSets * a.G;
-  put_partials<2>({wpart + P_RHR * a.G, wpart + P_RR * a.G}, {rhr, rr}, red3);
+  put_partials<2>({wpart + P_RHR * a.G, wpart + P_RR * a.G}, {rhr, rr}, redp);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     sc->it = j + 1;
     double* h = hist_of(a, sys);
