@@ -787,8 +787,8 @@ def main():
                          "size, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the solver path "
-              "is single-GPU; multi-GPU sharding is not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the solvers run "
+              "on one GPU; sharding a system across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
     global CSR_ONLY
     CSR_ONLY = args.csr_only
