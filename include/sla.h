@@ -425,7 +425,8 @@ sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
 /* Solver workgroups per compute unit (1024 threads each; 512 in the line
  * walk): 0 (default: automatic: 1 for solves of at most 2^21 unknowns over
  * the batch, where the kernels' fixed costs dominate, and for line-walk
- * patterns (2D stencils), whose waves then walk longer chunks; else 2), 1
+ * patterns (2D stencils), whose waves then walk longer chunks, and on
+ * reordered handles (sla_csr_reorder), whose gathers hit the L2; else 2), 1
  * (fewer DRAM pages open at once) or 2 (twice the waves to hide latency).
  * The grid sets the number and
  * order of the dot-product partial sums, so CG results differ in the last
