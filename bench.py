@@ -61,6 +61,14 @@ def spmv_step_bytes_banded(n: int, nnz: int, rp_bytes: int) -> int:
     return 8 * nnz + n + rp_bytes * (tiles + 1) + 48 * n
 
 
+def spmv_step_bytes_lines(n: int, nnz: int, rp_bytes: int) -> int:
+    """The same launch with the line walk, averaged over two steps: x and the
+    previous-but-one direction are read, and x written, at every other step
+    only (read 32 n / 16 n, write 24 n / 16 n of vectors)."""
+    tiles = (n + 63) // 64
+    return 8 * nnz + n + rp_bytes * (tiles + 1) + 44 * n
+
+
 def spmv_step_bytes_split(n: int, nnz: int, rp_bytes: int) -> int:
     """The SpMV step as two launches for wide-column patterns: the direction
     pass reads r, p_{k-1}, x and writes p_k, x (40 n); the product pass reads
@@ -82,10 +90,12 @@ STEP_KERNEL = {"lines": "k_cg_spmv_lines", "banded": "k_cg_spmv", "csr": "k_cg_s
 
 
 def spmv_bytes_for(variant: str, n: int, nnz: int, rp_bytes: int) -> int:
-    """Algorithmic bytes of one SpMV step under `variant` (the line walk
-    moves the same arrays as the banded kernel: values, mask bytes, one row
-    pointer per tile, r, p_{k-1}, x read once, p_k, q, x written once)."""
-    if variant in ("lines", "banded"):
+    """Algorithmic bytes of one SpMV step under `variant` (the line walk:
+    the banded kernel's arrays, with x's updates applied two steps at a time,
+    as the mean over two steps)."""
+    if variant == "lines":
+        return spmv_step_bytes_lines(n, nnz, rp_bytes)
+    if variant == "banded":
         return spmv_step_bytes_banded(n, nnz, rp_bytes)
     if variant == "split":
         return spmv_step_bytes_split(n, nnz, rp_bytes)

@@ -42,6 +42,7 @@
 //     polls the count of running systems between blocks.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 #include <vector>
 
 #include "handle.h"
@@ -459,7 +460,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
     sc->rr[1] = rr;
     sc->rz[0] = rz;
     sc->rz[1] = rz;
-    sc->alpha = 0.0;
+    sc->alpha[0] = 0.0;
+    sc->alpha[1] = 0.0;
     sc->bb = bb;
     sc->stop = (tol * tol) * bb;
     sc->rr_final = rr;
@@ -484,7 +486,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_init_scalars(const Ctx* __res
 // the system stops, its final state.
 struct StepHead {
   int64_t k;
-  double alpha, beta;
+  double alpha, beta;  // alpha_{k-1}, beta_k
+  double alpha2;       // alpha_{k-2} (k >= 2)
   bool lag;      // x still lacks alpha_{k-1} p_{k-1}
   int32_t stop;  // ST_RUNNING or the final state
 };
@@ -499,7 +502,7 @@ struct StepIn {
   int64_t k;      // index of this SpMV step (ka)
   int32_t state;  // state_r
   int32_t jacobi, grid;
-  double rr0, rr1, rz0, rz1, alpha, stop;
+  double rr0, rr1, rz0, rz1, alpha0, alpha1, stop;
   int64_t maxit;
 };
 
@@ -514,11 +517,12 @@ __device__ __forceinline__ StepIn step_in(const Ctx* __restrict__ c, int64_t s) 
   in.rr1 = scg->rr[1];
   in.rz0 = scg->rz[0];
   in.rz1 = scg->rz[1];
-  in.alpha = scg->alpha;
+  in.alpha0 = scg->alpha[0];
+  in.alpha1 = scg->alpha[1];
   in.stop = scg->stop;
   in.maxit = scg->maxit;
-  pin(in.k, in.state, in.jacobi, in.grid, in.rr0, in.rr1, in.rz0, in.rz1, in.alpha, in.stop,
-      in.maxit);
+  pin(in.k, in.state, in.jacobi, in.grid, in.rr0, in.rr1, in.rz0, in.rz1, in.alpha0, in.alpha1,
+      in.stop, in.maxit);
   return in;
 }
 
@@ -530,7 +534,9 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
   Scal* sc = scal_of(c, s);
   const int64_t k = in.k;
   const double rr_prev = (k & 1) ? in.rr0 : in.rr1, rz_prev = (k & 1) ? in.rz0 : in.rz1;
-  const double alpha_in = in.alpha, stop_at = in.stop;
+  // alpha_{k-1} and alpha_{k-2}, by parity
+  const double alpha_in = (k & 1) ? in.alpha0 : in.alpha1, stop_at = in.stop;
+  const double alpha2_in = (k & 1) ? in.alpha1 : in.alpha0;
   const int64_t maxit = in.maxit;
   const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
   const int G = in.grid;
@@ -544,6 +550,7 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
       jac ? sum_partials_once<NT>(part + (5 + (k & 1)) * G, G, red + NT / kWave) : 0.0;
   h.lag = k > 0;
   h.alpha = 0.0;
+  h.alpha2 = k >= 2 ? alpha2_in : 0.0;
   h.beta = 0.0;
   h.stop = ST_RUNNING;
   int64_t it_stop = k;
@@ -804,8 +811,10 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   struct Pre {
     double rb, pb, rc, pc, rn, pn;
     TileIndex<RP> ix0, ix1;
-    double rl, pl, rr, pr, x0;
+    double rl, pl, rr, pr, x0, q0;
   };
+  // this step's x update (see below): known before the step's scalars
+  const bool xs = k >= 2 && (k & 1) == 0;
   auto issue = [&](const Unit& ug) -> Pre {
     Pre e{};
     const int64_t first = ug.v0 * L + ug.col0;
@@ -828,7 +837,12 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
       e.ix0 = tile_index<NB, RP>(rowptr, mask, n, first, l0);
     }
     if constexpr (NEAR1) edges(first, len0, e.rl, e.pl, e.rr, e.pr);
-    if constexpr (PIPE) e.x0 = ld(x + first, l0);
+    if constexpr (PIPE) {
+      if (xs) {
+        e.x0 = ld(x + first, l0);
+        e.q0 = ld(pnew + first, l0);  // p_{k-2}, before p_k replaces it
+      }
+    }
     return e;
   };
   Pre pre = issue(unit_at(slot));
@@ -836,281 +850,305 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   const double alpha = uniform(h.alpha), beta = uniform(h.beta);
   const bool lag = h.lag;
   if (h.stop != ST_RUNNING) {
-    // last pass: only the deferred x update
+    // last pass: only the pending x updates (two after an odd step: p_{k-2}
+    // is still in the buffer this step would have overwritten)
     if (lag) {
+      const bool two = (k & 1) == 0;
+      const double alpha2 = uniform(h.alpha2);
       const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kLineWaves, w);
       for (int64_t t = wk.first; t < wk.end; t += wk.stride) {
         const int64_t i0 = t * kTileRows;
-        if (i0 + lane < n) st(x + i0, lane, ld(x + i0, lane) + alpha * ld(pold + i0, lane));
+        if (i0 + lane < n) {
+          double xi = ld(x + i0, lane);
+          if (two) xi = xi + alpha2 * ld(pnew + i0, lane);
+          st(x + i0, lane, xi + alpha * ld(pold + i0, lane));
+        }
       }
     }
     return;
   }
+  // this step's x update: alpha_{k-2} p_{k-2} (read from the buffer before
+  // p_k replaces it) and alpha_{k-1} p_{k-1} at even k >= 2, none at odd k;
+  // the walk is compiled with and without it (a store behind a branch would
+  // make the compiler wait for older stores)
+  const double alpha2 = uniform(h.alpha2);
   // offsets: off[0] = -L and off[count-1] = +L (from registers), 0 (the row
   // itself), the others within +-63 (gathered)
   const Gather<true, false> g{r, pold, beta};
   double pq = 0.0;
-  for (int64_t unit = slot; unit < units; unit += per_xcd) {
-    const Unit ug = unit_at(unit);
-    if (ug.ok) {
-      const int64_t v0 = ug.v0, v1 = ug.v1, col0 = ug.col0, lenu = ug.lenu;
-      wait_vmem();
-      // -L neighbours of the first tile
-      double pprev = v0 >= 1 ? pre.rb + beta * pre.pb : 0.0;
-      if constexpr (PIPE) {
-        // the tile's values at the slot positions of the lane's row (see
-        // band_row): issued from index data loaded a step earlier
-        auto load_values = [&](const TileIndex<RP>& ixv, const TileRef& tr, double (&a)[NB],
-                               unsigned& m) {
-          const int64_t s0 = uniform(int64_t(ixv.s0));
-          m = ixv.m;
-          const bool ownv = int64_t(lane) < tr.len;
-          const int kx = wave_exclusive_sum(ownv ? __builtin_popcount(m) : 0);
-          uint32_t kk = uint32_t(__shfl(kx, int(tr.lr), kWave));
-          const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
-  #pragma unroll
-          for (int t = 0; t < NB; ++t) {
-            const bool use = t < band.count && ((m >> t) & 1u);
-            a[t] = ld(vb_, use ? kk : 0u);
-            kk += use ? 1u : 0u;
-          }
-        };
-        // nothing past the chunk is loaded but the +L neighbours of its last
-        // tile: later tiles' loads repeat the tile before (cache hits)
-        auto pick = [&](bool c, const TileRef& a_, const TileRef& b_) -> TileRef {
-          return TileRef{c ? a_.r0 : b_.r0, c ? a_.len : b_.len, c ? a_.lr : b_.lr,
-                         c ? a_.has : b_.has};
-        };
-        // The walk is a pipeline two tiles deep: step v computes tile v from
-        // data issued in the steps before, and issues r, p_{k-1} and the index
-        // data of tile v + 2, and the values, x and edge rows of tile v + 1.
-        TileRef tc{v0 * L + col0, tile_len(ug, v0), 0u, true};
-        tc.lr = clamp_lane(tc.len);
-        TileRef t1 = tile_ref(ug, v0 + 1, tc);
-        double rc = pre.rc, pc = pre.pc, rn = pre.rn, pn = pre.pn;
-        TileIndex<RP> ixc = pre.ix0, ix1 = pre.ix1;
-        double rl = pre.rl, pl = pre.pl, rr = pre.rr, pr = pre.pr;
-        double a[NB];
-        unsigned m = 0;
-        load_values(ixc, tc, a, m);
-        double xo = pre.x0;
-        for (int64_t v = v0; v < v1; ++v) {
-          const int64_t r0 = tc.r0;
-          const uint32_t lr = tc.lr;
-          const int64_t len = tc.len;
-          const bool own = int64_t(lane) < len;
-          // tile v + 2: r, p_{k-1} and index data (the +L neighbours of tile
-          // v + 1, read in the next step; needed up to tile v1)
-          const TileRef t2 = pick(v + 2 <= v1, tile_ref(ug, v + 2, t1), t1);
-          const double rn2 = ld(r + t2.r0, t2.lr), pn2 = ld(pold + t2.r0, t2.lr);
-          const TileIndex<RP> ix2 = tile_index<NB, RP>(rowptr, mask, n, t2.r0, t2.lr);
-          // tile v + 1: x and edge rows, then its values (inside the chunk only)
-          const bool in1 = v + 1 < v1;
-          const TileRef tv = pick(in1, t1, tc);
-          const double xn = ld(x + tv.r0, tv.lr);
-          double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
-          if constexpr (NEAR1) edges(tv.r0, tv.len, rln, pln, rrn, prn);
-          double an[NB];
-          unsigned mn = 0;
-          TileIndex<RP> ixv = ixc;
-          ixv.s0 = in1 ? ix1.s0 : ixc.s0;
-          ixv.m = in1 ? ix1.m : ixc.m;
-          load_values(ixv, tv, an, mn);
-          // near offsets of tile v, gathered; the other kinds read the row
-          // itself (no branch; the value is not used)
-          const int64_t lo = r0 - kTileRows;
-          const int64_t base = lo > 0 ? lo : 0;
-          const int32_t d = int32_t(r0 - base) + int32_t(lr);
-          const int32_t top = int32_t(n - 1 - base);
-          // offsets are sorted: -L first, +L last, the near ones in between
-          double gu[NB], gw[NB];
-          if constexpr (!NEAR1) {
+  auto walk = [&](auto xs_tag) {
+    constexpr bool XS = decltype(xs_tag)::value;
+    for (int64_t unit = slot; unit < units; unit += per_xcd) {
+      const Unit ug = unit_at(unit);
+      if (ug.ok) {
+        const int64_t v0 = ug.v0, v1 = ug.v1, col0 = ug.col0, lenu = ug.lenu;
+        wait_vmem();
+        // -L neighbours of the first tile
+        double pprev = v0 >= 1 ? pre.rb + beta * pre.pb : 0.0;
+        if constexpr (PIPE) {
+          // the tile's values at the slot positions of the lane's row (see
+          // band_row): issued from index data loaded a step earlier
+          auto load_values = [&](const TileIndex<RP>& ixv, const TileRef& tr, double (&a)[NB],
+                                 unsigned& m) {
+            const int64_t s0 = uniform(int64_t(ixv.s0));
+            m = ixv.m;
+            const bool ownv = int64_t(lane) < tr.len;
+            const int kx = wave_exclusive_sum(ownv ? __builtin_popcount(m) : 0);
+            uint32_t kk = uint32_t(__shfl(kx, int(tr.lr), kWave));
+            const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
     #pragma unroll
-            for (int t = 1; t < NB - 1; ++t) {
-              const int32_t o = t < band.count - 1 ? band.off[t] : 0;
-              int32_t j = d + o;
-              j = j < 0 ? 0 : (j > top ? top : j);
-              g.load_at(base, uint32_t(j), gu[t], gw[t]);
+            for (int t = 0; t < NB; ++t) {
+              const bool use = t < band.count && ((m >> t) & 1u);
+              a[t] = ld(vb_, use ? kk : 0u);
+              kk += use ? 1u : 0u;
             }
-          }
-          // p_k at the row, below (-L) and above (+L)
-          const double pcur = rc + beta * pc;
-          const double pnext = rn + beta * pn;
-          // lanes past the end of a short tile compute its last row: take that
-          // row's -L value (the previous tile was loaded lane for lane)
-          const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
-          // NEAR1: p_k at the rows before and after, from the neighbouring lanes
-          // or, at the ends of the tile, from the rows just outside it
-          double pm1 = 0.0, pp1 = 0.0;
-          if constexpr (NEAR1) {
-            const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
-            const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
-            pm1 = lr == 0 ? rl + beta * pl : sm;
-            pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
-          }
-          double acc = 0.0;
-    #pragma unroll
-          for (int t = 0; t < NB; ++t) {
-            const int32_t o = t < band.count ? band.off[t] : 0;
-            const bool use = t < band.count && ((m >> t) & 1u);
-            double gv;
-            if (t == 0) gv = pbelow;
-            else if (t == NB - 1) gv = pnext;
-            else if (t == band.count - 1) gv = pnext;
-            else if (o == 0) gv = pcur;
-            else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
-            else gv = g.value(gu[t], gw[t]);
-            const double sum = acc + a[t] * gv;
-            acc = use ? sum : acc;
-          }
-          // lanes past the last row store the same bits as the row's own lane;
-          // x is stored back unchanged when there is no lagged update (no branch
-          // around a store: it would make the compiler wait for older stores)
-          st(x + r0, lr, lag ? xo + alpha * pc : xo);
-          st(pnew + r0, lr, pcur);
-          st(q + r0, lr, acc);
-          const double pq1 = pq + pcur * acc;
-          pq = own ? pq1 : pq;
-          // shift the walk down one line
-          if (!t1.has) break;
-          pprev = pcur;
-          rc = rn;
-          pc = pn;
-          rn = rn2;
-          pn = pn2;
-    #pragma unroll
-          for (int t = 0; t < NB; ++t) a[t] = an[t];
-          m = mn;
-          xo = xn;
-          if constexpr (NEAR1) {
-            rl = rln;
-            pl = pln;
-            rr = rrn;
-            pr = prn;
-          }
-          ixc = ix1;
-          ix1 = ix2;
-          tc = t1;
-          t1 = t2;
-        }
-      } else {
-        // the walk with one tile of look-ahead (r, p_{k-1} and index data of
-        // the next tile); shorter chunks run faster this way
-        int64_t len = tile_len(ug, v0);
-        uint32_t lr = clamp_lane(len);
-        double rc = pre.rc, pc = pre.pc;
-        TileIndex<RP> ix = pre.ix0;
-        // the current tile's edge rows live in scalar registers (the same value
-        // in every lane); the next tile's arrive in vector registers
-        double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
-        if constexpr (NEAR1) {
-          rl = uniform(pre.rl);
-          pl = uniform(pre.pl);
-          rr = uniform(pre.rr);
-          pr = uniform(pre.pr);
-        }
-        for (int64_t v = v0; v < v1; ++v) {
-          const int64_t r0 = v * L + col0;
-          const bool own = int64_t(lane) < len;
-          // the next tile: +L neighbours now, own operands in the next step
-          const int64_t lenn = v + 1 < V ? tile_len(ug, v + 1) : 0;
-          const bool hasn = lenn > 0;
-          const int64_t rn0 = hasn ? r0 + L : r0;
-          const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
-          const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
-          double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
-          if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
-          const TileIndex<RP> cur = ix;
-          // unconditional (the current tile again when there is no next one): a
-          // conditional load would make the compiler copy the old value into its
-          // register first, which waits for older loads and stores
-          ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
-          const double xo = ld(x + r0, lr);
-          // near offsets, gathered; the other kinds read the row itself (no
-          // branch; the value is not used)
-          const int64_t lo = r0 - kTileRows;
-          const int64_t base = lo > 0 ? lo : 0;
-          const int32_t d = int32_t(r0 - base) + int32_t(lr);
-          const int32_t top = int32_t(n - 1 - base);
-          // offsets are sorted: -L first, +L last, the near ones in between
-          double gu[NB], gw[NB];
-          if constexpr (!NEAR1) {
-    #pragma unroll
-            for (int t = 1; t < NB - 1; ++t) {
-              const int32_t o = t < band.count - 1 ? band.off[t] : 0;
-              int32_t j = d + o;
-              j = j < 0 ? 0 : (j > top ? top : j);
-              g.load_at(base, uint32_t(j), gu[t], gw[t]);
-            }
-          }
-          // values at the slot positions of the row (see band_row)
-          const int64_t s0 = uniform(int64_t(cur.s0));
-          const unsigned m = cur.m;
-          const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
-          uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
-          const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+          };
+          // nothing past the chunk is loaded but the +L neighbours of its last
+          // tile: later tiles' loads repeat the tile before (cache hits)
+          auto pick = [&](bool c, const TileRef& a_, const TileRef& b_) -> TileRef {
+            return TileRef{c ? a_.r0 : b_.r0, c ? a_.len : b_.len, c ? a_.lr : b_.lr,
+                           c ? a_.has : b_.has};
+          };
+          // The walk is a pipeline two tiles deep: step v computes tile v from
+          // data issued in the steps before, and issues r, p_{k-1} and the index
+          // data of tile v + 2, and the values, x and edge rows of tile v + 1.
+          TileRef tc{v0 * L + col0, tile_len(ug, v0), 0u, true};
+          tc.lr = clamp_lane(tc.len);
+          TileRef t1 = tile_ref(ug, v0 + 1, tc);
+          double rc = pre.rc, pc = pre.pc, rn = pre.rn, pn = pre.pn;
+          TileIndex<RP> ixc = pre.ix0, ix1 = pre.ix1;
+          double rl = pre.rl, pl = pre.pl, rr = pre.rr, pr = pre.pr;
           double a[NB];
-    #pragma unroll
-          for (int t = 0; t < NB; ++t) {
-            const bool use = t < band.count && ((m >> t) & 1u);
-            a[t] = ld(vb_, use ? kk : 0u);
-            kk += use ? 1u : 0u;
+          unsigned m = 0;
+          load_values(ixc, tc, a, m);
+          double xo = pre.x0, xq = pre.q0;
+          for (int64_t v = v0; v < v1; ++v) {
+            const int64_t r0 = tc.r0;
+            const uint32_t lr = tc.lr;
+            const int64_t len = tc.len;
+            const bool own = int64_t(lane) < len;
+            // tile v + 2: r, p_{k-1} and index data (the +L neighbours of tile
+            // v + 1, read in the next step; needed up to tile v1)
+            const TileRef t2 = pick(v + 2 <= v1, tile_ref(ug, v + 2, t1), t1);
+            const double rn2 = ld(r + t2.r0, t2.lr), pn2 = ld(pold + t2.r0, t2.lr);
+            const TileIndex<RP> ix2 = tile_index<NB, RP>(rowptr, mask, n, t2.r0, t2.lr);
+            // tile v + 1: x and edge rows, then its values (inside the chunk only)
+            const bool in1 = v + 1 < v1;
+            const TileRef tv = pick(in1, t1, tc);
+            double xn = 0.0, qn = 0.0;
+            if constexpr (XS) {
+              xn = ld(x + tv.r0, tv.lr);
+              qn = ld(pnew + tv.r0, tv.lr);  // p_{k-2}, before p_k replaces it
+            }
+            double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+            if constexpr (NEAR1) edges(tv.r0, tv.len, rln, pln, rrn, prn);
+            double an[NB];
+            unsigned mn = 0;
+            TileIndex<RP> ixv = ixc;
+            ixv.s0 = in1 ? ix1.s0 : ixc.s0;
+            ixv.m = in1 ? ix1.m : ixc.m;
+            load_values(ixv, tv, an, mn);
+            // near offsets of tile v, gathered; the other kinds read the row
+            // itself (no branch; the value is not used)
+            const int64_t lo = r0 - kTileRows;
+            const int64_t base = lo > 0 ? lo : 0;
+            const int32_t d = int32_t(r0 - base) + int32_t(lr);
+            const int32_t top = int32_t(n - 1 - base);
+            // offsets are sorted: -L first, +L last, the near ones in between
+            double gu[NB], gw[NB];
+            if constexpr (!NEAR1) {
+      #pragma unroll
+              for (int t = 1; t < NB - 1; ++t) {
+                const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+                int32_t j = d + o;
+                j = j < 0 ? 0 : (j > top ? top : j);
+                g.load_at(base, uint32_t(j), gu[t], gw[t]);
+              }
+            }
+            // p_k at the row, below (-L) and above (+L)
+            const double pcur = rc + beta * pc;
+            const double pnext = rn + beta * pn;
+            // lanes past the end of a short tile compute its last row: take that
+            // row's -L value (the previous tile was loaded lane for lane)
+            const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+            // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+            // or, at the ends of the tile, from the rows just outside it
+            double pm1 = 0.0, pp1 = 0.0;
+            if constexpr (NEAR1) {
+              const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+              const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+              pm1 = lr == 0 ? rl + beta * pl : sm;
+              pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+            }
+            double acc = 0.0;
+      #pragma unroll
+            for (int t = 0; t < NB; ++t) {
+              const int32_t o = t < band.count ? band.off[t] : 0;
+              const bool use = t < band.count && ((m >> t) & 1u);
+              double gv;
+              if (t == 0) gv = pbelow;
+              else if (t == NB - 1) gv = pnext;
+              else if (t == band.count - 1) gv = pnext;
+              else if (o == 0) gv = pcur;
+              else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+              else gv = g.value(gu[t], gw[t]);
+              const double sum = acc + a[t] * gv;
+              acc = use ? sum : acc;
+            }
+            // lanes past the last row store the same bits as the row's own lane
+            if constexpr (XS) st(x + r0, lr, (xo + alpha2 * xq) + alpha * pc);
+            st(pnew + r0, lr, pcur);
+            st(q + r0, lr, acc);
+            const double pq1 = pq + pcur * acc;
+            pq = own ? pq1 : pq;
+            // shift the walk down one line
+            if (!t1.has) break;
+            pprev = pcur;
+            rc = rn;
+            pc = pn;
+            rn = rn2;
+            pn = pn2;
+      #pragma unroll
+            for (int t = 0; t < NB; ++t) a[t] = an[t];
+            m = mn;
+            xo = xn;
+            xq = qn;
+            if constexpr (NEAR1) {
+              rl = rln;
+              pl = pln;
+              rr = rrn;
+              pr = prn;
+            }
+            ixc = ix1;
+            ix1 = ix2;
+            tc = t1;
+            t1 = t2;
           }
-          // p_k at the row, below (-L) and above (+L)
-          const double pcur = rc + beta * pc;
-          const double pnext = rn + beta * pn;
-          // lanes past the end of a short tile compute its last row: take that
-          // row's -L value (the previous tile was loaded lane for lane)
-          const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
-          // NEAR1: p_k at the rows before and after, from the neighbouring lanes
-          // or, at the ends of the tile, from the rows just outside it
-          double pm1 = 0.0, pp1 = 0.0;
+        } else {
+          // the walk with one tile of look-ahead (r, p_{k-1} and index data of
+          // the next tile); shorter chunks run faster this way
+          int64_t len = tile_len(ug, v0);
+          uint32_t lr = clamp_lane(len);
+          double rc = pre.rc, pc = pre.pc;
+          TileIndex<RP> ix = pre.ix0;
+          // the current tile's edge rows live in scalar registers (the same value
+          // in every lane); the next tile's arrive in vector registers
+          double rl = 0.0, pl = 0.0, rr = 0.0, pr = 0.0;
           if constexpr (NEAR1) {
-            const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
-            const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
-            pm1 = lr == 0 ? rl + beta * pl : sm;
-            pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+            rl = uniform(pre.rl);
+            pl = uniform(pre.pl);
+            rr = uniform(pre.rr);
+            pr = uniform(pre.pr);
           }
-          double acc = 0.0;
-    #pragma unroll
-          for (int t = 0; t < NB; ++t) {
-            const int32_t o = t < band.count ? band.off[t] : 0;
-            const bool use = t < band.count && ((m >> t) & 1u);
-            double gv;
-            if (t == 0) gv = pbelow;
-            else if (t == NB - 1) gv = pnext;
-            else if (t == band.count - 1) gv = pnext;
-            else if (o == 0) gv = pcur;
-            else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
-            else gv = g.value(gu[t], gw[t]);
-            const double sum = acc + a[t] * gv;
-            acc = use ? sum : acc;
+          for (int64_t v = v0; v < v1; ++v) {
+            const int64_t r0 = v * L + col0;
+            const bool own = int64_t(lane) < len;
+            // the next tile: +L neighbours now, own operands in the next step
+            const int64_t lenn = v + 1 < V ? tile_len(ug, v + 1) : 0;
+            const bool hasn = lenn > 0;
+            const int64_t rn0 = hasn ? r0 + L : r0;
+            const uint32_t lrn = hasn ? clamp_lane(lenn) : lr;
+            const double rn = ld(r + rn0, lrn), pn = ld(pold + rn0, lrn);
+            double rln = 0.0, pln = 0.0, rrn = 0.0, prn = 0.0;
+            if constexpr (NEAR1) edges(rn0, hasn ? lenn : len, rln, pln, rrn, prn);
+            const TileIndex<RP> cur = ix;
+            // unconditional (the current tile again when there is no next one): a
+            // conditional load would make the compiler copy the old value into its
+            // register first, which waits for older loads and stores
+            ix = tile_index<NB, RP>(rowptr, mask, n, rn0, lrn);
+            double xo = 0.0, xq = 0.0;
+            if constexpr (XS) {
+              xo = ld(x + r0, lr);
+              xq = ld(pnew + r0, lr);  // p_{k-2}, before p_k replaces it
+            }
+            // near offsets, gathered; the other kinds read the row itself (no
+            // branch; the value is not used)
+            const int64_t lo = r0 - kTileRows;
+            const int64_t base = lo > 0 ? lo : 0;
+            const int32_t d = int32_t(r0 - base) + int32_t(lr);
+            const int32_t top = int32_t(n - 1 - base);
+            // offsets are sorted: -L first, +L last, the near ones in between
+            double gu[NB], gw[NB];
+            if constexpr (!NEAR1) {
+      #pragma unroll
+              for (int t = 1; t < NB - 1; ++t) {
+                const int32_t o = t < band.count - 1 ? band.off[t] : 0;
+                int32_t j = d + o;
+                j = j < 0 ? 0 : (j > top ? top : j);
+                g.load_at(base, uint32_t(j), gu[t], gw[t]);
+              }
+            }
+            // values at the slot positions of the row (see band_row)
+            const int64_t s0 = uniform(int64_t(cur.s0));
+            const unsigned m = cur.m;
+            const int kx = wave_exclusive_sum(own ? __builtin_popcount(m) : 0);
+            uint32_t kk = uint32_t(__shfl(kx, int(lr), kWave));
+            const SLA_GLOBAL double* vb_ = gmem(vals) + (s0 < nnz ? s0 : nnz - 1);
+            double a[NB];
+      #pragma unroll
+            for (int t = 0; t < NB; ++t) {
+              const bool use = t < band.count && ((m >> t) & 1u);
+              a[t] = ld(vb_, use ? kk : 0u);
+              kk += use ? 1u : 0u;
+            }
+            // p_k at the row, below (-L) and above (+L)
+            const double pcur = rc + beta * pc;
+            const double pnext = rn + beta * pn;
+            // lanes past the end of a short tile compute its last row: take that
+            // row's -L value (the previous tile was loaded lane for lane)
+            const double pbelow = len < lenu ? __shfl(pprev, int(lr), kWave) : pprev;
+            // NEAR1: p_k at the rows before and after, from the neighbouring lanes
+            // or, at the ends of the tile, from the rows just outside it
+            double pm1 = 0.0, pp1 = 0.0;
+            if constexpr (NEAR1) {
+              const double sm = __shfl(pcur, int(lr) - 1 >= 0 ? int(lr) - 1 : 0, kWave);
+              const double sp = __shfl(pcur, int64_t(lr) + 1 < len ? int(lr) + 1 : int(lr), kWave);
+              pm1 = lr == 0 ? rl + beta * pl : sm;
+              pp1 = int64_t(lr) + 1 >= len ? rr + beta * pr : sp;
+            }
+            double acc = 0.0;
+      #pragma unroll
+            for (int t = 0; t < NB; ++t) {
+              const int32_t o = t < band.count ? band.off[t] : 0;
+              const bool use = t < band.count && ((m >> t) & 1u);
+              double gv;
+              if (t == 0) gv = pbelow;
+              else if (t == NB - 1) gv = pnext;
+              else if (t == band.count - 1) gv = pnext;
+              else if (o == 0) gv = pcur;
+              else if constexpr (NEAR1) gv = o < 0 ? pm1 : pp1;
+              else gv = g.value(gu[t], gw[t]);
+              const double sum = acc + a[t] * gv;
+              acc = use ? sum : acc;
+            }
+            // lanes past the last row store the same bits as the row's own lane
+            if constexpr (XS) st(x + r0, lr, (xo + alpha2 * xq) + alpha * pc);
+            st(pnew + r0, lr, pcur);
+            st(q + r0, lr, acc);
+            const double pq1 = pq + pcur * acc;
+            pq = own ? pq1 : pq;
+            // shift the walk down one line
+            pprev = pcur;
+            rc = rn;
+            pc = pn;
+            if constexpr (NEAR1) {
+              rl = uniform(rln);
+              pl = uniform(pln);
+              rr = uniform(rrn);
+              pr = uniform(prn);
+            }
+            len = lenn;
+            lr = lrn;
+            if (!hasn) break;
           }
-          // lanes past the last row store the same bits as the row's own lane
-          if (lag) st(x + r0, lr, xo + alpha * pc);
-          st(pnew + r0, lr, pcur);
-          st(q + r0, lr, acc);
-          const double pq1 = pq + pcur * acc;
-          pq = own ? pq1 : pq;
-          // shift the walk down one line
-          pprev = pcur;
-          rc = rn;
-          pc = pn;
-          if constexpr (NEAR1) {
-            rl = uniform(rln);
-            pl = uniform(pln);
-            rr = uniform(rrn);
-            pr = uniform(prn);
-          }
-          len = lenn;
-          lr = lrn;
-          if (!hasn) break;
         }
       }
+      // the next unit's first loads
+      if (unit + per_xcd < units) pre = issue(unit_at(unit + per_xcd));
     }
-    // the next unit's first loads
-    if (unit + per_xcd < units) pre = issue(unit_at(unit + per_xcd));
-  }
+  };
+  if (xs) walk(std::true_type{});
+  else walk(std::false_type{});
   pq = block_sum_once<NT>(pq, red + 2 * kLineWaves);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
@@ -1566,7 +1604,18 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   if (!isfinite(pq)) stop = ST_NONFINITE;
   else if (!(pq > 0.0)) stop = ST_NOT_SPD;
   if (stop != ST_RUNNING) {
-    // breakdown: x already holds x_k (the SpMV step applied the lagged update)
+    // breakdown: x must hold x_k.  The SpMV step applied the lagged update,
+    // except a line walk's odd step, which left alpha_{k-1} p_{k-1} pending
+    if (c->xpair != 0 && (k & 1)) {
+      SLA_GLOBAL double* x = gmem(c->x + s * n);
+      const SLA_GLOBAL double* pk1 = gmem(c->p[0] + s * n);  // p_{k-1} (k odd)
+      const double a1 = scg->alpha[0];                        // alpha_{k-1}
+      const TileWalk tw = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
+      for (int64_t t = tw.first; t < tw.end; t += tw.stride) {
+        const int64_t i0 = t * kTileRows;
+        if (i0 + lane < n) st(x + i0, lane, ld(x + i0, lane) + a1 * ld(pk1 + i0, lane));
+      }
+    }
     if (lead) {
       sc->it = k;
       sc->rr_final = rr;
@@ -1577,7 +1626,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   }
   const double alpha = uniform(num / pq);
   if (lead) {
-    sc->alpha = alpha;
+    sc->alpha[k & 1] = alpha;
     sc->ka = k + 1;
   }
   double rn = 0.0, rzn = 0.0;
@@ -1860,6 +1909,7 @@ void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool
   c.pblock = A->pblock;
   c.line = use_lines(A) ? A->line : 0;
   c.line_chunks = c.line > 0 ? line_chunks(A) : 0;
+  c.xpair = c.line > 0 ? 1 : 0;
 }
 
 // Workgroups for a one-pass kernel over `tiles` wave tiles and `batch` systems.
@@ -2183,9 +2233,9 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
   const dim3 grid2(unsigned(A->grid), 1u);
   // the SpMV step is one kernel, or the direction and product passes
   const bool split = use_split(A);
-  const void* fns[3];
-  size_t ldss[3];
-  unsigned blocks[3];
+  const void* fns[4];
+  size_t ldss[4];
+  unsigned blocks[4];
   int nk = 0;
   if (split) {
     fns[nk] = reinterpret_cast<const void*>(&k_cg_direction);
@@ -2202,6 +2252,16 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
   fns[nk] = reinterpret_cast<const void*>(&k_cg_residual<false>);
   blocks[nk] = kIterBlock;
   ldss[nk++] = 0;
+  const int res_k = nk - 1;  // the residual step's entry
+  // a one-kernel SpMV step is timed again after the residual launches, which
+  // move the solve to the next step: the line walk's steps alternate between
+  // two kinds (x updated at even steps only), and the result is their mean
+  if (!split) {
+    fns[nk] = fns[0];
+    blocks[nk] = blocks[0];
+    ldss[nk++] = ldss[0];
+  }
+  const double spmv_w = split ? 1.0 : 0.5;
   std::vector<hipEvent_t> ev(size_t(2 * reps), nullptr);
   for (auto& e : ev) SLA_TRY_HIP(hipEventCreate(&e));
   sla_status status = SLA_OK;
@@ -2229,7 +2289,8 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
       (void)hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]);
       total += ms;
     }
-    avg_ms[k == nk - 1 ? 1 : 0] += total / double(reps);
+    if (k == res_k) avg_ms[1] += total / double(reps);
+    else avg_ms[0] += spmv_w * total / double(reps);
   }
   for (auto& e : ev)
     if (e) (void)hipEventDestroy(e);

@@ -126,7 +126,7 @@ enum : int32_t {
 struct alignas(64) Scal {
   double rr[2];     // r_k . r_k, by parity of k          (SpMV step writes)
   double rz[2];     // r_k . z_k (Jacobi), by parity of k  (SpMV step writes)
-  double alpha;     // alpha_k                              (residual step writes)
+  double alpha[2];  // alpha_k, by parity of k               (residual step writes)
   double bb;        // b . b                                (set-up)
   double stop;      // (tol * tol) * bb                     (set-up)
   double rr_final;  // r . r when the system stopped        (the stopping step)
@@ -177,6 +177,10 @@ struct alignas(64) Ctx {
   int32_t pblock;       // tiles per column block of the panel order
   int64_t line;         // grid line length of a line-walk band (0: none)
   int32_t line_chunks;  // line chunks per XCD in the line walk
+  // the line walk applies x's deferred updates two at a time: the SpMV step
+  // of an even k >= 2 adds alpha_{k-2} p_{k-2} and alpha_{k-1} p_{k-1}, odd
+  // steps leave x alone (the other kernels add alpha_{k-1} p_{k-1} at every k)
+  int32_t xpair;
 };
 static_assert(sizeof(Ctx) % alignof(Scal) == 0, "Scal records follow the context");
 
