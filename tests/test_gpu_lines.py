@@ -113,3 +113,45 @@ def test_poisson_long_chunks():
     b = W.uniform_rhs(1700 * 1700, 29)
     g = W.normal_rhs(1700 * 1700, 30)
     _check("poisson1700 wg1", rp, c, v, b, g, 0.0, 40, wg=1)
+
+
+@pytest.mark.parametrize("maxit", [1, 2, 3, 4, 7, 8])
+def test_paired_x_updates_fixed_stops(maxit):
+    """The walk applies x's deferred updates two steps at a time: solves cut
+    off after an odd or an even number of iterations (the last pass adding
+    one or two pending updates) and their adjoints against the oracle."""
+    N = 1000
+    rp, c, v = W.poisson_csr(N)
+    A = oracle.CSR(N * N, rp.astype(np.int64), c, v)
+    b = W.uniform_rhs(N * N, 31)
+    g = W.normal_rhs(N * N, 32)
+    lines, x, gb, gv, info, ai = _solve(rp, c, v, b, g, 0.0, maxit, wg=1)
+    assert lines and info.iterations == maxit == ai.iterations
+    xo, _ = oracle.cg(A, b, 0.0, maxit)
+    gbo, gvo, _ = oracle.adjoint(A, xo, g, 0.0, maxit)
+    say(f"maxit {maxit}: x {rel(x, xo):.1e} grad_b {rel(gb, gbo):.1e}")
+    assert rel(x, xo) <= 1e-12 and rel(gb, gbo) <= 1e-12 and rel(gv, gvo) <= 1e-12
+
+
+def test_paired_x_updates_breakdown_at_odd_step():
+    """An indefinite shift of the 1000^2 Laplacian breaks down (p.Ap <= 0)
+    at an odd step, found by the residual step, which then adds the update
+    the walk left pending: status, iteration and x against the oracle."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    N = 1000
+    rp, c, v = W.poisson_csr(N)
+    rows = np.repeat(np.arange(N * N), np.diff(rp))
+    vs = v - np.where(rows == c, 0.05, 0.0)
+    b = W.uniform_rhs(N * N, 0)
+    P = csr_handle(rp, c)
+    assert P.lines
+    x, info = K.sla_cg_solve(P, t(vs), t(b), 1e-8, 5000, check=False)
+    torch.cuda.synchronize()
+    A = oracle.CSR(N * N, rp.astype(np.int64), c, vs)
+    xo, io = oracle.cg(A, b, 1e-8, 5000)
+    say(f"shift -0.05: status {info.status} it {info.iterations} (oracle {io.status} "
+        f"{io.iterations}) x {rel(x.cpu().numpy(), xo):.1e}")
+    assert info.status == K.ERR_NOT_SPD == io.status
+    assert info.iterations == io.iterations and info.iterations % 2 == 1
+    assert rel(x.cpu().numpy(), xo) <= 1e-10
