@@ -110,6 +110,8 @@ def _bind(lib):
     lib.oracle_permute.argtypes = [_I64, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.oracle_permute.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_progress.restype = None
+    lib.oracle_set_progress.argtypes = [_I64]
     lib.oracle_get_threads.restype = ctypes.c_int
     lib.oracle_get_threads.argtypes = []
     return lib
@@ -161,6 +163,33 @@ def set_threads(t: int) -> None:
 
 def get_threads() -> int:
     return int(_load().oracle_get_threads())
+
+
+def set_progress(every: int) -> None:
+    """Make cg() print one line to stderr every `every` iterations (0: off)."""
+    _load().oracle_set_progress(int(every))
+
+
+def host_threads() -> int:
+    """Threads for the oracle: the process's CPU share (OMP_NUM_THREADS when
+    the environment fixes it, else the CPUs this process may run on)."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    if env.isdigit() and int(env) > 0:
+        return min(int(env), avail)
+    return avail
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ('unknown' if absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def csr_from_coo(n: int, row, col, lib=None):

@@ -31,7 +31,8 @@
  *   - breakdown: p.Ap not finite -> NONFINITE; p.Ap <= 0 -> NOT_SPD.
  *   - dot products: sequential sums over fixed 4096-element blocks, then a
  *     sequential sum of the block sums; the bits do not depend on the number
- *     of OpenMP threads.
+ *     of OpenMP threads.  The CG's element-wise loops split their index
+ *     range over the threads; each element's arithmetic is unchanged.
  *   - SpMV: per row, ascending slot order, y = 0 then y = y + a*x per slot.
  *   - duplicate COO entries: merged into one CSR slot, values summed in
  *     input order, starting from the first value (not from 0.0).
@@ -41,6 +42,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -191,6 +193,11 @@ double oracle_dot(int64_t n, const double* u, const double* v) {
 /* Conjugate gradient                                                        */
 /* ------------------------------------------------------------------------ */
 
+/* Long solves can report their own progress: every `progress_every`
+ * completed iterations oracle_cg writes one line to stderr (0 = silent). */
+static int64_t progress_every = 0;
+void oracle_set_progress(int64_t every) { progress_every = every > 0 ? every : 0; }
+
 typedef struct {
   int64_t iterations;
   double rr;        /* final recursive residual norm squared */
@@ -219,13 +226,16 @@ int oracle_cg(int64_t n, const int64_t* rowptr, const int32_t* col,
   /* r0 = b - A x0 ; p0 = r0 */
   if (use_x0) {
     oracle_spmv(n, rowptr, col, vals, x, q);
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) r[i] = b[i] - q[i];
   } else {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
       x[i] = 0.0;
       r[i] = b[i];
     }
   }
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) p[i] = r[i];
 
   double bb = oracle_dot(n, b, b);
@@ -248,6 +258,7 @@ int oracle_cg(int64_t n, const int64_t* rowptr, const int32_t* col,
         break;
       }
       double alpha = rr / pq;
+#pragma omp parallel for schedule(static)
       for (int64_t i = 0; i < n; ++i) {
         x[i] = x[i] + alpha * p[i];
         r[i] = r[i] - alpha * q[i];
@@ -258,12 +269,18 @@ int oracle_cg(int64_t n, const int64_t* rowptr, const int32_t* col,
         break;
       }
       double beta = rr_new / rr;
+#pragma omp parallel for schedule(static)
       for (int64_t i = 0; i < n; ++i) p[i] = r[i] + beta * p[i];
       if (hist_alpha) hist_alpha[k] = alpha;
       if (hist_beta) hist_beta[k] = beta;
       if (hist_rr) hist_rr[k] = rr_new;
       rr = rr_new;
       k = k + 1;
+      if (progress_every && k % progress_every == 0) {
+        fprintf(stderr, "[oracle cg] n=%lld iteration %lld of %lld, rr/bb %.3e\n",
+                (long long)n, (long long)k, (long long)maxit, rr / bb);
+        fflush(stderr);
+      }
     }
   }
   info->iterations = k;

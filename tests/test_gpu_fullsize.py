@@ -6,11 +6,14 @@ bench.py times (default graph block, default grid).
 * Random geometric graph, 4M nodes, tol 1e-8 forward + adjoint: the CSR
   built on the GPU from the same COO is compared bit for bit, then x, lambda
   and grad_vals element-wise against the oracle.
-* Poisson 4000 x 4000 and 13000 x 13000 (int64 row pointers), 500 fixed
-  iterations: too long for the oracle's CG, so checked by properties that
-  hold at any size: the CG energy identity b.x_k = sum_j alpha_j r_j.r_j, the
-  recursive residual against b - A x computed by the oracle's SpMV, a bit-exact
-  SpMV against the oracle, and Ritz values inside the closed-form spectrum.
+* Poisson 4000 x 4000, 500 fixed iterations: x element-wise against the
+  oracle's CG on all of the process's host threads, the same iteration count,
+  and the alpha / beta / r.r history; besides, properties that hold at any
+  size: the CG energy identity b.x_k = sum_j alpha_j r_j.r_j, the recursive
+  residual against b - A x computed by the oracle's SpMV, a bit-exact SpMV
+  against the oracle, and Ritz values inside the closed-form spectrum.
+  (The 13000 x 13000 grid with int64 row pointers gets the same checks in a
+  file of its own, run after the others.)
 """
 import math
 import os
@@ -28,7 +31,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module", autouse=True)
 def _threads():
-    oracle.set_threads(min(16, os.cpu_count() or 1))
+    oracle.set_threads(oracle.host_threads())
 
 
 def test_poisson1000_fixed1000_forward_adjoint():
@@ -112,7 +115,10 @@ def test_rgg4m_csr_forward_adjoint():
     assert rel(xr, xo) <= TOL_X and rel(gbr, gbo) <= TOL_X and rel(gvr, gvo) <= TOL_GRAD
 
 
-def _properties(N, rp_dtype, maxit=500):
+def fixed_vs_oracle(N, rp_dtype, capfd, maxit=500):
+    """500 fixed CG iterations on the N x N Poisson grid, b ~ U(-1,1) seed 0,
+    in the launch configuration the benchmark times: properties of the GPU
+    iterate, then the oracle's CG on the same system."""
     import torch
     import krylov_solvers_adjoint_amd as K
     n = N * N
@@ -120,6 +126,7 @@ def _properties(N, rp_dtype, maxit=500):
     rp, c, v = W.poisson_csr(N, rp_dtype)
     b = W.uniform_rhs(n, 0)
     P = csr_handle(rp, c)
+    assert P.lines
     vt = t(v)
     bt = t(b)
     x, info = K.sla_cg_solve(P, vt, bt, 0.0, maxit, history=True)
@@ -128,12 +135,15 @@ def _properties(N, rp_dtype, maxit=500):
     torch.cuda.synchronize()
     x = x.cpu().numpy()
     y = y.cpu().numpy()
+    del vt, bt, P
+    torch.cuda.empty_cache()
     assert info.iterations == maxit and len(al) == maxit
     say(f"poisson{N}: GPU done; oracle SpMV")
     Ao = oracle.CSR(n, rp.astype(np.int64) if rp.dtype != np.int64 else rp, c, v)
     yo = oracle.spmv(Ao, x)
     # the library's SpMV is bit-identical to the oracle's
     assert np.array_equal(y, yo)
+    del y
     bb = float(b @ b)
     # energy identity: b.x_k = sum_j alpha_j rr_j with rr_0 = b.b
     rrs = np.concatenate([[bb], rr[:-1]])
@@ -144,6 +154,7 @@ def _properties(N, rp_dtype, maxit=500):
     assert abs(lhs - rhs) <= 1e-12 * abs(rhs)
     # the recursive residual tracks the true one
     true_rr = float(np.sum((b - yo) ** 2))
+    del yo
     say(f"poisson{N}: recursive rr {rr[-1]:.6e} true {true_rr:.6e}")
     assert abs(true_rr - rr[-1]) <= 1e-6 * rr[-1]
     assert abs(info.rel_residual - math.sqrt(rr[-1] / bb)) <= 1e-12
@@ -157,13 +168,26 @@ def _properties(N, rp_dtype, maxit=500):
     # spectrum; the top of the spectrum is found within a few hundred steps
     assert ritz.min() >= lo - 1e-12 and ritz.max() <= hi + 1e-12 * hi
     assert abs(ritz.max() - hi) <= 1e-4 * hi
-
-
-@pytest.mark.timeout(300)
-def test_poisson4000_fixed500_properties():
-    _properties(4000, np.int32)
+    # the oracle's own CG on the same system; it reports every 50 iterations
+    threads = oracle.get_threads()
+    say(f"poisson{N}: oracle CG, {maxit} iterations on {threads} threads")
+    oracle.set_progress(50)
+    try:
+        with capfd.disabled():
+            xo, io, (alo, beo, rro) = oracle.cg(Ao, b, 0.0, maxit, history=True)
+    finally:
+        oracle.set_progress(0)
+    da = float(np.max(np.abs(al - alo) / np.abs(alo)))
+    db = float(np.max(np.abs(be - beo) / np.abs(beo)))
+    dr = float(np.max(np.abs(rr - rro) / np.abs(rro)))
+    say(f"poisson{N}: oracle iterations {io.iterations}; x rel {rel(x, xo):.2e}; "
+        f"alpha {da:.1e} beta {db:.1e} rr {dr:.1e}")
+    assert io.status == oracle.OK and io.iterations == info.iterations == maxit
+    assert rel(x, xo) <= TOL_X
+    # the scalars of every iteration to the same relative bar as x
+    assert da <= TOL_X and db <= TOL_X and dr <= TOL_X
 
 
 @pytest.mark.timeout(600)
-def test_poisson13000_int64_fixed500_properties():
-    _properties(13000, np.int64)
+def test_poisson4000_fixed500_vs_oracle(capfd):
+    fixed_vs_oracle(4000, np.int32, capfd)

@@ -115,12 +115,15 @@ def test_poisson_long_chunks():
     _check("poisson1700 wg1", rp, c, v, b, g, 0.0, 40, wg=1)
 
 
+@pytest.mark.parametrize("N", [1000, 1700])
 @pytest.mark.parametrize("maxit", [1, 2, 3, 4, 7, 8])
-def test_paired_x_updates_fixed_stops(maxit):
+def test_paired_x_updates_fixed_stops(maxit, N):
     """The walk applies x's deferred updates two steps at a time: solves cut
     off after an odd or an even number of iterations (the last pass adding
-    one or two pending updates) and their adjoints against the oracle."""
-    N = 1000
+    one or two pending updates) and their adjoints against the oracle.  At
+    one workgroup per CU, 1000^2 gives ~7 lines per chunk (the one-tile
+    look-ahead walk) and 1700^2 gives 26 (the two-deep pipelined walk, the
+    one the 16M grid takes)."""
     rp, c, v = W.poisson_csr(N)
     A = oracle.CSR(N * N, rp.astype(np.int64), c, v)
     b = W.uniform_rhs(N * N, 31)
