@@ -50,7 +50,9 @@ typedef enum {
   SLA_ERR_NONFINITE = 6,  /* b.b, p.Ap or r.r is not finite                     */
   SLA_ERR_KRYLOV = 7,     /* eigsh: the Lanczos process ended (an invariant
                              subspace was reached) after fewer than k steps   */
-  SLA_ERR_BREAKDOWN = 8   /* BiCGStab: rhat.r, rhat.v or t.t became 0          */
+  SLA_ERR_BREAKDOWN = 8,  /* BiCGStab: rhat.r, rhat.v or t.t became 0          */
+  SLA_ERR_NOT_SYMMETRIC = 9 /* CG: the pattern (solve, adjoint) or the values
+                             (adjoint) are not symmetric                      */
 } sla_status;
 
 typedef enum { SLA_I32 = 4, SLA_I64 = 8 } sla_index;
@@ -70,7 +72,9 @@ enum {
 };
 
 /* Opaque matrix handle: the sparsity pattern (owned by the library, copied
- * or built at creation) plus a borrowed pointer to the values. */
+ * or built at creation), the values -- either a copy the handle owns
+ * (sla_csr_load_values) or a caller's array it reads in place
+ * (sla_csr_set_values) -- and the solver workspace. */
 typedef struct sla_csr_s* sla_csr;
 
 /*
@@ -100,45 +104,98 @@ sla_status sla_csr_create_from_csr(int64_t n, int64_t nnz, sla_index rowptr_idx,
                                    const void* rowptr, const int32_t* col,
                                    hipStream_t stream, sla_csr* out);
 
-/* Free the handle and everything the library allocated for it. */
+/* Free the handle and everything the library allocated for it (the sparse
+ * tensor's lifetime, Methodology 1).  Waits for the device first.  NULL is
+ * accepted. */
 sla_status sla_csr_destroy(sla_csr A);
 
-/* Sizes: order, stored slots, COO triplets it was built from (0 if from CSR),
- * row-pointer width.  Any output pointer may be NULL. */
+/* Sizes of the sparse tensor (Methodology 1): order, stored slots, COO
+ * triplets it was built from (0 if from CSR), row-pointer width.  Any output
+ * pointer may be NULL. */
 sla_status sla_csr_get_info(sla_csr A, int64_t* n_host, int64_t* nnz_host,
                             int64_t* nnz_coo_host, sla_index* rowptr_idx_host);
 
-/* Borrowed views of the pattern (valid until destroy).  perm[k] is the CSR
- * slot COO triplet k was merged into; NULL for a handle made from CSR. */
+/* Borrowed device views of the pattern (Methodology 1: the shared sparsity
+ * pattern), valid until destroy.  perm[k] is the CSR slot COO triplet k was
+ * merged into; NULL for a handle made from CSR.  sla_csr_arrays gives the
+ * same views plus the bound values. */
 sla_status sla_csr_pattern(sla_csr A, const void** rowptr_host,
                            const int32_t** col_host, const int64_t** perm_host);
 
-/* Copy the pattern into caller buffers (any may be NULL): rowptr_out [n+1]
- * of the handle's row-pointer width, col_out [nnz], perm_out [nnz_coo]
- * (COO-built handles only).  Asynchronous on `stream`. */
+/* Copy the pattern (Methodology 1) into caller buffers (any may be NULL):
+ * rowptr_out [n+1] of the handle's row-pointer width, col_out [nnz],
+ * perm_out [nnz_coo] (COO-built handles only).  Asynchronous on `stream`. */
 sla_status sla_csr_copy_pattern(sla_csr A, void* rowptr_out, int32_t* col_out,
                                 int64_t* perm_out, hipStream_t stream);
 
 /*
- * CSR values from COO values: vals[s][slot] = the COO values mapped onto that
- * slot, added in input order starting from the first one.  coo_val
- * [batch][nnz_coo], vals [batch][nnz].  Needs a COO-built handle.
+ * CSR values from COO values (Methodology 1: a SparseTensor built from
+ * coordinates): vals[s][slot] = the COO values mapped onto that slot, added
+ * in input order starting from the first one.  coo_val [batch][nnz_coo],
+ * vals [batch][nnz], caller-owned device memory.  Needs a COO-built handle.
+ * Asynchronous.
  */
 sla_status sla_csr_values_from_coo(sla_csr A, const double* coo_val, double* vals,
                                    int64_t batch, hipStream_t stream);
 
-/* Gradient of COO values from the gradient of CSR values:
- * grad_coo[s][k] = grad_vals[s][perm[k]] (every duplicate gets its slot's). */
+/* Gradient of COO values from the gradient of CSR values (Methodology 2:
+ * the matrix gradient lives on the pattern; a merged duplicate is one
+ * parameter of the slot): grad_coo[s][k] = grad_vals[s][perm[k]].
+ * Asynchronous. */
 sla_status sla_csr_grad_to_coo(sla_csr A, const double* grad_vals, double* grad_coo,
                                int64_t batch, hipStream_t stream);
 
 /*
- * Bind the values: vals [batch][nnz] in CSR slot order, owned by the caller,
- * read by every later spmv / solve / adjoint until re-bound.  batch >= 1.
+ * Bind the values (Methodology 1: a SparseTensor is one matrix or a batch of
+ * matrices on one pattern): vals [batch][nnz] in CSR slot order, owned by the
+ * caller, read in place by every later spmv / solve / adjoint until re-bound.
+ * The caller keeps the array alive and unchanged while work that reads it is
+ * queued.  batch >= 1.  A copy the handle owns (sla_csr_load_values) stays
+ * allocated; passing its pointer (from sla_csr_arrays) binds it again.
  */
 sla_status sla_csr_set_values(sla_csr A, const double* vals, int64_t batch);
 
-/* y[s] = A_s x[s] for every system s of the bound batch (the .matvec). */
+/*
+ * Copy values into an array the handle owns and bind it (Methodology 1: the
+ * sparse tensor holds its values; a batch shares the pattern).  order
+ * SLA_VALUES_CSR: vals [batch][nnz] in CSR slot order; SLA_VALUES_COO: vals
+ * [batch][nnz_coo] in the COO triplet order the handle was built from,
+ * merged into the slots as sla_csr_values_from_coo does (COO-built handles
+ * only).  The copy is enqueued on `stream`; the caller's array may be freed
+ * once that work is done.  The owned array lives until the handle is
+ * destroyed or a load with another batch size replaces it; sla_csr_arrays
+ * gives its device address, where callers may update values in place
+ * between calls (a training step, say).  Errors: SLA_ERR_ARG, SLA_ERR_OOM.
+ */
+enum { SLA_VALUES_CSR = 0, SLA_VALUES_COO = 1 };
+sla_status sla_csr_load_values(sla_csr A, const double* vals, int64_t batch, int order,
+                               hipStream_t stream);
+
+/*
+ * Borrowed device views of the handle's arrays (any output may be NULL),
+ * valid until the handle is destroyed (vals: until the values are re-bound
+ * or reloaded): rowptr [n+1] (of the handle's row-pointer width), col [nnz],
+ * the bound values [batch][nnz] (the handle's own copy after
+ * sla_csr_load_values, else the caller's array; NULL if none is bound), and
+ * perm [nnz_coo] (COO triplet -> slot; NULL for a handle made from CSR).
+ */
+sla_status sla_csr_arrays(sla_csr A, const void** rowptr_host, const int32_t** col_host,
+                          double** vals_host, const int64_t** perm_host);
+
+/*
+ * Device memory held by the library on the current device, over every handle
+ * and workspace: *live_host the bytes allocated now, *peak_host the most at
+ * any time since the process started or the last reset (either may be NULL);
+ * reset_peak != 0 then sets the peak to the live bytes.  Pinned host memory
+ * (a few small per-handle buffers) is not counted.  Compare with the adjoint
+ * memory the pages report (Experimental results, memory efficiency).
+ */
+sla_status sla_memory_usage(int64_t* live_host, int64_t* peak_host, int reset_peak);
+
+/* y[s] = A_s x[s] for every system s of the bound batch: the sparse
+ * tensor's .matvec (Methodology 1, unified backend abstraction).  Row i is
+ * summed in ascending slot order, y = 0 then y = y + a x, each product and
+ * sum rounded on its own.  x, y [batch][n] device memory.  Asynchronous. */
 sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream);
 
 /*
@@ -163,7 +220,12 @@ sla_status sla_matvec_grad(sla_csr A, const double* x, const double* grad_y, dou
                            double* grad_vals, hipStream_t stream);
 
 /*
- * Solve A x = b by CG (bound batch must be 1).  x0 = 0 unless SLA_FLAG_X0.
+ * Solve A x = b by CG (bound batch must be 1): the sparse tensor's .solve
+ * with the PyTorch-native iterative (CG) backend (Methodology 1), as
+ * benchmarked on 2D Poisson systems (Experimental results).  CG needs a
+ * symmetric positive definite A: a pattern that is not symmetric (checked
+ * once per handle) returns SLA_ERR_NOT_SYMMETRIC before any iteration, x
+ * untouched.  x0 = 0 unless SLA_FLAG_X0.
  * Stops when rr <= (tol*tol)*bb with rr the recursive residual norm squared
  * and bb = b.b (checked before each iteration), or after maxit iterations;
  * tol = 0 runs exactly maxit iterations.  Not converging is SLA_OK with
@@ -190,7 +252,11 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol,
  * SPD matrices CG accepts), write grad_b = lambda and
  * grad_vals[k] = -lambda_i x_j for every stored slot k = (i, j).  grad_vals
  * may be NULL (then only grad_b).  Memory: O(n + nnz), independent of the
- * iteration count.  Same stopping rule and statuses as sla_cg_solve.
+ * iteration count.  Same stopping rule and statuses as sla_cg_solve.  Since
+ * the solve uses A in place of A^T, every call first checks the bound values
+ * (each stored a_ij against a_ji, bit for bit, one pass over the values);
+ * a mismatch returns SLA_ERR_NOT_SYMMETRIC before any iteration (grad_b and
+ * grad_vals untouched).
  */
 sla_status sla_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
                           double* grad_b, double* grad_vals, double tol,
@@ -200,7 +266,9 @@ sla_status sla_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
 /* Shared-pattern batch (Methodology 1, SparseTensor batching): every system
  * of the bound batch solved independently, each with its own scalars and
  * stopping test.  b, x [batch][n]; info_host [batch] (may be NULL).  Returns
- * the first non-OK system status, else SLA_OK. */
+ * the first non-OK system status, else SLA_OK.  The symmetry checks are
+ * those of sla_cg_solve / sla_cg_adjoint (the adjoint's over every system's
+ * values). */
 sla_status sla_cg_solve_batched(sla_csr A, const double* b, double* x, double tol,
                                 int64_t maxit, uint32_t flags, sla_cg_info* info_host,
                                 hipStream_t stream);
@@ -210,19 +278,26 @@ sla_status sla_cg_adjoint_batched(sla_csr A, const double* x, const double* grad
                                   int64_t maxit, uint32_t flags,
                                   sla_cg_info* info_host, hipStream_t stream);
 
-/* The pattern gradient alone: grad_vals[s][k] = -lambda[s][i] * x[s][j]. */
+/* The pattern gradient alone (Methodology 2, linear systems: the matrix
+ * gradient only on the sparsity pattern): grad_vals[s][k] = -lambda[s][i] *
+ * x[s][j] for every stored slot k = (i, j), one correctly rounded product.
+ * lambda, x [batch][n]; grad_vals [batch][nnz].  Asynchronous. */
 sla_status sla_pattern_grad(sla_csr A, const double* lambda, const double* x,
                             double* grad_vals, hipStream_t stream);
 
 /* After a solve with SLA_FLAG_HISTORY: copy system `system`'s per-iteration
  * alpha_k, beta_k and r.r after iteration k (host arrays of length cap; any
- * may be NULL).  *count_host = iterations recorded. */
+ * may be NULL).  *count_host = iterations recorded.  The scalars of the CG
+ * the pages call "CG" (Methodology 1, iterative backend), for tracing and
+ * for checks (the CG-Lanczos Ritz values, the energy identity). */
 sla_status sla_cg_history(sla_csr A, int64_t system, double* alpha_host,
                           double* beta_host, double* rr_host, int64_t cap,
                           int64_t* count_host);
 
 /*
- * Instrumentation for benchmarks (batch 1): set up the solve of A x = b as
+ * Instrumentation for the measurements of the pages' kind (Experimental
+ * results: CG on 2D Poisson) at the kernel level (batch 1): set up the solve
+ * of A x = b as
  * sla_cg_solve does (tol 0) and run one iteration, then launch each of the
  * two kernels of a CG iteration `reps` times on `stream`, each launch
  * bracketed by start/stop events recorded around the kernel itself, and
@@ -382,7 +457,9 @@ sla_status sla_profile_lanczos_kernels(sla_csr A, int64_t nvec, int64_t reps,
                                       double* avg_ms_host, hipStream_t stream);
 
 /*
- * SpMV kernel family.  At creation the pattern analysis checks whether every
+ * SpMV kernel family (the .matvec and the SpMV inside the CG iteration,
+ * Methodology 1; a choice of this library, not on the pages).  At creation
+ * the pattern analysis checks whether every
  * stored column j of every row i equals i + d for one of at most 8 fixed
  * offsets d (a banded or stencil pattern such as the 5-point Laplacian); if
  * so, the banded kernels can read a mask byte per row and one row pointer per
@@ -419,11 +496,14 @@ enum {
 sla_status sla_csr_set_spmv_variant(sla_csr A, int variant, int* kernels_host);
 
 /* Iterations per captured HIP graph block (default 32; 0 = launch kernels
- * one by one without graphs).  Affects speed only, never results. */
+ * one by one without graphs): the remedy here for the kernel-launch cost of
+ * iterative solvers (Problem statement).  Affects speed only, never
+ * results. */
 sla_status sla_csr_set_graph_block(sla_csr A, int64_t iterations);
 
-/* Solver workgroups per compute unit (1024 threads each; 512 in the line
- * walk): 0 (default: automatic: 1 for solves of at most 2^21 unknowns over
+/* Solver workgroups per compute unit (a tuning knob of the CG backend,
+ * Methodology 1; 1024 threads each; 512 in the line walk): 0 (default:
+ * automatic: 1 for solves of at most 2^21 unknowns over
  * the batch, where the kernels' fixed costs dominate, and for line-walk
  * patterns (2D stencils), whose waves then walk longer chunks, and on
  * reordered handles (sla_csr_reorder), whose gathers hit the L2; else 2), 1
@@ -492,10 +572,11 @@ sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
 enum { SLA_ONE_GROUP_AUTO = 0, SLA_ONE_GROUP_OFF = 1 };
 sla_status sla_csr_set_one_group(sla_csr A, int mode);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none): the error
+ * reporting of this boundary (not on the pages). */
 const char* sla_last_error(void);
 
-/* Name of a status code. */
+/* Name of a status code (not on the pages). */
 const char* sla_status_string(sla_status s);
 
 #ifdef __cplusplus

@@ -30,14 +30,16 @@ __all__ = [
     "sla_spmv_transpose", "sla_matvec_grad", "sla_eigsh", "sla_eig_grad", "EigInfo",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_solve_list", "sla_adjoint_list", "SparseTensorList",
-    "sla_csr_reorder", "sla_csr_ordering",
+    "sla_csr_reorder", "sla_csr_ordering", "sla_csr_load_values", "sla_csr_arrays",
+    "sla_memory_usage",
     "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsla.so")
 
 (OK, ERR_ARG, ERR_CSR, ERR_OOM, ERR_DEVICE, ERR_NOT_SPD, ERR_NONFINITE, ERR_KRYLOV,
- ERR_BREAKDOWN) = range(9)
+ ERR_BREAKDOWN, ERR_NOT_SYMMETRIC) = range(10)
+VALUES_CSR, VALUES_COO = 0, 1
 EIG_SMALLEST, EIG_LARGEST = 0, 1
 METHOD_CG, METHOD_BICGSTAB = 0, 1
 I32, I64 = 4, 8
@@ -56,7 +58,8 @@ EXPORTS = [
     "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_solve_list", "sla_adjoint_list", "sla_csr_reorder", "sla_csr_ordering",
-    "sla_csr_set_one_group", "sla_last_error", "sla_status_string",
+    "sla_csr_set_one_group", "sla_csr_load_values", "sla_csr_arrays", "sla_memory_usage",
+    "sla_last_error", "sla_status_string",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -118,6 +121,10 @@ def _bind(lib):
         "sla_csr_reorder": [_P, _S, _P],
         "sla_csr_set_one_group": [_P, _S],
         "sla_csr_ordering": [_P, _P, _P],
+        "sla_csr_load_values": [_P, _P, _I64, _S, _P],
+        "sla_csr_arrays": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                           ctypes.POINTER(_P)],
+        "sla_memory_usage": [ctypes.POINTER(_I64), ctypes.POINTER(_I64), _S],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -352,6 +359,42 @@ def sla_csr_ordering(A: CSRPattern, stream=None) -> torch.Tensor:
     out = torch.empty(A.n, dtype=torch.int32, device=torch.device("cuda", torch.cuda.current_device()))
     _check(_lib.sla_csr_ordering(A.handle, out.data_ptr() if A.n else None, _stream(stream)))
     return out
+
+
+def sla_csr_load_values(A: CSRPattern, values: torch.Tensor, order: str = "csr",
+                        stream=None) -> int:
+    """Copy values into an array the handle owns and bind it: [nnz] or
+    [batch, nnz] in CSR slot order ("csr"), or [nnz_coo] / [batch, nnz_coo]
+    in the COO triplet order the pattern was built from ("coo").  Returns
+    the batch size.  The later calls of this module bind the values they are
+    given, so this serves callers of the C ABI that keep the handle's own
+    copy (sla_csr_arrays gives its address)."""
+    code = {"csr": VALUES_CSR, "coo": VALUES_COO}[order]
+    width = A.nnz if code == VALUES_CSR else A.nnz_coo
+    if values.dim() not in (1, 2) or values.shape[-1] != width:
+        raise ValueError(f"values has shape {tuple(values.shape)}; expected [..., {width}]")
+    batch = 1 if values.dim() == 1 else values.shape[0]
+    _check(_lib.sla_csr_load_values(A.handle, _dev(values, torch.float64, "values"), batch,
+                                    code, _stream(stream)))
+    A._bound = None
+    return batch
+
+
+def sla_csr_arrays(A: CSRPattern) -> dict:
+    """Device addresses of the handle's arrays (borrowed views): rowptr, col,
+    the bound values (0 if none) and perm (0 for a handle made from CSR)."""
+    rp, c, v, pm = _P(), _P(), _P(), _P()
+    _check(_lib.sla_csr_arrays(A.handle, ctypes.byref(rp), ctypes.byref(c), ctypes.byref(v),
+                               ctypes.byref(pm)))
+    return {"rowptr": rp.value or 0, "col": c.value or 0, "vals": v.value or 0,
+            "perm": pm.value or 0}
+
+
+def sla_memory_usage(reset_peak: bool = False) -> tuple:
+    """(live, peak) device bytes the library holds on the current device."""
+    live, peak = _I64(), _I64()
+    _check(_lib.sla_memory_usage(ctypes.byref(live), ctypes.byref(peak), 1 if reset_peak else 0))
+    return live.value, peak.value
 
 
 def sla_csr_values_from_coo(A: CSRPattern, coo_val: torch.Tensor, stream=None) -> torch.Tensor:

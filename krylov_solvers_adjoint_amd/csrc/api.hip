@@ -27,20 +27,63 @@ void set_error(const char* fmt, ...) {
 }
 void clear_error() { g_err[0] = '\0'; }
 
+// Every device allocation of the library goes through dev_alloc / dev_free,
+// which keep the live and peak bytes per device (sla_memory_usage).
+namespace {
+struct MemBook {
+  std::mutex mu;
+  std::map<void*, std::pair<int, size_t>> blocks;  // pointer -> (device, bytes)
+  std::map<int, int64_t> live, peak;
+};
+MemBook& mem_book() {
+  static MemBook* b = new MemBook();  // never destroyed: frees may come at exit
+  return *b;
+}
+}  // namespace
+
 sla_status dev_alloc(void** p, size_t bytes, const char* what) {
   *p = nullptr;
-  hipError_t e = hipMalloc(p, bytes == 0 ? 1 : bytes);
+  const size_t sz = bytes == 0 ? 1 : bytes;
+  hipError_t e = hipMalloc(p, sz);
   if (e != hipSuccess) {
     *p = nullptr;
     (void)hipGetLastError();
     set_error("out of device memory allocating %zu bytes for %s", bytes, what);
     return SLA_ERR_OOM;
   }
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  MemBook& b = mem_book();
+  std::lock_guard<std::mutex> lock(b.mu);
+  b.blocks[*p] = {dev, sz};
+  int64_t& live = b.live[dev];
+  live += int64_t(sz);
+  int64_t& peak = b.peak[dev];
+  if (live > peak) peak = live;
   return SLA_OK;
 }
 
 void dev_free(void* p) {
-  if (p) (void)hipFree(p);
+  if (!p) return;
+  {
+    MemBook& b = mem_book();
+    std::lock_guard<std::mutex> lock(b.mu);
+    auto it = b.blocks.find(p);
+    if (it != b.blocks.end()) {
+      b.live[it->second.first] -= int64_t(it->second.second);
+      b.blocks.erase(it);
+    }
+  }
+  (void)hipFree(p);
+}
+
+void memory_usage(int dev, int64_t* live, int64_t* peak, bool reset) {
+  MemBook& b = mem_book();
+  std::lock_guard<std::mutex> lock(b.mu);
+  const int64_t l = b.live.count(dev) ? b.live[dev] : 0;
+  if (live) *live = l;
+  if (peak) *peak = b.peak.count(dev) ? b.peak[dev] : 0;
+  if (reset) b.peak[dev] = l;
 }
 
 int device_cus() {
@@ -99,6 +142,8 @@ void free_handle(sla_csr A) {
   dev_free(A->sorted_idx);
   dev_free(A->grp);
   dev_free(A->band_mask);
+  dev_free(A->vals_owned);
+  dev_free(A->sym_flag);
   delete A;
 }
 }  // namespace sla
@@ -120,6 +165,7 @@ const char* sla_status_string(sla_status s) {
     case SLA_ERR_NONFINITE: return "SLA_ERR_NONFINITE";
     case SLA_ERR_KRYLOV: return "SLA_ERR_KRYLOV";
     case SLA_ERR_BREAKDOWN: return "SLA_ERR_BREAKDOWN";
+    case SLA_ERR_NOT_SYMMETRIC: return "SLA_ERR_NOT_SYMMETRIC";
   }
   return "SLA_UNKNOWN";
 }
@@ -261,9 +307,76 @@ sla_status sla_csr_set_values(sla_csr A, const double* vals, int64_t batch) {
   REQUIRE(A != nullptr, "sla_csr_set_values: NULL handle");
   REQUIRE(batch >= 1 && batch <= 65535, "sla_csr_set_values: batch out of range");
   REQUIRE(A->nnz == 0 || vals != nullptr, "sla_csr_set_values: NULL values");
+  REQUIRE(vals == nullptr || vals != A->vals_owned || batch <= A->owned_batch,
+          "sla_csr_set_values: the handle's own values hold %lld systems",
+          (long long)A->owned_batch);
   A->vals = vals;
   A->batch = batch;
   return SLA_OK;
+}
+
+sla_status sla_csr_load_values(sla_csr A, const double* vals, int64_t batch, int order,
+                               hipStream_t stream) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_load_values: NULL handle");
+  REQUIRE(batch >= 1 && batch <= 65535, "sla_csr_load_values: batch out of range");
+  REQUIRE(order == SLA_VALUES_CSR || order == SLA_VALUES_COO,
+          "sla_csr_load_values: bad order %d", order);
+  REQUIRE(order == SLA_VALUES_CSR || A->perm != nullptr,
+          "sla_csr_load_values: COO values need a handle built from COO");
+  const int64_t len = order == SLA_VALUES_CSR ? A->nnz : A->nnz_coo;
+  REQUIRE(len == 0 || vals != nullptr, "sla_csr_load_values: NULL values");
+  REQUIRE(vals == nullptr || A->vals_owned == nullptr || vals != A->vals_owned,
+          "sla_csr_load_values: the source is the handle's own array");
+  if (A->vals_owned == nullptr || A->owned_batch != batch) {
+    if (A->vals_owned != nullptr) {
+      // the old copy may still be read by queued work
+      SLA_TRY_HIP(hipStreamSynchronize(stream));
+      if (A->vals == A->vals_owned) {
+        A->vals = nullptr;
+        A->batch = 0;
+      }
+      dev_free(A->vals_owned);
+      A->vals_owned = nullptr;
+      A->owned_batch = 0;
+    }
+    SLA_TRY(dev_alloc(&A->vals_owned, size_t(batch) * size_t(A->nnz > 0 ? A->nnz : 1),
+                      "the handle's values"));
+    A->owned_batch = batch;
+  }
+  if (order == SLA_VALUES_CSR) {
+    if (A->nnz > 0)
+      SLA_TRY_HIP(hipMemcpyAsync(A->vals_owned, vals, sizeof(double) * size_t(batch) * A->nnz,
+                                 hipMemcpyDeviceToDevice, stream));
+  } else {
+    SLA_TRY(launch_values_from_coo(A, vals, A->vals_owned, batch, stream));
+  }
+  A->vals = A->vals_owned;
+  A->batch = batch;
+  return SLA_OK;
+  API_END
+}
+
+sla_status sla_csr_arrays(sla_csr A, const void** rowptr, const int32_t** col, double** vals,
+                          const int64_t** perm) {
+  clear_error();
+  REQUIRE(A != nullptr, "sla_csr_arrays: NULL handle");
+  if (rowptr) *rowptr = A->rowptr;
+  if (col) *col = A->col;
+  if (vals) *vals = const_cast<double*>(A->vals);
+  if (perm) *perm = A->perm;
+  return SLA_OK;
+}
+
+sla_status sla_memory_usage(int64_t* live_host, int64_t* peak_host, int reset_peak) {
+  API_BEGIN
+  clear_error();
+  int dev = 0;
+  SLA_TRY_HIP(hipGetDevice(&dev));
+  memory_usage(dev, live_host, peak_host, reset_peak != 0);
+  return SLA_OK;
+  API_END
 }
 
 sla_status sla_spmv(sla_csr A, const double* x, double* y, hipStream_t stream) {
@@ -344,11 +457,54 @@ static sla_status check_solve(sla_csr A, const void* b, const void* x, double to
   return SLA_OK;
 }
 
+// CG needs A^T = A.  The pattern's symmetry is checked once per handle (the
+// first CG call); a handle whose pattern is not symmetric is refused by
+// every CG solve and adjoint.  The adjoint, which solves with A in place of
+// A^T, also checks the bound values bit for bit on every call.
+static sla_status require_symmetric(sla_csr A, bool values, const char* who,
+                                    hipStream_t stream) {
+  if (A->sym_pattern < 0) {
+    int bad = 0;
+    SLA_TRY(check_symmetry(A, false, &bad, stream));
+    A->sym_pattern = (bad & 1) ? 0 : 1;
+  }
+  if (!A->sym_pattern) {
+    set_error("%s: the pattern is not symmetric (a stored (i, j) without (j, i)); CG needs "
+              "A^T = A (BiCGStab takes general matrices)", who);
+    return SLA_ERR_NOT_SYMMETRIC;
+  }
+  if (values) {
+    int bad = 0;
+    SLA_TRY(check_symmetry(A, true, &bad, stream));
+    if (bad) {
+      set_error("%s: the values are not symmetric (a_ij != a_ji bit for bit); the adjoint "
+                "solves with A in place of A^T", who);
+      return SLA_ERR_NOT_SYMMETRIC;
+    }
+  }
+  return SLA_OK;
+}
+
+static void fill_status(sla_cg_info* info, int64_t batch, sla_status s) {
+  if (!info) return;
+  for (int64_t i = 0; i < batch; ++i) {
+    info[i].iterations = 0;
+    info[i].rel_residual = 0.0;
+    info[i].converged = 0;
+    info[i].status = s;
+  }
+}
+
 sla_status sla_cg_solve_batched(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
                                 uint32_t flags, sla_cg_info* info, hipStream_t stream) {
   API_BEGIN
   clear_error();
   SLA_TRY(check_solve(A, b, x, tol, maxit, flags, "sla_cg_solve_batched"));
+  const sla_status sym = require_symmetric(A, false, "sla_cg_solve_batched", stream);
+  if (sym != SLA_OK) {
+    fill_status(info, A->batch, sym);
+    return sym;
+  }
   return run_cg_any(A, b, x, tol, maxit, flags, info, stream);
   API_END
 }
@@ -360,16 +516,27 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol, int64
   SLA_TRY(check_solve(A, b, x, tol, maxit, flags, "sla_cg_solve"));
   REQUIRE(A->batch == 1, "sla_cg_solve: %lld systems bound; use sla_cg_solve_batched",
           (long long)A->batch);
+  const sla_status sym = require_symmetric(A, false, "sla_cg_solve", stream);
+  if (sym != SLA_OK) {
+    fill_status(info, 1, sym);
+    return sym;
+  }
   return run_cg_any(A, b, x, tol, maxit, flags, info, stream);
   API_END
 }
 
-// A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix), then
-// the pattern gradient (also from the last iterate after a breakdown), on
-// A's own slots whether or not the solve ran on a reordered copy.
+// A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix; checked
+// first), then the pattern gradient (also from the last iterate after a
+// breakdown), on A's own slots whether or not the solve ran on a reordered
+// copy.
 static sla_status run_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  const sla_status sym = require_symmetric(A, true, "sla_cg_adjoint", stream);
+  if (sym != SLA_OK) {
+    fill_status(info, A->batch, sym);
+    return sym;
+  }
   sla_status s = run_cg_any(A, grad_x, grad_b, tol, maxit, flags, info, stream);
   if (grad_vals != nullptr && (s == SLA_OK || s == SLA_ERR_NOT_SPD || s == SLA_ERR_NONFINITE)) {
     sla_status g = launch_pattern_grad(A, A->batch, grad_b, x, grad_vals, stream);
@@ -505,8 +672,15 @@ sla_status sla_solve_list(int64_t count, const sla_csr* A, const double* const* 
   for (int64_t i = 0; i < count; ++i)
     SLA_TRY(check_solve(A[i], b[i], x[i], tol, maxit, flags, "sla_solve_list"));
   return run_list(count, info, stream, [&](int64_t i, hipStream_t st, sla_cg_info* in) {
-    return method == SLA_METHOD_CG ? run_cg_any(A[i], b[i], x[i], tol, maxit, flags, in, st)
-                                   : run_bicgstab_any(A[i], b[i], x[i], tol, maxit, flags, in, st);
+    if (method == SLA_METHOD_CG) {
+      const sla_status sym = require_symmetric(A[i], false, "sla_solve_list", st);
+      if (sym != SLA_OK) {
+        fill_status(in, 1, sym);
+        return sym;
+      }
+      return run_cg_any(A[i], b[i], x[i], tol, maxit, flags, in, st);
+    }
+    return run_bicgstab_any(A[i], b[i], x[i], tol, maxit, flags, in, st);
   });
   API_END
 }

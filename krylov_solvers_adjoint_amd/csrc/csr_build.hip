@@ -728,7 +728,67 @@ __global__ __launch_bounds__(kIterBlock) void k_spmv_transpose(
   }
 }
 
+// Symmetry: every stored (i, j) must have its mirror (j, i) stored, found by
+// a binary search of row j's ascending columns; with values, the two slots
+// must hold the same bits in every system.  One thread per row (a row's
+// slots in turn), bit 0 of *bad for a missing mirror, bit 1 for unequal
+// values.  Both slots of a pair are visited, each finding the other.
+template <typename RP>
+__global__ void k_symmetry(int64_t n, int64_t nnz, const RP* __restrict__ rowptr,
+                           const int32_t* __restrict__ col, const double* __restrict__ vals,
+                           int64_t batch, int* __restrict__ bad) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t a = rowptr[i], e = rowptr[i + 1];
+    for (int64_t k = a; k < e; ++k) {
+      const int64_t j = col[k];
+      if (j == i) continue;
+      const int64_t ja = rowptr[j], je = rowptr[j + 1];
+      int64_t lo = ja, hi = je;
+      while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (int64_t(col[mid]) < i) lo = mid + 1;
+        else hi = mid;
+      }
+      if (lo == je || int64_t(col[lo]) != i) {
+        atomicOr(bad, 1);
+        continue;
+      }
+      if (vals == nullptr) continue;
+      for (int64_t s = 0; s < batch; ++s) {
+        const unsigned long long u = __double_as_longlong(vals[s * nnz + k]);
+        const unsigned long long w = __double_as_longlong(vals[s * nnz + lo]);
+        if (u != w) {
+          atomicOr(bad, 2);
+          break;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
+
+sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t st) {
+  *bad = 0;
+  if (A->nnz == 0) return SLA_OK;
+  if (A->sym_flag == nullptr) SLA_TRY(dev_alloc(&A->sym_flag, 1, "symmetry flag"));
+  const double* v = values ? A->vals : nullptr;
+  const int64_t batch = values ? A->batch : 0;
+  SLA_TRY_HIP(hipMemsetAsync(A->sym_flag, 0, sizeof(int), st));
+  if (A->rp_idx == SLA_I32)
+    k_symmetry<int32_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, A->nnz, (const int32_t*)A->rowptr,
+                                                           A->col, v, batch, A->sym_flag);
+  else
+    k_symmetry<int64_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, A->nnz, (const int64_t*)A->rowptr,
+                                                           A->col, v, batch, A->sym_flag);
+  LAUNCH_CHECK();
+  int h = 0;
+  SLA_TRY_HIP(hipMemcpyAsync(&h, A->sym_flag, sizeof(int), hipMemcpyDeviceToHost, st));
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  *bad = h;
+  return SLA_OK;
+}
 
 sla_status analyse_pattern(sla_csr A, hipStream_t st) {
   A->tiles = (A->n + kTileRows - 1) / kTileRows;

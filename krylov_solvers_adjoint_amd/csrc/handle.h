@@ -40,9 +40,16 @@ struct sla_csr_s {
   bool wide_cols = false;        // sampled tiles reach columns far apart
   int32_t pblock = 0;
 
-  // bound values (borrowed)
+  // bound values: the caller's array (sla_csr_set_values) or the handle's
+  // own copy (sla_csr_load_values), [batch][nnz] in CSR slot order
   const double* vals = nullptr;
   int64_t batch = 0;
+  double* vals_owned = nullptr;  // the handle's copy, [owned_batch][nnz]
+  int64_t owned_batch = 0;
+
+  // symmetry of the pattern (CG needs A^T = A): -1 not yet checked, 0 no, 1 yes
+  int sym_pattern = -1;
+  int* sym_flag = nullptr;  // device word of the symmetry checks
 
   // the transposed pattern, built on first use by the transposed product:
   // a handle of its own whose COO triplets are this pattern's slots with
@@ -111,6 +118,11 @@ sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const
 void release_workspace(sla_csr A);
 void free_handle(sla_csr A);  // the handle, its workspace and its transposed pattern
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
+// Symmetry of the pattern and, with values = true, of the bound values of
+// every system (bit for bit): *bad gets bit 0 for a stored (i, j) whose
+// mirror (j, i) is not stored, bit 1 for a mirror pair with different values.
+// Synchronises `stream` (csr_build.hip).
+sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t stream);
 
 sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x,
                        double* y, hipStream_t stream);

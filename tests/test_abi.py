@@ -69,4 +69,11 @@ def test_argument_errors_need_no_gpu():
     assert lib.sla_csr_ordering(None, None, None) == K.ERR_ARG
     assert lib.sla_csr_set_one_group(None, K.ONE_GROUP_AUTO) == K.ERR_ARG
     assert lib.sla_status_string(K.ERR_NOT_SPD) == b"SLA_ERR_NOT_SPD"
+    assert lib.sla_status_string(K.ERR_NOT_SYMMETRIC) == b"SLA_ERR_NOT_SYMMETRIC"
+    # the borrowed views and the owned values copy
+    rp, c, v, pm = (ctypes.c_void_p() for _ in range(4))
+    assert lib.sla_csr_arrays(None, ctypes.byref(rp), ctypes.byref(c), ctypes.byref(v),
+                              ctypes.byref(pm)) == K.ERR_ARG
+    assert b"NULL handle" in lib.sla_last_error()
+    assert lib.sla_csr_load_values(None, None, 1, K.VALUES_CSR, None) == K.ERR_ARG
     assert lib.sla_csr_destroy(None) == K.OK
