@@ -254,9 +254,11 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol,
  * may be NULL (then only grad_b).  Memory: O(n + nnz), independent of the
  * iteration count.  Same stopping rule and statuses as sla_cg_solve.  Since
  * the solve uses A in place of A^T, every call first checks the bound values
- * (each stored a_ij against a_ji, bit for bit, one pass over the values);
- * a mismatch returns SLA_ERR_NOT_SYMMETRIC before any iteration (grad_b and
- * grad_vals untouched).
+ * (each stored a_ij against a_ji, one pass over the values; equal, or within
+ * 1e-12 of the larger magnitude, as symmetric expressions such as D A D
+ * round mirror entries a few ulps apart); a mismatch returns
+ * SLA_ERR_NOT_SYMMETRIC before any iteration (grad_b and grad_vals
+ * untouched).
  */
 sla_status sla_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
                           double* grad_b, double* grad_vals, double tol,

@@ -460,7 +460,8 @@ static sla_status check_solve(sla_csr A, const void* b, const void* x, double to
 // CG needs A^T = A.  The pattern's symmetry is checked once per handle (the
 // first CG call); a handle whose pattern is not symmetric is refused by
 // every CG solve and adjoint.  The adjoint, which solves with A in place of
-// A^T, also checks the bound values bit for bit on every call.
+// A^T, also checks the bound values on every call (mirror entries equal to
+// within 1e-12 relative).
 static sla_status require_symmetric(sla_csr A, bool values, const char* who,
                                     hipStream_t stream) {
   if (A->sym_pattern < 0) {
@@ -477,8 +478,8 @@ static sla_status require_symmetric(sla_csr A, bool values, const char* who,
     int bad = 0;
     SLA_TRY(check_symmetry(A, true, &bad, stream));
     if (bad) {
-      set_error("%s: the values are not symmetric (a_ij != a_ji bit for bit); the adjoint "
-                "solves with A in place of A^T", who);
+      set_error("%s: the values are not symmetric (a_ij and a_ji differ by more than 1e-12 "
+                "relative); the adjoint solves with A in place of A^T", who);
       return SLA_ERR_NOT_SYMMETRIC;
     }
   }

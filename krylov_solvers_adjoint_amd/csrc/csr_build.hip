@@ -730,9 +730,13 @@ __global__ __launch_bounds__(kIterBlock) void k_spmv_transpose(
 
 // Symmetry: every stored (i, j) must have its mirror (j, i) stored, found by
 // a binary search of row j's ascending columns; with values, the two slots
-// must hold the same bits in every system.  One thread per row (a row's
+// must hold the same value in every system: equal, or within 1e-12 of the
+// larger magnitude (symmetric expressions such as D A D round the two
+// mirror entries differently by a few ulps).  One thread per row (a row's
 // slots in turn), bit 0 of *bad for a missing mirror, bit 1 for unequal
 // values.  Both slots of a pair are visited, each finding the other.
+constexpr double kSymRel = 1e-12;
+
 template <typename RP>
 __global__ void k_symmetry(int64_t n, int64_t nnz, const RP* __restrict__ rowptr,
                            const int32_t* __restrict__ col, const double* __restrict__ vals,
@@ -756,9 +760,10 @@ __global__ void k_symmetry(int64_t n, int64_t nnz, const RP* __restrict__ rowptr
       }
       if (vals == nullptr) continue;
       for (int64_t s = 0; s < batch; ++s) {
-        const unsigned long long u = __double_as_longlong(vals[s * nnz + k]);
-        const unsigned long long w = __double_as_longlong(vals[s * nnz + lo]);
-        if (u != w) {
+        const double u = vals[s * nnz + k], w = vals[s * nnz + lo];
+        if (__double_as_longlong(u) == __double_as_longlong(w)) continue;
+        const double m = fabs(u) > fabs(w) ? fabs(u) : fabs(w);
+        if (!(fabs(u - w) <= kSymRel * m)) {
           atomicOr(bad, 2);
           break;
         }

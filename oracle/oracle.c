@@ -298,12 +298,25 @@ int oracle_cg(int64_t n, const int64_t* rowptr, const int32_t* col,
 /* ------------------------------------------------------------------------ */
 
 /*
+ * Two stored values count as the same entry of a symmetric matrix when they
+ * are equal or differ by at most 1e-12 of the larger magnitude: symmetric
+ * expressions such as D A D round the two mirror entries differently by a
+ * few ulps, far below what changes a CG solve.
+ */
+static int same_entry(double a, double b) {
+  if (memcmp(&a, &b, sizeof(double)) == 0) return 1;
+  double m = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
+  return fabs(a - b) <= 1e-12 * m;
+}
+
+/*
  * Backward pass of x = A^{-1} b for a loss L with g = dL/dx:
  *   A^T lambda = g          (solved by the same CG, on an explicit A^T)
  *   grad_b     = lambda
  *   grad_A     = -lambda_i x_j for every stored slot (i, j), nothing else.
  * Returns the CG status; ORACLE_ERR_NOT_SYMMETRIC if A^T differs from A
- * (CG needs a symmetric matrix; the solve is still done on A^T).
+ * (pattern, or values beyond same_entry) (CG needs a symmetric matrix; the
+ * solve is still done on A^T).
  */
 int oracle_adjoint(int64_t n, const int64_t* rowptr, const int32_t* col,
                    const double* vals, const double* x, const double* g,
@@ -318,8 +331,7 @@ int oracle_adjoint(int64_t n, const int64_t* rowptr, const int32_t* col,
   for (int64_t i = 0; i <= n && symmetric; ++i)
     if (rowptr_t[i] != rowptr[i]) symmetric = 0;
   for (int64_t k = 0; k < nnz && symmetric; ++k)
-    if (col_t[k] != col[k] || memcmp(&vals_t[k], &vals[k], sizeof(double)) != 0)
-      symmetric = 0;
+    if (col_t[k] != col[k] || !same_entry(vals_t[k], vals[k])) symmetric = 0;
 
   int status = oracle_cg(n, rowptr_t, col_t, vals_t, g, grad_b, tol, maxit, 0,
                          info, NULL, NULL, NULL);
@@ -468,8 +480,7 @@ int oracle_adjoint_jacobi(int64_t n, const int64_t* rowptr, const int32_t* col,
   for (int64_t i = 0; i <= n && symmetric; ++i)
     if (rowptr_t[i] != rowptr[i]) symmetric = 0;
   for (int64_t k = 0; k < nnz && symmetric; ++k)
-    if (col_t[k] != col[k] || memcmp(&vals_t[k], &vals[k], sizeof(double)) != 0)
-      symmetric = 0;
+    if (col_t[k] != col[k] || !same_entry(vals_t[k], vals[k])) symmetric = 0;
   int status = oracle_pcg_jacobi(n, rowptr_t, col_t, vals_t, g, grad_b, tol, maxit, 0,
                                  info, NULL, NULL, NULL, NULL);
   oracle_pattern_grad(n, rowptr, col, grad_b, x, grad_vals);

@@ -440,6 +440,28 @@ def pin_adjoint_nonsymmetric_flag(lib=None):
     assert info.status == oracle.ERR_NOT_SYMMETRIC
     # the gradient is still -lambda_i x_j on the four stored slots
     assert np.array_equal(gv, -(np.repeat(gb, 2) * x[[0, 1, 0, 1]]))
+    # D A D of a symmetric A: mirror entries (a s_i) s_j and (a s_j) s_i round
+    # apart by a few ulps and still count as symmetric; a relative change of
+    # 1e-9 in one entry does not
+    N = 12
+    rp, c, v = W.poisson_csr(N, np.int64)
+    rows = np.repeat(np.arange(N * N), np.diff(rp))
+    s = np.exp(np.random.default_rng(40).uniform(-3.0, 3.0, N * N))
+    vs = (1.1 * v) * s[rows] * s[c]
+    mirror = {(int(i), int(j)): k for k, (i, j) in enumerate(zip(rows, c))}
+    assert any(vs[k] != vs[mirror[(int(j), int(i))]] for k, (i, j) in enumerate(zip(rows, c)))
+    A = oracle.CSR(N * N, rp, c, vs)
+    b = W.normal_rhs(N * N, 41)
+    xd, _ = oracle.cg(A, b, 1e-12, 1000, lib=lib)
+    _, _, info = oracle.adjoint(A, xd, b, 1e-12, 1000, lib=lib)
+    assert info.status == oracle.OK
+    _, _, info = oracle.adjoint_jacobi(A, xd, b, 1e-12, 1000, lib=lib)
+    assert info.status == oracle.OK
+    off = int(np.flatnonzero(rows != c)[7])
+    vb = vs.copy()
+    vb[off] = vb[off] * (1.0 + 1e-9)
+    _, _, info = oracle.adjoint(oracle.CSR(N * N, rp, c, vb), xd, b, 1e-12, 1000, lib=lib)
+    assert info.status == oracle.ERR_NOT_SYMMETRIC
 
 
 # --------------------------------------------------------------------------
