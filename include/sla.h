@@ -247,6 +247,32 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol,
                         hipStream_t stream);
 
 /*
+ * sla_cg_solve for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same CG iteration as sla_cg_solve on the same handle (the same
+ * kernels and grid, so the same results bit for bit), with its workspace
+ * (r, p, q, partials, scalars) in a static device array of the library
+ * instead of the handle's: 64 MiB, which every GPU the library runs on holds
+ * until the process ends (not counted by sla_memory_usage).  The call
+ * allocates nothing; the caller still provides b and x (device memory).
+ * Kernels are launched one by one (no graphs, no events) and the host waits
+ * for `stream` every 32 iterations to read the running count.
+ * Limits: exactly one system bound; 4 n + 7 G doubles of scratch (G the
+ * solver grid) within the 64 MiB, i.e. n up to about 2.09 million unknowns
+ * (larger n returns SLA_ERR_ARG, message giving the limit); flags
+ * SLA_FLAG_X0 only; a handle without a locality ordering.  The first call
+ * on a device looks up the array's address there (set-up).
+ * Every call on one GPU shares that GPU's array and overwrites what the last
+ * call left in it: calls that overlap on one GPU (other host threads, other
+ * streams) race and give wrong results.  Statuses as sla_cg_solve (a pattern
+ * that is not symmetric returns SLA_ERR_NOT_SYMMETRIC).  Synchronises
+ * `stream`.
+ */
+sla_status sla_cg_solve_noalloc(sla_csr A, const double* b, double* x, double tol,
+                                int64_t maxit, uint32_t flags, sla_cg_info* info_host,
+                                hipStream_t stream);
+
+/*
  * Backward pass of x = A^{-1} b (Methodology 2, linear systems): given x and
  * grad_x = dL/dx, solve A^T lambda = grad_x by the same CG (A^T = A for the
  * SPD matrices CG accepts), write grad_b = lambda and

@@ -59,7 +59,7 @@ EXPORTS = [
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_solve_list", "sla_adjoint_list", "sla_csr_reorder", "sla_csr_ordering",
     "sla_csr_set_one_group", "sla_csr_load_values", "sla_csr_arrays", "sla_memory_usage",
-    "sla_last_error", "sla_status_string",
+    "sla_cg_solve_noalloc", "sla_last_error", "sla_status_string",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -125,6 +125,7 @@ def _bind(lib):
         "sla_csr_arrays": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
                            ctypes.POINTER(_P)],
         "sla_memory_usage": [ctypes.POINTER(_I64), ctypes.POINTER(_I64), _S],
+        "sla_cg_solve_noalloc": [_P, _P, _P, _D, _I64, _U32, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -541,6 +542,19 @@ def sla_cg_solve(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: floa
     flags = _flags(x0, history, jacobi)
     st, infos = _solve_call(_lib.sla_cg_solve, A, b, x, tol, maxit, flags, 1, stream, check)
     return x, infos[0]
+
+
+def sla_cg_solve_noalloc(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, x: torch.Tensor,
+                         tol: float, maxit: int, x0: bool = False, stream=None,
+                         check: bool = True):
+    """CGInfo of sla_cg_solve_noalloc: the solve of sla_cg_solve writing into
+    the caller's x (its start vector when x0), with the library's static
+    scratch as workspace; nothing is allocated (x must be given)."""
+    if A.bind(values) != 1:
+        raise ValueError("sla_cg_solve_noalloc takes one system")
+    st, infos = _solve_call(_lib.sla_cg_solve_noalloc, A, b, x, tol, maxit,
+                            FLAG_X0 if x0 else 0, 1, stream, check)
+    return infos[0]
 
 
 def sla_cg_solve_batched(A: CSRPattern, values: torch.Tensor, b: torch.Tensor, tol: float,

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsla.so")
-SOURCES = ["api.hip", "csr_build.hip", "cg.hip", "lanczos.hip", "bicgstab.hip", "reorder.hip"]
+SOURCES = ["api.hip", "csr_build.hip", "cg.hip", "lanczos.hip", "bicgstab.hip", "reorder.hip",
+           "noalloc.hip"]
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

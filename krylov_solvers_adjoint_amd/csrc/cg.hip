@@ -48,6 +48,8 @@
 #include "handle.h"
 
 namespace sla {
+CgSpace own_space(sla_csr A);  // the handle's own workspace as a space
+
 namespace {
 
 // Slots a lane gathers at a time in a plain CSR tile (two rounds cover the
@@ -1726,8 +1728,8 @@ bool wide_vectors(const sla_csr A) { return uint64_t(A->n) * sizeof(double) >= (
 // Line-walk chunks per XCD, so that every workgroup of an XCD gets the same
 // number of (kLineWaves-column group, chunk) units: per_xcd / gcd(groups,
 // per_xcd).
-int64_t line_chunks(const sla_csr A) {
-  const int64_t per_xcd = A->grid / kXcds;
+int64_t line_chunks(const sla_csr A, int32_t grid) {
+  const int64_t per_xcd = grid / kXcds;
   const int64_t U = (A->line + kTileRows - 1) / kTileRows;
   const int64_t groups = (U + kLineWaves - 1) / kLineWaves;
   int64_t a = per_xcd, b = groups;
@@ -1740,9 +1742,9 @@ int64_t line_chunks(const sla_csr A) {
 }
 
 // Lines a wave walks in one chunk (about).
-int64_t line_chunk_lines(const sla_csr A) {
+int64_t line_chunk_lines(const sla_csr A, int32_t grid) {
   const int64_t V = (A->n + A->line - 1) / A->line;
-  return V / kXcds / std::max<int64_t>(1, line_chunks(A));
+  return V / kXcds / std::max<int64_t>(1, line_chunks(A, grid));
 }
 
 int band_class(const sla_csr A) {
@@ -1751,7 +1753,7 @@ int band_class(const sla_csr A) {
 }
 
 template <typename RP>
-const void* spmv_step_kernel(const sla_csr A) {
+const void* spmv_step_kernel(const sla_csr A, int32_t grid) {
   const int nb = band_class(A);
   if (use_lines(A)) {
     // NEAR1: the offsets between -L and +L are only -1, 0, +1
@@ -1760,7 +1762,7 @@ const void* spmv_step_kernel(const sla_csr A) {
       near1 = near1 && A->band.off[t] >= -1 && A->band.off[t] <= 1;
     // the two-deep pipeline pays off once a wave walks a dozen lines or more,
     // on matrices whose vectors stay partly in the Infinity Cache
-    if (line_chunk_lines(A) >= kPipeLines && A->n <= kPipeMaxRows) {
+    if (line_chunk_lines(A, grid) >= kPipeLines && A->n <= kPipeMaxRows) {
       if (near1 && nb <= 5)
         return nb == 3 ? reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 3, true, true>)
                        : reinterpret_cast<const void*>(&k_cg_spmv_lines<RP, 5, true, true>);
@@ -1809,26 +1811,28 @@ sla_status launch_ctx_kernel(const void* fn, dim3 grid, unsigned block, size_t l
 }
 
 template <typename RP>
-sla_status enqueue_iteration(sla_csr A, int64_t batch, bool jacobi, hipStream_t st) {
-  const dim3 grid2(unsigned(A->grid), unsigned(batch));
+sla_status enqueue_iteration(sla_csr A, const CgSpace& sp, int64_t batch, bool jacobi,
+                             hipStream_t st) {
+  const dim3 grid2(unsigned(sp.grid), unsigned(batch));
   if (use_split(A)) {
-    k_cg_direction<<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
-    SLA_TRY(launch_ctx_kernel(product_kernel<RP>(A), grid2, kIterBlock, lds_bytes(A), A->ctx_dev,
+    k_cg_direction<<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev);
+    SLA_TRY(launch_ctx_kernel(product_kernel<RP>(A), grid2, kIterBlock, lds_bytes(A), sp.ctx_dev,
                               st));
   } else {
-    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A), grid2, spmv_step_block(A), lds_bytes(A),
-                              A->ctx_dev, st));
+    SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A, sp.grid), grid2, spmv_step_block(A),
+                              lds_bytes(A), sp.ctx_dev, st));
   }
-  if (jacobi) k_cg_residual<true><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
-  else k_cg_residual<false><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev);
+  if (jacobi) k_cg_residual<true><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev);
+  else k_cg_residual<false><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev);
   LAUNCH_CHECK();
   return SLA_OK;
 }
 
-sla_status enqueue_block(sla_csr A, int64_t batch, bool jacobi, int64_t iters, hipStream_t st) {
+sla_status enqueue_block(sla_csr A, const CgSpace& sp, int64_t batch, bool jacobi,
+                         int64_t iters, hipStream_t st) {
   for (int64_t k = 0; k < iters; ++k) {
-    if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, batch, jacobi, st));
-    else SLA_TRY(enqueue_iteration<int64_t>(A, batch, jacobi, st));
+    if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, sp, batch, jacobi, st));
+    else SLA_TRY(enqueue_iteration<int64_t>(A, sp, batch, jacobi, st));
   }
   return SLA_OK;
 }
@@ -1846,7 +1850,7 @@ sla_status get_graph(sla_csr A, int64_t batch, bool jacobi, hipGraphExec_t* exec
   hipGraph_t g = nullptr;
   hipGraphExec_t e = nullptr;
   SLA_TRY_HIP(hipStreamBeginCapture(A->capture_stream, hipStreamCaptureModeThreadLocal));
-  sla_status s = enqueue_block(A, batch, jacobi, A->graph_block, A->capture_stream);
+  sla_status s = enqueue_block(A, own_space(A), batch, jacobi, A->graph_block, A->capture_stream);
   hipError_t he = hipStreamEndCapture(A->capture_stream, &g);
   if (s != SLA_OK) {
     if (g) (void)hipGraphDestroy(g);
@@ -1875,40 +1879,40 @@ void drop_graphs(sla_csr A) {
   A->graphs.clear();
 }
 
-void fill_ctx(sla_csr A, Ctx& c, const double* b, double* x, int64_t batch, bool hist,
-              bool jacobi = false) {
+void fill_ctx(sla_csr A, const CgSpace& sp, Ctx& c, const double* b, double* x, int64_t batch,
+              bool hist, bool jacobi = false) {
   c = Ctx{};
   c.rowptr = A->rowptr;
   c.col = A->col;
   c.vals = A->vals;
   c.x = x;
   c.b = b;
-  c.r = A->r;
+  c.r = sp.r;
   c.jacobi = jacobi ? 1 : 0;
   c.diag = jacobi ? A->jdiag : nullptr;
   c.z = jacobi ? A->jz : nullptr;
   c.bad = jacobi ? A->jbad : nullptr;
-  c.rd = jacobi ? A->jz : A->r;
-  c.p[0] = A->p0;
-  c.p[1] = A->p1;
-  c.q = A->q;
-  c.part = A->part;
-  c.scal = A->scal;
+  c.rd = jacobi ? A->jz : sp.r;
+  c.p[0] = sp.p0;
+  c.p[1] = sp.p1;
+  c.q = sp.q;
+  c.part = sp.part;
+  c.scal = scal_of(sp.ctx_dev, 0);
   c.hist = hist ? A->hist : nullptr;
   c.hist_cap = hist ? A->hist_cap : 0;
-  c.n_running = A->n_running;
+  c.n_running = sp.n_running;
   c.n = A->n;
   c.nnz = A->nnz;
   c.batch = batch;
   c.tiles = A->tiles;
-  c.grid = A->grid;
+  c.grid = sp.grid;
   c.wave_cap = A->wave_cap;
   c.mask = use_band(A) ? A->band_mask : nullptr;
   c.band = A->band;
   c.panel = A->panel;
   c.pblock = A->pblock;
   c.line = use_lines(A) ? A->line : 0;
-  c.line_chunks = c.line > 0 ? line_chunks(A) : 0;
+  c.line_chunks = c.line > 0 ? line_chunks(A, sp.grid) : 0;
   c.xpair = c.line > 0 ? 1 : 0;
 }
 
@@ -1977,23 +1981,45 @@ void release_workspace(sla_csr A) {
   A->hist_cap = A->hist_batch = 0;
 }
 
-sla_status ensure_workspace(sla_csr A, int64_t batch) {
-  if (A->ws_batch == batch && A->r != nullptr) return SLA_OK;
-  release_workspace(A);
-  const int64_t n = A->n;
-  // solver grid: wg_per_cu workgroups per CU in total, a multiple of the XCD
-  // count per system, never more than the wave tiles need (rounded up)
-  // (automatic: one per CU up to kSmallSolve unknowns over the batch, where
-  // the kernels' fixed costs -- each workgroup summing the partials of the
-  // previous kernel -- weigh more than the latency hiding of a second one)
-  // (and for line walks at any size: their waves stream long chunks, and
-  // with half the workgroups each chunk is twice as long)
+// Solver grid: wg_per_cu workgroups per CU in total, a multiple of the XCD
+// count per system, never more than the wave tiles need (rounded up)
+// (automatic: one per CU up to kSmallSolve unknowns over the batch, where
+// the kernels' fixed costs -- each workgroup summing the partials of the
+// previous kernel -- weigh more than the latency hiding of a second one)
+// (and for line walks at any size: their waves stream long chunks, and
+// with half the workgroups each chunk is twice as long)
+int32_t solver_grid(const sla_csr A, int64_t batch) {
   const int wg = A->wg_per_cu > 0 ? A->wg_per_cu
                                   : (A->n * batch <= kSmallSolve || use_lines(A) ? 1 : 2);
   const int64_t target = std::max<int64_t>(kXcds, int64_t(device_cus()) * wg / batch);
   int64_t g = std::min<int64_t>((A->tiles + kWaves - 1) / kWaves, target);
   g = (g + kXcds - 1) / kXcds * kXcds;
-  A->grid = int32_t(std::max<int64_t>(g, kXcds));
+  return int32_t(std::max<int64_t>(g, kXcds));
+}
+
+CgSpace own_space(sla_csr A) {
+  CgSpace sp;
+  sp.r = A->r;
+  sp.p0 = A->p0;
+  sp.p1 = A->p1;
+  sp.q = A->q;
+  sp.part = A->part;
+  sp.ctx_dev = A->ctx_dev;
+  sp.n_running = A->n_running;
+  sp.ctx_host = A->ctx_host;
+  sp.scal_host = A->scal_host;
+  sp.poll_host = A->poll_host;
+  sp.poll_ev = A->poll_ev;
+  sp.grid = A->grid;
+  sp.own = true;
+  return sp;
+}
+
+sla_status ensure_workspace(sla_csr A, int64_t batch) {
+  if (A->ws_batch == batch && A->r != nullptr) return SLA_OK;
+  release_workspace(A);
+  const int64_t n = A->n;
+  A->grid = solver_grid(A, batch);
   const size_t vec = size_t(batch) * size_t(n);
   SLA_TRY(dev_alloc(&A->r, vec, "r"));
   SLA_TRY(dev_alloc(&A->p0, vec, "p"));
@@ -2090,7 +2116,8 @@ sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda, c
   return launch_slot_products(A, batch, lambda, x, grad_vals, true, st);
 }
 
-static sla_status finish_cg(sla_csr A, int64_t batch, sla_cg_info* info, hipStream_t st);
+static sla_status finish_cg(const CgSpace& sp, int64_t batch, sla_cg_info* info,
+                            hipStream_t st);
 
 // Rows per thread of the small-system kernel (1 or 2), 0 when it does not
 // apply: more than kOneGroupRows * kIterBlock unknowns, a 64-row tile with
@@ -2110,8 +2137,8 @@ bool use_one_group(const sla_csr A) {
   return A->one_group == SLA_ONE_GROUP_AUTO && one_group_rows(A) > 0;
 }
 
-static sla_status launch_one_group(sla_csr A, int64_t batch, bool jac, double tol,
-                                   int64_t maxit, bool x0, hipStream_t st) {
+static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch, bool jac,
+                                   double tol, int64_t maxit, bool x0, hipStream_t st) {
   const size_t lds = one_group_lds_bytes(A->n);
   const unsigned g = unsigned(batch);
   const int u = x0 ? 1 : 0;
@@ -2119,11 +2146,11 @@ static sla_status launch_one_group(sla_csr A, int64_t batch, bool jac, double to
   if (A->rp_idx == SLA_I32) {
     auto k = two ? (jac ? k_cg_onegroup<int32_t, 2, true> : k_cg_onegroup<int32_t, 2, false>)
                  : (jac ? k_cg_onegroup<int32_t, 1, true> : k_cg_onegroup<int32_t, 1, false>);
-    k<<<g, kIterBlock, lds, st>>>(A->ctx_dev, tol, maxit, u);
+    k<<<g, kIterBlock, lds, st>>>(ctx_dev, tol, maxit, u);
   } else {
     auto k = two ? (jac ? k_cg_onegroup<int64_t, 2, true> : k_cg_onegroup<int64_t, 2, false>)
                  : (jac ? k_cg_onegroup<int64_t, 1, true> : k_cg_onegroup<int64_t, 1, false>);
-    k<<<g, kIterBlock, lds, st>>>(A->ctx_dev, tol, maxit, u);
+    k<<<g, kIterBlock, lds, st>>>(ctx_dev, tol, maxit, u);
   }
   LAUNCH_CHECK();
   return SLA_OK;
@@ -2154,56 +2181,83 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
     SLA_TRY(dev_alloc(&A->jbad, size_t(batch), "diagonal flags"));
     SLA_TRY_HIP(hipMemsetAsync(A->jbad, 0, sizeof(int) * size_t(batch), st));
   }
-  fill_ctx(A, *A->ctx_host, b, x, batch, want_hist, jacobi);
-  SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
+  return run_cg_space(A, own_space(A), b, x, tol, maxit, flags, info, st);
+}
+
+// The context of a solve written into device memory by a one-thread kernel
+// (the context passed by value): no host staging buffer is involved.
+__global__ void k_store_ctx(Ctx c, Ctx* __restrict__ dst) { *dst = c; }
+
+sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x, double tol,
+                        int64_t maxit, uint32_t flags, sla_cg_info* info, hipStream_t st) {
+  const int64_t batch = A->batch;
+  const bool want_hist = (flags & SLA_FLAG_HISTORY) != 0;
+  const bool jacobi = (flags & SLA_FLAG_JACOBI) != 0;
+  fill_ctx(A, sp, *sp.ctx_host, b, x, batch, want_hist, jacobi);
+  if (sp.own) {
+    SLA_TRY_HIP(hipMemcpyAsync(sp.ctx_dev, sp.ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
+  } else {
+    k_store_ctx<<<1, 1, 0, st>>>(*sp.ctx_host, sp.ctx_dev);
+    LAUNCH_CHECK();
+  }
 
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
   if (use_one_group(A)) {
-    SLA_TRY(launch_one_group(A, batch, jacobi, tol, maxit, x0, st));
-    return finish_cg(A, batch, info, st);
+    SLA_TRY(launch_one_group(A, sp.ctx_dev, batch, jacobi, tol, maxit, x0, st));
+    return finish_cg(sp, batch, info, st);
   }
-  if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, A->q, st));  // q = A x0
-  const dim3 grid2(unsigned(A->grid), unsigned(batch));
-  if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
-  else k_cg_init<int64_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, x0 ? 1 : 0);
-  k_cg_init_scalars<<<unsigned(batch), kIterBlock, 0, st>>>(A->ctx_dev, tol, maxit);
+  if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, sp.q, st));  // q = A x0
+  const dim3 grid2(unsigned(sp.grid), unsigned(batch));
+  if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev, x0 ? 1 : 0);
+  else k_cg_init<int64_t><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev, x0 ? 1 : 0);
+  k_cg_init_scalars<<<unsigned(batch), kIterBlock, 0, st>>>(sp.ctx_dev, tol, maxit);
   LAUNCH_CHECK();
-  SLA_TRY_HIP(hipMemcpyAsync(A->poll_host, A->n_running, sizeof(int), hipMemcpyDeviceToHost,
+  SLA_TRY_HIP(hipMemcpyAsync(sp.poll_host, sp.n_running, sizeof(int), hipMemcpyDeviceToHost,
                              st));
   SLA_TRY_HIP(hipStreamSynchronize(st));
 
-  if (A->poll_host[0] > 0) {
+  if (sp.poll_host[0] > 0) {
     // at most maxit + 1 SpMV steps: the last one only applies the x update
-    const int64_t K = A->graph_block > 0 ? A->graph_block : 16;
+    // (without graphs: 16 iterations between polls on the handle's workspace,
+    // whose events keep one block queued; 32 on a space without events, where
+    // every poll waits for the stream)
+    const int64_t K = sp.own ? (A->graph_block > 0 ? A->graph_block : 16) : 32;
     const int64_t nblocks = (maxit + 1 + K - 1) / K;
     hipGraphExec_t exec = nullptr;
-    if (A->graph_block > 0) SLA_TRY(get_graph(A, batch, jacobi, &exec));
+    if (sp.own && A->graph_block > 0) SLA_TRY(get_graph(A, batch, jacobi, &exec));
     for (int64_t j = 0; j < nblocks; ++j) {
       if (exec) SLA_TRY_HIP(hipGraphLaunch(exec, st));
-      else SLA_TRY(enqueue_block(A, batch, jacobi, K, st));
-      SLA_TRY_HIP(hipMemcpyAsync(A->poll_host + (j & 1), A->n_running, sizeof(int),
+      else SLA_TRY(enqueue_block(A, sp, batch, jacobi, K, st));
+      SLA_TRY_HIP(hipMemcpyAsync(sp.poll_host + (j & 1), sp.n_running, sizeof(int),
                                  hipMemcpyDeviceToHost, st));
-      SLA_TRY_HIP(hipEventRecord(A->poll_ev[j & 1], st));
-      if (j >= 1) {
-        // wait for the previous block only, so one block is always queued
-        SLA_TRY_HIP(hipEventSynchronize(A->poll_ev[(j - 1) & 1]));
-        if (A->poll_host[(j - 1) & 1] == 0) break;
+      if (sp.poll_ev != nullptr) {
+        SLA_TRY_HIP(hipEventRecord(sp.poll_ev[j & 1], st));
+        if (j >= 1) {
+          // wait for the previous block only, so one block is always queued
+          SLA_TRY_HIP(hipEventSynchronize(sp.poll_ev[(j - 1) & 1]));
+          if (sp.poll_host[(j - 1) & 1] == 0) break;
+        }
+      } else {
+        // no events: wait for this block
+        SLA_TRY_HIP(hipStreamSynchronize(st));
+        if (sp.poll_host[j & 1] == 0) break;
       }
     }
   }
-  return finish_cg(A, batch, info, st);
+  return finish_cg(sp, batch, info, st);
 }
 
 // The per-system scalars back to the host, the infos and the status of the
 // solve (the first failing system's).
-static sla_status finish_cg(sla_csr A, int64_t batch, sla_cg_info* info, hipStream_t st) {
-  SLA_TRY_HIP(hipMemcpyAsync(A->scal_host, A->scal, sizeof(Scal) * batch,
+static sla_status finish_cg(const CgSpace& sp, int64_t batch, sla_cg_info* info,
+                            hipStream_t st) {
+  SLA_TRY_HIP(hipMemcpyAsync(sp.scal_host, scal_of(sp.ctx_dev, 0), sizeof(Scal) * batch,
                              hipMemcpyDeviceToHost, st));
   SLA_TRY_HIP(hipStreamSynchronize(st));
 
   sla_status first = SLA_OK;
   for (int64_t s = 0; s < batch; ++s) {
-    const Scal& sc = A->scal_host[s];
+    const Scal& sc = sp.scal_host[s];
     const int32_t state = sc.state_a != ST_RUNNING ? sc.state_a : sc.state_r;
     const sla_status ss = state >= SLA_ERR_NOT_SPD ? sla_status(state) : SLA_OK;
     if (info) {
@@ -2245,7 +2299,7 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
     blocks[nk] = kIterBlock;
     ldss[nk++] = lds_bytes(A);
   } else {
-    fns[nk] = spmv_step_kernel<RP>(A);
+    fns[nk] = spmv_step_kernel<RP>(A, A->grid);
     blocks[nk] = spmv_step_block(A);
     ldss[nk++] = lds_bytes(A);
   }
@@ -2304,15 +2358,15 @@ sla_status profile_kernels(sla_csr A, const double* b, double* x, int64_t reps, 
   // iteration, so that the timed SpMV steps include the deferred x update
   const int64_t huge = int64_t(1) << 40;
   SLA_TRY(ensure_workspace(A, 1));
-  fill_ctx(A, *A->ctx_host, b, x, 1, false);
+  fill_ctx(A, own_space(A), *A->ctx_host, b, x, 1, false);
   SLA_TRY_HIP(hipMemcpyAsync(A->ctx_dev, A->ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
   const dim3 grid2(unsigned(A->grid), 1u);
   if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, 0);
   else k_cg_init<int64_t><<<grid2, kIterBlock, 0, st>>>(A->ctx_dev, 0);
   k_cg_init_scalars<<<1u, kIterBlock, 0, st>>>(A->ctx_dev, 0.0, huge);
   LAUNCH_CHECK();
-  if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, 1, false, st));
-  else SLA_TRY(enqueue_iteration<int64_t>(A, 1, false, st));
+  if (A->rp_idx == SLA_I32) SLA_TRY(enqueue_iteration<int32_t>(A, own_space(A), 1, false, st));
+  else SLA_TRY(enqueue_iteration<int64_t>(A, own_space(A), 1, false, st));
   if (A->rp_idx == SLA_I32) return time_kernels<int32_t>(A, reps, avg_ms, st);
   return time_kernels<int64_t>(A, reps, avg_ms, st);
 }

@@ -737,6 +737,8 @@ __global__ __launch_bounds__(kIterBlock) void k_spmv_transpose(
 // values.  Both slots of a pair are visited, each finding the other.
 constexpr double kSymRel = 1e-12;
 
+__global__ void k_zero_flag(int* __restrict__ flag) { *flag = 0; }
+
 template <typename RP>
 __global__ void k_symmetry(int64_t n, int64_t nnz, const RP* __restrict__ rowptr,
                            const int32_t* __restrict__ col, const double* __restrict__ vals,
@@ -774,22 +776,26 @@ __global__ void k_symmetry(int64_t n, int64_t nnz, const RP* __restrict__ rowptr
 
 }  // namespace
 
-sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t st) {
+sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t st, int* flag_dev) {
   *bad = 0;
   if (A->nnz == 0) return SLA_OK;
-  if (A->sym_flag == nullptr) SLA_TRY(dev_alloc(&A->sym_flag, 1, "symmetry flag"));
+  int* flag = flag_dev;
+  if (flag == nullptr) {
+    if (A->sym_flag == nullptr) SLA_TRY(dev_alloc(&A->sym_flag, 1, "symmetry flag"));
+    flag = A->sym_flag;
+  }
   const double* v = values ? A->vals : nullptr;
   const int64_t batch = values ? A->batch : 0;
-  SLA_TRY_HIP(hipMemsetAsync(A->sym_flag, 0, sizeof(int), st));
+  k_zero_flag<<<1, 1, 0, st>>>(flag);  // a kernel, not a memset: callers may capture
   if (A->rp_idx == SLA_I32)
     k_symmetry<int32_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, A->nnz, (const int32_t*)A->rowptr,
-                                                           A->col, v, batch, A->sym_flag);
+                                                           A->col, v, batch, flag);
   else
     k_symmetry<int64_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, A->nnz, (const int64_t*)A->rowptr,
-                                                           A->col, v, batch, A->sym_flag);
+                                                           A->col, v, batch, flag);
   LAUNCH_CHECK();
   int h = 0;
-  SLA_TRY_HIP(hipMemcpyAsync(&h, A->sym_flag, sizeof(int), hipMemcpyDeviceToHost, st));
+  SLA_TRY_HIP(hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, st));
   SLA_TRY_HIP(hipStreamSynchronize(st));
   *bad = h;
   return SLA_OK;

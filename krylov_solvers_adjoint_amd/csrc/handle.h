@@ -104,8 +104,36 @@ struct sla_csr_s {
 
 namespace sla {
 
+// Where a CG solve keeps its device state (r, both search directions, q, the
+// partials, the context with the systems' scalar records, the running
+// count) and the host copies it reads back: the handle's own workspace
+// (own = true: captured graphs, history and Jacobi preconditioning allowed),
+// or caller-provided memory such as the allocation-free entry point's static
+// scratch (own = false: kernels launched one by one, no events).
+struct CgSpace {
+  double* r = nullptr;
+  double* p0 = nullptr;
+  double* p1 = nullptr;
+  double* q = nullptr;
+  double* part = nullptr;        // kPartSets * batch * grid
+  Ctx* ctx_dev = nullptr;        // the context, then the batch's Scal records
+  int* n_running = nullptr;
+  Ctx* ctx_host = nullptr;       // host copy of the context
+  Scal* scal_host = nullptr;     // [batch] host copies of the records
+  int* poll_host = nullptr;      // [2]
+  hipEvent_t* poll_ev = nullptr; // [2], or nullptr: wait for the stream at each poll
+  int32_t grid = 0;              // solver workgroups per system
+  bool own = true;
+};
+
 // Workspace and launch helpers implemented in cg.hip
 sla_status ensure_workspace(sla_csr A, int64_t batch);
+// the solver grid (workgroups per system) of a solve of `batch` systems
+int32_t solver_grid(const sla_csr A, int64_t batch);
+// the CG loop of run_cg on a given space (flags: X0 always; HISTORY and
+// JACOBI only on the handle's own space)
+sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x, double tol,
+                        int64_t maxit, uint32_t flags, sla_cg_info* info, hipStream_t stream);
 bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
 bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
 bool use_lines(const sla_csr A);  // line-walk SpMV step (a banded pattern with far offsets +-L)?
@@ -119,10 +147,13 @@ void release_workspace(sla_csr A);
 void free_handle(sla_csr A);  // the handle, its workspace and its transposed pattern
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 // Symmetry of the pattern and, with values = true, of the bound values of
-// every system (bit for bit): *bad gets bit 0 for a stored (i, j) whose
-// mirror (j, i) is not stored, bit 1 for a mirror pair with different values.
-// Synchronises `stream` (csr_build.hip).
-sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t stream);
+// every system (mirror entries equal to within 1e-12 relative): *bad gets
+// bit 0 for a stored (i, j) whose mirror (j, i) is not stored, bit 1 for a
+// mirror pair with different values.  flag_dev: a device int to use for the
+// result (nullptr: the handle's own, allocated on first use).  Synchronises
+// `stream` (csr_build.hip).
+sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t stream,
+                          int* flag_dev = nullptr);
 
 sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x,
                        double* y, hipStream_t stream);
