@@ -34,9 +34,24 @@ ERR_NOT_SYMMETRIC = 7
 ERR_BREAKDOWN = 8
 
 
-def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle with gcc (always recompiles)."""
-    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+# Sanitizers: with SLA_ORACLE_SANITIZE=1 the oracle is built and loaded with
+# AddressSanitizer and UndefinedBehaviorSanitizer (gcc; every finding aborts).
+# The interpreter is not instrumented, so the process must preload the ASan
+# runtime:  LD_PRELOAD=$(gcc -print-file-name=libasan.so)
+#           ASAN_OPTIONS=detect_leaks=0 SLA_ORACLE_SANITIZE=1 python -m pytest ...
+_SANITIZE = os.environ.get("SLA_ORACLE_SANITIZE", "") == "1"
+
+
+def build(src: str = _SRC, out: str | None = None, sanitize: bool | None = None) -> str:
+    """Compile the oracle with gcc (always recompiles); sanitize=True adds
+    -fsanitize=address,undefined (default: the SLA_ORACLE_SANITIZE setting)."""
+    san = _SANITIZE if sanitize is None else sanitize
+    if out is None:
+        out = _SAN_LIB if san else _LIB
+    flags = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=all"] if san else ["-O2"])
+    cmd = ["gcc", *flags, "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-shared", "-fPIC", "-std=c11", "-Wall", "-o", out + ".tmp", src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
@@ -51,9 +66,10 @@ def _load(path: str | None = None):
     if path is not None:
         return _bind(ctypes.CDLL(path))
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        _lib = _bind(ctypes.CDLL(_LIB))
+        lib_path = _SAN_LIB if _SANITIZE else _LIB
+        if not os.path.exists(lib_path):
+            build(out=lib_path, sanitize=_SANITIZE)
+        _lib = _bind(ctypes.CDLL(lib_path))
     return _lib
 
 

@@ -102,7 +102,7 @@ def test_mutation_is_caught(name):
         with open(msrc, "w") as f:
             f.write(src.replace(old, new))
         lib = os.path.join(d, "liboracle_mut.so")
-        oracle.build(msrc, lib)
+        oracle.build(msrc, lib, sanitize=False)
         code = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
         env = dict(os.environ, OMP_NUM_THREADS="1")
         p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
