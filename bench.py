@@ -967,6 +967,44 @@ def cpu_baseline(seconds: float):
                        f"with the pattern gradient, fp64, {dt:.1f} s")
 
 
+def stream_ceiling(reps: int = 10) -> dict:
+    """Bandwidth of plain stream kernels (torch's own element-wise and
+    reduction kernels) on fp64 vectors of n = 16M and 169M elements: read
+    (sum), R1W1 (copy), R2W1 (add), R3W1 (addcmul), each the median of
+    `reps` event-timed launches after a warm-up.  At 16M the four vectors
+    (512 MB) exceed the 256 MB Infinity Cache only twice over, at 169M
+    (5.4 GB) every byte comes from HBM."""
+    import numpy as np
+    import torch
+    out = {"peak_GBps": HBM_PEAK_GBPS}
+    for n in (16_000_000, 169_000_000):
+        a, b, c, d = (torch.rand(n, dtype=torch.float64, device="cuda") for _ in range(4))
+        ops = {"read (sum)": (lambda: torch.sum(a), 1, 0),
+               "R1W1 (copy)": (lambda: d.copy_(a), 1, 1),
+               "R2W1 (add)": (lambda: torch.add(a, b, out=d), 2, 1),
+               "R3W1 (addcmul)": (lambda: torch.addcmul(a, b, c, out=d), 3, 1)}
+        res = {}
+        for name, (fn, r, w) in ops.items():
+            fn()
+            torch.cuda.synchronize()
+            ms = []
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            t = float(np.median(ms))
+            res[name] = dict(ms=t, GBps=(r + w) * 8 * n / (t * 1e-3) / 1e9)
+            log(f"[bench] stream n={n} {name}: {res[name]['GBps']:.0f} GB/s")
+        out[f"n{n}"] = res
+        del a, b, c, d
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -989,6 +1027,11 @@ def main():
                     help="only the --sizes runs (for profiler passes); prints no JSON line")
     ap.add_argument("--csr-only", action="store_true",
                     help="force the plain CSR kernels (no banded-pattern kernels)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only measure what plain element-wise stream kernels (torch's sum, "
+                         "copy, add, addcmul) reach on fp64 vectors of the 16M and 169M "
+                         "workloads' size: the practical bandwidth for each read/write mix; "
+                         "prints one JSON line of its own and exits")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy a 1 GiB fp64 tensor 5 times (a plain copy kernel of known "
                          "size, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -1003,6 +1046,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import krylov_solvers_adjoint_amd  # noqa: F401  (fails loudly without the HIP library)
 
+    if args.stream_ceiling:
+        print(json.dumps(stream_ceiling()), flush=True)
+        return
     if args.calibrate_copy:
         src = torch.ones(1 << 27, dtype=torch.float64, device="cuda")
         dst = torch.empty_like(src)
