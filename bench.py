@@ -251,11 +251,11 @@ def bench_headline(args):
         eff_GBps=step_bytes * args.steps / wall / 1e9,
         solution_rel_error=err,
         footprint_MB=(free0 - free1) / 2**20,
-        library_MB=(lib1 - lib0) / 2**20,
-        library_peak_MB=(libpeak - lib0) / 2**20,
+        library_MB=(lib1 - lib0) / 1e6,
+        library_peak_MB=(libpeak - lib0) / 1e6,
         # the caller's tensors of one forward + adjoint step: values, b, grad_x
         # (inputs), x, grad_b, grad_vals (outputs)
-        caller_MB=(8 * nnz * 2 + 8 * n * 4) / 2**20,
+        caller_MB=(8 * nnz * 2 + 8 * n * 4) / 1e6,
         kernel_ms=kern,
     )
     res["pct_peak_effective"] = 100.0 * res["eff_GBps"] / HBM_PEAK_GBPS
@@ -312,8 +312,8 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int, runs: int = 3):
                canonical_GBps=cbytes / (ms_it * 1e-3) / 1e9,
                rel_residual=info.rel_residual,
                footprint_MB=(free0 - free1) / 2**20,
-               library_MB=(lib1 - lib0) / 2**20,
-               library_peak_MB=(libpeak - lib0) / 2**20,
+               library_MB=(lib1 - lib0) / 1e6,
+               library_peak_MB=(libpeak - lib0) / 1e6,
                kernel_ms=kern,
                spmv_GBps=sbytes / (kern["spmv_step"] * 1e-3) / 1e9)
     out["pct_peak_canonical"] = 100.0 * out["canonical_GBps"] / HBM_PEAK_GBPS
