@@ -715,9 +715,10 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
 //     in the tile's own cache lines or the neighbouring columns'.
 // Lines are split into kXcds contiguous ranges, one per XCD; a range into
 // `chunks` chunks; a workgroup takes kLineWaves adjacent columns of one
-// chunk.  Workgroups of kLineWaves waves, two per CU: 16 waves per CU with
-// 128 registers each, enough to keep the next tile, its edge rows and the
-// current tile's values in flight together.
+// chunk.  Workgroups of kLineWaves waves, one per CU by default (two when
+// asked for, which the register bound of 128 per lane allows), enough to
+// keep the next tile, its edge rows and the current tile's values in flight
+// together.
 template <typename RP, int NB, bool NEAR1, bool PIPE>
 __global__ __launch_bounds__(kLineWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(kLineWavesPerEu)))
@@ -757,17 +758,22 @@ void k_cg_spmv_lines(const Ctx* __restrict__ c) {
   const int64_t units = groups * chunks;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, per_xcd = G / kXcds;
   const int64_t va = V * xcd / kXcds, vb = V * (xcd + 1) / kXcds;
-  // A unit of the walk: tile column u over the lines [v0, v1).  A unit with
-  // no rows (past the last unit, a column past the line, an empty chunk)
-  // stands for column 0 on line 0: its loads stay in the matrix, and it is
-  // not walked.
+  // A unit of the walk: tile column u over the lines [v0, v1).  Units are
+  // numbered group first, so that the workgroups of an XCD, which take
+  // consecutive units, walk side by side across whole grid lines of one or
+  // two chunks at a time: fewer places in memory are open at once than with
+  // chunk-first numbering (the same units, 5-6 % faster at 169M unknowns),
+  // and neighbouring groups' edge rows meet in the XCD's L2.  A unit with no
+  // rows (past the last unit, a column past the line, an empty chunk) stands
+  // for column 0 on line 0: its loads stay in the matrix, and it is not
+  // walked.
   struct Unit {
     int64_t v0, v1, col0, lenu;
     bool ok;
   };
   auto unit_at = [&](int64_t unit) -> Unit {
-    const int64_t u = (unit / chunks) * kLineWaves + w;
-    const int64_t ch = unit % chunks;
+    const int64_t u = (unit % groups) * kLineWaves + w;
+    const int64_t ch = unit / groups;
     const int64_t v0 = va + (vb - va) * ch / chunks, v1 = va + (vb - va) * (ch + 1) / chunks;
     const int64_t col0 = u * kTileRows;
     if (unit >= units || u >= U || v0 >= v1 || v0 * L + col0 >= n)
