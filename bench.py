@@ -266,12 +266,13 @@ def bench_headline(args):
     return res
 
 
-def bench_size(N: int, rp_dtype, its: int, kernel_reps: int, runs: int = 3):
+def bench_size(N: int, rp_dtype, its: int, kernel_reps: int, runs: int = 5, warmups: int = 2):
     """Poisson N x N, b ~ U(-1,1) seed 0, `its` fixed CG iterations: the
-    median of `runs` timed solves after a warm-up, per-kernel times, the
-    roofline of the SpMV step and of the whole iteration (canonical bytes and
-    the bytes the committed counters saw), and the library's device memory.
-    Also returns (b, x) on the host for the oracle leg."""
+    median of `runs` solves timed with HIP events on the solve's stream after
+    `warmups` untimed ones, per-kernel times, the roofline of the SpMV step
+    and of the whole iteration (canonical bytes and the bytes the committed
+    counters saw), and the library's device memory.  Also returns (b, x) on
+    the host for the oracle leg."""
     import numpy as np
     import torch
     import krylov_solvers_adjoint_amd as K
@@ -284,15 +285,20 @@ def bench_size(N: int, rp_dtype, its: int, kernel_reps: int, runs: int = 3):
     rp_bytes = 8 if rp_dtype == np.int64 else 4
     b_np = W.uniform_rhs(n, 0)
     b = torch.from_numpy(b_np).to(dev)
-    # warm-up: captures the iteration graph and touches the workspace
-    K.sla_cg_solve(P, v, b, 0.0, 40)
+    # warm-ups: capture the iteration graph and touch the workspace
+    for _ in range(warmups):
+        K.sla_cg_solve(P, v, b, 0.0, its)
     torch.cuda.synchronize()
     walls = []
+    stream = torch.cuda.current_stream()
     for _ in range(runs):
-        t0 = time.perf_counter()
-        x, info = K.sla_cg_solve(P, v, b, 0.0, its)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        x, info = K.sla_cg_solve(P, v, b, 0.0, its, stream=stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        walls.append(time.perf_counter() - t0)
+        walls.append(1e-3 * e0.elapsed_time(e1))
     wall = float(np.median(walls))
     free1 = torch.cuda.mem_get_info()[0]
     lib1, libpeak = K.sla_memory_usage()
@@ -1089,7 +1095,7 @@ def main():
                 continue
             N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
                      "169m": (13000, np.int64)}[s.lower()]
-            out = bench_size(N, rp, 500, args.kernel_reps, runs=1)[0]
+            out = bench_size(N, rp, 500, args.kernel_reps, runs=1, warmups=1)[0]
             log(f"[bench] size {s}: {out['ms_per_iteration']:.3f} ms/it, "
                 f"{out['canonical_GBps']:.0f} GB/s canonical, kernels {out['kernel_ms']}")
         return
@@ -1134,7 +1140,7 @@ def main():
             continue
         N, rp = {"1m": (1000, np.int32), "16m": (4000, np.int32),
                  "169m": (13000, np.int64)}[s.lower()]
-        log(f"[bench] size {s}: Poisson {N}x{N}, 500 fixed iterations, median of 3")
+        log(f"[bench] size {s}: Poisson {N}x{N}, 500 fixed iterations, median of 5 after 2 warm-ups")
         out, b_np, x_np = bench_size(N, rp, 500, args.kernel_reps)
         sizes[s.lower()] = out
         ro = out["roofline"]
