@@ -26,6 +26,11 @@ HIPCC_FLAGS = [
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # the kernel's first two arguments arrive in scalar registers at wave
+    # launch (the solver kernels' only argument is the context pointer):
+    # without it the first memory access of every wave waits for a load of
+    # that pointer from the argument segment
+    "-mllvm", "-amdgpu-kernarg-preload-count=2",
 ]
 
 

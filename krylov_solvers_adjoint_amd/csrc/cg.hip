@@ -1550,26 +1550,24 @@ __global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWav
 void k_cg_residual(const Ctx* __restrict__ c) {
   __shared__ double red[3 * kWaves];  // p.Ap sum, r.r and r.z partials
   const int64_t s = blockIdx.y;
-  // context fields first (scalar loads, see k_cg_spmv)
-  const int64_t n = c->n, tiles = c->tiles;
-  const int G = c->grid;
-  SLA_GLOBAL double* part = gmem(c->part + s * kPartSets * G);
-  SLA_GLOBAL double* r = gmem(c->r + s * n);
-  const SLA_GLOBAL double* q = gmem(c->q + s * n);
-  const SLA_GLOBAL double* dg = gmem(c->diag + s * n);
-  SLA_GLOBAL double* z = gmem(c->z + s * n);
-  int* const n_running = c->n_running;
+  // the context fields and the system's record (step index, state, r.r and
+  // r.z by parity: an index from k would wait for k) in one round trip
+  const CtxWords cw = load_ctx(c, s);
+  const int64_t n = SLA_CTX(cw, int64_t, n), tiles = SLA_CTX(cw, int64_t, tiles);
+  const int G = SLA_CTX(cw, int32_t, grid);
+  SLA_GLOBAL double* part = gmem(SLA_CTX(cw, double*, part) + s * kPartSets * G);
+  SLA_GLOBAL double* r = gmem(SLA_CTX(cw, double*, r) + s * n);
+  const SLA_GLOBAL double* q = gmem(SLA_CTX(cw, double*, q) + s * n);
+  const SLA_GLOBAL double* dg = gmem(SLA_CTX(cw, const double*, diag) + s * n);
+  SLA_GLOBAL double* z = gmem(SLA_CTX(cw, double*, z) + s * n);
+  int* const n_running = SLA_CTX(cw, int*, n_running);
   Scal* sc = scal_of(c, s);
   const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
-  // the step index and state come in the context's round trip (read through
-  // the global address space: a flat load would make the first wait below
-  // cover the tile loads issued after it)
   const SLA_GLOBAL Scal* scg = gmem(static_cast<const Scal*>(sc));
-  const int64_t k = scg->kr;
-  const int32_t st_in = scg->state_a;
-  // (both parities: an index from k would wait for k)
-  const double rr0 = scg->rr[0], rr1 = scg->rr[1], rz0 = scg->rz[0], rz1 = scg->rz[1];
-  pin(n, tiles, G, part, r, q, dg, z, k, st_in, rr0, rr1, rz0, rz1);
+  const int64_t k = SLA_REC(cw, int64_t, kr);
+  const int32_t st_in = SLA_REC(cw, int32_t, state_a);
+  const double rr0 = SLA_REC(cw, double, rr[0]), rr1 = SLA_REC(cw, double, rr[1]);
+  const double rz0 = SLA_REC(cw, double, rz[0]), rz1 = SLA_REC(cw, double, rz[1]);
   const double rr = (k & 1) ? rr1 : rr0;
   const double num = JAC ? ((k & 1) ? rz1 : rz0) : rr;
   const uint32_t lane = lane_id();

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 
@@ -191,6 +192,13 @@ __host__ __device__ __forceinline__ Scal* scal_of(const Ctx* c, int64_t s) {
   return reinterpret_cast<Scal*>(const_cast<Ctx*>(c) + 1) + s;
 }
 
+// The context and one system's record in one round trip (see load_ctx).
+constexpr uint32_t kCtxWords = sizeof(Ctx) / 8;
+constexpr uint32_t kScalWords = sizeof(Scal) / 8;
+struct CtxWords {
+  uint32_t lo, hi;
+};
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
@@ -270,6 +278,42 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
 }
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+// The context and system s's record in one vector load: lane l loads 8-byte
+// word l of the context (l < kCtxWords) or word l - kCtxWords of the record,
+// and the kernel moves the fields it uses into scalar registers with
+// readlane (no memory access).  Scalar loads of the same fields issue in
+// dependent rounds (the compiler reuses scalar registers between them): four
+// in the residual step, whose iteration at 10^6 unknowns this load shortens
+// by about 0.5 us.  The line walk's rounds cost no more than this load (its
+// context fields hit the scalar cache), and it keeps scalar loads.
+__device__ __forceinline__ CtxWords load_ctx(const Ctx* c, int64_t s) {
+  static_assert(kCtxWords + kScalWords <= kWave, "the context and a record fit one wave load");
+  const uint32_t l = lane_id();
+  const uint32_t lr = l - kCtxWords < kScalWords ? l - kCtxWords : 0u;
+  const uint64_t* src = l < kCtxWords ? reinterpret_cast<const uint64_t*>(c) + l
+                                      : reinterpret_cast<const uint64_t*>(scal_of(c, s)) + lr;
+  const uint64_t w = *gmem(src);
+  return CtxWords{uint32_t(w), uint32_t(w >> 32)};
+}
+// The field at byte offset `off` of the context, or (off >= sizeof(Ctx)) of
+// the record, from the words of load_ctx.
+template <typename T, uint32_t off>
+__device__ __forceinline__ T ctx_get(const CtxWords& w) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte fields");
+  static_assert(off % sizeof(T) == 0 && off / 8 < kCtxWords + kScalWords, "an aligned field");
+  constexpr int word = int(off / 8);
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(w.hi), word))) << 32) |
+                       uint32_t(__builtin_amdgcn_readlane(int(w.lo), word));
+    return __builtin_bit_cast(T, u);
+  } else {
+    const uint32_t u = uint32_t(__builtin_amdgcn_readlane(int((off & 4u) ? w.hi : w.lo), word));
+    return __builtin_bit_cast(T, u);
+  }
+}
+#define SLA_CTX(w, T, field) ctx_get<T, uint32_t(offsetof(Ctx, field))>(w)
+#define SLA_REC(w, T, field) ctx_get<T, uint32_t(sizeof(Ctx) + offsetof(Scal, field))>(w)
 
 // A double moved across lanes by a DPP pattern (two 32-bit moves); lanes
 // without a source lane, or in rows the mask leaves out, read 0.
