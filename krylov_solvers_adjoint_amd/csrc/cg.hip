@@ -1545,10 +1545,12 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
 
 // Residual step k (see the file comment).  JAC: Jacobi preconditioning, so
 // alpha = r.z / p.Ap, and the step also writes z = r / d and the r.z partials.
-template <bool JAC>
-__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+// NT threads per workgroup (residual_block).
+template <bool JAC, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 * (NT / kWave) / 4)))
 void k_cg_residual(const Ctx* __restrict__ c) {
-  __shared__ double red[3 * kWaves];  // p.Ap sum, r.r and r.z partials
+  constexpr int W = NT / kWave;
+  __shared__ double red[3 * W];  // p.Ap sum, r.r and r.z partials
   const int64_t s = blockIdx.y;
   // the context fields and the system's record (step index, state, r.r and
   // r.z by parity: an index from k would wait for k) in one round trip
@@ -1580,7 +1582,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
   constexpr int B = kStreamTiles;
   constexpr int U = JAC ? 2 : kStreamTiles;
   static_assert(B % U == 0, "whole rounds per block");
-  const TileWalk wk = wave_walk((tiles + B - 1) / B, G, blockIdx.x, kWaves, wave_index());
+  const TileWalk wk = wave_walk((tiles + B - 1) / B, G, blockIdx.x, W, wave_index());
   double rv[U], qv[U], dv[U];
   // unconditional loads: tiles past the matrix read the round's first tile
   // and lanes past the last row read that row (their values are not used,
@@ -1605,7 +1607,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
     if (lead) sc->state_r = st_in;
     return;
   }
-  const double pq = sum_partials_once(part + (2 + (k & 1)) * G, G, red);
+  const double pq = sum_partials_once<NT>(part + (2 + (k & 1)) * G, G, red);
   int32_t stop = ST_RUNNING;
   if (!isfinite(pq)) stop = ST_NONFINITE;
   else if (!(pq > 0.0)) stop = ST_NOT_SPD;
@@ -1616,7 +1618,7 @@ void k_cg_residual(const Ctx* __restrict__ c) {
       SLA_GLOBAL double* x = gmem(c->x + s * n);
       const SLA_GLOBAL double* pk1 = gmem(c->p[0] + s * n);  // p_{k-1} (k odd)
       const double a1 = scg->alpha[0];                        // alpha_{k-1}
-      const TileWalk tw = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
+      const TileWalk tw = wave_walk(tiles, G, blockIdx.x, W, wave_index());
       for (int64_t t = tw.first; t < tw.end; t += tw.stride) {
         const int64_t i0 = t * kTileRows;
         if (i0 + lane < n) st(x + i0, lane, ld(x + i0, lane) + a1 * ld(pk1 + i0, lane));
@@ -1666,8 +1668,8 @@ void k_cg_residual(const Ctx* __restrict__ c) {
       }
     }
   }
-  rn = block_sum_once<kIterBlock>(rn, red + kWaves);
-  if constexpr (JAC) rzn = block_sum_once<kIterBlock>(rzn, red + 2 * kWaves);
+  rn = block_sum_once<NT>(rn, red + W);
+  if constexpr (JAC) rzn = block_sum_once<NT>(rzn, red + 2 * W);
   if (threadIdx.x == 0) {
     part[((k + 1) & 1) * G + blockIdx.x] = rn;
     if constexpr (JAC) part[(5 + ((k + 1) & 1)) * G + blockIdx.x] = rzn;
@@ -1803,6 +1805,25 @@ const void* product_kernel(const sla_csr A) {
 // Threads per workgroup of the SpMV step kernel.
 unsigned spmv_step_block(const sla_csr A) { return use_lines(A) ? kLineWaves * kWave : kIterBlock; }
 
+// Threads per workgroup of the residual step: 8 waves, whose blocks of
+// kStreamTiles tiles stream faster than 16 waves' (at 169M unknowns 0.77 vs
+// 0.81 ms per step: fewer waves per CU keep fewer DRAM pages open), and 16
+// where that lets every wave finish in one round of loads while 8 waves
+// would need two (the 10^6-unknown grid at one workgroup per CU).
+unsigned residual_block(const sla_csr A, int32_t grid) {
+  const int64_t blocks = (A->tiles + kStreamTiles - 1) / kStreamTiles;
+  const int64_t g = grid;
+  return blocks > g * (512 / kWave) && blocks <= g * (1024 / kWave) ? 1024u : 512u;
+}
+
+const void* residual_kernel(bool jacobi, unsigned threads) {
+  if (threads == 1024u)
+    return jacobi ? reinterpret_cast<const void*>(&k_cg_residual<true, 1024>)
+                  : reinterpret_cast<const void*>(&k_cg_residual<false, 1024>);
+  return jacobi ? reinterpret_cast<const void*>(&k_cg_residual<true, 512>)
+                : reinterpret_cast<const void*>(&k_cg_residual<false, 512>);
+}
+
 sla_status launch_ctx_kernel(const void* fn, dim3 grid, unsigned block, size_t lds, const Ctx* cd,
                              hipStream_t st) {
   void* args[1] = {&cd};
@@ -1826,8 +1847,8 @@ sla_status enqueue_iteration(sla_csr A, const CgSpace& sp, int64_t batch, bool j
     SLA_TRY(launch_ctx_kernel(spmv_step_kernel<RP>(A, sp.grid), grid2, spmv_step_block(A),
                               lds_bytes(A), sp.ctx_dev, st));
   }
-  if (jacobi) k_cg_residual<true><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev);
-  else k_cg_residual<false><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev);
+  const unsigned rb = residual_block(A, sp.grid);
+  SLA_TRY(launch_ctx_kernel(residual_kernel(jacobi, rb), grid2, rb, 0, sp.ctx_dev, st));
   LAUNCH_CHECK();
   return SLA_OK;
 }
@@ -2307,8 +2328,8 @@ sla_status time_kernels(sla_csr A, int64_t reps, double* avg_ms, hipStream_t st)
     blocks[nk] = spmv_step_block(A);
     ldss[nk++] = lds_bytes(A);
   }
-  fns[nk] = reinterpret_cast<const void*>(&k_cg_residual<false>);
-  blocks[nk] = kIterBlock;
+  blocks[nk] = residual_block(A, A->grid);
+  fns[nk] = residual_kernel(false, blocks[nk]);
   ldss[nk++] = 0;
   const int res_k = nk - 1;  // the residual step's entry
   // a one-kernel SpMV step is timed again after the residual launches, which
