@@ -593,11 +593,12 @@ __device__ __forceinline__ StepHead step_head(const Ctx* __restrict__ c, int64_t
 
 // SpMV step k (see the file comment): direction update, deferred x update,
 // q = A p_k with p_k recomputed at each gathered column, p.Ap partials.
-template <typename RP, int NB>
-__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+template <typename RP, int NB, int NT = kIterBlock>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 * (NT / kWave) / 4)))
 void k_cg_spmv(const Ctx* __restrict__ c) {
+  constexpr int W = NT / kWave;
   extern __shared__ double lds_dyn[];
-  __shared__ double red[3 * kWaves];  // step head (2 areas), the p.Ap partial
+  __shared__ double red[3 * W];  // step head (2 areas), the p.Ap partial
   const int64_t s = blockIdx.y;
   // context fields first: read before the kernel's first store, they come
   // in through scalar loads
@@ -621,14 +622,14 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
     if (blockIdx.x == 0 && threadIdx.x == 0) sc->state_a = st_in;
     return;
   }
-  const StepHead h = step_head(c, s, in, red);
+  const StepHead h = step_head<NT>(c, s, in, red);
   const int64_t k = uniform(h.k);
   const double alpha = uniform(h.alpha), beta = uniform(h.beta);
   const bool lag = h.lag;
   // p_{k-1} and p_k
   const SLA_GLOBAL double* pold = gmem((k & 1) ? p0 : p1);
   SLA_GLOBAL double* pnew = gmem((k & 1) ? p1 : p0);
-  const TileWalk wk = wave_walk(tiles, G, blockIdx.x, kWaves, wave_index());
+  const TileWalk wk = wave_walk(tiles, G, blockIdx.x, W, wave_index());
   if (h.stop != ST_RUNNING) {
     // last pass: only the deferred x update
     if (lag) {
@@ -689,7 +690,7 @@ void k_cg_spmv(const Ctx* __restrict__ c) {
     pq = own ? pq1 : pq;
     t = tn;
   }
-  pq = block_sum_once<kIterBlock>(pq, red + 2 * kWaves);
+  pq = block_sum_once<NT>(pq, red + 2 * W);
   if (threadIdx.x == 0) part[(2 + (k & 1)) * G + blockIdx.x] = pq;
 }
 
@@ -1788,9 +1789,15 @@ const void* spmv_step_kernel(const sla_csr A, int32_t grid) {
     }
   }
   switch (nb) {
-    case 3: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 3>);
-    case 5: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 5>);
-    case 8: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 8>);
+    case 3:
+      return A->panel > 0 ? reinterpret_cast<const void*>(&k_cg_spmv<RP, 3, 512>)
+                          : reinterpret_cast<const void*>(&k_cg_spmv<RP, 3, 1024>);
+    case 5:
+      return A->panel > 0 ? reinterpret_cast<const void*>(&k_cg_spmv<RP, 5, 512>)
+                          : reinterpret_cast<const void*>(&k_cg_spmv<RP, 5, 1024>);
+    case 8:
+      return A->panel > 0 ? reinterpret_cast<const void*>(&k_cg_spmv<RP, 8, 512>)
+                          : reinterpret_cast<const void*>(&k_cg_spmv<RP, 8, 1024>);
     case -1: return reinterpret_cast<const void*>(&k_cg_spmv<RP, -1>);
     default: return reinterpret_cast<const void*>(&k_cg_spmv<RP, 0>);
   }
@@ -1802,8 +1809,15 @@ const void* product_kernel(const sla_csr A) {
                          : reinterpret_cast<const void*>(&k_cg_product<RP, false>);
 }
 
-// Threads per workgroup of the SpMV step kernel.
-unsigned spmv_step_block(const sla_csr A) { return use_lines(A) ? kLineWaves * kWave : kIterBlock; }
+// Threads per workgroup of the SpMV step kernel: the line walk's; 8 waves for
+// a band in panel order (measured on the 7-point 3D Laplacian: 23.5 vs 30.6
+// us per step at 100^3, 216 vs 280 us at 200^3, against 16 waves); 16 for the
+// other bands (a 2D band without panels, 1000^2: 17.2 us, 18.7 with 8 waves)
+// and plain CSR rows.
+unsigned spmv_step_block(const sla_csr A) {
+  if (use_lines(A)) return kLineWaves * kWave;
+  return use_band(A) && A->panel > 0 ? 512u : unsigned(kIterBlock);
+}
 
 // Threads per workgroup of the residual step: 8 waves, whose blocks of
 // kStreamTiles tiles stream faster than 16 waves' (at 169M unknowns 0.77 vs
