@@ -285,8 +285,9 @@ __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1)
 // readlane (no memory access).  Scalar loads of the same fields issue in
 // dependent rounds (the compiler reuses scalar registers between them): four
 // in the residual step, whose iteration at 10^6 unknowns this load shortens
-// by about 0.5 us.  The line walk's rounds cost no more than this load (its
-// context fields hit the scalar cache), and it keeps scalar loads.
+// by about 0.5 us.  The pipelined line walk uses it too (fewer spills); the
+// one-tile walk's rounds cost no more than this load (its context fields hit
+// the scalar cache), and it keeps scalar loads.
 __device__ __forceinline__ CtxWords load_ctx(const Ctx* c, int64_t s) {
   static_assert(kCtxWords + kScalWords <= kWave, "the context and a record fit one wave load");
   const uint32_t l = lane_id();
@@ -314,6 +315,21 @@ __device__ __forceinline__ T ctx_get(const CtxWords& w) {
 }
 #define SLA_CTX(w, T, field) ctx_get<T, uint32_t(offsetof(Ctx, field))>(w)
 #define SLA_REC(w, T, field) ctx_get<T, uint32_t(sizeof(Ctx) + offsetof(Scal, field))>(w)
+__device__ __forceinline__ BandOffsets ctx_band(const CtxWords& w) {
+  static_assert(kMaxBand == 8, "one line per offset below");
+  constexpr uint32_t o = uint32_t(offsetof(Ctx, band));
+  BandOffsets b;
+  b.count = ctx_get<int32_t, o>(w);
+  b.off[0] = ctx_get<int32_t, o + 4>(w);
+  b.off[1] = ctx_get<int32_t, o + 8>(w);
+  b.off[2] = ctx_get<int32_t, o + 12>(w);
+  b.off[3] = ctx_get<int32_t, o + 16>(w);
+  b.off[4] = ctx_get<int32_t, o + 20>(w);
+  b.off[5] = ctx_get<int32_t, o + 24>(w);
+  b.off[6] = ctx_get<int32_t, o + 28>(w);
+  b.off[7] = ctx_get<int32_t, o + 32>(w);
+  return b;
+}
 
 // A double moved across lanes by a DPP pattern (two 32-bit moves); lanes
 // without a source lane, or in rows the mask leaves out, read 0.
