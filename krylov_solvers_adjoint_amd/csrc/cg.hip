@@ -31,12 +31,15 @@
 //   * Rows are cut into 64-row wave tiles (one row per lane).  A tile's slots
 //     [rowptr[r0], rowptr[r0+64]) are contiguous: the wave stages them into
 //     its own LDS area with coalesced loads, then each lane walks its row.
-//     Only wave-level synchronisation is needed, so the 16 waves of a
+//     Only wave-level synchronisation is needed, so the waves of a
 //     workgroup progress independently.
-//   * Fixed grid of two 1024-thread workgroups per CU; each wave walks tiles
-//     inside its XCD's contiguous share of the rows, interleaved with the
-//     other waves of that XCD, so stencil neighbours (rows i +- N) are read
-//     while still in that XCD's L2.
+//   * A fixed grid per handle, one or two workgroups per CU (solver_grid);
+//     workgroups of 1024 threads, or 512 for the line walk, for the residual
+//     step unless 16 waves finish it in one round of loads
+//     (residual_block), and for bands in panel order (spmv_step_block).
+//     Each wave walks tiles inside its XCD's contiguous share of the rows,
+//     interleaved with the other waves of that XCD, so stencil neighbours
+//     (rows i +- N) are read while still in that XCD's L2.
 //   * Blocks of iterations are captured once per handle as a HIP graph; a
 //     kernel returns at once when its system has stopped, and the host only
 //     polls the count of running systems between blocks.

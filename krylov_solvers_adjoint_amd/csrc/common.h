@@ -59,7 +59,7 @@ void dev_free(void* p);
 // ---------------------------------------------------------------------------
 constexpr int kWave = 64;
 constexpr int kBlock = 256;        // workgroup of the set-up kernels (4 waves)
-constexpr int kIterBlock = 1024;   // workgroup of the solver kernels (16 waves)
+constexpr int kIterBlock = 1024;   // workgroup of most solver kernels (16 waves)
 constexpr int kWaves = kIterBlock / kWave;
 // two solver workgroups per CU: 8 waves on each of its 4 SIMDs, which caps a
 // kernel at 64 VGPRs
