@@ -1192,6 +1192,13 @@ def main():
                     note="1M working set (about 110 MB) fits the 256 MB Infinity Cache: the "
                          "counted traffic leaves the L2 and is mostly served there, not by HBM; "
                          "sizes.16m / sizes.169m carry the HBM-resident rooflines")
+    # as in the size legs: the whole iteration on canonical bytes, and the
+    # counted bytes of the SpMV step over its live time
+    ms_it = head["ms_per_step"] / (head["iterations_fwd"] + head["iterations_adj"])
+    roofline["frac_canonical"] = canonical_bytes(head["n"], head["nnz"], 4) / (ms_it * 1e-3) / \
+        1e9 / HBM_PEAK_GBPS
+    if roofline["traffic"]:
+        roofline["frac_kernel_moved"] = roofline["traffic"] / (spmv_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
