@@ -575,16 +575,17 @@ def _event_ms(fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def bench_matvec(reps: int):
-    """The differentiable .matvec on the 1000 x 1000 Poisson matrix: y = A x,
+def bench_matvec(reps: int, N: int = 1000):
+    """The differentiable .matvec on the N x N Poisson matrix: y = A x,
     y = A^T x (values gathered into the transposed pattern's order on each
-    call) and the backward pass (grad_x = A^T g plus grad_vals = g_i x_j)."""
+    call) and the backward pass (grad_x = A^T g plus grad_vals = g_i x_j).
+    At N = 1000 the matrix and vectors fit the Infinity Cache; at N = 4000
+    they come from HBM."""
     import numpy as np
     import torch
     import krylov_solvers_adjoint_amd as K
     import workloads as W
     dev = torch.device("cuda", 0)
-    N = 1000
     n = N * N
     P, v, _, _ = gpu_setup(N, np.int32)
     x = torch.from_numpy(W.normal_rhs(n, 2)).to(dev)
@@ -621,15 +622,14 @@ def lanczos_bytes(n: int, steps: int, k: int, spmv: int) -> int:
     return gs + steps * spmv + 24 * n + 8 * n * (steps + k)
 
 
-def bench_eigsh(m: int, k: int):
-    """The .eigsh on the 1000 x 1000 Poisson matrix: the k largest
-    eigenvalues by m Lanczos steps with full reorthogonalisation."""
+def bench_eigsh(m: int, k: int, N: int = 1000):
+    """The .eigsh on the N x N Poisson matrix: the k largest eigenvalues by m
+    Lanczos steps with full reorthogonalisation."""
     import numpy as np
     import torch
     import krylov_solvers_adjoint_amd as K
     import workloads as W
     dev = torch.device("cuda", 0)
-    N = 1000
     n = N * N
     P, v, _, free0 = gpu_setup(N, np.int32)
     v0 = torch.from_numpy(W.normal_rhs(n, 72)).to(dev)
@@ -666,7 +666,8 @@ def bench_eigsh(m: int, k: int):
         bound="hbm", kernel="k_lz_dot (Gram-Schmidt dot pass)",
         achieved=gs_roof["dot_GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
         frac=gs_roof["dot_GBps"] / HBM_PEAK_GBPS,
-        traffic=traffic_from_profile("k_lz_dot", "poisson1000_m300", lanczos_digest()),
+        traffic=(traffic_from_profile("k_lz_dot", "poisson1000_m300", lanczos_digest())
+                 if (N, m) == (1000, 300) else None),
         **{k_: v_ for k_, v_ in gs_roof.items()})
     del P, v, v0, th, X, res
     torch.cuda.synchronize()
@@ -683,16 +684,16 @@ def bicgstab_bytes(n: int, nnz: int, variant: str) -> int:
     return 2 * spmv_bytes(variant, n, nnz, 4) + 16 * 8 * n
 
 
-def bench_bicgstab():
-    """BiCGStab forward + adjoint on the 1000 x 1000 upwind
-    convection-diffusion matrix (non-symmetric, 10^6 unknowns) to tol 1e-8."""
+def bench_bicgstab(N: int = 1000, fixed: int = 0):
+    """BiCGStab forward + adjoint on the N x N upwind convection-diffusion
+    matrix (non-symmetric) to tol 1e-8, or `fixed` iterations each (tol 0)."""
     import numpy as np
     import torch
     import krylov_solvers_adjoint_amd as K
     import workloads as W
     dev = torch.device("cuda", 0)
-    N = 1000
     n = N * N
+    tol, maxit = (0.0, fixed) if fixed else (1e-8, 10000)
     rp, c, v = W.convection_diffusion_csr(N)
     P = K.sla_csr_create_from_csr(torch.from_numpy(rp).to(dev), torch.from_numpy(c).to(dev))
     vt = torch.from_numpy(v).to(dev)
@@ -702,11 +703,11 @@ def bench_bicgstab():
     K.sla_bicgstab_adjoint(P, vt, b, g, 1e-8, 40)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    x, fi = K.sla_bicgstab_solve(P, vt, b, 1e-8, 10000)
+    x, fi = K.sla_bicgstab_solve(P, vt, b, tol, maxit)
     torch.cuda.synchronize()
     fwd = time.perf_counter() - t0
     t0 = time.perf_counter()
-    gb, gv, ai = K.sla_bicgstab_adjoint(P, vt, x, g, 1e-8, 10000)
+    gb, gv, ai = K.sla_bicgstab_adjoint(P, vt, x, g, tol, maxit)
     torch.cuda.synchronize()
     adj = time.perf_counter() - t0
     variant = "banded" if P.banded else "csr"
@@ -1083,6 +1084,11 @@ def main():
             if s.lower() == "matvec":
                 log(f"[bench] matvec: {bench_matvec(args.kernel_reps)}")
                 continue
+            if s.lower() == "next16m":
+                log(f"[bench] matvec 16M: {bench_matvec(args.kernel_reps, 4000)}")
+                log(f"[bench] eigsh 16M: {bench_eigsh(60, 4, 4000)}")
+                log(f"[bench] bicgstab 16M: {bench_bicgstab(4000, fixed=200)}")
+                continue
             if s.lower() == "list":
                 log(f"[bench] list: {bench_list()}")
                 continue
@@ -1177,6 +1183,17 @@ def main():
         log("[bench] SparseTensorList: 32 Poisson grids 100^2 .. 410^2, CG tol 1e-8")
         nxt["list"] = bench_list()
         log(f"[bench] list: {nxt['list']}")
+        # the same operations at 4000^2 (16M unknowns), where every byte comes
+        # from HBM
+        log("[bench] .matvec, .eigsh (60 steps) and BiCGStab (200 + 200 fixed iterations) "
+            "at 4000x4000")
+        nxt["matvec_16m"] = bench_matvec(args.kernel_reps, 4000)
+        nxt["eigsh_16m"] = bench_eigsh(60, 4, 4000)
+        nxt["bicgstab_16m"] = bench_bicgstab(4000, fixed=200)
+        log(f"[bench] 16M: matvec {nxt['matvec_16m']['spmv_GBps']:.0f} / "
+            f"{nxt['matvec_16m']['transpose_GBps']:.0f} / {nxt['matvec_16m']['backward_GBps']:.0f} "
+            f"GB/s, eigsh {nxt['eigsh_16m']['eff_GBps']:.0f} GB/s, BiCGStab "
+            f"{nxt['bicgstab_16m']['eff_GBps']:.0f} GB/s")
 
     digest = source_digest()
     spmv_ms = head["kernel_ms"]["spmv_step"]
