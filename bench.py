@@ -243,9 +243,13 @@ def bench_headline(args):
     err = float(torch.linalg.norm(x - torch.from_numpy(u).to(dev)) /
                 torch.linalg.norm(torch.from_numpy(u).to(dev)))
     kern = K.sla_profile_iteration_kernels(P, v, b, reps=args.kernel_reps)
+    # the pattern gradient on its own (grad_vals = -lambda_i x_j), event-timed
+    pg_ms = _event_ms(lambda: K.sla_pattern_grad(P, v, gb, x), args.kernel_reps)
+    pg_bytes = pattern_grad_bytes(n, nnz, 4)
     torch.cuda.synchronize()
     res = dict(
         n=n, nnz=nnz, iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
+        pattern_grad=dict(ms=pg_ms, bytes=pg_bytes, GBps=pg_bytes / (pg_ms * 1e-3) / 1e9),
         ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps,
         it_per_s=total_iters / wall,
         eff_GBps=step_bytes * args.steps / wall / 1e9,
@@ -1254,6 +1258,7 @@ def main():
         "library_peak_MB": head["library_peak_MB"],
         "caller_MB": head["caller_MB"],
         "kernel_ms": head["kernel_ms"],
+        "pattern_grad": head["pattern_grad"],
         "roofline": roofline,
         "sizes": sizes,
         "next": nxt,
