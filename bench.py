@@ -225,14 +225,23 @@ def bench_headline(args):
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # events around each half of a step (forward solve, adjoint) as well
+    halves = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+              for _ in range(args.steps)]
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        x, gb, gv, fi, ai = step()
+    for ea, em, ez in halves:
+        ea.record(stream)
+        x, fi = K.sla_cg_solve(P, v, b, 0.0, its)
+        em.record(stream)
+        gb, gv, ai = K.sla_cg_adjoint(P, v, x, g, 0.0, its)
+        ez.record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
+    fwd_ms = sum(ea.elapsed_time(em) for ea, em, _ in halves) / args.steps
+    adj_ms = sum(em.elapsed_time(ez) for _, em, ez in halves) / args.steps
     free1 = torch.cuda.mem_get_info()[0]
     lib1, libpeak = K.sla_memory_usage()
     total_iters = (fi.iterations + ai.iterations) * args.steps
@@ -249,6 +258,7 @@ def bench_headline(args):
     torch.cuda.synchronize()
     res = dict(
         n=n, nnz=nnz, iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
+        forward_ms=fwd_ms, adjoint_ms=adj_ms,
         pattern_grad=dict(ms=pg_ms, bytes=pg_bytes, GBps=pg_bytes / (pg_ms * 1e-3) / 1e9),
         ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps,
         it_per_s=total_iters / wall,
@@ -428,14 +438,16 @@ def bench_poisson32():
     for mode, key in (("auto", "one_group"), ("off", "two_kernel")):
         P = K.sla_csr_create_from_csr(rpt, ct)
         P.set_one_group(mode)
-        times, btimes = [], []
+        times, ftimes, btimes = [], [], []
         for rep in range(22):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            x, fi = K.sla_cg_solve(P, vt, bt, 1e-10, 10000)
+            x, fi = K.sla_cg_solve(P, vt, bt, 1e-10, 10000)  # returns after the solve
+            tm = time.perf_counter()
             gb, gv, ai = K.sla_cg_adjoint(P, vt, x, gt, 1e-10, 10000)
             torch.cuda.synchronize()
             times.append(time.perf_counter() - t0)
+            ftimes.append(tm - t0)
             t0 = time.perf_counter()
             xb, fb = K.sla_cg_solve_batched(P, vbt, bbt, 1e-10, 10000)
             gbb, gvb, ab = K.sla_cg_adjoint_batched(P, vbt, xb, gbt, 1e-10, 10000)
@@ -447,6 +459,8 @@ def bench_poisson32():
         steps = max(i.iterations for i in fb) + max(i.iterations for i in ab)
         out[key] = dict(iterations_fwd=fi.iterations, iterations_adj=ai.iterations,
                         solve_adjoint_ms=ms, us_per_iteration=1e3 * ms / its,
+                        forward_ms=1e3 * float(np.median(ftimes[2:])),
+                        adjoint_ms=1e3 * float(np.median(np.subtract(times, ftimes)[2:])),
                         batch256_ms=bms, batch256_us_per_step=1e3 * bms / steps)
         del P
     out["speedup"] = out["two_kernel"]["solve_adjoint_ms"] / out["one_group"]["solve_adjoint_ms"]
@@ -1258,6 +1272,8 @@ def main():
         "library_peak_MB": head["library_peak_MB"],
         "caller_MB": head["caller_MB"],
         "kernel_ms": head["kernel_ms"],
+        "forward_ms": head["forward_ms"],
+        "adjoint_ms": head["adjoint_ms"],
         "pattern_grad": head["pattern_grad"],
         "roofline": roofline,
         "sizes": sizes,
