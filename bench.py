@@ -1238,6 +1238,8 @@ def main():
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         cpu = cpu_baseline(args.cpu_seconds)
+        # the same system on one thread, a bounded sample
+        cpu["one_thread"] = oracle_one_thread_poisson(1000, 100)
         if nxt:
             log("[bench] CPU oracle beside the NEXT legs")
             for key, val in oracle_next(nxt).items():
