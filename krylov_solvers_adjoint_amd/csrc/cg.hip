@@ -317,8 +317,8 @@ __device__ __forceinline__ double sum_partials_once(const SLA_GLOBAL double* __r
 // iteration (BiCGStab): ND = 1 the partial of wdot.y at part[set0], ND = 2 in
 // addition that of y.y at part[set1] (part[set][blockIdx.x] for system
 // blockIdx.y, `pstride` doubles per system).
-template <typename RP, int NB, int ND = 0>
-__global__ __launch_bounds__(kIterBlock) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+template <typename RP, int NB, int ND = 0, int NT = kIterBlock>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2 * (NT / kWave) / 4)))
 void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
             const uint8_t* __restrict__ mask, BandOffsets band, const double* __restrict__ vals,
             int64_t n, int64_t nnz, int64_t tiles, int cap, const double* __restrict__ x,
@@ -338,7 +338,7 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
   const uint32_t lane = lane_id();
   // each XCD walks a contiguous eighth of the tiles (the grid is a multiple
   // of kXcds), so a tile and the tiles its band reaches share one L2
-  const TileWalk walk = wave_walk(tiles, int(gridDim.x), int(blockIdx.x), kWaves, w);
+  const TileWalk walk = wave_walk(tiles, int(gridDim.x), int(blockIdx.x), NT / kWave, w);
   int64_t t = walk.first;
   double d0 = 0.0, d1 = 0.0;
   // each tile's index data is loaded one tile ahead
@@ -366,7 +366,7 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
   if constexpr (ND > 0) {
     // both sums in one pass: a wave sum each, one barrier, then thread 0
     // adds the waves' sums in wave order
-    __shared__ double red[2][kWaves];
+    __shared__ double red[2][NT / kWave];
     d0 = wave_sum(d0);
     if constexpr (ND > 1) d1 = wave_sum(d1);
     if (lane == 0) {
@@ -376,7 +376,7 @@ void k_spmv(const RP* __restrict__ rowptr, const int32_t* __restrict__ col,
     __syncthreads();
     if (threadIdx.x == 0) {
       double a = 0.0, b = 0.0;
-      for (int q = 0; q < kWaves; ++q) {
+      for (int q = 0; q < NT / kWave; ++q) {
         a = a + red[0][q];
         if constexpr (ND > 1) b = b + red[1][q];
       }
@@ -2146,20 +2146,24 @@ static sla_status launch_spmv_nd(sla_csr A, const double* vals, int64_t batch, c
   const dim3 grid(spmv_grid(A->tiles, batch), unsigned(batch));
   const size_t lds = lds_bytes(A);
   const int nb = band_class(A);
+  // banded rows on 8-wave workgroups once 16 waves would walk 4 tiles or more
+  // each (4000^2 Poisson: 198 vs 214 us per product; at 1000^2, 2 tiles per
+  // wave, 16 waves are faster: 11.3 vs 12.3 us)
+  const bool eight = nb > 0 && A->tiles >= int64_t(grid.x) * 64;
   if (A->rp_idx == SLA_I32) {
-    auto k = nb == 3 ? k_spmv<int32_t, 3, ND>
-             : nb == 5 ? k_spmv<int32_t, 5, ND>
-             : nb == 8 ? k_spmv<int32_t, 8, ND>
+    auto k = nb == 3 ? (eight ? k_spmv<int32_t, 3, ND, 512> : k_spmv<int32_t, 3, ND>)
+             : nb == 5 ? (eight ? k_spmv<int32_t, 5, ND, 512> : k_spmv<int32_t, 5, ND>)
+             : nb == 8 ? (eight ? k_spmv<int32_t, 8, ND, 512> : k_spmv<int32_t, 8, ND>)
              : nb == 0 ? k_spmv<int32_t, 0, ND> : k_spmv<int32_t, -1, ND>;
-    k<<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->band_mask, A->band,
+    k<<<grid, eight ? 512 : kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->band_mask, A->band,
                                      vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y, wdot, part,
                                      pstride, set0, set1);
   } else {
-    auto k = nb == 3 ? k_spmv<int64_t, 3, ND>
-             : nb == 5 ? k_spmv<int64_t, 5, ND>
-             : nb == 8 ? k_spmv<int64_t, 8, ND>
+    auto k = nb == 3 ? (eight ? k_spmv<int64_t, 3, ND, 512> : k_spmv<int64_t, 3, ND>)
+             : nb == 5 ? (eight ? k_spmv<int64_t, 5, ND, 512> : k_spmv<int64_t, 5, ND>)
+             : nb == 8 ? (eight ? k_spmv<int64_t, 8, ND, 512> : k_spmv<int64_t, 8, ND>)
              : nb == 0 ? k_spmv<int64_t, 0, ND> : k_spmv<int64_t, -1, ND>;
-    k<<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->band_mask, A->band,
+    k<<<grid, eight ? 512 : kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->band_mask, A->band,
                                      vals, A->n, A->nnz, A->tiles, A->wave_cap, x, y, wdot, part,
                                      pstride, set0, set1);
   }

@@ -275,15 +275,16 @@ def test_fullsize_convection_diffusion():
     assert rel(x, xo) <= 1e-4
 
 
-def test_fullsize_convection_diffusion_first_iterations():
-    """The same 10^6-unknown grid, 20 fixed iterations (tol 0): x within 1e-8
-    of the oracle's and rho, alpha, omega, r.r of every iteration within
+@pytest.mark.parametrize("N", [1000, 2000])
+def test_fullsize_convection_diffusion_first_iterations(N):
+    """The same 10^6-unknown grid (and 2000^2, whose SpMVs take the 8-wave
+    form with the fused dot partials), 20 fixed iterations (tol 0): x within
+    1e-8 of the oracle's and rho, alpha, omega, r.r of every iteration within
     1e-7.  BiCGStab on this matrix is chaotic under rounding (one-ulp changes
     of five entries of b move the oracle's own x by 1e-11 after 20
     iterations and by 4e-2 after 50), so element-wise parity is checked where
     it is defined, and the converged solve above by its residual."""
     import krylov_solvers_adjoint_amd as K
-    N = 1000
     rp, c, v = W.convection_diffusion_csr(N)
     b = W.normal_rhs(N * N, 90)
     oracle.set_threads(oracle.host_threads())
@@ -291,5 +292,5 @@ def test_fullsize_convection_diffusion_first_iterations():
     rho, alpha, omega, rr = K.sla_bicgstab_history(P)
     assert info.iterations == io.iterations == 20 and len(rr) == 20
     d = [float(np.max(np.abs(g - o) / np.abs(o))) for g, o in zip((rho, alpha, omega, rr), ho)]
-    say(f"1000^2, 20 iterations: x {rel(x, xo):.1e}; rho/alpha/omega/rr {max(d):.1e}")
+    say(f"{N}^2, 20 iterations: x {rel(x, xo):.1e}; rho/alpha/omega/rr {max(d):.1e}")
     assert rel(x, xo) <= TOL_X and max(d) <= 1e-7
