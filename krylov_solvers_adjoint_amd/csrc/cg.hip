@@ -1330,11 +1330,12 @@ void k_cg_product(const Ctx* __restrict__ c) {
 // tiles hold at most kWaveCap slots each, the two-kernel iteration is bound
 // by launch gaps and by every workgroup summing partials.  Here one workgroup
 // owns a system and iterates with workgroup barriers only (no cross-workgroup
-// signal exists), with nothing in memory but LDS:
-//   * thread t owns rows t + j * kIterBlock (j < R) and keeps their r, x, p
-//     (and the Jacobi diagonal) in registers;
-//   * wave w owns tiles w + j * kWaves; lane l holds the values and columns
-//     of slots l, l + 64, ... of each of its tiles in registers, loaded once;
+// signal exists), with nothing in memory but LDS.  With NT threads (256, 512
+// or 1024 by size, one_group_block) of W = NT / 64 waves:
+//   * thread t owns rows t + j * NT (j < R) and keeps their r, x, p (and the
+//     Jacobi diagonal) in registers;
+//   * wave w owns tiles w + j * W; lane l holds the values and columns of
+//     slots l, l + 64, ... of each of its tiles in registers, loaded once;
 //   * p is published in LDS; an SpMV gathers p from LDS at the held columns,
 //     stores the products in the wave's LDS area and each lane adds its own
 //     row's products in slot order (the bits of the sequential row sum).
@@ -1342,20 +1343,22 @@ void k_cg_product(const Ctx* __restrict__ c) {
 // x update is applied at once rather than one step late (the same
 // expression); the dot products are summed in another fixed order.
 
-// Two sums over the workgroup at once, fixed order, results in every thread.
+// Two sums over a workgroup of W waves at once, fixed order, results in every
+// thread.
+template <int W = kWaves>
 __device__ __forceinline__ void block_sum2(double& u, double& v, double* lds) {
   u = wave_sum(u);
   v = wave_sum(v);
   if ((threadIdx.x & (kWave - 1)) == 0) {
     lds[threadIdx.x / kWave] = u;
-    lds[kWaves + threadIdx.x / kWave] = v;
+    lds[W + threadIdx.x / kWave] = v;
   }
   __syncthreads();
   double a = 0.0, b = 0.0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     a = a + lds[w];
-    b = b + lds[kWaves + w];
+    b = b + lds[W + w];
   }
   __syncthreads();
   u = a;
@@ -1365,50 +1368,63 @@ __device__ __forceinline__ void block_sum2(double& u, double& v, double* lds) {
 // The same sums without the closing barrier, for a loop that alternates two
 // `lds` areas: the next use of an area comes after another sum's barrier, by
 // which every thread has read it.  sum1 is the one-value form.
+template <int W = kWaves>
 __device__ __forceinline__ void block_sum2_open(double& u, double& v, double* lds) {
   u = wave_sum(u);
   v = wave_sum(v);
   if ((threadIdx.x & (kWave - 1)) == 0) {
     lds[threadIdx.x / kWave] = u;
-    lds[kWaves + threadIdx.x / kWave] = v;
+    lds[W + threadIdx.x / kWave] = v;
   }
   __syncthreads();
   double a = 0.0, b = 0.0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     a = a + lds[w];
-    b = b + lds[kWaves + w];
+    b = b + lds[W + w];
   }
   u = a;
   v = b;
 }
+template <int W = kWaves>
 __device__ __forceinline__ double block_sum1_open(double u, double* lds) {
   u = wave_sum(u);
   if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = u;
   __syncthreads();
   double a = 0.0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) a = a + lds[w];
+  for (int w = 0; w < W; ++w) a = a + lds[w];
   return a;
 }
+
+// Threads per workgroup of the small-system kernel: the smallest of 256, 512
+// and 1024 that leaves each thread at most two rows at 1024 unknowns or more,
+// and one below.  Per iteration (Poisson, the same run): 144 and 256
+// unknowns 2.26 -> 1.3 us with 256 threads instead of 1024, 484 unknowns 2.29
+// -> 1.54 us with 512 (1.65 with 256 and two rows each), 1024 unknowns 2.52
+// -> 2.0 us with 512, 2025 unknowns 3.0 us with 1024 (2.95 with 512 and four
+// rows each): fewer waves meet at every barrier and sum fewer partials.
+int one_group_block(int64_t n) { return n <= 256 ? 256 : (n <= 1024 ? 512 : 1024); }
 
 // LDS of the small-system kernel: p [n rounded up to the workgroup] and one
 // product area of kWaveCap doubles per wave.
 size_t one_group_lds_bytes(int64_t n) {
-  const int64_t rows = (n + kIterBlock - 1) / kIterBlock * kIterBlock;
-  return size_t(rows + int64_t(kWaves) * kWaveCap) * sizeof(double);
+  const int64_t nt = one_group_block(n);
+  const int64_t rows = (n + nt - 1) / nt * nt;
+  return size_t(rows + (nt / kWave) * kWaveCap) * sizeof(double);
 }
 
-template <typename RP, int R, bool JAC>
-__global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restrict__ c,
+template <typename RP, int R, bool JAC, int NT>
+__global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
                                                             double tol, int64_t maxit,
                                                             int use_x0) {
+  constexpr int W = NT / kWave;
   extern __shared__ double lds_dyn[];
-  __shared__ double red[2 * kWaves];
-  __shared__ double red_a[kWaves], red_b[2 * kWaves];  // the loop's two areas
+  __shared__ double red[2 * W];
+  __shared__ double red_a[W], red_b[2 * W];  // the loop's two areas
   const int64_t s = blockIdx.x;
   const int64_t n = c->n, nnz = c->nnz;
-  const int64_t npad = (n + kIterBlock - 1) / kIterBlock * kIterBlock;
+  const int64_t npad = (n + NT - 1) / NT * NT;
   double* pl = lds_dyn;                                         // p, or x0 at set-up
   double* prod = lds_dyn + npad + int64_t(wave_index()) * kWaveCap;  // this wave's products
   const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(c->rowptr));
@@ -1427,7 +1443,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
   int32_t hc[R][kStageLoads];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const int64_t r0 = (int64_t(j) * kWaves + wave_index()) * kTileRows;
+    const int64_t r0 = (int64_t(j) * W + wave_index()) * kTileRows;
     row[j] = r0 + lane;
     rlen[j] = ra[j] = re[j] = 0;
     if (r0 < n) {
@@ -1479,7 +1495,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
   double r[R], xv[R], pv[R], dv[R], q[R];
   // r0 = b - A x0 (or b, x0 = 0); the Jacobi diagonal
   if (use_x0) {
-    for (int64_t i = t; i < npad; i += kIterBlock) pl[i] = i < n ? x[i] : 0.0;
+    for (int64_t i = t; i < npad; i += NT) pl[i] = i < n ? x[i] : 0.0;
     __syncthreads();
     spmv(q);
     __syncthreads();
@@ -1487,7 +1503,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
   double bb = 0.0, rr = 0.0, rz = 0.0, bad = 0.0;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const int64_t i = t + int64_t(j) * kIterBlock;
+    const int64_t i = t + int64_t(j) * NT;
     r[j] = xv[j] = pv[j] = 0.0;
     dv[j] = 1.0;
     if (i < n) {
@@ -1506,8 +1522,8 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
       }
     }
   }
-  block_sum2(bb, rr, red);
-  if constexpr (JAC) block_sum2(rz, bad, red);
+  block_sum2<W>(bb, rr, red);
+  if constexpr (JAC) block_sum2<W>(rz, bad, red);
   const double stop = (tol * tol) * bb;
   int32_t state = (!isfinite(bb) || !isfinite(rr) || !isfinite(rz)) ? ST_NONFINITE : ST_RUNNING;
   if (JAC && bad != 0.0) state = ST_NOT_SPD;  // a diagonal entry is not > 0
@@ -1542,7 +1558,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
     for (int j = 0; j < R; ++j) {
       const double src = JAC ? r[j] / dv[j] : r[j];
       pv[j] = src + beta * pv[j];
-      const int64_t i = t + int64_t(j) * kIterBlock;
+      const int64_t i = t + int64_t(j) * NT;
       if (i < npad) pl[i] = pv[j];
     }
     __syncthreads();
@@ -1550,10 +1566,10 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
     double pq = 0.0;
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      if (t + int64_t(j) * kIterBlock < n) pq = pq + pv[j] * q[j];
+      if (t + int64_t(j) * NT < n) pq = pq + pv[j] * q[j];
     // (the barrier of the sum also ends every wave's gathers of p_k; red_a
     // was last read before the previous iteration's second sum)
-    pq = block_sum1_open(pq, red_a);
+    pq = block_sum1_open<W>(pq, red_a);
     if (!isfinite(pq) || !(pq > 0.0)) {
       state = !isfinite(pq) ? ST_NONFINITE : ST_NOT_SPD;
       it = k;
@@ -1564,7 +1580,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
     double rn = 0.0, rzn = 0.0;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      if (t + int64_t(j) * kIterBlock < n) {
+      if (t + int64_t(j) * NT < n) {
         xv[j] = xv[j] + alpha * pv[j];
         r[j] = r[j] - alpha * q[j];
         rn = rn + r[j] * r[j];
@@ -1572,7 +1588,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
       }
     }
     // (red_b was last read before this iteration's first sum)
-    block_sum2_open(rn, rzn, red_b);
+    block_sum2_open<W>(rn, rzn, red_b);
     rr_prev = rr;
     rz_prev = rz;
     rr = rn;
@@ -1580,7 +1596,7 @@ __global__ __launch_bounds__(kIterBlock) void k_cg_onegroup(const Ctx* __restric
   }
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const int64_t i = t + int64_t(j) * kIterBlock;
+    const int64_t i = t + int64_t(j) * NT;
     if (i < n) x[i] = xv[j];
   }
   if (t == 0) {
@@ -2224,11 +2240,22 @@ static int one_group_rows(const sla_csr A) {
           hipSuccess ||
       one_group_lds_bytes(A->n) + 5 * kWaves * sizeof(double) > size_t(lim))  // + red*
     return 0;
-  return A->n <= kIterBlock ? 1 : 2;
+  return A->n <= one_group_block(A->n) ? 1 : 2;
 }
 
 bool use_one_group(const sla_csr A) {
   return A->one_group == SLA_ONE_GROUP_AUTO && one_group_rows(A) > 0;
+}
+
+// The small-system kernel for two rows per thread or one, Jacobi or not, and
+// nt threads per workgroup.
+template <typename RP>
+static auto one_group_kernel(bool two, bool jac, int nt) {
+#define SLA_OG(R_, NT_) (jac ? k_cg_onegroup<RP, R_, true, NT_> : k_cg_onegroup<RP, R_, false, NT_>)
+  if (nt == 256) return two ? SLA_OG(2, 256) : SLA_OG(1, 256);
+  if (nt == 512) return two ? SLA_OG(2, 512) : SLA_OG(1, 512);
+  return two ? SLA_OG(2, 1024) : SLA_OG(1, 1024);
+#undef SLA_OG
 }
 
 static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch, bool jac,
@@ -2237,14 +2264,13 @@ static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch,
   const unsigned g = unsigned(batch);
   const int u = x0 ? 1 : 0;
   const bool two = one_group_rows(A) == 2;
+  const int nt = one_group_block(A->n);
   if (A->rp_idx == SLA_I32) {
-    auto k = two ? (jac ? k_cg_onegroup<int32_t, 2, true> : k_cg_onegroup<int32_t, 2, false>)
-                 : (jac ? k_cg_onegroup<int32_t, 1, true> : k_cg_onegroup<int32_t, 1, false>);
-    k<<<g, kIterBlock, lds, st>>>(ctx_dev, tol, maxit, u);
+    auto k = one_group_kernel<int32_t>(two, jac, nt);
+    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u);
   } else {
-    auto k = two ? (jac ? k_cg_onegroup<int64_t, 2, true> : k_cg_onegroup<int64_t, 2, false>)
-                 : (jac ? k_cg_onegroup<int64_t, 1, true> : k_cg_onegroup<int64_t, 1, false>);
-    k<<<g, kIterBlock, lds, st>>>(ctx_dev, tol, maxit, u);
+    auto k = one_group_kernel<int64_t>(two, jac, nt);
+    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u);
   }
   LAUNCH_CHECK();
   return SLA_OK;
