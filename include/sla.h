@@ -585,8 +585,9 @@ sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
 
 /*
  * CG loop of small systems.  SLA_ONE_GROUP_AUTO (default): a system of at
- * most 2048 unknowns whose 64-row tiles hold at most 336 stored entries each
- * (and whose vectors fit one workgroup's LDS) runs its whole CG loop in one
+ * most 2048 unknowns with a banded pattern (at most 8 column offsets), or
+ * whose 64-row tiles hold at most 336 stored entries each (and whose vectors
+ * fit one workgroup's LDS), runs its whole CG loop in one
  * workgroup (one launch per solve, one workgroup per system of the batch,
  * workgroup barriers only),
  * instead of two kernels over the whole GPU per iteration, whose launch gaps

@@ -265,8 +265,9 @@ class CSRPattern:
         _check(_lib.sla_csr_set_workgroups_per_cu(self._h, int(workgroups)))
 
     def set_one_group(self, mode: str = "auto"):
-        """"auto": systems of up to 2048 unknowns (64-row tiles of at most
-        336 stored entries) run the CG loop in one workgroup per system;
+        """"auto": systems of up to 2048 unknowns (a banded pattern, or
+        64-row tiles of at most 336 stored entries) run the CG loop in one
+        workgroup per system;
         "off": always the two-kernel loop."""
         _check(_lib.sla_csr_set_one_group(self._h, {"auto": ONE_GROUP_AUTO,
                                                     "off": ONE_GROUP_OFF}[mode]))

@@ -1326,19 +1326,23 @@ void k_cg_product(const Ctx* __restrict__ c) {
 // ---------------------------------------------------------------------------
 // Small systems: one workgroup per system, the whole CG loop in one launch
 // ---------------------------------------------------------------------------
-// For a system of at most kOneGroupRows * kIterBlock unknowns whose 64-row
-// tiles hold at most kWaveCap slots each, the two-kernel iteration is bound
+// For a system of at most kOneGroupMaxN unknowns (banded, or with 64-row
+// tiles of at most kWaveCap slots each), the two-kernel iteration is bound
 // by launch gaps and by every workgroup summing partials.  Here one workgroup
 // owns a system and iterates with workgroup barriers only (no cross-workgroup
-// signal exists), with nothing in memory but LDS.  With NT threads (256, 512
-// or 1024 by size, one_group_block) of W = NT / 64 waves:
-//   * thread t owns rows t + j * NT (j < R) and keeps their r, x, p (and the
-//     Jacobi diagonal) in registers;
-//   * wave w owns tiles w + j * W; lane l holds the values and columns of
-//     slots l, l + 64, ... of each of its tiles in registers, loaded once;
-//   * p is published in LDS; an SpMV gathers p from LDS at the held columns,
-//     stores the products in the wave's LDS area and each lane adds its own
-//     row's products in slot order (the bits of the sequential row sum).
+// signal exists), with nothing in memory but LDS.  With NT threads (256 or
+// 512 by size, one_group_block) of W = NT / 64 waves:
+//   * thread t owns rows t + j * NT (j < R, R = 1, 2 or 4) and keeps their
+//     r, x, p (and the Jacobi diagonal) in registers;
+//   * p is published in LDS and every SpMV gathers it there;
+//   * banded rows: each thread holds its rows' values by band offset, loaded
+//     once, and adds value x p[i + off] in ascending offset order;
+//   * plain CSR rows: wave w owns tiles w + j * W; lane l holds the values
+//     and columns of slots l, l + 64, ... of each of its tiles, loaded once;
+//     the SpMV stores the products in the wave's LDS area and each lane adds
+//     its own row's products in slot order.
+// Both add a row's products in ascending column order (the bits of the
+// sequential row sum).
 // Same steps, stopping rule, statuses and history as the two-kernel loop; the
 // x update is applied at once rather than one step late (the same
 // expression); the dot products are summed in another fixed order.
@@ -1397,24 +1401,38 @@ __device__ __forceinline__ double block_sum1_open(double u, double* lds) {
   return a;
 }
 
-// Threads per workgroup of the small-system kernel: the smallest of 256, 512
-// and 1024 that leaves each thread at most two rows at 1024 unknowns or more,
-// and one below.  Per iteration (Poisson, the same run): 144 and 256
-// unknowns 2.26 -> 1.3 us with 256 threads instead of 1024, 484 unknowns 2.29
-// -> 1.54 us with 512 (1.65 with 256 and two rows each), 1024 unknowns 2.52
-// -> 2.0 us with 512, 2025 unknowns 3.0 us with 1024 (2.95 with 512 and four
-// rows each): fewer waves meet at every barrier and sum fewer partials.
-int one_group_block(int64_t n) { return n <= 256 ? 256 : (n <= 1024 ? 512 : 1024); }
-
-// LDS of the small-system kernel: p [n rounded up to the workgroup] and one
-// product area of kWaveCap doubles per wave.
-size_t one_group_lds_bytes(int64_t n) {
-  const int64_t nt = one_group_block(n);
-  const int64_t rows = (n + nt - 1) / nt * nt;
-  return size_t(rows + (nt / kWave) * kWaveCap) * sizeof(double);
+// Threads per workgroup of the small-system kernel: 256 up to 256 unknowns
+// (and up to 512 for banded rows, two rows per thread), 512 above, with up
+// to four rows per thread.  Fewer waves meet at every barrier and sum fewer
+// partials; the staged CSR rows prefer one row per thread at 257-512
+// unknowns.  Per iteration, Poisson (banded rows, the same run): 484
+// unknowns 1.29 -> 1.10 us with 256 threads instead of 512, 1024 unknowns
+// 1.42 us with 512 (1.52 with 256 and four rows each), 2025 unknowns 2.40 ->
+// 1.91 us with 512 and four rows each instead of 1024 and two.
+int one_group_block(int64_t n, bool band) {
+  return n <= 256 || (band && n <= 512) ? 256 : 512;
 }
 
-template <typename RP, int R, bool JAC, int NT>
+// Rows per thread of the small-system kernel: 1, 2 or 4.
+int one_group_rows_per_thread(int64_t n, bool band) {
+  const int64_t nt = one_group_block(n, band);
+  return n <= nt ? 1 : (n <= 2 * nt ? 2 : 4);
+}
+
+// LDS of the small-system kernel: p [n rounded up to the workgroup] and, for
+// plain CSR rows, one product area of kWaveCap doubles per wave.
+size_t one_group_lds_bytes(int64_t n, bool band) {
+  const int64_t nt = one_group_block(n, band);
+  const int64_t rows = (n + nt - 1) / nt * nt;
+  return size_t(rows + (band ? 0 : (nt / kWave) * kWaveCap)) * sizeof(double);
+}
+
+// BAND: a banded pattern (the context's mask and offsets).  Each thread then
+// holds its rows' values by band offset and adds value x p[i + off] straight
+// from the LDS copy of p in ascending offset (= column) order, which is the
+// slot order the staged CSR rows are summed in: the same bits without the
+// product area and its two wave barriers per tile.
+template <typename RP, int R, bool JAC, int NT, bool BAND>
 __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
                                                             double tol, int64_t maxit,
                                                             int use_x0) {
@@ -1436,17 +1454,37 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
   const int64_t hist_cap = c->hist_cap;
   const int t = threadIdx.x;
   const int lane = int(lane_id());
-  // this thread's rows and tiles; the held slots of each tile
+  // this thread's rows and tiles; the held slots of each tile (CSR), or the
+  // rows' values by band offset (BAND)
   int64_t row[R];
   int rlen[R], ra[R], re[R];   // tile length; the row's slots [ra, re) in the tile
   double hv[R][kStageLoads];
   int32_t hc[R][kStageLoads];
+  double bv[R][kMaxBand];
+  uint32_t bm[R];              // the row's bits among the band's offsets
+  int32_t boff[kMaxBand];      // the offsets (uniform)
+#pragma unroll
+  for (int o = 0; o < kMaxBand; ++o) boff[o] = BAND ? c->band.off[o] : 0;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int64_t r0 = (int64_t(j) * W + wave_index()) * kTileRows;
     row[j] = r0 + lane;
     rlen[j] = ra[j] = re[j] = 0;
-    if (r0 < n) {
+    if constexpr (BAND) {
+      const int cnt = c->band.count;
+      bm[j] = 0;
+      int64_t k = 0;
+      if (row[j] < n) {
+        bm[j] = uint32_t(c->mask[row[j]]) & ((1u << cnt) - 1u);
+        k = int64_t(rowptr[row[j]]);
+      }
+#pragma unroll
+      for (int o = 0; o < kMaxBand; ++o) {
+        const bool use = (bm[j] >> o) & 1u;
+        bv[j][o] = use ? vals[k] : 0.0;
+        k += use ? 1 : 0;
+      }
+    } else if (r0 < n) {
       const int64_t last = (r0 + kTileRows < n ? r0 + kTileRows : n);
       const int64_t s0 = int64_t(rowptr[r0]);
       rlen[j] = int(int64_t(rowptr[last]) - s0);
@@ -1469,7 +1507,19 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       q[j] = 0.0;
-      if (rlen[j] > 0) {  // wave-uniform
+      if constexpr (BAND) {
+        double g[kMaxBand];
+#pragma unroll
+        for (int o = 0; o < kMaxBand; ++o)
+          g[o] = pl[((bm[j] >> o) & 1u) ? int32_t(row[j]) + boff[o] : 0];
+        double acc = 0.0;
+#pragma unroll
+        for (int o = 0; o < kMaxBand; ++o) {
+          const double sum = acc + bv[j][o] * g[o];
+          acc = ((bm[j] >> o) & 1u) ? sum : acc;
+        }
+        q[j] = acc;
+      } else if (rlen[j] > 0) {  // wave-uniform
 #pragma unroll
         for (int m = 0; m < kStageLoads; ++m) {
           const int k = lane + m * kWave;
@@ -2229,47 +2279,71 @@ sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda, c
 static sla_status finish_cg(const CgSpace& sp, int64_t batch, sla_cg_info* info,
                             hipStream_t st);
 
-// Rows per thread of the small-system kernel (1 or 2), 0 when it does not
-// apply: more than kOneGroupRows * kIterBlock unknowns, a 64-row tile with
-// more slots than a wave holds, or LDS beyond the device's limit.
+// Rows per thread of the small-system kernel (1, 2 or 4), 0 when it does not
+// apply: more than kOneGroupMaxN unknowns, plain CSR rows whose 64-row tile
+// has more slots than a wave stages, or LDS beyond the device's limit.
 static int one_group_rows(const sla_csr A) {
-  if (A->n <= 0 || A->n > int64_t(kOneGroupRows) * kIterBlock) return 0;
-  if (A->max_tile_nnz > kWaveCap) return 0;
+  if (A->n <= 0 || A->n > kOneGroupMaxN) return 0;
+  const bool band = use_band(A);
+  if (!band && A->max_tile_nnz > kWaveCap) return 0;
   int lim = 0;
   if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, A->device) !=
           hipSuccess ||
-      one_group_lds_bytes(A->n) + 5 * kWaves * sizeof(double) > size_t(lim))  // + red*
+      one_group_lds_bytes(A->n, band) + 5 * kWaves * sizeof(double) > size_t(lim))  // + red*
     return 0;
-  return A->n <= one_group_block(A->n) ? 1 : 2;
+  return one_group_rows_per_thread(A->n, band);
 }
 
 bool use_one_group(const sla_csr A) {
   return A->one_group == SLA_ONE_GROUP_AUTO && one_group_rows(A) > 0;
 }
 
-// The small-system kernel for two rows per thread or one, Jacobi or not, and
-// nt threads per workgroup.
-template <typename RP>
-static auto one_group_kernel(bool two, bool jac, int nt) {
-#define SLA_OG(R_, NT_) (jac ? k_cg_onegroup<RP, R_, true, NT_> : k_cg_onegroup<RP, R_, false, NT_>)
-  if (nt == 256) return two ? SLA_OG(2, 256) : SLA_OG(1, 256);
-  if (nt == 512) return two ? SLA_OG(2, 512) : SLA_OG(1, 512);
-  return two ? SLA_OG(2, 1024) : SLA_OG(1, 1024);
+// The small-system kernel for `rows` rows per thread and `nt` threads per
+// workgroup (one_group_rows, one_group_block), Jacobi or not, banded rows or
+// plain CSR; nullptr for a combination the size rule never picks.
+using OneGroupFn = void (*)(const Ctx*, double, int64_t, int);
+
+template <typename RP, bool BAND>
+static OneGroupFn one_group_kernel(int rows, int nt, bool jac) {
+#define SLA_OG(R_, NT_) \
+  (jac ? k_cg_onegroup<RP, R_, true, NT_, BAND> : k_cg_onegroup<RP, R_, false, NT_, BAND>)
+  if (nt == 256) {
+    if (rows == 1) return SLA_OG(1, 256);
+    if constexpr (BAND)
+      if (rows == 2) return SLA_OG(2, 256);
+  } else if (nt == 512) {
+    if constexpr (!BAND)
+      if (rows == 1) return SLA_OG(1, 512);
+    if (rows == 2) return SLA_OG(2, 512);
+    if (rows == 4) return SLA_OG(4, 512);
+  }
+  return nullptr;
 #undef SLA_OG
 }
 
 static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch, bool jac,
                                    double tol, int64_t maxit, bool x0, hipStream_t st) {
-  const size_t lds = one_group_lds_bytes(A->n);
+  const bool band = use_band(A);
+  const size_t lds = one_group_lds_bytes(A->n, band);
   const unsigned g = unsigned(batch);
   const int u = x0 ? 1 : 0;
-  const bool two = one_group_rows(A) == 2;
-  const int nt = one_group_block(A->n);
+  const int rows = one_group_rows(A);
+  const int nt = one_group_block(A->n, band);
   if (A->rp_idx == SLA_I32) {
-    auto k = one_group_kernel<int32_t>(two, jac, nt);
+    auto k = band ? one_group_kernel<int32_t, true>(rows, nt, jac)
+                  : one_group_kernel<int32_t, false>(rows, nt, jac);
+    if (k == nullptr) {
+      set_error("small-system kernel: no variant for %d rows x %d threads", rows, nt);
+      return SLA_ERR_DEVICE;
+    }
     k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u);
   } else {
-    auto k = one_group_kernel<int64_t>(two, jac, nt);
+    auto k = band ? one_group_kernel<int64_t, true>(rows, nt, jac)
+                  : one_group_kernel<int64_t, false>(rows, nt, jac);
+    if (k == nullptr) {
+      set_error("small-system kernel: no variant for %d rows x %d threads", rows, nt);
+      return SLA_ERR_DEVICE;
+    }
     k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u);
   }
   LAUNCH_CHECK();

@@ -93,9 +93,9 @@ constexpr int64_t kLocalSpan = int64_t(1) << 17;
 // solves of at most this many unknowns (over the batch) run one solver
 // workgroup per CU unless the handle asks otherwise
 constexpr int64_t kSmallSolve = int64_t(1) << 21;
-// the one-workgroup CG solver takes systems of up to kOneGroupRows rows per
-// thread (2048 unknowns; beyond, one CU per system is slower than the grid)
-constexpr int kOneGroupRows = 2;
+// the one-workgroup CG solver takes systems of up to this many unknowns
+// (beyond, one CU per system is slower than the grid)
+constexpr int64_t kOneGroupMaxN = 2048;
 
 // Column offsets j - i of a banded pattern, ascending: row i's slots are the
 // columns i + off[t] for the bits t set in its mask byte.

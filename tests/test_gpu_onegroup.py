@@ -1,8 +1,9 @@
-"""The one-workgroup CG loop for small systems (at most 2048 unknowns, 64-row
-tiles of at most 336 slots): ragged sizes, Jacobi, history, warm starts,
-statuses and batches against the oracle, in the default (automatic) mode and
-with the two-kernel loop forced; systems outside its range take the
-two-kernel loop bit for bit."""
+"""The one-workgroup CG loop for small systems (at most 2048 unknowns; a
+banded pattern, or plain CSR rows whose 64-row tiles hold at most 336 slots):
+ragged sizes, Jacobi, history, warm starts, statuses and batches against the
+oracle, in the default (automatic) mode and with the two-kernel loop forced;
+banded rows against the staged CSR rows bit for bit; systems outside its range
+take the two-kernel loop bit for bit."""
 import numpy as np
 import pytest
 
@@ -78,11 +79,12 @@ def test_mode_argument():
 
 
 def test_outside_the_range_takes_the_two_kernel_loop():
-    """2049 unknowns, or tiles of more than 336 slots (7 per row): the
-    automatic mode gives the two-kernel loop's bits."""
+    """2049 unknowns, or plain CSR tiles of more than 336 slots (9 per row,
+    more offsets than a band holds): the automatic mode gives the two-kernel
+    loop's bits."""
     import torch
     import krylov_solvers_adjoint_amd as K
-    for n, offs in ((2049, (-37, -1, 1, 37)), (1000, (-3, -2, -1, 1, 2, 3))):
+    for n, offs in ((2049, (-37, -1, 1, 37)), (1000, (-4, -3, -2, -1, 1, 2, 3, 4))):
         rp, c, v = _banded(n, offs, 7)
         b = W.normal_rhs(n, 8)
         xs = []
@@ -92,6 +94,77 @@ def test_outside_the_range_takes_the_two_kernel_loop():
             torch.cuda.synchronize()
             xs.append((x.cpu().numpy(), info.iterations))
         assert np.array_equal(xs[0][0], xs[1][0]) and xs[0][1] == xs[1][1]
+
+
+@pytest.mark.parametrize("n,offs", [(1024, (-32, -1, 1, 32)), (777, (-29, -2, 2, 29)),
+                                    (2048, (-45, -1, 1, 45)), (1500, (-40, -1, 1, 40)),
+                                    (400, (-20, -1, 1, 20)), (65, (-1, 1)),
+                                    (256, (-16, -1, 1, 16))])
+def test_banded_rows_match_staged_csr_rows(n, offs):
+    """A banded pattern runs the loop with each row's values held by band
+    offset; the same pattern forced onto plain CSR rows (products staged in
+    LDS) gives the same bits, forward and adjoint, with and without Jacobi:
+    both add a row's products in ascending column order.  Between 257 and
+    512 unknowns the two take different workgroup shapes (256 threads with
+    two banded rows each, 512 with one staged row), so their dot products
+    are summed in different orders: there both are held to the oracle
+    only."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    rp, c, v = _banded(n, offs, n + 1)
+    A = _A(rp, c, v)
+    b = W.normal_rhs(n, 21)
+    g = W.normal_rhs(n, 22)
+    P1 = csr_handle(rp, c)
+    P2 = csr_handle(rp, c)
+    P2.set_spmv_variant("csr")
+    assert P1.banded and not P2.banded
+    vt = t(v)
+    for jac in (False, True):
+        out = []
+        for P in (P1, P2):
+            x, info = K.sla_cg_solve(P, vt, t(b), 1e-11, 5000, jacobi=jac)
+            gb, gv, ai = K.sla_cg_adjoint(P, vt, x, t(g), 1e-11, 5000, jacobi=jac)
+            torch.cuda.synchronize()
+            out.append((x.cpu().numpy(), gb.cpu().numpy(), gv.cpu().numpy(),
+                        info.iterations, ai.iterations))
+        if not 256 < n <= 512:
+            for a1, a2 in zip(out[0], out[1]):
+                assert np.array_equal(a1, a2)
+        xo, io = (oracle.pcg_jacobi if jac else oracle.cg)(A, b, 1e-11, 5000)
+        for o in out:
+            say(f"n={n} jacobi={jac}: it {o[3]}/{io.iterations} x {rel(o[0], xo):.1e}")
+            assert iters_close(o[3], io.iterations) and rel(o[0], xo) <= TOL_X
+
+
+def test_wide_band_in_range():
+    """Seven offsets (448 slots per 64-row tile, more than the staged CSR
+    rows take): the banded loop runs it, against the oracle and against the
+    two-kernel loop's iterate."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    n = 1000
+    rp, c, v = _banded(n, (-3, -2, -1, 1, 2, 3), 31)
+    A = _A(rp, c, v)
+    b = W.normal_rhs(n, 32)
+    g = W.normal_rhs(n, 33)
+    xo, io = oracle.cg(A, b, 1e-11, 5000)
+    gbo, gvo, aio = oracle.adjoint(A, xo, g, 1e-11, 5000)
+    res = []
+    for mode in ("auto", "off"):
+        P = csr_handle(rp, c, one_group=mode)
+        assert P.banded
+        x, info = K.sla_cg_solve(P, t(v), t(b), 1e-11, 5000)
+        gb, gv, ai = K.sla_cg_adjoint(P, t(v), x, t(g), 1e-11, 5000)
+        torch.cuda.synchronize()
+        x, gb, gv = x.cpu().numpy(), gb.cpu().numpy(), gv.cpu().numpy()
+        assert info.converged and ai.converged
+        assert iters_close(info.iterations, io.iterations)
+        assert iters_close(ai.iterations, aio.iterations)
+        assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+        res.append(x)
+    # the two loops sum their dot products in different orders
+    assert not np.array_equal(res[0], res[1])
 
 
 def test_history_warm_start_and_reproducibility():
