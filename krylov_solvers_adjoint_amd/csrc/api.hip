@@ -462,6 +462,10 @@ static sla_status check_solve(sla_csr A, const void* b, const void* x, double to
 // every CG solve and adjoint.  The adjoint, which solves with A in place of
 // A^T, also checks the bound values on every call (mirror entries equal to
 // within 1e-12 relative).
+static const char kValuesNotSymmetric[] =
+    "%s: the values are not symmetric (a_ij and a_ji differ by more than 1e-12 relative); "
+    "the adjoint solves with A in place of A^T";
+
 static sla_status require_symmetric(sla_csr A, bool values, const char* who,
                                     hipStream_t stream) {
   if (A->sym_pattern < 0) {
@@ -478,8 +482,7 @@ static sla_status require_symmetric(sla_csr A, bool values, const char* who,
     int bad = 0;
     SLA_TRY(check_symmetry(A, true, &bad, stream));
     if (bad) {
-      set_error("%s: the values are not symmetric (a_ij and a_ji differ by more than 1e-12 "
-                "relative); the adjoint solves with A in place of A^T", who);
+      set_error(kValuesNotSymmetric, who);
       return SLA_ERR_NOT_SYMMETRIC;
     }
   }
@@ -529,10 +532,29 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol, int64
 // A^T lambda = grad_x with A^T = A (CG requires a symmetric matrix; checked
 // first), then the pattern gradient (also from the last iterate after a
 // breakdown), on A's own slots whether or not the solve ran on a reordered
-// copy.
+// copy.  Systems on the one-workgroup loop take the values' check on the
+// device: its flag stops the solve and the pattern gradient there, and one
+// read-back at the end reports the refusal (no round trip before the solve,
+// which at such sizes costs more than the solve's own launch).
 static sla_status run_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
+  if (A->ro == nullptr && use_one_group(A)) {
+    const sla_status ps = require_symmetric(A, false, "sla_cg_adjoint", stream);
+    if (ps != SLA_OK) {
+      fill_status(info, A->batch, ps);
+      return ps;
+    }
+    int* gate = nullptr;
+    SLA_TRY(enqueue_symmetry_check(A, true, stream, &gate));
+    AdjointTail tail;
+    tail.gate = gate;
+    tail.x = x;
+    tail.grad_vals = grad_vals;
+    const sla_status s = run_cg(A, grad_x, grad_b, tol, maxit, flags, info, stream, &tail);
+    if (s == SLA_ERR_NOT_SYMMETRIC) set_error(kValuesNotSymmetric, "sla_cg_adjoint");
+    return s;
+  }
   const sla_status sym = require_symmetric(A, true, "sla_cg_adjoint", stream);
   if (sym != SLA_OK) {
     fill_status(info, A->batch, sym);

@@ -1432,10 +1432,14 @@ size_t one_group_lds_bytes(int64_t n, bool band) {
 // from the LDS copy of p in ascending offset (= column) order, which is the
 // slot order the staged CSR rows are summed in: the same bits without the
 // product area and its two wave barriers per tile.
+//
+// gate (or nullptr): a device flag set when the adjoint's values are not
+// symmetric; then every system is refused (status SLA_ERR_NOT_SYMMETRIC, no
+// iteration) and x is not touched.
 template <typename RP, int R, bool JAC, int NT, bool BAND>
 __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
                                                             double tol, int64_t maxit,
-                                                            int use_x0) {
+                                                            int use_x0, const int* gate) {
   constexpr int W = NT / kWave;
   extern __shared__ double lds_dyn[];
   __shared__ double red[2 * W];
@@ -1454,6 +1458,19 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
   const int64_t hist_cap = c->hist_cap;
   const int t = threadIdx.x;
   const int lane = int(lane_id());
+  if (gate != nullptr && *gate != 0) {  // uniform
+    if (t == 0) {
+      Scal* sc = scal_of(c, s);
+      sc->bb = 0.0;
+      sc->stop = 0.0;
+      sc->maxit = maxit;
+      sc->it = 0;
+      sc->rr_final = 0.0;
+      sc->state_a = SLA_ERR_NOT_SYMMETRIC;
+      sc->state_r = SLA_ERR_NOT_SYMMETRIC;
+    }
+    return;
+  }
   // this thread's rows and tiles; the held slots of each tile (CSR), or the
   // rows' values by band offset (BAND)
   int64_t row[R];
@@ -1805,7 +1822,9 @@ __global__ __launch_bounds__(kIterBlock) void k_pattern_grad(const RP* __restric
                                                              int cap,
                                                              const double* __restrict__ lambda,
                                                              const double* __restrict__ x,
-                                                             double* __restrict__ grad) {
+                                                             double* __restrict__ grad,
+                                                             const int* __restrict__ gate) {
+  if (gate != nullptr && *gate != 0) return;  // refused: nothing written
   extern __shared__ double lds_dyn[];
   const int w = wave_index();
   const int lane = threadIdx.x & (kWave - 1);
@@ -2253,7 +2272,7 @@ sla_status launch_spmv_dots(sla_csr A, const double* vals, int64_t batch, const 
 }
 
 sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const double* x,
-                                double* out, bool negate, hipStream_t st) {
+                                double* out, bool negate, hipStream_t st, const int* gate) {
   const unsigned per_xcd = std::max(1u, plain_grid(A->tiles, batch) / unsigned(kXcds));
   const dim3 grid(per_xcd * kXcds, unsigned(batch));
   const int cap = A->wave_cap;
@@ -2261,11 +2280,11 @@ sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const
   if (A->rp_idx == SLA_I32) {
     auto k = negate ? k_pattern_grad<int32_t, true> : k_pattern_grad<int32_t, false>;
     k<<<grid, kIterBlock, lds, st>>>((const int32_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles,
-                                     cap, g, x, out);
+                                     cap, g, x, out, gate);
   } else {
     auto k = negate ? k_pattern_grad<int64_t, true> : k_pattern_grad<int64_t, false>;
     k<<<grid, kIterBlock, lds, st>>>((const int64_t*)A->rowptr, A->col, A->n, A->nnz, A->tiles,
-                                     cap, g, x, out);
+                                     cap, g, x, out, gate);
   }
   LAUNCH_CHECK();
   return SLA_OK;
@@ -2301,7 +2320,7 @@ bool use_one_group(const sla_csr A) {
 // The small-system kernel for `rows` rows per thread and `nt` threads per
 // workgroup (one_group_rows, one_group_block), Jacobi or not, banded rows or
 // plain CSR; nullptr for a combination the size rule never picks.
-using OneGroupFn = void (*)(const Ctx*, double, int64_t, int);
+using OneGroupFn = void (*)(const Ctx*, double, int64_t, int, const int*);
 
 template <typename RP, bool BAND>
 static OneGroupFn one_group_kernel(int rows, int nt, bool jac) {
@@ -2322,7 +2341,8 @@ static OneGroupFn one_group_kernel(int rows, int nt, bool jac) {
 }
 
 static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch, bool jac,
-                                   double tol, int64_t maxit, bool x0, hipStream_t st) {
+                                   double tol, int64_t maxit, bool x0, const int* gate,
+                                   hipStream_t st) {
   const bool band = use_band(A);
   const size_t lds = one_group_lds_bytes(A->n, band);
   const unsigned g = unsigned(batch);
@@ -2336,7 +2356,7 @@ static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch,
       set_error("small-system kernel: no variant for %d rows x %d threads", rows, nt);
       return SLA_ERR_DEVICE;
     }
-    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u);
+    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u, gate);
   } else {
     auto k = band ? one_group_kernel<int64_t, true>(rows, nt, jac)
                   : one_group_kernel<int64_t, false>(rows, nt, jac);
@@ -2344,14 +2364,14 @@ static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch,
       set_error("small-system kernel: no variant for %d rows x %d threads", rows, nt);
       return SLA_ERR_DEVICE;
     }
-    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u);
+    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u, gate);
   }
   LAUNCH_CHECK();
   return SLA_OK;
 }
 
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
-                  uint32_t flags, sla_cg_info* info, hipStream_t st) {
+                  uint32_t flags, sla_cg_info* info, hipStream_t st, const AdjointTail* tail) {
   const int64_t batch = A->batch;
   SLA_TRY(ensure_workspace(A, batch));
   const bool want_hist = (flags & SLA_FLAG_HISTORY) != 0;
@@ -2375,7 +2395,7 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
     SLA_TRY(dev_alloc(&A->jbad, size_t(batch), "diagonal flags"));
     SLA_TRY_HIP(hipMemsetAsync(A->jbad, 0, sizeof(int) * size_t(batch), st));
   }
-  return run_cg_space(A, own_space(A), b, x, tol, maxit, flags, info, st);
+  return run_cg_space(A, own_space(A), b, x, tol, maxit, flags, info, st, tail);
 }
 
 // The context of a solve written into device memory by a one-thread kernel
@@ -2383,7 +2403,8 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
 __global__ void k_store_ctx(Ctx c, Ctx* __restrict__ dst) { *dst = c; }
 
 sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x, double tol,
-                        int64_t maxit, uint32_t flags, sla_cg_info* info, hipStream_t st) {
+                        int64_t maxit, uint32_t flags, sla_cg_info* info, hipStream_t st,
+                        const AdjointTail* tail) {
   const int64_t batch = A->batch;
   const bool want_hist = (flags & SLA_FLAG_HISTORY) != 0;
   const bool jacobi = (flags & SLA_FLAG_JACOBI) != 0;
@@ -2397,8 +2418,15 @@ sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x
 
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
   if (use_one_group(A)) {
-    SLA_TRY(launch_one_group(A, sp.ctx_dev, batch, jacobi, tol, maxit, x0, st));
+    SLA_TRY(launch_one_group(A, sp.ctx_dev, batch, jacobi, tol, maxit, x0,
+                             tail ? tail->gate : nullptr, st));
+    if (tail != nullptr && tail->grad_vals != nullptr)  // from the last iterate, as below
+      SLA_TRY(launch_slot_products(A, batch, x, tail->x, tail->grad_vals, true, st, tail->gate));
     return finish_cg(sp, batch, info, st);
+  }
+  if (tail != nullptr) {
+    set_error("CG: an adjoint tail needs the one-workgroup loop (internal error)");
+    return SLA_ERR_DEVICE;
   }
   if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, sp.q, st));  // q = A x0
   const dim3 grid2(unsigned(sp.grid), unsigned(batch));

@@ -776,14 +776,7 @@ __global__ void k_symmetry(int64_t n, int64_t nnz, const RP* __restrict__ rowptr
 
 }  // namespace
 
-sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t st, int* flag_dev) {
-  *bad = 0;
-  if (A->nnz == 0) return SLA_OK;
-  int* flag = flag_dev;
-  if (flag == nullptr) {
-    if (A->sym_flag == nullptr) SLA_TRY(dev_alloc(&A->sym_flag, 1, "symmetry flag"));
-    flag = A->sym_flag;
-  }
+static sla_status enqueue_check(sla_csr A, bool values, hipStream_t st, int* flag) {
   const double* v = values ? A->vals : nullptr;
   const int64_t batch = values ? A->batch : 0;
   k_zero_flag<<<1, 1, 0, st>>>(flag);  // a kernel, not a memset: callers may capture
@@ -794,6 +787,27 @@ sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t st, int*
     k_symmetry<int64_t><<<grid_for(A->n), kBlock, 0, st>>>(A->n, A->nnz, (const int64_t*)A->rowptr,
                                                            A->col, v, batch, flag);
   LAUNCH_CHECK();
+  return SLA_OK;
+}
+
+sla_status enqueue_symmetry_check(sla_csr A, bool values, hipStream_t st, int** flag_out) {
+  *flag_out = nullptr;
+  if (A->nnz == 0) return SLA_OK;
+  if (A->sym_flag == nullptr) SLA_TRY(dev_alloc(&A->sym_flag, 1, "symmetry flag"));
+  SLA_TRY(enqueue_check(A, values, st, A->sym_flag));
+  *flag_out = A->sym_flag;
+  return SLA_OK;
+}
+
+sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t st, int* flag_dev) {
+  *bad = 0;
+  if (A->nnz == 0) return SLA_OK;
+  int* flag = flag_dev;
+  if (flag == nullptr) {
+    if (A->sym_flag == nullptr) SLA_TRY(dev_alloc(&A->sym_flag, 1, "symmetry flag"));
+    flag = A->sym_flag;
+  }
+  SLA_TRY(enqueue_check(A, values, st, flag));
   int h = 0;
   SLA_TRY_HIP(hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, st));
   SLA_TRY_HIP(hipStreamSynchronize(st));

@@ -126,6 +126,17 @@ struct CgSpace {
   bool own = true;
 };
 
+// The adjoint's tail on the one-workgroup loop: `gate` (a device int the
+// values' symmetry check sets) stops the solve and the pattern gradient on
+// the device, so no host round trip precedes the solve; grad_vals (or
+// nullptr) receives -lambda_i x_j, enqueued before the solve's results are
+// read back.
+struct AdjointTail {
+  const int* gate = nullptr;
+  const double* x = nullptr;
+  double* grad_vals = nullptr;
+};
+
 // Workspace and launch helpers implemented in cg.hip
 sla_status ensure_workspace(sla_csr A, int64_t batch);
 // the solver grid (workgroups per system) of a solve of `batch` systems
@@ -133,16 +144,19 @@ int32_t solver_grid(const sla_csr A, int64_t batch);
 // the CG loop of run_cg on a given space (flags: X0 always; HISTORY and
 // JACOBI only on the handle's own space)
 sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x, double tol,
-                        int64_t maxit, uint32_t flags, sla_cg_info* info, hipStream_t stream);
+                        int64_t maxit, uint32_t flags, sla_cg_info* info, hipStream_t stream,
+                        const AdjointTail* tail = nullptr);
 bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
 bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
 bool use_lines(const sla_csr A);  // line-walk SpMV step (a banded pattern with far offsets +-L)?
 bool use_one_group(const sla_csr A);  // the one-workgroup-per-system CG loop?
 // y[s] = A_s^T x[s] (builds the transposed pattern on first use)
 sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t st);
-// grad_vals[s][k] = sign * g[s][i] * x[s][col[k]] on every stored slot
+// grad_vals[s][k] = sign * g[s][i] * x[s][col[k]] on every stored slot;
+// nothing is written when `gate` (a device int, or nullptr) is set
 sla_status launch_slot_products(sla_csr A, int64_t batch, const double* g, const double* x,
-                                double* out, bool negate, hipStream_t st);
+                                double* out, bool negate, hipStream_t st,
+                                const int* gate = nullptr);
 void release_workspace(sla_csr A);
 void free_handle(sla_csr A);  // the handle, its workspace and its transposed pattern
 sla_status analyse_pattern(sla_csr A, hipStream_t stream);
@@ -154,6 +168,9 @@ sla_status analyse_pattern(sla_csr A, hipStream_t stream);
 // `stream` (csr_build.hip).
 sla_status check_symmetry(sla_csr A, bool values, int* bad, hipStream_t stream,
                           int* flag_dev = nullptr);
+// The same check enqueued only: *flag_out (device, the handle's flag) holds
+// its result once the stream reaches it; nullptr for a pattern without slots.
+sla_status enqueue_symmetry_check(sla_csr A, bool values, hipStream_t stream, int** flag_out);
 
 sla_status launch_spmv(sla_csr A, const double* vals, int64_t batch, const double* x,
                        double* y, hipStream_t stream);
@@ -167,7 +184,8 @@ int64_t spmv_groups(const sla_csr A, int64_t batch);
 sla_status launch_pattern_grad(sla_csr A, int64_t batch, const double* lambda,
                                const double* x, double* grad_vals, hipStream_t stream);
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
-                  uint32_t flags, sla_cg_info* info, hipStream_t stream);
+                  uint32_t flags, sla_cg_info* info, hipStream_t stream,
+                  const AdjointTail* tail = nullptr);
 // Lanczos eigenpairs of every bound system (lanczos.hip)
 sla_status run_eigsh(sla_csr A, int64_t k, int which, int64_t m, const double* v0,
                      double* theta, double* X, double* resid, sla_eig_info* info,

@@ -279,3 +279,51 @@ def test_batch_of_small_systems():
     assert [i.status for i in i4] == [0, K.ERR_NOT_SPD, 0, 0]
     for s in (0, 2, 3):
         assert rel(x4[s].cpu().numpy(), xo[s]) <= TOL_X
+
+
+def test_adjoint_refused_on_the_device():
+    """Values that are not symmetric on the one-workgroup loop: the check runs
+    on the device and gates the solve and the pattern gradient there, so every
+    system of the batch is refused (SLA_ERR_NOT_SYMMETRIC, no iteration, the
+    message) and grad_b and grad_vals keep what they held; with and without
+    Jacobi.  The next call, with symmetric values, is solved (against the
+    oracle): the flag is cleared by every check."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    N = 32
+    n = N * N
+    rp, c, v = W.poisson_csr(N)
+    vn = v.copy()
+    off = np.flatnonzero(vn != 4.0)
+    vn[int(off[17])] = -1.25  # a_ij changed, a_ji not
+    b = W.uniform_rhs(n, 6)
+    g = W.normal_rhs(n, 7)
+    P = csr_handle(rp, c)
+    x1, _ = K.sla_cg_solve(P, t(v), t(b), 1e-10, 5000)
+    torch.cuda.synchronize()
+    nnz = v.shape[0]
+    for jac in (False, True):
+        for vals in (vn[None, :], np.stack([v, vn, v])):
+            batch = vals.shape[0]
+            P.bind(t(vals))
+            xb = x1.repeat(batch, 1).contiguous()
+            gx = t(np.tile(g, (batch, 1)))
+            gb = torch.full((batch, n), 7.0, dtype=torch.float64, device=xb.device)
+            gv = torch.full((batch, nnz), 7.0, dtype=torch.float64, device=xb.device)
+            infos = (K._Info * batch)()
+            st = K._lib.sla_cg_adjoint_batched(P.handle, xb.data_ptr(), gx.data_ptr(),
+                                               gb.data_ptr(), gv.data_ptr(), 1e-10, 5000,
+                                               K.FLAG_JACOBI if jac else 0, infos, None)
+            torch.cuda.synchronize()
+            assert st == K.ERR_NOT_SYMMETRIC
+            for i in infos:
+                assert i.status == K.ERR_NOT_SYMMETRIC and i.iterations == 0 and not i.converged
+            assert b"values are not symmetric" in K._lib.sla_last_error()
+            assert bool((gb == 7.0).all()) and bool((gv == 7.0).all())
+    A = _A(rp, c, v)
+    xo, _ = oracle.cg(A, b, 1e-10, 5000)
+    gbo, gvo, aio = oracle.adjoint(A, xo, g, 1e-10, 5000)
+    gb, gv, ai = K.sla_cg_adjoint(P, t(v), x1, t(g), 1e-10, 5000)
+    torch.cuda.synchronize()
+    assert ai.converged and iters_close(ai.iterations, aio.iterations)
+    assert rel(gb.cpu().numpy(), gbo) <= TOL_X and rel(gv.cpu().numpy(), gvo) <= TOL_GRAD
