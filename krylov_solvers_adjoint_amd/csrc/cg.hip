@@ -1433,11 +1433,13 @@ size_t one_group_lds_bytes(int64_t n, bool band) {
 // slot order the staged CSR rows are summed in: the same bits without the
 // product area and its two wave barriers per tile.
 //
-// gate (or nullptr): a device flag set when the adjoint's values are not
-// symmetric; then every system is refused (status SLA_ERR_NOT_SYMMETRIC, no
-// iteration) and x is not touched.
+// The context comes by value (no copy to the device before the launch);
+// the systems' records `scal` are in device memory, read back after the
+// solve.  gate (or nullptr): a device flag set when the adjoint's values are
+// not symmetric; then every system is refused (status SLA_ERR_NOT_SYMMETRIC,
+// no iteration) and x is not touched.
 template <typename RP, int R, bool JAC, int NT, bool BAND>
-__global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
+__global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restrict__ scal,
                                                             double tol, int64_t maxit,
                                                             int use_x0, const int* gate) {
   constexpr int W = NT / kWave;
@@ -1445,22 +1447,22 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
   __shared__ double red[2 * W];
   __shared__ double red_a[W], red_b[2 * W];  // the loop's two areas
   const int64_t s = blockIdx.x;
-  const int64_t n = c->n, nnz = c->nnz;
+  const int64_t n = cv.n, nnz = cv.nnz;
   const int64_t npad = (n + NT - 1) / NT * NT;
   double* pl = lds_dyn;                                         // p, or x0 at set-up
   double* prod = lds_dyn + npad + int64_t(wave_index()) * kWaveCap;  // this wave's products
-  const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(c->rowptr));
-  const SLA_GLOBAL int32_t* col = gmem(c->col);
-  const SLA_GLOBAL double* vals = gmem(c->vals + s * nnz);
-  const SLA_GLOBAL double* b = gmem(c->b + s * n);
-  SLA_GLOBAL double* x = gmem(c->x + s * n);
-  SLA_GLOBAL double* hist = c->hist != nullptr ? gmem(c->hist + s * c->hist_cap * 3) : nullptr;
-  const int64_t hist_cap = c->hist_cap;
+  const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(cv.rowptr));
+  const SLA_GLOBAL int32_t* col = gmem(cv.col);
+  const SLA_GLOBAL double* vals = gmem(cv.vals + s * nnz);
+  const SLA_GLOBAL double* b = gmem(cv.b + s * n);
+  SLA_GLOBAL double* x = gmem(cv.x + s * n);
+  SLA_GLOBAL double* hist = cv.hist != nullptr ? gmem(cv.hist + s * cv.hist_cap * 3) : nullptr;
+  const int64_t hist_cap = cv.hist_cap;
   const int t = threadIdx.x;
   const int lane = int(lane_id());
   if (gate != nullptr && *gate != 0) {  // uniform
     if (t == 0) {
-      Scal* sc = scal_of(c, s);
+      Scal* sc = scal + s;
       sc->bb = 0.0;
       sc->stop = 0.0;
       sc->maxit = maxit;
@@ -1481,18 +1483,18 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
   uint32_t bm[R];              // the row's bits among the band's offsets
   int32_t boff[kMaxBand];      // the offsets (uniform)
 #pragma unroll
-  for (int o = 0; o < kMaxBand; ++o) boff[o] = BAND ? c->band.off[o] : 0;
+  for (int o = 0; o < kMaxBand; ++o) boff[o] = BAND ? cv.band.off[o] : 0;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int64_t r0 = (int64_t(j) * W + wave_index()) * kTileRows;
     row[j] = r0 + lane;
     rlen[j] = ra[j] = re[j] = 0;
     if constexpr (BAND) {
-      const int cnt = c->band.count;
+      const int cnt = cv.band.count;
       bm[j] = 0;
       int64_t k = 0;
       if (row[j] < n) {
-        bm[j] = uint32_t(c->mask[row[j]]) & ((1u << cnt) - 1u);
+        bm[j] = uint32_t(cv.mask[row[j]]) & ((1u << cnt) - 1u);
         k = int64_t(rowptr[row[j]]);
       }
 #pragma unroll
@@ -1667,7 +1669,7 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx* __restrict__ c,
     if (i < n) x[i] = xv[j];
   }
   if (t == 0) {
-    Scal* sc = scal_of(c, s);
+    Scal* sc = scal + s;
     sc->bb = bb;
     sc->stop = stop;
     sc->maxit = maxit;
@@ -2320,7 +2322,7 @@ bool use_one_group(const sla_csr A) {
 // The small-system kernel for `rows` rows per thread and `nt` threads per
 // workgroup (one_group_rows, one_group_block), Jacobi or not, banded rows or
 // plain CSR; nullptr for a combination the size rule never picks.
-using OneGroupFn = void (*)(const Ctx*, double, int64_t, int, const int*);
+using OneGroupFn = void (*)(const Ctx, Scal*, double, int64_t, int, const int*);
 
 template <typename RP, bool BAND>
 static OneGroupFn one_group_kernel(int rows, int nt, bool jac) {
@@ -2340,9 +2342,9 @@ static OneGroupFn one_group_kernel(int rows, int nt, bool jac) {
 #undef SLA_OG
 }
 
-static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch, bool jac,
-                                   double tol, int64_t maxit, bool x0, const int* gate,
-                                   hipStream_t st) {
+static sla_status launch_one_group(sla_csr A, const Ctx& ctx, Scal* scal, int64_t batch,
+                                   bool jac, double tol, int64_t maxit, bool x0,
+                                   const int* gate, hipStream_t st) {
   const bool band = use_band(A);
   const size_t lds = one_group_lds_bytes(A->n, band);
   const unsigned g = unsigned(batch);
@@ -2356,7 +2358,7 @@ static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch,
       set_error("small-system kernel: no variant for %d rows x %d threads", rows, nt);
       return SLA_ERR_DEVICE;
     }
-    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u, gate);
+    k<<<g, unsigned(nt), lds, st>>>(ctx, scal, tol, maxit, u, gate);
   } else {
     auto k = band ? one_group_kernel<int64_t, true>(rows, nt, jac)
                   : one_group_kernel<int64_t, false>(rows, nt, jac);
@@ -2364,7 +2366,7 @@ static sla_status launch_one_group(sla_csr A, const Ctx* ctx_dev, int64_t batch,
       set_error("small-system kernel: no variant for %d rows x %d threads", rows, nt);
       return SLA_ERR_DEVICE;
     }
-    k<<<g, unsigned(nt), lds, st>>>(ctx_dev, tol, maxit, u, gate);
+    k<<<g, unsigned(nt), lds, st>>>(ctx, scal, tol, maxit, u, gate);
   }
   LAUNCH_CHECK();
   return SLA_OK;
@@ -2409,17 +2411,11 @@ sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x
   const bool want_hist = (flags & SLA_FLAG_HISTORY) != 0;
   const bool jacobi = (flags & SLA_FLAG_JACOBI) != 0;
   fill_ctx(A, sp, *sp.ctx_host, b, x, batch, want_hist, jacobi);
-  if (sp.own) {
-    SLA_TRY_HIP(hipMemcpyAsync(sp.ctx_dev, sp.ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
-  } else {
-    k_store_ctx<<<1, 1, 0, st>>>(*sp.ctx_host, sp.ctx_dev);
-    LAUNCH_CHECK();
-  }
-
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
   if (use_one_group(A)) {
-    SLA_TRY(launch_one_group(A, sp.ctx_dev, batch, jacobi, tol, maxit, x0,
-                             tail ? tail->gate : nullptr, st));
+    // the context by value; the records are read back from the device
+    SLA_TRY(launch_one_group(A, *sp.ctx_host, scal_of(sp.ctx_dev, 0), batch, jacobi, tol, maxit,
+                             x0, tail ? tail->gate : nullptr, st));
     if (tail != nullptr && tail->grad_vals != nullptr)  // from the last iterate, as below
       SLA_TRY(launch_slot_products(A, batch, x, tail->x, tail->grad_vals, true, st, tail->gate));
     return finish_cg(sp, batch, info, st);
@@ -2428,6 +2424,13 @@ sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x
     set_error("CG: an adjoint tail needs the one-workgroup loop (internal error)");
     return SLA_ERR_DEVICE;
   }
+  if (sp.own) {
+    SLA_TRY_HIP(hipMemcpyAsync(sp.ctx_dev, sp.ctx_host, sizeof(Ctx), hipMemcpyHostToDevice, st));
+  } else {
+    k_store_ctx<<<1, 1, 0, st>>>(*sp.ctx_host, sp.ctx_dev);
+    LAUNCH_CHECK();
+  }
+
   if (x0) SLA_TRY(launch_spmv(A, A->vals, batch, x, sp.q, st));  // q = A x0
   const dim3 grid2(unsigned(sp.grid), unsigned(batch));
   if (A->rp_idx == SLA_I32) k_cg_init<int32_t><<<grid2, kIterBlock, 0, st>>>(sp.ctx_dev, x0 ? 1 : 0);
