@@ -2154,7 +2154,7 @@ void release_workspace(sla_csr A) {
   A->poll_host = nullptr;
   A->poll_ev[0] = A->poll_ev[1] = nullptr;
   A->capture_stream = nullptr;
-  A->ws_batch = 0;
+  A->ws_batch = A->ws_cap = A->part_cap = 0;
   A->hist_cap = A->hist_batch = 0;
 }
 
@@ -2192,17 +2192,28 @@ CgSpace own_space(sla_csr A) {
   return sp;
 }
 
+// The buffers of a larger batch serve a smaller one as they are (a handle
+// that alternates batch sizes, e.g. one system and then a batch of them, is
+// not reallocated on every call; the captured graphs are kept per batch and
+// stay valid as long as the buffers do).  A larger batch, or more partials
+// than the buffers hold, reallocates everything.
 sla_status ensure_workspace(sla_csr A, int64_t batch) {
-  if (A->ws_batch == batch && A->r != nullptr) return SLA_OK;
+  const int32_t grid = solver_grid(A, batch);
+  const int64_t parts = int64_t(kPartSets) * batch * grid;
+  if (A->r != nullptr && batch <= A->ws_cap && parts <= A->part_cap) {
+    A->grid = grid;
+    A->ws_batch = batch;
+    return SLA_OK;
+  }
   release_workspace(A);
   const int64_t n = A->n;
-  A->grid = solver_grid(A, batch);
+  A->grid = grid;
   const size_t vec = size_t(batch) * size_t(n);
   SLA_TRY(dev_alloc(&A->r, vec, "r"));
   SLA_TRY(dev_alloc(&A->p0, vec, "p"));
   SLA_TRY(dev_alloc(&A->p1, vec, "p"));
   SLA_TRY(dev_alloc(&A->q, vec, "q"));
-  SLA_TRY(dev_alloc(&A->part, size_t(kPartSets) * batch * A->grid, "partials"));
+  SLA_TRY(dev_alloc(&A->part, size_t(parts), "partials"));
   SLA_TRY(dev_alloc(&A->n_running, 1, "running count"));
   // the context, then the systems' scalars (scal_of)
   SLA_TRY(dev_alloc(reinterpret_cast<void**>(&A->ctx_dev), sizeof(Ctx) + sizeof(Scal) * batch,
@@ -2212,7 +2223,8 @@ sla_status ensure_workspace(sla_csr A, int64_t batch) {
   SLA_TRY_HIP(hipHostMalloc(reinterpret_cast<void**>(&A->scal_host), sizeof(Scal) * batch));
   SLA_TRY_HIP(hipHostMalloc(reinterpret_cast<void**>(&A->poll_host), sizeof(int) * 2));
   for (auto& e : A->poll_ev) SLA_TRY_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  A->ws_batch = batch;
+  A->ws_batch = A->ws_cap = batch;
+  A->part_cap = parts;
   return SLA_OK;
 }
 
@@ -2389,13 +2401,13 @@ sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t max
   }
   const bool jacobi = (flags & SLA_FLAG_JACOBI) != 0;
   if (jacobi && A->jz == nullptr) {
-    // Jacobi workspace: z and the diagonal [batch][n], a flag per system
+    // Jacobi workspace: z and the diagonal [ws_cap][n], a flag per system
     // (zero here, and cleared again by every solve that sets it)
-    const size_t vec = size_t(batch) * size_t(A->n);
+    const size_t vec = size_t(A->ws_cap) * size_t(A->n);
     SLA_TRY(dev_alloc(&A->jz, vec, "z"));
     SLA_TRY(dev_alloc(&A->jdiag, vec, "diagonal"));
-    SLA_TRY(dev_alloc(&A->jbad, size_t(batch), "diagonal flags"));
-    SLA_TRY_HIP(hipMemsetAsync(A->jbad, 0, sizeof(int) * size_t(batch), st));
+    SLA_TRY(dev_alloc(&A->jbad, size_t(A->ws_cap), "diagonal flags"));
+    SLA_TRY_HIP(hipMemsetAsync(A->jbad, 0, sizeof(int) * size_t(A->ws_cap), st));
   }
   return run_cg_space(A, own_space(A), b, x, tol, maxit, flags, info, st, tail);
 }

@@ -57,19 +57,22 @@ struct sla_csr_s {
   // to the slot of ours it transposes
   sla_csr_s* trans = nullptr;
 
-  // workspace, sized for ws_batch systems
+  // workspace, sized for ws_cap systems (and part_cap partials); the last
+  // solve ran ws_batch <= ws_cap of them
   int64_t ws_batch = 0;
-  int32_t grid = 0;            // iteration workgroups per system
+  int64_t ws_cap = 0;
+  int64_t part_cap = 0;
+  int32_t grid = 0;            // iteration workgroups per system of ws_batch
   double* r = nullptr;
   double* p0 = nullptr;
   double* p1 = nullptr;
   double* q = nullptr;
-  double* part = nullptr;      // kPartSets * ws_batch * grid
-  sla::Scal* scal = nullptr;   // [ws_batch]
+  double* part = nullptr;      // [part_cap] >= kPartSets * ws_batch * grid
+  sla::Scal* scal = nullptr;   // [ws_cap]
   int* n_running = nullptr;
   sla::Ctx* ctx_dev = nullptr;
   sla::Ctx* ctx_host = nullptr;      // pinned
-  sla::Scal* scal_host = nullptr;    // pinned [ws_batch]
+  sla::Scal* scal_host = nullptr;    // pinned [ws_cap]
   int* poll_host = nullptr;          // pinned [2]
   hipEvent_t poll_ev[2] = {nullptr, nullptr};
   double* hist = nullptr;

@@ -52,3 +52,35 @@ def test_batched_equals_single_solves():
         torch.cuda.synchronize()
         assert iters_close(ib[s].iterations, i_s.iterations)
         assert rel(xb[s].cpu().numpy(), xs.cpu().numpy()) <= 1e-12
+
+
+@pytest.mark.parametrize("one_group", ["auto", "off"])
+def test_alternating_batch_sizes_on_one_handle(one_group):
+    """One handle solving batches of 4, 2, 4, 8, 1 and 4 systems in turn (the
+    buffers of a larger batch serve a smaller one; a larger batch
+    reallocates; the captured graphs are kept per batch), with and without
+    Jacobi: every call gives the bits of a fresh handle solving the same
+    batch.  40^2 and 33^2 Poisson: the two-kernel loop ("off") and the
+    one-workgroup loop."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    N = 40 if one_group == "off" else 33
+    n = N * N
+    rp, c, vals, b, _ = W.batched_poisson(N, 8, 2, 3)
+    g = W.normal_rhs(n, 4, shape=(8, n))
+    P = csr_handle(rp, c, one_group=one_group)
+
+    def run(H, B, jac):
+        x, infos = K.sla_cg_solve_batched(H, t(vals[:B]), t(b[:B]), 1e-10, 5000, jacobi=jac)
+        gb, gv, ai = K.sla_cg_adjoint_batched(H, t(vals[:B]), x, t(g[:B]), 1e-10, 5000,
+                                              jacobi=jac)
+        torch.cuda.synchronize()
+        return ([a.cpu().numpy() for a in (x, gb, gv)],
+                [i.iterations for i in infos] + [i.iterations for i in ai])
+
+    for B, jac in ((4, False), (2, False), (4, True), (8, False), (1, True), (4, False)):
+        got, its = run(P, B, jac)
+        ref, its_ref = run(csr_handle(rp, c, one_group=one_group), B, jac)
+        assert its == its_ref, (B, jac)
+        for a1, a2 in zip(got, ref):
+            assert np.array_equal(a1, a2), (B, jac)
