@@ -250,7 +250,10 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol,
  * sla_cg_solve for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * The same CG iteration as sla_cg_solve on the same handle (the same
- * kernels and grid, so the same results bit for bit), with its workspace
+ * kernels and grid, so the same results bit for bit), except that a system
+ * sla_cg_solve would give the resident grid loop (sla_csr_set_one_group),
+ * whose exchange buffers are allocated, runs the two-kernel loop here (the
+ * bits of sla_cg_solve with SLA_ONE_GROUP_OFF); with its workspace
  * (r, p, q, partials, scalars) in a static device array of the library
  * instead of the handle's: 64 MiB, which every GPU the library runs on holds
  * until the process ends (not counted by sla_memory_usage).  The call
@@ -584,7 +587,7 @@ sla_status sla_csr_reorder(sla_csr A, int ordering, hipStream_t stream);
 sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
 
 /*
- * CG loop of small systems.  SLA_ONE_GROUP_AUTO (default): a system of at
+ * CG loops in one launch.  SLA_ONE_GROUP_AUTO (default): a system of at
  * most 2048 unknowns with a banded pattern (at most 8 column offsets), or
  * whose 64-row tiles hold at most 336 stored entries each (and whose vectors
  * fit one workgroup's LDS), runs its whole CG loop in one
@@ -592,14 +595,32 @@ sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
  * workgroup barriers only),
  * instead of two kernels over the whole GPU per iteration, whose launch gaps
  * and partial sums dominate at such sizes (Problem statement: launch costs
- * of iterative solvers on small problems).  The same steps, stopping rule,
- * statuses and history; the dot products are summed in another order, so the
- * results differ from the two-kernel loop's in the last bits.
- * SLA_ONE_GROUP_OFF: always the two-kernel loop.  Applies to sla_cg_solve /
- * _batched, the adjoint solves and the CG lists.
+ * of iterative solvers on small problems).  A single banded system (no
+ * preconditioner) of 262144 to about a million unknowns whose rows fit the
+ * chip (at most 8 rows per thread of one 512-thread workgroup per CU, its
+ * largest column offset at most 1024 and at most the rows of a workgroup)
+ * runs its whole CG loop in one cooperative launch with the system held in
+ * registers and LDS (the resident grid loop): the matrix is read once per
+ * solve, and the workgroups exchange only halo rows and the two partial sums
+ * of each iteration.  The same steps, stopping rule, statuses and history;
+ * the dot products are summed in another order, so the results differ from
+ * the two-kernel loop's in the last bits.  A grid-wide wait of the resident
+ * loop that exceeds its poll limit (seconds) ends the solve with
+ * SLA_ERR_DEVICE.  SLA_ONE_GROUP_OFF: always the two-kernel loop.  Applies to
+ * sla_cg_solve / _batched, the adjoint solves and the CG lists.
  */
 enum { SLA_ONE_GROUP_AUTO = 0, SLA_ONE_GROUP_OFF = 1 };
 sla_status sla_csr_set_one_group(sla_csr A, int mode);
+
+/*
+ * Instrumentation (Experimental results: CG on 2D Poisson, timed per solve):
+ * the duration in milliseconds of the last resident grid CG loop launched on
+ * this handle (see sla_csr_set_one_group), from events recorded on its
+ * stream just before and after the cooperative launch; *ms_host receives it.
+ * Waits for that launch.  SLA_ERR_ARG if no resident loop has run since the
+ * handle's workspace was last built.
+ */
+sla_status sla_resident_loop_ms(sla_csr A, double* ms_host);
 
 /* Message of the last failed call on this thread ("" if none): the error
  * reporting of this boundary (not on the pages). */

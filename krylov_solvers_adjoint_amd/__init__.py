@@ -58,7 +58,8 @@ EXPORTS = [
     "sla_eigsh", "sla_eig_grad", "sla_profile_lanczos_kernels",
     "sla_bicgstab_solve", "sla_bicgstab_adjoint", "sla_bicgstab_history",
     "sla_solve_list", "sla_adjoint_list", "sla_csr_reorder", "sla_csr_ordering",
-    "sla_csr_set_one_group", "sla_csr_load_values", "sla_csr_arrays", "sla_memory_usage",
+    "sla_csr_set_one_group", "sla_resident_loop_ms", "sla_csr_load_values", "sla_csr_arrays",
+    "sla_memory_usage",
     "sla_cg_solve_noalloc", "sla_last_error", "sla_status_string",
 ]
 
@@ -120,6 +121,7 @@ def _bind(lib):
         "sla_csr_set_spmv_variant": [_P, _S, ctypes.POINTER(_S)],
         "sla_csr_reorder": [_P, _S, _P],
         "sla_csr_set_one_group": [_P, _S],
+        "sla_resident_loop_ms": [_P, ctypes.POINTER(_D)],
         "sla_csr_ordering": [_P, _P, _P],
         "sla_csr_load_values": [_P, _P, _I64, _S, _P],
         "sla_csr_arrays": [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
@@ -722,6 +724,14 @@ def sla_pattern_grad(A: CSRPattern, values_shape_ref: torch.Tensor, lam: torch.T
     _check(_lib.sla_pattern_grad(A.handle, _dev(lam, torch.float64, "lambda"),
                                  _dev(x, torch.float64, "x"), out.data_ptr(), _stream(stream)))
     return out
+
+
+def sla_resident_loop_ms(A: CSRPattern) -> float:
+    """Duration (ms) of the last resident grid CG loop launched on A (events
+    around the launch); SlaError if none has run."""
+    ms = _D()
+    _check(_lib.sla_resident_loop_ms(A.handle, ctypes.byref(ms)))
+    return ms.value
 
 
 def sla_profile_iteration_kernels(A: CSRPattern, values: torch.Tensor, b: torch.Tensor,

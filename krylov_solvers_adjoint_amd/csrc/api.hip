@@ -539,7 +539,8 @@ sla_status sla_cg_solve(sla_csr A, const double* b, double* x, double tol, int64
 static sla_status run_cg_adjoint(sla_csr A, const double* x, const double* grad_x,
                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
-  if (A->ro == nullptr && use_one_group(A)) {
+  if (A->ro == nullptr &&
+      (use_one_group(A) || use_grid(A, A->batch, (flags & SLA_FLAG_JACOBI) != 0))) {
     const sla_status ps = require_symmetric(A, false, "sla_cg_adjoint", stream);
     if (ps != SLA_OK) {
       fill_status(info, A->batch, ps);
@@ -786,6 +787,18 @@ sla_status sla_pattern_grad(sla_csr A, const double* lambda, const double* x, do
   REQUIRE(lambda != nullptr && x != nullptr && (A->nnz == 0 || grad_vals != nullptr),
           "sla_pattern_grad: NULL array");
   return launch_pattern_grad(A, A->batch, lambda, x, grad_vals, stream);
+  API_END
+}
+
+sla_status sla_resident_loop_ms(sla_csr A, double* ms_host) {
+  API_BEGIN
+  clear_error();
+  REQUIRE(A != nullptr && ms_host != nullptr, "sla_resident_loop_ms: NULL argument");
+  A = solver_handle(A);
+  const sla_status s = grid_loop_ms(A, ms_host);
+  if (s == SLA_ERR_ARG)
+    set_error("sla_resident_loop_ms: no resident CG loop has run on this handle");
+  return s;
   API_END
 }
 

@@ -1680,6 +1680,435 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Mid-size banded systems: the whole CG loop in one cooperative launch, the
+// system resident on chip
+// ---------------------------------------------------------------------------
+// A banded system of a few hundred thousand to about a million unknowns fits
+// the chip's registers and LDS (256 CUs hold 128 MB of VGPRs and 40 MB of
+// LDS): workgroup g of G (one per CU, all resident: cooperative launch) owns
+// rows [g rw, min(n, (g + 1) rw)), rw >= H = the band's largest |offset|,
+// and keeps their values by band offset, r, x and p in registers for the
+// whole solve.  p is published in LDS with H halo rows on each side.  The
+// matrix is read once per solve; an iteration moves only halo rows and
+// partial sums between workgroups, so it is bound by the two grid-wide sums
+// of Hestenes-Stiefel CG, not by HBM.
+//
+// Grid sums (grid_sum): each workgroup writes its partial for round R into
+// slot[R & 1][g] as two 8-byte words, the double's high and low halves each
+// beside the tag R (a word is written whole, so a reader never sees a half
+// of another round), with relaxed device-scope stores, which the hardware
+// writes through to the device-coherent level; every workgroup polls all G
+// slots with device-scope loads until every tag reads R, then adds the G
+// partials in slot order (lane l the slots l, l + 64, ..., then the fixed
+// wave sum), so every workgroup gets the same bits.  No fence that writes
+// back or invalidates a whole L2 runs in the polling loop (8.7-10.5 us per
+// round with acquire polls, 3.3 us with these).  A poll limit bounds every
+// wait: past it the workgroup sets the shared failure flag, which every
+// other poll reads, and all leave the loop (ST_GRID_TIMEOUT).
+//
+// Halo: the neighbours' rows of p_{k+1} = r_{k+1} + beta_k p_k are formed
+// locally from their published boundary rows of r_{k+1} (written before the
+// second sum of iteration k, into halo[(k + 1) & 1]; the release fence
+// before the tags orders them) and the halo rows of p_k kept in LDS: the same
+// operations on the same operands as the owner's, hence the owner's bits.
+// Double buffering by parity suffices: a buffer is written again two
+// iterations later, after sums that need every reader's partials, which
+// each reader posts only after reading it.
+//
+// Same steps, stopping rule, statuses, history and x update as the
+// one-workgroup loop (k_cg_onegroup, banded rows); the dot products are
+// summed in another fixed order.
+constexpr int kGridThreads = 512;   // threads per workgroup of the grid loop
+constexpr int kGridVals = 2;        // values one grid sum carries at most
+constexpr int kGridHaloPT = 4;      // halo rows per thread: 2 H <= 4 * 512
+
+struct GridSync {
+  uint64_t* slot;      // [2][G][2 * kGridVals] tagged words, by round parity
+  double* halo;        // [2][G][2][H] boundary rows of r: first H, last H
+  int* fail;           // set when a wait passed its poll limit
+  int64_t rw;          // rows per workgroup
+  int32_t H;           // halo rows on each side
+  int32_t pad;
+  int64_t poll_limit;  // polls per wait before giving up
+};
+
+__device__ __forceinline__ void dev_put(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t dev_get(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void dev_put(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double dev_get(double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void dev_put(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int dev_get(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Slots and the failure flag cleared before a launch (a kernel: a caller's
+// stream may be captured).
+__global__ void k_grid_clear(uint64_t* __restrict__ slot, int64_t words, int* __restrict__ fail) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < words) slot[i] = 0;
+  if (i == 0) *fail = 0;
+}
+
+// RPT rows per thread (rows t + j * 512 of the block), NB band offsets at
+// most.  gate: as in k_cg_onegroup.  Indices inside a block are 32-bit (a
+// block and its halo hold fewer than 2^13 rows).
+template <typename RP, int RPT, int NB>
+__global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __restrict__ scal,
+                                                          const GridSync gs, double tol,
+                                                          int64_t maxit, int use_x0,
+                                                          const int* gate) {
+  constexpr int NT = kGridThreads, W = NT / kWave;
+  extern __shared__ double lds_dyn[];
+  __shared__ double red[kGridVals * W];
+  __shared__ double bcast[kGridVals];
+  __shared__ int lfail;
+  const int t = threadIdx.x;
+  const int lane = int(lane_id()), w = wave_index();
+  const int g = int(blockIdx.x), G = int(gridDim.x);
+  const int64_t n = cv.n;
+  const int H = gs.H;
+  const int64_t r0 = int64_t(g) * gs.rw;
+  const int nloc = int((r0 + gs.rw < n ? r0 + gs.rw : n) - r0);
+  double* pl = lds_dyn;  // row r0 + l at pl[H + l], halo rows below and above
+  // the block's slices of the arrays (bases uniform, offsets 32-bit)
+  const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(cv.rowptr) + r0);
+  const SLA_GLOBAL uint8_t* mask = gmem(cv.mask + r0);
+  const SLA_GLOBAL double* vals = gmem(cv.vals);
+  const SLA_GLOBAL double* b = gmem(cv.b + r0);
+  SLA_GLOBAL double* x = gmem(cv.x + r0);
+  SLA_GLOBAL double* hist = cv.hist != nullptr ? gmem(cv.hist) : nullptr;
+  const int64_t hist_cap = cv.hist_cap;
+  if (gate != nullptr && *gate != 0) {  // uniform
+    if (g == 0 && t == 0) {
+      scal->bb = 0.0;
+      scal->stop = 0.0;
+      scal->maxit = maxit;
+      scal->it = 0;
+      scal->rr_final = 0.0;
+      scal->state_a = SLA_ERR_NOT_SYMMETRIC;
+      scal->state_r = SLA_ERR_NOT_SYMMETRIC;
+    }
+    return;
+  }
+  // this thread's rows: values by band offset, the row's bits
+  double bv[RPT][NB];
+  uint32_t bm[RPT];
+  int32_t boff[NB];
+#pragma unroll
+  for (int o = 0; o < NB; ++o) boff[o] = cv.band.off[o];
+  const int cnt = cv.band.count;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int l = t + j * NT;
+    bm[j] = 0;
+    int64_t k = 0;
+    if (l < nloc) {
+      bm[j] = uint32_t(mask[l]) & ((1u << cnt) - 1u);
+      k = int64_t(rowptr[l]);
+    }
+#pragma unroll
+    for (int o = 0; o < NB; ++o) {
+      const bool use = (bm[j] >> o) & 1u;
+      bv[j][o] = use ? vals[k] : 0.0;
+      k += use ? 1 : 0;
+    }
+    // one row's loads at a time (set-up only): all rows' 64-bit addresses at
+    // once would not leave the registers the loop keeps
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // this thread's halo entries e = t + u * 512 < 2 H: e < H the row
+  // r0 - H + e (the lower neighbour's last rows), else r0 + nloc + e - H (the
+  // upper neighbour's first rows); LDS index e, or nloc + e.  hsrc: the
+  // entry's offset in a halo buffer of one parity, or -1 (no such row).
+  int32_t hsrc[kGridHaloPT];
+#pragma unroll
+  for (int u = 0; u < kGridHaloPT; ++u) {
+    const int e = t + u * NT;
+    hsrc[u] = -1;
+    if (e < 2 * H) {
+      const bool low = e < H;
+      const int64_t row = low ? r0 - H + e : r0 + nloc + (e - H);
+      if (row >= 0 && row < n)
+        hsrc[u] = low ? ((g - 1) * 2 + 1) * H + e : ((g + 1) * 2) * H + (e - H);
+    }
+  }
+  auto hidx = [&](int u) -> int { return t + u * NT < H ? t + u * NT : nloc + t + u * NT; };
+  // the same entries as this workgroup's published boundary rows: e < H the
+  // row l = e, else l = nloc - H + (e - H); psrc: the row's LDS index, or -1
+  int32_t psrc[kGridHaloPT];
+#pragma unroll
+  for (int u = 0; u < kGridHaloPT; ++u) {
+    const int e = t + u * NT;
+    const int l = e < H ? e : nloc - H + (e - H);
+    psrc[u] = (e < 2 * H && l >= 0 && l < nloc) ? H + l : -1;
+  }
+  // LDS index of row l of the block; rows past the block (lanes without a
+  // row, whose values are all zero) store to one spare slot past the halo
+  const int spare = nloc + 2 * H;
+  auto own_idx = [&](int l) -> int { return l < nloc ? H + l : spare; };
+  for (int i = t; i < nloc + 2 * H; i += NT) pl[i] = 0.0;
+  __syncthreads();
+  // q = A v for this thread's rows, v published in pl (rows and halo)
+  auto spmv = [&](double (&q)[RPT]) {
+    // an opaque zero: the gather addresses and the slot masks are formed
+    // here at every call, not hoisted out of the CG loop into registers (40
+    // lane masks would take 80 SGPRs) that the rows' values need
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int li = own_idx(t + j * NT) + z;  // (rows past the block: m = 0)
+      const uint32_t m = bm[j] + uint32_t(z);
+      double gv[NB];
+#pragma unroll
+      for (int o = 0; o < NB; ++o) gv[o] = pl[((m >> o) & 1u) ? li + boff[o] : li];
+      double acc = 0.0;
+#pragma unroll
+      for (int o = 0; o < NB; ++o) {
+        const double sum = acc + bv[j][o] * gv[o];
+        acc = ((m >> o) & 1u) ? sum : acc;
+      }
+      q[j] = acc;
+    }
+  };
+  // boundary rows of r into halo buffer `par` (first H rows for g - 1, last
+  // H rows for g + 1), staged in pl's rows (p there is no longer read: every
+  // gather ended before the last barrier); pl's halo is left alone
+  auto publish_r = [&](int par, const double (&r)[RPT]) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) pl[own_idx(t + j * NT)] = r[j];
+    __syncthreads();
+    double* hb = gs.halo + (int64_t(par) * G + g) * 2 * H;
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u)
+      if (psrc[u] >= 0) dev_put(hb + uint32_t(t + u * NT), pl[psrc[u]]);
+  };
+  auto read_halo = [&](int par, double (&rh)[kGridHaloPT]) {
+    double* hb = gs.halo + int64_t(par) * G * 2 * H;
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u) rh[u] = hsrc[u] >= 0 ? dev_get(hb + hsrc[u]) : 0.0;
+  };
+  // sum of K values over the grid, in place in every thread; false when a
+  // wait timed out (here or in another workgroup)
+  uint32_t round = 0;
+  auto grid_sum = [&](auto kc, double* v) -> bool {
+    constexpr int K = decltype(kc)::value;
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = wave_sum(v[k]);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) red[k * W + w] = v[k];
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's published rows have landed
+    __syncthreads();
+    ++round;
+    if (w == 0) {
+      uint64_t* sl = gs.slot + int64_t(round & 1) * G * (2 * kGridVals);
+      if (lane == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          double a = 0.0;
+          for (int ww = 0; ww < W; ++ww) a = a + red[k * W + ww];
+          const uint64_t bits = uint64_t(__double_as_longlong(a));
+          dev_put(sl + g * 2 * kGridVals + 2 * k, (bits & 0xffffffff00000000ull) | round);
+          dev_put(sl + g * 2 * kGridVals + 2 * k + 1, (bits << 32) | round);
+        }
+      }
+      double s[K];
+      bool failed = false;
+      for (int64_t polls = 0;; ++polls) {
+        bool ok = true;
+        double ss[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) ss[k] = 0.0;
+        for (int gg = lane; gg < G; gg += kWave) {
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            const uint64_t hi = dev_get(sl + gg * 2 * kGridVals + 2 * k);
+            const uint64_t lo = dev_get(sl + gg * 2 * kGridVals + 2 * k + 1);
+            ok = ok && uint32_t(hi) == round && uint32_t(lo) == round;
+            ss[k] = ss[k] + __longlong_as_double(
+                                (long long)((hi & 0xffffffff00000000ull) | (lo >> 32)));
+          }
+        }
+        if (__all(ok)) {
+#pragma unroll
+          for (int k = 0; k < K; ++k) s[k] = ss[k];
+          break;
+        }
+        const int f = (polls & 15) == 15 ? __builtin_amdgcn_readfirstlane(dev_get(gs.fail)) : 0;
+        if (f != 0 || polls >= gs.poll_limit) {
+          if (f == 0 && lane == 0) dev_put(gs.fail, 1);
+          failed = true;
+#pragma unroll
+          for (int k = 0; k < K; ++k) s[k] = 0.0;
+          break;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) s[k] = wave_sum(s[k]);
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) bcast[k] = s[k];
+        lfail = failed ? 1 : 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = bcast[k];
+    return lfail == 0;
+  };
+  using One = std::integral_constant<int, 1>;
+  using Two = std::integral_constant<int, 2>;
+
+  double r[RPT], xv[RPT], pv[RPT], q[RPT], rh[kGridHaloPT];
+  // r0 = b - A x0 (or b, x0 = 0): x0 of the rows and of the halo from x,
+  // which no workgroup writes before every one has passed the first grid sum
+  if (use_x0) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int l = t + j * NT;
+      pl[own_idx(l)] = l < nloc ? x[l] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u)
+      if (hsrc[u] >= 0) {
+        const int e = t + u * NT;
+        pl[hidx(u)] = x[e < H ? e - H : nloc + (e - H)];
+      }
+    __syncthreads();
+    spmv(q);
+    __syncthreads();
+  }
+  double sums[2] = {0.0, 0.0};  // b.b, r.r
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int l = t + j * NT;
+    r[j] = xv[j] = pv[j] = 0.0;
+    if (l < nloc) {
+      const double bi = b[l];
+      xv[j] = use_x0 ? x[l] : 0.0;
+      r[j] = use_x0 ? bi - q[j] : bi;
+      sums[0] = sums[0] + bi * bi;
+      sums[1] = sums[1] + r[j] * r[j];
+    }
+  }
+  // p's halo starts from zero (p_{-1} = 0), as p does; the barrier keeps
+  // the clearing apart from the staging of r in publish_r
+  if (use_x0) {
+    for (int i = t; i < nloc + 2 * H; i += NT) pl[i] = 0.0;
+    __syncthreads();
+  }
+  publish_r(0, r);
+  const bool ok0 = grid_sum(Two{}, sums);
+  read_halo(0, rh);
+  const double bb = sums[0];
+  double rr = sums[1];
+  const double stop = (tol * tol) * bb;
+  int32_t state = (!isfinite(bb) || !isfinite(rr)) ? ST_NONFINITE : ST_RUNNING;
+  if (!ok0) state = ST_GRID_TIMEOUT;
+  int64_t it = 0;
+  double rr_final = rr;
+  double alpha = 0.0, rr_prev = rr;
+  // every thread holds the same scalars, so every branch below is uniform
+  for (int64_t k = 0; state == ST_RUNNING; ++k) {
+    double beta = 0.0;
+    if (k > 0) {
+      if (!isfinite(rr)) {
+        state = ST_NONFINITE;  // iteration k-1 did not complete
+        it = k - 1;
+        rr_final = rr_prev;
+        break;
+      }
+      beta = rr / rr_prev;
+      if (hist != nullptr && g == 0 && t == 0 && k - 1 < hist_cap) {
+        hist[(k - 1) * 3 + 0] = alpha;
+        hist[(k - 1) * 3 + 1] = beta;
+        hist[(k - 1) * 3 + 2] = rr;
+      }
+    }
+    if (rr <= stop || k >= maxit) {
+      state = rr <= stop ? ST_CONVERGED : ST_MAXIT;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    // p_k on the rows and on the halo, published in LDS for the gathers
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      pv[j] = r[j] + beta * pv[j];
+      pl[own_idx(t + j * NT)] = pv[j];
+    }
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u)
+      if (hsrc[u] >= 0) pl[hidx(u)] = rh[u] + beta * pl[hidx(u)];
+    __syncthreads();
+    spmv(q);
+    // rows past the block hold zeros throughout (values, r, p, x), so they
+    // add +0.0 to the sums and leave their bits alone: no row test here
+    double pq = 0.0;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) pq = pq + pv[j] * q[j];
+    // (the barriers of the sum also end every wave's gathers of p_k)
+    if (!grid_sum(One{}, &pq)) {
+      state = ST_GRID_TIMEOUT;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    if (!isfinite(pq) || !(pq > 0.0)) {
+      state = !isfinite(pq) ? ST_NONFINITE : ST_NOT_SPD;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    alpha = rr / pq;
+    double rn = 0.0;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      xv[j] = xv[j] + alpha * pv[j];
+      r[j] = r[j] - alpha * q[j];
+      rn = rn + r[j] * r[j];
+    }
+    publish_r(int((k + 1) & 1), r);
+    if (!grid_sum(One{}, &rn)) {
+      state = ST_GRID_TIMEOUT;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    read_halo(int((k + 1) & 1), rh);
+    rr_prev = rr;
+    rr = rn;
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int l = t + j * NT;
+    if (l < nloc) x[l] = xv[j];
+  }
+  if (g == 0 && t == 0) {
+    scal->bb = bb;
+    scal->stop = stop;
+    scal->maxit = maxit;
+    scal->it = it;
+    scal->rr_final = rr_final;
+    scal->state_a = state;
+    scal->state_r = state;
+  }
+}
+
 // Residual step k (see the file comment).  JAC: Jacobi preconditioning, so
 // alpha = r.z / p.Ap, and the step also writes z = r / d and the r.z partials.
 // NT threads per workgroup (residual_block).
@@ -2139,6 +2568,17 @@ void release_workspace(sla_csr A) {
   dev_free(A->jbad);
   A->jz = A->jdiag = nullptr;
   A->jbad = nullptr;
+  dev_free(A->grid_slot);
+  dev_free(A->grid_halo);
+  dev_free(A->grid_fail);
+  A->grid_slot = nullptr;
+  A->grid_halo = nullptr;
+  A->grid_fail = nullptr;
+  A->grid_slot_words = A->grid_halo_len = 0;
+  for (auto& e : A->grid_ev)
+    if (e) (void)hipEventDestroy(e);
+  A->grid_ev[0] = A->grid_ev[1] = nullptr;
+  A->grid_timed = false;
   if (A->ctx_host) (void)hipHostFree(A->ctx_host);
   if (A->scal_host) (void)hipHostFree(A->scal_host);
   if (A->poll_host) (void)hipHostFree(A->poll_host);
@@ -2384,6 +2824,155 @@ static sla_status launch_one_group(sla_csr A, const Ctx& ctx, Scal* scal, int64_
   return SLA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The resident grid loop: plan and launch
+// ---------------------------------------------------------------------------
+// Single banded systems from kGridMinN unknowns (below, the two-kernel
+// iteration costs as much or less: Poisson 500^2 12.2 vs 12.0 us, 300^2 11.4
+// vs 10.8) while the rows fit: rw = max(ceil(n / CUs),
+// H) rows per workgroup, at most 8 per thread, p with its halo in 64 KB of
+// LDS, 2 H halo rows at most 4 per thread, every workgroup resident.
+constexpr int64_t kGridMinN = int64_t(1) << 18;
+constexpr int64_t kGridPollLimit = int64_t(1) << 20;  // about a second of polling
+
+struct GridPlan {
+  int32_t G = 0;
+  int64_t rw = 0;
+  int32_t H = 0;
+  int32_t rpt = 0;
+  int32_t nb = 0;
+  size_t lds = 0;
+};
+
+using GridFn = void (*)(const Ctx, Scal*, const GridSync, double, int64_t, int, const int*);
+
+template <typename RP>
+static GridFn grid_kernel_rp(int rpt, int nb) {
+#define SLA_GK(R_)                                                                     \
+  (nb == 3 ? k_cg_grid<RP, R_, 3> : nb == 5 ? k_cg_grid<RP, R_, 5> : k_cg_grid<RP, R_, 8>)
+  switch (rpt) {
+    case 1: return SLA_GK(1);
+    case 2: return SLA_GK(2);
+    case 4: return SLA_GK(4);
+    case 8: return SLA_GK(8);
+    default: return nullptr;
+  }
+#undef SLA_GK
+}
+
+static GridFn grid_kernel(const sla_csr A, int rpt, int nb) {
+  return A->rp_idx == SLA_I32 ? grid_kernel_rp<int32_t>(rpt, nb) : grid_kernel_rp<int64_t>(rpt, nb);
+}
+
+static bool grid_plan(const sla_csr A, int64_t batch, bool jacobi, GridPlan* gp) {
+  if (A->one_group != SLA_ONE_GROUP_AUTO || batch != 1 || jacobi || !use_band(A)) return false;
+  const int64_t n = A->n;
+  if (n < kGridMinN) return false;
+  int32_t H = 0;
+  for (int o = 0; o < A->band.count; ++o)
+    H = std::max<int32_t>(H, A->band.off[o] < 0 ? -A->band.off[o] : A->band.off[o]);
+  const int cus = device_cus();
+  const int64_t rw = std::max<int64_t>((n + cus - 1) / cus, std::max<int32_t>(H, 1));
+  const int64_t G = (n + rw - 1) / rw;
+  const int64_t need = (rw + kGridThreads - 1) / kGridThreads;
+  const int rpt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
+  if (rpt == 0 || 2 * int64_t(H) > int64_t(kGridHaloPT) * kGridThreads) return false;
+  const int nb = band_class(A);
+  if (rpt == 8 && nb == 8) return false;  // (that variant spills registers)
+  const size_t lds = size_t(rw + 2 * int64_t(H) + 1) * sizeof(double);  // + the spare slot
+  if (lds > size_t(64) * 1024) return false;
+  int coop = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, A->device) != hipSuccess ||
+      !coop)
+    return false;
+  const GridFn fn = grid_kernel(A, rpt, nb);
+  int per_cu = 0;
+  if (fn == nullptr ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
+                                                   kGridThreads, lds) != hipSuccess ||
+      G > int64_t(per_cu) * cus)
+    return false;
+  gp->G = int32_t(G);
+  gp->rw = rw;
+  gp->H = H;
+  gp->rpt = rpt;
+  gp->nb = nb;
+  gp->lds = lds;
+  return true;
+}
+
+bool use_grid(const sla_csr A, int64_t batch, bool jacobi) {
+  GridPlan gp;
+  return grid_plan(A, batch, jacobi, &gp);
+}
+
+static sla_status launch_grid(sla_csr A, const GridPlan& gp, const Ctx& ctx, Scal* scal,
+                              double tol, int64_t maxit, bool x0, const int* gate,
+                              hipStream_t st) {
+  const int64_t words = int64_t(2) * gp.G * 2 * kGridVals;
+  const int64_t halo = int64_t(2) * gp.G * 2 * gp.H;
+  if (A->grid_slot == nullptr || A->grid_slot_words < words || A->grid_halo_len < halo) {
+    dev_free(A->grid_slot);
+    dev_free(A->grid_halo);
+    A->grid_slot = nullptr;
+    A->grid_halo = nullptr;
+    A->grid_slot_words = A->grid_halo_len = 0;
+    SLA_TRY(dev_alloc(&A->grid_slot, size_t(words), "grid sum slots"));
+    SLA_TRY(dev_alloc(&A->grid_halo, size_t(std::max<int64_t>(halo, 1)), "grid halo rows"));
+    A->grid_slot_words = words;
+    A->grid_halo_len = halo;
+  }
+  if (A->grid_fail == nullptr) SLA_TRY(dev_alloc(&A->grid_fail, 1, "grid failure flag"));
+  if (A->grid_ev[0] == nullptr)
+    for (auto& e : A->grid_ev) SLA_TRY_HIP(hipEventCreate(&e));
+  k_grid_clear<<<unsigned((words + 255) / 256), 256, 0, st>>>(A->grid_slot, words, A->grid_fail);
+  LAUNCH_CHECK();
+  GridSync gs;
+  gs.slot = A->grid_slot;
+  gs.halo = A->grid_halo;
+  gs.fail = A->grid_fail;
+  gs.rw = gp.rw;
+  gs.H = gp.H;
+  gs.pad = 0;
+  gs.poll_limit = kGridPollLimit;
+  const GridFn fn = grid_kernel(A, gp.rpt, gp.nb);
+  if (fn == nullptr) {
+    set_error("resident CG loop: no variant for %d rows per thread", gp.rpt);
+    return SLA_ERR_DEVICE;
+  }
+  Ctx c = ctx;
+  int u = x0 ? 1 : 0;
+  void* args[] = {&c, &scal, &gs, &tol, &maxit, &u, const_cast<const int**>(&gate)};
+  SLA_TRY_HIP(hipEventRecord(A->grid_ev[0], st));
+  SLA_TRY_HIP(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(unsigned(gp.G)),
+                                         dim3(kGridThreads), args, gp.lds, st));
+  SLA_TRY_HIP(hipEventRecord(A->grid_ev[1], st));
+  A->grid_timed = true;
+  return SLA_OK;
+}
+
+// After a resident grid solve: a wait that timed out anywhere is an error,
+// whatever the state the first workgroup recorded.
+static sla_status grid_check(sla_csr A, sla_status s, hipStream_t st) {
+  int h = 0;
+  SLA_TRY_HIP(hipMemcpyAsync(&h, A->grid_fail, sizeof(int), hipMemcpyDeviceToHost, st));
+  SLA_TRY_HIP(hipStreamSynchronize(st));
+  if (h != 0) {
+    set_error("resident CG loop: a grid-wide wait timed out");
+    return SLA_ERR_DEVICE;
+  }
+  return s;
+}
+
+sla_status grid_loop_ms(sla_csr A, double* ms) {
+  if (!A->grid_timed) return SLA_ERR_ARG;
+  float f = 0.0f;
+  SLA_TRY_HIP(hipEventSynchronize(A->grid_ev[1]));
+  SLA_TRY_HIP(hipEventElapsedTime(&f, A->grid_ev[0], A->grid_ev[1]));
+  *ms = double(f);
+  return SLA_OK;
+}
+
 sla_status run_cg(sla_csr A, const double* b, double* x, double tol, int64_t maxit,
                   uint32_t flags, sla_cg_info* info, hipStream_t st, const AdjointTail* tail) {
   const int64_t batch = A->batch;
@@ -2424,6 +3013,15 @@ sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x
   const bool jacobi = (flags & SLA_FLAG_JACOBI) != 0;
   fill_ctx(A, sp, *sp.ctx_host, b, x, batch, want_hist, jacobi);
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
+  GridPlan gp;
+  if (sp.own && grid_plan(A, batch, jacobi, &gp)) {
+    // the context by value; the record is read back from the device
+    SLA_TRY(launch_grid(A, gp, *sp.ctx_host, scal_of(sp.ctx_dev, 0), tol, maxit, x0,
+                        tail ? tail->gate : nullptr, st));
+    if (tail != nullptr && tail->grad_vals != nullptr)
+      SLA_TRY(launch_slot_products(A, batch, x, tail->x, tail->grad_vals, true, st, tail->gate));
+    return grid_check(A, finish_cg(sp, batch, info, st), st);
+  }
   if (use_one_group(A)) {
     // the context by value; the records are read back from the device
     SLA_TRY(launch_one_group(A, *sp.ctx_host, scal_of(sp.ctx_dev, 0), batch, jacobi, tol, maxit,
@@ -2496,6 +3094,17 @@ static sla_status finish_cg(const CgSpace& sp, int64_t batch, sla_cg_info* info,
   for (int64_t s = 0; s < batch; ++s) {
     const Scal& sc = sp.scal_host[s];
     const int32_t state = sc.state_a != ST_RUNNING ? sc.state_a : sc.state_r;
+    if (state == ST_GRID_TIMEOUT) {
+      set_error("resident CG loop: a grid-wide wait timed out");
+      if (info) {
+        info[s].iterations = sc.it;
+        info[s].rel_residual = 0.0;
+        info[s].converged = 0;
+        info[s].status = SLA_ERR_DEVICE;
+      }
+      if (first == SLA_OK) first = SLA_ERR_DEVICE;
+      continue;
+    }
     const sla_status ss = state >= SLA_ERR_NOT_SPD ? sla_status(state) : SLA_OK;
     if (info) {
       info[s].iterations = sc.it;

@@ -117,6 +117,9 @@ enum : int32_t {
   ST_NOT_SPD = SLA_ERR_NOT_SPD,
   ST_NONFINITE = SLA_ERR_NONFINITE,
   ST_BREAKDOWN = SLA_ERR_BREAKDOWN,
+  // the resident grid loop: a wait for the other workgroups exceeded its
+  // poll limit (every workgroup then leaves the loop); no sla_status value
+  ST_GRID_TIMEOUT = 100,
 };
 
 // Per-system CG scalars, resident on the device for the whole solve.  An

@@ -76,6 +76,16 @@ struct sla_csr_s {
   int* poll_host = nullptr;          // pinned [2]
   hipEvent_t poll_ev[2] = {nullptr, nullptr};
   double* hist = nullptr;
+  // resident grid loop (allocated by its first solve): tagged sum slots,
+  // published boundary rows of r, the failure flag, the time of the last
+  // launch
+  uint64_t* grid_slot = nullptr;
+  double* grid_halo = nullptr;
+  int* grid_fail = nullptr;
+  int64_t grid_slot_words = 0;
+  int64_t grid_halo_len = 0;
+  hipEvent_t grid_ev[2] = {nullptr, nullptr};
+  bool grid_timed = false;     // grid_ev hold the last launch
   // Jacobi workspace (allocated by the first preconditioned solve)
   double* jz = nullptr;
   double* jdiag = nullptr;
@@ -87,9 +97,10 @@ struct sla_csr_s {
   int64_t graph_block = 32;
   // solver workgroups per compute unit: 1, 2, or 0 (by problem size)
   int32_t wg_per_cu = 0;
-  // SLA_ONE_GROUP_AUTO: systems of up to 2048 unknowns (tiles of at most
-  // kWaveCap slots) run the CG loop in one workgroup per system;
-  // SLA_ONE_GROUP_OFF: always the two-kernel loop
+  // SLA_ONE_GROUP_AUTO: systems of up to 2048 unknowns (banded, or tiles of
+  // at most kWaveCap slots) run the CG loop in one workgroup per system, and
+  // single banded systems that fit the chip in one cooperative launch (the
+  // resident grid loop); SLA_ONE_GROUP_OFF: always the two-kernel loop
   int32_t one_group = SLA_ONE_GROUP_AUTO;
   // grid line length L of a band whose far offsets are +-L and whose other
   // offsets lie within +-63 (0: the line walk does not apply)
@@ -153,6 +164,10 @@ bool use_band(const sla_csr A);   // banded SpMV kernels for this handle?
 bool use_split(const sla_csr A);  // separate direction pass before the SpMV?
 bool use_lines(const sla_csr A);  // line-walk SpMV step (a banded pattern with far offsets +-L)?
 bool use_one_group(const sla_csr A);  // the one-workgroup-per-system CG loop?
+// the resident grid loop for `batch` systems (with or without Jacobi)?
+bool use_grid(const sla_csr A, int64_t batch, bool jacobi);
+// duration of the last resident grid loop (SLA_ERR_ARG: none)
+sla_status grid_loop_ms(sla_csr A, double* ms);
 // y[s] = A_s^T x[s] (builds the transposed pattern on first use)
 sla_status launch_spmv_transpose(sla_csr A, const double* x, double* y, hipStream_t st);
 // grad_vals[s][k] = sign * g[s][i] * x[s][col[k]] on every stored slot;

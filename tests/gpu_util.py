@@ -41,8 +41,9 @@ def iters_close(a: int, b: int) -> bool:
 
 
 def csr_handle(rowptr, col, one_group="auto"):
-    """A pattern handle; one_group="off" keeps small systems on the two-kernel
-    CG loop (for tests of its kernel families)."""
+    """A pattern handle; one_group="off" keeps small systems and single
+    mid-size banded systems on the two-kernel CG loop (for tests of its kernel
+    families)."""
     import krylov_solvers_adjoint_amd as K
     P = K.sla_csr_create_from_csr(t(rowptr), t(col.astype(np.int32)))
     if one_group != "auto":

@@ -64,11 +64,12 @@ def _check_vs_oracle(name, rp, c, v, b, g, tol, maxit, variant="auto"):
     return x, info
 
 
-@pytest.mark.parametrize("N,one_group", [(40, "off"), (40, "auto"), (1000, "auto")])
+@pytest.mark.parametrize("N,one_group", [(40, "off"), (40, "auto"), (1000, "off")])
 def test_uniform_diagonal_is_cg_bit_for_bit(N, one_group):
     """Diagonal 4: z = r/4 rescales everything by powers of two, so the
     preconditioned iterates, beta and r.r are CG's exactly (row-order kernel
-    and the one-workgroup loop at 40^2, line walk at 1000^2)."""
+    and the one-workgroup loop at 40^2, line walk at 1000^2: the resident
+    grid loop, which unpreconditioned 1000^2 would take, has no Jacobi form)."""
     import torch
     import krylov_solvers_adjoint_amd as K
     rp, c, v = W.poisson_csr(N, np.int32)

@@ -1,5 +1,7 @@
 """The line-walk CG iteration (a band whose far offsets are +-L): the
-automatic choice for 2D stencils on grids with lines of 961 points or more;
+automatic choice of the two-kernel loop for 2D stencils on grids with lines
+of 961 points or more (the handles here keep that loop: single systems of up
+to about a million unknowns would otherwise take the resident grid loop);
 CG and the adjoint match the oracle, two runs give the same bits, and the
 walk handles short last lines, lines that are not a multiple of 64 points,
 a matrix whose length is not a multiple of L, and batches."""
@@ -16,7 +18,7 @@ pytestmark = pytest.mark.gpu
 def _solve(rp, c, v, b, g, tol, maxit, variant="auto", wg=2):
     import torch
     import krylov_solvers_adjoint_amd as K
-    P = csr_handle(rp, c)
+    P = csr_handle(rp, c, one_group="off")
     P.set_workgroups_per_cu(wg)
     P.set_spmv_variant(variant)
     lines = P.lines
@@ -147,7 +149,7 @@ def test_paired_x_updates_breakdown_at_odd_step():
     rows = np.repeat(np.arange(N * N), np.diff(rp))
     vs = v - np.where(rows == c, 0.05, 0.0)
     b = W.uniform_rhs(N * N, 0)
-    P = csr_handle(rp, c)
+    P = csr_handle(rp, c, one_group="off")
     assert P.lines
     x, info = K.sla_cg_solve(P, t(vs), t(b), 1e-8, 5000, check=False)
     torch.cuda.synchronize()

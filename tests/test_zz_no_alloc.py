@@ -45,13 +45,14 @@ def _noalloc(P, vt, bt, x, tol, maxit, flags=0):
     return info
 
 
-def _case(name, rp, c, v, b, tol, maxit, x0=None):
+def _case(name, rp, c, v, b, tol, maxit, x0=None, one_group="auto"):
     import torch
     import krylov_solvers_adjoint_amd as K
     n = len(rp) - 1
     vt, bt = t(v), t(b)
-    # the existing entry point, on a handle of its own
-    R = csr_handle(rp, c)
+    # the existing entry point, on a handle of its own ("off" where it would
+    # take the resident grid loop, which the allocation-free variant does not)
+    R = csr_handle(rp, c, one_group=one_group)
     x_ref, info_ref = K.sla_cg_solve(R, vt, bt, tol, maxit,
                                      x0=t(x0) if x0 is not None else None)
     torch.cuda.synchronize()
@@ -80,10 +81,11 @@ def test_noalloc_matches_cg_solve_twice_then_smaller():
     # the 1000^2 workload: b = A u*, 1000 fixed iterations (the line walk)
     rp, c, v = W.poisson_csr(1000)
     _, b = W.manufactured(1000)
-    _case("poisson1000 fixed", rp, c, v, b, 0.0, 1000)
+    _case("poisson1000 fixed", rp, c, v, b, 0.0, 1000, one_group="off")
     # a smaller system next (the row-order banded step), to a tolerance
     rp, c, v = W.poisson_csr(300)
-    _case("poisson300 tol", rp, c, v, W.uniform_rhs(300 * 300, 3), 1e-10, 5000)
+    _case("poisson300 tol", rp, c, v, W.uniform_rhs(300 * 300, 3), 1e-10, 5000,
+          one_group="off")
     # smaller still: the one-workgroup loop, from a start vector
     rp, c, v = W.poisson_csr(32)
     _case("poisson32 x0", rp, c, v, W.uniform_rhs(1024, 4), 1e-10, 5000,
