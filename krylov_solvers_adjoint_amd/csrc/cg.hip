@@ -1697,21 +1697,30 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
 // Grid sums (grid_sum): each workgroup writes its partial for round R into
 // slot[R & 1][g] as two 8-byte words, the double's high and low halves each
 // beside the tag R (a word is written whole, so a reader never sees a half
-// of another round), with relaxed device-scope stores, which the hardware
-// writes through to the device-coherent level; every workgroup polls all G
-// slots with device-scope loads until every tag reads R, then adds the G
-// partials in slot order (lane l the slots l, l + 64, ..., then the fixed
-// wave sum), so every workgroup gets the same bits.  No fence that writes
-// back or invalidates a whole L2 runs in the polling loop (8.7-10.5 us per
-// round with acquire polls, 3.3 us with these).  A poll limit bounds every
-// wait: past it the workgroup sets the shared failure flag, which every
-// other poll reads, and all leave the loop (ST_GRID_TIMEOUT).
+// of another round), with relaxed device-scope stores (sc1: written through
+// the L2 to the device-coherent level); every workgroup polls all G slots
+// with device-scope loads (sc1: served from that level) until every tag
+// reads R, then adds the G partials in slot order (lane l the slots l,
+// l + 64, ..., then the fixed wave sum), so every workgroup gets the same
+// bits.  No fence that writes back or invalidates a whole L2 runs in the
+// loop: a release fence (an L2 write-back walk) costs about 2 us per sum on
+// MI355X, acquire polls 8.7-10.5 us per round against 3.3 us for these.  A
+// poll limit bounds every wait: past it the workgroup sets the shared
+// failure flag, which every other poll reads, and all leave the loop
+// (ST_GRID_TIMEOUT).
 //
 // Halo: the neighbours' rows of p_{k+1} = r_{k+1} + beta_k p_k are formed
 // locally from their published boundary rows of r_{k+1} (written before the
-// second sum of iteration k, into halo[(k + 1) & 1]; the release fence
-// before the tags orders them) and the halo rows of p_k kept in LDS: the same
-// operations on the same operands as the owner's, hence the owner's bits.
+// second sum of iteration k, into halo[(k + 1) & 1]) and the halo rows of
+// p_k kept in LDS: the same operations on the same operands as the owner's,
+// hence the owner's bits.  Order: the rows go out as device-scope stores
+// too, every thread then waits for its stores to complete (s_waitcnt
+// vmcnt(0): a device-scope store completes once it is performed at the
+// device-coherent level), and only after the workgroup barrier does lane 0
+// write the tags; a reader that has seen every tag loads the rows with
+// device-scope loads after its own barrier.  Nothing the loop shares is
+// written through plain (L2 write-back) stores, which is what a release
+// fence would be needed for.
 // Double buffering by parity suffices: a buffer is written again two
 // iterations later, after sums that need every reader's partials, which
 // each reader posts only after reading it.
@@ -1910,13 +1919,14 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
 #pragma unroll
       for (int k = 0; k < K; ++k) red[k * W + w] = v[k];
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's published rows have landed
+    // this thread's published rows have been performed at device scope
+    // (below: why no release fence follows)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     ++round;
     if (w == 0) {
       uint64_t* sl = gs.slot + int64_t(round & 1) * G * (2 * kGridVals);
       if (lane == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           double a = 0.0;
