@@ -596,7 +596,7 @@ sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
  * instead of two kernels over the whole GPU per iteration, whose launch gaps
  * and partial sums dominate at such sizes (Problem statement: launch costs
  * of iterative solvers on small problems).  A single banded system (no
- * preconditioner) of 262144 to about a million unknowns whose rows fit the
+ * preconditioner) of 2049 to about a million unknowns whose rows fit the
  * chip (at most 8 rows per thread of one 512-thread workgroup per CU, its
  * largest column offset at most 1024 and at most the rows of a workgroup)
  * runs its whole CG loop in one cooperative launch with the system held in

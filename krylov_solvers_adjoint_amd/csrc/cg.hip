@@ -2837,12 +2837,14 @@ static sla_status launch_one_group(sla_csr A, const Ctx& ctx, Scal* scal, int64_
 // ---------------------------------------------------------------------------
 // The resident grid loop: plan and launch
 // ---------------------------------------------------------------------------
-// Single banded systems from kGridMinN unknowns (below, the two-kernel
-// iteration costs as much or less: Poisson 500^2 12.2 vs 12.0 us, 300^2 11.4
-// vs 10.8) while the rows fit: rw = max(ceil(n / CUs),
+// Single banded systems above the one-workgroup loop's range (that loop is
+// faster up to its 2048 unknowns: 1.9 us per iteration at 45^2) while the
+// rows fit: per iteration on Poisson grids, 100^2 5.8 us against 10.4 on the
+// two-kernel loop, 300^2 7.1 / 10.9, 512^2 7.8 / 12.3, 1000^2 10.5 / 22.9:
+// rw = max(ceil(n / CUs),
 // H) rows per workgroup, at most 8 per thread, p with its halo in 64 KB of
 // LDS, 2 H halo rows at most 4 per thread, every workgroup resident.
-constexpr int64_t kGridMinN = int64_t(1) << 18;
+constexpr int64_t kGridMinN = kOneGroupMaxN + 1;
 constexpr int64_t kGridPollLimit = int64_t(1) << 20;  // about a second of polling
 
 struct GridPlan {

@@ -3,7 +3,7 @@ banded pattern, or plain CSR rows whose 64-row tiles hold at most 336 slots):
 ragged sizes, Jacobi, history, warm starts, statuses and batches against the
 oracle, in the default (automatic) mode and with the two-kernel loop forced;
 banded rows against the staged CSR rows bit for bit; systems outside its range
-take the two-kernel loop bit for bit."""
+take the resident grid loop (banded) or the two-kernel loop bit for bit."""
 import numpy as np
 import pytest
 
@@ -78,22 +78,33 @@ def test_mode_argument():
     assert K._lib.sla_csr_set_one_group(P.handle, K.ONE_GROUP_AUTO) == K.OK
 
 
-def test_outside_the_range_takes_the_two_kernel_loop():
-    """2049 unknowns, or plain CSR tiles of more than 336 slots (9 per row,
-    more offsets than a band holds): the automatic mode gives the two-kernel
-    loop's bits."""
+def test_outside_the_range():
+    """2049 unknowns on a band: the resident grid loop (one launch over the
+    whole GPU), against the oracle; plain CSR tiles of more than 336 slots (9
+    per row, more offsets than a band holds): the automatic mode gives the
+    two-kernel loop's bits."""
     import torch
     import krylov_solvers_adjoint_amd as K
-    for n, offs in ((2049, (-37, -1, 1, 37)), (1000, (-4, -3, -2, -1, 1, 2, 3, 4))):
-        rp, c, v = _banded(n, offs, 7)
-        b = W.normal_rhs(n, 8)
-        xs = []
-        for mode in ("auto", "off"):
-            P = csr_handle(rp, c, one_group=mode)
-            x, info = K.sla_cg_solve(P, t(v), t(b), 1e-11, 5000)
-            torch.cuda.synchronize()
-            xs.append((x.cpu().numpy(), info.iterations))
-        assert np.array_equal(xs[0][0], xs[1][0]) and xs[0][1] == xs[1][1]
+    n = 2049
+    rp, c, v = _banded(n, (-37, -1, 1, 37), 7)
+    b = W.normal_rhs(n, 8)
+    P = csr_handle(rp, c)
+    x, info = K.sla_cg_solve(P, t(v), t(b), 1e-11, 5000)
+    torch.cuda.synchronize()
+    assert K.sla_resident_loop_ms(P) > 0.0
+    xo, io = oracle.cg(_A(rp, c, v), b, 1e-11, 5000)
+    assert iters_close(info.iterations, io.iterations) and rel(x.cpu().numpy(), xo) <= TOL_X
+    n = 1000
+    rp, c, v = _banded(n, (-4, -3, -2, -1, 1, 2, 3, 4), 7)
+    b = W.normal_rhs(n, 8)
+    xs = []
+    for mode in ("auto", "off"):
+        P = csr_handle(rp, c, one_group=mode)
+        assert not P.banded
+        x, info = K.sla_cg_solve(P, t(v), t(b), 1e-11, 5000)
+        torch.cuda.synchronize()
+        xs.append((x.cpu().numpy(), info.iterations))
+    assert np.array_equal(xs[0][0], xs[1][0]) and xs[0][1] == xs[1][1]
 
 
 @pytest.mark.parametrize("n,offs", [(1024, (-32, -1, 1, 32)), (777, (-29, -2, 2, 29)),
