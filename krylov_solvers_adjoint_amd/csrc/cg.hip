@@ -1709,18 +1709,23 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
 // failure flag, which every other poll reads, and all leave the loop
 // (ST_GRID_TIMEOUT).
 //
-// Halo: the neighbours' rows of p_{k+1} = r_{k+1} + beta_k p_k are formed
-// locally from their published boundary rows of r_{k+1} (written before the
-// second sum of iteration k, into halo[(k + 1) & 1]) and the halo rows of
-// p_k kept in LDS: the same operations on the same operands as the owner's,
-// hence the owner's bits.  Order: the rows go out as device-scope stores
-// too, every thread then waits for its stores to complete (s_waitcnt
-// vmcnt(0): a device-scope store completes once it is performed at the
-// device-coherent level), and only after the workgroup barrier does lane 0
-// write the tags; a reader that has seen every tag loads the rows with
-// device-scope loads after its own barrier.  Nothing the loop shares is
-// written through plain (L2 write-back) stores, which is what a release
-// fence would be needed for.
+// Halo: the neighbours' rows of r and p are formed locally, by the same
+// operations on the same operands as their owners', hence the owners' bits:
+// r_{k+1} = r_k - alpha_k q_k from the neighbours' boundary rows of q_k and
+// p_{k+1} = r_{k+1} + beta_k p_k from the halo rows of p_k kept in LDS (r_0's
+// boundary rows are exchanged once).  Each workgroup publishes its boundary
+// rows of q_k right after its SpMV, into halo[k & 1]; the stores complete
+// while the first sum and the updates run, the second sum waits for them,
+// and the neighbours read them after that sum (a buffer is written again
+// two iterations later, after sums that need every reader's partials, which
+// each reader posts only after reading it).  Order: the rows go out as
+// device-scope stores too, every thread waits for its stores to complete
+// before the second sum (s_waitcnt vmcnt(0): a device-scope store completes
+// once it is performed at the device-coherent level), and only after the
+// workgroup barrier does lane 0 write the tags; a reader that has seen
+// every tag loads the rows with device-scope loads after its own barrier.
+// Nothing the loop shares is written through plain (L2 write-back) stores,
+// which is what a release fence would be needed for.
 // Double buffering by parity suffices: a buffer is written again two
 // iterations later, after sums that need every reader's partials, which
 // each reader posts only after reading it.
@@ -1790,6 +1795,9 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   const int64_t r0 = int64_t(g) * gs.rw;
   const int nloc = int((r0 + gs.rw < n ? r0 + gs.rw : n) - r0);
   double* pl = lds_dyn;  // row r0 + l at pl[H + l], halo rows below and above
+  // q_k of the rows, staged for publish_q (rows past the block at ql[rw])
+  double* ql = lds_dyn + (gs.rw + 2 * H + 1);
+  auto x_idx = [&](int l) -> int { return l < nloc ? l : int(gs.rw); };
   // the block's slices of the arrays (bases uniform, offsets 32-bit)
   const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(cv.rowptr) + r0);
   const SLA_GLOBAL uint8_t* mask = gmem(cv.mask + r0);
@@ -1903,6 +1911,20 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
     for (int u = 0; u < kGridHaloPT; ++u)
       if (psrc[u] >= 0) dev_put(hb + uint32_t(t + u * NT), pl[psrc[u]]);
   };
+  // q_k of the rows staged in LDS (ql, rows past the block at ql[rw]) before
+  // the first sum's barrier; its boundary rows go out from there after that
+  // barrier (the same buffer layout as publish_r): no row tests on the
+  // registers
+  auto stage_q = [&](const double (&q)[RPT]) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) ql[x_idx(t + j * NT)] = q[j];
+  };
+  auto publish_q = [&](int par) {
+    double* hb = gs.halo + (int64_t(par) * G + g) * 2 * H;
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u)
+      if (psrc[u] >= 0) dev_put(hb + uint32_t(t + u * NT), ql[psrc[u] - H]);
+  };
   auto read_halo = [&](int par, double (&rh)[kGridHaloPT]) {
     double* hb = gs.halo + int64_t(par) * G * 2 * H;
 #pragma unroll
@@ -1911,18 +1933,21 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   // sum of K values over the grid, in place in every thread; false when a
   // wait timed out (here or in another workgroup)
   uint32_t round = 0;
-  auto grid_sum = [&](auto kc, double* v) -> bool {
+  auto no_hook = [] {};
+  auto grid_sum = [&](auto kc, double* v, auto wc, auto after_barrier) -> bool {
     constexpr int K = decltype(kc)::value;
+    constexpr bool WAIT = decltype(wc)::value;
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = wave_sum(v[k]);
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < K; ++k) red[k * W + w] = v[k];
     }
-    // this thread's published rows have been performed at device scope
-    // (below: why no release fence follows)
-    __builtin_amdgcn_s_waitcnt(0);
+    // WAIT: this thread's published rows have been performed at device
+    // scope (see above: why no release fence follows)
+    if constexpr (WAIT) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (w != 0) after_barrier();  // (wave 0 after posting its tag)
     ++round;
     if (w == 0) {
       uint64_t* sl = gs.slot + int64_t(round & 1) * G * (2 * kGridVals);
@@ -1936,6 +1961,7 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
           dev_put(sl + g * 2 * kGridVals + 2 * k + 1, (bits << 32) | round);
         }
       }
+      after_barrier();
       double s[K];
       bool failed = false;
       for (int64_t polls = 0;; ++polls) {
@@ -1982,8 +2008,10 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   };
   using One = std::integral_constant<int, 1>;
   using Two = std::integral_constant<int, 2>;
+  using Wait = std::true_type;
+  using NoWait = std::false_type;
 
-  double r[RPT], xv[RPT], pv[RPT], q[RPT], rh[kGridHaloPT];
+  double r[RPT], pv[RPT], q[RPT], rh[kGridHaloPT], xv[RPT];
   // r0 = b - A x0 (or b, x0 = 0): x0 of the rows and of the halo from x,
   // which no workgroup writes before every one has passed the first grid sum
   if (use_x0) {
@@ -2006,10 +2034,10 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int l = t + j * NT;
-    r[j] = xv[j] = pv[j] = 0.0;
+    r[j] = pv[j] = 0.0;
+    xv[j] = l < nloc && use_x0 ? x[l] : 0.0;
     if (l < nloc) {
       const double bi = b[l];
-      xv[j] = use_x0 ? x[l] : 0.0;
       r[j] = use_x0 ? bi - q[j] : bi;
       sums[0] = sums[0] + bi * bi;
       sums[1] = sums[1] + r[j] * r[j];
@@ -2021,9 +2049,12 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
     for (int i = t; i < nloc + 2 * H; i += NT) pl[i] = 0.0;
     __syncthreads();
   }
-  publish_r(0, r);
-  const bool ok0 = grid_sum(Two{}, sums);
-  read_halo(0, rh);
+  // r_0's boundary rows into buffer 1: buffer 0 takes q_0 right after this
+  // sum, while a neighbour may still be reading; q_1 goes to buffer 1 only
+  // after the second sum of iteration 0, which needs every reader's partials
+  publish_r(1, r);
+  const bool ok0 = grid_sum(Two{}, sums, Wait{}, no_hook);
+  read_halo(1, rh);
   const double bb = sums[0];
   double rr = sums[1];
   const double stop = (tol * tol) * bb;
@@ -2066,13 +2097,17 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
       if (hsrc[u] >= 0) pl[hidx(u)] = rh[u] + beta * pl[hidx(u)];
     __syncthreads();
     spmv(q);
+    // the boundary rows of q_k go out right after the first sum's barrier;
+    // the stores complete while that sum and the updates run, and the
+    // second sum waits for them
+    stage_q(q);
     // rows past the block hold zeros throughout (values, r, p, x), so they
     // add +0.0 to the sums and leave their bits alone: no row test here
     double pq = 0.0;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) pq = pq + pv[j] * q[j];
     // (the barriers of the sum also end every wave's gathers of p_k)
-    if (!grid_sum(One{}, &pq)) {
+    if (!grid_sum(One{}, &pq, NoWait{}, [&] { publish_q(int(k & 1)); })) {
       state = ST_GRID_TIMEOUT;
       it = k;
       rr_final = rr;
@@ -2092,14 +2127,18 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
       r[j] = r[j] - alpha * q[j];
       rn = rn + r[j] * r[j];
     }
-    publish_r(int((k + 1) & 1), r);
-    if (!grid_sum(One{}, &rn)) {
+    if (!grid_sum(One{}, &rn, Wait{}, no_hook)) {
       state = ST_GRID_TIMEOUT;
       it = k;
       rr_final = rr;
       break;
     }
-    read_halo(int((k + 1) & 1), rh);
+    // the halo rows of r_{k+1} = r_k - alpha_k q_k from the neighbours' q_k
+    // (published before their second sum), as their owners form them
+    double qh[kGridHaloPT];
+    read_halo(int(k & 1), qh);
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u) rh[u] = rh[u] - alpha * qh[u];
     rr_prev = rr;
     rr = rn;
   }
@@ -2891,13 +2930,22 @@ static bool grid_plan(const sla_csr A, int64_t batch, bool jacobi, GridPlan* gp)
   if (rpt == 0 || 2 * int64_t(H) > int64_t(kGridHaloPT) * kGridThreads) return false;
   const int nb = band_class(A);
   if (rpt == 8 && nb == 8) return false;  // (that variant spills registers)
-  const size_t lds = size_t(rw + 2 * int64_t(H) + 1) * sizeof(double);  // + the spare slot
-  if (lds > size_t(64) * 1024) return false;
+  // p with its halo and a spare slot, then q of the rows and a spare slot
+  const size_t lds = size_t(2 * rw + 2 * int64_t(H) + 2) * sizeof(double);
+  int lds_max = 0;
+  if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, A->device) !=
+          hipSuccess ||
+      lds + 1024 > size_t(lds_max))  // + the static areas
+    return false;
   int coop = 0;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, A->device) != hipSuccess ||
       !coop)
     return false;
   const GridFn fn = grid_kernel(A, rpt, nb);
+  if (fn != nullptr && lds > size_t(64) * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+    return false;
   int per_cu = 0;
   if (fn == nullptr ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
