@@ -450,7 +450,11 @@ sla_status sla_bicgstab_history(sla_csr A, int64_t system, double* rho_host,
  * twice.  method SLA_METHOD_CG (SPD systems; flags as sla_cg_solve, so
  * SLA_FLAG_JACOBI too) or SLA_METHOD_BICGSTAB (flags as sla_bicgstab_solve).
  * Every system is solved exactly as by the single-system call on its
- * handle (the same kernels and bits); up to 8 systems run at once, each on
+ * handle (the same kernels and bits), except that CG systems never take the
+ * resident grid loop (sla_csr_set_one_group): its cooperative launch holds
+ * every CU and would serialize the list, so such a system gets the
+ * two-kernel loop's bits (those of SLA_ONE_GROUP_OFF); up to 8 systems run
+ * at once, each on
  * a worker stream of the library's (created once per device, default
  * priority) that first waits for the work already queued on `stream`.
  * Host arrays of device pointers: b[i], x[i] [n_i].  info_host [count]

@@ -540,7 +540,8 @@ static sla_status run_cg_adjoint(sla_csr A, const double* x, const double* grad_
                                  double* grad_b, double* grad_vals, double tol, int64_t maxit,
                                  uint32_t flags, sla_cg_info* info, hipStream_t stream) {
   if (A->ro == nullptr &&
-      (use_one_group(A) || use_grid(A, A->batch, (flags & SLA_FLAG_JACOBI) != 0))) {
+      (use_one_group(A) || ((flags & kFlagNoResident) == 0 &&
+                            use_grid(A, A->batch, (flags & SLA_FLAG_JACOBI) != 0)))) {
     const sla_status ps = require_symmetric(A, false, "sla_cg_adjoint", stream);
     if (ps != SLA_OK) {
       fill_status(info, A->batch, ps);
@@ -702,7 +703,7 @@ sla_status sla_solve_list(int64_t count, const sla_csr* A, const double* const* 
         fill_status(in, 1, sym);
         return sym;
       }
-      return run_cg_any(A[i], b[i], x[i], tol, maxit, flags, in, st);
+      return run_cg_any(A[i], b[i], x[i], tol, maxit, flags | kFlagNoResident, in, st);
     }
     return run_bicgstab_any(A[i], b[i], x[i], tol, maxit, flags, in, st);
   });
@@ -727,7 +728,8 @@ sla_status sla_adjoint_list(int64_t count, const sla_csr* A, const double* const
     double* gv = grad_vals ? grad_vals[i] : nullptr;
     const double* xi = x ? x[i] : nullptr;
     return method == SLA_METHOD_CG
-               ? run_cg_adjoint(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in, st)
+               ? run_cg_adjoint(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit,
+                                flags | kFlagNoResident, in, st)
                : run_bicgstab_adjoint_any(A[i], xi, grad_x[i], grad_b[i], gv, tol, maxit, flags, in,
                                       st);
   });

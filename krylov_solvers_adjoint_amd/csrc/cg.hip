@@ -3074,7 +3074,7 @@ sla_status run_cg_space(sla_csr A, const CgSpace& sp, const double* b, double* x
   fill_ctx(A, sp, *sp.ctx_host, b, x, batch, want_hist, jacobi);
   const bool x0 = (flags & SLA_FLAG_X0) != 0;
   GridPlan gp;
-  if (sp.own && grid_plan(A, batch, jacobi, &gp)) {
+  if (sp.own && (flags & kFlagNoResident) == 0 && grid_plan(A, batch, jacobi, &gp)) {
     // the context by value; the record is read back from the device
     SLA_TRY(launch_grid(A, gp, *sp.ctx_host, scal_of(sp.ctx_dev, 0), tol, maxit, x0,
                         tail ? tail->gate : nullptr, st));

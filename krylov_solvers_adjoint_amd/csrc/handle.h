@@ -145,6 +145,12 @@ struct CgSpace {
 // the device, so no host round trip precedes the solve; grad_vals (or
 // nullptr) receives -lambda_i x_j, enqueued before the solve's results are
 // read back.
+// Internal solve flag (never accepted from callers): keep the solve off the
+// resident grid loop.  The list calls set it: their systems run concurrently
+// on worker streams, which cooperative launches, each holding every CU,
+// would serialize.
+constexpr uint32_t kFlagNoResident = 0x40000000u;
+
 struct AdjointTail {
   const int* gate = nullptr;
   const double* x = nullptr;

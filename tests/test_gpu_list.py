@@ -1,6 +1,9 @@
 """Lists of systems with distinct patterns (SparseTensorList): every system
 of a list solve is its single solve bit for bit (the same kernels on its
-own handle, run concurrently on worker streams) and matches the oracle; the
+own handle, run concurrently on worker streams; where the single solve takes
+the resident grid loop, whose cooperative launch would serialize the list,
+the list takes the two-kernel loop: the bits of a single solve with that
+loop) and matches the oracle; the
 adjoint list, the autograd node, Jacobi and BiCGStab lists, and the error
 reporting of a failing system."""
 import numpy as np
@@ -51,6 +54,15 @@ def _cg_systems():
     return out
 
 
+def _resident(P) -> bool:
+    """Whether the last solve on P ran the resident grid loop."""
+    import krylov_solvers_adjoint_amd as K
+    try:
+        return K.sla_resident_loop_ms(P) > 0.0
+    except K.SlaError:
+        return False
+
+
 def _oracle_A(rp, c, v):
     return oracle.CSR(len(rp) - 1, rp.astype(np.int64), c, v)
 
@@ -64,9 +76,17 @@ def test_cg_list_matches_single_solves_and_oracle():
     bs = [t(W.normal_rhs(len(rp) - 1, 10 + i)) for i, (rp, _, _) in enumerate(systems)]
     xs, infos = K.sla_solve_list(Ps, vals, bs, 1e-10, 5000)
     torch.cuda.synchronize()
+    single = []  # the handle whose single solves give the list's bits
     for i, (rp, c, v) in enumerate(systems):
         x1, i1 = K.sla_cg_solve(Ps[i], vals[i], bs[i], 1e-10, 5000)
         torch.cuda.synchronize()
+        if _resident(Ps[i]):
+            Q = csr_handle(rp, c, one_group="off")
+            x1, i1 = K.sla_cg_solve(Q, vals[i], bs[i], 1e-10, 5000)
+            torch.cuda.synchronize()
+            single.append(Q)
+        else:
+            single.append(Ps[i])
         assert np.array_equal(xs[i].cpu().numpy(), x1.cpu().numpy()), i
         assert infos[i].iterations == i1.iterations and infos[i].converged
         xo, io = oracle.cg(_oracle_A(rp, c, v), bs[i].cpu().numpy(), 1e-10, 5000)
@@ -75,8 +95,9 @@ def test_cg_list_matches_single_solves_and_oracle():
     gs = [t(W.normal_rhs(len(rp) - 1, 30 + i)) for i, (rp, _, _) in enumerate(systems)]
     gbs, gvs, ainf = K.sla_adjoint_list(Ps, vals, xs, gs, 1e-10, 5000)
     torch.cuda.synchronize()
+    assert any(S is not P for S, P in zip(single, Ps))  # a resident-size system is listed
     for i in range(len(systems)):
-        gb1, gv1, _ = K.sla_cg_adjoint(Ps[i], vals[i], xs[i], gs[i], 1e-10, 5000)
+        gb1, gv1, _ = K.sla_cg_adjoint(single[i], vals[i], xs[i], gs[i], 1e-10, 5000)
         torch.cuda.synchronize()
         assert np.array_equal(gbs[i].cpu().numpy(), gb1.cpu().numpy())
         assert np.array_equal(gvs[i].cpu().numpy(), gv1.cpu().numpy())
