@@ -1331,9 +1331,10 @@ def main():
         "eff_GBps": head["eff_GBps"],
         "pct_peak_effective": head["pct_peak_effective"],
         "bandwidth_note": "eff_GBps: canonical bytes (12 nnz + 4 (n+1) + 88 n per iteration, "
-                          "plus the pattern gradient) over the step's wall time; the 1M working "
-                          "set is Infinity-Cache resident, so this is an effective rate, not "
-                          "HBM bandwidth",
+                          "plus the pattern gradient) over the step's wall time; the resident "
+                          "loop holds the 1M system on chip (the two-kernel loop's working set "
+                          "is Infinity-Cache resident), so this is an effective rate, not HBM "
+                          "bandwidth",
         "solution_rel_error": head["solution_rel_error"],
         "free_delta_MB": head["free_delta_MB"],
         "library_MB": head["library_MB"],
