@@ -1688,89 +1688,108 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
 // the chip's registers and LDS (256 CUs hold 128 MB of VGPRs and 40 MB of
 // LDS): workgroup g of G (one per CU, all resident: cooperative launch) owns
 // rows [g rw, min(n, (g + 1) rw)), rw >= H = the band's largest |offset|,
-// and keeps their values by band offset, r, x and p in registers for the
-// whole solve.  p is published in LDS with H halo rows on each side.  The
-// matrix is read once per solve; an iteration moves only halo rows and
-// partial sums between workgroups, so it is bound by the two grid-wide sums
-// of Hestenes-Stiefel CG, not by HBM.
+// and keeps their values by band offset, r and s in registers and A r, p and
+// x in LDS for the whole solve; r is published in LDS with H halo rows on
+// each side.  The matrix is read once per solve; an iteration moves only
+// halo rows and partial sums between workgroups, so it is bound by the
+// latency of its grid-wide sum, not by HBM.
 //
-// Grid sums (grid_sum): each workgroup writes its partial for round R into
-// slot[R & 1][g] as two 8-byte words, the double's high and low halves each
-// beside the tag R (a word is written whole, so a reader never sees a half
-// of another round), with relaxed device-scope stores (sc1: written through
-// the L2 to the device-coherent level); every workgroup polls all G slots
-// with device-scope loads (sc1: served from that level) until every tag
-// reads R, then adds the G partials in slot order (lane l the slots l,
-// l + 64, ..., then the fixed wave sum), so every workgroup gets the same
-// bits.  No fence that writes back or invalidates a whole L2 runs in the
-// loop: a release fence (an L2 write-back walk) costs about 2 us per sum on
-// MI355X, acquire polls 8.7-10.5 us per round against 3.3 us for these.  A
-// poll limit bounds every wait: past it the workgroup sets the shared
+// The iteration is CG in the single-reduction form of Chronopoulos and Gear:
+// the SpMV takes r instead of p, u_k = A r_k, and one grid sum carries both
+// gamma_k = r_k.r_k and delta_k = r_k.u_k.  Then
+//   beta_k = gamma_k / gamma_{k-1},
+//   p_k.A p_k = delta_k - beta_k gamma_k / alpha_{k-1}   (delta_0 at k = 0),
+//   alpha_k = gamma_k / p_k.A p_k,
+//   p_k = r_k + beta_k p_{k-1},  s_k = u_k + beta_k s_{k-1}   (s_k = A p_k),
+//   x_{k+1} = x_k + alpha_k p_k,  r_{k+1} = r_k - alpha_k s_k.
+// The middle identity expands p_k.A p_k with r_k.r_{k-1} = 0 and
+// A p_{k-1} = (r_{k-1} - r_k) / alpha_{k-1}.  In exact arithmetic these are
+// the iterates, scalars, stopping rule and statuses of the loop with two sums
+// (Hestenes-Stiefel, the one-workgroup and two-kernel loops); in floating
+// point they differ from it by rounding.  The sum's latency is most of an
+// iteration here, so one sum per iteration instead of two is what counts.
+//
+// Grid sums (grid_sum): each workgroup writes its partials for round R into
+// slot[R & 1], every double as two 8-byte words, its high and low halves
+// each beside the tag R (a word is written whole, so a reader never sees a
+// half of another round), with relaxed device-scope stores (sc1: written
+// through the L2 to the device-coherent level), once into each of 8
+// replicas; workgroup g polls replica g % 8 (its waves share the G slots, a
+// slot per lane) with device-scope loads (sc1: served from that level) until
+// every tag reads R, then adds the G partials in slot order (a wave sum per
+// wave, then the waves in order), so every workgroup gets the same bits.  The
+// replicas spread the polls of 256 workgroups over 8 times as many memory
+// lines.  No fence that writes back or invalidates a whole L2 runs in the
+// loop: on MI355X a release fence (an L2 write-back walk) costs about 2 us per
+// sum, and acquire polls 8.7-10.5 us per round against about 3 us for these.
+// A poll limit bounds every wait: past it the workgroup sets the shared
 // failure flag, which every other poll reads, and all leave the loop
 // (ST_GRID_TIMEOUT).
 //
-// Halo: the neighbours' rows of r and p are formed locally, by the same
-// operations on the same operands as their owners', hence the owners' bits:
-// r_{k+1} = r_k - alpha_k q_k from the neighbours' boundary rows of q_k and
-// p_{k+1} = r_{k+1} + beta_k p_k from the halo rows of p_k kept in LDS (r_0's
-// boundary rows are exchanged once).  Each workgroup publishes its boundary
-// rows of q_k right after its SpMV, into halo[k & 1]; the stores complete
-// while the first sum and the updates run, the second sum waits for them,
-// and the neighbours read them after that sum (a buffer is written again
-// two iterations later, after sums that need every reader's partials, which
-// each reader posts only after reading it).  Order: the rows go out as
-// device-scope stores too, every thread waits for its stores to complete
-// before the second sum (s_waitcnt vmcnt(0): a device-scope store completes
-// once it is performed at the device-coherent level), and only after the
-// workgroup barrier does lane 0 write the tags; a reader that has seen
-// every tag loads the rows with device-scope loads after its own barrier.
-// Nothing the loop shares is written through plain (L2 write-back) stores,
-// which is what a release fence would be needed for.
+// Halo: the neighbours' rows of r are formed locally, by the same operations
+// on the same operands as their owners', hence the owners' bits:
+// s_k = u_k + beta_k s_{k-1} and r_{k+1} = r_k - alpha_k s_k from the
+// neighbours' boundary rows of u_k (r_0's boundary rows are exchanged once).
+// Each workgroup publishes its boundary rows of u_k during the sum, after its
+// first barrier, into halo[k & 1], tagged as the slots are with the round of
+// that sum; a reader loads them once the sum is complete and loads again
+// while a tag is not that round (the writer issued them before its own slot
+// tags, so that is rare).  Nothing waits for the stores and no fence runs.
 // Double buffering by parity suffices: a buffer is written again two
-// iterations later, after sums that need every reader's partials, which
-// each reader posts only after reading it.
-//
-// Same steps, stopping rule, statuses, history and x update as the
-// one-workgroup loop (k_cg_onegroup, banded rows); the dot products are
-// summed in another fixed order.
+// iterations later, after a sum that needs every reader's partials, which
+// each reader posts only after reading it.  Slots and halo words are cleared
+// before every launch, so no tag of an earlier launch is read.
 constexpr int kGridThreads = 512;   // threads per workgroup of the grid loop
 constexpr int kGridVals = 2;        // values one grid sum carries at most
 constexpr int kGridHaloPT = 4;      // halo rows per thread: 2 H <= 4 * 512
 
 struct GridSync {
-  uint64_t* slot;      // [2][G][2 * kGridVals] tagged words, by round parity
-  double* halo;        // [2][G][2][H] boundary rows of r: first H, last H
+  // [2][reps][kGridVals][2][G] tagged words (round parity, replica, value,
+  // high/low half, workgroup), a replica every rep_words words
+  uint64_t* slot;
+  uint64_t* halo;      // [2][G][2 H][2] tagged words: first H rows, last H rows
   int* fail;           // set when a wait passed its poll limit
   int64_t rw;          // rows per workgroup
   int32_t H;           // halo rows on each side
-  int32_t pad;
+  int32_t reps;        // replicas of the slots: workgroup g polls replica g % reps
+  int64_t rep_words;   // words from one replica to the next
   int64_t poll_limit;  // polls per wait before giving up
 };
 
 __device__ __forceinline__ void dev_put(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t dev_get(uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void dev_put(double* p, double v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double dev_get(double* p) {
+__device__ __forceinline__ uint64_t dev_get(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void dev_put(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int dev_get(int* p) {
+__device__ __forceinline__ int dev_get(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Slots and the failure flag cleared before a launch (a kernel: a caller's
-// stream may be captured).
-__global__ void k_grid_clear(uint64_t* __restrict__ slot, int64_t words, int* __restrict__ fail) {
+// v as two words at p, p + 1: its high and low 32 bits each beside the tag
+__device__ __forceinline__ void put_tagged(uint64_t* p, double v, uint32_t tag) {
+  const uint64_t bits = uint64_t(__double_as_longlong(v));
+  dev_put(p, (bits & 0xffffffff00000000ull) | tag);
+  dev_put(p + 1, (bits << 32) | tag);
+}
+__device__ __forceinline__ bool has_tag(uint64_t hi, uint64_t lo, uint32_t tag) {
+  return uint32_t(hi) == tag && uint32_t(lo) == tag;
+}
+__device__ __forceinline__ double untag(uint64_t hi, uint64_t lo) {
+  return __longlong_as_double((long long)((hi & 0xffffffff00000000ull) | (lo >> 32)));
+}
+
+// Slots, halo words and the failure flag cleared before a launch (a kernel:
+// a caller's stream may be captured).
+__global__ void k_grid_clear(uint64_t* __restrict__ slot, int64_t slot_words,
+                             uint64_t* __restrict__ halo, int64_t halo_words,
+                             int* __restrict__ fail) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < words) slot[i] = 0;
+  if (i < slot_words) slot[i] = 0;
+  else if (i < slot_words + halo_words) halo[i - slot_words] = 0;
   if (i == 0) *fail = 0;
 }
 
@@ -1784,20 +1803,24 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
                                                           const int* gate) {
   constexpr int NT = kGridThreads, W = NT / kWave;
   extern __shared__ double lds_dyn[];
-  __shared__ double red[kGridVals * W];
-  __shared__ double bcast[kGridVals];
-  __shared__ int lfail;
+  __shared__ double red[kGridVals * W], red2[kGridVals * W];
+  __shared__ int lfail, hfail;
   const int t = threadIdx.x;
   const int lane = int(lane_id()), w = wave_index();
   const int g = int(blockIdx.x), G = int(gridDim.x);
   const int64_t n = cv.n;
   const int H = gs.H;
+  const int rw = int(gs.rw);
   const int64_t r0 = int64_t(g) * gs.rw;
   const int nloc = int((r0 + gs.rw < n ? r0 + gs.rw : n) - r0);
-  double* pl = lds_dyn;  // row r0 + l at pl[H + l], halo rows below and above
-  // q_k of the rows, staged for publish_q (rows past the block at ql[rw])
-  double* ql = lds_dyn + (gs.rw + 2 * H + 1);
-  auto x_idx = [&](int l) -> int { return l < nloc ? l : int(gs.rw); };
+  // r of row r0 + l at rl[H + l], the halo rows below and above, a spare
+  // slot; then u = A r, p and x of the rows, each with a spare slot at index
+  // rw for the rows past the block
+  double* rl = lds_dyn;
+  double* ul = rl + (rw + 2 * H + 1);
+  double* pl = ul + (rw + 1);
+  double* xl = pl + (rw + 1);
+  auto x_idx = [&](int l) -> int { return l < nloc ? l : rw; };
   // the block's slices of the arrays (bases uniform, offsets 32-bit)
   const SLA_GLOBAL RP* rowptr = gmem(static_cast<const RP*>(cv.rowptr) + r0);
   const SLA_GLOBAL uint8_t* mask = gmem(cv.mask + r0);
@@ -1847,7 +1870,7 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   // this thread's halo entries e = t + u * 512 < 2 H: e < H the row
   // r0 - H + e (the lower neighbour's last rows), else r0 + nloc + e - H (the
   // upper neighbour's first rows); LDS index e, or nloc + e.  hsrc: the
-  // entry's offset in a halo buffer of one parity, or -1 (no such row).
+  // entry's index in a halo buffer of one parity, or -1 (no such row).
   int32_t hsrc[kGridHaloPT];
 #pragma unroll
   for (int u = 0; u < kGridHaloPT; ++u) {
@@ -1862,21 +1885,21 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   }
   auto hidx = [&](int u) -> int { return t + u * NT < H ? t + u * NT : nloc + t + u * NT; };
   // the same entries as this workgroup's published boundary rows: e < H the
-  // row l = e, else l = nloc - H + (e - H); psrc: the row's LDS index, or -1
-  int32_t psrc[kGridHaloPT];
-#pragma unroll
-  for (int u = 0; u < kGridHaloPT; ++u) {
+  // row l = e, else l = nloc - H + (e - H); psrc: the row's index in rl, or
+  // -1 (formed where used: no registers held through the loop)
+  auto psrc = [&](int u) -> int {
     const int e = t + u * NT;
     const int l = e < H ? e : nloc - H + (e - H);
-    psrc[u] = (e < 2 * H && l >= 0 && l < nloc) ? H + l : -1;
-  }
-  // LDS index of row l of the block; rows past the block (lanes without a
+    return (e < 2 * H && l >= 0 && l < nloc) ? H + l : -1;
+  };
+  // index of row l of the block in rl; rows past the block (lanes without a
   // row, whose values are all zero) store to one spare slot past the halo
   const int spare = nloc + 2 * H;
   auto own_idx = [&](int l) -> int { return l < nloc ? H + l : spare; };
-  for (int i = t; i < nloc + 2 * H; i += NT) pl[i] = 0.0;
+  for (int i = t; i < nloc + 2 * H; i += NT) rl[i] = 0.0;
+  if (t == 0) lfail = hfail = 0;
   __syncthreads();
-  // q = A v for this thread's rows, v published in pl (rows and halo)
+  // q = A v for this thread's rows, v published in rl (rows and halo)
   auto spmv = [&](double (&q)[RPT]) {
     // an opaque zero: the gather addresses and the slot masks are formed
     // here at every call, not hoisted out of the CG loop into registers (40
@@ -1889,7 +1912,7 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
       const uint32_t m = bm[j] + uint32_t(z);
       double gv[NB];
 #pragma unroll
-      for (int o = 0; o < NB; ++o) gv[o] = pl[((m >> o) & 1u) ? li + boff[o] : li];
+      for (int o = 0; o < NB; ++o) gv[o] = rl[((m >> o) & 1u) ? li + boff[o] : li];
       double acc = 0.0;
 #pragma unroll
       for (int o = 0; o < NB; ++o) {
@@ -1899,132 +1922,183 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
       q[j] = acc;
     }
   };
-  // boundary rows of r into halo buffer `par` (first H rows for g - 1, last
-  // H rows for g + 1), staged in pl's rows (p there is no longer read: every
-  // gather ended before the last barrier); pl's halo is left alone
-  auto publish_r = [&](int par, const double (&r)[RPT]) {
+  // this workgroup's entries in halo buffer `par` (first H rows for g - 1,
+  // last H rows for g + 1)
+  auto own_halo = [&](int par) -> uint64_t* {
+    return gs.halo + (int64_t(par) * G + g) * (4 * int64_t(H));
+  };
+  // boundary rows of r_0 into halo buffer `par`, staged in rl's rows (the
+  // halo of rl is left alone)
+  auto publish_r = [&](int par, uint32_t tag, const double (&r)[RPT]) {
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) pl[own_idx(t + j * NT)] = r[j];
+    for (int j = 0; j < RPT; ++j) rl[own_idx(t + j * NT)] = r[j];
     __syncthreads();
-    double* hb = gs.halo + (int64_t(par) * G + g) * 2 * H;
+    uint64_t* hb = own_halo(par);
 #pragma unroll
     for (int u = 0; u < kGridHaloPT; ++u)
-      if (psrc[u] >= 0) dev_put(hb + uint32_t(t + u * NT), pl[psrc[u]]);
+      if (psrc(u) >= 0) put_tagged(hb + 2 * uint32_t(t + u * NT), rl[psrc(u)], tag);
   };
-  // q_k of the rows staged in LDS (ql, rows past the block at ql[rw]) before
-  // the first sum's barrier; its boundary rows go out from there after that
-  // barrier (the same buffer layout as publish_r): no row tests on the
-  // registers
-  auto stage_q = [&](const double (&q)[RPT]) {
+  // u_k of the rows staged in ul (rows past the block at ul[rw]) before the
+  // sum's first barrier; its boundary rows go out from there after that
+  // barrier: no row tests on the registers
+  auto stage_u = [&](const double (&q)[RPT]) {
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) ql[x_idx(t + j * NT)] = q[j];
+    for (int j = 0; j < RPT; ++j) ul[x_idx(t + j * NT)] = q[j];
   };
-  auto publish_q = [&](int par) {
-    double* hb = gs.halo + (int64_t(par) * G + g) * 2 * H;
+  auto publish_u = [&](int par, uint32_t tag) {
+    uint64_t* hb = own_halo(par);
 #pragma unroll
     for (int u = 0; u < kGridHaloPT; ++u)
-      if (psrc[u] >= 0) dev_put(hb + uint32_t(t + u * NT), ql[psrc[u] - H]);
+      if (psrc(u) >= 0) put_tagged(hb + 2 * uint32_t(t + u * NT), ul[psrc(u) - H], tag);
   };
-  auto read_halo = [&](int par, double (&rh)[kGridHaloPT]) {
-    double* hb = gs.halo + int64_t(par) * G * 2 * H;
+  // the neighbours' words of this thread's halo entries in buffer `par`
+  // (entries without a row read as tagged zeros)
+  auto halo_load = [&](int par, uint32_t tag, uint64_t (&hw)[kGridHaloPT][2]) {
+    const uint64_t* hb = gs.halo + int64_t(par) * G * (4 * int64_t(H));
 #pragma unroll
-    for (int u = 0; u < kGridHaloPT; ++u) rh[u] = hsrc[u] >= 0 ? dev_get(hb + hsrc[u]) : 0.0;
+    for (int u = 0; u < kGridHaloPT; ++u) {
+      hw[u][0] = hw[u][1] = tag;
+      if (hsrc[u] >= 0) {
+        hw[u][0] = dev_get(hb + 2 * uint32_t(hsrc[u]));
+        hw[u][1] = dev_get(hb + 2 * uint32_t(hsrc[u]) + 1);
+      }
+    }
+  };
+  // the halo values once every word carries `tag`, loading again meanwhile;
+  // zeros and hfail set when a wait timed out (here or in another workgroup)
+  auto halo_take = [&](int par, uint32_t tag, uint64_t (&hw)[kGridHaloPT][2],
+                       double (&v)[kGridHaloPT]) {
+    for (int64_t polls = 0;; ++polls) {
+      bool ok = true;
+#pragma unroll
+      for (int u = 0; u < kGridHaloPT; ++u) ok = ok && has_tag(hw[u][0], hw[u][1], tag);
+      if (__all(ok)) break;
+      const int f = (polls & 15) == 15 ? __builtin_amdgcn_readfirstlane(dev_get(gs.fail)) : 0;
+      if (f != 0 || polls >= gs.poll_limit) {
+        if (lane == 0) {
+          if (f == 0) dev_put(gs.fail, 1);
+          hfail = 1;
+        }
+#pragma unroll
+        for (int u = 0; u < kGridHaloPT; ++u) hw[u][0] = hw[u][1] = 0;
+        break;
+      }
+      halo_load(par, tag, hw);
+    }
+#pragma unroll
+    for (int u = 0; u < kGridHaloPT; ++u) v[u] = hsrc[u] >= 0 ? untag(hw[u][0], hw[u][1]) : 0.0;
   };
   // sum of K values over the grid, in place in every thread; false when a
-  // wait timed out (here or in another workgroup)
+  // wait timed out (here or in another workgroup).  after_barrier runs in
+  // every thread once the partials are in red (wave 0: after posting its tag).
   uint32_t round = 0;
   auto no_hook = [] {};
-  auto grid_sum = [&](auto kc, double* v, auto wc, auto after_barrier) -> bool {
+  auto grid_sum = [&](auto kc, double* v, auto after_barrier) -> bool {
     constexpr int K = decltype(kc)::value;
-    constexpr bool WAIT = decltype(wc)::value;
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = wave_sum(v[k]);
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < K; ++k) red[k * W + w] = v[k];
     }
-    // WAIT: this thread's published rows have been performed at device
-    // scope (see above: why no release fence follows)
-    if constexpr (WAIT) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (w != 0) after_barrier();  // (wave 0 after posting its tag)
     ++round;
-    if (w == 0) {
-      uint64_t* sl = gs.slot + int64_t(round & 1) * G * (2 * kGridVals);
-      if (lane == 0) {
+    uint64_t* sl = gs.slot + int64_t(round & 1) * gs.reps * gs.rep_words;
+    // lane i < reps of wave 0 posts the partials into replica i: value k's
+    // halves at words (2 k) G + g and (2 k + 1) G + g, so a poll's lanes read
+    // consecutive words
+    if (w == 0 && lane < gs.reps) {
+      uint64_t* mine = sl + lane * gs.rep_words + g;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          double a = 0.0;
-          for (int ww = 0; ww < W; ++ww) a = a + red[k * W + ww];
-          const uint64_t bits = uint64_t(__double_as_longlong(a));
-          dev_put(sl + g * 2 * kGridVals + 2 * k, (bits & 0xffffffff00000000ull) | round);
-          dev_put(sl + g * 2 * kGridVals + 2 * k + 1, (bits << 32) | round);
+      for (int k = 0; k < K; ++k) {
+        double a = 0.0;
+        for (int ww = 0; ww < W; ++ww) a = a + red[k * W + ww];
+        const uint64_t bits = uint64_t(__double_as_longlong(a));
+        dev_put(mine + (2 * k) * G, (bits & 0xffffffff00000000ull) | round);
+        dev_put(mine + (2 * k + 1) * G, (bits << 32) | round);
+      }
+    }
+    after_barrier();
+    // every wave polls its share of the slots, lane l the slot w S + l (a
+    // few loads per lane, all the workgroup's waves at once, where one wave
+    // alone took 4 slots per lane)
+    sl += (g % gs.reps) * gs.rep_words;
+    const int S = (G + W - 1) / W;  // (<= 64: G <= 512)
+    const int gg = w * S + lane;
+    const bool mine = lane < S && gg < G;
+    uint64_t wa[K][2];
+    auto poll = [&](uint64_t (&wd)[K][2]) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        wd[k][0] = wd[k][1] = round;  // (no slot: reads as tagged zero)
+        if (mine) {
+          wd[k][0] = dev_get(sl + (2 * k) * G + gg);
+          wd[k][1] = dev_get(sl + (2 * k + 1) * G + gg);
         }
       }
-      after_barrier();
-      double s[K];
-      bool failed = false;
-      for (int64_t polls = 0;; ++polls) {
-        bool ok = true;
-        double ss[K];
+    };
+    auto ready = [&](const uint64_t (&wd)[K][2]) {
+      bool ok = true;
 #pragma unroll
-        for (int k = 0; k < K; ++k) ss[k] = 0.0;
-        for (int gg = lane; gg < G; gg += kWave) {
+      for (int k = 0; k < K; ++k) ok = ok && has_tag(wd[k][0], wd[k][1], round);
+      return __all(ok);
+    };
+    double s[K];
+    auto take = [&](const uint64_t (&wd)[K][2]) {
 #pragma unroll
-          for (int k = 0; k < K; ++k) {
-            const uint64_t hi = dev_get(sl + gg * 2 * kGridVals + 2 * k);
-            const uint64_t lo = dev_get(sl + gg * 2 * kGridVals + 2 * k + 1);
-            ok = ok && uint32_t(hi) == round && uint32_t(lo) == round;
-            ss[k] = ss[k] + __longlong_as_double(
-                                (long long)((hi & 0xffffffff00000000ull) | (lo >> 32)));
-          }
-        }
-        if (__all(ok)) {
-#pragma unroll
-          for (int k = 0; k < K; ++k) s[k] = ss[k];
-          break;
-        }
-        const int f = (polls & 15) == 15 ? __builtin_amdgcn_readfirstlane(dev_get(gs.fail)) : 0;
-        if (f != 0 || polls >= gs.poll_limit) {
-          if (f == 0 && lane == 0) dev_put(gs.fail, 1);
-          failed = true;
-#pragma unroll
-          for (int k = 0; k < K; ++k) s[k] = 0.0;
-          break;
-        }
+      for (int k = 0; k < K; ++k) s[k] = mine ? untag(wd[k][0], wd[k][1]) : 0.0;
+    };
+    bool failed = false;
+    poll(wa);
+    for (int64_t polls = 0;; ++polls) {
+      if (ready(wa)) {
+        take(wa);
+        break;
       }
+      poll(wa);
+      const int f = (polls & 15) == 15 ? __builtin_amdgcn_readfirstlane(dev_get(gs.fail)) : 0;
+      if (f != 0 || polls >= gs.poll_limit) {
+        if (f == 0 && lane == 0) dev_put(gs.fail, 1);
+        failed = true;
 #pragma unroll
-      for (int k = 0; k < K; ++k) s[k] = wave_sum(s[k]);
-      if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) bcast[k] = s[k];
-        lfail = failed ? 1 : 0;
+        for (int k = 0; k < K; ++k) s[k] = 0.0;
+        break;
       }
+    }
+    // the waves' sums in wave order: the same bits in every workgroup
+#pragma unroll
+    for (int k = 0; k < K; ++k) s[k] = wave_sum(s[k]);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) red2[k * W + w] = s[k];
+      if (failed) lfail = 1;
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < K; ++k) v[k] = bcast[k];
+    for (int k = 0; k < K; ++k) {
+      double a = 0.0;
+      for (int ww = 0; ww < W; ++ww) a = a + red2[k * W + ww];
+      v[k] = a;
+    }
     return lfail == 0;
   };
-  using One = std::integral_constant<int, 1>;
   using Two = std::integral_constant<int, 2>;
-  using Wait = std::true_type;
-  using NoWait = std::false_type;
 
-  double r[RPT], pv[RPT], q[RPT], rh[kGridHaloPT], xv[RPT];
+  double r[RPT], s[RPT], q[RPT], rh[kGridHaloPT], sh[kGridHaloPT];
+  uint64_t hw[kGridHaloPT][2];
   // r0 = b - A x0 (or b, x0 = 0): x0 of the rows and of the halo from x,
   // which no workgroup writes before every one has passed the first grid sum
   if (use_x0) {
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int l = t + j * NT;
-      pl[own_idx(l)] = l < nloc ? x[l] : 0.0;
+      rl[own_idx(l)] = l < nloc ? x[l] : 0.0;
     }
 #pragma unroll
     for (int u = 0; u < kGridHaloPT; ++u)
       if (hsrc[u] >= 0) {
         const int e = t + u * NT;
-        pl[hidx(u)] = x[e < H ? e - H : nloc + (e - H)];
+        rl[hidx(u)] = x[e < H ? e - H : nloc + (e - H)];
       }
     __syncthreads();
     spmv(q);
@@ -2034,8 +2108,10 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int l = t + j * NT;
-    r[j] = pv[j] = 0.0;
-    xv[j] = l < nloc && use_x0 ? x[l] : 0.0;
+    const int xi = x_idx(l);
+    r[j] = s[j] = 0.0;
+    pl[xi] = 0.0;
+    xl[xi] = l < nloc && use_x0 ? x[l] : 0.0;
     if (l < nloc) {
       const double bi = b[l];
       r[j] = use_x0 ? bi - q[j] : bi;
@@ -2043,109 +2119,114 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
       sums[1] = sums[1] + r[j] * r[j];
     }
   }
-  // p's halo starts from zero (p_{-1} = 0), as p does; the barrier keeps
-  // the clearing apart from the staging of r in publish_r
-  if (use_x0) {
-    for (int i = t; i < nloc + 2 * H; i += NT) pl[i] = 0.0;
-    __syncthreads();
-  }
-  // r_0's boundary rows into buffer 1: buffer 0 takes q_0 right after this
-  // sum, while a neighbour may still be reading; q_1 goes to buffer 1 only
-  // after the second sum of iteration 0, which needs every reader's partials
-  publish_r(1, r);
-  const bool ok0 = grid_sum(Two{}, sums, Wait{}, no_hook);
-  read_halo(1, rh);
+#pragma unroll
+  for (int u = 0; u < kGridHaloPT; ++u) sh[u] = 0.0;
+  // r_0's boundary rows into buffer 1 (iteration 0 writes buffer 0 while a
+  // neighbour may still be reading them); the halo of rl takes them after the
+  // sum (entries without a row keep their zeros)
+  uint32_t tag = round + 1;
+  publish_r(1, tag, r);
+  const bool ok0 = grid_sum(Two{}, sums, no_hook);
+  halo_load(1, tag, hw);
+  halo_take(1, tag, hw, rh);
+#pragma unroll
+  for (int u = 0; u < kGridHaloPT; ++u)
+    if (hsrc[u] >= 0) rl[hidx(u)] = rh[u];
+  __syncthreads();
   const double bb = sums[0];
   double rr = sums[1];
   const double stop = (tol * tol) * bb;
   int32_t state = (!isfinite(bb) || !isfinite(rr)) ? ST_NONFINITE : ST_RUNNING;
-  if (!ok0) state = ST_GRID_TIMEOUT;
+  if (!ok0 || hfail != 0) state = ST_GRID_TIMEOUT;
   int64_t it = 0;
   double rr_final = rr;
-  double alpha = 0.0, rr_prev = rr;
+  double alpha = 0.0;
   // every thread holds the same scalars, so every branch below is uniform
   for (int64_t k = 0; state == ST_RUNNING; ++k) {
+    // rl holds r_k on the rows and the halo
+    spmv(q);
+    stage_u(q);
+    // rows past the block hold zeros throughout (values, r, s, u, p, x), so
+    // they add +0.0 to the sums and leave their bits alone: no row test here
+    double gd[2] = {0.0, 0.0};  // r.r, r.u
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      gd[0] = gd[0] + r[j] * r[j];
+      gd[1] = gd[1] + r[j] * q[j];
+    }
+    const int par = int(k & 1);
+    tag = round + 1;
+    // (the sum's barriers also end every wave's gathers of r_k)
+    if (!grid_sum(Two{}, gd, [&] { publish_u(par, tag); })) {
+      state = ST_GRID_TIMEOUT;
+      it = k;
+      rr_final = rr;
+      break;
+    }
+    const double gk = gd[0], dk = gd[1];
     double beta = 0.0;
     if (k > 0) {
-      if (!isfinite(rr)) {
+      if (!isfinite(gk)) {
         state = ST_NONFINITE;  // iteration k-1 did not complete
         it = k - 1;
-        rr_final = rr_prev;
+        rr_final = rr;
         break;
       }
-      beta = rr / rr_prev;
+      beta = gk / rr;
       if (hist != nullptr && g == 0 && t == 0 && k - 1 < hist_cap) {
         hist[(k - 1) * 3 + 0] = alpha;
         hist[(k - 1) * 3 + 1] = beta;
-        hist[(k - 1) * 3 + 2] = rr;
+        hist[(k - 1) * 3 + 2] = gk;
       }
     }
-    if (rr <= stop || k >= maxit) {
-      state = rr <= stop ? ST_CONVERGED : ST_MAXIT;
+    if (gk <= stop || k >= maxit) {
+      state = gk <= stop ? ST_CONVERGED : ST_MAXIT;
       it = k;
-      rr_final = rr;
+      rr_final = gk;
       break;
     }
-    // p_k on the rows and on the halo, published in LDS for the gathers
+    const double pap = k > 0 ? dk - beta * (gk / alpha) : dk;  // p_k.A p_k
+    if (!isfinite(pap) || !(pap > 0.0)) {
+      state = !isfinite(pap) ? ST_NONFINITE : ST_NOT_SPD;
+      it = k;
+      rr_final = gk;
+      break;
+    }
+    alpha = gk / pap;
+    rr = gk;
+    // the neighbours' u_k: loaded before the rows' updates, taken after
+    halo_load(par, tag, hw);
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      pv[j] = r[j] + beta * pv[j];
-      pl[own_idx(t + j * NT)] = pv[j];
+      const int l = t + j * NT;
+      const int xi = x_idx(l);
+      s[j] = ul[xi] + beta * s[j];
+      const double pj = r[j] + beta * pl[xi];
+      pl[xi] = pj;
+      xl[xi] = xl[xi] + alpha * pj;
+      r[j] = r[j] - alpha * s[j];
+      rl[own_idx(l)] = r[j];
     }
+    double uh[kGridHaloPT];
+    halo_take(par, tag, hw, uh);
 #pragma unroll
-    for (int u = 0; u < kGridHaloPT; ++u)
-      if (hsrc[u] >= 0) pl[hidx(u)] = rh[u] + beta * pl[hidx(u)];
+    for (int u = 0; u < kGridHaloPT; ++u) {
+      sh[u] = uh[u] + beta * sh[u];
+      rh[u] = rh[u] - alpha * sh[u];
+      if (hsrc[u] >= 0) rl[hidx(u)] = rh[u];
+    }
     __syncthreads();
-    spmv(q);
-    // the boundary rows of q_k go out right after the first sum's barrier;
-    // the stores complete while that sum and the updates run, and the
-    // second sum waits for them
-    stage_q(q);
-    // rows past the block hold zeros throughout (values, r, p, x), so they
-    // add +0.0 to the sums and leave their bits alone: no row test here
-    double pq = 0.0;
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) pq = pq + pv[j] * q[j];
-    // (the barriers of the sum also end every wave's gathers of p_k)
-    if (!grid_sum(One{}, &pq, NoWait{}, [&] { publish_q(int(k & 1)); })) {
+    if (hfail != 0) {
       state = ST_GRID_TIMEOUT;
-      it = k;
+      it = k + 1;
       rr_final = rr;
       break;
     }
-    if (!isfinite(pq) || !(pq > 0.0)) {
-      state = !isfinite(pq) ? ST_NONFINITE : ST_NOT_SPD;
-      it = k;
-      rr_final = rr;
-      break;
-    }
-    alpha = rr / pq;
-    double rn = 0.0;
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      xv[j] = xv[j] + alpha * pv[j];
-      r[j] = r[j] - alpha * q[j];
-      rn = rn + r[j] * r[j];
-    }
-    if (!grid_sum(One{}, &rn, Wait{}, no_hook)) {
-      state = ST_GRID_TIMEOUT;
-      it = k;
-      rr_final = rr;
-      break;
-    }
-    // the halo rows of r_{k+1} = r_k - alpha_k q_k from the neighbours' q_k
-    // (published before their second sum), as their owners form them
-    double qh[kGridHaloPT];
-    read_halo(int(k & 1), qh);
-#pragma unroll
-    for (int u = 0; u < kGridHaloPT; ++u) rh[u] = rh[u] - alpha * qh[u];
-    rr_prev = rr;
-    rr = rn;
   }
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int l = t + j * NT;
-    if (l < nloc) x[l] = xv[j];
+    if (l < nloc) x[l] = xl[l];
   }
   if (g == 0 && t == 0) {
     scal->bb = bb;
@@ -2885,6 +2966,10 @@ static sla_status launch_one_group(sla_csr A, const Ctx& ctx, Scal* scal, int64_
 // LDS, 2 H halo rows at most 4 per thread, every workgroup resident.
 constexpr int64_t kGridMinN = kOneGroupMaxN + 1;
 constexpr int64_t kGridPollLimit = int64_t(1) << 20;  // about a second of polling
+// Copies of the sum slots: every workgroup posts its partials into each, and
+// polls the copy g % kGridReps, so no few memory lines take every poll
+constexpr int32_t kGridReps = 8;
+constexpr int64_t kGridRepAlign = 528;  // words (4 KB + 128 B: replicas on other lines)
 
 struct GridPlan {
   int32_t G = 0;
@@ -2928,10 +3013,12 @@ static bool grid_plan(const sla_csr A, int64_t batch, bool jacobi, GridPlan* gp)
   const int64_t need = (rw + kGridThreads - 1) / kGridThreads;
   const int rpt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 0;
   if (rpt == 0 || 2 * int64_t(H) > int64_t(kGridHaloPT) * kGridThreads) return false;
+  if (G > int64_t(kGridThreads / kWave) * kWave) return false;  // a slot per polling lane
   const int nb = band_class(A);
   if (rpt == 8 && nb == 8) return false;  // (that variant spills registers)
-  // p with its halo and a spare slot, then q of the rows and a spare slot
-  const size_t lds = size_t(2 * rw + 2 * int64_t(H) + 2) * sizeof(double);
+  // r with its halo and a spare slot, then A r, p and x of the rows, each
+  // with a spare slot
+  const size_t lds = size_t(4 * rw + 2 * int64_t(H) + 4) * sizeof(double);
   int lds_max = 0;
   if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, A->device) !=
           hipSuccess ||
@@ -2969,8 +3056,12 @@ bool use_grid(const sla_csr A, int64_t batch, bool jacobi) {
 static sla_status launch_grid(sla_csr A, const GridPlan& gp, const Ctx& ctx, Scal* scal,
                               double tol, int64_t maxit, bool x0, const int* gate,
                               hipStream_t st) {
-  const int64_t words = int64_t(2) * gp.G * 2 * kGridVals;
-  const int64_t halo = int64_t(2) * gp.G * 2 * gp.H;
+  // replicas kGridRepAlign words apart at least, each a whole number of
+  // those
+  const int64_t rep_words =
+      (int64_t(2) * kGridVals * gp.G + kGridRepAlign - 1) / kGridRepAlign * kGridRepAlign;
+  const int64_t words = int64_t(2) * kGridReps * rep_words;
+  const int64_t halo = int64_t(2) * gp.G * 2 * gp.H * 2;  // tagged words
   if (A->grid_slot == nullptr || A->grid_slot_words < words || A->grid_halo_len < halo) {
     dev_free(A->grid_slot);
     dev_free(A->grid_halo);
@@ -2985,7 +3076,9 @@ static sla_status launch_grid(sla_csr A, const GridPlan& gp, const Ctx& ctx, Sca
   if (A->grid_fail == nullptr) SLA_TRY(dev_alloc(&A->grid_fail, 1, "grid failure flag"));
   if (A->grid_ev[0] == nullptr)
     for (auto& e : A->grid_ev) SLA_TRY_HIP(hipEventCreate(&e));
-  k_grid_clear<<<unsigned((words + 255) / 256), 256, 0, st>>>(A->grid_slot, words, A->grid_fail);
+  k_grid_clear<<<unsigned((words + halo + 255) / 256), 256, 0, st>>>(A->grid_slot, words,
+                                                                     A->grid_halo, halo,
+                                                                     A->grid_fail);
   LAUNCH_CHECK();
   GridSync gs;
   gs.slot = A->grid_slot;
@@ -2993,7 +3086,8 @@ static sla_status launch_grid(sla_csr A, const GridPlan& gp, const Ctx& ctx, Sca
   gs.fail = A->grid_fail;
   gs.rw = gp.rw;
   gs.H = gp.H;
-  gs.pad = 0;
+  gs.reps = kGridReps;
+  gs.rep_words = rep_words;
   gs.poll_limit = kGridPollLimit;
   const GridFn fn = grid_kernel(A, gp.rpt, gp.nb);
   if (fn == nullptr) {

@@ -77,10 +77,10 @@ struct sla_csr_s {
   hipEvent_t poll_ev[2] = {nullptr, nullptr};
   double* hist = nullptr;
   // resident grid loop (allocated by its first solve): tagged sum slots,
-  // published boundary rows of r, the failure flag, the time of the last
+  // published boundary rows (tagged words), the failure flag, the time of the last
   // launch
   uint64_t* grid_slot = nullptr;
-  double* grid_halo = nullptr;
+  uint64_t* grid_halo = nullptr;
   int* grid_fail = nullptr;
   int64_t grid_slot_words = 0;
   int64_t grid_halo_len = 0;
