@@ -1747,7 +1747,10 @@ struct GridSync {
   // [2][reps][kGridVals][2][G] tagged words (round parity, replica, value,
   // high/low half, workgroup), a replica every rep_words words
   uint64_t* slot;
-  uint64_t* halo;      // [2][G][2 H][2] tagged words: first H rows, last H rows
+  // [2][G][2][2 H] tagged words (parity, workgroup, high/low half, entry:
+  // first H rows, then last H rows), so a store or load of a wave is
+  // contiguous
+  uint64_t* halo;
   int* fail;           // set when a wait passed its poll limit
   int64_t rw;          // rows per workgroup
   int32_t H;           // halo rows on each side
@@ -1769,11 +1772,11 @@ __device__ __forceinline__ int dev_get(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// v as two words at p, p + 1: its high and low 32 bits each beside the tag
-__device__ __forceinline__ void put_tagged(uint64_t* p, double v, uint32_t tag) {
+// v as two words at hi and lo: its high and low 32 bits each beside the tag
+__device__ __forceinline__ void put_tagged(uint64_t* hi, uint64_t* lo, double v, uint32_t tag) {
   const uint64_t bits = uint64_t(__double_as_longlong(v));
-  dev_put(p, (bits & 0xffffffff00000000ull) | tag);
-  dev_put(p + 1, (bits << 32) | tag);
+  dev_put(hi, (bits & 0xffffffff00000000ull) | tag);
+  dev_put(lo, (bits << 32) | tag);
 }
 __device__ __forceinline__ bool has_tag(uint64_t hi, uint64_t lo, uint32_t tag) {
   return uint32_t(hi) == tag && uint32_t(lo) == tag;
@@ -1841,9 +1844,10 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
     }
     return;
   }
-  // this thread's rows: values by band offset, the row's bits
+  // this thread's rows: values by band offset, the rows' bits packed a byte
+  // per row (NB <= 8)
   double bv[RPT][NB];
-  uint32_t bm[RPT];
+  uint64_t bmp = 0;
   int32_t boff[NB];
 #pragma unroll
   for (int o = 0; o < NB; ++o) boff[o] = cv.band.off[o];
@@ -1851,15 +1855,16 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int l = t + j * NT;
-    bm[j] = 0;
+    uint32_t bm = 0;
     int64_t k = 0;
     if (l < nloc) {
-      bm[j] = uint32_t(mask[l]) & ((1u << cnt) - 1u);
+      bm = uint32_t(mask[l]) & ((1u << cnt) - 1u);
       k = int64_t(rowptr[l]);
     }
+    bmp |= uint64_t(bm) << (8 * j);
 #pragma unroll
     for (int o = 0; o < NB; ++o) {
-      const bool use = (bm[j] >> o) & 1u;
+      const bool use = (bm >> o) & 1u;
       bv[j][o] = use ? vals[k] : 0.0;
       k += use ? 1 : 0;
     }
@@ -1870,7 +1875,8 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   // this thread's halo entries e = t + u * 512 < 2 H: e < H the row
   // r0 - H + e (the lower neighbour's last rows), else r0 + nloc + e - H (the
   // upper neighbour's first rows); LDS index e, or nloc + e.  hsrc: the
-  // entry's index in a halo buffer of one parity, or -1 (no such row).
+  // high word's index in a halo buffer of one parity (the low word 2 H
+  // further), or -1 (no such row).
   int32_t hsrc[kGridHaloPT];
 #pragma unroll
   for (int u = 0; u < kGridHaloPT; ++u) {
@@ -1880,18 +1886,19 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
       const bool low = e < H;
       const int64_t row = low ? r0 - H + e : r0 + nloc + (e - H);
       if (row >= 0 && row < n)
-        hsrc[u] = low ? ((g - 1) * 2 + 1) * H + e : ((g + 1) * 2) * H + (e - H);
+        hsrc[u] = low ? (g - 1) * 4 * H + H + e : (g + 1) * 4 * H + (e - H);
     }
   }
   auto hidx = [&](int u) -> int { return t + u * NT < H ? t + u * NT : nloc + t + u * NT; };
   // the same entries as this workgroup's published boundary rows: e < H the
-  // row l = e, else l = nloc - H + (e - H); psrc: the row's index in rl, or
-  // -1 (formed where used: no registers held through the loop)
-  auto psrc = [&](int u) -> int {
+  // row l = e, else l = nloc - H + (e - H); psrc: the row's index in rl, or -1
+  int32_t psrc[kGridHaloPT];
+#pragma unroll
+  for (int u = 0; u < kGridHaloPT; ++u) {
     const int e = t + u * NT;
     const int l = e < H ? e : nloc - H + (e - H);
-    return (e < 2 * H && l >= 0 && l < nloc) ? H + l : -1;
-  };
+    psrc[u] = (e < 2 * H && l >= 0 && l < nloc) ? H + l : -1;
+  }
   // index of row l of the block in rl; rows past the block (lanes without a
   // row, whose values are all zero) store to one spare slot past the halo
   const int spare = nloc + 2 * H;
@@ -1909,7 +1916,7 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int li = own_idx(t + j * NT) + z;  // (rows past the block: m = 0)
-      const uint32_t m = bm[j] + uint32_t(z);
+      const uint32_t m = uint32_t(bmp >> (8 * j)) + uint32_t(z);
       double gv[NB];
 #pragma unroll
       for (int o = 0; o < NB; ++o) gv[o] = rl[((m >> o) & 1u) ? li + boff[o] : li];
@@ -1936,7 +1943,10 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
     uint64_t* hb = own_halo(par);
 #pragma unroll
     for (int u = 0; u < kGridHaloPT; ++u)
-      if (psrc(u) >= 0) put_tagged(hb + 2 * uint32_t(t + u * NT), rl[psrc(u)], tag);
+      if (psrc[u] >= 0) {
+        const uint32_t e = uint32_t(t + u * NT);
+        put_tagged(hb + e, hb + 2 * H + e, rl[psrc[u]], tag);
+      }
   };
   // u_k of the rows staged in ul (rows past the block at ul[rw]) before the
   // sum's first barrier; its boundary rows go out from there after that
@@ -1949,7 +1959,10 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
     uint64_t* hb = own_halo(par);
 #pragma unroll
     for (int u = 0; u < kGridHaloPT; ++u)
-      if (psrc(u) >= 0) put_tagged(hb + 2 * uint32_t(t + u * NT), ul[psrc(u) - H], tag);
+      if (psrc[u] >= 0) {
+        const uint32_t e = uint32_t(t + u * NT);
+        put_tagged(hb + e, hb + 2 * H + e, ul[psrc[u] - H], tag);
+      }
   };
   // the neighbours' words of this thread's halo entries in buffer `par`
   // (entries without a row read as tagged zeros)
@@ -1959,8 +1972,8 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
     for (int u = 0; u < kGridHaloPT; ++u) {
       hw[u][0] = hw[u][1] = tag;
       if (hsrc[u] >= 0) {
-        hw[u][0] = dev_get(hb + 2 * uint32_t(hsrc[u]));
-        hw[u][1] = dev_get(hb + 2 * uint32_t(hsrc[u]) + 1);
+        hw[u][0] = dev_get(hb + uint32_t(hsrc[u]));
+        hw[u][1] = dev_get(hb + uint32_t(hsrc[u]) + 2 * H);
       }
     }
   };
@@ -2084,6 +2097,8 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
   };
   using Two = std::integral_constant<int, 2>;
 
+  // (the halo rows of r live in rl, whose entries hidx(u) only this thread
+  // reads and writes; rh holds r_0's while they arrive)
   double r[RPT], s[RPT], q[RPT], rh[kGridHaloPT], sh[kGridHaloPT];
   uint64_t hw[kGridHaloPT][2];
   // r0 = b - A x0 (or b, x0 = 0): x0 of the rows and of the halo from x,
@@ -2212,8 +2227,7 @@ __global__ __launch_bounds__(kGridThreads) void k_cg_grid(const Ctx cv, Scal* __
 #pragma unroll
     for (int u = 0; u < kGridHaloPT; ++u) {
       sh[u] = uh[u] + beta * sh[u];
-      rh[u] = rh[u] - alpha * sh[u];
-      if (hsrc[u] >= 0) rl[hidx(u)] = rh[u];
+      if (hsrc[u] >= 0) rl[hidx(u)] = rl[hidx(u)] - alpha * sh[u];
     }
     __syncthreads();
     if (hfail != 0) {
