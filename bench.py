@@ -1271,13 +1271,13 @@ def main():
                         us_per_iteration=1e3 * loop_ms / head["loop_iterations"],
                         source_digest=digest,
                         note="the loop reads the matrix once per launch and per iteration moves "
-                             "only halo rows and two partial sums between workgroups, so the "
+                             "only halo rows and the partial sums between workgroups, so the "
                              "canonical bytes a streaming iteration moves (12 nnz + 4 (n+1) + "
                              "88 n) exceed what HBM could deliver in its time (frac > 1); "
                              "traffic is what the counters saw per launch.  It is bound by the "
-                             "two grid-wide sums per iteration (3.3 us each measured alone) and "
-                             "the halo exchange, not by HBM; sizes.16m / sizes.169m carry the "
-                             "HBM-bound rooflines of the two-kernel loop")
+                             "latency of its one grid-wide sum per iteration (single-reduction "
+                             "CG) and the on-chip SpMV, not by HBM; sizes.16m / sizes.169m "
+                             "carry the HBM-bound rooflines of the two-kernel loop")
         if roofline["traffic"]:
             roofline["frac_kernel_moved"] = roofline["traffic"] / (loop_ms * 1e-3) / 1e9 / \
                 HBM_PEAK_GBPS
