@@ -3,7 +3,8 @@ million unknowns held in registers and LDS, one cooperative launch per
 solve): Poisson grids from 46^2 (46 workgroups of one grid line) and 100^2
 to the 1000^2 workload (eight rows per thread), a band whose length is not a
 multiple of the workgroups' rows, fixed and converged stops, warm starts,
-history, statuses and the adjoint's refusal, against the oracle; two runs
+history, statuses and the adjoint's refusal, rough coefficients (thousands
+of iterations), against the oracle; two runs
 give the same bits; the two-kernel loop agrees within rounding."""
 import numpy as np
 import pytest
@@ -111,6 +112,33 @@ def test_band_ragged_blocks(n, offs):
     xo, io = oracle.cg(A, b, 1e-11, 5000)
     gbo, gvo, aio = oracle.adjoint(A, xo, g, 1e-11, 5000)
     say(f"band n={n} offs={offs}: it {info.iterations}/{io.iterations} x {rel(x, xo):.1e}")
+    assert iters_close(info.iterations, io.iterations)
+    assert iters_close(ai.iterations, aio.iterations)
+    assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("N,spread", [(300, 3.0), (640, 1.5), (1000, 1.0)])
+def test_rough_coefficients_against_oracle(N, spread):
+    """Diffusion with log-uniform edge conductances (a contrast of e^(2
+    spread), thousands of iterations to 1e-10): the loop's single-reduction
+    recurrences stay within the parity bounds of the oracle's two-sum CG on
+    one, four and eight rows per thread, forward and adjoint."""
+    import oracle as O
+    O.set_threads(O.host_threads())
+    rp, c, v = W.rough_diffusion_csr(N, 3, spread)
+    n = N * N
+    b = W.normal_rhs(n, 5)
+    g = W.normal_rhs(n, 6)
+    P = csr_handle(rp, c)
+    x, gb, gv, info, ai = _solve_adjoint(P, v, b, g, 1e-10, 40000)
+    assert _resident(P)
+    A = _A(rp, c, v)
+    xo, io = oracle.cg(A, b, 1e-10, 40000)
+    gbo, gvo, aio = oracle.adjoint(A, xo, g, 1e-10, 40000)
+    say(f"rough {N}^2 spread {spread}: it {info.iterations}/{io.iterations} adj "
+        f"{ai.iterations}/{aio.iterations}; x {rel(x, xo):.1e} lam {rel(gb, gbo):.1e} "
+        f"gv {rel(gv, gvo):.1e}")
+    assert info.converged and ai.converged
     assert iters_close(info.iterations, io.iterations)
     assert iters_close(ai.iterations, aio.iterations)
     assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD

@@ -37,3 +37,45 @@ def test_convection_diffusion_csr(N, dtype):
     D = np.zeros((n, n))
     D[rows, c] = v
     assert np.array_equal(D, _dense_convection_diffusion(N))
+
+
+@pytest.mark.parametrize("N", [1, 2, 5])
+def test_rough_diffusion_csr(N):
+    """The rough-coefficient operator against its definition written cell by
+    cell: every edge's conductance on both its cells' diagonals and, between
+    two cells, off the diagonal with a minus sign; symmetric positive
+    definite; rows ascending; the same seed gives the same matrix."""
+    rp, c, v = W.rough_diffusion_csr(N, 11, 2.0)
+    n = N * N
+    D = np.zeros((n, n))
+    rows = np.repeat(np.arange(n), np.diff(rp))
+    D[rows, c] = v
+    for i in range(n):
+        assert np.all(np.diff(c[rp[i]:rp[i + 1]]) > 0)
+    rng = np.random.default_rng(11)
+    cx = np.exp(rng.uniform(-2.0, 2.0, (N, N + 1)))
+    cy = np.exp(rng.uniform(-2.0, 2.0, (N + 1, N)))
+    M = np.zeros((n, n))
+    for r in range(N):
+        for q in range(N + 1):      # edge left of cell (r, q) / right of (r, q - 1)
+            for cell in ((r, q - 1), (r, q)):
+                if 0 <= cell[1] < N:
+                    M[cell[0] * N + cell[1], cell[0] * N + cell[1]] += cx[r, q]
+            if 0 < q < N:
+                a, b = r * N + q - 1, r * N + q
+                M[a, b] -= cx[r, q]
+                M[b, a] -= cx[r, q]
+    for r in range(N + 1):
+        for q in range(N):          # edge above cell (r, q) / below (r - 1, q)
+            for cell in ((r - 1, q), (r, q)):
+                if 0 <= cell[0] < N:
+                    M[cell[0] * N + cell[1], cell[0] * N + cell[1]] += cy[r, q]
+            if 0 < r < N:
+                a, b = (r - 1) * N + q, r * N + q
+                M[a, b] -= cy[r, q]
+                M[b, a] -= cy[r, q]
+    assert np.allclose(D, M, rtol=1e-15, atol=0)
+    assert np.array_equal(D, D.T)
+    assert np.linalg.eigvalsh(D).min() > 0
+    rp2, c2, v2 = W.rough_diffusion_csr(N, 11, 2.0)
+    assert np.array_equal(v, v2) and np.array_equal(c, c2)

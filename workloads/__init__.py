@@ -179,6 +179,39 @@ def band_csr(n: int, offsets, diag: float, off: float = -1.0, rowptr_dtype=np.in
     return np.cumsum(rowptr).astype(rowptr_dtype), col.astype(np.int32), val
 
 
+def rough_diffusion_csr(N: int, seed: int, spread: float, rowptr_dtype=np.int32):
+    """CSR of the 5-point finite-volume diffusion operator on an N x N grid
+    with a conductance per cell edge drawn log-uniform from [e^-spread,
+    e^spread] (seeded) and the grid's boundary edges held at zero (their
+    conductances on the diagonal): a_ij = -c_ij for neighbours, a_ii = the
+    sum of the cell's edge conductances.  Symmetric positive definite, its
+    condition number about e^(2 spread) times the Laplacian's.  Columns come
+    out ascending."""
+    rng = np.random.default_rng(seed)
+    n = N * N
+    cx = np.exp(rng.uniform(-spread, spread, (N, N + 1)))  # edges along a grid line
+    cy = np.exp(rng.uniform(-spread, spread, (N + 1, N)))  # edges across grid lines
+    i, j = np.divmod(np.arange(n), N)
+    diag = cx[i, j] + cx[i, j + 1] + cy[i, j] + cy[i + 1, j]
+    entries = [(np.arange(n), np.arange(n), diag)]
+    ok = j + 1 < N
+    entries.append((np.flatnonzero(ok), np.flatnonzero(ok) + 1, -cx[i[ok], j[ok] + 1]))
+    ok = j > 0
+    entries.append((np.flatnonzero(ok), np.flatnonzero(ok) - 1, -cx[i[ok], j[ok]]))
+    ok = i + 1 < N
+    entries.append((np.flatnonzero(ok), np.flatnonzero(ok) + N, -cy[i[ok] + 1, j[ok]]))
+    ok = i > 0
+    entries.append((np.flatnonzero(ok), np.flatnonzero(ok) - N, -cy[i[ok], j[ok]]))
+    row = np.concatenate([e[0] for e in entries])
+    col = np.concatenate([e[1] for e in entries])
+    val = np.concatenate([e[2] for e in entries]).astype(np.float64)
+    order = np.lexsort((col, row))
+    row, col, val = row[order], col[order], val[order]
+    rowptr = np.zeros(n + 1, np.int64)
+    np.add.at(rowptr, row + 1, 1)
+    return np.cumsum(rowptr).astype(rowptr_dtype), col.astype(np.int32), val
+
+
 def laplacian3d_csr(N: int):
     """7-point Laplacian on an N^3 grid: diagonal 6, neighbours -1."""
     st = {(0, 0, 0): 6.0}
