@@ -1733,8 +1733,9 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
 // Each workgroup publishes its boundary rows of u_k during the sum, after its
 // first barrier, into halo[k & 1], tagged as the slots are with the round of
 // that sum; a reader loads them once the sum is complete and loads again
-// while a tag is not that round (the writer issued them before its own slot
-// tags, so that is rare).  Nothing waits for the stores and no fence runs.
+// while a tag is not that round (the writer issued them alongside its slot
+// tags, so by the time every tag has been seen they have nearly always
+// landed).  Nothing waits for the stores and no fence runs.
 // Double buffering by parity suffices: a buffer is written again two
 // iterations later, after a sum that needs every reader's partials, which
 // each reader posts only after reading it.  Slots and halo words are cleared
