@@ -1333,8 +1333,9 @@ void k_cg_product(const Ctx* __restrict__ c) {
 // signal exists), with nothing in memory but LDS.  With NT threads (256 or
 // 512 by size, one_group_block) of W = NT / 64 waves:
 //   * thread t owns rows t + j * NT (j < R, R = 1, 2 or 4) and keeps their
-//     r, x, p (and the Jacobi diagonal) in registers;
-//   * p is published in LDS and every SpMV gathers it there;
+//     r, x, p, s = A p (and the Jacobi diagonal) in registers;
+//   * z = r (Jacobi: r / d) is published in LDS and every SpMV gathers it
+//     there;
 //   * banded rows: each thread holds its rows' values by band offset, loaded
 //     once, and adds value x p[i + off] in ascending offset order;
 //   * plain CSR rows: wave w owns tiles w + j * W; lane l holds the values
@@ -1343,9 +1344,13 @@ void k_cg_product(const Ctx* __restrict__ c) {
 //     its own row's products in slot order.
 // Both add a row's products in ascending column order (the bits of the
 // sequential row sum).
-// Same steps, stopping rule, statuses and history as the two-kernel loop; the
-// x update is applied at once rather than one step late (the same
-// expression); the dot products are summed in another fixed order.
+// The iteration is CG in the single-reduction form described at the resident
+// grid loop (k_cg_grid), preconditioned: w_k = A z_k, one block sum of r.r,
+// z.w and r.z, p_k.A p_k = z_k.w_k - beta_k rz_k / alpha_{k-1}, p_k = z_k +
+// beta_k p_{k-1}, s_k = w_k + beta_k s_{k-1}: one barrier fewer per
+// iteration than the two sums of the Hestenes-Stiefel form.  Stopping rule,
+// statuses and history as the two-kernel loop; results equal to it in exact
+// arithmetic, differing by rounding.
 
 // Two sums over a workgroup of W waves at once, fixed order, results in every
 // thread.
@@ -1369,36 +1374,25 @@ __device__ __forceinline__ void block_sum2(double& u, double& v, double* lds) {
   v = b;
 }
 
-// The same sums without the closing barrier, for a loop that alternates two
-// `lds` areas: the next use of an area comes after another sum's barrier, by
-// which every thread has read it.  sum1 is the one-value form.
-template <int W = kWaves>
-__device__ __forceinline__ void block_sum2_open(double& u, double& v, double* lds) {
-  u = wave_sum(u);
-  v = wave_sum(v);
+// K sums without the closing barrier, for a loop whose next use of `lds`
+// ([K][W] doubles) comes after another barrier, by which every thread has
+// read it.
+template <int W, int K>
+__device__ __forceinline__ void block_sums_open(double (&v)[K], double* lds) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = wave_sum(v[k]);
   if ((threadIdx.x & (kWave - 1)) == 0) {
-    lds[threadIdx.x / kWave] = u;
-    lds[W + threadIdx.x / kWave] = v;
+#pragma unroll
+    for (int k = 0; k < K; ++k) lds[k * W + threadIdx.x / kWave] = v[k];
   }
   __syncthreads();
-  double a = 0.0, b = 0.0;
 #pragma unroll
-  for (int w = 0; w < W; ++w) {
-    a = a + lds[w];
-    b = b + lds[W + w];
+  for (int k = 0; k < K; ++k) {
+    double a = 0.0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) a = a + lds[k * W + w];
+    v[k] = a;
   }
-  u = a;
-  v = b;
-}
-template <int W = kWaves>
-__device__ __forceinline__ double block_sum1_open(double u, double* lds) {
-  u = wave_sum(u);
-  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = u;
-  __syncthreads();
-  double a = 0.0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) a = a + lds[w];
-  return a;
 }
 
 // Threads per workgroup of the small-system kernel: 256 up to 256 unknowns
@@ -1445,7 +1439,7 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
   constexpr int W = NT / kWave;
   extern __shared__ double lds_dyn[];
   __shared__ double red[2 * W];
-  __shared__ double red_a[W], red_b[2 * W];  // the loop's two areas
+  __shared__ double red3[3 * W];  // the loop's sums
   const int64_t s = blockIdx.x;
   const int64_t n = cv.n, nnz = cv.nnz;
   const int64_t npad = (n + NT - 1) / NT * NT;
@@ -1598,70 +1592,80 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
   if (JAC && bad != 0.0) state = ST_NOT_SPD;  // a diagonal entry is not > 0
   int64_t it = 0;
   double rr_final = rr;
-  double alpha = 0.0, rr_prev = rr, rz_prev = rz;
+  double alpha = 0.0;
+  double sv[R];  // s = A p
+#pragma unroll
+  for (int j = 0; j < R; ++j) sv[j] = 0.0;
+  // single-reduction form (see the resident grid loop): w_k = A z_k, one
+  // block sum of r.r, r.z and z.w, then p.Ap = z.w - beta rz / alpha_{k-1};
   // every thread holds the same scalars, so every branch below is uniform
   for (int64_t k = 0; state == ST_RUNNING; ++k) {
-    double beta = 0.0;
-    if (k > 0) {
-      if (!isfinite(rr) || !isfinite(rz)) {
-        state = ST_NONFINITE;  // iteration k-1 did not complete
-        it = k - 1;
-        rr_final = rr_prev;
-        break;
-      }
-      beta = JAC ? rz / rz_prev : rr / rr_prev;
-      if (hist != nullptr && t == 0 && k - 1 < hist_cap) {
-        hist[(k - 1) * 3 + 0] = alpha;
-        hist[(k - 1) * 3 + 1] = beta;
-        hist[(k - 1) * 3 + 2] = rr;
-      }
-    }
-    if (rr <= stop || k >= maxit) {
-      state = rr <= stop ? ST_CONVERGED : ST_MAXIT;
-      it = k;
-      rr_final = rr;
-      break;
-    }
-    // p_k = r_k (z_k) + beta p_{k-1}, published in LDS for the gathers
+    // z_k = r_k (Jacobi: r_k / d) published in LDS for the gathers (the
+    // last sum's barrier ended every wave's gathers of z_{k-1} and every
+    // read of red3)
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const double src = JAC ? r[j] / dv[j] : r[j];
-      pv[j] = src + beta * pv[j];
       const int64_t i = t + int64_t(j) * NT;
-      if (i < npad) pl[i] = pv[j];
+      if (i < npad) pl[i] = JAC ? r[j] / dv[j] : r[j];
     }
     __syncthreads();
     spmv(q);
-    double pq = 0.0;
+    // r.r, z.w and (Jacobi) r.z
+    constexpr int K = JAC ? 3 : 2;
+    double g[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) g[c] = 0.0;
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      if (t + int64_t(j) * NT < n) pq = pq + pv[j] * q[j];
-    // (the barrier of the sum also ends every wave's gathers of p_k; red_a
-    // was last read before the previous iteration's second sum)
-    pq = block_sum1_open<W>(pq, red_a);
+      if (t + int64_t(j) * NT < n) {
+        const double zj = JAC ? r[j] / dv[j] : r[j];
+        g[0] = g[0] + r[j] * r[j];
+        g[1] = g[1] + zj * q[j];
+        if constexpr (JAC) g[2] = g[2] + r[j] * zj;
+      }
+    block_sums_open<W, K>(g, red3);
+    const double g_rr = g[0], g_zw = g[1], g_rz = g[JAC ? 2 : 0];
+    double beta = 0.0;
+    if (k > 0) {
+      if (!isfinite(g_rr) || !isfinite(g_rz)) {
+        state = ST_NONFINITE;  // iteration k-1 did not complete
+        it = k - 1;
+        rr_final = rr;
+        break;
+      }
+      beta = g_rz / rz;
+      if (hist != nullptr && t == 0 && k - 1 < hist_cap) {
+        hist[(k - 1) * 3 + 0] = alpha;
+        hist[(k - 1) * 3 + 1] = beta;
+        hist[(k - 1) * 3 + 2] = g_rr;
+      }
+    }
+    if (g_rr <= stop || k >= maxit) {
+      state = g_rr <= stop ? ST_CONVERGED : ST_MAXIT;
+      it = k;
+      rr_final = g_rr;
+      break;
+    }
+    const double pq = k > 0 ? g_zw - beta * (g_rz / alpha) : g_zw;  // p_k.A p_k
     if (!isfinite(pq) || !(pq > 0.0)) {
       state = !isfinite(pq) ? ST_NONFINITE : ST_NOT_SPD;
       it = k;
-      rr_final = rr;
+      rr_final = g_rr;
       break;
     }
-    alpha = (JAC ? rz : rr) / pq;
-    double rn = 0.0, rzn = 0.0;
+    alpha = g_rz / pq;
+    rr = g_rr;
+    rz = g_rz;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       if (t + int64_t(j) * NT < n) {
+        const double zj = JAC ? r[j] / dv[j] : r[j];
+        pv[j] = zj + beta * pv[j];
+        sv[j] = q[j] + beta * sv[j];
         xv[j] = xv[j] + alpha * pv[j];
-        r[j] = r[j] - alpha * q[j];
-        rn = rn + r[j] * r[j];
-        if constexpr (JAC) rzn = rzn + r[j] * (r[j] / dv[j]);
+        r[j] = r[j] - alpha * sv[j];
       }
     }
-    // (red_b was last read before this iteration's first sum)
-    block_sum2_open<W>(rn, rzn, red_b);
-    rr_prev = rr;
-    rz_prev = rz;
-    rr = rn;
-    rz = rzn;
   }
 #pragma unroll
   for (int j = 0; j < R; ++j) {
@@ -1705,7 +1709,7 @@ __global__ __launch_bounds__(NT) void k_cg_onegroup(const Ctx cv, Scal* __restri
 // The middle identity expands p_k.A p_k with r_k.r_{k-1} = 0 and
 // A p_{k-1} = (r_{k-1} - r_k) / alpha_{k-1}.  In exact arithmetic these are
 // the iterates, scalars, stopping rule and statuses of the loop with two sums
-// (Hestenes-Stiefel, the one-workgroup and two-kernel loops); in floating
+// (Hestenes-Stiefel, the two-kernel loop); in floating
 // point they differ from it by rounding.  The sum's latency is most of an
 // iteration here, so one sum per iteration instead of two is what counts.
 //
