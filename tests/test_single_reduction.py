@@ -1,5 +1,6 @@
 """The single-reduction rearrangement of CG (Chronopoulos and Gear) that the
-resident grid loop runs, written out in numpy from its recurrences, against
+resident grid loop and the one-workgroup loop run (the latter also with
+Jacobi preconditioning), written out in numpy from its recurrences, against
 the oracle's two-sum CG ([torch-sla · Methodology 1], the CG iteration): the
 same alpha, beta and r.r history and the same x, to rounding, on a Poisson
 grid and on rough-coefficient diffusion; and, step by step, the identity it
@@ -92,6 +93,52 @@ def test_single_reduction_converged_solution():
     assert gm[-1] <= stop and np.all(gm[:-1] > stop)
     assert abs(k - io.iterations) <= max(1, 0.02 * io.iterations)
     assert np.linalg.norm(x - xo) <= 1e-9 * np.linalg.norm(xo)
+
+
+def test_single_reduction_jacobi_matches_oracle_pcg():
+    """The preconditioned form (z = r / d, w = A z; one sum of r.r, z.w and
+    r.z; p.Ap = z.w - beta r.z / alpha) against the oracle's Jacobi PCG:
+    alpha, beta, r.r and r.z histories and x."""
+    rp, c, v = W.rough_diffusion_csr(16, 7, 2.0)
+    n = len(rp) - 1
+    A = sp.csr_matrix((v, c, rp), shape=(n, n))
+    d = A.diagonal()
+    b = W.normal_rhs(n, 8)
+    iters = 25
+    Ao = oracle.CSR(n, np.asarray(rp, np.int64), np.asarray(c, np.int32), v)
+    xo, io, (ao, bo, ro, zo) = oracle.pcg_jacobi(Ao, b, 0.0, iters, history=True)
+    assert io.iterations == iters
+    x = np.zeros(n)
+    r = b.copy()
+    p = np.zeros(n)
+    s = np.zeros(n)
+    alpha = rz_prev = 0.0
+    al, be, rrs, rzs = [], [], [], []
+    for k in range(iters + 1):
+        z = r / d
+        w = A @ z
+        rr, zw, rz = r @ r, z @ w, r @ z
+        beta = rz / rz_prev if k > 0 else 0.0
+        if k > 0:
+            be.append(beta)
+            rrs.append(rr)
+            rzs.append(rz)
+        if k == iters:
+            break
+        pap = zw - beta * (rz / alpha) if k > 0 else zw
+        p = z + beta * p
+        s = w + beta * s
+        assert abs(pap - p @ (A @ p)) <= 1e-10 * abs(pap)
+        alpha = rz / pap
+        al.append(alpha)
+        x = x + alpha * p
+        r = r - alpha * s
+        rz_prev = rz
+    assert np.allclose(al, ao, rtol=1e-9, atol=0)
+    assert np.allclose(be, bo, rtol=1e-9, atol=0)
+    assert np.allclose(rrs, ro, rtol=1e-8, atol=0)
+    assert np.allclose(rzs, zo, rtol=1e-8, atol=0)
+    assert np.linalg.norm(x - xo) <= 1e-10 * np.linalg.norm(xo)
 
 
 def test_planted_sign_error_is_caught():
