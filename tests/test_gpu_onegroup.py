@@ -1,7 +1,8 @@
 """The one-workgroup CG loop for small systems (at most 2048 unknowns; a
 banded pattern, or plain CSR rows whose 64-row tiles hold at most 336 slots):
-ragged sizes, Jacobi, history, warm starts, statuses and batches against the
-oracle, in the default (automatic) mode and with the two-kernel loop forced;
+ragged sizes, Jacobi, history, warm starts, statuses, batches and rough
+coefficients against the oracle, in the default (automatic) mode and with
+the two-kernel loop forced;
 banded rows against the staged CSR rows bit for bit; systems outside its range
 take the resident grid loop (banded) or the two-kernel loop bit for bit."""
 import numpy as np
@@ -338,3 +339,38 @@ def test_adjoint_refused_on_the_device():
     torch.cuda.synchronize()
     assert ai.converged and iters_close(ai.iterations, aio.iterations)
     assert rel(gb.cpu().numpy(), gbo) <= TOL_X and rel(gv.cpu().numpy(), gvo) <= TOL_GRAD
+
+
+@pytest.mark.parametrize("jac", [False, True])
+def test_rough_coefficients_single_reduction(jac):
+    """Rough-coefficient diffusion on 45^2 = 2025 unknowns (four rows per
+    thread), plain and Jacobi-preconditioned, forward and adjoint to 1e-10
+    (hundreds of iterations at a conductance contrast of e^6): the loop's
+    single-reduction recurrences within the parity bounds of the oracle's
+    two-sum CG and PCG."""
+    import torch
+    import krylov_solvers_adjoint_amd as K
+    rp, c, v = W.rough_diffusion_csr(45, 4, 3.0)
+    n = len(rp) - 1
+    b = W.normal_rhs(n, 15)
+    g = W.normal_rhs(n, 16)
+    P = csr_handle(rp, c)
+    vt = t(v)
+    x, info = K.sla_cg_solve(P, vt, t(b), 1e-10, 20000, jacobi=jac)
+    gb, gv, ai = K.sla_cg_adjoint(P, vt, x, t(g), 1e-10, 20000, jacobi=jac)
+    torch.cuda.synchronize()
+    A = _A(rp, c, v)
+    if jac:
+        xo, io = oracle.pcg_jacobi(A, b, 1e-10, 20000)
+        gbo, gvo, aio = oracle.adjoint_jacobi(A, xo, g, 1e-10, 20000)
+    else:
+        xo, io = oracle.cg(A, b, 1e-10, 20000)
+        gbo, gvo, aio = oracle.adjoint(A, xo, g, 1e-10, 20000)
+    x, gb, gv = x.cpu().numpy(), gb.cpu().numpy(), gv.cpu().numpy()
+    say(f"rough 45^2 jacobi={jac}: it {info.iterations}/{io.iterations} adj "
+        f"{ai.iterations}/{aio.iterations}; x {rel(x, xo):.1e} lam {rel(gb, gbo):.1e} "
+        f"gv {rel(gv, gvo):.1e}")
+    assert info.converged and ai.converged
+    assert iters_close(info.iterations, io.iterations)
+    assert iters_close(ai.iterations, aio.iterations)
+    assert rel(x, xo) <= TOL_X and rel(gb, gbo) <= TOL_X and rel(gv, gvo) <= TOL_GRAD
