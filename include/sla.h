@@ -606,12 +606,13 @@ sla_status sla_csr_ordering(sla_csr A, int32_t* order_out, hipStream_t stream);
  * runs its whole CG loop in one cooperative launch with the system held in
  * registers and LDS (the resident grid loop): the matrix is read once per
  * solve, and the workgroups exchange only halo rows and the partial sums of
- * each iteration.  It runs CG in its single-reduction form (Chronopoulos and
- * Gear: r.r and r.Ar summed together, p.Ap from them), so one grid-wide sum
- * per iteration: the same iterates, scalars, stopping rule, statuses and
- * history in exact arithmetic, results that differ from the two-kernel
- * loop's by rounding (relative 1e-13 in x after 1000 iterations at 10^6
- * unknowns).  A grid-wide wait of the resident
+ * each iteration.  Both loops run CG in its single-reduction form
+ * (Chronopoulos and Gear: r.r and r.Ar summed together, p.Ap from them; with
+ * Jacobi, r.r, z.Az and r.z), so one grid-wide or workgroup sum per
+ * iteration: the same iterates, scalars, stopping rule, statuses and history
+ * in exact arithmetic, results that differ from the two-kernel loop's by
+ * rounding (relative 1e-13 in x after 1000 iterations at 10^6 unknowns).  A
+ * grid-wide wait of the resident
  * loop that exceeds its poll limit (seconds) ends the solve with
  * SLA_ERR_DEVICE.  SLA_ONE_GROUP_OFF: always the two-kernel loop.  Applies to
  * sla_cg_solve / _batched, the adjoint solves and the CG lists.
